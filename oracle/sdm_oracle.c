@@ -1,0 +1,347 @@
+/*
+ * Sparse Delta Memory: CPU oracle. TEST INFRASTRUCTURE ONLY.
+ *
+ * Plain, slow, sequential per-token implementation of what the SDM write/read computes, in fp64 arithmetic.
+ * It shares no code with the HIP library (no common headers, helpers or tables). Only the test-suite, the smoke
+ * check and the bench's cpu_baseline leg load it. Build: gcc -O2 -fPIC -shared -ffp-contract=off -pthread
+ * (no fast-math: the factor score and the float32 slot-score additions must be IEEE round-to-nearest-even).
+ *
+ * Sources (web pages):
+ *  [CL]  facebookresearch/sparse-delta-memory, CHANGELOG.md, 2.0.0: "Upgrading from v1" (slot score is the float32
+ *        sum of the factor scores; exact top-k; tie order), "New" (any number of factors of any widths; exact top-k),
+ *        "Deterministic", "Behavior changes".
+ *  [RM]  facebookresearch/sparse-delta-memory, README.md: summary (product keys + gated forget/input delta-rule
+ *        updates of a sparse memory), ideas (product-key memory of Lample et al. 2019; the gated delta rule of
+ *        Yang et al. 2025).
+ *  [PR]  latticedynamics/lumen PR #29 "0.8.0 - a state holds only itself, and a step can give it up": cost model
+ *        (per-token arithmetic is O((W+R) d_v), independent of the slot count).
+ *
+ * Readings taken where the pages are silent:
+ *  - factor score: float32 rounding of an fp64 fused-multiply-add chain over the sub-key coordinates, in order,
+ *    starting from +0. Factor f uses query columns [f*dk, (f+1)*dk).
+ *  - slot score: float32 sum of the factor scores, left to right, each partial rounded to float32 [CL].
+ *  - slot id: mixed radix of the per-factor sub-key indices, factor 0 most significant.
+ *  - per-factor rank: sub-keys ordered by (score descending, index ascending); position p_f = 0 is the best, so the
+ *    pages' "rank" is n_f - 1 - p_f and "larger rank sum, then larger first rank" [CL] is "smaller sum of
+ *    positions, then smaller first position"; equal first positions fall through to the next factor's position.
+ *  - exact top-k = the k best slots over ALL N slots under that total order (brute force here, by definition).
+ *  - address weights: softmax over the k selected slot scores (no temperature), as in product-key memory [RM].
+ *  - gated delta rule restricted to the selected rows [RM][PR]: with w the write weights, alpha the forget gate and
+ *    beta the input gate, r = sum_i w_i M[S_i];  delta = beta (v - alpha r);  M[S_i] <- alpha M[S_i] + w_i delta.
+ *    Rows outside the write set are untouched (per-token work independent of N [PR]).
+ *  - the read happens after the token's write: out = sum_i rho_i M[R_i].
+ *  - the bank is stored in its dtype: every written row is rounded (round-to-nearest-even) to float32 or bfloat16
+ *    after each token; the output is rounded to the activation dtype.
+ *
+ * Parity pins: the factor score against exact rational arithmetic; brute force top-k against an independent Python
+ * enumeration; tie closed forms; F = 1 textbook top-k; no-op gates; single-write closed form; the dense Gated
+ * DeltaNet limit (W = R = N); linearity. See tests/test_oracle_pins.py.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_MAX_F 4
+
+/* ---------------------------------------------------------------------------------------------------------------
+ * Rounding helpers (IEEE round-to-nearest-even).
+ * ------------------------------------------------------------------------------------------------------------- */
+
+/* Round an fp64 value to the nearest bfloat16 (8 significant bits, float32 exponent range), ties to even, returned
+ * as a float (exactly representable). Done directly from fp64 so there is no double rounding through float32. */
+double oracle_round_bf16(double x) {
+  if (x == 0.0 || !isfinite(x)) return (double)(float)x;
+  int e;
+  frexp(x, &e);                            /* |x| = m * 2^e, m in [0.5, 1) */
+  int lsb_exp = e - 8;                     /* 8 significant bits */
+  if (lsb_exp < -133) lsb_exp = -133;      /* bfloat16 subnormal spacing = 2^-133 */
+  double q = nearbyint(ldexp(x, -lsb_exp)); /* exact scaling, then RNE to an integer */
+  double r = ldexp(q, lsb_exp);
+  if (fabs(r) > 3.3895313892515355e38) r = copysign(INFINITY, x); /* above the largest finite bfloat16 */
+  return r;
+}
+
+static inline float round_to(double x, int bf16) { return bf16 ? (float)oracle_round_bf16(x) : (float)x; }
+
+/* ---------------------------------------------------------------------------------------------------------------
+ * Factor scores.
+ * ------------------------------------------------------------------------------------------------------------- */
+
+/* s[i] = fl32( fma chain over c of q[c] * C[i][c], starting from +0, in coordinate order ). */
+void oracle_factor_scores(int n, int dk, const float* q, const float* C, float* s) {
+  for (int i = 0; i < n; ++i) {
+    double acc = 0.0;
+    for (int c = 0; c < dk; ++c) acc = fma((double)q[c], (double)C[(size_t)i * dk + c], acc);
+    s[i] = (float)acc;
+  }
+}
+
+/* ---------------------------------------------------------------------------------------------------------------
+ * Exact product-key top-k, by brute force over every slot.
+ * ------------------------------------------------------------------------------------------------------------- */
+
+typedef struct {
+  float S;               /* float32 slot score */
+  int psum;              /* sum of per-factor positions */
+  int p[ORACLE_MAX_F];   /* per-factor positions (0 = best) */
+  int64_t id;
+} cand_t;
+
+/* Total order: larger slot score first; then smaller position sum (= larger rank sum); then smaller position in
+ * factor 0 (= larger first rank), then factor 1, ... Returns <0 if a precedes b. */
+static int cand_cmp(const cand_t* a, const cand_t* b, int F) {
+  if (a->S > b->S) return -1;
+  if (a->S < b->S) return 1;
+  if (a->psum != b->psum) return a->psum < b->psum ? -1 : 1;
+  for (int f = 0; f < F; ++f)
+    if (a->p[f] != b->p[f]) return a->p[f] < b->p[f] ? -1 : 1;
+  return 0;
+}
+
+typedef struct { float s; int i; } fs_t;
+static int fs_cmp(const void* x, const void* y) {
+  const fs_t* a = (const fs_t*)x; const fs_t* b = (const fs_t*)y;
+  if (a->s > b->s) return -1;
+  if (a->s < b->s) return 1;
+  return a->i < b->i ? -1 : (a->i > b->i ? 1 : 0);
+}
+
+/* One query of one head. q: [F*dk]; sub: [sum_f n_f, dk] (factor tables stacked in factor order).
+ * Outputs the k best slots, best first: ids (int32) and float32 slot scores. Scratch is allocated here.
+ * Returns 0, or -1 on allocation failure / bad arguments. */
+int oracle_topk_one(int F, const int* widths, int dk, const float* q, const float* sub, int k, int32_t* ids,
+                    float* scores) {
+  if (F < 1 || F > ORACLE_MAX_F || k < 1) return -1;
+  int64_t N = 1;
+  for (int f = 0; f < F; ++f) N *= widths[f];
+  if (k > N) return -1;
+  float* fsc[ORACLE_MAX_F];
+  int* pos[ORACLE_MAX_F];
+  fs_t* tmp = NULL;
+  int maxw = 0;
+  for (int f = 0; f < F; ++f) if (widths[f] > maxw) maxw = widths[f];
+  tmp = (fs_t*)malloc(sizeof(fs_t) * (size_t)maxw);
+  cand_t* best = (cand_t*)malloc(sizeof(cand_t) * (size_t)k);
+  int ok = tmp && best;
+  for (int f = 0; f < F; ++f) { fsc[f] = NULL; pos[f] = NULL; }
+  size_t off = 0;
+  for (int f = 0; f < F && ok; ++f) {
+    fsc[f] = (float*)malloc(sizeof(float) * (size_t)widths[f]);
+    pos[f] = (int*)malloc(sizeof(int) * (size_t)widths[f]);
+    if (!fsc[f] || !pos[f]) { ok = 0; break; }
+    oracle_factor_scores(widths[f], dk, q + (size_t)f * dk, sub + off * dk, fsc[f]);
+    off += widths[f];
+    for (int i = 0; i < widths[f]; ++i) { tmp[i].s = fsc[f][i]; tmp[i].i = i; }
+    qsort(tmp, (size_t)widths[f], sizeof(fs_t), fs_cmp);
+    for (int p = 0; p < widths[f]; ++p) pos[f][tmp[p].i] = p;
+  }
+  if (ok) {
+    int nbest = 0;
+    int dig[ORACLE_MAX_F] = {0, 0, 0, 0};
+    for (int64_t id = 0; id < N; ++id) {
+      /* digits of id in mixed radix (factor 0 most significant), kept incrementally */
+      if (id > 0) {
+        for (int f = F - 1; f >= 0; --f) {
+          if (++dig[f] < widths[f]) break;
+          dig[f] = 0;
+        }
+      }
+      cand_t c;
+      float S = fsc[0][dig[0]];
+      for (int f = 1; f < F; ++f) S = S + fsc[f][dig[f]]; /* float32 addition, left to right */
+      c.S = S;
+      c.psum = 0;
+      for (int f = 0; f < ORACLE_MAX_F; ++f) c.p[f] = 0;
+      for (int f = 0; f < F; ++f) { c.p[f] = pos[f][dig[f]]; c.psum += c.p[f]; }
+      c.id = id;
+      if (nbest == k && cand_cmp(&c, &best[k - 1], F) >= 0) continue;
+      /* insert into the sorted list */
+      int j = nbest < k ? nbest : k - 1;
+      while (j > 0 && cand_cmp(&c, &best[j - 1], F) < 0) { best[j] = best[j - 1]; --j; }
+      best[j] = c;
+      if (nbest < k) ++nbest;
+    }
+    for (int i = 0; i < k; ++i) { ids[i] = (int32_t)best[i].id; scores[i] = best[i].S; }
+  }
+  for (int f = 0; f < F; ++f) { free(fsc[f]); free(pos[f]); }
+  free(tmp);
+  free(best);
+  return ok ? 0 : -1;
+}
+
+/* Softmax over k float32 scores, in fp64, max-subtracted. */
+static void softmax64(int k, const float* s, double* w) {
+  double m = s[0];
+  for (int i = 1; i < k; ++i) if (s[i] > m) m = s[i];
+  double z = 0.0;
+  for (int i = 0; i < k; ++i) { w[i] = exp((double)s[i] - m); z += w[i]; }
+  for (int i = 0; i < k; ++i) w[i] /= z;
+}
+
+void oracle_softmax(int k, const float* s, double* w) { softmax64(k, s, w); }
+
+/* ---------------------------------------------------------------------------------------------------------------
+ * Top-k over a [B, T, H, F*dk] query tensor (per-head sub-key tables [H, sum n_f, dk]).
+ * ------------------------------------------------------------------------------------------------------------- */
+
+typedef struct {
+  int B, T, H, F, dk, k;
+  const int* widths;
+  const float* q;
+  const float* sub;
+  int32_t* ids;
+  float* scores;
+  int64_t sumn;
+  int64_t begin, end; /* row range [begin, end) over B*T*H rows */
+  int err;
+} topk_job_t;
+
+static void* topk_worker(void* arg) {
+  topk_job_t* j = (topk_job_t*)arg;
+  for (int64_t row = j->begin; row < j->end; ++row) {
+    int h = (int)(row % j->H);
+    if (oracle_topk_one(j->F, j->widths, j->dk, j->q + row * (int64_t)j->F * j->dk, j->sub + (int64_t)h * j->sumn * j->dk,
+                        j->k, j->ids + row * j->k, j->scores + row * j->k) != 0)
+      j->err = 1;
+  }
+  return NULL;
+}
+
+int oracle_topk(int B, int T, int H, int F, const int* widths, int dk, const float* queries, const float* subkeys,
+                int k, int32_t* ids, float* scores, int nthreads) {
+  int64_t rows = (int64_t)B * T * H;
+  int64_t sumn = 0;
+  for (int f = 0; f < F; ++f) sumn += widths[f];
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 256) nthreads = 256;
+  pthread_t th[256];
+  int started[256];
+  topk_job_t jobs[256];
+  int err = 0;
+  for (int i = 0; i < nthreads; ++i) {
+    topk_job_t* j = &jobs[i];
+    j->B = B; j->T = T; j->H = H; j->F = F; j->dk = dk; j->k = k; j->widths = widths; j->q = queries;
+    j->sub = subkeys; j->ids = ids; j->scores = scores; j->sumn = sumn; j->err = 0;
+    j->begin = rows * i / nthreads; j->end = rows * (i + 1) / nthreads;
+    started[i] = pthread_create(&th[i], NULL, topk_worker, j) == 0;
+    if (!started[i]) topk_worker(j);
+  }
+  for (int i = 0; i < nthreads; ++i) { if (started[i]) pthread_join(th[i], NULL); err |= jobs[i].err; }
+  return err ? -1 : 0;
+}
+
+/* ---------------------------------------------------------------------------------------------------------------
+ * The write/read: sequential per token, one stream (b, h) at a time.
+ * ------------------------------------------------------------------------------------------------------------- */
+
+typedef struct {
+  int B, T, H, F, dk, d, W, R, bank_bf16, act_bf16;
+  const int* widths;
+  const float *wkeys, *rq, *values, *alpha, *beta, *sub;
+  float* bank;
+  int64_t bank_rows;
+  float* out;
+  int32_t *widx, *ridx;
+  float *wsc, *rsc;
+  int64_t sumn;
+  int s_begin, s_end; /* stream range over B*H streams, stream = b*H + h */
+  int err;
+} wr_job_t;
+
+static void* wr_worker(void* arg) {
+  wr_job_t* j = (wr_job_t*)arg;
+  const int F = j->F, dk = j->dk, d = j->d, W = j->W, R = j->R, H = j->H, T = j->T;
+  int32_t* S = (int32_t*)malloc(sizeof(int32_t) * (size_t)W);
+  int32_t* Rd = (int32_t*)malloc(sizeof(int32_t) * (size_t)R);
+  float* sS = (float*)malloc(sizeof(float) * (size_t)W);
+  float* sR = (float*)malloc(sizeof(float) * (size_t)R);
+  double* w = (double*)malloc(sizeof(double) * (size_t)W);
+  double* rho = (double*)malloc(sizeof(double) * (size_t)R);
+  double* r = (double*)malloc(sizeof(double) * (size_t)d);
+  double* delta = (double*)malloc(sizeof(double) * (size_t)d);
+  double* o = (double*)malloc(sizeof(double) * (size_t)d);
+  if (!S || !Rd || !sS || !sR || !w || !rho || !r || !delta || !o) { j->err = 1; goto done; }
+  for (int st = j->s_begin; st < j->s_end; ++st) {
+    int b = st / H, h = st % H;
+    float* M = j->bank + (int64_t)st * j->bank_rows * d;
+    const float* sub = j->sub + (int64_t)h * j->sumn * dk;
+    for (int t = 0; t < T; ++t) {
+      int64_t row = ((int64_t)b * T + t) * H + h; /* [B, T, H] row */
+      if (oracle_topk_one(F, j->widths, dk, j->wkeys + row * F * dk, sub, W, S, sS) != 0 ||
+          oracle_topk_one(F, j->widths, dk, j->rq + row * F * dk, sub, R, Rd, sR) != 0) { j->err = 1; goto done; }
+      softmax64(W, sS, w);
+      softmax64(R, sR, rho);
+      const double a = j->alpha[row], be = j->beta[row];
+      const float* v = j->values + row * d;
+      /* prediction at the write address, from the rows before this token's write */
+      for (int c = 0; c < d; ++c) r[c] = 0.0;
+      for (int i = 0; i < W; ++i) {
+        const float* m = M + (int64_t)S[i] * d;
+        for (int c = 0; c < d; ++c) r[c] += w[i] * (double)m[c];
+      }
+      for (int c = 0; c < d; ++c) delta[c] = be * ((double)v[c] - a * r[c]);
+      /* gated delta-rule update of the W selected rows; stored in the bank dtype */
+      for (int i = 0; i < W; ++i) {
+        float* m = M + (int64_t)S[i] * d;
+        for (int c = 0; c < d; ++c) m[c] = round_to(a * (double)m[c] + w[i] * delta[c], j->bank_bf16);
+      }
+      /* read after the write */
+      for (int c = 0; c < d; ++c) o[c] = 0.0;
+      for (int i = 0; i < R; ++i) {
+        const float* m = M + (int64_t)Rd[i] * d;
+        for (int c = 0; c < d; ++c) o[c] += rho[i] * (double)m[c];
+      }
+      float* out = j->out + row * d;
+      for (int c = 0; c < d; ++c) out[c] = round_to(o[c], j->act_bf16);
+      if (j->widx) memcpy(j->widx + row * W, S, sizeof(int32_t) * (size_t)W);
+      if (j->ridx) memcpy(j->ridx + row * R, Rd, sizeof(int32_t) * (size_t)R);
+      if (j->wsc) memcpy(j->wsc + row * W, sS, sizeof(float) * (size_t)W);
+      if (j->rsc) memcpy(j->rsc + row * R, sR, sizeof(float) * (size_t)R);
+    }
+  }
+done:
+  free(S); free(Rd); free(sS); free(sR); free(w); free(rho); free(r); free(delta); free(o);
+  return NULL;
+}
+
+/* Tensors (all float32 arrays holding values already rounded to their dtype; bfloat16 values are exact in float32):
+ *   wkeys, rq  [B, T, H, F*dk]   write keys / read queries
+ *   values     [B, T, H, d]
+ *   alpha,beta [B, T, H]         forget / input gates
+ *   subkeys    [H, sum n_f, dk]
+ *   bank       [B, H, bank_rows, d]  advanced in place (rows >= N untouched)
+ *   out        [B, T, H, d]
+ *   widx/ridx  [B, T, H, W|R] int32 and wsc/rsc float32 slot scores: optional (NULL to skip)
+ * Streams (b, h) are independent and are spread over nthreads threads. Returns 0 or -1. */
+int oracle_write_read(int B, int T, int H, int F, const int* widths, int dk, int d, int W, int R, int bank_bf16,
+                      int act_bf16, const float* wkeys, const float* rq, const float* values, const float* alpha,
+                      const float* beta, const float* subkeys, float* bank, int64_t bank_rows, float* out,
+                      int32_t* widx, int32_t* ridx, float* wsc, float* rsc, int nthreads) {
+  int64_t sumn = 0, N = 1;
+  for (int f = 0; f < F; ++f) { sumn += widths[f]; N *= widths[f]; }
+  if (F < 1 || F > ORACLE_MAX_F || W < 1 || R < 1 || W > N || R > N || bank_rows < N) return -1;
+  int streams = B * H;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > streams) nthreads = streams > 0 ? streams : 1;
+  if (nthreads > 256) nthreads = 256;
+  pthread_t th[256];
+  int started[256];
+  wr_job_t jobs[256];
+  int err = 0;
+  for (int i = 0; i < nthreads; ++i) {
+    wr_job_t* j = &jobs[i];
+    j->B = B; j->T = T; j->H = H; j->F = F; j->dk = dk; j->d = d; j->W = W; j->R = R;
+    j->bank_bf16 = bank_bf16; j->act_bf16 = act_bf16; j->widths = widths; j->wkeys = wkeys; j->rq = rq;
+    j->values = values; j->alpha = alpha; j->beta = beta; j->sub = subkeys; j->bank = bank;
+    j->bank_rows = bank_rows; j->out = out; j->widx = widx; j->ridx = ridx; j->wsc = wsc; j->rsc = rsc;
+    j->sumn = sumn; j->err = 0;
+    j->s_begin = (int)((int64_t)streams * i / nthreads);
+    j->s_end = (int)((int64_t)streams * (i + 1) / nthreads);
+    started[i] = pthread_create(&th[i], NULL, wr_worker, j) == 0;
+    if (!started[i]) wr_worker(j);
+  }
+  for (int i = 0; i < nthreads; ++i) { if (started[i]) pthread_join(th[i], NULL); err |= jobs[i].err; }
+  return err ? -1 : 0;
+}

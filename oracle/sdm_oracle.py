@@ -1,0 +1,165 @@
+"""ctypes wrapper around the C oracle (``sdm_oracle.c``). Test infrastructure only.
+
+All tensors cross the boundary as contiguous float32 numpy arrays whose values are already rounded to their dtype
+(bfloat16 values are exact in float32); the oracle rounds written bank rows and outputs to the requested dtypes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sdm_oracle.c")
+_LIB = os.path.join(_HERE, "libsdm_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+_f32p = np.ctypeslib.ndpointer(dtype=np.float32, flags="C_CONTIGUOUS")
+_f64p = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
+_i32p = np.ctypeslib.ndpointer(dtype=np.int32, flags="C_CONTIGUOUS")
+
+
+def lib_path() -> str:
+    return _LIB
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (IEEE arithmetic: no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fPIC", "-shared", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-pthread",
+               "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB):
+                build(force=False)
+            lib = ctypes.CDLL(_LIB)
+            lib.oracle_round_bf16.restype = ctypes.c_double
+            lib.oracle_round_bf16.argtypes = [ctypes.c_double]
+            lib.oracle_factor_scores.restype = None
+            lib.oracle_factor_scores.argtypes = [ctypes.c_int, ctypes.c_int, _f32p, _f32p, _f32p]
+            lib.oracle_softmax.restype = None
+            lib.oracle_softmax.argtypes = [ctypes.c_int, _f32p, _f64p]
+            lib.oracle_topk_one.restype = ctypes.c_int
+            lib.oracle_topk_one.argtypes = [ctypes.c_int, _i32p, ctypes.c_int, _f32p, _f32p, ctypes.c_int, _i32p,
+                                            _f32p]
+            lib.oracle_topk.restype = ctypes.c_int
+            lib.oracle_topk.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, ctypes.c_int,
+                                        _f32p, _f32p, ctypes.c_int, _i32p, _f32p, ctypes.c_int]
+            vp = ctypes.c_void_p
+            lib.oracle_write_read.restype = ctypes.c_int
+            lib.oracle_write_read.argtypes = [
+                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, ctypes.c_int, ctypes.c_int,
+                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, ctypes.c_int64, _f32p,
+                vp, vp, vp, vp, ctypes.c_int]
+            _lib = lib
+    return _lib
+
+
+def _f32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+
+
+def round_bf16(x: float) -> float:
+    """Nearest bfloat16 (ties to even) of an fp64 value."""
+    return float(_load().oracle_round_bf16(float(x)))
+
+
+def factor_scores(q, C) -> np.ndarray:
+    """float32 rounding of the fp64 FMA chain <q, C[i]> for every row i of C. q: [dk], C: [n, dk]."""
+    q = _f32(q)
+    C = _f32(C)
+    n, dk = C.shape
+    assert q.shape == (dk,)
+    s = np.empty(n, dtype=np.float32)
+    _load().oracle_factor_scores(n, dk, q, C, s)
+    return s
+
+
+def softmax(scores) -> np.ndarray:
+    s = _f32(scores)
+    w = np.empty(s.shape[0], dtype=np.float64)
+    _load().oracle_softmax(s.shape[0], s, w)
+    return w
+
+
+def topk_one(q, subkeys, widths, k):
+    """Exact product-key top-k of one query q [F*dk] against one head's stacked sub-key tables [sum n_f, dk]."""
+    widths = np.ascontiguousarray(np.asarray(widths, dtype=np.int32))
+    q = _f32(q)
+    sub = _f32(subkeys)
+    dk = sub.shape[1]
+    ids = np.empty(k, dtype=np.int32)
+    sc = np.empty(k, dtype=np.float32)
+    rc = _load().oracle_topk_one(len(widths), widths, dk, q, sub, k, ids, sc)
+    if rc != 0:
+        raise ValueError("oracle_topk_one rejected its arguments")
+    return ids, sc
+
+
+def topk(queries, subkeys, widths, k, nthreads: int | None = None):
+    """queries [B, T, H, F*dk], subkeys [H, sum n_f, dk] -> ids int32 [B, T, H, k], scores float32 [B, T, H, k]."""
+    q = _f32(queries)
+    sub = _f32(subkeys)
+    B, T, H, _ = q.shape
+    widths = np.ascontiguousarray(np.asarray(widths, dtype=np.int32))
+    dk = sub.shape[2]
+    ids = np.empty((B, T, H, k), dtype=np.int32)
+    sc = np.empty((B, T, H, k), dtype=np.float32)
+    nt = nthreads or min(os.cpu_count() or 1, 16)
+    rc = _load().oracle_topk(B, T, H, len(widths), widths, dk, q, sub, k, ids, sc, nt)
+    if rc != 0:
+        raise ValueError("oracle_topk rejected its arguments")
+    return ids, sc
+
+
+def write_read(wkeys, rq, values, alpha, beta, subkeys, bank, widths, num_writes, num_reads, *, bank_bf16=False,
+               act_bf16=False, nthreads: int | None = None, want_index=True):
+    """Sequential per-token SDM write/read over every stream (b, h).
+
+    Arguments (float32 arrays, values already in their dtype): wkeys/rq [B, T, H, F*dk], values [B, T, H, d],
+    alpha/beta [B, T, H], subkeys [H, sum n_f, dk], bank [B, H, bank_rows, d] (not modified: a copy advances).
+    Returns dict(out [B,T,H,d] float32, bank [B,H,bank_rows,d] float32, widx, ridx, wscore, rscore).
+    """
+    wk = _f32(wkeys)
+    rqa = _f32(rq)
+    v = _f32(values)
+    al = _f32(alpha)
+    be = _f32(beta)
+    sub = _f32(subkeys)
+    M = np.array(bank, dtype=np.float32, copy=True, order="C")
+    B, T, H, Fdk = wk.shape
+    d = v.shape[-1]
+    widths = np.ascontiguousarray(np.asarray(widths, dtype=np.int32))
+    dk = sub.shape[2]
+    W, R = int(num_writes), int(num_reads)
+    out = np.empty((B, T, H, d), dtype=np.float32)
+    res = {"out": out, "bank": M}
+    ptrs = []
+    for name, k in (("widx", W), ("ridx", R)):
+        arr = np.empty((B, T, H, k), dtype=np.int32) if want_index else None
+        res[name] = arr
+        ptrs.append(arr.ctypes.data if arr is not None else None)
+    for name, k in (("wscore", W), ("rscore", R)):
+        arr = np.empty((B, T, H, k), dtype=np.float32) if want_index else None
+        res[name] = arr
+        ptrs.append(arr.ctypes.data if arr is not None else None)
+    nt = nthreads or min(os.cpu_count() or 1, 16)
+    rc = _load().oracle_write_read(B, T, H, len(widths), widths, dk, d, W, R, int(bool(bank_bf16)),
+                                   int(bool(act_bf16)), wk, rqa, v, al, be, sub, M, M.shape[2], out,
+                                   ptrs[0], ptrs[1], ptrs[2], ptrs[3], nt)
+    if rc != 0:
+        raise ValueError("oracle_write_read rejected its arguments")
+    return res
