@@ -1,0 +1,260 @@
+#!/usr/bin/env python
+"""SDM benchmark on one MI355X: write/read tokens/s on the 65,536-slot layer workload, decode steps/s at B = 128,
+the chunk-loop kernel against the HBM roofline, and the CPU oracle timed beside it.
+
+One step = one sdm_write_read call over the whole batch of the layer workload (B 2 x T 4096 tokens, 2 heads of
+1024, 2 factors of 256 sub-keys = 65,536 slots per head, W = R = 64, chunk 64, bf16 activations on a float32 bank),
+inputs resident in HBM before the timed region; the bank advances in place from step to step.
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SDM write/read tokens/s (65536 slots, W=R=64) + decode steps/s at B=128; % HBM roofline"
+HBM_PEAK_GBS = 8000.0
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "loop_kernel_layer_65k_pmc.txt")
+LOOP_SOURCES = ("gated_delta_rule_product_amd/csrc/loop.hip", "gated_delta_rule_product_amd/csrc/sdm_internal.h")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def loop_sources_sha() -> str:
+    h = hashlib.sha256()
+    for p in LOOP_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_from_counters():
+    """HBM bytes per chunk-loop launch from the committed rocprofv3 counter summary, if it was taken on the
+    current loop-kernel sources (else None)."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    vals = {}
+    with open(PMC_SUMMARY) as f:
+        for ln in f:
+            if ":" in ln and not ln.startswith("#"):
+                k, v = ln.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_sources_sha256") != loop_sources_sha():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def loop_algorithmic_bytes(s, token_heads):
+    """Bytes the chunk loop must move per launch: per token-head, W bank rows read and written and R bank rows read
+    ((2W + R) d bank elements), the value row read and the output row written (2 d act elements), 2 gates."""
+    sb = 2 if s.bank == "bf16" else 4
+    sa = 2 if s.act == "bf16" else 4
+    return token_heads * ((2 * s.num_writes + s.num_reads) * s.head_dim * sb + 2 * s.head_dim * sa + 2 * sa)
+
+
+def bench_write_read(args, torch, binding, synth):
+    s = synth.WORKLOADS["layer_65k"]
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16}
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating {s.name} inputs")
+    x = synth.make_inputs(s)
+    t = {k: torch.from_numpy(x[k]).to(dev).to(dt[s.act]) for k in ("wkeys", "rq", "values", "alpha", "beta",
+                                                                    "subkeys")}
+    bank = torch.from_numpy(x["bank"]).to(dev).to(dt[s.bank])
+    del x
+    cfg = binding.make_config(s.batch, s.tokens, s.heads, s.widths, s.subkey_dim, s.head_dim, s.num_writes,
+                              s.num_reads, s.chunk_size, binding.SDM_BF16 if s.act == "bf16" else binding.SDM_F32,
+                              binding.SDM_BF16 if s.bank == "bf16" else binding.SDM_F32, s.rows)
+    ws = torch.empty(binding.workspace_size(cfg, binding.SDM_OP_WRITE_READ), dtype=torch.uint8, device=dev)
+    out = torch.empty((s.batch, s.tokens, s.heads, s.head_dim), dtype=dt[s.act], device=dev)
+
+    def step():
+        binding.sdm_write_read(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"], t["subkeys"], bank,
+                               widths=s.widths, num_writes=s.num_writes, num_reads=s.num_reads,
+                               chunk_size=s.chunk_size, out=out, workspace=ws)
+
+    log(f"[bench] write/read warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] write/read timed {args.steps}")
+    binding.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    prof = binding.profile_read()
+    binding.profile_enable(False)
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    tokens = s.batch * s.tokens
+    kernels = {k: round(v[0] / v[1], 4) for k, v in prof.items() if v[1]}
+    loop_ms = prof["loop"][0] / prof["loop"][1]
+    alg = loop_algorithmic_bytes(s, s.batch * s.tokens * s.heads)
+    achieved = alg / (loop_ms * 1e-3) / 1e9
+    traffic = traffic_from_counters()
+    roof = {"kernel": "loop_kernel (chunk loop: gather, solve, read, scatter)", "bound": "hbm",
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "algorithmic_bytes_per_launch": alg, "avg_launch_ms": round(loop_ms, 4)}
+    step_bytes = alg  # the loop's bank traffic dominates the call's bytes
+    return {
+        "tokens_per_s": tokens / (ms_step * 1e-3), "ms_per_step": ms_step, "kernels_avg_ms": kernels,
+        "roofline": roof, "whole_call_hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "shape": s,
+    }
+
+
+def bench_decode(args, torch, binding, synth):
+    s = synth.WORKLOADS["decode_b128"]
+    dev = torch.device("cuda:0")
+    nsteps = args.decode_warmup + args.decode_steps
+    log(f"[bench] decode {s.name}: {nsteps} steps of inputs")
+    steps = []
+    for i in range(nsteps):
+        x = synth.make_step_inputs(s, step=i)
+        steps.append({k: torch.from_numpy(v).to(dev) for k, v in x.items()})
+    sub = torch.from_numpy(synth.make_subkeys(s)).to(dev)
+    bank0 = torch.from_numpy(synth.make_bank(s)).to(dev)
+    cfg = binding.make_config(s.batch, 1, s.heads, s.widths, s.subkey_dim, s.head_dim, s.num_writes, s.num_reads, 1,
+                              binding.SDM_F32, binding.SDM_F32, s.rows)
+    ws = torch.empty(binding.workspace_size(cfg, binding.SDM_OP_DECODE), dtype=torch.uint8, device=dev)
+    kw = dict(widths=s.widths, num_writes=s.num_writes, num_reads=s.num_reads, workspace=ws)
+    res = {}
+    outs = {}
+    for mode in ("donated", "copied"):
+        banks = [bank0.clone(), torch.empty_like(bank0)]
+        out = torch.empty((s.batch, 1, s.heads, s.head_dim), dtype=torch.float32, device=dev)
+        cur = 0
+
+        def one(i):
+            nonlocal cur
+            a = steps[i]
+            if mode == "donated":
+                binding.sdm_decode_step(a["wkeys"], a["rq"], a["values"], a["alpha"], a["beta"], sub, banks[0],
+                                        out=out, **kw)
+            else:
+                binding.sdm_decode_step(a["wkeys"], a["rq"], a["values"], a["alpha"], a["beta"], sub, banks[cur],
+                                        banks[1 - cur], out=out, **kw)
+                cur = 1 - cur
+
+        for i in range(args.decode_warmup):
+            one(i)
+        torch.cuda.synchronize()
+        binding.profile_enable(True)
+        t0 = time.perf_counter()
+        for i in range(args.decode_warmup, nsteps):
+            one(i)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        prof = binding.profile_read()
+        binding.profile_enable(False)
+        ms = (t1 - t0) * 1e3 / args.decode_steps
+        res[mode] = {"steps_per_s": round(1e3 / ms, 1), "ms_per_step": round(ms, 4),
+                     "kernels_avg_ms": {k: round(v[0] / v[1], 4) for k, v in prof.items() if v[1]}}
+        outs[mode] = (out.clone(), banks[0] if mode == "donated" else banks[cur])
+    equal = bool(torch.equal(outs["donated"][0], outs["copied"][0]) and torch.equal(outs["donated"][1],
+                                                                                    outs["copied"][1]))
+    sb = 4
+    per_step = s.batch * s.heads * ((2 * s.num_writes + s.num_reads) * s.head_dim * sb + 2 * s.head_dim * 4 + 8)
+    dms = res["donated"]["kernels_avg_ms"].get("decode")
+    return {
+        "workload": "decode_b128: B128 streams x 1 token, H2 d256 N1024 (2x32) W=R=64, fp32 bank",
+        "steps_per_s": res["donated"]["steps_per_s"], "steps_per_s_copied": res["copied"]["steps_per_s"],
+        "donated": res["donated"], "copied": res["copied"], "donated_equals_copied_bitwise": equal,
+        "warmup": args.decode_warmup, "steps": args.decode_steps,
+        "decode_kernel_hbm_frac": round(per_step / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if dms else None,
+    }
+
+
+def cpu_baseline(args, s, synth):
+    import numpy as np
+
+    import oracle
+
+    ncpu = os.cpu_count() or 1
+    threads = min(s.batch * s.heads, ncpu, 16)
+    T = args.cpu_tokens or s.tokens
+    ss = s.with_(tokens=T)
+    log(f"[bench] cpu baseline: oracle on {ss.name} B{ss.batch} T{T} H{ss.heads}, {threads} threads")
+    x = synth.make_inputs(ss)
+    t0 = time.perf_counter()
+    oracle.write_read(x["wkeys"], x["rq"], x["values"], x["alpha"], x["beta"], x["subkeys"], x["bank"], ss.widths,
+                      ss.num_writes, ss.num_reads, bank_bf16=ss.bank == "bf16", act_bf16=ss.act == "bf16",
+                      nthreads=threads, want_index=False)
+    dt = time.perf_counter() - t0
+    model = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    del np
+    return {"value": round(ss.batch * T / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"the full {ss.name} workload (B{ss.batch} x T{T} tokens, H{ss.heads}) in {dt:.1f} s; "
+                      f"sequential per-token fp64 oracle, one thread per stream; host CPU {model}, {ncpu} "
+                      f"logical CPUs visible"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=64)
+    ap.add_argument("--decode-warmup", type=int, default=8)
+    ap.add_argument("--cpu-tokens", type=int, default=0, help="tokens of the oracle sample (0: the whole workload)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only: the SDM hot path here is built and measured on a single MI355X "
+              f"(requested --gpus {args.gpus}, WORLD_SIZE {world}); streams shard across GPUs with no exchange, "
+              f"so the multi-GPU rate is N times the one-GPU rate by construction and is not measured.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from gated_delta_rule_product_amd import binding, synth
+
+    binding.load()
+    wr = bench_write_read(args, torch, binding, synth)
+    dec = bench_decode(args, torch, binding, synth)
+    s = wr["shape"]
+    line = {
+        "metric": METRIC, "value": round(wr["tokens_per_s"], 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wr["ms_per_step"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded Philox: queries, keys, sub-keys, values ~ N(0,1); gates sigmoid(N(0,1)); "
+                "bank ~ N(0, 0.02^2))",
+        "config": {"workload": "layer_65k: B2 T4096 H2 d1024, 2 factors x 256 sub-keys (65536 slots/head), dk 64, "
+                               "W=R=64, chunk 64, bf16 activations, f32 bank",
+                   "global_batch": s.batch, "seq_len": s.tokens, "heads": s.heads, "head_dim": s.head_dim,
+                   "slots_per_head": s.slots, "num_writes": s.num_writes, "num_reads": s.num_reads,
+                   "chunk_size": s.chunk_size, "act_dtype": s.act, "bank_dtype": s.bank, "parallelism": "none (1 GPU)"},
+        "kernels_avg_ms": wr["kernels_avg_ms"],
+        "roofline": wr["roofline"],
+        "decode": dec,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args, s, synth)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,248 @@
+"""Thin ctypes binding of libsdm.so (include/sdm.h): argument marshalling only.
+
+Every step of the write/read, the top-k and the decode step runs in the library's HIP kernels. Torch supplies
+device memory (outputs and the workspace) and the current stream. If the library is missing the binding raises; it
+never falls back to another implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsdm.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "sdm.h")
+
+SDM_OK, SDM_ERR_DTYPE, SDM_ERR_RANGE, SDM_ERR_BANK_TOO_SMALL, SDM_ERR_ALIAS = 0, 1, 2, 3, 4
+SDM_ERR_LAYOUT, SDM_ERR_WORKSPACE, SDM_ERR_DEVICE, SDM_ERR_HIP, SDM_ERR_NULL = 5, 6, 7, 8, 9
+STATUS_NAMES = {0: "SDM_OK", 1: "SDM_ERR_DTYPE", 2: "SDM_ERR_RANGE", 3: "SDM_ERR_BANK_TOO_SMALL", 4: "SDM_ERR_ALIAS",
+                5: "SDM_ERR_LAYOUT", 6: "SDM_ERR_WORKSPACE", 7: "SDM_ERR_DEVICE", 8: "SDM_ERR_HIP", 9: "SDM_ERR_NULL"}
+SDM_F32, SDM_BF16, SDM_F16 = 0, 1, 2
+SDM_OP_TOPK, SDM_OP_WRITE_READ, SDM_OP_DECODE = 0, 1, 2
+
+
+class UnsupportedConfigurationError(ValueError):
+    """Raised when the library refuses a call before doing any work."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class SdmConfig(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("tokens", ctypes.c_int32), ("heads", ctypes.c_int32),
+        ("num_factors", ctypes.c_int32), ("factor_widths", ctypes.c_int32 * 4), ("subkey_dim", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("num_writes", ctypes.c_int32), ("num_reads", ctypes.c_int32),
+        ("chunk_size", ctypes.c_int32), ("act_dtype", ctypes.c_int32), ("bank_dtype", ctypes.c_int32),
+        ("bank_rows", ctypes.c_int64),
+    ]
+
+
+def make_config(batch, tokens, heads, widths, subkey_dim, head_dim=1, num_writes=1, num_reads=1, chunk_size=1,
+                act_dtype=SDM_F32, bank_dtype=SDM_F32, bank_rows=None) -> SdmConfig:
+    c = SdmConfig()
+    c.batch, c.tokens, c.heads = int(batch), int(tokens), int(heads)
+    c.num_factors = len(widths)
+    for i in range(4):
+        c.factor_widths[i] = int(widths[i]) if i < len(widths) else 0
+    c.subkey_dim, c.head_dim = int(subkey_dim), int(head_dim)
+    c.num_writes, c.num_reads, c.chunk_size = int(num_writes), int(num_reads), int(chunk_size)
+    c.act_dtype, c.bank_dtype = int(act_dtype), int(bank_dtype)
+    n = 1
+    for w in widths:
+        n *= int(w)
+    c.bank_rows = int(bank_rows) if bank_rows is not None else n
+    return c
+
+
+_lib = None
+_lock = threading.Lock()
+_vp = ctypes.c_void_p
+
+
+def load():
+    """Load libsdm.so (raises if it is not built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() (no fallback exists)")
+            lib = ctypes.CDLL(LIB_PATH)
+            cfgp = ctypes.POINTER(SdmConfig)
+            lib.sdm_last_error.restype = ctypes.c_char_p
+            lib.sdm_last_error.argtypes = []
+            lib.sdm_workspace_size.restype = ctypes.c_int
+            lib.sdm_workspace_size.argtypes = [cfgp, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+            lib.topk_product_keys.restype = ctypes.c_int
+            lib.topk_product_keys.argtypes = [cfgp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+            lib.sdm_write_read.restype = ctypes.c_int
+            lib.sdm_write_read.argtypes = [cfgp] + [_vp] * 11 + [ctypes.c_size_t, _vp]
+            lib.sdm_decode_step.restype = ctypes.c_int
+            lib.sdm_decode_step.argtypes = [cfgp] + [_vp] * 12 + [ctypes.c_size_t, _vp]
+            lib.sdm_profile_enable.restype = ctypes.c_int
+            lib.sdm_profile_enable.argtypes = [ctypes.c_int32]
+            lib.sdm_profile_read.restype = ctypes.c_int
+            lib.sdm_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+            _lib = lib
+    return _lib
+
+
+def declared_functions() -> list:
+    """Names of the functions include/sdm.h declares."""
+    src = open(HEADER_PATH).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return re.findall(r"^[A-Za-z_][\w \*]*?\b(\w+)\s*\(", src, flags=re.M)
+
+
+def last_error() -> str:
+    return load().sdm_last_error().decode()
+
+
+def _check(status: int):
+    if status != SDM_OK:
+        msg = last_error()
+        raise UnsupportedConfigurationError(status, msg)
+
+
+def workspace_size(cfg: SdmConfig, op: int, k: int = 0) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().sdm_workspace_size(ctypes.byref(cfg), op, k, ctypes.byref(n)))
+    return n.value
+
+
+KERNELS = ("cand", "topk", "plan", "loop", "decode", "copy")
+
+
+def profile_enable(on: bool = True):
+    """Start (and reset) or stop HIP-event timing of the library's kernel launches."""
+    _check(load().sdm_profile_enable(1 if on else 0))
+
+
+def profile_read() -> dict:
+    """{kernel: (total ms, launches)} since timing was enabled (waits for the recorded events)."""
+    ms = (ctypes.c_double * len(KERNELS))()
+    n = (ctypes.c_int64 * len(KERNELS))()
+    _check(load().sdm_profile_read(ms, n))
+    return {k: (ms[i], n[i]) for i, k in enumerate(KERNELS)}
+
+
+_DT = {torch.float32: SDM_F32, torch.bfloat16: SDM_BF16, torch.float16: SDM_F16}
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise UnsupportedConfigurationError(SDM_ERR_DTYPE, f"unsupported dtype {t.dtype}")
+    return _DT[t.dtype]
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, shape=None, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _workspace(nbytes: int, device, workspace=None):
+    if nbytes == 0:
+        return None
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError(f"workspace too small: {nbytes} bytes needed")
+        return workspace
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def topk_product_keys(queries: torch.Tensor, subkeys: torch.Tensor, widths, k: int, want_scores=True,
+                      workspace=None):
+    """queries [B, T, H, F*dk], subkeys [H, sum n_f, dk] (same dtype) -> (ids int32 [B,T,H,k], scores f32 or None)."""
+    B, T, H, Fdk = queries.shape
+    F = len(widths)
+    dk = Fdk // F
+    _need(queries, "queries")
+    _need(subkeys, "subkeys", (H, sum(widths), dk), queries.dtype)
+    cfg = make_config(B, T, H, widths, dk, act_dtype=_dt(queries))
+    ws = _workspace(workspace_size(cfg, SDM_OP_TOPK, k), queries.device, workspace)
+    ids = torch.empty((B, T, H, k), dtype=torch.int32, device=queries.device)
+    scores = torch.empty((B, T, H, k), dtype=torch.float32, device=queries.device) if want_scores else None
+    _check(load().topk_product_keys(ctypes.byref(cfg), _ptr(queries), _ptr(subkeys), k, _ptr(ids), _ptr(scores),
+                                    _ptr(ws), 0 if ws is None else ws.numel(), _stream(queries.device)))
+    return ids, scores
+
+
+def sdm_write_read(write_keys, read_queries, values, forget_gate, input_gate, subkeys, bank, *, widths, num_writes,
+                   num_reads, chunk_size, want_index=False, out=None, workspace=None):
+    """Chunked SDM write/read. bank [B, H, bank_rows, d] advances in place. Returns (out, write_idx, read_idx)."""
+    B, T, H, Fdk = write_keys.shape
+    F = len(widths)
+    dk = Fdk // F
+    d = values.shape[-1]
+    act = write_keys.dtype
+    for name, t, shp in (("write_keys", write_keys, (B, T, H, Fdk)), ("read_queries", read_queries, (B, T, H, Fdk)),
+                         ("values", values, (B, T, H, d)), ("forget_gate", forget_gate, (B, T, H)),
+                         ("input_gate", input_gate, (B, T, H)), ("subkeys", subkeys, (H, sum(widths), dk))):
+        _need(t, name, shp, act)
+    _need(bank, "bank")
+    if bank.dim() != 4 or bank.shape[0] != B or bank.shape[1] != H or bank.shape[3] != d:
+        raise ValueError(f"bank has shape {tuple(bank.shape)}, expected ({B}, {H}, bank_rows, {d})")
+    cfg = make_config(B, T, H, widths, dk, d, num_writes, num_reads, chunk_size, _dt(write_keys), _dt(bank),
+                      bank.shape[2])
+    ws = _workspace(workspace_size(cfg, SDM_OP_WRITE_READ), bank.device, workspace)
+    if out is None:
+        out = torch.empty((B, T, H, d), dtype=act, device=bank.device)
+    else:
+        _need(out, "out", (B, T, H, d), act)
+    widx = torch.empty((B, T, H, num_writes), dtype=torch.int32, device=bank.device) if want_index else None
+    ridx = torch.empty((B, T, H, num_reads), dtype=torch.int32, device=bank.device) if want_index else None
+    _check(load().sdm_write_read(ctypes.byref(cfg), _ptr(write_keys), _ptr(read_queries), _ptr(values),
+                                 _ptr(forget_gate), _ptr(input_gate), _ptr(subkeys), _ptr(bank), _ptr(out),
+                                 _ptr(widx), _ptr(ridx), _ptr(ws), 0 if ws is None else ws.numel(),
+                                 _stream(bank.device)))
+    return out, widx, ridx
+
+
+def sdm_decode_step(write_keys, read_queries, values, forget_gate, input_gate, subkeys, bank_in, bank_out=None, *,
+                    widths, num_writes, num_reads, want_index=False, out=None, workspace=None):
+    """One decode step. bank_out None or bank_in: donated (in place); else a disjoint successor buffer.
+    Inputs [B, 1, H, ...]. Returns (out, write_idx, read_idx, bank_out)."""
+    if bank_out is None:
+        bank_out = bank_in
+    B, T, H, Fdk = write_keys.shape
+    F = len(widths)
+    dk = Fdk // F
+    d = values.shape[-1]
+    act = write_keys.dtype
+    for name, t, shp in (("write_keys", write_keys, (B, T, H, Fdk)), ("read_queries", read_queries, (B, T, H, Fdk)),
+                         ("values", values, (B, T, H, d)), ("forget_gate", forget_gate, (B, T, H)),
+                         ("input_gate", input_gate, (B, T, H)), ("subkeys", subkeys, (H, sum(widths), dk))):
+        _need(t, name, shp, act)
+    _need(bank_in, "bank_in")
+    _need(bank_out, "bank_out", tuple(bank_in.shape), bank_in.dtype)
+    cfg = make_config(B, T, H, widths, dk, d, num_writes, num_reads, 1, _dt(write_keys), _dt(bank_in),
+                      bank_in.shape[2])
+    ws = _workspace(workspace_size(cfg, SDM_OP_DECODE), bank_in.device, workspace)
+    if out is None:
+        out = torch.empty((B, T, H, d), dtype=act, device=bank_in.device)
+    widx = torch.empty((B, T, H, num_writes), dtype=torch.int32, device=bank_in.device) if want_index else None
+    ridx = torch.empty((B, T, H, num_reads), dtype=torch.int32, device=bank_in.device) if want_index else None
+    _check(load().sdm_decode_step(ctypes.byref(cfg), _ptr(write_keys), _ptr(read_queries), _ptr(values),
+                                  _ptr(forget_gate), _ptr(input_gate), _ptr(subkeys), _ptr(bank_in), _ptr(bank_out),
+                                  _ptr(out), _ptr(widx), _ptr(ridx), _ptr(ws), 0 if ws is None else ws.numel(),
+                                  _stream(bank_in.device)))
+    return out, widx, ridx, bank_out

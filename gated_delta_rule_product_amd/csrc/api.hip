@@ -1,0 +1,574 @@
+// The C ABI (include/sdm.h): argument checks, refusals, workspace layout and kernel launches.
+//
+// Refusal policy (sparse-delta-memory CHANGELOG.md 2.0.0, "Behavior changes" and "Known limitations"): float16
+// raises; out-of-range settings (for example more writes or reads than slots) raise instead of being capped; a bank
+// with fewer rows than slots raises instead of being read out of bounds; head_dim above 2^20 raises; there is no
+// fallback path (only gfx950 runs); every refusal happens before any device work; the device check runs once per
+// device (memoized), the argument checks on every call.
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "sdm_internal.h"
+
+using namespace sdm;
+
+namespace {
+
+thread_local std::string g_err;
+
+sdm_status fail(sdm_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+sdm_status fail(sdm_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+sdm_status ok() {
+  g_err.clear();
+  return SDM_OK;
+}
+
+size_t esize(int dt) { return dt == SDM_BF16 ? 2 : 4; }
+
+// Number of position tuples with p_f < kp[f] and prod(p_f + 1) <= k (same enumeration as cand_table_kernel).
+long long count_candidates(const int* kp, int F, int k) {
+  int p[MAX_F] = {0, 0, 0, 0};
+  long long c = 0;
+  while (true) {
+    long long prod = 1;
+    for (int f = 0; f < F; ++f) prod *= p[f] + 1;
+    if (prod <= k) ++c;
+    int f = F - 1;
+    for (; f >= 0; --f) {
+      ++p[f];
+      long long pp = 1;
+      for (int g = 0; g <= f; ++g) pp *= p[g] + 1;
+      if (p[f] < kp[f] && pp <= k) break;
+      p[f] = 0;
+    }
+    if (f < 0) break;
+  }
+  return c;
+}
+
+sdm_status make_plan(const Dims& D, int k, const char* what, TopkPlan* P) {
+  if (k < 1 || (long long)k > D.N || k > MAX_K)
+    return fail(SDM_ERR_RANGE, "%s = %d out of range [1, min(N = %lld, %d)]", what, k, D.N, MAX_K);
+  P->k = k;
+  P->kpmax = 0;
+  int nfmax = 0;
+  for (int f = 0; f < MAX_F; ++f) P->kp[f] = 0;
+  for (int f = 0; f < D.F; ++f) {
+    P->kp[f] = k < D.widths[f] ? k : D.widths[f];
+    if (P->kp[f] > P->kpmax) P->kpmax = P->kp[f];
+    if (D.widths[f] > nfmax) nfmax = D.widths[f];
+  }
+  const long long nc = count_candidates(P->kp, D.F, k);
+  if (nc > MAX_CAND)
+    return fail(SDM_ERR_RANGE, "%s = %d with these factor widths gives %lld candidate tuples (limit %d)", what, k,
+                nc, MAX_CAND);
+  P->ncand = (int)nc;
+  P->cand_pow2 = pow2_ceil((int)nc);
+  P->nf_pow2 = pow2_ceil(nfmax);
+  return SDM_OK;
+}
+
+// op: SDM_OP_TOPK (k given), SDM_OP_WRITE_READ, SDM_OP_DECODE
+sdm_status validate(const sdm_config* cfg, int op, int k, Dims* D, TopkPlan* pw, TopkPlan* pr) {
+  if (!cfg) return fail(SDM_ERR_NULL, "cfg is NULL");
+  if (op < SDM_OP_TOPK || op > SDM_OP_DECODE) return fail(SDM_ERR_RANGE, "unknown op %d", op);
+  const int act = cfg->act_dtype, bank = cfg->bank_dtype;
+  if (act == SDM_F16 || (op != SDM_OP_TOPK && bank == SDM_F16))
+    return fail(SDM_ERR_DTYPE, "float16 is not supported (use float32 or bfloat16)");
+  if (act != SDM_F32 && act != SDM_BF16) return fail(SDM_ERR_DTYPE, "unknown act_dtype %d", act);
+  if (op != SDM_OP_TOPK && bank != SDM_F32 && bank != SDM_BF16) return fail(SDM_ERR_DTYPE, "unknown bank_dtype %d", bank);
+  if (cfg->batch < 0 || cfg->tokens < 0 || cfg->heads < 0)
+    return fail(SDM_ERR_RANGE, "batch, tokens and heads must be >= 0");
+  if (op == SDM_OP_DECODE && cfg->tokens != 1)
+    return fail(SDM_ERR_RANGE, "sdm_decode_step takes exactly one token per stream (tokens = %d)", cfg->tokens);
+  if ((long long)cfg->batch * cfg->heads > 65535 && op == SDM_OP_WRITE_READ)
+    return fail(SDM_ERR_RANGE, "batch * heads = %lld exceeds 65535 streams", (long long)cfg->batch * cfg->heads);
+  if ((long long)cfg->batch * cfg->heads > 0x7FFFFFFFLL)
+    return fail(SDM_ERR_RANGE, "batch * heads exceeds 2^31 - 1");
+  if ((long long)cfg->batch * cfg->tokens * cfg->heads > (1LL << 24))
+    return fail(SDM_ERR_RANGE, "batch * tokens * heads exceeds 2^24 token rows per call");
+  const int F = cfg->num_factors;
+  if (F < 1 || F > MAX_F) return fail(SDM_ERR_RANGE, "num_factors = %d out of range [1, %d]", F, MAX_F);
+  memset(D, 0, sizeof *D);
+  long long N = 1;
+  for (int f = 0; f < F; ++f) {
+    const int n = cfg->factor_widths[f];
+    if (n < 1 || n > MAX_NF) return fail(SDM_ERR_RANGE, "factor_widths[%d] = %d out of range [1, %d]", f, n, MAX_NF);
+    D->widths[f] = n;
+    N *= n;
+    if (N > 0x7FFFFFFFLL) return fail(SDM_ERR_RANGE, "slot count (product of factor widths) exceeds 2^31 - 1");
+  }
+  if (cfg->subkey_dim < 1 || (long long)F * cfg->subkey_dim > MAX_FDK)
+    return fail(SDM_ERR_RANGE, "subkey_dim = %d out of range (num_factors * subkey_dim must be in [1, %d])",
+                cfg->subkey_dim, MAX_FDK);
+  D->B = cfg->batch; D->T = cfg->tokens; D->H = cfg->heads; D->F = F; D->dk = cfg->subkey_dim;
+  D->act = act; D->bank = bank; D->N = N; D->S = cfg->batch * cfg->heads;
+  if (op == SDM_OP_TOPK) return make_plan(*D, k, "k", pw);
+
+  const int d = cfg->head_dim;
+  if (d < 1 || d > (1 << 20)) return fail(SDM_ERR_RANGE, "head_dim = %d out of range [1, 2^20]", d);
+  const int lane = bank == SDM_BF16 ? 8 : 4;
+  if (d % lane) return fail(SDM_ERR_LAYOUT, "head_dim = %d must be a multiple of %d for this bank dtype", d, lane);
+  D->d = d;
+  D->W = cfg->num_writes; D->R = cfg->num_reads;
+  sdm_status s = make_plan(*D, D->W, "num_writes", pw);
+  if (s != SDM_OK) return s;
+  s = make_plan(*D, D->R, "num_reads", pr);
+  if (s != SDM_OK) return s;
+  if (cfg->bank_rows < N)
+    return fail(SDM_ERR_BANK_TOO_SMALL, "bank_rows = %lld is smaller than the slot count N = %lld",
+                (long long)cfg->bank_rows, N);
+  D->rows = cfg->bank_rows;
+  if (op == SDM_OP_WRITE_READ) {
+    const int C = cfg->chunk_size;
+    if (C < 1 || C > MAX_CHUNK) return fail(SDM_ERR_RANGE, "chunk_size = %d out of range [1, %d]", C, MAX_CHUNK);
+    if ((long long)C * D->W > MAX_CHUNK_EVENTS)
+      return fail(SDM_ERR_RANGE, "chunk_size * num_writes = %lld exceeds %d", (long long)C * D->W, MAX_CHUNK_EVENTS);
+    D->C = C;
+    D->nch = (D->T + C - 1) / C;
+  } else {
+    D->C = 1;
+    D->nch = 1;
+  }
+  return SDM_OK;
+}
+
+// Device check, memoized per device: 0 unknown, 1 gfx950, 2 other.
+std::atomic<int> g_dev_ok[64];
+size_t g_dev_lds[64];
+
+sdm_status check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(SDM_ERR_HIP, "hipGetDevice failed");
+  if (dev < 0 || dev >= 64) return fail(SDM_ERR_DEVICE, "device index %d not supported", dev);
+  int st = g_dev_ok[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t p;
+    if (hipGetDeviceProperties(&p, dev) != hipSuccess) return fail(SDM_ERR_HIP, "hipGetDeviceProperties failed");
+    st = strncmp(p.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_dev_lds[dev] = p.sharedMemPerBlock;
+    g_dev_ok[dev].store(st, std::memory_order_release);
+  }
+  if (st != 1) return fail(SDM_ERR_DEVICE, "device %d is not gfx950 (MI355X); no other GPU is supported", dev);
+  return SDM_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+WsLayout layout(const Dims& D, int op) {
+  WsLayout L;
+  memset(&L, 0, sizeof L);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t r = o;
+    o = align256(o + bytes);
+    return r;
+  };
+  L.cand_w = take(MAX_CAND * 8);
+  L.cand_r = take(MAX_CAND * 8);
+  if (op == SDM_OP_WRITE_READ) {
+    const size_t nw = (size_t)D.S * D.T * D.W, nr = (size_t)D.S * D.T * D.R;
+    const size_t nc = (size_t)D.S * D.nch;
+    const size_t CW = (size_t)chunk_events(D);
+    L.widx = take(nw * 4);
+    L.wwt = take(nw * 4);
+    L.ridx = take(nr * 4);
+    L.rwt = take(nr * 4);
+    L.wcoef = take(nw * 4);
+    L.rcoef = take(nr * 4);
+    L.wlast = take(nw * 4);
+    L.nseg = take(nc * 4);
+    L.seg_slot = take(nc * CW * 4);
+    L.seg_start = take(nc * (CW + 1) * 4);
+    L.ev = take(nc * CW * sizeof(Ev));
+    L.lptr = take(nc * (D.C + 1) * 4);
+    L.lent = take(nc * (size_t)chunk_lents(D) * sizeof(Ent));
+    L.qptr = take(nc * (D.C + 1) * 4);
+    L.qent = take(nc * (size_t)chunk_qents(D) * sizeof(Ent));
+  }
+  L.total = o;
+  return L;
+}
+
+struct Range {
+  const void* p;
+  size_t n;
+  const char* name;
+};
+
+bool overlap(const Range& a, const Range& b) {
+  if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, a1 = a0 + a.n, b0 = (uintptr_t)b.p, b1 = b0 + b.n;
+  return a0 < b1 && b0 < a1;
+}
+
+// Every output must be disjoint from every other range (inputs and outputs).
+sdm_status check_alias(const Range* outs, int nout, const Range* ins, int nin) {
+  for (int i = 0; i < nout; ++i) {
+    for (int j = 0; j < nin; ++j)
+      if (overlap(outs[i], ins[j])) return fail(SDM_ERR_ALIAS, "%s overlaps %s", outs[i].name, ins[j].name);
+    for (int j = i + 1; j < nout; ++j)
+      if (overlap(outs[i], outs[j])) return fail(SDM_ERR_ALIAS, "%s overlaps %s", outs[i].name, outs[j].name);
+  }
+  return SDM_OK;
+}
+
+sdm_status need(const void* p, const char* name) {
+  return p ? SDM_OK : fail(SDM_ERR_NULL, "%s is NULL", name);
+}
+
+sdm_status aligned(const void* p, size_t a, const char* name) {
+  return ((uintptr_t)p % a) == 0 ? SDM_OK : fail(SDM_ERR_LAYOUT, "%s must be %zu-byte aligned", name, a);
+}
+
+sdm_status check_ws(const void* ws, size_t ws_bytes, size_t need_bytes) {
+  if (need_bytes == 0) return SDM_OK;
+  if (!ws) return fail(SDM_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need_bytes);
+  if ((uintptr_t)ws % 256) return fail(SDM_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < need_bytes) return fail(SDM_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need_bytes);
+  return SDM_OK;
+}
+
+// ------------------------------------------------------------------------------------------- kernel timing
+struct ProfPair {
+  int kernel;
+  hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfPair> g_prof_pending;
+std::vector<hipEvent_t> g_prof_pool;
+double g_prof_ms[SDM_K_COUNT];
+long long g_prof_n[SDM_K_COUNT];
+
+hipEvent_t prof_event() {
+  if (!g_prof_pool.empty()) {
+    hipEvent_t e = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Runs `launch` (returns hipError_t); when timing is on, brackets it with events on stream st.
+template <typename F>
+hipError_t timed(int kernel, hipStream_t st, F&& launch) {
+  bool on;
+  {
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    on = g_prof_on;
+  }
+  if (!on) return launch();
+  ProfPair p;
+  {
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    p.kernel = kernel;
+    p.a = prof_event();
+    p.b = prof_event();
+  }
+  if (p.a) (void)hipEventRecord(p.a, st);
+  const hipError_t e = launch();
+  if (p.b) (void)hipEventRecord(p.b, st);
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  if (p.a && p.b) g_prof_pending.push_back(p);
+  return e;
+}
+
+sdm_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return SDM_OK;
+  return fail(SDM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define TRY(x)                        \
+  do {                                \
+    sdm_status _s = (x);              \
+    if (_s != SDM_OK) return _s;      \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* sdm_last_error(void) { return g_err.c_str(); }
+
+sdm_status sdm_workspace_size(const sdm_config* cfg, int32_t op, int32_t k, size_t* bytes) {
+  if (!bytes) return fail(SDM_ERR_NULL, "bytes is NULL");
+  Dims D;
+  TopkPlan pw, pr;
+  TRY(validate(cfg, op, k, &D, &pw, &pr));
+  *bytes = layout(D, op).total;
+  return ok();
+}
+
+sdm_status topk_product_keys(const sdm_config* cfg, const void* queries, const void* subkeys, int32_t k,
+                             int32_t* idx, float* scores, void* workspace, size_t workspace_bytes, void* stream) {
+  Dims D;
+  TopkPlan P, unused;
+  TRY(validate(cfg, SDM_OP_TOPK, k, &D, &P, &unused));
+  const long long rows = (long long)D.B * D.T * D.H;
+  long long sumn = 0;
+  for (int f = 0; f < D.F; ++f) sumn += D.widths[f];
+  const size_t ea = esize(D.act);
+  if (rows > 0) {
+    TRY(need(queries, "queries"));
+    TRY(need(idx, "idx"));
+  }
+  if (D.H > 0) TRY(need(subkeys, "subkeys"));
+  const WsLayout L = layout(D, SDM_OP_TOPK);
+  TRY(check_ws(workspace, workspace_bytes, L.total));
+  const Range ins[] = {{queries, (size_t)rows * D.F * D.dk * ea, "queries"},
+                       {subkeys, (size_t)D.H * sumn * D.dk * ea, "subkeys"}};
+  const Range outs[] = {{idx, (size_t)rows * k * 4, "idx"},
+                        {scores, (size_t)rows * k * 4, "scores"},
+                        {workspace, L.total, "workspace"}};
+  TRY(check_alias(outs, 3, ins, 2));
+  TRY(check_device());
+  if (rows == 0) return ok();
+  hipStream_t st = (hipStream_t)stream;
+  unsigned char* ws = (unsigned char*)workspace;
+  TRY(hip_status(timed(SDM_K_CAND, st, [&] { return launch_cand_table(P, D.F, (uint64_t*)(ws + L.cand_w), st); }),
+                 "candidate table launch"));
+  TopkArgs a;
+  memset(&a, 0, sizeof a);
+  a.queries[0] = queries;
+  a.subkeys = subkeys;
+  a.cand[0] = (const uint64_t*)(ws + L.cand_w);
+  a.plan[0] = P;
+  a.nkinds = 1;
+  a.stream_major = 0;
+  a.ids[0] = idx;
+  a.vals[0] = scores;
+  TRY(hip_status(timed(SDM_K_TOPK, st, [&] { return launch_topk(D, a, st); }), "top-k launch"));
+  return ok();
+}
+
+sdm_status sdm_write_read(const sdm_config* cfg, const void* write_keys, const void* read_queries,
+                          const void* values, const void* forget_gate, const void* input_gate, const void* subkeys,
+                          void* bank, void* out, int32_t* write_idx, int32_t* read_idx, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  Dims D;
+  TopkPlan pw, pr;
+  TRY(validate(cfg, SDM_OP_WRITE_READ, 0, &D, &pw, &pr));
+  const long long rows = (long long)D.B * D.T * D.H;
+  long long sumn = 0;
+  for (int f = 0; f < D.F; ++f) sumn += D.widths[f];
+  const size_t ea = esize(D.act), eb = esize(D.bank);
+  const size_t bank_bytes = (size_t)D.S * (size_t)D.rows * D.d * eb;
+  if (rows > 0) {
+    TRY(need(write_keys, "write_keys"));
+    TRY(need(read_queries, "read_queries"));
+    TRY(need(values, "values"));
+    TRY(need(forget_gate, "forget_gate"));
+    TRY(need(input_gate, "input_gate"));
+    TRY(need(subkeys, "subkeys"));
+    TRY(need(bank, "bank"));
+    TRY(need(out, "out"));
+  }
+  TRY(aligned(bank, 16, "bank"));
+  const WsLayout L = layout(D, SDM_OP_WRITE_READ);
+  TRY(check_ws(workspace, workspace_bytes, L.total));
+  const size_t qb = (size_t)rows * D.F * D.dk * ea;
+  const Range ins[] = {{write_keys, qb, "write_keys"},
+                       {read_queries, qb, "read_queries"},
+                       {values, (size_t)rows * D.d * ea, "values"},
+                       {forget_gate, (size_t)rows * ea, "forget_gate"},
+                       {input_gate, (size_t)rows * ea, "input_gate"},
+                       {subkeys, (size_t)D.H * sumn * D.dk * ea, "subkeys"}};
+  const Range outs[] = {{bank, bank_bytes, "bank"},
+                        {out, (size_t)rows * D.d * ea, "out"},
+                        {write_idx, (size_t)rows * D.W * 4, "write_idx"},
+                        {read_idx, (size_t)rows * D.R * 4, "read_idx"},
+                        {workspace, L.total, "workspace"}};
+  TRY(check_alias(outs, 5, ins, 6));
+  TRY(check_device());
+  if (rows == 0) return ok();
+  hipStream_t st = (hipStream_t)stream;
+  unsigned char* ws = (unsigned char*)workspace;
+  TRY(hip_status(timed(SDM_K_CAND, st, [&] { return launch_cand_table(pw, D.F, (uint64_t*)(ws + L.cand_w), st); }),
+                 "candidate table launch"));
+  TRY(hip_status(timed(SDM_K_CAND, st, [&] { return launch_cand_table(pr, D.F, (uint64_t*)(ws + L.cand_r), st); }),
+                 "candidate table launch"));
+  TopkArgs ta;
+  memset(&ta, 0, sizeof ta);
+  ta.queries[0] = write_keys;
+  ta.queries[1] = read_queries;
+  ta.subkeys = subkeys;
+  ta.cand[0] = (const uint64_t*)(ws + L.cand_w);
+  ta.cand[1] = (const uint64_t*)(ws + L.cand_r);
+  ta.plan[0] = pw;
+  ta.plan[1] = pr;
+  ta.nkinds = 2;
+  ta.stream_major = 1;
+  ta.ids[0] = (int32_t*)(ws + L.widx);
+  ta.ids[1] = (int32_t*)(ws + L.ridx);
+  ta.vals[0] = (float*)(ws + L.wwt);
+  ta.vals[1] = (float*)(ws + L.rwt);
+  ta.user_ids[0] = write_idx;
+  ta.user_ids[1] = read_idx;
+  TRY(hip_status(timed(SDM_K_TOPK, st, [&] { return launch_topk(D, ta, st); }), "top-k launch"));
+  PlanArgs pa;
+  pa.widx = (const int32_t*)(ws + L.widx);
+  pa.wwt = (const float*)(ws + L.wwt);
+  pa.ridx = (const int32_t*)(ws + L.ridx);
+  pa.rwt = (const float*)(ws + L.rwt);
+  pa.alpha = forget_gate;
+  pa.beta = input_gate;
+  pa.wcoef = (float*)(ws + L.wcoef);
+  pa.rcoef = (float*)(ws + L.rcoef);
+  pa.wlast = (int32_t*)(ws + L.wlast);
+  pa.nseg = (int32_t*)(ws + L.nseg);
+  pa.seg_slot = (int32_t*)(ws + L.seg_slot);
+  pa.seg_start = (int32_t*)(ws + L.seg_start);
+  pa.ev = (Ev*)(ws + L.ev);
+  pa.lptr = (int32_t*)(ws + L.lptr);
+  pa.lent = (Ent*)(ws + L.lent);
+  pa.qptr = (int32_t*)(ws + L.qptr);
+  pa.qent = (Ent*)(ws + L.qent);
+  TRY(hip_status(timed(SDM_K_PLAN, st, [&] { return launch_plan(D, pa, st); }), "chunk plan launch"));
+  LoopArgs la;
+  la.widx = pa.widx;
+  la.wcoef = pa.wcoef;
+  la.ridx = pa.ridx;
+  la.rcoef = pa.rcoef;
+  la.alpha = forget_gate;
+  la.beta = input_gate;
+  la.values = values;
+  la.nseg = pa.nseg;
+  la.seg_slot = pa.seg_slot;
+  la.seg_start = pa.seg_start;
+  la.ev = pa.ev;
+  la.lptr = pa.lptr;
+  la.lent = pa.lent;
+  la.qptr = pa.qptr;
+  la.qent = pa.qent;
+  la.bank = bank;
+  la.out = out;
+  TRY(hip_status(timed(SDM_K_LOOP, st, [&] { return launch_loop(D, la, st); }), "chunk loop launch"));
+  return ok();
+}
+
+sdm_status sdm_decode_step(const sdm_config* cfg, const void* write_keys, const void* read_queries,
+                           const void* values, const void* forget_gate, const void* input_gate, const void* subkeys,
+                           const void* bank_in, void* bank_out, void* out, int32_t* write_idx, int32_t* read_idx,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  Dims D;
+  TopkPlan pw, pr;
+  TRY(validate(cfg, SDM_OP_DECODE, 0, &D, &pw, &pr));
+  const long long rows = (long long)D.B * D.H;
+  long long sumn = 0;
+  for (int f = 0; f < D.F; ++f) sumn += D.widths[f];
+  const size_t ea = esize(D.act), eb = esize(D.bank);
+  const size_t bank_bytes = (size_t)D.S * (size_t)D.rows * D.d * eb;
+  if (rows > 0) {
+    TRY(need(write_keys, "write_keys"));
+    TRY(need(read_queries, "read_queries"));
+    TRY(need(values, "values"));
+    TRY(need(forget_gate, "forget_gate"));
+    TRY(need(input_gate, "input_gate"));
+    TRY(need(subkeys, "subkeys"));
+    TRY(need(bank_in, "bank_in"));
+    TRY(need(bank_out, "bank_out"));
+    TRY(need(out, "out"));
+  }
+  TRY(aligned(bank_in, 16, "bank_in"));
+  TRY(aligned(bank_out, 16, "bank_out"));
+  const WsLayout L = layout(D, SDM_OP_DECODE);
+  TRY(check_ws(workspace, workspace_bytes, L.total));
+  const bool donated = bank_in == bank_out;
+  const size_t qb = (size_t)rows * D.F * D.dk * ea;
+  const Range ins[] = {{write_keys, qb, "write_keys"},
+                       {read_queries, qb, "read_queries"},
+                       {values, (size_t)rows * D.d * ea, "values"},
+                       {forget_gate, (size_t)rows * ea, "forget_gate"},
+                       {input_gate, (size_t)rows * ea, "input_gate"},
+                       {subkeys, (size_t)D.H * sumn * D.dk * ea, "subkeys"},
+                       {donated ? nullptr : bank_in, bank_bytes, "bank_in"}};
+  const Range outs[] = {{bank_out, bank_bytes, "bank_out"},
+                        {out, (size_t)rows * D.d * ea, "out"},
+                        {write_idx, (size_t)rows * D.W * 4, "write_idx"},
+                        {read_idx, (size_t)rows * D.R * 4, "read_idx"},
+                        {workspace, L.total, "workspace"}};
+  TRY(check_alias(outs, 5, ins, 7));
+  TRY(check_device());
+  if (rows == 0) return ok();
+  hipStream_t st = (hipStream_t)stream;
+  unsigned char* ws = (unsigned char*)workspace;
+  TRY(hip_status(timed(SDM_K_CAND, st, [&] { return launch_cand_table(pw, D.F, (uint64_t*)(ws + L.cand_w), st); }),
+                 "candidate table launch"));
+  TRY(hip_status(timed(SDM_K_CAND, st, [&] { return launch_cand_table(pr, D.F, (uint64_t*)(ws + L.cand_r), st); }),
+                 "candidate table launch"));
+  if (!donated)
+    TRY(hip_status(timed(SDM_K_COPY, st, [&] { return launch_copy(bank_in, bank_out, bank_bytes, st); }),
+                   "successor copy launch"));
+  DecodeArgs a;
+  a.wkeys = write_keys;
+  a.rq = read_queries;
+  a.values = values;
+  a.alpha = forget_gate;
+  a.beta = input_gate;
+  a.subkeys = subkeys;
+  a.bank_in = bank_in;
+  a.bank_out = bank_out;
+  a.out = out;
+  a.widx = write_idx;
+  a.ridx = read_idx;
+  a.cand[0] = (const uint64_t*)(ws + L.cand_w);
+  a.cand[1] = (const uint64_t*)(ws + L.cand_r);
+  a.plan[0] = pw;
+  a.plan[1] = pr;
+  TRY(hip_status(timed(SDM_K_DECODE, st, [&] { return launch_decode(D, a, st); }), "decode launch"));
+  return ok();
+}
+
+sdm_status sdm_profile_enable(int32_t on) {
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  for (auto& p : g_prof_pending) {
+    g_prof_pool.push_back(p.a);
+    g_prof_pool.push_back(p.b);
+  }
+  g_prof_pending.clear();
+  for (int k = 0; k < SDM_K_COUNT; ++k) {
+    g_prof_ms[k] = 0.0;
+    g_prof_n[k] = 0;
+  }
+  g_prof_on = on != 0;
+  return ok();
+}
+
+sdm_status sdm_profile_read(double* ms, int64_t* launches) {
+  if (!ms || !launches) return fail(SDM_ERR_NULL, "ms and launches must not be NULL");
+  std::lock_guard<std::mutex> g(g_prof_mu);
+  for (auto& p : g_prof_pending) {
+    float t = 0.0f;
+    if (hipEventSynchronize(p.b) != hipSuccess || hipEventElapsedTime(&t, p.a, p.b) != hipSuccess)
+      return fail(SDM_ERR_HIP, "reading kernel timing events failed");
+    g_prof_ms[p.kernel] += t;
+    g_prof_n[p.kernel] += 1;
+    g_prof_pool.push_back(p.a);
+    g_prof_pool.push_back(p.b);
+  }
+  g_prof_pending.clear();
+  for (int k = 0; k < SDM_K_COUNT; ++k) {
+    ms[k] = g_prof_ms[k];
+    launches[k] = g_prof_n[k];
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,241 @@
+// Chunk plan: everything of a chunk that does not depend on the bank, for every (stream, chunk) in parallel.
+//
+// Chunked form of the per-token recurrence (gated delta rule restricted to the selected rows; sparse-delta-memory
+// CHANGELOG.md 2.0.0: a chunked write/read whose chunk size changes results only through rounding, an IEEE-float32
+// triangular ("WY") solve and a "dual" product inside the op). For a chunk of tokens 0..C-1 with bank M_0 at its
+// start, let gamma_j(s -> t) be the product of alpha_u over the chunk's tokens u in (s, t] that write slot j. Then
+//   h_t = sum_{j in S_t} w_tj gamma_j(0 -> t-1) M_0[j]       (write gather, coefficient a_tj)
+//   g_t = sum_{j in R_t} rho_tj gamma_j(0 -> t) M_0[j]       (read gather, coefficient b_tj)
+//   K_ts = sum_{j in S_t and S_s} w_tj w_sj gamma_j(s -> t-1)             for s < t
+//   Q_ts = sum_{j in R_t and S_s} rho_tj w_sj gamma_j(s -> t)             for s <= t
+//   (I + diag(alpha beta) K) delta = diag(beta) V - diag(alpha beta) H,   out_t = g_t + sum_s Q_ts delta_s,
+// and each written row ends as the in-order application of M[j] <- alpha_s M[j] + w_sj delta_s over its events.
+// This kernel sorts the chunk's write events by (slot, token), and emits: a and b, the slot segments with their
+// events, L = diag(alpha beta) K and Q as row-sorted sparse lists. Every sum runs in a fixed order (bitwise
+// repeatable; no atomics).
+#include "sdm_internal.h"
+
+namespace sdm {
+
+__host__ __device__ inline size_t plan_lds_bytes(int C, int W) {
+  const size_t CW = (size_t)C * W;
+  size_t keys = (size_t)pow2_ceil((int)CW) * 8;
+  const size_t dense = (size_t)C * C * 4;
+  if (dense > keys) keys = dense;
+  return keys + CW * 4 /*sslot*/ + CW * 2 /*sev*/ + CW * 2 /*pos*/ + (size_t)C * 8 /*alpha, beta*/ +
+         (size_t)PLAN_NT * 4 /*scan*/ + 16;
+}
+
+template <typename A>
+__global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int tid = threadIdx.x;
+  const int st = blockIdx.y;
+  const int ch = blockIdx.x;
+  const int b = st / D.H, h = st % D.H;
+  const int W = D.W, R = D.R, C = D.C;
+  const int t0 = ch * C;
+  const int Cc = min(C, D.T - t0);
+  const int E = Cc * W;
+  const int Ep2 = pow2_ceil(E);
+  const long long CW = (long long)C * W;
+  const long long cidx = (long long)st * D.nch + ch;
+  const long long wbase = ((long long)st * D.T + t0) * W;  // [S][T][W] offset of the chunk's first event
+  const long long rbase = ((long long)st * D.T + t0) * R;
+
+  size_t keys_bytes = (size_t)pow2_ceil((int)CW) * 8;
+  if ((size_t)C * C * 4 > keys_bytes) keys_bytes = (size_t)C * C * 4;
+  uint64_t* keys = (uint64_t*)lds;
+  float* dense = (float*)lds;
+  int32_t* sslot = (int32_t*)(lds + keys_bytes);
+  uint16_t* sev = (uint16_t*)(sslot + CW);
+  uint16_t* pos = sev + CW;
+  float* sA = (float*)(pos + CW + (CW & 1));
+  float* sB = sA + C;
+  int32_t* scan = (int32_t*)(sB + C);
+
+  // 1. write events -> sort keys (slot, event index); gates of the chunk.
+  for (int e = tid; e < Ep2; e += PLAN_NT) {
+    uint64_t key = ~0ull;
+    if (e < E) key = ((uint64_t)(uint32_t)a.widx[wbase + e] << 32) | (uint32_t)e;
+    keys[e] = key;
+  }
+  for (int t = tid; t < Cc; t += PLAN_NT) {
+    const long long g = ((long long)b * D.T + t0 + t) * D.H + h;
+    sA[t] = to_f<A>(((const A*)a.alpha)[g]);
+    sB[t] = to_f<A>(((const A*)a.beta)[g]);
+  }
+  __syncthreads();
+  bitonic_sort_u64<PLAN_NT>(keys, Ep2);
+  for (int e = tid; e < E; e += PLAN_NT) {
+    const uint64_t k = keys[e];
+    sslot[e] = (int32_t)(k >> 32);
+    sev[e] = (uint16_t)(k & 0xFFFF);
+    pos[k & 0xFFFF] = (uint16_t)e;
+  }
+  __syncthreads();
+
+  // 2. segments (runs of equal slots): ids by a block scan over contiguous per-thread ranges.
+  const int per = (E + PLAN_NT - 1) / PLAN_NT;
+  const int lo = min(E, tid * per), hi = min(E, lo + per);
+  int cnt = 0;
+  for (int e = lo; e < hi; ++e) cnt += (e == 0 || sslot[e] != sslot[e - 1]);
+  scan[tid] = cnt;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int i = 0; i < PLAN_NT; ++i) {
+      const int c = scan[i];
+      scan[i] = run;
+      run += c;
+    }
+    a.nseg[cidx] = run;
+    a.seg_start[cidx * (CW + 1) + run] = E;
+  }
+  __syncthreads();
+  {
+    int g = scan[tid] - 1;  // segment id of the element before lo
+    for (int e = lo; e < hi; ++e) {
+      const bool first = (e == 0 || sslot[e] != sslot[e - 1]);
+      if (first) {
+        ++g;
+        a.seg_slot[cidx * CW + g] = sslot[e];
+        a.seg_start[cidx * (CW + 1) + g] = e;
+      }
+      const bool last = (e == E - 1 || sslot[e + 1] != sslot[e]);
+      const int ev = sev[e];
+      a.wlast[wbase + ev] = last ? g : -1;
+      Ev x;
+      x.w = a.wwt[wbase + ev];
+      x.tok = ev / W;
+      a.ev[cidx * CW + e] = x;
+    }
+  }
+  __syncthreads();
+
+  // 3. K (dense rows in LDS) and the write-gather coefficients a_ti; one thread per token, events in order.
+  for (int i = tid; i < C * C; i += PLAN_NT) dense[i] = 0.0f;
+  __syncthreads();
+  for (int t = tid; t < Cc; t += PLAN_NT) {
+    for (int i = 0; i < W; ++i) {
+      const int evi = t * W + i;
+      const int e = pos[evi];
+      const int slot = sslot[e];
+      const float wt = a.wwt[wbase + evi];
+      float prod = 1.0f;
+      for (int e2 = e - 1; e2 >= 0 && sslot[e2] == slot; --e2) {
+        const int s = sev[e2] / W;
+        dense[t * C + s] += wt * a.wwt[wbase + sev[e2]] * prod;
+        prod *= sA[s];
+      }
+      a.wcoef[wbase + evi] = wt * prod;
+    }
+  }
+  __syncthreads();
+  // L = diag(alpha beta) K as row-sorted sparse lists.
+  const long long lcap = chunk_lents(D);
+  for (int t = tid; t < Cc; t += PLAN_NT) {
+    int n = 0;
+    for (int s = 0; s < t; ++s) n += dense[t * C + s] != 0.0f;
+    scan[t] = n;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int t = 0; t < Cc; ++t) {
+      const int c = scan[t];
+      scan[t] = run;
+      a.lptr[cidx * (C + 1) + t] = run;
+      run += c;
+    }
+    a.lptr[cidx * (C + 1) + Cc] = run;
+  }
+  __syncthreads();
+  for (int t = tid; t < Cc; t += PLAN_NT) {
+    int o = scan[t];
+    const float ab = sA[t] * sB[t];
+    for (int s = 0; s < t; ++s) {
+      const float k = dense[t * C + s];
+      if (k != 0.0f) {
+        Ent x;
+        x.col = s;
+        x.val = ab * k;
+        a.lent[cidx * lcap + o++] = x;
+      }
+    }
+  }
+  __syncthreads();
+
+  // 4. Q (dense rows) and the read-gather coefficients b_ti.
+  for (int i = tid; i < C * C; i += PLAN_NT) dense[i] = 0.0f;
+  __syncthreads();
+  for (int t = tid; t < Cc; t += PLAN_NT) {
+    for (int i = 0; i < R; ++i) {
+      const int j = a.ridx[rbase + (long long)t * R + i];
+      const float rho = a.rwt[rbase + (long long)t * R + i];
+      int l = 0, r = E;  // lower bound of j in sslot
+      while (l < r) {
+        const int m = (l + r) >> 1;
+        if (sslot[m] < j) l = m + 1; else r = m;
+      }
+      float prod = 1.0f;
+      if (l < E && sslot[l] == j && sev[l] / W <= t) {
+        int e1 = l;
+        while (e1 + 1 < E && sslot[e1 + 1] == j && sev[e1 + 1] / W <= t) ++e1;
+        for (int e2 = e1; e2 >= l; --e2) {
+          const int s = sev[e2] / W;
+          dense[t * C + s] += rho * a.wwt[wbase + sev[e2]] * prod;
+          prod *= sA[s];
+        }
+      }
+      a.rcoef[rbase + (long long)t * R + i] = rho * prod;
+    }
+  }
+  __syncthreads();
+  const long long qcap = chunk_qents(D);
+  for (int t = tid; t < Cc; t += PLAN_NT) {
+    int n = 0;
+    for (int s = 0; s <= t; ++s) n += dense[t * C + s] != 0.0f;
+    scan[t] = n;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int t = 0; t < Cc; ++t) {
+      const int c = scan[t];
+      scan[t] = run;
+      a.qptr[cidx * (C + 1) + t] = run;
+      run += c;
+    }
+    a.qptr[cidx * (C + 1) + Cc] = run;
+  }
+  __syncthreads();
+  for (int t = tid; t < Cc; t += PLAN_NT) {
+    int o = scan[t];
+    for (int s = 0; s <= t; ++s) {
+      const float q = dense[t * C + s];
+      if (q != 0.0f) {
+        Ent x;
+        x.col = s;
+        x.val = q;
+        a.qent[cidx * qcap + o++] = x;
+      }
+    }
+  }
+}
+
+hipError_t launch_plan(const Dims& D, const PlanArgs& a, hipStream_t st) {
+  if (D.S == 0 || D.T == 0) return hipSuccess;
+  const size_t lds = plan_lds_bytes(D.C, D.W);
+  dim3 grid((unsigned)D.nch, (unsigned)D.S);
+  if (D.act == SDM_BF16) {
+    (void)hipFuncSetAttribute((const void*)plan_kernel<bf16_t>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipLaunchKernelGGL(plan_kernel<bf16_t>, grid, dim3(PLAN_NT), lds, st, D, a);
+  } else {
+    (void)hipFuncSetAttribute((const void*)plan_kernel<float>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipLaunchKernelGGL(plan_kernel<float>, grid, dim3(PLAN_NT), lds, st, D, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sdm

@@ -1,0 +1,187 @@
+// Internal declarations shared by the SDM HIP translation units: validated dimensions, workspace layout, device
+// helpers (bfloat16 conversion, order-preserving sort keys, LDS bitonic sort) and kernel launch wrappers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "sdm.h"
+
+namespace sdm {
+
+constexpr int MAX_F = 4;
+constexpr int MAX_K = 512;           // num_writes, num_reads, top-k k
+constexpr int MAX_NF = 4096;         // sub-keys per factor
+constexpr int MAX_CAND = 4096;       // candidate tuples prod(p_f + 1) <= k
+constexpr int MAX_FDK = 1024;        // F * dk
+constexpr int MAX_CHUNK = 128;       // chunk_size
+constexpr int MAX_CHUNK_EVENTS = 8192;  // chunk_size * num_writes
+constexpr int TOPK_NT = 256;
+constexpr int PLAN_NT = 512;
+constexpr int LOOP_NT = 512;
+constexpr int DECODE_NT = 256;
+
+typedef uint16_t bf16_t;
+
+// Validated problem dimensions (host and device).
+struct Dims {
+  int B, T, H, F, dk, d, W, R, C;
+  int widths[MAX_F];
+  int act, bank;        // sdm_dtype
+  long long N;          // slots per head
+  long long rows;       // bank rows per stream
+  int nch;              // chunks per stream
+  int S;                // streams = B * H
+};
+
+// Per-query-kind top-k plan: kept positions per factor and the candidate table.
+struct TopkPlan {
+  int k;
+  int kp[MAX_F];        // min(k, n_f)
+  int kpmax;
+  int ncand;            // tuples with prod(p_f + 1) <= k, p_f < kp[f]
+  int cand_pow2;
+  int nf_pow2;          // next power of two of max n_f
+};
+
+// One scatter event of a chunk: (weight, chunk-local token), sorted by (slot, token).
+struct Ev {
+  float w;
+  int32_t tok;
+};
+
+// One sparse entry of the chunk's strictly-lower L = diag(alpha*beta) K or of the read-coupling matrix Q.
+struct Ent {
+  int32_t col;
+  float val;
+};
+
+// ------------------------------------------------------------------------------------------- device helpers
+__device__ __forceinline__ float bf16_to_f(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// float -> bfloat16, round to nearest even (finite inputs).
+__device__ __forceinline__ bf16_t f_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float to_f(T v);
+template <> __device__ __forceinline__ float to_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f<bf16_t>(bf16_t v) { return bf16_to_f(v); }
+
+template <typename T> __device__ __forceinline__ double to_d(T v) { return (double)to_f<T>(v); }
+
+template <typename T> __device__ __forceinline__ T from_f(float v);
+template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float v) { return f_to_bf16(v); }
+
+// Sort key half for "larger float first": ascending order of the returned value = descending order of x.
+// -0 and +0 map to the same key (they compare equal).
+__device__ __forceinline__ uint32_t desc_key(float x) {
+  if (x == 0.0f) x = 0.0f;
+  uint32_t u = __float_as_uint(x);
+  uint32_t m = (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // ascending map
+  return ~m;
+}
+__device__ __forceinline__ float desc_key_value(uint32_t k) {
+  uint32_t m = ~k;
+  uint32_t u = (m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m;
+  return __uint_as_float(u);
+}
+
+// Ascending bitonic sort of n (a power of two) 64-bit keys in LDS by the whole block. Ends with a barrier.
+template <int NT>
+__device__ __forceinline__ void bitonic_sort_u64(uint64_t* keys, int n) {
+  const int tid = threadIdx.x;
+  for (int size = 2; size <= n; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < (n >> 1); i += NT) {
+        int lo = 2 * i - (i & (stride - 1));
+        int hi = lo + stride;
+        bool up = (lo & size) == 0;
+        uint64_t a = keys[lo], b = keys[hi];
+        if ((a > b) == up) {
+          keys[lo] = b;
+          keys[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__host__ __device__ inline int pow2_ceil(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+// ------------------------------------------------------------------------------------------- workspace layout
+struct WsLayout {
+  size_t cand_w, cand_r;                       // uint64 [MAX_CAND] each
+  size_t widx, wwt, ridx, rwt;                 // [S][T][W|R]
+  size_t wcoef, rcoef, wlast;                  // [S][T][W|R]
+  size_t nseg, seg_slot, seg_start, ev;        // per chunk
+  size_t lptr, lent, qptr, qent;               // per chunk
+  size_t total;
+};
+
+// ------------------------------------------------------------------------------------------- launch wrappers
+// Candidate tuples (p_0..p_{F-1}) with prod(p_f + 1) <= k, p_f < kp[f], in lexicographic order; p_f in bits
+// [16 f, 16 f + 16) of each entry.
+hipError_t launch_cand_table(const TopkPlan& p, int F, uint64_t* table, hipStream_t st);
+
+// Top-k of every row of one or two query tensors. For kind q (0, 1): queries[q], k = plan[q].k.
+//  stream_major != 0: ids/weights go to ws arrays [S][T][k] (+ optional user ids [B,T,H,k]);
+//  otherwise ids/scores go to [B,T,H,k].
+struct TopkArgs {
+  const void* queries[2];
+  const void* subkeys;
+  const uint64_t* cand[2];
+  TopkPlan plan[2];
+  int nkinds;
+  int stream_major;
+  int32_t* ids[2];       // stream-major ids or user ids
+  float* vals[2];        // stream-major weights (softmax) or user scores (may be NULL)
+  int32_t* user_ids[2];  // optional user ids [B,T,H,k] in stream-major mode
+};
+hipError_t launch_topk(const Dims& D, const TopkArgs& a, hipStream_t st);
+
+struct PlanArgs {
+  const int32_t* widx; const float* wwt; const int32_t* ridx; const float* rwt;
+  const void* alpha; const void* beta;
+  float* wcoef; float* rcoef; int32_t* wlast;
+  int32_t* nseg; int32_t* seg_slot; int32_t* seg_start; Ev* ev;
+  int32_t* lptr; Ent* lent; int32_t* qptr; Ent* qent;
+};
+hipError_t launch_plan(const Dims& D, const PlanArgs& a, hipStream_t st);
+
+struct LoopArgs {
+  const int32_t* widx; const float* wcoef; const int32_t* ridx; const float* rcoef;
+  const void* alpha; const void* beta; const void* values;
+  const int32_t* nseg; const int32_t* seg_slot; const int32_t* seg_start; const Ev* ev;
+  const int32_t* lptr; const Ent* lent; const int32_t* qptr; const Ent* qent;
+  void* bank; void* out;
+};
+hipError_t launch_loop(const Dims& D, const LoopArgs& a, hipStream_t st);
+
+struct DecodeArgs {
+  const void* wkeys; const void* rq; const void* values; const void* alpha; const void* beta; const void* subkeys;
+  const void* bank_in; void* bank_out; void* out; int32_t* widx; int32_t* ridx;
+  const uint64_t* cand[2];
+  TopkPlan plan[2];
+};
+hipError_t launch_decode(const Dims& D, const DecodeArgs& a, hipStream_t st);
+hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t st);
+
+// sizes per chunk
+__host__ __device__ inline long long chunk_events(const Dims& D) { return (long long)D.C * D.W; }
+__host__ __device__ inline long long chunk_lents(const Dims& D) {
+  const long long n = (long long)D.C * (D.C - 1) / 2;
+  return n > 0 ? n : 1;
+}
+__host__ __device__ inline long long chunk_qents(const Dims& D) { return (long long)D.C * (D.C + 1) / 2; }
+
+}  // namespace sdm

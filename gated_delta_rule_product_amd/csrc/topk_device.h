@@ -1,0 +1,141 @@
+// Exact product-key top-k of one query, computed by one workgroup (shared by the top-k and decode kernels).
+//
+// Method (sparse-delta-memory CHANGELOG.md 2.0.0, "Upgrading from v1" and "New"): the slot score is the float32
+// sum of the factor scores and the top-k is exact; equal slot scores go to the larger rank sum, then the larger
+// first rank. Here a factor score is the float32 rounding of an fp64 FMA chain in coordinate order, and ranks are
+// per-factor positions p_f under (score descending, index ascending), p_f = 0 best.
+//
+// Exactness of the candidate set: if slot a is at a position <= slot b's in every factor (and differs), a's slot
+// score is >= b's (float32 addition is monotone) and its position sum is smaller, so a precedes b. A slot with
+// prod(p_f + 1) > k is therefore preceded by at least k others and cannot be in the top k; every slot of the top k
+// lies among the tuples with prod(p_f + 1) <= k (the candidate table), and those need only the best
+// min(k, n_f) sub-keys of each factor.
+#pragma once
+#include "sdm_internal.h"
+
+namespace sdm {
+
+// LDS bytes of one topk_query workspace (8-byte aligned regions).
+__host__ __device__ inline size_t topk_lds_bytes(int F, int dk, const TopkPlan& P) {
+  size_t n = 0;
+  n += (size_t)F * dk * 8;                                              // query (fp64)
+  n += (size_t)(P.nf_pow2 > P.cand_pow2 ? P.nf_pow2 : P.cand_pow2) * 8;  // sort keys
+  n += (size_t)F * P.kpmax * 8;                                        // kept factor scores + sub-key ids
+  n += (size_t)P.k * 16;                                               // result ids, scores, exp values
+  return n;
+}
+
+struct TopkLds {
+  double* q;
+  uint64_t* keys;
+  float* fsc;
+  int32_t* fid;
+  int32_t* rid;
+  float* rsc;
+  double* rexp;
+};
+
+__device__ inline TopkLds topk_lds_carve(unsigned char* base, int F, int dk, const TopkPlan& P) {
+  TopkLds L;
+  size_t o = 0;
+  L.q = (double*)(base + o);
+  o += (size_t)F * dk * 8;
+  L.keys = (uint64_t*)(base + o);
+  o += (size_t)(P.nf_pow2 > P.cand_pow2 ? P.nf_pow2 : P.cand_pow2) * 8;
+  L.fsc = (float*)(base + o);
+  o += (size_t)F * P.kpmax * 4;
+  L.fid = (int32_t*)(base + o);
+  o += (size_t)F * P.kpmax * 4;
+  L.rexp = (double*)(base + o);
+  o += (size_t)P.k * 8;
+  L.rid = (int32_t*)(base + o);
+  o += (size_t)P.k * 4;
+  L.rsc = (float*)(base + o);
+  return L;
+}
+
+// All NT threads of the block call this. On return (after a barrier) L.rid[0..k) / L.rsc[0..k) hold the top-k
+// slot ids and float32 slot scores, best first.
+template <typename A, int NT>
+__device__ void topk_query(const A* __restrict__ q, const A* __restrict__ sub, const int* widths, int F, int dk,
+                           const TopkPlan& P, const uint64_t* __restrict__ cand, const TopkLds& L) {
+  const int tid = threadIdx.x;
+  for (int c = tid; c < F * dk; c += NT) L.q[c] = to_d<A>(q[c]);
+  __syncthreads();
+  size_t off = 0;
+  for (int f = 0; f < F; ++f) {
+    const int n = widths[f];
+    const int np2 = pow2_ceil(n);
+    const A* tab = sub + off * dk;
+    const double* qf = L.q + f * dk;
+    for (int i = tid; i < np2; i += NT) {
+      uint64_t key = ~0ull;
+      if (i < n) {
+        const A* row = tab + (size_t)i * dk;
+        double acc = 0.0;
+        for (int c = 0; c < dk; ++c) acc = fma(qf[c], to_d<A>(row[c]), acc);
+        key = ((uint64_t)desc_key((float)acc) << 32) | (uint32_t)i;
+      }
+      L.keys[i] = key;
+    }
+    __syncthreads();
+    bitonic_sort_u64<NT>(L.keys, np2);
+    for (int p = tid; p < P.kp[f]; p += NT) {
+      const uint64_t k = L.keys[p];
+      L.fid[f * P.kpmax + p] = (int32_t)(uint32_t)k;
+      L.fsc[f * P.kpmax + p] = desc_key_value((uint32_t)(k >> 32));
+    }
+    __syncthreads();
+    off += n;
+  }
+  for (int c = tid; c < P.cand_pow2; c += NT) {
+    uint64_t key = ~0ull;
+    if (c < P.ncand) {
+      const uint64_t tup = cand[c];
+      int p = (int)(tup & 0xFFFF);
+      float S = L.fsc[p];
+      int ps = p;
+      for (int f = 1; f < F; ++f) {
+        p = (int)((tup >> (16 * f)) & 0xFFFF);
+        S = S + L.fsc[f * P.kpmax + p];  // float32 sum, left to right
+        ps += p;
+      }
+      // ascending key = (slot score descending, position sum ascending, lexicographic positions ascending)
+      key = ((uint64_t)desc_key(S) << 32) | ((uint64_t)ps << 20) | (uint64_t)c;
+    }
+    L.keys[c] = key;
+  }
+  __syncthreads();
+  bitonic_sort_u64<NT>(L.keys, P.cand_pow2);
+  for (int r = tid; r < P.k; r += NT) {
+    const uint64_t key = L.keys[r];
+    const uint64_t tup = cand[(int)(key & 0xFFFFF)];
+    long long id = 0;
+    for (int f = 0; f < F; ++f) id = id * widths[f] + L.fid[f * P.kpmax + (int)((tup >> (16 * f)) & 0xFFFF)];
+    L.rid[r] = (int32_t)id;
+    L.rsc[r] = desc_key_value((uint32_t)(key >> 32));
+  }
+  __syncthreads();
+}
+
+// Softmax over the k selected scores (fp64, max-subtracted, sequential sum); weights into w (may alias nothing
+// in L). All threads call; ends with a barrier.
+template <int NT>
+__device__ void topk_softmax(const TopkLds& L, int k, float* w) {
+  const int tid = threadIdx.x;
+  const double m = (double)L.rsc[0];  // best first: the maximum
+  for (int r = tid; r < k; r += NT) L.rexp[r] = exp((double)L.rsc[r] - m);
+  __syncthreads();
+  __shared__ double s_z;
+  if (tid == 0) {
+    double z = 0.0;
+    for (int r = 0; r < k; ++r) z += L.rexp[r];
+    s_z = z;
+  }
+  __syncthreads();
+  const double z = s_z;
+  for (int r = tid; r < k; r += NT) w[r] = (float)(L.rexp[r] / z);
+  __syncthreads();
+}
+
+}  // namespace sdm

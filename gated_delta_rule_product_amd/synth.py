@@ -125,11 +125,19 @@ def make_bank_stream(s: Shape, b: int, h: int, seed: int = 0) -> np.ndarray:
     return _as(_normal(seed, _T_BANK, (s.rows, s.head_dim), scale=0.02, sub=b * s.heads + h), s.bank)
 
 
-def make_bank(s: Shape, seed: int = 0) -> np.ndarray:
+def make_bank(s: Shape, seed: int = 0, threads: int = 8) -> np.ndarray:
+    """Initial bank [B, H, bank_rows, d]; streams are drawn independently (in parallel threads)."""
+    from concurrent.futures import ThreadPoolExecutor
+
     out = np.empty((s.batch, s.heads, s.rows, s.head_dim), dtype=np.float32)
-    for b in range(s.batch):
-        for h in range(s.heads):
-            out[b, h] = make_bank_stream(s, b, h, seed)
+
+    def one(bh):
+        b, h = bh
+        out[b, h] = make_bank_stream(s, b, h, seed)
+
+    pairs = [(b, h) for b in range(s.batch) for h in range(s.heads)]
+    with ThreadPoolExecutor(max_workers=max(1, min(threads, len(pairs)))) as ex:
+        list(ex.map(one, pairs))
     return out
 
 

@@ -1,0 +1,147 @@
+/*
+ * sdm.h - Sparse Delta Memory (SDM) chunked write/read, exact product-key top-k and single-token decode step,
+ * as a C ABI over hand-written HIP kernels for AMD Instinct MI355X (gfx950).
+ *
+ * The method (sparse-delta-memory README.md, summary; CHANGELOG.md 2.0.0): a sequence mixer that keeps a large bank
+ * of slots per head. For every token and head it
+ *   1. addresses slots with product keys: the query is split into F factors, each factor is scored against its own
+ *      sub-key table, and a slot (one sub-key per factor) scores the float32 sum of its factor scores; the top-k
+ *      slots are exact (equal to brute force over all slots); equal slot scores go to the larger rank sum, then the
+ *      larger first rank (CHANGELOG 2.0.0, "Upgrading from v1" and "New");
+ *   2. applies a gated forget/input delta-rule update to the num_writes selected rows (README summary; gated delta
+ *      rule of Gated DeltaNet, README "ideas");
+ *   3. reads a score-weighted sum of the num_reads selected rows (CHANGELOG 2.0.0, "Removed": the op gathers its own
+ *      rows);
+ *   processing chunk_size tokens at a time; chunk_size changes results only through floating-point rounding
+ *   (CHANGELOG 2.0.0, "Upgrading from v1"). The decode step is the one-token case with a successor bank that may be
+ *   the predecessor's own storage (lumen PR #29, "Donating is a permission, not a demand").
+ *
+ * Arithmetic, as this library defines it (per stream s = (b, h), per token t, all address work bank-independent):
+ *   factor score   s_f[i] = float32( fp64 fused-multiply-add chain over c = 0..dk-1 of q[f*dk + c] * C_f[h][i][c] )
+ *   rank order     per factor by (score descending, index ascending); p_f = position (0 = best)
+ *   slot           (i_0, ..., i_{F-1}); id = ((i_0 * n_1 + i_1) * n_2 + i_2) ...; score = float32 sum, left to right
+ *   top-k order    slot score descending, then sum of p_f ascending, then p_0 ascending, p_1 ascending, ...
+ *   weights        w = softmax of the W selected write scores, rho = softmax of the R selected read scores
+ *   update         r = sum_i w_i M[S_i];  delta = beta * (v - alpha * r);  M[S_i] <- alpha * M[S_i] + w_i * delta
+ *   read           out = sum_i rho_i M[R_i], after the update
+ * alpha (forget gate) and beta (input gate) are one scalar each per (token, head), given by the caller.
+ *
+ * Layouts (row-major, contiguous, no strides):
+ *   queries / write_keys / read_queries  [B, T, H, F*dk]   act dtype; factor f uses columns [f*dk, (f+1)*dk)
+ *   subkeys                              [H, sum_f n_f, dk] act dtype; factor tables stacked in factor order
+ *   values, out                          [B, T, H, d]      act dtype
+ *   forget_gate, input_gate              [B, T, H]         act dtype
+ *   bank                                 [B, H, bank_rows, d] bank dtype; rows >= N are never read or written
+ *   write_idx, read_idx (optional)       [B, T, H, W] / [B, T, H, R] int32 slot ids, best first
+ *
+ * Ownership and streams: the caller owns every buffer. The library never allocates or frees memory (temporary
+ * storage comes from the caller's workspace, sized by sdm_workspace_size), never synchronises the stream, keeps no
+ * pointer after a call returns, and writes only the outputs named for each call and the workspace. All work is
+ * enqueued on `stream` (a hipStream_t; NULL = the null stream) of the current HIP device. Results are bitwise
+ * repeatable for fixed inputs and settings (no floating-point atomics).
+ *
+ * Errors: every check runs on the host before any device work, and a refused call does no work (CHANGELOG 2.0.0,
+ * "Behavior changes": refusals are raised at the entry of the op, no fallback paths). On a non-OK status,
+ * sdm_last_error() returns a message for the calling thread. The device check (gfx950 only) is memoized per device.
+ */
+#ifndef SDM_H
+#define SDM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SDM_OK = 0,
+  SDM_ERR_DTYPE = 1,          /* float16 (refused, CHANGELOG 2.0.0 "Behavior changes") or an unknown dtype code */
+  SDM_ERR_RANGE = 2,          /* a size outside the supported range (listed per field of sdm_config) */
+  SDM_ERR_BANK_TOO_SMALL = 3, /* bank_rows < N (CHANGELOG 2.0.0 "Behavior changes": a too-small cache bank) */
+  SDM_ERR_ALIAS = 4,          /* an output overlaps an input or another output (except bank_out == bank_in) */
+  SDM_ERR_LAYOUT = 5,         /* misaligned pointer or head_dim not a multiple of the bank's 16-byte lane */
+  SDM_ERR_WORKSPACE = 6,      /* workspace NULL, too small, or not 256-byte aligned */
+  SDM_ERR_DEVICE = 7,         /* the current device is not gfx950 (no fallback path) */
+  SDM_ERR_HIP = 8,            /* a HIP runtime call failed (launch or device query) */
+  SDM_ERR_NULL = 9            /* a required pointer is NULL */
+} sdm_status;
+
+typedef enum { SDM_F32 = 0, SDM_BF16 = 1, SDM_F16 = 2 /* always refused */ } sdm_dtype;
+
+typedef struct {
+  int32_t batch;            /* B >= 0 */
+  int32_t tokens;           /* T >= 0 (exactly 1 for sdm_decode_step) */
+  int32_t heads;            /* H >= 0 */
+  int32_t num_factors;      /* F in [1, 4] */
+  int32_t factor_widths[4]; /* n_f in [1, 4096]; N = prod n_f < 2^31; entries >= F are ignored */
+  int32_t subkey_dim;       /* dk >= 1, F * dk <= 1024 */
+  int32_t head_dim;         /* d in [1, 2^20]; multiple of 4 (float32 bank) or 8 (bfloat16 bank) */
+  int32_t num_writes;       /* W in [1, min(N, 512)] */
+  int32_t num_reads;        /* R in [1, min(N, 512)] */
+  int32_t chunk_size;       /* C in [1, 128], C * W <= 8192 (write/read only) */
+  int32_t act_dtype;        /* sdm_dtype of queries, sub-keys, values, gates and out: F32 or BF16 */
+  int32_t bank_dtype;       /* sdm_dtype of the bank: F32 or BF16 */
+  int64_t bank_rows;        /* rows per stream in the bank buffer, >= N */
+} sdm_config;
+
+enum { SDM_OP_TOPK = 0, SDM_OP_WRITE_READ = 1, SDM_OP_DECODE = 2 };
+
+/* Message for the last non-OK status returned on the calling thread ("" if none). Valid until the next call. */
+const char* sdm_last_error(void);
+
+/* Workspace bytes needed by `op` for `cfg` (k: the top-k size for SDM_OP_TOPK, ignored otherwise).
+ * Validates cfg like the op itself, without the device check. */
+sdm_status sdm_workspace_size(const sdm_config* cfg, int32_t op, int32_t k, size_t* bytes);
+
+/* Exact product-key top-k (CHANGELOG 2.0.0, "Upgrading from v1" and "New"; README package layout: exact
+ * product-key top-k). For every row (b, t, h) of queries [B, T, H, F*dk] (act dtype) against head h's sub-key
+ * tables (subkeys [H, sum n_f, dk], act dtype): the k best slots, best first, as int32 ids idx [B, T, H, k] and
+ * float32 slot scores scores [B, T, H, k] (scores may be NULL). k in [1, min(N, 512)]. Uses cfg's batch, tokens,
+ * heads, factors, subkey_dim and act_dtype; the other fields are not read. */
+sdm_status topk_product_keys(const sdm_config* cfg, const void* queries, const void* subkeys, int32_t k,
+                             int32_t* idx, float* scores, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The chunked write/read (CHANGELOG 2.0.0: one chunked write/read op; README summary). For every stream (b, h),
+ * tokens in order, chunk_size at a time: top-k write slots of write_keys, top-k read slots of read_queries, the
+ * gated delta-rule update of the W write rows with values, forget_gate and input_gate, and the read of the R read
+ * rows into out. `bank` [B, H, bank_rows, d] advances in place. write_idx / read_idx, if not NULL, receive the
+ * selected slot ids. The result equals the one-token-at-a-time recurrence up to floating-point rounding, for any
+ * chunk_size; two calls split at a multiple of chunk_size give the same bits as one call. */
+sdm_status sdm_write_read(const sdm_config* cfg, const void* write_keys, const void* read_queries,
+                          const void* values, const void* forget_gate, const void* input_gate, const void* subkeys,
+                          void* bank, void* out, int32_t* write_idx, int32_t* read_idx, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* Single-token decode step (CHANGELOG 2.0.0 "New": a single-token decode kernel; lumen PR #29: donate). cfg.tokens
+ * must be 1; every stream (b, h) takes one token. bank_out == bank_in: donated, the successor is written in place.
+ * bank_out disjoint from bank_in: copied successor, bank_out receives a full copy of bank_in with the W rows
+ * updated, and bank_in is left unchanged. Partial overlap -> SDM_ERR_ALIAS. Both forms run one body and give
+ * bit-identical bank_out, out and indices. Rows are rounded to the bank dtype before the read. */
+sdm_status sdm_decode_step(const sdm_config* cfg, const void* write_keys, const void* read_queries,
+                           const void* values, const void* forget_gate, const void* input_gate, const void* subkeys,
+                           const void* bank_in, void* bank_out, void* out, int32_t* write_idx, int32_t* read_idx,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Kernel timing (diagnostics, not part of the method). While enabled, every kernel launch of this library is
+ * bracketed by a pair of HIP events recorded on the call's stream. sdm_profile_read waits for the recorded events
+ * and returns, per kernel family, the summed milliseconds (ms) and the number of launches (launches) since timing
+ * was enabled; both arrays have SDM_K_COUNT entries and are owned by the caller. Enabling resets the totals;
+ * disabling drops pending events. Not thread-safe with concurrent calls on other threads. */
+typedef enum {
+  SDM_K_CAND = 0,   /* candidate-tuple table */
+  SDM_K_TOPK = 1,   /* batched exact top-k */
+  SDM_K_PLAN = 2,   /* chunk plan */
+  SDM_K_LOOP = 3,   /* chunk loop: gather, solve, read, scatter */
+  SDM_K_DECODE = 4, /* decode step */
+  SDM_K_COPY = 5,   /* successor copy */
+  SDM_K_COUNT = 6
+} sdm_kernel;
+sdm_status sdm_profile_enable(int32_t on);
+sdm_status sdm_profile_read(double* ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDM_H */

@@ -1,0 +1,138 @@
+"""The C ABI on the host (no GPU): the library loads, exports every function include/sdm.h declares, sizes its
+workspace, and refuses bad calls before any device work with the documented status codes."""
+import ctypes
+import os
+
+import pytest
+
+from gated_delta_rule_product_amd import binding as B
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from gated_delta_rule_product_amd import build
+
+        build.build()
+    return B.load()
+
+
+def test_exports_every_declared_function(lib):
+    names = B.declared_functions()
+    assert set(names) >= {"sdm_last_error", "sdm_workspace_size", "topk_product_keys", "sdm_write_read",
+                          "sdm_decode_step"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_binding_refuses_to_run_without_the_library(monkeypatch):
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", "/nonexistent/libsdm.so")
+    with pytest.raises(RuntimeError):
+        B.load()
+
+
+def _cfg(**kw):
+    base = dict(batch=2, tokens=256, heads=2, widths=(32, 32), subkey_dim=16, head_dim=64, num_writes=4,
+                num_reads=4, chunk_size=64, act_dtype=B.SDM_F32, bank_dtype=B.SDM_F32)
+    base.update(kw)
+    return B.make_config(**base)
+
+
+def _status(cfg, op=B.SDM_OP_WRITE_READ, k=0):
+    n = ctypes.c_size_t(0)
+    return B.load().sdm_workspace_size(ctypes.byref(cfg), op, k, ctypes.byref(n)), n.value
+
+
+def test_workspace_sizes(lib):
+    s, n = _status(_cfg())
+    assert s == B.SDM_OK and n > 0
+    s2, n2 = _status(_cfg(tokens=512))
+    assert s2 == B.SDM_OK and n2 > n
+    s, n = _status(_cfg(), B.SDM_OP_DECODE)
+    assert s == B.SDM_ERR_RANGE  # decode needs tokens == 1
+    s, n = _status(_cfg(tokens=1), B.SDM_OP_DECODE)
+    assert s == B.SDM_OK and n > 0
+    s, n = _status(_cfg(), B.SDM_OP_TOPK, 64)
+    assert s == B.SDM_OK and n > 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(act_dtype=B.SDM_F16), B.SDM_ERR_DTYPE),
+    (dict(bank_dtype=B.SDM_F16), B.SDM_ERR_DTYPE),
+    (dict(act_dtype=7), B.SDM_ERR_DTYPE),
+    (dict(widths=(2, 2, 2, 2, 2)[:4], subkey_dim=400), B.SDM_ERR_RANGE),   # F * dk > 1024
+    (dict(widths=(0, 32)), B.SDM_ERR_RANGE),
+    (dict(widths=(4096, 4096)), B.SDM_ERR_RANGE),                          # N >= 2^31 ... 2^24 fine, see below
+    (dict(num_writes=2000), B.SDM_ERR_RANGE),
+    (dict(num_writes=0), B.SDM_ERR_RANGE),
+    (dict(widths=(2, 2), num_writes=5), B.SDM_ERR_RANGE),                  # more writes than slots
+    (dict(num_reads=1025), B.SDM_ERR_RANGE),
+    (dict(head_dim=(1 << 20) + 4), B.SDM_ERR_RANGE),
+    (dict(head_dim=66), B.SDM_ERR_LAYOUT),
+    (dict(head_dim=68, bank_dtype=B.SDM_BF16), B.SDM_ERR_LAYOUT),
+    (dict(chunk_size=129), B.SDM_ERR_RANGE),
+    (dict(chunk_size=0), B.SDM_ERR_RANGE),
+    (dict(chunk_size=128, num_writes=128, widths=(256, 256)), B.SDM_ERR_RANGE),  # C * W > 8192
+    (dict(bank_rows=1023), B.SDM_ERR_BANK_TOO_SMALL),
+    (dict(tokens=-1), B.SDM_ERR_RANGE),
+])
+def test_refusals(lib, kw, status):
+    if kw.get("widths") == (4096, 4096):
+        # 2^24 slots is fine; a product past 2^31 is not
+        assert _status(_cfg(**kw))[0] == B.SDM_OK
+        kw = dict(widths=(4096, 4096, 256))
+    s, _ = _status(_cfg(**kw))
+    assert s == status, (kw, B.STATUS_NAMES.get(s), B.last_error())
+    assert B.last_error() != ""
+
+
+def test_candidate_limit(lib):
+    # four factors with k = 512 give more than 4096 candidate tuples
+    s, _ = _status(_cfg(widths=(16, 16, 16, 16), num_writes=512, num_reads=4, chunk_size=16))
+    assert s == B.SDM_ERR_RANGE and "candidate" in B.last_error()
+
+
+def _fake(addr):
+    return ctypes.c_void_p(addr)
+
+
+def test_write_read_refuses_before_device_work(lib):
+    cfg = _cfg()
+    n = ctypes.c_size_t(0)
+    assert lib.sdm_workspace_size(ctypes.byref(cfg), B.SDM_OP_WRITE_READ, 0, ctypes.byref(n)) == B.SDM_OK
+    base = 1 << 40  # fake, never dereferenced: every check below fails before any HIP call
+    step = 1 << 32
+    ptrs = [_fake(base + i * step) for i in range(10)]
+    args = lambda p, ws, wsn: (ctypes.byref(cfg), *p, ws, wsn, None)
+    # NULL input
+    p = list(ptrs)
+    p[0] = None
+    assert lib.sdm_write_read(*args(p, ptrs[9], n.value)) == B.SDM_ERR_NULL
+    # workspace too small / misaligned
+    assert lib.sdm_write_read(*args(ptrs[:9] + [None], _fake(base + 20 * step), n.value - 1)) == B.SDM_ERR_WORKSPACE
+    assert lib.sdm_write_read(*args(ptrs[:9] + [None], _fake(base + 20 * step + 8), n.value)) == B.SDM_ERR_WORKSPACE
+    # misaligned bank
+    p = list(ptrs[:9]) + [None]
+    p[6] = _fake(base + 6 * step + 4)
+    assert lib.sdm_write_read(*args(p, _fake(base + 20 * step), n.value)) == B.SDM_ERR_LAYOUT
+    # out overlapping the bank
+    p = list(ptrs[:9]) + [None]
+    p[7] = _fake(base + 6 * step + 4096)
+    assert lib.sdm_write_read(*args(p, _fake(base + 20 * step), n.value)) == B.SDM_ERR_ALIAS
+    # out overlapping an input (values)
+    p = list(ptrs[:9]) + [None]
+    p[7] = p[2]
+    assert lib.sdm_write_read(*args(p, _fake(base + 20 * step), n.value)) == B.SDM_ERR_ALIAS
+    assert "overlaps" in B.last_error()
+
+
+def test_decode_partial_overlap_refused(lib):
+    cfg = _cfg(tokens=1)
+    n = ctypes.c_size_t(0)
+    assert lib.sdm_workspace_size(ctypes.byref(cfg), B.SDM_OP_DECODE, 0, ctypes.byref(n)) == B.SDM_OK
+    base, step = 1 << 40, 1 << 32
+    p = [_fake(base + i * step) for i in range(11)]
+    p[7] = _fake(base + 6 * step + 256)  # bank_out starts inside bank_in
+    st = lib.sdm_decode_step(ctypes.byref(cfg), *p, _fake(base + 20 * step), n.value, None)
+    assert st == B.SDM_ERR_ALIAS and "bank_out" in B.last_error()

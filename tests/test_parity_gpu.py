@@ -1,0 +1,275 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on seeded synthetic inputs.
+
+Bar: slot ids and float32 slot scores bit-exact; outputs and bank rows within 1e-5 (float32) / 2e-2 (bfloat16) of the
+oracle, measured row-wise as max|gpu - ref| <= rtol * max|ref| per output row and per bank row; GPU results bitwise
+repeatable; a donated decode step equal to a copied one bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_delta_rule_product_amd import binding, synth
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+RTOL = {"f32": 1e-5, "bf16": 2e-2}
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def rowwise_rel(got, ref):
+    got = np.asarray(got, np.float64).reshape(-1, got.shape[-1])
+    ref = np.asarray(ref, np.float64).reshape(-1, ref.shape[-1])
+    err = np.abs(got - ref).max(axis=1)
+    scale = np.maximum(np.abs(ref).max(axis=1), 1e-30)
+    return float((err / scale).max())
+
+
+def to_dev(x, dtype):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV).to(dtype)
+
+
+def to_np(t):
+    return t.float().cpu().numpy() if t.dtype != torch.int32 else t.cpu().numpy()
+
+
+def run_gpu(s, x, chunk_size=None, bank=None):
+    at, bt = TORCH_DT[s.act], TORCH_DT[s.bank]
+    t = {k: to_dev(x[k], at) for k in ("wkeys", "rq", "values", "alpha", "beta", "subkeys")}
+    g_bank = to_dev(x["bank"] if bank is None else bank, bt)
+    out, widx, ridx = binding.sdm_write_read(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"], t["subkeys"],
+                                             g_bank, widths=s.widths, num_writes=s.num_writes,
+                                             num_reads=s.num_reads, chunk_size=chunk_size or s.chunk_size,
+                                             want_index=True)
+    torch.cuda.synchronize()
+    return to_np(out), to_np(g_bank), to_np(widx), to_np(ridx)
+
+
+def run_oracle(s, x):
+    return oracle.write_read(x["wkeys"], x["rq"], x["values"], x["alpha"], x["beta"], x["subkeys"], x["bank"],
+                             s.widths, s.num_writes, s.num_reads, bank_bf16=s.bank == "bf16",
+                             act_bf16=s.act == "bf16")
+
+
+def check_parity(s, gpu, ref):
+    out, bank, widx, ridx = gpu
+    assert np.array_equal(widx, ref["widx"]), "write slot ids differ"
+    assert np.array_equal(ridx, ref["ridx"]), "read slot ids differ"
+    e_out = rowwise_rel(out, ref["out"])
+    e_bank = rowwise_rel(bank, ref["bank"])
+    # out is read from bank rows: its tolerance is that of the coarser of its own dtype and the bank dtype
+    assert e_out <= max(RTOL[s.act], RTOL[s.bank]), f"out rel err {e_out}"
+    assert e_bank <= RTOL[s.bank], f"bank rel err {e_bank}"
+    return e_out, e_bank
+
+
+# ------------------------------------------------------------------------------------------------ top-k
+def _topk_case(widths, dk, k, act, kind, B=1, T=24, H=2, seed=0):
+    rng = np.random.default_rng(seed)
+    F = len(widths)
+    if kind == "ternary":
+        q = rng.integers(-1, 2, (B, T, H, F * dk)).astype(np.float32)
+        sub = rng.integers(-1, 2, (H, sum(widths), dk)).astype(np.float32)
+    else:
+        q = rng.standard_normal((B, T, H, F * dk)).astype(np.float32)
+        sub = rng.standard_normal((H, sum(widths), dk)).astype(np.float32)
+        if kind == "dup":
+            for _ in range(sum(widths) // 3):
+                i, j = rng.integers(0, sum(widths), 2)
+                sub[:, j] = sub[:, i]
+    if act == "bf16":
+        q, sub = synth.round_bf16_rne(q), synth.round_bf16_rne(sub)
+    ids, sc = binding.topk_product_keys(to_dev(q, TORCH_DT[act]), to_dev(sub, TORCH_DT[act]), widths, k)
+    torch.cuda.synchronize()
+    rid, rsc = oracle.topk(q, sub, widths, k)
+    assert np.array_equal(ids.cpu().numpy(), rid)
+    assert np.array_equal(sc.cpu().numpy(), rsc)
+
+
+@pytest.mark.parametrize("widths,dk,k", [((32, 32), 16, 4), ((32, 32), 16, 64), ((8, 8), 4, 5), ((4, 3, 5), 3, 7),
+                                         ((16,), 4, 6), ((3, 2, 2, 3), 2, 9), ((7, 9), 5, 63), ((64, 32, 32), 8, 64)])
+@pytest.mark.parametrize("kind", ["random", "ternary", "dup"])
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_topk_exact(widths, dk, k, kind, act):
+    print(f"topk widths={widths} dk={dk} k={k} kind={kind} act={act}", flush=True)
+    _topk_case(widths, dk, k, act, kind)
+
+
+def test_topk_zero_query_tie_order():
+    q = np.zeros((1, 1, 1, 2 * 8), np.float32)
+    sub = np.random.default_rng(0).standard_normal((1, 64, 8)).astype(np.float32)
+    ids, sc = binding.topk_product_keys(to_dev(q, torch.float32), to_dev(sub, torch.float32), (32, 32), 4)
+    assert ids.cpu().numpy().ravel().tolist() == [0, 1, 32, 2]
+
+
+@pytest.mark.parametrize("name", ["layer_65k", "three_factor_65k", "large_1m"])
+def test_topk_full_size_factors_sampled(name):
+    """The full-size factor tables (65,536 and 1,048,576 slots) on sampled token rows."""
+    s = synth.WORKLOADS[name]
+    x = synth.make_step_inputs(s.with_(tokens=8))
+    sub = synth.make_subkeys(s)
+    print(f"topk full-size {name}", flush=True)
+    for key in ("wkeys", "rq"):
+        ids, sc = binding.topk_product_keys(to_dev(x[key], TORCH_DT[s.act]), to_dev(sub, TORCH_DT[s.act]), s.widths,
+                                            s.num_writes)
+        torch.cuda.synchronize()
+        rid, rsc = oracle.topk(x[key], sub, s.widths, s.num_writes)
+        assert np.array_equal(ids.cpu().numpy(), rid)
+        assert np.array_equal(sc.cpu().numpy(), rsc)
+
+
+# ------------------------------------------------------------------------------------------------ write / read
+def test_write_read_tiny():
+    s = synth.WORKLOADS["tiny_1k"]
+    x = synth.make_inputs(s)
+    print("write/read tiny_1k", flush=True)
+    e = check_parity(s, run_gpu(s, x), run_oracle(s, x))
+    print("errors", e)
+
+
+@pytest.mark.parametrize("chunk", [1, 7, 16, 64, 128])
+def test_write_read_chunk_sizes_ragged(chunk):
+    """chunk_size changes results only through rounding; T = 200 leaves a ragged last chunk."""
+    s = synth.WORKLOADS["tiny_1k"].with_(tokens=200, batch=2, heads=2, chunk_size=chunk)
+    x = synth.make_inputs(s, seed=3)
+    print(f"write/read chunk={chunk}", flush=True)
+    check_parity(s, run_gpu(s, x), run_oracle(s, x))
+
+
+@pytest.mark.parametrize("act,bank", [("bf16", "f32"), ("bf16", "bf16"), ("f32", "bf16")])
+def test_write_read_dtypes(act, bank):
+    s = synth.WORKLOADS["tiny_1k"].with_(tokens=130, batch=2, act=act, bank=bank, head_dim=64, chunk_size=32)
+    x = synth.make_inputs(s, seed=4)
+    print(f"write/read act={act} bank={bank}", flush=True)
+    check_parity(s, run_gpu(s, x), run_oracle(s, x))
+
+
+def test_write_read_collisions_heavy():
+    """A tiny bank (64 slots, W = R = 16) makes most writes collide inside a chunk."""
+    s = synth.Shape(1, 96, 2, (8, 8), 4, 32, 16, 16, 32, name="collide")
+    x = synth.make_inputs(s, seed=5)
+    print("write/read collisions", flush=True)
+    check_parity(s, run_gpu(s, x), run_oracle(s, x))
+
+
+def test_write_read_dense_limit():
+    """W = R = N: every slot is written and read by every token (Gated DeltaNet in slot space)."""
+    s = synth.Shape(1, 40, 1, (4, 4), 3, 16, 16, 16, 8, name="dense")
+    x = synth.make_inputs(s, seed=6)
+    print("write/read dense limit", flush=True)
+    check_parity(s, run_gpu(s, x), run_oracle(s, x))
+
+
+def test_write_read_three_factors_small():
+    s = synth.Shape(1, 80, 2, (8, 4, 4), 8, 32, 16, 12, 16, "bf16", "bf16", name="f3")
+    x = synth.make_inputs(s, seed=7)
+    print("write/read three factors", flush=True)
+    check_parity(s, run_gpu(s, x), run_oracle(s, x))
+
+
+def test_write_read_bank_rows_padding():
+    """bank_rows > N: rows past N are never touched."""
+    s = synth.WORKLOADS["tiny_1k"].with_(tokens=64, bank_rows=1100)
+    x = synth.make_inputs(s, seed=8)
+    out, bank, widx, ridx = run_gpu(s, x)
+    assert np.array_equal(bank[:, :, 1024:], x["bank"][:, :, 1024:])
+    ref = run_oracle(s, x)
+    check_parity(s, (out, bank, widx, ridx), ref)
+
+
+def test_write_read_bitwise_repeatable():
+    s = synth.WORKLOADS["tiny_1k"].with_(tokens=192, batch=2, heads=2)
+    x = synth.make_inputs(s, seed=9)
+    a = run_gpu(s, x)
+    b = run_gpu(s, x)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+def test_write_read_split_at_chunk_multiple_is_bitwise():
+    s = synth.WORKLOADS["tiny_1k"].with_(tokens=256, chunk_size=32)
+    x = synth.make_inputs(s, seed=10)
+    full = run_gpu(s, x)
+    h = 96
+    first = {k: (v[:, :h] if k in ("wkeys", "rq", "values", "alpha", "beta") else v) for k, v in x.items()}
+    second = {k: (v[:, h:] if k in ("wkeys", "rq", "values", "alpha", "beta") else v) for k, v in x.items()}
+    o1, b1, w1, r1 = run_gpu(s.with_(tokens=h), first)
+    o2, b2, w2, r2 = run_gpu(s.with_(tokens=256 - h), second, bank=b1)
+    assert np.array_equal(np.concatenate([o1, o2], 1), full[0])
+    assert np.array_equal(b2, full[1])
+    assert np.array_equal(np.concatenate([w1, w2], 1), full[2])
+
+
+def test_write_read_empty_tokens():
+    s = synth.WORKLOADS["tiny_1k"].with_(tokens=0)
+    x = synth.make_inputs(s)
+    out, bank, widx, ridx = run_gpu(s, x)
+    assert out.shape[1] == 0 and np.array_equal(bank, x["bank"])
+
+
+# ------------------------------------------------------------------------------------------------ decode
+def _decode_inputs(s, step):
+    x = synth.make_step_inputs(s, seed=0, step=step)
+    return {k: to_dev(v, TORCH_DT[s.act]) for k, v in x.items()}, x
+
+
+@pytest.mark.parametrize("bank_dt", ["f32", "bf16"])
+def test_decode_matches_oracle_and_donated_equals_copied(bank_dt):
+    s = synth.WORKLOADS["decode_b128"].with_(batch=16, bank=bank_dt)
+    sub_np = synth.make_subkeys(s)
+    bank_np = synth.make_bank(s)
+    sub = to_dev(sub_np, TORCH_DT[s.act])
+    bank_d = to_dev(bank_np, TORCH_DT[bank_dt])   # donated chain
+    bank_c = bank_d.clone()                         # copied chain
+    ref_bank = bank_np
+    print(f"decode bank={bank_dt}", flush=True)
+    for step in range(6):
+        t, x = _decode_inputs(s, step)
+        args = (t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"], sub)
+        kw = dict(widths=s.widths, num_writes=s.num_writes, num_reads=s.num_reads, want_index=True)
+        od, wd, rd, bd = binding.sdm_decode_step(*args, bank_d, **kw)
+        succ = torch.empty_like(bank_c)
+        prev = bank_c.clone()
+        oc, wc, rc, bc = binding.sdm_decode_step(*args, bank_c, succ, **kw)
+        torch.cuda.synchronize()
+        assert bd.data_ptr() == bank_d.data_ptr()          # in place
+        assert torch.equal(bank_c, prev)                    # predecessor untouched
+        assert torch.equal(od, oc) and torch.equal(wd, wc) and torch.equal(rd, rc)
+        assert torch.equal(bd, bc)
+        bank_c = bc
+        ref = oracle.write_read(x["wkeys"], x["rq"], x["values"], x["alpha"], x["beta"], sub_np, ref_bank,
+                                s.widths, s.num_writes, s.num_reads, bank_bf16=bank_dt == "bf16")
+        assert np.array_equal(wd.cpu().numpy(), ref["widx"]) and np.array_equal(rd.cpu().numpy(), ref["ridx"])
+        assert rowwise_rel(to_np(od), ref["out"]) <= RTOL[s.act]
+        assert rowwise_rel(to_np(bd), ref["bank"]) <= RTOL[bank_dt]
+        ref_bank = ref["bank"]
+
+
+def test_decode_equals_one_token_write_read():
+    s = synth.WORKLOADS["tiny_1k"].with_(tokens=1, batch=3, heads=2)
+    x = synth.make_inputs(s, seed=11)
+    o1, b1, w1, r1 = run_gpu(s, x)
+    t = {k: to_dev(x[k], torch.float32) for k in ("wkeys", "rq", "values", "alpha", "beta", "subkeys")}
+    bank = to_dev(x["bank"], torch.float32)
+    out, widx, ridx, _ = binding.sdm_decode_step(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"],
+                                                 t["subkeys"], bank, widths=s.widths, num_writes=s.num_writes,
+                                                 num_reads=s.num_reads, want_index=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(widx.cpu().numpy(), w1) and np.array_equal(ridx.cpu().numpy(), r1)
+    assert rowwise_rel(to_np(out), o1) <= 1e-5
+    assert rowwise_rel(to_np(bank), b1) <= 1e-5
+
+
+# ------------------------------------------------------------------------------------------------ full size
+def test_layer_65k_full_size():
+    """The 65,536-slot layer workload (B 2, T 4096, H 2, d 1024, W = R = 64, chunk 64, bf16 on a float32 bank),
+    every output row and every bank row against the oracle."""
+    s = synth.WORKLOADS["layer_65k"]
+    print("full-size layer_65k: generating inputs", flush=True)
+    x = synth.make_inputs(s)
+    print("full-size layer_65k: GPU", flush=True)
+    gpu = run_gpu(s, x)
+    print("full-size layer_65k: oracle", flush=True)
+    ref = run_oracle(s, x)
+    e = check_parity(s, gpu, ref)
+    print("full-size layer_65k errors", e, flush=True)
