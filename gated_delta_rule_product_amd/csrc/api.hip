@@ -178,27 +178,16 @@ WsLayout layout(const Dims& D, int op) {
     o = align256(o + bytes);
     return r;
   };
-  L.cand_w = take(MAX_CAND * 8);
-  L.cand_r = take(MAX_CAND * 8);
+  L.cand = take(2 * MAX_CAND * 8);
   if (op == SDM_OP_WRITE_READ) {
     const size_t nw = (size_t)D.S * D.T * D.W, nr = (size_t)D.S * D.T * D.R;
     const size_t nc = (size_t)D.S * D.nch;
-    const size_t CW = (size_t)chunk_events(D);
     L.widx = take(nw * 4);
     L.wwt = take(nw * 4);
     L.ridx = take(nr * 4);
     L.rwt = take(nr * 4);
-    L.wcoef = take(nw * 4);
-    L.rcoef = take(nr * 4);
-    L.wlast = take(nw * 4);
-    L.nseg = take(nc * 4);
-    L.seg_slot = take(nc * CW * 4);
-    L.seg_start = take(nc * (CW + 1) * 4);
-    L.ev = take(nc * CW * sizeof(Ev));
-    L.lptr = take(nc * (D.C + 1) * 4);
-    L.lent = take(nc * (size_t)chunk_lents(D) * sizeof(Ent));
-    L.qptr = take(nc * (D.C + 1) * 4);
-    L.qent = take(nc * (size_t)chunk_qents(D) * sizeof(Ent));
+    L.chunks = take(nc * (size_t)chunk_layout(D.C, D.W, D.R).bytes);
+    L.counts = take(nc * sizeof(ChunkCounts));
   }
   L.total = o;
   return L;
@@ -342,13 +331,13 @@ sdm_status topk_product_keys(const sdm_config* cfg, const void* queries, const v
   if (rows == 0) return ok();
   hipStream_t st = (hipStream_t)stream;
   unsigned char* ws = (unsigned char*)workspace;
-  TRY(hip_status(timed(SDM_K_CAND, st, [&] { return launch_cand_table(P, D.F, (uint64_t*)(ws + L.cand_w), st); }),
+  TRY(hip_status(timed(SDM_K_CAND, st, [&] { return launch_cand_tables(&P, 1, D.F, (uint64_t*)(ws + L.cand), st); }),
                  "candidate table launch"));
   TopkArgs a;
   memset(&a, 0, sizeof a);
   a.queries[0] = queries;
   a.subkeys = subkeys;
-  a.cand[0] = (const uint64_t*)(ws + L.cand_w);
+  a.cand[0] = (const uint64_t*)(ws + L.cand);
   a.plan[0] = P;
   a.nkinds = 1;
   a.stream_major = 0;
@@ -400,17 +389,16 @@ sdm_status sdm_write_read(const sdm_config* cfg, const void* write_keys, const v
   if (rows == 0) return ok();
   hipStream_t st = (hipStream_t)stream;
   unsigned char* ws = (unsigned char*)workspace;
-  TRY(hip_status(timed(SDM_K_CAND, st, [&] { return launch_cand_table(pw, D.F, (uint64_t*)(ws + L.cand_w), st); }),
-                 "candidate table launch"));
-  TRY(hip_status(timed(SDM_K_CAND, st, [&] { return launch_cand_table(pr, D.F, (uint64_t*)(ws + L.cand_r), st); }),
+  const TopkPlan plans[2] = {pw, pr};
+  TRY(hip_status(timed(SDM_K_CAND, st, [&] { return launch_cand_tables(plans, 2, D.F, (uint64_t*)(ws + L.cand), st); }),
                  "candidate table launch"));
   TopkArgs ta;
   memset(&ta, 0, sizeof ta);
   ta.queries[0] = write_keys;
   ta.queries[1] = read_queries;
   ta.subkeys = subkeys;
-  ta.cand[0] = (const uint64_t*)(ws + L.cand_w);
-  ta.cand[1] = (const uint64_t*)(ws + L.cand_r);
+  ta.cand[0] = (const uint64_t*)(ws + L.cand);
+  ta.cand[1] = (const uint64_t*)(ws + L.cand) + MAX_CAND;
   ta.plan[0] = pw;
   ta.plan[1] = pr;
   ta.nkinds = 2;
@@ -429,34 +417,15 @@ sdm_status sdm_write_read(const sdm_config* cfg, const void* write_keys, const v
   pa.rwt = (const float*)(ws + L.rwt);
   pa.alpha = forget_gate;
   pa.beta = input_gate;
-  pa.wcoef = (float*)(ws + L.wcoef);
-  pa.rcoef = (float*)(ws + L.rcoef);
-  pa.wlast = (int32_t*)(ws + L.wlast);
-  pa.nseg = (int32_t*)(ws + L.nseg);
-  pa.seg_slot = (int32_t*)(ws + L.seg_slot);
-  pa.seg_start = (int32_t*)(ws + L.seg_start);
-  pa.ev = (Ev*)(ws + L.ev);
-  pa.lptr = (int32_t*)(ws + L.lptr);
-  pa.lent = (Ent*)(ws + L.lent);
-  pa.qptr = (int32_t*)(ws + L.qptr);
-  pa.qent = (Ent*)(ws + L.qent);
+  pa.chunks = ws + L.chunks;
+  pa.counts = (ChunkCounts*)(ws + L.counts);
   TRY(hip_status(timed(SDM_K_PLAN, st, [&] { return launch_plan(D, pa, st); }), "chunk plan launch"));
   LoopArgs la;
-  la.widx = pa.widx;
-  la.wcoef = pa.wcoef;
-  la.ridx = pa.ridx;
-  la.rcoef = pa.rcoef;
   la.alpha = forget_gate;
   la.beta = input_gate;
   la.values = values;
-  la.nseg = pa.nseg;
-  la.seg_slot = pa.seg_slot;
-  la.seg_start = pa.seg_start;
-  la.ev = pa.ev;
-  la.lptr = pa.lptr;
-  la.lent = pa.lent;
-  la.qptr = pa.qptr;
-  la.qent = pa.qent;
+  la.chunks = pa.chunks;
+  la.counts = pa.counts;
   la.bank = bank;
   la.out = out;
   TRY(hip_status(timed(SDM_K_LOOP, st, [&] { return launch_loop(D, la, st); }), "chunk loop launch"));
@@ -509,9 +478,8 @@ sdm_status sdm_decode_step(const sdm_config* cfg, const void* write_keys, const 
   if (rows == 0) return ok();
   hipStream_t st = (hipStream_t)stream;
   unsigned char* ws = (unsigned char*)workspace;
-  TRY(hip_status(timed(SDM_K_CAND, st, [&] { return launch_cand_table(pw, D.F, (uint64_t*)(ws + L.cand_w), st); }),
-                 "candidate table launch"));
-  TRY(hip_status(timed(SDM_K_CAND, st, [&] { return launch_cand_table(pr, D.F, (uint64_t*)(ws + L.cand_r), st); }),
+  const TopkPlan plans[2] = {pw, pr};
+  TRY(hip_status(timed(SDM_K_CAND, st, [&] { return launch_cand_tables(plans, 2, D.F, (uint64_t*)(ws + L.cand), st); }),
                  "candidate table launch"));
   if (!donated)
     TRY(hip_status(timed(SDM_K_COPY, st, [&] { return launch_copy(bank_in, bank_out, bank_bytes, st); }),
@@ -528,8 +496,8 @@ sdm_status sdm_decode_step(const sdm_config* cfg, const void* write_keys, const 
   a.out = out;
   a.widx = write_idx;
   a.ridx = read_idx;
-  a.cand[0] = (const uint64_t*)(ws + L.cand_w);
-  a.cand[1] = (const uint64_t*)(ws + L.cand_r);
+  a.cand[0] = (const uint64_t*)(ws + L.cand);
+  a.cand[1] = (const uint64_t*)(ws + L.cand) + MAX_CAND;
   a.plan[0] = pw;
   a.plan[1] = pr;
   TRY(hip_status(timed(SDM_K_DECODE, st, [&] { return launch_decode(D, a, st); }), "decode launch"));

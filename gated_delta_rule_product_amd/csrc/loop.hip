@@ -3,13 +3,19 @@
 // Column slices of the bank are independent (every coefficient comes from the bank-independent plan), so one
 // workgroup owns one (stream, 64-byte column slice) pair and runs every chunk of its stream in order with no
 // synchronisation beyond its own barriers. Per chunk (notation of plan.hip):
-//   A  gather  H[t] = sum_i a_ti M_0[S_ti],  G[t] = sum_i b_ti M_0[R_ti]           (HBM: W + R row slices/token)
-//   B  solve   delta_t = beta_t v_t - alpha_t beta_t H[t] - sum_m L_tm delta_m      (forward substitution)
-//   C  read    out_t = G[t] + sum_s Q_ts delta_s                                   (act dtype)
+//   A  gather  H[t] = sum_i a_ti M_0[S_ti],  G[t] = sum_i b_ti M_0[R_ti]     (HBM: W + R row slices per token)
+//   B  solve   U_t = beta_t v_t - alpha_t beta_t H[t];  delta_t = sum_s T_ts U_s      (T from the plan)
+//   C  read    out_t = G[t] + sum_s Q_ts delta_s                             (act dtype)
 //   D  scatter per written slot j, its events in token order: M[j] <- alpha_s M[j] + w_sj delta_s, one read and
-//              one write of the row slice, rounded once to the bank dtype            (HBM: W row slices/token)
-// Each group of 4 lanes moves one 64-byte row slice (16 bytes per lane). Blocks are mapped so that neighbouring
-// column slices of a stream run on the same XCD and share its L2 (a 128-byte L2 line holds two 64-byte slices).
+//              one write of the row slice, rounded once to the bank dtype      (HBM: W row slices per token)
+// A group of 4 lanes moves one 64-byte row slice (16 bytes per lane). In phase A each group accumulates one token's
+// terms in order (no cross-lane reduction), with its row loads back to back. Blocks are mapped so that
+// neighbouring column slices of a stream run on the same XCD and share its L2 (a 128-byte L2 line holds two
+// 64-byte slices).
+//
+// Two variants: STAGED copies each chunk's plan region into LDS with one coalesced pass (the scatter part is
+// prefetched into registers during the solve); the direct variant reads it from global memory (used when the
+// region does not fit in LDS, e.g. chunk 128).
 #include "sdm_internal.h"
 
 namespace sdm {
@@ -42,17 +48,33 @@ template <> struct Lane<bf16_t> {
   }
 };
 
-template <typename A, typename Bk>
+constexpr int PREF = 8;  // uint4 per thread of register prefetch (64 KiB per 512-thread block)
+
+__host__ __device__ inline size_t loop_region_lds(int C, int W, int R) {
+  const ChunkLayout CL = chunk_layout(C, W, R);
+  const long long r1 = CL.pairs_bytes + CL.ptrs_bytes + CL.lists_cap;
+  return (size_t)(r1 > CL.scat_cap ? r1 : CL.scat_cap);
+}
+
+__host__ __device__ inline size_t loop_lds_bytes(int C, int W, int R, int cols, bool staged) {
+  size_t n = (size_t)C * cols * 4 * 3 + (size_t)C * 8;
+  if (staged) n = align16(n) + loop_region_lds(C, W, R);
+  return n;
+}
+
+template <typename A, typename Bk, bool STAGED>
 __global__ __launch_bounds__(LOOP_NT) void loop_kernel(Dims D, LoopArgs a, int nslices) {
   constexpr int EPL = Lane<Bk>::EPL;
   constexpr int COLS = 4 * EPL;  // columns per 64-byte slice
   constexpr int NW = LOOP_NT / 64;
   extern __shared__ __align__(16) unsigned char lds[];
-  float* sH = (float*)lds;              // [C][COLS]
-  float* sG = sH + D.C * COLS;          // [C][COLS]
-  float* sD = sG + D.C * COLS;          // [C][COLS]
-  float* sA = sD + D.C * COLS;          // [C]
-  float* sB = sA + D.C;                 // [C]
+  const int C = D.C, W = D.W, R = D.R;
+  float* sH = (float*)lds;              // [C][COLS]  H, then U
+  float* sG = sH + C * COLS;            // [C][COLS]
+  float* sD = sG + C * COLS;            // [C][COLS]  delta
+  float* sA = sD + C * COLS;            // [C]
+  float* sB = sA + C;                   // [C]
+  unsigned char* sReg = lds + align16((long long)C * COLS * 4 * 3 + (long long)C * 8);
 
   // XCD-aware mapping: blocks b, b+8, b+16, ... run on one XCD; give them consecutive work units.
   const int nblk = gridDim.x;
@@ -71,112 +93,151 @@ __global__ __launch_bounds__(LOOP_NT) void loop_kernel(Dims D, LoopArgs a, int n
   const A* beta = (const A*)a.beta;
   const A* values = (const A*)a.values;
   A* out = (A*)a.out;
-  const int W = D.W, R = D.R, C = D.C;
+  const ChunkLayout CL = chunk_layout(C, W, R);
   const long long CW = (long long)C * W;
-  const long long lcap = chunk_lents(D), qcap = chunk_qents(D);
 
+  ChunkCounts cnt = a.counts[(long long)st * D.nch];
   for (int ch = 0; ch < D.nch; ++ch) {
     const int t0 = ch * C;
     const int Cc = min(C, D.T - t0);
     const long long cidx = (long long)st * D.nch + ch;
+    const unsigned char* greg = a.chunks + cidx * CL.bytes;
+    const ChunkCounts next = a.counts[ch + 1 < D.nch ? cidx + 1 : cidx];
+    // region pointers (LDS copy or global)
+    const unsigned char* reg = greg;
+    if (STAGED) {
+      const int n16 = (int)((CL.pairs_bytes + CL.ptrs_bytes + (long long)(cnt.nnzT + cnt.nnzQ) * 8 + 15) >> 4);
+      const uint4* src = (const uint4*)greg;
+      uint4* dst = (uint4*)sReg;
+      for (int i = tid; i < n16; i += LOOP_NT) dst[i] = src[i];
+      reg = sReg;
+    }
     for (int t = tid; t < Cc; t += LOOP_NT) {
       const long long g = ((long long)b * D.T + t0 + t) * D.H + h;
       sA[t] = to_f<A>(alpha[g]);
       sB[t] = to_f<A>(beta[g]);
     }
-    // A: gathers, one token per wave at a time.
-    for (int t = wv; t < Cc; t += NW) {
-      const long long wrow = ((long long)st * D.T + t0 + t) * W;
-      const long long rrow = ((long long)st * D.T + t0 + t) * R;
-      float accH[EPL], accG[EPL];
+    if (STAGED) __syncthreads();
+    const Pair* pw = (const Pair*)(reg + CL.pairs);
+    const Pair* pr = pw + CW;
+    const int32_t* tptr = (const int32_t*)(reg + CL.ptrs);
+    const int32_t* qptr = tptr + (C + 1);
+    const Ent* lists = (const Ent*)(reg + CL.lists);
+
+    // A: gathers. Waves 0..3 take the write terms (H), waves 4..7 the read terms (G); group = token.
+    {
+      const int kind = wv >> 2;
+      const int n = kind ? R : W;
+      const Pair* base = kind ? pr : pw;
+      float* dst = kind ? sG : sH;
+      for (int t = (wv & 3) * 16 + grp; t < Cc; t += 64) {
+        float acc[EPL];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) accH[e] = accG[e] = 0.0f;
-      if (valid) {
-#pragma unroll 4
-        for (int i = grp; i < W; i += 16) {
-          const int slot = a.widx[wrow + i];
-          const float cf = a.wcoef[wrow + i];
-          float v[EPL];
-          Lane<Bk>::load(bank + (long long)slot * D.d + mycol, v);
+        for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
+        if (valid) {
+          const Pair* pp = base + (long long)t * n;
+#pragma unroll 16
+          for (int i = 0; i < n; ++i) {
+            const Pair p = pp[i];
+            float v[EPL];
+            Lane<Bk>::load(bank + (long long)p.slot * D.d + mycol, v);
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) accH[e] += cf * v[e];
+            for (int e = 0; e < EPL; ++e) acc[e] += p.coef * v[e];
+          }
         }
-#pragma unroll 4
-        for (int i = grp; i < R; i += 16) {
-          const int slot = a.ridx[rrow + i];
-          const float cf = a.rcoef[rrow + i];
-          float v[EPL];
-          Lane<Bk>::load(bank + (long long)slot * D.d + mycol, v);
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) accG[e] += cf * v[e];
-        }
+        for (int e = 0; e < EPL; ++e) dst[t * COLS + q * EPL + e] = acc[e];
       }
-      // reduce over the 16 groups of the wave (lanes with equal q), fixed order
+    }
+    // prefetch the scatter part of the plan region into registers while the solve runs
+    uint4 pf[PREF];
+    const int s16 = (int)(((long long)(cnt.nseg + cnt.nev) * 8 + 15) >> 4);
+    if (STAGED) {
+      const uint4* src = (const uint4*)(greg + CL.scat);
 #pragma unroll
-      for (int off = 4; off < 64; off <<= 1) {
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          accH[e] += __shfl_xor(accH[e], off);
-          accG[e] += __shfl_xor(accG[e], off);
-        }
-      }
-      if (grp == 0) {
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          sH[t * COLS + q * EPL + e] = accH[e];
-          sG[t * COLS + q * EPL + e] = accG[e];
-        }
+      for (int k = 0; k < PREF; ++k) {
+        const int i = tid + k * LOOP_NT;
+        if (i < s16) pf[k] = src[i];
       }
     }
     __syncthreads();
-    // B: forward substitution, one thread per column.
-    if (tid < COLS && col0 + tid < D.d) {
-      const int c = tid;
-      const int32_t* lp = a.lptr + cidx * (C + 1);
-      const Ent* le = a.lent + cidx * lcap;
-      for (int t = 0; t < Cc; ++t) {
+    // B: U = beta v - alpha beta H (in place), then delta = T U.
+    for (int idx = tid; idx < Cc * COLS; idx += LOOP_NT) {
+      const int t = idx / COLS, c = idx % COLS;
+      if (col0 + c < D.d) {
         const long long g = ((long long)b * D.T + t0 + t) * D.H + h;
         const float v = to_f<A>(values[g * D.d + col0 + c]);
-        float u = sB[t] * v - sA[t] * sB[t] * sH[t * COLS + c];
-        for (int e = lp[t]; e < lp[t + 1]; ++e) u -= le[e].val * sD[le[e].col * COLS + c];
-        sD[t * COLS + c] = u;
+        sH[idx] = sB[t] * v - sA[t] * sB[t] * sH[idx];
       }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < Cc * COLS; idx += LOOP_NT) {
+      const int t = idx / COLS, c = idx % COLS;
+      float d = 0.0f;
+      for (int e = tptr[t]; e < tptr[t + 1]; ++e) d += lists[e].val * sH[lists[e].col * COLS + c];
+      sD[idx] = d;
     }
     __syncthreads();
     // C: read output.
-    {
-      const int32_t* qp = a.qptr + cidx * (C + 1);
-      const Ent* qe = a.qent + cidx * qcap;
-      for (int idx = tid; idx < Cc * COLS; idx += LOOP_NT) {
-        const int t = idx / COLS, c = idx % COLS;
-        if (col0 + c < D.d) {
-          float o = sG[t * COLS + c];
-          for (int e = qp[t]; e < qp[t + 1]; ++e) o += qe[e].val * sD[qe[e].col * COLS + c];
-          const long long g = ((long long)b * D.T + t0 + t) * D.H + h;
-          out[g * D.d + col0 + c] = from_f<A>(o);
-        }
+    for (int idx = tid; idx < Cc * COLS; idx += LOOP_NT) {
+      const int t = idx / COLS, c = idx % COLS;
+      if (col0 + c < D.d) {
+        float o = sG[idx];
+        for (int e = qptr[t]; e < qptr[t + 1]; ++e) o += lists[e].val * sD[lists[e].col * COLS + c];
+        const long long g = ((long long)b * D.T + t0 + t) * D.H + h;
+        out[g * D.d + col0 + c] = from_f<A>(o);
       }
     }
     // D: in-order segmented scatter, one 64-byte row slice per group of 4 lanes.
-    if (valid) {
-      const int nseg = a.nseg[cidx];
-      const int32_t* sslot = a.seg_slot + cidx * CW;
-      const int32_t* sst = a.seg_start + cidx * (CW + 1);
-      const Ev* ev = a.ev + cidx * CW;
-#pragma unroll 2
-      for (int sg = wv * 16 + grp; sg < nseg; sg += NW * 16) {
-        Bk* p = bank + (long long)sslot[sg] * D.d + mycol;
-        float m[EPL];
-        Lane<Bk>::load(p, m);
-        for (int e = sst[sg]; e < sst[sg + 1]; ++e) {
-          const Ev x = ev[e];
-          const float al = sA[x.tok];
+    const Seg* segs = (const Seg*)(greg + CL.scat);
+    if (STAGED) {
+      __syncthreads();  // the LDS region is reused
+      uint4* dst = (uint4*)sReg;
 #pragma unroll
-          for (int k = 0; k < EPL; ++k) m[k] = al * m[k] + x.w * sD[x.tok * COLS + q * EPL + k];
+      for (int k = 0; k < PREF; ++k) {
+        const int i = tid + k * LOOP_NT;
+        if (i < s16) dst[i] = pf[k];
+      }
+      const uint4* src = (const uint4*)(greg + CL.scat);
+      for (int i = tid + PREF * LOOP_NT; i < s16; i += LOOP_NT) dst[i] = src[i];
+      __syncthreads();
+      segs = (const Seg*)sReg;
+    }
+    const Ev* ev = (const Ev*)(segs + cnt.nseg);
+    if (valid) {
+      constexpr int UB = 4;
+      for (int sg0 = wv * 16 + grp; sg0 < cnt.nseg; sg0 += NW * 16 * UB) {
+        float m[UB][EPL];
+        int beg[UB], end[UB];
+        Bk* p[UB];
+#pragma unroll
+        for (int u = 0; u < UB; ++u) {
+          const int sg = sg0 + u * NW * 16;
+          beg[u] = end[u] = 0;
+          p[u] = nullptr;
+          if (sg < cnt.nseg) {
+            const Seg sgm = segs[sg];
+            beg[u] = sg > 0 ? segs[sg - 1].end : 0;
+            end[u] = sgm.end;
+            p[u] = bank + (long long)sgm.slot * D.d + mycol;
+            Lane<Bk>::load(p[u], m[u]);
+          }
         }
-        Lane<Bk>::store(p, m);
+#pragma unroll
+        for (int u = 0; u < UB; ++u) {
+          if (p[u]) {
+            for (int e = beg[u]; e < end[u]; ++e) {
+              const Ev x = ev[e];
+              const float al = sA[x.tok];
+#pragma unroll
+              for (int k = 0; k < EPL; ++k) m[u][k] = al * m[u][k] + x.w * sD[x.tok * COLS + q * EPL + k];
+            }
+            Lane<Bk>::store(p[u], m[u]);
+          }
+        }
       }
     }
+    cnt = next;
     __syncthreads();
   }
 }
@@ -186,8 +247,15 @@ static hipError_t launch_loop_t(const Dims& D, const LoopArgs& a, hipStream_t st
   constexpr int COLS = 4 * Lane<Bk>::EPL;
   const int nslices = (D.d + COLS - 1) / COLS;
   const long long nblk = (long long)D.S * nslices;
-  const size_t lds = (size_t)D.C * COLS * 4 * 3 + (size_t)D.C * 8;
-  hipLaunchKernelGGL((loop_kernel<A, Bk>), dim3((unsigned)nblk), dim3(LOOP_NT), lds, st, D, a, nslices);
+  const size_t staged = loop_lds_bytes(D.C, D.W, D.R, COLS, true);
+  if (staged <= 150 * 1024) {
+    (void)hipFuncSetAttribute((const void*)loop_kernel<A, Bk, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)staged);
+    hipLaunchKernelGGL((loop_kernel<A, Bk, true>), dim3((unsigned)nblk), dim3(LOOP_NT), staged, st, D, a, nslices);
+  } else {
+    const size_t lds = loop_lds_bytes(D.C, D.W, D.R, COLS, false);
+    hipLaunchKernelGGL((loop_kernel<A, Bk, false>), dim3((unsigned)nblk), dim3(LOOP_NT), lds, st, D, a, nslices);
+  }
   return hipGetLastError();
 }
 

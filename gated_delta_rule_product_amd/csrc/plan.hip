@@ -1,18 +1,21 @@
 // Chunk plan: everything of a chunk that does not depend on the bank, for every (stream, chunk) in parallel.
 //
 // Chunked form of the per-token recurrence (gated delta rule restricted to the selected rows; sparse-delta-memory
-// CHANGELOG.md 2.0.0: a chunked write/read whose chunk size changes results only through rounding, an IEEE-float32
-// triangular ("WY") solve and a "dual" product inside the op). For a chunk of tokens 0..C-1 with bank M_0 at its
-// start, let gamma_j(s -> t) be the product of alpha_u over the chunk's tokens u in (s, t] that write slot j. Then
+// CHANGELOG.md 2.0.0: a chunked write/read whose chunk size changes results only through rounding, with an
+// IEEE-float32 triangular ("WY") solve and a "dual" product inside the op). For a chunk of tokens 0..C-1 with bank
+// M_0 at its start, let gamma_j(s -> t) be the product of alpha_u over the chunk's tokens u in (s, t] that write
+// slot j. Then
 //   h_t = sum_{j in S_t} w_tj gamma_j(0 -> t-1) M_0[j]       (write gather, coefficient a_tj)
 //   g_t = sum_{j in R_t} rho_tj gamma_j(0 -> t) M_0[j]       (read gather, coefficient b_tj)
 //   K_ts = sum_{j in S_t and S_s} w_tj w_sj gamma_j(s -> t-1)             for s < t
 //   Q_ts = sum_{j in R_t and S_s} rho_tj w_sj gamma_j(s -> t)             for s <= t
-//   (I + diag(alpha beta) K) delta = diag(beta) V - diag(alpha beta) H,   out_t = g_t + sum_s Q_ts delta_s,
+//   delta = T (diag(beta) V - diag(alpha beta) H),  T = (I + diag(alpha beta) K)^-1  (unit lower triangular)
+//   out_t = g_t + sum_s Q_ts delta_s,
 // and each written row ends as the in-order application of M[j] <- alpha_s M[j] + w_sj delta_s over its events.
-// This kernel sorts the chunk's write events by (slot, token), and emits: a and b, the slot segments with their
-// events, L = diag(alpha beta) K and Q as row-sorted sparse lists. Every sum runs in a fixed order (bitwise
-// repeatable; no atomics).
+// The kernel sorts the chunk's write events by (slot, token) and writes the chunk region of chunk_layout: the
+// gather terms (slot, a) and (slot, b), T and Q as row-sorted sparse lists, and the slot segments with their
+// events. T is solved in IEEE float32 by forward substitution, row after row. Every sum runs in a fixed order
+// (bitwise repeatable; no atomics).
 #include "sdm_internal.h"
 
 namespace sdm {
@@ -22,8 +25,47 @@ __host__ __device__ inline size_t plan_lds_bytes(int C, int W) {
   size_t keys = (size_t)pow2_ceil((int)CW) * 8;
   const size_t dense = (size_t)C * C * 4;
   if (dense > keys) keys = dense;
-  return keys + CW * 4 /*sslot*/ + CW * 2 /*sev*/ + CW * 2 /*pos*/ + (size_t)C * 8 /*alpha, beta*/ +
+  return keys + CW * 4 /*sslot*/ + CW * 2 /*sev*/ + CW * 2 /*pos*/ + (size_t)C * 12 /*alpha, beta, flags*/ +
          (size_t)PLAN_NT * 4 /*scan*/ + 16;
+}
+
+// Row-sorted sparse compaction of the dense rows 0..Cc-1 (columns 0..t for row t) into ptr / out; returns nnz.
+// ptr[t] are absolute offsets (base + running count). All threads call; ends with a barrier.
+__device__ inline int compact_rows(const float* dense, int C, int Cc, int* scan, int32_t* ptr, Ent* out, int base) {
+  const int tid = threadIdx.x;
+  for (int t = tid; t < Cc; t += PLAN_NT) {
+    int n = 0;
+    for (int s = 0; s <= t; ++s) n += dense[t * C + s] != 0.0f;
+    scan[t] = n;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int t = 0; t < Cc; ++t) {
+      const int c = scan[t];
+      scan[t] = run;
+      ptr[t] = base + run;
+      run += c;
+    }
+    ptr[Cc] = base + run;
+    scan[PLAN_NT - 1] = run;
+  }
+  __syncthreads();
+  const int total = scan[PLAN_NT - 1];
+  for (int t = tid; t < Cc; t += PLAN_NT) {
+    int o = base + scan[t];
+    for (int s = 0; s <= t; ++s) {
+      const float v = dense[t * C + s];
+      if (v != 0.0f) {
+        Ent x;
+        x.col = s;
+        x.val = v;
+        out[o++] = x;
+      }
+    }
+  }
+  __syncthreads();
+  return total;
 }
 
 template <typename A>
@@ -42,6 +84,14 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
   const long long cidx = (long long)st * D.nch + ch;
   const long long wbase = ((long long)st * D.T + t0) * W;  // [S][T][W] offset of the chunk's first event
   const long long rbase = ((long long)st * D.T + t0) * R;
+  const ChunkLayout CL = chunk_layout(C, W, R);
+  unsigned char* reg = a.chunks + cidx * CL.bytes;
+  Pair* pw = (Pair*)(reg + CL.pairs);
+  Pair* pr = pw + CW;
+  int32_t* tptr = (int32_t*)(reg + CL.ptrs);
+  int32_t* qptr = tptr + (C + 1);
+  Ent* lists = (Ent*)(reg + CL.lists);
+  Seg* segs = (Seg*)(reg + CL.scat);
 
   size_t keys_bytes = (size_t)pow2_ceil((int)CW) * 8;
   if ((size_t)C * C * 4 > keys_bytes) keys_bytes = (size_t)C * C * 4;
@@ -52,7 +102,9 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
   uint16_t* pos = sev + CW;
   float* sA = (float*)(pos + CW + (CW & 1));
   float* sB = sA + C;
-  int32_t* scan = (int32_t*)(sB + C);
+  int32_t* sHasL = (int32_t*)(sB + C);
+  int32_t* scan = sHasL + C;
+  __shared__ int s_nseg;
 
   // 1. write events -> sort keys (slot, event index); gates of the chunk.
   for (int e = tid; e < Ep2; e += PLAN_NT) {
@@ -60,10 +112,16 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
     if (e < E) key = ((uint64_t)(uint32_t)a.widx[wbase + e] << 32) | (uint32_t)e;
     keys[e] = key;
   }
-  for (int t = tid; t < Cc; t += PLAN_NT) {
-    const long long g = ((long long)b * D.T + t0 + t) * D.H + h;
-    sA[t] = to_f<A>(((const A*)a.alpha)[g]);
-    sB[t] = to_f<A>(((const A*)a.beta)[g]);
+  for (int t = tid; t < C; t += PLAN_NT) {
+    float al = 1.0f, be = 0.0f;
+    if (t < Cc) {
+      const long long g = ((long long)b * D.T + t0 + t) * D.H + h;
+      al = to_f<A>(((const A*)a.alpha)[g]);
+      be = to_f<A>(((const A*)a.beta)[g]);
+    }
+    sA[t] = al;
+    sB[t] = be;
+    sHasL[t] = 0;
   }
   __syncthreads();
   bitonic_sort_u64<PLAN_NT>(keys, Ep2);
@@ -89,34 +147,38 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
       scan[i] = run;
       run += c;
     }
-    a.nseg[cidx] = run;
-    a.seg_start[cidx * (CW + 1) + run] = E;
+    ChunkCounts cc;
+    cc.nnzT = cc.nnzQ = 0;
+    cc.nseg = run;
+    cc.nev = E;
+    a.counts[cidx] = cc;
+    s_nseg = run;
   }
   __syncthreads();
+  const int nseg = s_nseg;
+  Ev* ev = (Ev*)(segs + nseg);
   {
     int g = scan[tid] - 1;  // segment id of the element before lo
     for (int e = lo; e < hi; ++e) {
-      const bool first = (e == 0 || sslot[e] != sslot[e - 1]);
-      if (first) {
+      if (e == 0 || sslot[e] != sslot[e - 1]) {
         ++g;
-        a.seg_slot[cidx * CW + g] = sslot[e];
-        a.seg_start[cidx * (CW + 1) + g] = e;
+        segs[g].slot = sslot[e];
       }
-      const bool last = (e == E - 1 || sslot[e + 1] != sslot[e]);
-      const int ev = sev[e];
-      a.wlast[wbase + ev] = last ? g : -1;
+      if (e == E - 1 || sslot[e + 1] != sslot[e]) segs[g].end = e + 1;
+      const int evi = sev[e];
       Ev x;
-      x.w = a.wwt[wbase + ev];
-      x.tok = ev / W;
-      a.ev[cidx * CW + e] = x;
+      x.w = a.wwt[wbase + evi];
+      x.tok = evi / W;
+      ev[e] = x;
     }
   }
   __syncthreads();
 
-  // 3. K (dense rows in LDS) and the write-gather coefficients a_ti; one thread per token, events in order.
+  // 3. K (dense rows in LDS) and the write-gather terms (slot, a_ti); one thread per token, events in order.
   for (int i = tid; i < C * C; i += PLAN_NT) dense[i] = 0.0f;
   __syncthreads();
   for (int t = tid; t < Cc; t += PLAN_NT) {
+    int has = 0;
     for (int i = 0; i < W; ++i) {
       const int evi = t * W + i;
       const int e = pos[evi];
@@ -127,46 +189,41 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
         const int s = sev[e2] / W;
         dense[t * C + s] += wt * a.wwt[wbase + sev[e2]] * prod;
         prod *= sA[s];
+        has = 1;
       }
-      a.wcoef[wbase + evi] = wt * prod;
+      Pair p;
+      p.slot = slot;
+      p.coef = wt * prod;
+      pw[evi] = p;
     }
-  }
-  __syncthreads();
-  // L = diag(alpha beta) K as row-sorted sparse lists.
-  const long long lcap = chunk_lents(D);
-  for (int t = tid; t < Cc; t += PLAN_NT) {
-    int n = 0;
-    for (int s = 0; s < t; ++s) n += dense[t * C + s] != 0.0f;
-    scan[t] = n;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int t = 0; t < Cc; ++t) {
-      const int c = scan[t];
-      scan[t] = run;
-      a.lptr[cidx * (C + 1) + t] = run;
-      run += c;
-    }
-    a.lptr[cidx * (C + 1) + Cc] = run;
-  }
-  __syncthreads();
-  for (int t = tid; t < Cc; t += PLAN_NT) {
-    int o = scan[t];
-    const float ab = sA[t] * sB[t];
-    for (int s = 0; s < t; ++s) {
-      const float k = dense[t * C + s];
-      if (k != 0.0f) {
-        Ent x;
-        x.col = s;
-        x.val = ab * k;
-        a.lent[cidx * lcap + o++] = x;
-      }
-    }
+    sHasL[t] = has;
   }
   __syncthreads();
 
-  // 4. Q (dense rows) and the read-gather coefficients b_ti.
+  // 4. T = (I + L)^-1 with L = diag(alpha beta) K, in place, row after row (IEEE float32).
+  for (int i = tid; i < Cc * C; i += PLAN_NT) {
+    const int t = i / C, s = i % C;
+    if (s < t) dense[i] *= sA[t] * sB[t];
+    else if (s == t) dense[i] = 1.0f;
+  }
+  __syncthreads();
+  for (int t = 1; t < Cc; ++t) {
+    if (!sHasL[t]) continue;  // row t of T is e_t
+    const int s = tid;
+    float acc = 0.0f;
+    if (s < t) {
+      for (int m = s; m < t; ++m) {
+        const float l = dense[t * C + m];
+        if (l != 0.0f) acc += l * dense[m * C + s];
+      }
+    }
+    __syncthreads();
+    if (s < t) dense[t * C + s] = -acc;
+    __syncthreads();
+  }
+  const int nnzT = compact_rows(dense, C, Cc, scan, tptr, lists, 0);
+
+  // 5. Q (dense rows) and the read-gather terms (slot, b_ti).
   for (int i = tid; i < C * C; i += PLAN_NT) dense[i] = 0.0f;
   __syncthreads();
   for (int t = tid; t < Cc; t += PLAN_NT) {
@@ -188,39 +245,17 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
           prod *= sA[s];
         }
       }
-      a.rcoef[rbase + (long long)t * R + i] = rho * prod;
+      Pair p;
+      p.slot = j;
+      p.coef = rho * prod;
+      pr[(long long)t * R + i] = p;
     }
   }
   __syncthreads();
-  const long long qcap = chunk_qents(D);
-  for (int t = tid; t < Cc; t += PLAN_NT) {
-    int n = 0;
-    for (int s = 0; s <= t; ++s) n += dense[t * C + s] != 0.0f;
-    scan[t] = n;
-  }
-  __syncthreads();
+  const int nnzQ = compact_rows(dense, C, Cc, scan, qptr, lists, nnzT);
   if (tid == 0) {
-    int run = 0;
-    for (int t = 0; t < Cc; ++t) {
-      const int c = scan[t];
-      scan[t] = run;
-      a.qptr[cidx * (C + 1) + t] = run;
-      run += c;
-    }
-    a.qptr[cidx * (C + 1) + Cc] = run;
-  }
-  __syncthreads();
-  for (int t = tid; t < Cc; t += PLAN_NT) {
-    int o = scan[t];
-    for (int s = 0; s <= t; ++s) {
-      const float q = dense[t * C + s];
-      if (q != 0.0f) {
-        Ent x;
-        x.col = s;
-        x.val = q;
-        a.qent[cidx * qcap + o++] = x;
-      }
-    }
+    a.counts[cidx].nnzT = nnzT;
+    a.counts[cidx].nnzQ = nnzQ;
   }
 }
 

@@ -51,10 +51,51 @@ struct Ev {
   int32_t tok;
 };
 
-// One sparse entry of the chunk's strictly-lower L = diag(alpha*beta) K or of the read-coupling matrix Q.
+// One sparse entry (column, value) of a row-sorted list: T = (I + diag(alpha beta) K)^-1 or the read coupling Q.
 struct Ent {
   int32_t col;
   float val;
+};
+
+// A gather term: bank row `slot` times `coef`.
+struct Pair {
+  int32_t slot;
+  float coef;
+};
+
+// A written slot of a chunk and the exclusive end of its events in the chunk's event list.
+struct Seg {
+  int32_t slot;
+  int32_t end;
+};
+
+// Per-chunk plan region (byte offsets; every part 16-byte aligned). Written by the plan kernel, read by the loop.
+//   pairs  [C*W] write gather terms, then [C*R] read gather terms            (token-major, fixed size)
+//   ptrs   tptr[C+1], qptr[C+1] row starts of the two lists                  (fixed size)
+//   lists  T entries [nnzT] immediately followed by Q entries [nnzQ]         (packed; capacity C(C+1))
+//   scat   segments [nseg] immediately followed by events [E]                 (packed; capacity 2 C W)
+struct ChunkLayout {
+  long long pairs, ptrs, lists, scat, bytes;
+  long long pairs_bytes, ptrs_bytes, lists_cap, scat_cap;
+};
+__host__ __device__ inline long long align16(long long x) { return (x + 15) & ~15LL; }
+__host__ __device__ inline ChunkLayout chunk_layout(int C, int W, int R) {
+  ChunkLayout L;
+  L.pairs = 0;
+  L.pairs_bytes = align16((long long)C * (W + R) * 8);
+  L.ptrs = L.pairs + L.pairs_bytes;
+  L.ptrs_bytes = align16((long long)2 * (C + 1) * 4);
+  L.lists = L.ptrs + L.ptrs_bytes;
+  L.lists_cap = align16((long long)C * (C + 1) * 8);
+  L.scat = L.lists + L.lists_cap;
+  L.scat_cap = align16((long long)2 * C * W * 8);
+  L.bytes = L.scat + L.scat_cap;
+  return L;
+}
+
+// Per-chunk counts written by the plan.
+struct ChunkCounts {
+  int32_t nnzT, nnzQ, nseg, nev;
 };
 
 // ------------------------------------------------------------------------------------------- device helpers
@@ -120,18 +161,17 @@ __host__ __device__ inline int pow2_ceil(int x) {
 
 // ------------------------------------------------------------------------------------------- workspace layout
 struct WsLayout {
-  size_t cand_w, cand_r;                       // uint64 [MAX_CAND] each
-  size_t widx, wwt, ridx, rwt;                 // [S][T][W|R]
-  size_t wcoef, rcoef, wlast;                  // [S][T][W|R]
-  size_t nseg, seg_slot, seg_start, ev;        // per chunk
-  size_t lptr, lent, qptr, qent;               // per chunk
+  size_t cand;                                 // uint64 [2][MAX_CAND]: write then read candidate tables
+  size_t widx, wwt, ridx, rwt;                 // [S][T][W|R] slot ids and softmax weights, stream-major
+  size_t chunks;                               // [S * nch] chunk plan regions (chunk_layout)
+  size_t counts;                               // [S * nch] ChunkCounts
   size_t total;
 };
 
 // ------------------------------------------------------------------------------------------- launch wrappers
 // Candidate tuples (p_0..p_{F-1}) with prod(p_f + 1) <= k, p_f < kp[f], in lexicographic order; p_f in bits
-// [16 f, 16 f + 16) of each entry.
-hipError_t launch_cand_table(const TopkPlan& p, int F, uint64_t* table, hipStream_t st);
+// [16 f, 16 f + 16) of each entry. One launch builds the tables of `nkinds` plans (table q at tables + q*MAX_CAND).
+hipError_t launch_cand_tables(const TopkPlan* plans, int nkinds, int F, uint64_t* tables, hipStream_t st);
 
 // Top-k of every row of one or two query tensors. For kind q (0, 1): queries[q], k = plan[q].k.
 //  stream_major != 0: ids/weights go to ws arrays [S][T][k] (+ optional user ids [B,T,H,k]);
@@ -152,17 +192,15 @@ hipError_t launch_topk(const Dims& D, const TopkArgs& a, hipStream_t st);
 struct PlanArgs {
   const int32_t* widx; const float* wwt; const int32_t* ridx; const float* rwt;
   const void* alpha; const void* beta;
-  float* wcoef; float* rcoef; int32_t* wlast;
-  int32_t* nseg; int32_t* seg_slot; int32_t* seg_start; Ev* ev;
-  int32_t* lptr; Ent* lent; int32_t* qptr; Ent* qent;
+  unsigned char* chunks;  // [S * nch] regions of chunk_layout(C, W, R).bytes
+  ChunkCounts* counts;    // [S * nch]
 };
 hipError_t launch_plan(const Dims& D, const PlanArgs& a, hipStream_t st);
 
 struct LoopArgs {
-  const int32_t* widx; const float* wcoef; const int32_t* ridx; const float* rcoef;
   const void* alpha; const void* beta; const void* values;
-  const int32_t* nseg; const int32_t* seg_slot; const int32_t* seg_start; const Ev* ev;
-  const int32_t* lptr; const Ent* lent; const int32_t* qptr; const Ent* qent;
+  const unsigned char* chunks;
+  const ChunkCounts* counts;
   void* bank; void* out;
 };
 hipError_t launch_loop(const Dims& D, const LoopArgs& a, hipStream_t st);
@@ -176,12 +214,5 @@ struct DecodeArgs {
 hipError_t launch_decode(const Dims& D, const DecodeArgs& a, hipStream_t st);
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t st);
 
-// sizes per chunk
-__host__ __device__ inline long long chunk_events(const Dims& D) { return (long long)D.C * D.W; }
-__host__ __device__ inline long long chunk_lents(const Dims& D) {
-  const long long n = (long long)D.C * (D.C - 1) / 2;
-  return n > 0 ? n : 1;
-}
-__host__ __device__ inline long long chunk_qents(const Dims& D) { return (long long)D.C * (D.C + 1) / 2; }
 
 }  // namespace sdm

@@ -1,37 +1,20 @@
 // Exact product-key top-k kernels: the candidate table and the batched top-k (write keys and read queries).
 #include "sdm_internal.h"
 #include "topk_device.h"
+#include "topk_wave.h"
 
 namespace sdm {
 
-// One thread enumerates, in lexicographic order, the position tuples with prod(p_f + 1) <= k and p_f < kp[f]
-// (an odometer that skips the rest of a digit's range once the prefix product exceeds k).
-__global__ void cand_table_kernel(TopkPlan P, int F, uint64_t* __restrict__ table) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  int p[MAX_F] = {0, 0, 0, 0};
-  int c = 0;
-  while (true) {
-    long long prod = 1;
-    for (int f = 0; f < F; ++f) prod *= p[f] + 1;
-    if (prod <= P.k && c < MAX_CAND) {
-      uint64_t t = 0;
-      for (int f = 0; f < F; ++f) t |= (uint64_t)p[f] << (16 * f);
-      table[c++] = t;
-    }
-    int f = F - 1;
-    for (; f >= 0; --f) {
-      ++p[f];
-      long long pp = 1;
-      for (int g = 0; g <= f; ++g) pp *= p[g] + 1;
-      if (p[f] < P.kp[f] && pp <= P.k) break;
-      p[f] = 0;
-    }
-    if (f < 0) break;
-  }
+// One block per plan builds its candidate table (see build_cand_table).
+__global__ __launch_bounds__(256) void cand_table_kernel(TopkPlan p0, TopkPlan p1, int F, uint64_t* __restrict__ tables) {
+  __shared__ int scratch[MAX_K + 1];
+  const TopkPlan& P = blockIdx.x == 0 ? p0 : p1;
+  build_cand_table<256>(P, F, tables + (size_t)blockIdx.x * MAX_CAND, scratch);
 }
 
-hipError_t launch_cand_table(const TopkPlan& p, int F, uint64_t* table, hipStream_t st) {
-  hipLaunchKernelGGL(cand_table_kernel, dim3(1), dim3(64), 0, st, p, F, table);
+hipError_t launch_cand_tables(const TopkPlan* plans, int nkinds, int F, uint64_t* tables, hipStream_t st) {
+  hipLaunchKernelGGL(cand_table_kernel, dim3(nkinds), dim3(256), 0, st, plans[0], plans[nkinds > 1 ? 1 : 0], F,
+                     tables);
   return hipGetLastError();
 }
 
@@ -66,9 +49,233 @@ __global__ __launch_bounds__(TOPK_NT) void topk_kernel(Dims D, TopkArgs a) {
   }
 }
 
+// ------------------------------------------------------------------------------------------- wave-level top-k
+// One wave scores QW query rows (same head and kind) against every sub-key with the fp64 FMA chain, each lane
+// owning NPL sub-keys (its rows read as 16-byte vectors and reused across the QW queries), selects each factor's
+// top min(k, n_f) exactly (wave_select_sorted), then merges the candidate tuples (CPL per lane) the same way.
+template <int NPL> struct WaveTile { static constexpr int QW = (32 / NPL) < 16 ? (32 / NPL < 1 ? 1 : 32 / NPL) : 16; };
+
+// Per-wave LDS: factor scores [QW][64 NPL] (float), kept factor lists [QW][F][kpmax] (float score + uint16 id),
+// selection scratch and sorted output [KS] each (uint64).
+__host__ __device__ inline size_t topk2_wave_lds(int F, int kpmax, int k, int QW, int NPL) {
+  const int KS = kpmax > k ? kpmax : k;
+  size_t n = (size_t)QW * 64 * NPL * 4;
+  n += (size_t)QW * F * kpmax * 6;
+  n = (n + 7) & ~(size_t)7;
+  return n + (size_t)KS * 16;
+}
+
+// 16 bytes of a sub-key row and element e of it as fp64 (exact widening).
+template <typename A> struct Vec16;
+template <> struct Vec16<float> {
+  static constexpr int N = 4;
+  __device__ static double at(const uint4& x, int e) {
+    const uint32_t w = e == 0 ? x.x : e == 1 ? x.y : e == 2 ? x.z : x.w;
+    return (double)__uint_as_float(w);
+  }
+};
+template <> struct Vec16<bf16_t> {
+  static constexpr int N = 8;
+  __device__ static double at(const uint4& x, int e) {
+    const uint32_t w = (e >> 1) == 0 ? x.x : (e >> 1) == 1 ? x.y : (e >> 1) == 2 ? x.z : x.w;
+    return (double)__uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+  }
+};
+
+template <typename A, int NPL, int CPL>
+__global__ __launch_bounds__(256) void topk2_kernel(Dims D, TopkArgs a) {
+  constexpr int QW = WaveTile<NPL>::QW;
+  constexpr int VEC = Vec16<A>::N;
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int kind = blockIdx.y, h = blockIdx.z;
+  const TopkPlan& P = a.plan[kind];
+  const int F = D.F, dk = D.dk, k = P.k, kpmax = P.kpmax;
+  const long long BT = (long long)D.B * D.T;
+  const long long bt0 = ((long long)blockIdx.x * 4 + wv) * QW;
+  if (bt0 >= BT) return;  // no block-wide barriers below: idle waves may leave
+  const int KS = kpmax > k ? kpmax : k;
+  unsigned char* wl = lds + (size_t)wv * topk2_wave_lds(F, kpmax, k, QW, NPL);
+  float* scs = (float*)wl;                                  // [QW][64 NPL]
+  float* fsc = scs + QW * 64 * NPL;                         // [QW][F][kpmax]
+  uint16_t* fid = (uint16_t*)(fsc + QW * F * kpmax);        // [QW][F][kpmax]
+  uint64_t* scratch =
+      (uint64_t*)(wl + (((size_t)QW * 64 * NPL * 4 + (size_t)QW * F * kpmax * 6 + 7) & ~(size_t)7));
+  uint64_t* sorted = scratch + KS;
+  long long sumn = 0;
+  for (int f = 0; f < F; ++f) sumn += D.widths[f];
+  const A* sub = (const A*)a.subkeys + (long long)h * sumn * dk;
+  const int Fdk = F * dk;
+  const int nq = (int)min((long long)QW, BT - bt0);
+  // rows (b, t) = bt0 + q are consecutive: row index (bt0 + q) * H + h
+  const A* qbase = (const A*)a.queries[kind] + ((long long)bt0 * D.H + h) * Fdk;
+  const long long qstride = (long long)D.H * Fdk;
+
+  long long off = 0;
+  for (int f = 0; f < F; ++f) {
+    const int n = D.widths[f];
+    const A* tab = sub + off * dk;
+    double acc[QW][NPL];
+#pragma unroll
+    for (int q = 0; q < QW; ++q)
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) acc[q][j] = 0.0;
+    for (int c0 = 0; c0 < dk; c0 += VEC) {
+      uint4 rv[NPL];
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) {
+        const int i = lane + 64 * j;
+        rv[j] = i < n ? *(const uint4*)(tab + (long long)i * dk + c0) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+#pragma unroll
+        for (int q = 0; q < QW; ++q) {
+          const long long qq = q < nq ? q : 0;
+          const double x = to_d<A>(qbase[qq * qstride + f * dk + c0 + e]);
+#pragma unroll
+          for (int j = 0; j < NPL; ++j) acc[q][j] = fma(x, Vec16<A>::at(rv[j], e), acc[q][j]);
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < QW; ++q)
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) scs[q * 64 * NPL + lane + 64 * j] = (float)acc[q][j];
+    wave_sync();
+    for (int q = 0; q < nq; ++q) {
+      uint64_t key[NPL];
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) {
+        const int i = lane + 64 * j;
+        key[j] = i < n ? (((uint64_t)desc_key(scs[q * 64 * NPL + i]) << 32) | (uint32_t)i) : ~0ull;
+      }
+      wave_select_sorted<NPL>(key, P.kp[f], scratch, sorted);
+      for (int p = lane; p < P.kp[f]; p += 64) {
+        const uint64_t kk = sorted[p];
+        fsc[(q * F + f) * kpmax + p] = desc_key_value((uint32_t)(kk >> 32));
+        fid[(q * F + f) * kpmax + p] = (uint16_t)(uint32_t)kk;
+      }
+      wave_sync();
+    }
+    off += n;
+  }
+
+  const uint64_t* cand = a.cand[kind];
+  for (int q = 0; q < nq; ++q) {
+    uint64_t ck[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = lane + 64 * j;
+      uint64_t key = ~0ull;
+      if (c < P.ncand) {
+        const uint64_t tup = cand[c];
+        int p = (int)(tup & 0xFFFF);
+        float S = fsc[(q * F) * kpmax + p];
+        int ps = p;
+        for (int f = 1; f < F; ++f) {
+          p = (int)((tup >> (16 * f)) & 0xFFFF);
+          S = S + fsc[(q * F + f) * kpmax + p];  // float32 sum, left to right
+          ps += p;
+        }
+        key = ((uint64_t)desc_key(S) << 32) | ((uint64_t)ps << 20) | (uint64_t)c;
+      }
+      ck[j] = key;
+    }
+    wave_select_sorted<CPL>(ck, k, scratch, sorted);
+    const long long bt = bt0 + q;
+    const long long b = bt / D.T, t = bt % D.T;
+    const long long row = (b * D.T + t) * D.H + h;
+    const double m = (double)desc_key_value((uint32_t)(sorted[0] >> 32));
+    double zpart = 0.0;
+    for (int r = lane; r < k; r += 64) {
+      const uint64_t kk = sorted[r];
+      const uint64_t tup = cand[(int)(kk & 0xFFFFF)];
+      long long id = 0;
+      for (int f = 0; f < F; ++f)
+        id = id * D.widths[f] + fid[(q * F + f) * kpmax + (int)((tup >> (16 * f)) & 0xFFFF)];
+      const float sc = desc_key_value((uint32_t)(kk >> 32));
+      if (a.stream_major) {
+        const long long so = ((b * D.H + h) * D.T + t) * k;
+        a.ids[kind][so + r] = (int32_t)id;
+        if (a.user_ids[kind]) a.user_ids[kind][row * k + r] = (int32_t)id;
+        zpart += exp((double)sc - m);
+      } else {
+        a.ids[kind][row * k + r] = (int32_t)id;
+        if (a.vals[kind]) a.vals[kind][row * k + r] = sc;
+      }
+    }
+    if (a.stream_major) {
+      // softmax normaliser: per-lane partial sums (fixed order), then a fixed butterfly across the wave
+      double z = zpart;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) z += __shfl_xor(z, o);
+      const long long so = ((b * D.H + h) * D.T + t) * k;
+      for (int r = lane; r < k; r += 64) {
+        const float sc = desc_key_value((uint32_t)(sorted[r] >> 32));
+        a.vals[kind][so + r] = (float)(exp((double)sc - m) / z);
+      }
+    }
+    wave_sync();
+  }
+}
+
+template <typename A, int NPL>
+static bool launch_topk2_npl(const Dims& D, const TopkArgs& a, hipStream_t st, int cpl, size_t lds) {
+  constexpr int QW = WaveTile<NPL>::QW;
+  const long long BT = (long long)D.B * D.T;
+  const long long tiles = (BT + QW - 1) / QW;
+  dim3 grid((unsigned)((tiles + 3) / 4), (unsigned)a.nkinds, (unsigned)D.H);
+  if (cpl == 8) {
+    (void)hipFuncSetAttribute((const void*)topk2_kernel<A, NPL, 8>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)lds);
+    hipLaunchKernelGGL((topk2_kernel<A, NPL, 8>), grid, dim3(256), lds, st, D, a);
+  } else {
+    (void)hipFuncSetAttribute((const void*)topk2_kernel<A, NPL, 16>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)lds);
+    hipLaunchKernelGGL((topk2_kernel<A, NPL, 16>), grid, dim3(256), lds, st, D, a);
+  }
+  return true;
+}
+
+template <typename A>
+static bool launch_topk2(const Dims& D, const TopkArgs& a, hipStream_t st) {
+  int nfmax = 0;
+  for (int f = 0; f < D.F; ++f) nfmax = D.widths[f] > nfmax ? D.widths[f] : nfmax;
+  int npl = 1;
+  while (npl * 64 < nfmax) npl <<= 1;
+  if (npl > 16) return false;
+  int ncand = 0, kpmax = 0, kmax = 0;
+  for (int q = 0; q < a.nkinds; ++q) {
+    ncand = a.plan[q].ncand > ncand ? a.plan[q].ncand : ncand;
+    kpmax = a.plan[q].kpmax > kpmax ? a.plan[q].kpmax : kpmax;
+    kmax = a.plan[q].k > kmax ? a.plan[q].k : kmax;
+  }
+  if (ncand > 1024 || kpmax > 1024) return false;
+  if ((D.dk * (int)sizeof(A)) % 16 != 0 || ((uintptr_t)a.subkeys) % 16 != 0) return false;
+  const int cpl = ncand <= 512 ? 8 : 16;
+  const int QW = 32 / npl < 16 ? (32 / npl < 1 ? 1 : 32 / npl) : 16;
+  size_t lds = 0;
+  for (int q = 0; q < a.nkinds; ++q) {
+    const size_t l = 4 * topk2_wave_lds(D.F, a.plan[q].kpmax, a.plan[q].k, QW, npl);
+    lds = l > lds ? l : lds;
+  }
+  if (lds > 128 * 1024) return false;
+  switch (npl) {
+    case 1: return launch_topk2_npl<A, 1>(D, a, st, cpl, lds);
+    case 2: return launch_topk2_npl<A, 2>(D, a, st, cpl, lds);
+    case 4: return launch_topk2_npl<A, 4>(D, a, st, cpl, lds);
+    case 8: return launch_topk2_npl<A, 8>(D, a, st, cpl, lds);
+    default: return launch_topk2_npl<A, 16>(D, a, st, cpl, lds);
+  }
+}
+
 hipError_t launch_topk(const Dims& D, const TopkArgs& a, hipStream_t st) {
   const long long rows = (long long)D.B * D.T * D.H;
   if (rows == 0) return hipSuccess;
+  const bool done = D.act == SDM_BF16 ? launch_topk2<bf16_t>(D, a, st) : launch_topk2<float>(D, a, st);
+  if (done) return hipGetLastError();
   size_t lds = 0;
   for (int q = 0; q < a.nkinds; ++q) {
     size_t l = topk_lds_bytes(D.F, D.dk, a.plan[q]);

@@ -15,6 +15,81 @@
 
 namespace sdm {
 
+// Number of position tuples (p_1..p_{F-1}) with p_f < kp[f] and prod_{f >= 1}(p_f + 1) <= budget.
+__device__ inline int cand_count_rest(const TopkPlan& P, int F, int budget) {
+  if (F == 1) return 1;
+  const int l1 = min(P.kp[1], budget);
+  if (F == 2) return l1;
+  int n = 0;
+  for (int p1 = 0; p1 < l1; ++p1) {
+    const int b1 = budget / (p1 + 1);
+    const int l2 = min(P.kp[2], b1);
+    if (F == 3) {
+      n += l2;
+      continue;
+    }
+    for (int p2 = 0; p2 < l2; ++p2) n += min(P.kp[3], b1 / (p2 + 1));
+  }
+  return n;
+}
+
+// Writes those tuples after first position p0, in lexicographic order, to out[0..) (at most `room` entries).
+__device__ inline void cand_emit_rest(const TopkPlan& P, int F, int p0, int budget, uint64_t* out, int room) {
+  int n = 0;
+  if (F == 1) {
+    if (n < room) out[n] = (uint64_t)p0;
+    return;
+  }
+  const int l1 = min(P.kp[1], budget);
+  for (int p1 = 0; p1 < l1; ++p1) {
+    const uint64_t t1 = (uint64_t)p0 | ((uint64_t)p1 << 16);
+    if (F == 2) {
+      if (n < room) out[n] = t1;
+      ++n;
+      continue;
+    }
+    const int b1 = budget / (p1 + 1);
+    const int l2 = min(P.kp[2], b1);
+    for (int p2 = 0; p2 < l2; ++p2) {
+      const uint64_t t2 = t1 | ((uint64_t)p2 << 32);
+      if (F == 3) {
+        if (n < room) out[n] = t2;
+        ++n;
+        continue;
+      }
+      const int l3 = min(P.kp[3], b1 / (p2 + 1));
+      for (int p3 = 0; p3 < l3; ++p3) {
+        if (n < room) out[n] = t2 | ((uint64_t)p3 << 48);
+        ++n;
+      }
+    }
+  }
+}
+
+// The whole block builds the candidate table of plan P in lexicographic order: thread i takes first positions
+// p_0 = i, i + NT, ...; an exclusive scan of their counts gives each first position its output range.
+// scratch: >= kp[0] + 1 ints (LDS). Ends with a barrier.
+template <int NT>
+__device__ void build_cand_table(const TopkPlan& P, int F, uint64_t* out, int* scratch) {
+  const int tid = threadIdx.x;
+  for (int p0 = tid; p0 < P.kp[0]; p0 += NT) scratch[p0] = cand_count_rest(P, F, P.k / (p0 + 1));
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int i = 0; i < P.kp[0]; ++i) {
+      const int c = scratch[i];
+      scratch[i] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  for (int p0 = tid; p0 < P.kp[0]; p0 += NT) {
+    const int o = scratch[p0];
+    if (o < MAX_CAND) cand_emit_rest(P, F, p0, P.k / (p0 + 1), out + o, MAX_CAND - o);
+  }
+  __syncthreads();
+}
+
 // LDS bytes of one topk_query workspace (8-byte aligned regions).
 __host__ __device__ inline size_t topk_lds_bytes(int F, int dk, const TopkPlan& P) {
   size_t n = 0;
