@@ -71,11 +71,13 @@ def bench_write_read(args, torch, binding, synth):
     x = synth.make_inputs(s)
     t = {k: torch.from_numpy(x[k]).to(dev).to(dt[s.act]) for k in ("wkeys", "rq", "values", "alpha", "beta",
                                                                     "subkeys")}
-    bank = torch.from_numpy(x["bank"]).to(dev).to(dt[s.bank])
+    pitch = binding.bank_pitch(s.head_dim, dt[s.bank])
+    bank = binding.alloc_bank(s.batch, s.heads, s.rows, s.head_dim, dt[s.bank], dev, pitch=pitch)
+    bank.copy_(torch.from_numpy(x["bank"]).to(dev).to(dt[s.bank]))
     del x
     cfg = binding.make_config(s.batch, s.tokens, s.heads, s.widths, s.subkey_dim, s.head_dim, s.num_writes,
                               s.num_reads, s.chunk_size, binding.SDM_BF16 if s.act == "bf16" else binding.SDM_F32,
-                              binding.SDM_BF16 if s.bank == "bf16" else binding.SDM_F32, s.rows)
+                              binding.SDM_BF16 if s.bank == "bf16" else binding.SDM_F32, s.rows, pitch)
     ws = torch.empty(binding.workspace_size(cfg, binding.SDM_OP_WRITE_READ), dtype=torch.uint8, device=dev)
     out = torch.empty((s.batch, s.tokens, s.heads, s.head_dim), dtype=dt[s.act], device=dev)
 
@@ -109,10 +111,28 @@ def bench_write_read(args, torch, binding, synth):
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "algorithmic_bytes_per_launch": alg, "avg_launch_ms": round(loop_ms, 4)}
     step_bytes = alg  # the loop's bank traffic dominates the call's bytes
+    # the same workload on an unpadded bank (row pitch = head_dim), for comparison
+    bank_np = torch.empty((s.batch, s.heads, s.rows, s.head_dim), dtype=dt[s.bank], device=dev)
+    bank_np.copy_(bank)
+    for _ in range(2):
+        binding.sdm_write_read(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"], t["subkeys"], bank_np,
+                               widths=s.widths, num_writes=s.num_writes, num_reads=s.num_reads,
+                               chunk_size=s.chunk_size, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    binding.profile_enable(True)
+    for _ in range(5):
+        binding.sdm_write_read(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"], t["subkeys"], bank_np,
+                               widths=s.widths, num_writes=s.num_writes, num_reads=s.num_reads,
+                               chunk_size=s.chunk_size, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    p2 = binding.profile_read()
+    binding.profile_enable(False)
+    roof["unpadded_pitch_avg_launch_ms"] = round(p2["loop"][0] / p2["loop"][1], 4)
+    del bank_np
     return {
         "tokens_per_s": tokens / (ms_step * 1e-3), "ms_per_step": ms_step, "kernels_avg_ms": kernels,
         "roofline": roof, "whole_call_hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "shape": s,
+        "shape": s, "pitch": pitch,
     }
 
 
@@ -246,7 +266,8 @@ def main():
                                "W=R=64, chunk 64, bf16 activations, f32 bank",
                    "global_batch": s.batch, "seq_len": s.tokens, "heads": s.heads, "head_dim": s.head_dim,
                    "slots_per_head": s.slots, "num_writes": s.num_writes, "num_reads": s.num_reads,
-                   "chunk_size": s.chunk_size, "act_dtype": s.act, "bank_dtype": s.bank, "parallelism": "none (1 GPU)"},
+                   "chunk_size": s.chunk_size, "act_dtype": s.act, "bank_dtype": s.bank,
+                   "bank_row_stride": wr["pitch"], "parallelism": "none (1 GPU)"},
         "kernels_avg_ms": wr["kernels_avg_ms"],
         "roofline": wr["roofline"],
         "decode": dec,

@@ -39,12 +39,12 @@ class SdmConfig(ctypes.Structure):
         ("num_factors", ctypes.c_int32), ("factor_widths", ctypes.c_int32 * 4), ("subkey_dim", ctypes.c_int32),
         ("head_dim", ctypes.c_int32), ("num_writes", ctypes.c_int32), ("num_reads", ctypes.c_int32),
         ("chunk_size", ctypes.c_int32), ("act_dtype", ctypes.c_int32), ("bank_dtype", ctypes.c_int32),
-        ("bank_rows", ctypes.c_int64),
+        ("bank_rows", ctypes.c_int64), ("bank_row_stride", ctypes.c_int64),
     ]
 
 
 def make_config(batch, tokens, heads, widths, subkey_dim, head_dim=1, num_writes=1, num_reads=1, chunk_size=1,
-                act_dtype=SDM_F32, bank_dtype=SDM_F32, bank_rows=None) -> SdmConfig:
+                act_dtype=SDM_F32, bank_dtype=SDM_F32, bank_rows=None, bank_row_stride=0) -> SdmConfig:
     c = SdmConfig()
     c.batch, c.tokens, c.heads = int(batch), int(tokens), int(heads)
     c.num_factors = len(widths)
@@ -57,7 +57,35 @@ def make_config(batch, tokens, heads, widths, subkey_dim, head_dim=1, num_writes
     for w in widths:
         n *= int(w)
     c.bank_rows = int(bank_rows) if bank_rows is not None else n
+    c.bank_row_stride = int(bank_row_stride)
     return c
+
+
+def bank_pitch(head_dim: int, dtype: torch.dtype) -> int:
+    """Row pitch (elements) for a bank on MI355X: rows whose byte size is a multiple of 512 get 128 bytes of padding,
+    so that gathering rows in column slices spreads over the HBM channels instead of hitting one channel group."""
+    es = torch.empty(0, dtype=dtype).element_size()
+    return head_dim + (128 // es if (head_dim * es) % 512 == 0 else 0)
+
+
+def alloc_bank(batch, heads, rows, head_dim, dtype, device, pitch=None) -> torch.Tensor:
+    """Uninitialised bank [batch, heads, rows, head_dim] whose rows are `pitch` elements apart (a view)."""
+    ld = bank_pitch(head_dim, dtype) if pitch is None else int(pitch)
+    buf = torch.empty((batch, heads, rows, ld), dtype=dtype, device=device)
+    return buf[..., :head_dim]
+
+
+def _bank_ld(bank: torch.Tensor, name: str) -> int:
+    """Row stride of a bank tensor [B, H, rows, d] whose rows may be padded (unit column stride)."""
+    if not bank.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    B, H, rows, d = bank.shape
+    ld = bank.stride(2) if rows > 1 else max(d, bank.stride(2))
+    if bank.stride(3) != 1 or ld < d or (H > 1 and bank.stride(1) != rows * ld) or \
+            (B > 1 and bank.stride(0) != H * rows * ld):
+        raise ValueError(f"{name} must be [B, H, rows, d] with unit column stride and a uniform row pitch "
+                         f"(strides {tuple(bank.stride())})")
+    return ld
 
 
 _lib = None
@@ -198,11 +226,11 @@ def sdm_write_read(write_keys, read_queries, values, forget_gate, input_gate, su
                          ("values", values, (B, T, H, d)), ("forget_gate", forget_gate, (B, T, H)),
                          ("input_gate", input_gate, (B, T, H)), ("subkeys", subkeys, (H, sum(widths), dk))):
         _need(t, name, shp, act)
-    _need(bank, "bank")
     if bank.dim() != 4 or bank.shape[0] != B or bank.shape[1] != H or bank.shape[3] != d:
         raise ValueError(f"bank has shape {tuple(bank.shape)}, expected ({B}, {H}, bank_rows, {d})")
+    ld = _bank_ld(bank, "bank")
     cfg = make_config(B, T, H, widths, dk, d, num_writes, num_reads, chunk_size, _dt(write_keys), _dt(bank),
-                      bank.shape[2])
+                      bank.shape[2], ld)
     ws = _workspace(workspace_size(cfg, SDM_OP_WRITE_READ), bank.device, workspace)
     if out is None:
         out = torch.empty((B, T, H, d), dtype=act, device=bank.device)
@@ -232,10 +260,14 @@ def sdm_decode_step(write_keys, read_queries, values, forget_gate, input_gate, s
                          ("values", values, (B, T, H, d)), ("forget_gate", forget_gate, (B, T, H)),
                          ("input_gate", input_gate, (B, T, H)), ("subkeys", subkeys, (H, sum(widths), dk))):
         _need(t, name, shp, act)
-    _need(bank_in, "bank_in")
-    _need(bank_out, "bank_out", tuple(bank_in.shape), bank_in.dtype)
+    if bank_in.dim() != 4 or bank_in.shape[0] != B or bank_in.shape[1] != H or bank_in.shape[3] != d:
+        raise ValueError(f"bank_in has shape {tuple(bank_in.shape)}, expected ({B}, {H}, bank_rows, {d})")
+    ld = _bank_ld(bank_in, "bank_in")
+    if tuple(bank_out.shape) != tuple(bank_in.shape) or bank_out.dtype != bank_in.dtype or \
+            bank_out.stride() != bank_in.stride():
+        raise ValueError("bank_out must have bank_in's shape, dtype and strides")
     cfg = make_config(B, T, H, widths, dk, d, num_writes, num_reads, 1, _dt(write_keys), _dt(bank_in),
-                      bank_in.shape[2])
+                      bank_in.shape[2], ld)
     ws = _workspace(workspace_size(cfg, SDM_OP_DECODE), bank_in.device, workspace)
     if out is None:
         out = torch.empty((B, T, H, d), dtype=act, device=bank_in.device)

@@ -133,6 +133,10 @@ sdm_status validate(const sdm_config* cfg, int op, int k, Dims* D, TopkPlan* pw,
     return fail(SDM_ERR_BANK_TOO_SMALL, "bank_rows = %lld is smaller than the slot count N = %lld",
                 (long long)cfg->bank_rows, N);
   D->rows = cfg->bank_rows;
+  const long long ld = cfg->bank_row_stride ? cfg->bank_row_stride : d;
+  if (ld < d || (ld * (bank == SDM_BF16 ? 2 : 4)) % 16 != 0)
+    return fail(SDM_ERR_LAYOUT, "bank_row_stride = %lld must be >= head_dim = %d and a multiple of 16 bytes", ld, d);
+  D->ld = ld;
   if (op == SDM_OP_WRITE_READ) {
     const int C = cfg->chunk_size;
     if (C < 1 || C > MAX_CHUNK) return fail(SDM_ERR_RANGE, "chunk_size = %d out of range [1, %d]", C, MAX_CHUNK);
@@ -358,7 +362,7 @@ sdm_status sdm_write_read(const sdm_config* cfg, const void* write_keys, const v
   long long sumn = 0;
   for (int f = 0; f < D.F; ++f) sumn += D.widths[f];
   const size_t ea = esize(D.act), eb = esize(D.bank);
-  const size_t bank_bytes = (size_t)D.S * (size_t)D.rows * D.d * eb;
+  const size_t bank_bytes = (size_t)D.S * (size_t)D.rows * (size_t)D.ld * eb;
   if (rows > 0) {
     TRY(need(write_keys, "write_keys"));
     TRY(need(read_queries, "read_queries"));
@@ -443,7 +447,7 @@ sdm_status sdm_decode_step(const sdm_config* cfg, const void* write_keys, const 
   long long sumn = 0;
   for (int f = 0; f < D.F; ++f) sumn += D.widths[f];
   const size_t ea = esize(D.act), eb = esize(D.bank);
-  const size_t bank_bytes = (size_t)D.S * (size_t)D.rows * D.d * eb;
+  const size_t bank_bytes = (size_t)D.S * (size_t)D.rows * (size_t)D.ld * eb;
   if (rows > 0) {
     TRY(need(write_keys, "write_keys"));
     TRY(need(read_queries, "read_queries"));

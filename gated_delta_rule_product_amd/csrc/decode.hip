@@ -97,7 +97,7 @@ __global__ __launch_bounds__(DECODE_NT) void decode_kernel(Dims D, DecodeArgs a)
   const float be = to_f<A>(((const A*)a.beta)[row]);
   const A* v = (const A*)a.values + row * D.d;
   A* out = (A*)a.out + row * D.d;
-  const long long rowsd = D.rows * (long long)D.d;
+  const long long rowsd = D.rows * D.ld;
   const Bk* bin = (const Bk*)a.bank_in + (long long)st * rowsd;
   Bk* bout = (Bk*)a.bank_out + (long long)st * rowsd;
 
@@ -118,7 +118,7 @@ __global__ __launch_bounds__(DECODE_NT) void decode_kernel(Dims D, DecodeArgs a)
     if (on) {
       for (int i = rg; i < D.W; i += RG) {
         float m[EPL];
-        DLane<Bk>::load(bin + (long long)sWid[i] * D.d + col, m);
+        DLane<Bk>::load(bin + (long long)sWid[i] * D.ld + col, m);
         const float wi = sWw[i];
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[e] += wi * m[e];
@@ -139,7 +139,7 @@ __global__ __launch_bounds__(DECODE_NT) void decode_kernel(Dims D, DecodeArgs a)
     // M[S_i] <- alpha M[S_i] + w_i delta, rounded to the bank dtype, into the successor
     if (on) {
       for (int i = rg; i < D.W; i += RG) {
-        const long long o = (long long)sWid[i] * D.d + col;
+        const long long o = (long long)sWid[i] * D.ld + col;
         float m[EPL];
         DLane<Bk>::load(bin + o, m);
         const float wi = sWw[i];
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(DECODE_NT) void decode_kernel(Dims D, DecodeArgs a)
     if (on) {
       for (int i = rg; i < D.R; i += RG) {
         float m[EPL];
-        DLane<Bk>::load(bout + (long long)sRid[i] * D.d + col, m);
+        DLane<Bk>::load(bout + (long long)sRid[i] * D.ld + col, m);
         const float ri = sRw[i];
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[e] += ri * m[e];

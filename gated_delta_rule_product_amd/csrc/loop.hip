@@ -13,9 +13,10 @@
 // neighbouring column slices of a stream run on the same XCD and share its L2 (a 128-byte L2 line holds two
 // 64-byte slices).
 //
-// Two variants: STAGED copies each chunk's plan region into LDS with one coalesced pass (the scatter part is
-// prefetched into registers during the solve); the direct variant reads it from global memory (used when the
-// region does not fit in LDS, e.g. chunk 128).
+// Two variants: STAGED copies each chunk's plan region into LDS in batched coalesced passes (gather terms and
+// lists before A, the scatter part before D); the direct variant reads it from global memory (used when the
+// region does not fit in LDS, e.g. chunk 128). Every global load stream is issued in batches so that many loads
+// are in flight per lane.
 #include "sdm_internal.h"
 
 namespace sdm {
@@ -28,6 +29,9 @@ template <> struct Lane<float> {
     v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
   }
   __device__ static void store(float* p, const float* v) { *(float4*)p = make_float4(v[0], v[1], v[2], v[3]); }
+  __device__ static void unpack(const uint4& x, float* v) {
+    v[0] = __uint_as_float(x.x); v[1] = __uint_as_float(x.y); v[2] = __uint_as_float(x.z); v[3] = __uint_as_float(x.w);
+  }
 };
 template <> struct Lane<bf16_t> {
   static constexpr int EPL = 8;
@@ -45,6 +49,14 @@ template <> struct Lane<bf16_t> {
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f_to_bf16(v[2 * i]) | ((uint32_t)f_to_bf16(v[2 * i + 1]) << 16);
     *(uint4*)p = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  __device__ static void unpack(const uint4& x, float* v) {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
   }
 };
 
@@ -87,7 +99,7 @@ __global__ __launch_bounds__(LOOP_NT) void loop_kernel(Dims D, LoopArgs a, int n
   const int col0 = slice * COLS;
   const int mycol = col0 + q * EPL;
   const bool valid = mycol < D.d;
-  const long long rowsd = D.rows * (long long)D.d;
+  const long long rowsd = D.rows * D.ld;
   Bk* bank = (Bk*)a.bank + (long long)st * rowsd;
   const A* alpha = (const A*)a.alpha;
   const A* beta = (const A*)a.beta;
@@ -109,7 +121,16 @@ __global__ __launch_bounds__(LOOP_NT) void loop_kernel(Dims D, LoopArgs a, int n
       const int n16 = (int)((CL.pairs_bytes + CL.ptrs_bytes + (long long)(cnt.nnzT + cnt.nnzQ) * 8 + 15) >> 4);
       const uint4* src = (const uint4*)greg;
       uint4* dst = (uint4*)sReg;
-      for (int i = tid; i < n16; i += LOOP_NT) dst[i] = src[i];
+      for (int i0 = 0; i0 < n16; i0 += LOOP_NT * PREF) {  // batches of PREF loads per thread in flight
+        uint4 tmp[PREF];
+#pragma unroll
+        for (int k = 0; k < PREF; ++k) tmp[k] = src[min(i0 + tid + k * LOOP_NT, n16 - 1)];  // clamped: in bounds
+#pragma unroll
+        for (int k = 0; k < PREF; ++k) {
+          const int i = i0 + tid + k * LOOP_NT;
+          if (i < n16) dst[i] = tmp[k];
+        }
+      }
       reg = sReg;
     }
     for (int t = tid; t < Cc; t += LOOP_NT) {
@@ -124,6 +145,19 @@ __global__ __launch_bounds__(LOOP_NT) void loop_kernel(Dims D, LoopArgs a, int n
     const int32_t* qptr = tptr + (C + 1);
     const Ent* lists = (const Ent*)(reg + CL.lists);
 
+    // value rows of this chunk and slice (bank-independent): loaded now, used in B
+    constexpr int VPT = (128 * COLS + LOOP_NT - 1) / LOOP_NT;  // per thread, chunk <= 128
+    float vreg[VPT];
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const int idx = tid + k * LOOP_NT;
+      const int t = idx / COLS, c = idx % COLS;
+      vreg[k] = 0.0f;
+      if (t < Cc && col0 + c < D.d) {
+        const long long g = ((long long)b * D.T + t0 + t) * D.H + h;
+        vreg[k] = to_f<A>(values[g * D.d + col0 + c]);
+      }
+    }
     // A: gathers. Waves 0..3 take the write terms (H), waves 4..7 the read terms (G); group = token.
     {
       const int kind = wv >> 2;
@@ -136,39 +170,43 @@ __global__ __launch_bounds__(LOOP_NT) void loop_kernel(Dims D, LoopArgs a, int n
         for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
         if (valid) {
           const Pair* pp = base + (long long)t * n;
-#pragma unroll 16
-          for (int i = 0; i < n; ++i) {
-            const Pair p = pp[i];
-            float v[EPL];
-            Lane<Bk>::load(bank + (long long)p.slot * D.d + mycol, v);
+          constexpr int GB = 12;  // row loads in flight per lane
+          for (int i0 = 0; i0 < n; i0 += GB) {
+            uint4 raw[GB];
+            float cf[GB];
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) acc[e] += p.coef * v[e];
+            for (int u = 0; u < GB; ++u) {
+              const int i = i0 + u;
+              cf[u] = 0.0f;
+              if (i < n) {
+                const Pair p = pp[i];
+                cf[u] = p.coef;
+                raw[u] = *(const uint4*)(bank + (long long)p.slot * D.ld + mycol);
+              }
+            }
+#pragma unroll
+            for (int u = 0; u < GB; ++u) {
+              if (i0 + u < n) {
+                float v[EPL];
+                Lane<Bk>::unpack(raw[u], v);
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) acc[e] += cf[u] * v[e];
+              }
+            }
           }
         }
 #pragma unroll
         for (int e = 0; e < EPL; ++e) dst[t * COLS + q * EPL + e] = acc[e];
       }
     }
-    // prefetch the scatter part of the plan region into registers while the solve runs
-    uint4 pf[PREF];
     const int s16 = (int)(((long long)(cnt.nseg + cnt.nev) * 8 + 15) >> 4);
-    if (STAGED) {
-      const uint4* src = (const uint4*)(greg + CL.scat);
-#pragma unroll
-      for (int k = 0; k < PREF; ++k) {
-        const int i = tid + k * LOOP_NT;
-        if (i < s16) pf[k] = src[i];
-      }
-    }
     __syncthreads();
     // B: U = beta v - alpha beta H (in place), then delta = T U.
-    for (int idx = tid; idx < Cc * COLS; idx += LOOP_NT) {
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const int idx = tid + k * LOOP_NT;
       const int t = idx / COLS, c = idx % COLS;
-      if (col0 + c < D.d) {
-        const long long g = ((long long)b * D.T + t0 + t) * D.H + h;
-        const float v = to_f<A>(values[g * D.d + col0 + c]);
-        sH[idx] = sB[t] * v - sA[t] * sB[t] * sH[idx];
-      }
+      if (t < Cc && col0 + c < D.d) sH[idx] = sB[t] * vreg[k] - sA[t] * sB[t] * sH[idx];
     }
     __syncthreads();
     for (int idx = tid; idx < Cc * COLS; idx += LOOP_NT) {
@@ -193,19 +231,23 @@ __global__ __launch_bounds__(LOOP_NT) void loop_kernel(Dims D, LoopArgs a, int n
     if (STAGED) {
       __syncthreads();  // the LDS region is reused
       uint4* dst = (uint4*)sReg;
-#pragma unroll
-      for (int k = 0; k < PREF; ++k) {
-        const int i = tid + k * LOOP_NT;
-        if (i < s16) dst[i] = pf[k];
-      }
       const uint4* src = (const uint4*)(greg + CL.scat);
-      for (int i = tid + PREF * LOOP_NT; i < s16; i += LOOP_NT) dst[i] = src[i];
+      for (int i0 = 0; i0 < s16; i0 += LOOP_NT * PREF) {
+        uint4 tmp[PREF];
+#pragma unroll
+        for (int k = 0; k < PREF; ++k) tmp[k] = src[min(i0 + tid + k * LOOP_NT, s16 - 1)];
+#pragma unroll
+        for (int k = 0; k < PREF; ++k) {
+          const int i = i0 + tid + k * LOOP_NT;
+          if (i < s16) dst[i] = tmp[k];
+        }
+      }
       __syncthreads();
       segs = (const Seg*)sReg;
     }
     const Ev* ev = (const Ev*)(segs + cnt.nseg);
     if (valid) {
-      constexpr int UB = 4;
+      constexpr int UB = 8;
       for (int sg0 = wv * 16 + grp; sg0 < cnt.nseg; sg0 += NW * 16 * UB) {
         float m[UB][EPL];
         int beg[UB], end[UB];
@@ -219,7 +261,7 @@ __global__ __launch_bounds__(LOOP_NT) void loop_kernel(Dims D, LoopArgs a, int n
             const Seg sgm = segs[sg];
             beg[u] = sg > 0 ? segs[sg - 1].end : 0;
             end[u] = sgm.end;
-            p[u] = bank + (long long)sgm.slot * D.d + mycol;
+            p[u] = bank + (long long)sgm.slot * D.ld + mycol;
             Lane<Bk>::load(p[u], m[u]);
           }
         }

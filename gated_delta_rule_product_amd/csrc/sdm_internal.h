@@ -31,6 +31,7 @@ struct Dims {
   int act, bank;        // sdm_dtype
   long long N;          // slots per head
   long long rows;       // bank rows per stream
+  long long ld;         // bank row stride (elements)
   int nch;              // chunks per stream
   int S;                // streams = B * H
 };

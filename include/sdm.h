@@ -31,7 +31,8 @@
  *   subkeys                              [H, sum_f n_f, dk] act dtype; factor tables stacked in factor order
  *   values, out                          [B, T, H, d]      act dtype
  *   forget_gate, input_gate              [B, T, H]         act dtype
- *   bank                                 [B, H, bank_rows, d] bank dtype; rows >= N are never read or written
+ *   bank                                 [B, H, bank_rows, d] bank dtype, row pitch bank_row_stride elements (padding
+ *                                        columns are never read or written); rows >= N are never read or written
  *   write_idx, read_idx (optional)       [B, T, H, W] / [B, T, H, R] int32 slot ids, best first
  *
  * Ownership and streams: the caller owns every buffer. The library never allocates or frees memory (temporary
@@ -60,7 +61,8 @@ typedef enum {
   SDM_ERR_RANGE = 2,          /* a size outside the supported range (listed per field of sdm_config) */
   SDM_ERR_BANK_TOO_SMALL = 3, /* bank_rows < N (CHANGELOG 2.0.0 "Behavior changes": a too-small cache bank) */
   SDM_ERR_ALIAS = 4,          /* an output overlaps an input or another output (except bank_out == bank_in) */
-  SDM_ERR_LAYOUT = 5,         /* misaligned pointer or head_dim not a multiple of the bank's 16-byte lane */
+  SDM_ERR_LAYOUT = 5,         /* misaligned pointer, head_dim not a multiple of the bank's 16-byte lane, or a bank
+                                 row stride below head_dim or not a 16-byte multiple */
   SDM_ERR_WORKSPACE = 6,      /* workspace NULL, too small, or not 256-byte aligned */
   SDM_ERR_DEVICE = 7,         /* the current device is not gfx950 (no fallback path) */
   SDM_ERR_HIP = 8,            /* a HIP runtime call failed (launch or device query) */
@@ -83,6 +85,9 @@ typedef struct {
   int32_t act_dtype;        /* sdm_dtype of queries, sub-keys, values, gates and out: F32 or BF16 */
   int32_t bank_dtype;       /* sdm_dtype of the bank: F32 or BF16 */
   int64_t bank_rows;        /* rows per stream in the bank buffer, >= N */
+  int64_t bank_row_stride;  /* elements from one bank row to the next (0: head_dim); >= head_dim, 16-byte multiple.
+                               A pitch that is not a power of two (e.g. head_dim + 128 bytes) spreads the rows over
+                               HBM channels evenly when rows are gathered in column slices. */
 } sdm_config;
 
 enum { SDM_OP_TOPK = 0, SDM_OP_WRITE_READ = 1, SDM_OP_DECODE = 2 };
@@ -116,7 +121,7 @@ sdm_status sdm_write_read(const sdm_config* cfg, const void* write_keys, const v
 /* Single-token decode step (CHANGELOG 2.0.0 "New": a single-token decode kernel; lumen PR #29: donate). cfg.tokens
  * must be 1; every stream (b, h) takes one token. bank_out == bank_in: donated, the successor is written in place.
  * bank_out disjoint from bank_in: copied successor, bank_out receives a full copy of bank_in with the W rows
- * updated, and bank_in is left unchanged. Partial overlap -> SDM_ERR_ALIAS. Both forms run one body and give
+ * updated (the whole buffer, B * H * bank_rows * bank_row_stride elements, is copied), and bank_in is left unchanged. Partial overlap -> SDM_ERR_ALIAS. Both forms run one body and give
  * bit-identical bank_out, out and indices. Rows are rounded to the bank dtype before the read. */
 sdm_status sdm_decode_step(const sdm_config* cfg, const void* write_keys, const void* read_queries,
                            const void* values, const void* forget_gate, const void* input_gate, const void* subkeys,

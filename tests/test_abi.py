@@ -75,6 +75,8 @@ def test_workspace_sizes(lib):
     (dict(chunk_size=0), B.SDM_ERR_RANGE),
     (dict(chunk_size=128, num_writes=128, widths=(256, 256)), B.SDM_ERR_RANGE),  # C * W > 8192
     (dict(bank_rows=1023), B.SDM_ERR_BANK_TOO_SMALL),
+    (dict(bank_row_stride=60), B.SDM_ERR_LAYOUT),                          # pitch below head_dim
+    (dict(bank_row_stride=66), B.SDM_ERR_LAYOUT),                          # pitch not a 16-byte multiple
     (dict(tokens=-1), B.SDM_ERR_RANGE),
 ])
 def test_refusals(lib, kw, status):
@@ -85,6 +87,12 @@ def test_refusals(lib, kw, status):
     s, _ = _status(_cfg(**kw))
     assert s == status, (kw, B.STATUS_NAMES.get(s), B.last_error())
     assert B.last_error() != ""
+
+
+def test_padded_pitch_accepted_and_sized(lib):
+    s0, n0 = _status(_cfg(bank_row_stride=0))
+    s1, n1 = _status(_cfg(bank_row_stride=96))
+    assert s0 == B.SDM_OK and s1 == B.SDM_OK and n0 == n1  # the workspace does not depend on the pitch
 
 
 def test_candidate_limit(lib):

@@ -33,15 +33,31 @@ def to_np(t):
     return t.float().cpu().numpy() if t.dtype != torch.int32 else t.cpu().numpy()
 
 
-def run_gpu(s, x, chunk_size=None, bank=None):
+SENTINEL = 1234.5
+
+
+def padded_bank(arr, dtype, pitch):
+    """Device bank view [B, H, rows, d] with rows `pitch` elements apart; padding filled with a sentinel."""
+    B, H, rows, d = arr.shape
+    buf = torch.full((B, H, rows, pitch), SENTINEL, dtype=dtype, device=DEV)
+    g = buf[..., :d]
+    g.copy_(torch.from_numpy(np.ascontiguousarray(arr)).to(DEV).to(dtype))
+    return g
+
+
+def run_gpu(s, x, chunk_size=None, bank=None, pitch=None):
     at, bt = TORCH_DT[s.act], TORCH_DT[s.bank]
     t = {k: to_dev(x[k], at) for k in ("wkeys", "rq", "values", "alpha", "beta", "subkeys")}
-    g_bank = to_dev(x["bank"] if bank is None else bank, bt)
+    src = x["bank"] if bank is None else bank
+    g_bank = to_dev(src, bt) if pitch is None else padded_bank(src, bt, pitch)
     out, widx, ridx = binding.sdm_write_read(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"], t["subkeys"],
                                              g_bank, widths=s.widths, num_writes=s.num_writes,
                                              num_reads=s.num_reads, chunk_size=chunk_size or s.chunk_size,
                                              want_index=True)
     torch.cuda.synchronize()
+    if pitch is not None and pitch > s.head_dim:
+        pad = g_bank._base[..., s.head_dim:]
+        assert bool((pad == SENTINEL).all()), "padding columns of the bank were written"
     return to_np(out), to_np(g_bank), to_np(widx), to_np(ridx)
 
 
@@ -177,6 +193,19 @@ def test_write_read_bank_rows_padding():
     check_parity(s, (out, bank, widx, ridx), ref)
 
 
+@pytest.mark.parametrize("bank_dt,pitch", [("f32", 96), ("f32", 68), ("bf16", 72), ("bf16", 128)])
+def test_write_read_padded_bank_pitch(bank_dt, pitch):
+    """A bank whose rows are `pitch` elements apart: same results, padding never touched."""
+    s = synth.WORKLOADS["tiny_1k"].with_(tokens=150, batch=2, heads=2, bank=bank_dt, act="bf16", chunk_size=32)
+    x = synth.make_inputs(s, seed=12)
+    print(f"write/read pitch={pitch} bank={bank_dt}", flush=True)
+    got = run_gpu(s, x, pitch=pitch)
+    check_parity(s, got, run_oracle(s, x))
+    same = run_gpu(s, x)
+    for u, v in zip(got, same):
+        assert np.array_equal(u, v)  # the pitch does not change the arithmetic
+
+
 def test_write_read_bitwise_repeatable():
     s = synth.WORKLOADS["tiny_1k"].with_(tokens=192, batch=2, heads=2)
     x = synth.make_inputs(s, seed=9)
@@ -245,6 +274,27 @@ def test_decode_matches_oracle_and_donated_equals_copied(bank_dt):
         ref_bank = ref["bank"]
 
 
+def test_decode_padded_pitch_donated_equals_copied():
+    s = synth.WORKLOADS["decode_b128"].with_(batch=8)
+    x = synth.make_inputs(s, seed=13)
+    t = {k: to_dev(x[k], torch.float32) for k in ("wkeys", "rq", "values", "alpha", "beta", "subkeys")}
+    kw = dict(widths=s.widths, num_writes=s.num_writes, num_reads=s.num_reads, want_index=True)
+    args = (t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"], t["subkeys"])
+    b_don = padded_bank(x["bank"], torch.float32, 288)
+    b_in = padded_bank(x["bank"], torch.float32, 288)
+    b_out = binding.alloc_bank(s.batch, s.heads, s.rows, s.head_dim, torch.float32, DEV, pitch=288)
+    o1, w1, r1, _ = binding.sdm_decode_step(*args, b_don, **kw)
+    o2, w2, r2, _ = binding.sdm_decode_step(*args, b_in, b_out, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(b_don, b_out) and torch.equal(w1, w2)
+    ref = oracle.write_read(x["wkeys"], x["rq"], x["values"], x["alpha"], x["beta"], x["subkeys"], x["bank"],
+                            s.widths, s.num_writes, s.num_reads)
+    assert np.array_equal(w1.cpu().numpy(), ref["widx"]) and np.array_equal(r1.cpu().numpy(), ref["ridx"])
+    assert rowwise_rel(to_np(o1), ref["out"]) <= 1e-5
+    assert rowwise_rel(to_np(b_don), ref["bank"]) <= 1e-5
+    assert bool((b_don._base[..., s.head_dim:] == SENTINEL).all())
+
+
 def test_decode_equals_one_token_write_read():
     s = synth.WORKLOADS["tiny_1k"].with_(tokens=1, batch=3, heads=2)
     x = synth.make_inputs(s, seed=11)
@@ -268,7 +318,7 @@ def test_layer_65k_full_size():
     print("full-size layer_65k: generating inputs", flush=True)
     x = synth.make_inputs(s)
     print("full-size layer_65k: GPU", flush=True)
-    gpu = run_gpu(s, x)
+    gpu = run_gpu(s, x, pitch=binding.bank_pitch(s.head_dim, torch.float32))
     print("full-size layer_65k: oracle", flush=True)
     ref = run_oracle(s, x)
     e = check_parity(s, gpu, ref)
