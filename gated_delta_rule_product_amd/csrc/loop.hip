@@ -64,7 +64,7 @@ constexpr int PREF = 8;  // uint4 per thread of register prefetch (64 KiB per 51
 
 __host__ __device__ inline size_t loop_region_lds(int C, int W, int R) {
   const ChunkLayout CL = chunk_layout(C, W, R);
-  const long long r1 = CL.pairs_bytes + CL.ptrs_bytes + CL.lists_cap;
+  const long long r1 = CL.pairs_bytes + CL.wlast_bytes + CL.ptrs_bytes + CL.lists_cap;
   return (size_t)(r1 > CL.scat_cap ? r1 : CL.scat_cap);
 }
 
@@ -118,7 +118,8 @@ __global__ __launch_bounds__(LOOP_NT) void loop_kernel(Dims D, LoopArgs a, int n
     // region pointers (LDS copy or global)
     const unsigned char* reg = greg;
     if (STAGED) {
-      const int n16 = (int)((CL.pairs_bytes + CL.ptrs_bytes + (long long)(cnt.nnzT + cnt.nnzQ) * 8 + 15) >> 4);
+      const int n16 =
+          (int)((CL.pairs_bytes + CL.wlast_bytes + CL.ptrs_bytes + (long long)(cnt.nnzT + cnt.nnzQ) * 8 + 15) >> 4);
       const uint4* src = (const uint4*)greg;
       uint4* dst = (uint4*)sReg;
       for (int i0 = 0; i0 < n16; i0 += LOOP_NT * PREF) {  // batches of PREF loads per thread in flight
@@ -284,12 +285,261 @@ __global__ __launch_bounds__(LOOP_NT) void loop_kernel(Dims D, LoopArgs a, int n
   }
 }
 
+// ------------------------------------------------------------------------------------------- held-row variant
+// For chunks with C a power of two and C * W <= 128 * 32: the 128 lane groups split every token's write terms in
+// gpt = 128 / C equal parts of at most 32 rows (float32 banks; a bfloat16 bank's lanes carry twice the elements
+// and do not fit); each group keeps its gathered rows M_0[S_ti] in registers, so the
+// scatter applies a slot's events to the row its last event's holder loaded and only stores (no second read).
+// H and G are summed per part, then over the parts in order (bitwise repeatable).
+template <typename Bk> struct Hold { static constexpr int N = 32; };  // float32 banks only (see launch_loop_t)
+
+__host__ __device__ inline size_t loop_held_lds_bytes(int C, int W, int R, int cols) {
+  const int gpt = 128 / C;
+  size_t n = (size_t)2 * C * gpt * cols * 4 + (size_t)2 * C * cols * 4 + (size_t)C * 8;
+  return align16(n) + loop_region_lds(C, W, R);
+}
+
+template <typename A, typename Bk>
+__global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, int nslices) {
+  constexpr int EPL = Lane<Bk>::EPL;
+  constexpr int COLS = 4 * EPL;
+  constexpr int HOLD = Hold<Bk>::N;
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int C = D.C, W = D.W, R = D.R;
+  const int gpt = 128 / C;
+  const int tpw = W / gpt, tpr = R / gpt;
+  float* sHp = (float*)lds;                 // [C * gpt][COLS] partial H
+  float* sGp = sHp + C * gpt * COLS;        // [C * gpt][COLS] partial G
+  float* sH = sGp + C * gpt * COLS;         // [C][COLS]  U
+  float* sD = sH + C * COLS;                // [C][COLS]  delta
+  float* sA = sD + C * COLS;                // [C]
+  float* sB = sA + C;                       // [C]
+  unsigned char* sReg = lds + align16((long long)2 * C * gpt * COLS * 4 + (long long)2 * C * COLS * 4 + (long long)C * 8);
+
+  const int nblk = gridDim.x;
+  int w = blockIdx.x;
+  if ((nblk & 7) == 0) w = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+  const int st = w / nslices, slice = w % nslices;
+  const int b = st / D.H, h = st % D.H;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int q = lane & 3, grp = lane >> 2;
+  const int G = wv * 16 + grp;              // lane group 0..127
+  const int gt = G / gpt, part = G % gpt;   // its token and part
+  const int col0 = slice * COLS;
+  const int mycol = col0 + q * EPL;
+  const bool valid = mycol < D.d;
+  Bk* bank = (Bk*)a.bank + (long long)st * D.rows * D.ld;
+  const A* alpha = (const A*)a.alpha;
+  const A* beta = (const A*)a.beta;
+  const A* values = (const A*)a.values;
+  A* out = (A*)a.out;
+  const ChunkLayout CL = chunk_layout(C, W, R);
+  const long long CW = (long long)C * W;
+
+  ChunkCounts cnt = a.counts[(long long)st * D.nch];
+  for (int ch = 0; ch < D.nch; ++ch) {
+    const int t0 = ch * C;
+    const int Cc = min(C, D.T - t0);
+    const long long cidx = (long long)st * D.nch + ch;
+    const unsigned char* greg = a.chunks + cidx * CL.bytes;
+    const ChunkCounts next = a.counts[ch + 1 < D.nch ? cidx + 1 : cidx];
+    {
+      const int n16 =
+          (int)((CL.pairs_bytes + CL.wlast_bytes + CL.ptrs_bytes + (long long)(cnt.nnzT + cnt.nnzQ) * 8 + 15) >> 4);
+      const uint4* src = (const uint4*)greg;
+      uint4* dst = (uint4*)sReg;
+      for (int i0 = 0; i0 < n16; i0 += LOOP_NT * PREF) {
+        uint4 tmp[PREF];
+#pragma unroll
+        for (int k = 0; k < PREF; ++k) tmp[k] = src[min(i0 + tid + k * LOOP_NT, n16 - 1)];  // clamped: in bounds
+#pragma unroll
+        for (int k = 0; k < PREF; ++k) {
+          const int i = i0 + tid + k * LOOP_NT;
+          if (i < n16) dst[i] = tmp[k];
+        }
+      }
+    }
+    for (int t = tid; t < Cc; t += LOOP_NT) {
+      const long long g = ((long long)b * D.T + t0 + t) * D.H + h;
+      sA[t] = to_f<A>(alpha[g]);
+      sB[t] = to_f<A>(beta[g]);
+    }
+    __syncthreads();
+    const Pair* pw = (const Pair*)(sReg + CL.pairs);
+    const Pair* pr = pw + CW;
+    const int32_t* wl = (const int32_t*)(sReg + CL.wlast);
+    const int32_t* tptr = (const int32_t*)(sReg + CL.ptrs);
+    const int32_t* qptr = tptr + (C + 1);
+    const Ent* lists = (const Ent*)(sReg + CL.lists);
+
+    constexpr int VPT = (128 * COLS + LOOP_NT - 1) / LOOP_NT;
+    float vreg[VPT];
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const int idx = tid + k * LOOP_NT;
+      const int t = idx / COLS, c = idx % COLS;
+      vreg[k] = 0.0f;
+      if (t < Cc && col0 + c < D.d) {
+        const long long g = ((long long)b * D.T + t0 + t) * D.H + h;
+        vreg[k] = to_f<A>(values[g * D.d + col0 + c]);
+      }
+    }
+    const bool act = valid && gt < Cc;
+    // A1: write terms, rows held in registers
+    uint4 held[HOLD];
+    int segi[HOLD];
+    {
+      const Pair* pp = pw + (long long)gt * W + part * tpw;
+      const int32_t* wp = wl + (long long)gt * W + part * tpw;
+#pragma unroll
+      for (int u = 0; u < HOLD; ++u) {
+        segi[u] = -1;
+        if (act && u < tpw) {
+          held[u] = *(const uint4*)(bank + (long long)pp[u].slot * D.ld + mycol);
+          segi[u] = wp[u];
+        }
+      }
+      float acc[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
+#pragma unroll
+      for (int u = 0; u < HOLD; ++u) {
+        if (act && u < tpw) {
+          float v[EPL];
+          Lane<Bk>::unpack(held[u], v);
+          const float cf = pp[u].coef;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[e] += cf * v[e];
+        }
+      }
+      if (gt < Cc) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) sHp[G * COLS + q * EPL + e] = acc[e];
+      }
+    }
+    // A2: read terms
+    {
+      const Pair* pp = pr + (long long)gt * R + part * tpr;
+      float acc[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
+      if (act) {
+        constexpr int GB = 8;
+        for (int i0 = 0; i0 < tpr; i0 += GB) {
+          uint4 raw[GB];
+#pragma unroll
+          for (int u = 0; u < GB; ++u)
+            if (i0 + u < tpr) raw[u] = *(const uint4*)(bank + (long long)pp[i0 + u].slot * D.ld + mycol);
+#pragma unroll
+          for (int u = 0; u < GB; ++u) {
+            if (i0 + u < tpr) {
+              float v[EPL];
+              Lane<Bk>::unpack(raw[u], v);
+              const float cf = pp[i0 + u].coef;
+#pragma unroll
+              for (int e = 0; e < EPL; ++e) acc[e] += cf * v[e];
+            }
+          }
+        }
+      }
+      if (gt < Cc) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) sGp[G * COLS + q * EPL + e] = acc[e];
+      }
+    }
+    const int s16 = (int)(((long long)(cnt.nseg + cnt.nev) * 8 + 15) >> 4);
+    __syncthreads();
+    // B: U = beta v - alpha beta H (H = sum of the parts, in order), then delta = T U.
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const int idx = tid + k * LOOP_NT;
+      const int t = idx / COLS, c = idx % COLS;
+      if (t < Cc) {
+        float hv = 0.0f;
+        for (int pp = 0; pp < gpt; ++pp) hv += sHp[(t * gpt + pp) * COLS + c];
+        sH[idx] = sB[t] * vreg[k] - sA[t] * sB[t] * hv;
+      }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < Cc * COLS; idx += LOOP_NT) {
+      const int t = idx / COLS, c = idx % COLS;
+      float d = 0.0f;
+      for (int e = tptr[t]; e < tptr[t + 1]; ++e) d += lists[e].val * sH[lists[e].col * COLS + c];
+      sD[idx] = d;
+    }
+    __syncthreads();
+    // C: read output.
+    for (int idx = tid; idx < Cc * COLS; idx += LOOP_NT) {
+      const int t = idx / COLS, c = idx % COLS;
+      if (col0 + c < D.d) {
+        float o = 0.0f;
+        for (int pp = 0; pp < gpt; ++pp) o += sGp[(t * gpt + pp) * COLS + c];
+        for (int e = qptr[t]; e < qptr[t + 1]; ++e) o += lists[e].val * sD[lists[e].col * COLS + c];
+        const long long g = ((long long)b * D.T + t0 + t) * D.H + h;
+        out[g * D.d + col0 + c] = from_f<A>(o);
+      }
+    }
+    __syncthreads();  // the LDS region is reused for the scatter part
+    {
+      uint4* dst = (uint4*)sReg;
+      const uint4* src = (const uint4*)(greg + CL.scat);
+      for (int i0 = 0; i0 < s16; i0 += LOOP_NT * PREF) {
+        uint4 tmp[PREF];
+#pragma unroll
+        for (int k = 0; k < PREF; ++k) tmp[k] = src[min(i0 + tid + k * LOOP_NT, s16 - 1)];
+#pragma unroll
+        for (int k = 0; k < PREF; ++k) {
+          const int i = i0 + tid + k * LOOP_NT;
+          if (i < s16) dst[i] = tmp[k];
+        }
+      }
+    }
+    __syncthreads();
+    // D: the holder of each slot's last event applies the slot's events in token order and stores the row.
+    {
+      const Seg* segs = (const Seg*)sReg;
+      const Ev* ev = (const Ev*)(segs + cnt.nseg);
+#pragma unroll
+      for (int u = 0; u < HOLD; ++u) {
+        const int g = segi[u];
+        if (g >= 0) {
+          float m[EPL];
+          Lane<Bk>::unpack(held[u], m);
+          const Seg sg = segs[g];
+          for (int e = g > 0 ? segs[g - 1].end : 0; e < sg.end; ++e) {
+            const Ev x = ev[e];
+            const float al = sA[x.tok];
+#pragma unroll
+            for (int k = 0; k < EPL; ++k) m[k] = al * m[k] + x.w * sD[x.tok * COLS + q * EPL + k];
+          }
+          Lane<Bk>::store(bank + (long long)sg.slot * D.ld + mycol, m);
+        }
+      }
+    }
+    cnt = next;
+    __syncthreads();
+  }
+}
+
 template <typename A, typename Bk>
 static hipError_t launch_loop_t(const Dims& D, const LoopArgs& a, hipStream_t st) {
   constexpr int COLS = 4 * Lane<Bk>::EPL;
   const int nslices = (D.d + COLS - 1) / COLS;
   const long long nblk = (long long)D.S * nslices;
   const size_t staged = loop_lds_bytes(D.C, D.W, D.R, COLS, true);
+  const bool pow2 = (D.C & (D.C - 1)) == 0;
+  const int gpt = 128 / D.C;
+  const bool held_ok = pow2 && D.C <= 128 && D.W % gpt == 0 && D.R % gpt == 0 && D.W / gpt <= Hold<Bk>::N &&
+                       D.W >= gpt && D.R >= gpt;
+  if constexpr (sizeof(Bk) == 4) {
+    if (held_ok && loop_held_lds_bytes(D.C, D.W, D.R, COLS) <= 150 * 1024) {
+      const size_t lds = loop_held_lds_bytes(D.C, D.W, D.R, COLS);
+      (void)hipFuncSetAttribute((const void*)loop_held_kernel<A, Bk>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)lds);
+      hipLaunchKernelGGL((loop_held_kernel<A, Bk>), dim3((unsigned)nblk), dim3(LOOP_NT), lds, st, D, a, nslices);
+      return hipGetLastError();
+    }
+  }
   if (staged <= 150 * 1024) {
     (void)hipFuncSetAttribute((const void*)loop_kernel<A, Bk, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)staged);

@@ -88,6 +88,7 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
   unsigned char* reg = a.chunks + cidx * CL.bytes;
   Pair* pw = (Pair*)(reg + CL.pairs);
   Pair* pr = pw + CW;
+  int32_t* wlast = (int32_t*)(reg + CL.wlast);
   int32_t* tptr = (int32_t*)(reg + CL.ptrs);
   int32_t* qptr = tptr + (C + 1);
   Ent* lists = (Ent*)(reg + CL.lists);
@@ -164,8 +165,10 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
         ++g;
         segs[g].slot = sslot[e];
       }
-      if (e == E - 1 || sslot[e + 1] != sslot[e]) segs[g].end = e + 1;
+      const bool last = e == E - 1 || sslot[e + 1] != sslot[e];
+      if (last) segs[g].end = e + 1;
       const int evi = sev[e];
+      wlast[evi] = last ? g : -1;
       Ev x;
       x.w = a.wwt[wbase + evi];
       x.tok = evi / W;

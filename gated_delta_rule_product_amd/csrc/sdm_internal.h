@@ -72,19 +72,22 @@ struct Seg {
 
 // Per-chunk plan region (byte offsets; every part 16-byte aligned). Written by the plan kernel, read by the loop.
 //   pairs  [C*W] write gather terms, then [C*R] read gather terms            (token-major, fixed size)
+//   wlast  [C*W] per write term: its slot segment's index if it is the segment's last event, else -1
 //   ptrs   tptr[C+1], qptr[C+1] row starts of the two lists                  (fixed size)
 //   lists  T entries [nnzT] immediately followed by Q entries [nnzQ]         (packed; capacity C(C+1))
 //   scat   segments [nseg] immediately followed by events [E]                 (packed; capacity 2 C W)
 struct ChunkLayout {
-  long long pairs, ptrs, lists, scat, bytes;
-  long long pairs_bytes, ptrs_bytes, lists_cap, scat_cap;
+  long long pairs, wlast, ptrs, lists, scat, bytes;
+  long long pairs_bytes, wlast_bytes, ptrs_bytes, lists_cap, scat_cap;
 };
 __host__ __device__ inline long long align16(long long x) { return (x + 15) & ~15LL; }
 __host__ __device__ inline ChunkLayout chunk_layout(int C, int W, int R) {
   ChunkLayout L;
   L.pairs = 0;
   L.pairs_bytes = align16((long long)C * (W + R) * 8);
-  L.ptrs = L.pairs + L.pairs_bytes;
+  L.wlast = L.pairs + L.pairs_bytes;
+  L.wlast_bytes = align16((long long)C * W * 4);
+  L.ptrs = L.wlast + L.wlast_bytes;
   L.ptrs_bytes = align16((long long)2 * (C + 1) * 4);
   L.lists = L.ptrs + L.ptrs_bytes;
   L.lists_cap = align16((long long)C * (C + 1) * 8);
