@@ -64,7 +64,7 @@ constexpr int PREF = 8;  // uint4 per thread of register prefetch (64 KiB per 51
 
 __host__ __device__ inline size_t loop_region_lds(int C, int W, int R) {
   const ChunkLayout CL = chunk_layout(C, W, R);
-  const long long r1 = CL.pairs_bytes + CL.wlast_bytes + CL.ptrs_bytes + CL.lists_cap;
+  const long long r1 = CL.wpairs_bytes + CL.wlast_bytes + CL.rpairs_bytes + CL.ptrs_bytes + CL.lists_cap;
   return (size_t)(r1 > CL.scat_cap ? r1 : CL.scat_cap);
 }
 
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(LOOP_NT) void loop_kernel(Dims D, LoopArgs a, int n
     const unsigned char* reg = greg;
     if (STAGED) {
       const int n16 =
-          (int)((CL.pairs_bytes + CL.wlast_bytes + CL.ptrs_bytes + (long long)(cnt.nnzT + cnt.nnzQ) * 8 + 15) >> 4);
+          (int)((CL.lists + (long long)(cnt.nnzT + cnt.nnzQ) * 8 + 15) >> 4);
       const uint4* src = (const uint4*)greg;
       uint4* dst = (uint4*)sReg;
       for (int i0 = 0; i0 < n16; i0 += LOOP_NT * PREF) {  // batches of PREF loads per thread in flight
@@ -140,8 +140,8 @@ __global__ __launch_bounds__(LOOP_NT) void loop_kernel(Dims D, LoopArgs a, int n
       sB[t] = to_f<A>(beta[g]);
     }
     if (STAGED) __syncthreads();
-    const Pair* pw = (const Pair*)(reg + CL.pairs);
-    const Pair* pr = pw + CW;
+    const Pair* pw = (const Pair*)(reg + CL.wpairs);
+    const Pair* pr = (const Pair*)(reg + CL.rpairs);
     const int32_t* tptr = (const int32_t*)(reg + CL.ptrs);
     const int32_t* qptr = tptr + (C + 1);
     const Ent* lists = (const Ent*)(reg + CL.lists);
@@ -286,17 +286,46 @@ __global__ __launch_bounds__(LOOP_NT) void loop_kernel(Dims D, LoopArgs a, int n
 }
 
 // ------------------------------------------------------------------------------------------- held-row variant
-// For chunks with C a power of two and C * W <= 128 * 32: the 128 lane groups split every token's write terms in
-// gpt = 128 / C equal parts of at most 32 rows (float32 banks; a bfloat16 bank's lanes carry twice the elements
-// and do not fit); each group keeps its gathered rows M_0[S_ti] in registers, so the
-// scatter applies a slot's events to the row its last event's holder loaded and only stores (no second read).
-// H and G are summed per part, then over the parts in order (bitwise repeatable).
+// For chunks with C a power of two and C * W <= 128 * 32 (float32 banks): the 128 lane groups split every token's
+// write terms in gpt = 128 / C equal parts of at most 32 rows; each group keeps its gathered rows M_0[S_ti] in
+// registers, and the group holding a slot's last event of the chunk applies the slot's events to that row and
+// stores it (no second read of the bank). A slot written once needs only the holder's own term; slots written more
+// than once take their events from the plan's multi-event table. H and G are summed per part, then over the parts
+// in order (bitwise repeatable). Staging: the write terms and their last-event codes first (one coalesced pass),
+// then, while the held rows are in flight, the read terms, T, Q and the multi-event table. T/Q lists and
+// multi-event tables larger than their LDS areas are read from the plan region in HBM instead.
 template <typename Bk> struct Hold { static constexpr int N = 32; };  // float32 banks only (see launch_loop_t)
+constexpr int HELD_LISTS_LDS = 16 * 1024;  // T and Q entries kept in LDS
+constexpr int HELD_MULTI_LDS = 16 * 1024;  // multi-event table kept in LDS
 
+__host__ __device__ inline size_t loop_held_region(int C, int W, int R) {
+  const ChunkLayout CL = chunk_layout(C, W, R);
+  return (size_t)(CL.wpairs_bytes + CL.wlast_bytes + CL.rpairs_bytes + CL.ptrs_bytes + HELD_LISTS_LDS +
+                  HELD_MULTI_LDS);
+}
+
+// LDS: partial H and G [C*gpt][cols], U and delta [C][cols], gates [C], then the staged region (mirror of the plan
+// region from wpairs to the lists, lists capped) and the multi-event table.
 __host__ __device__ inline size_t loop_held_lds_bytes(int C, int W, int R, int cols) {
   const int gpt = 128 / C;
   size_t n = (size_t)2 * C * gpt * cols * 4 + (size_t)2 * C * cols * 4 + (size_t)C * 8;
-  return align16(n) + loop_region_lds(C, W, R);
+  return align16(n) + loop_held_region(C, W, R);
+}
+
+// Copies n16 16-byte words from global to LDS, NB loads in flight per thread.
+template <int NB>
+__device__ __forceinline__ void stage16(const uint4* __restrict__ src, uint4* dst, int n16) {
+  const int tid = threadIdx.x;
+  for (int i0 = 0; i0 < n16; i0 += LOOP_NT * NB) {
+    uint4 tmp[NB];
+#pragma unroll
+    for (int k = 0; k < NB; ++k) tmp[k] = src[min(i0 + tid + k * LOOP_NT, n16 - 1)];  // clamped: in bounds
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int i = i0 + tid + k * LOOP_NT;
+      if (i < n16) dst[i] = tmp[k];
+    }
+  }
 }
 
 template <typename A, typename Bk>
@@ -314,7 +343,11 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
   float* sD = sH + C * COLS;                // [C][COLS]  delta
   float* sA = sD + C * COLS;                // [C]
   float* sB = sA + C;                       // [C]
-  unsigned char* sReg = lds + align16((long long)2 * C * gpt * COLS * 4 + (long long)2 * C * COLS * 4 + (long long)C * 8);
+  unsigned char* sReg =
+      lds + align16((long long)2 * C * gpt * COLS * 4 + (long long)2 * C * COLS * 4 + (long long)C * 8);
+  const ChunkLayout CL = chunk_layout(C, W, R);
+  const long long lists_lds = CL.lists;                                   // offset of the lists in sReg
+  MSeg* msegs_lds = (MSeg*)(sReg + CL.lists + HELD_LISTS_LDS);
 
   const int nblk = gridDim.x;
   int w = blockIdx.x;
@@ -333,8 +366,11 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
   const A* beta = (const A*)a.beta;
   const A* values = (const A*)a.values;
   A* out = (A*)a.out;
-  const ChunkLayout CL = chunk_layout(C, W, R);
-  const long long CW = (long long)C * W;
+  const Pair* pw = (const Pair*)(sReg + CL.wpairs);
+  const int32_t* wl = (const int32_t*)(sReg + CL.wlast);
+  const Pair* pr = (const Pair*)(sReg + CL.rpairs);
+  const int32_t* tptr = (const int32_t*)(sReg + CL.ptrs);
+  const int32_t* qptr = tptr + (C + 1);
 
   ChunkCounts cnt = a.counts[(long long)st * D.nch];
   for (int ch = 0; ch < D.nch; ++ch) {
@@ -343,35 +379,29 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
     const long long cidx = (long long)st * D.nch + ch;
     const unsigned char* greg = a.chunks + cidx * CL.bytes;
     const ChunkCounts next = a.counts[ch + 1 < D.nch ? cidx + 1 : cidx];
-    {
-      const int n16 =
-          (int)((CL.pairs_bytes + CL.wlast_bytes + CL.ptrs_bytes + (long long)(cnt.nnzT + cnt.nnzQ) * 8 + 15) >> 4);
-      const uint4* src = (const uint4*)greg;
-      uint4* dst = (uint4*)sReg;
-      for (int i0 = 0; i0 < n16; i0 += LOOP_NT * PREF) {
-        uint4 tmp[PREF];
+    const bool act = valid && gt < Cc;
+    // write terms and last-event codes
+    stage16<PREF>((const uint4*)greg, (uint4*)sReg, (int)((CL.wpairs_bytes + CL.wlast_bytes) >> 4));
+    __syncthreads();
+    // A1: held write rows
+    uint4 held[HOLD];
+    const int wbase = gt * W + part * tpw;
 #pragma unroll
-        for (int k = 0; k < PREF; ++k) tmp[k] = src[min(i0 + tid + k * LOOP_NT, n16 - 1)];  // clamped: in bounds
-#pragma unroll
-        for (int k = 0; k < PREF; ++k) {
-          const int i = i0 + tid + k * LOOP_NT;
-          if (i < n16) dst[i] = tmp[k];
-        }
-      }
-    }
+    for (int u = 0; u < HOLD; ++u)
+      if (act && u < tpw) held[u] = *(const uint4*)(bank + (long long)pw[wbase + u].slot * D.ld + mycol);
+    // while they arrive: read terms, T and Q (lists in LDS if they fit), multi-event table, gates, value rows
+    const long long lbytes = (long long)(cnt.nnzT + cnt.nnzQ) * 8;
+    const bool llds = lbytes <= HELD_LISTS_LDS;
+    stage16<2>((const uint4*)(greg + CL.rpairs), (uint4*)(sReg + CL.rpairs),
+               (int)((CL.rpairs_bytes + CL.ptrs_bytes + (llds ? lbytes : 0) + 15) >> 4));
+    const long long mbytes = (long long)cnt.nmseg * 16 + (long long)cnt.nmev * 8;
+    const bool mlds = mbytes <= HELD_MULTI_LDS;
+    if (mlds) stage16<2>((const uint4*)(greg + CL.multi), (uint4*)msegs_lds, (int)((mbytes + 15) >> 4));
     for (int t = tid; t < Cc; t += LOOP_NT) {
       const long long g = ((long long)b * D.T + t0 + t) * D.H + h;
       sA[t] = to_f<A>(alpha[g]);
       sB[t] = to_f<A>(beta[g]);
     }
-    __syncthreads();
-    const Pair* pw = (const Pair*)(sReg + CL.pairs);
-    const Pair* pr = pw + CW;
-    const int32_t* wl = (const int32_t*)(sReg + CL.wlast);
-    const int32_t* tptr = (const int32_t*)(sReg + CL.ptrs);
-    const int32_t* qptr = tptr + (C + 1);
-    const Ent* lists = (const Ent*)(sReg + CL.lists);
-
     constexpr int VPT = (128 * COLS + LOOP_NT - 1) / LOOP_NT;
     float vreg[VPT];
 #pragma unroll
@@ -384,21 +414,7 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
         vreg[k] = to_f<A>(values[g * D.d + col0 + c]);
       }
     }
-    const bool act = valid && gt < Cc;
-    // A1: write terms, rows held in registers
-    uint4 held[HOLD];
-    int segi[HOLD];
     {
-      const Pair* pp = pw + (long long)gt * W + part * tpw;
-      const int32_t* wp = wl + (long long)gt * W + part * tpw;
-#pragma unroll
-      for (int u = 0; u < HOLD; ++u) {
-        segi[u] = -1;
-        if (act && u < tpw) {
-          held[u] = *(const uint4*)(bank + (long long)pp[u].slot * D.ld + mycol);
-          segi[u] = wp[u];
-        }
-      }
       float acc[EPL];
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
@@ -407,7 +423,7 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
         if (act && u < tpw) {
           float v[EPL];
           Lane<Bk>::unpack(held[u], v);
-          const float cf = pp[u].coef;
+          const float cf = pw[wbase + u].coef;
 #pragma unroll
           for (int e = 0; e < EPL; ++e) acc[e] += cf * v[e];
         }
@@ -417,9 +433,11 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
         for (int e = 0; e < EPL; ++e) sHp[G * COLS + q * EPL + e] = acc[e];
       }
     }
+    __syncthreads();  // read terms, lists and multi-event table staged
+    const Ent* lists = llds ? (const Ent*)(sReg + lists_lds) : (const Ent*)(greg + CL.lists);
     // A2: read terms
     {
-      const Pair* pp = pr + (long long)gt * R + part * tpr;
+      const Pair* pp = pr + gt * R + part * tpr;
       float acc[EPL];
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
@@ -447,7 +465,6 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
         for (int e = 0; e < EPL; ++e) sGp[G * COLS + q * EPL + e] = acc[e];
       }
     }
-    const int s16 = (int)(((long long)(cnt.nseg + cnt.nev) * 8 + 15) >> 4);
     __syncthreads();
     // B: U = beta v - alpha beta H (H = sum of the parts, in order), then delta = T U.
 #pragma unroll
@@ -479,40 +496,33 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
         out[g * D.d + col0 + c] = from_f<A>(o);
       }
     }
-    __syncthreads();  // the LDS region is reused for the scatter part
-    {
-      uint4* dst = (uint4*)sReg;
-      const uint4* src = (const uint4*)(greg + CL.scat);
-      for (int i0 = 0; i0 < s16; i0 += LOOP_NT * PREF) {
-        uint4 tmp[PREF];
-#pragma unroll
-        for (int k = 0; k < PREF; ++k) tmp[k] = src[min(i0 + tid + k * LOOP_NT, s16 - 1)];
-#pragma unroll
-        for (int k = 0; k < PREF; ++k) {
-          const int i = i0 + tid + k * LOOP_NT;
-          if (i < s16) dst[i] = tmp[k];
-        }
-      }
-    }
-    __syncthreads();
     // D: the holder of each slot's last event applies the slot's events in token order and stores the row.
-    {
-      const Seg* segs = (const Seg*)sReg;
-      const Ev* ev = (const Ev*)(segs + cnt.nseg);
+    if (act) {
+      const MSeg* msegs = mlds ? msegs_lds : (const MSeg*)(greg + CL.multi);
+      const Ev* mev = (const Ev*)(msegs + cnt.nmseg);
 #pragma unroll
       for (int u = 0; u < HOLD; ++u) {
-        const int g = segi[u];
-        if (g >= 0) {
-          float m[EPL];
-          Lane<Bk>::unpack(held[u], m);
-          const Seg sg = segs[g];
-          for (int e = g > 0 ? segs[g - 1].end : 0; e < sg.end; ++e) {
-            const Ev x = ev[e];
-            const float al = sA[x.tok];
+        if (u < tpw) {
+          const int code = wl[wbase + u];
+          if (code != -1) {
+            float m[EPL];
+            Lane<Bk>::unpack(held[u], m);
+            const Pair p = pw[wbase + u];
+            if (code == -2) {  // the slot's only event: own token, own weight
+              const float al = sA[gt];
 #pragma unroll
-            for (int k = 0; k < EPL; ++k) m[k] = al * m[k] + x.w * sD[x.tok * COLS + q * EPL + k];
+              for (int k = 0; k < EPL; ++k) m[k] = al * m[k] + p.coef * sD[gt * COLS + q * EPL + k];
+            } else {
+              const MSeg sg = msegs[code];
+              for (int e = sg.beg; e < sg.end; ++e) {
+                const Ev x = mev[e];
+                const float al = sA[x.tok];
+#pragma unroll
+                for (int k = 0; k < EPL; ++k) m[k] = al * m[k] + x.w * sD[x.tok * COLS + q * EPL + k];
+              }
+            }
+            Lane<Bk>::store(bank + (long long)p.slot * D.ld + mycol, m);
           }
-          Lane<Bk>::store(bank + (long long)sg.slot * D.ld + mycol, m);
         }
       }
     }

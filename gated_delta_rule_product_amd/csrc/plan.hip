@@ -26,7 +26,7 @@ __host__ __device__ inline size_t plan_lds_bytes(int C, int W) {
   const size_t dense = (size_t)C * C * 4;
   if (dense > keys) keys = dense;
   return keys + CW * 4 /*sslot*/ + CW * 2 /*sev*/ + CW * 2 /*pos*/ + (size_t)C * 12 /*alpha, beta, flags*/ +
-         (size_t)PLAN_NT * 4 /*scan*/ + 16;
+         (size_t)PLAN_NT * 4 * 3 /*scans*/ + 16;
 }
 
 // Row-sorted sparse compaction of the dense rows 0..Cc-1 (columns 0..t for row t) into ptr / out; returns nnz.
@@ -86,8 +86,8 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
   const long long rbase = ((long long)st * D.T + t0) * R;
   const ChunkLayout CL = chunk_layout(C, W, R);
   unsigned char* reg = a.chunks + cidx * CL.bytes;
-  Pair* pw = (Pair*)(reg + CL.pairs);
-  Pair* pr = pw + CW;
+  Pair* pw = (Pair*)(reg + CL.wpairs);
+  Pair* pr = (Pair*)(reg + CL.rpairs);
   int32_t* wlast = (int32_t*)(reg + CL.wlast);
   int32_t* tptr = (int32_t*)(reg + CL.ptrs);
   int32_t* qptr = tptr + (C + 1);
@@ -105,7 +105,10 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
   float* sB = sA + C;
   int32_t* sHasL = (int32_t*)(sB + C);
   int32_t* scan = sHasL + C;
-  __shared__ int s_nseg;
+  int32_t* scanM = scan + PLAN_NT;   // multi-event segment starts per thread range
+  int32_t* scanE = scanM + PLAN_NT;  // multi-event events per thread range
+  __shared__ int s_nseg, s_nmseg;
+  MSeg* msegs = (MSeg*)(reg + CL.multi);
 
   // 1. write events -> sort keys (slot, event index); gates of the chunk.
   for (int e = tid; e < Ep2; e += PLAN_NT) {
@@ -134,45 +137,78 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
   }
   __syncthreads();
 
-  // 2. segments (runs of equal slots): ids by a block scan over contiguous per-thread ranges.
+  // 2. segments (runs of equal slots) and the multi-event table: ids by block scans over contiguous ranges.
   const int per = (E + PLAN_NT - 1) / PLAN_NT;
   const int lo = min(E, tid * per), hi = min(E, lo + per);
-  int cnt = 0;
-  for (int e = lo; e < hi; ++e) cnt += (e == 0 || sslot[e] != sslot[e - 1]);
-  scan[tid] = cnt;
+  {
+    int cnt = 0, cm = 0, ce = 0;
+    for (int e = lo; e < hi; ++e) {
+      const bool first = e == 0 || sslot[e] != sslot[e - 1];
+      const bool multi = !first || (e + 1 < E && sslot[e + 1] == sslot[e]);
+      cnt += first;
+      cm += first && multi;
+      ce += multi;
+    }
+    scan[tid] = cnt;
+    scanM[tid] = cm;
+    scanE[tid] = ce;
+  }
   __syncthreads();
   if (tid == 0) {
-    int run = 0;
+    int run = 0, rm = 0, re = 0;
     for (int i = 0; i < PLAN_NT; ++i) {
-      const int c = scan[i];
+      const int c = scan[i], m = scanM[i], x = scanE[i];
       scan[i] = run;
+      scanM[i] = rm;
+      scanE[i] = re;
       run += c;
+      rm += m;
+      re += x;
     }
     ChunkCounts cc;
     cc.nnzT = cc.nnzQ = 0;
     cc.nseg = run;
     cc.nev = E;
+    cc.nmseg = rm;
+    cc.nmev = re;
+    cc.pad0 = cc.pad1 = 0;
     a.counts[cidx] = cc;
     s_nseg = run;
+    s_nmseg = rm;
   }
   __syncthreads();
   const int nseg = s_nseg;
   Ev* ev = (Ev*)(segs + nseg);
+  Ev* mev = (Ev*)(msegs + s_nmseg);
   {
-    int g = scan[tid] - 1;  // segment id of the element before lo
+    int g = scan[tid] - 1;   // segment id of the element before lo
+    int m = scanM[tid] - 1;  // multi-event segment id of the element before lo
+    int me = scanE[tid];     // next multi-event event slot
     for (int e = lo; e < hi; ++e) {
-      if (e == 0 || sslot[e] != sslot[e - 1]) {
+      const bool first = e == 0 || sslot[e] != sslot[e - 1];
+      const bool last = e == E - 1 || sslot[e + 1] != sslot[e];
+      const bool multi = !(first && last);
+      if (first) {
         ++g;
         segs[g].slot = sslot[e];
+        if (multi) {
+          ++m;
+          msegs[m].slot = sslot[e];
+          msegs[m].beg = me;
+          msegs[m].pad = 0;
+        }
       }
-      const bool last = e == E - 1 || sslot[e + 1] != sslot[e];
       if (last) segs[g].end = e + 1;
       const int evi = sev[e];
-      wlast[evi] = last ? g : -1;
       Ev x;
       x.w = a.wwt[wbase + evi];
       x.tok = evi / W;
       ev[e] = x;
+      if (multi) {
+        mev[me++] = x;
+        if (last) msegs[m].end = me;
+      }
+      wlast[evi] = !last ? -1 : (multi ? m : -2);
     }
   }
   __syncthreads();

@@ -71,35 +71,47 @@ struct Seg {
 };
 
 // Per-chunk plan region (byte offsets; every part 16-byte aligned). Written by the plan kernel, read by the loop.
-//   pairs  [C*W] write gather terms, then [C*R] read gather terms            (token-major, fixed size)
-//   wlast  [C*W] per write term: its slot segment's index if it is the segment's last event, else -1
+//   wpairs [C*W] write gather terms (slot, a)                               (token-major, fixed size)
+//   wlast  [C*W] per write term: -1 if it is not its slot's last event in the chunk; -2 if it is the slot's only
+//          event; else the index of the slot in the multi-event table
+//   rpairs [C*R] read gather terms (slot, b)                                (token-major, fixed size)
 //   ptrs   tptr[C+1], qptr[C+1] row starts of the two lists                  (fixed size)
 //   lists  T entries [nnzT] immediately followed by Q entries [nnzQ]         (packed; capacity C(C+1))
 //   scat   segments [nseg] immediately followed by events [E]                 (packed; capacity 2 C W)
+//   multi  slots written more than once: MSeg [nmseg] then their events Ev [nmev] (packed; capacity 3 C W / 2)
 struct ChunkLayout {
-  long long pairs, wlast, ptrs, lists, scat, bytes;
-  long long pairs_bytes, wlast_bytes, ptrs_bytes, lists_cap, scat_cap;
+  long long wpairs, wlast, rpairs, ptrs, lists, scat, multi, bytes;
+  long long wpairs_bytes, wlast_bytes, rpairs_bytes, ptrs_bytes, lists_cap, scat_cap, multi_cap;
 };
 __host__ __device__ inline long long align16(long long x) { return (x + 15) & ~15LL; }
 __host__ __device__ inline ChunkLayout chunk_layout(int C, int W, int R) {
   ChunkLayout L;
-  L.pairs = 0;
-  L.pairs_bytes = align16((long long)C * (W + R) * 8);
-  L.wlast = L.pairs + L.pairs_bytes;
+  L.wpairs = 0;
+  L.wpairs_bytes = align16((long long)C * W * 8);
+  L.wlast = L.wpairs + L.wpairs_bytes;
   L.wlast_bytes = align16((long long)C * W * 4);
-  L.ptrs = L.wlast + L.wlast_bytes;
+  L.rpairs = L.wlast + L.wlast_bytes;
+  L.rpairs_bytes = align16((long long)C * R * 8);
+  L.ptrs = L.rpairs + L.rpairs_bytes;
   L.ptrs_bytes = align16((long long)2 * (C + 1) * 4);
   L.lists = L.ptrs + L.ptrs_bytes;
   L.lists_cap = align16((long long)C * (C + 1) * 8);
   L.scat = L.lists + L.lists_cap;
   L.scat_cap = align16((long long)2 * C * W * 8);
-  L.bytes = L.scat + L.scat_cap;
+  L.multi = L.scat + L.scat_cap;
+  L.multi_cap = align16((long long)C * W / 2 * 16 + (long long)C * W * 8);
+  L.bytes = L.multi + L.multi_cap;
   return L;
 }
 
+// A slot written more than once in a chunk: its events are mev[beg, end) of the multi-event table.
+struct MSeg {
+  int32_t slot, beg, end, pad;
+};
+
 // Per-chunk counts written by the plan.
 struct ChunkCounts {
-  int32_t nnzT, nnzQ, nseg, nev;
+  int32_t nnzT, nnzQ, nseg, nev, nmseg, nmev, pad0, pad1;
 };
 
 // ------------------------------------------------------------------------------------------- device helpers
