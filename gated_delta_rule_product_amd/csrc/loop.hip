@@ -287,29 +287,44 @@ __global__ __launch_bounds__(LOOP_NT) void loop_kernel(Dims D, LoopArgs a, int n
 
 // ------------------------------------------------------------------------------------------- held-row variant
 // For chunks with C a power of two and C * W <= 128 * 32 (float32 banks): the 128 lane groups split every token's
-// write terms in gpt = 128 / C equal parts of at most 32 rows; each group keeps its gathered rows M_0[S_ti] in
-// registers, and the group holding a slot's last event of the chunk applies the slot's events to that row and
-// stores it (no second read of the bank). A slot written once needs only the holder's own term; slots written more
-// than once take their events from the plan's multi-event table. H and G are summed per part, then over the parts
-// in order (bitwise repeatable). Staging: the write terms and their last-event codes first (one coalesced pass),
-// then, while the held rows are in flight, the read terms, T, Q and the multi-event table. T/Q lists and
-// multi-event tables larger than their LDS areas are read from the plan region in HBM instead.
+// write terms, and its read terms, in gpt = 128 / C equal parts of at most 32; each group keeps its gathered write
+// rows M_0[S_ti] in registers, and the group holding a slot's last event of the chunk applies the slot's events to
+// that row and stores it (no second read of the bank). A slot written once needs only the holder's own term; slots
+// written more than once take their events from the plan's multi-event table. H and G are summed per part, then
+// over the parts in order (bitwise repeatable).
+//
+// Memory pipeline per chunk: the write terms (slot, coefficient, last-event code) sit in one of two LDS buffers,
+// filled during the previous chunk; each lane reads 8 of its group's read terms straight into registers and the
+// group shares them with quad DPP broadcasts. Loads are issued oldest first: next chunk's write terms, read terms,
+// T/Q lists and multi-event table, gates, values, then held rows and read rows interleaved (16 held, 16 read,
+// 16 held, 16 read), so that each wait for a batch leaves the younger batches in flight. T/Q lists and multi-event
+// tables larger than their LDS areas are read from the plan region in HBM instead.
 template <typename Bk> struct Hold { static constexpr int N = 32; };  // float32 banks only (see launch_loop_t)
-constexpr int HELD_LISTS_LDS = 16 * 1024;  // T and Q entries kept in LDS
-constexpr int HELD_MULTI_LDS = 16 * 1024;  // multi-event table kept in LDS
+constexpr int HELD_LISTS_LDS = 12 * 1024;  // T and Q entries kept in LDS
+constexpr int HELD_MULTI_LDS = 12 * 1024;  // multi-event table kept in LDS
+constexpr int HELD_RPL = 8;                // read terms per lane (32 per group)
 
-__host__ __device__ inline size_t loop_held_region(int C, int W, int R) {
-  const ChunkLayout CL = chunk_layout(C, W, R);
-  return (size_t)(CL.wpairs_bytes + CL.wlast_bytes + CL.rpairs_bytes + CL.ptrs_bytes + HELD_LISTS_LDS +
-                  HELD_MULTI_LDS);
+// one LDS buffer of write terms: pairs [C * W], then last-event codes [C * W] (the plan region's first two sections)
+__host__ __device__ inline long long held_wterm_bytes(int C, int W) {
+  return align16((long long)C * W * 8) + align16((long long)C * W * 4);
 }
 
-// LDS: partial H and G [C*gpt][cols], U and delta [C][cols], gates [C], then the staged region (mirror of the plan
-// region from wpairs to the lists, lists capped) and the multi-event table.
-__host__ __device__ inline size_t loop_held_lds_bytes(int C, int W, int R, int cols) {
+__host__ __device__ inline long long held_sums_bytes(int C, int cols) {
   const int gpt = 128 / C;
-  size_t n = (size_t)2 * C * gpt * cols * 4 + (size_t)2 * C * cols * 4 + (size_t)C * 8;
-  return align16(n) + loop_held_region(C, W, R);
+  return align16((long long)2 * C * gpt * cols * 4 + (long long)2 * C * cols * 4 + (long long)C * 8);
+}
+
+// LDS: partial H and G [C*gpt][cols], U and delta [C][cols], gates [C]; two write-term buffers; T/Q row pointers and
+// lists; the multi-event table.
+__host__ __device__ inline size_t loop_held_lds_bytes(int C, int W, int cols) {
+  return (size_t)(held_sums_bytes(C, cols) + 2 * held_wterm_bytes(C, W) + align16((long long)2 * (C + 1) * 4) +
+                  HELD_LISTS_LDS + HELD_MULTI_LDS);
+}
+
+// Value of `v` in lane K of each quad of lanes.
+template <int K>
+__device__ __forceinline__ int quad_bcast(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, K * 0x55, 0xF, 0xF, false);
 }
 
 // Copies n16 16-byte words from global to LDS, NB loads in flight per thread.
@@ -328,6 +343,67 @@ __device__ __forceinline__ void stage16(const uint4* __restrict__ src, uint4* ds
   }
 }
 
+// Read term u (0..31) of the lane's group: held by lane u / 8 of the quad, as pair u % 8 of its 4 words.
+template <int U>
+__device__ __forceinline__ Pair read_term(const uint4 (&rp)[HELD_RPL / 2]) {
+  constexpr int K = U / HELD_RPL, E = U % HELD_RPL;
+  const uint4 w = rp[E / 2];
+  Pair p;
+  p.slot = quad_bcast<K>((int)((E & 1) ? w.z : w.x));
+  p.coef = __int_as_float(quad_bcast<K>((int)((E & 1) ? w.w : w.y)));
+  return p;
+}
+
+template <int U0, int N>
+struct ReadBatch {
+  template <typename Bk>
+  __device__ __forceinline__ static void load(uint4 (&raw)[N], const uint4 (&rp)[HELD_RPL / 2], const Bk* bank,
+                                              long long ld, int mycol, bool act, int tpr) {
+    ReadBatch<U0, N - 1>::load(*(uint4(*)[N - 1]) & raw, rp, bank, ld, mycol, act, tpr);
+    const Pair p = read_term<U0 + N - 1>(rp);
+    const long long off = (act && U0 + N - 1 < tpr) ? (long long)p.slot * ld + mycol : 0;
+    raw[N - 1] = *(const uint4*)(bank + off);
+  }
+  __device__ __forceinline__ static void coefs(float (&cf)[N], const uint4 (&rp)[HELD_RPL / 2]) {
+    ReadBatch<U0, N - 1>::coefs(*(float(*)[N - 1]) & cf, rp);
+    cf[N - 1] = read_term<U0 + N - 1>(rp).coef;
+  }
+};
+template <int U0>
+struct ReadBatch<U0, 0> {
+  template <typename Bk>
+  __device__ __forceinline__ static void load(uint4 (&)[0], const uint4 (&)[HELD_RPL / 2], const Bk*, long long, int,
+                                              bool, int) {}
+  __device__ __forceinline__ static void coefs(float (&)[0], const uint4 (&)[HELD_RPL / 2]) {}
+};
+
+// Sliding window over the 32 row registers of a lane: step U consumes read row U (the oldest load in flight) into
+// G, then issues held write row U into the same registers, so 32 loads stay in flight with 32 registers of rows.
+template <int U, int N>
+struct Window {
+  template <typename Bk>
+  __device__ __forceinline__ static void run(uint4 (&row)[N], const uint4 (&rp)[HELD_RPL / 2],
+                                             float (&g)[Lane<Bk>::EPL], const Pair* pw, const Bk* bank, long long ld,
+                                             int mycol, bool act, int tpr, int tpw) {
+    if (act && U < tpr) {
+      const float cf = read_term<U>(rp).coef;
+      float v[Lane<Bk>::EPL];
+      Lane<Bk>::unpack(row[U], v);
+#pragma unroll
+      for (int e = 0; e < Lane<Bk>::EPL; ++e) g[e] += cf * v[e];
+    }
+    const long long off = (act && U < tpw) ? (long long)pw[U].slot * ld + mycol : 0;
+    row[U] = *(const uint4*)(bank + off);
+    Window<U + 1, N>::run(row, rp, g, pw, bank, ld, mycol, act, tpr, tpw);
+  }
+};
+template <int N>
+struct Window<N, N> {
+  template <typename Bk>
+  __device__ __forceinline__ static void run(uint4 (&)[N], const uint4 (&)[HELD_RPL / 2], float (&)[Lane<Bk>::EPL],
+                                             const Pair*, const Bk*, long long, int, bool, int, int) {}
+};
+
 template <typename A, typename Bk>
 __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, int nslices) {
   constexpr int EPL = Lane<Bk>::EPL;
@@ -343,11 +419,14 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
   float* sD = sH + C * COLS;                // [C][COLS]  delta
   float* sA = sD + C * COLS;                // [C]
   float* sB = sA + C;                       // [C]
-  unsigned char* sReg =
-      lds + align16((long long)2 * C * gpt * COLS * 4 + (long long)2 * C * COLS * 4 + (long long)C * 8);
   const ChunkLayout CL = chunk_layout(C, W, R);
-  const long long lists_lds = CL.lists;                                   // offset of the lists in sReg
-  MSeg* msegs_lds = (MSeg*)(sReg + CL.lists + HELD_LISTS_LDS);
+  const long long WT = held_wterm_bytes(C, W);
+  unsigned char* sW0 = lds + held_sums_bytes(C, COLS);
+  unsigned char* sLst = sW0 + 2 * WT;       // T/Q row pointers, then lists (mirror of the plan region's layout)
+  const long long ptrs_b = align16((long long)2 * (C + 1) * 4);
+  MSeg* msegs_lds = (MSeg*)(sLst + ptrs_b + HELD_LISTS_LDS);
+  const int32_t* tptr = (const int32_t*)sLst;
+  const int32_t* qptr = tptr + (C + 1);
 
   const int nblk = gridDim.x;
   int w = blockIdx.x;
@@ -366,11 +445,13 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
   const A* beta = (const A*)a.beta;
   const A* values = (const A*)a.values;
   A* out = (A*)a.out;
-  const Pair* pw = (const Pair*)(sReg + CL.wpairs);
-  const int32_t* wl = (const int32_t*)(sReg + CL.wlast);
-  const Pair* pr = (const Pair*)(sReg + CL.rpairs);
-  const int32_t* tptr = (const int32_t*)(sReg + CL.ptrs);
-  const int32_t* qptr = tptr + (C + 1);
+  const int nw16 = (int)(WT >> 4);          // <= 3072: C * W <= 4096
+  constexpr int NWP = 6;                    // 16-byte words of the next write terms per thread
+  constexpr int NST = 4;                    // 16-byte words of row pointers, lists and multi-event table per thread
+
+  // write terms of the first chunk
+  stage16<NWP>((const uint4*)(a.chunks + (long long)st * D.nch * CL.bytes), (uint4*)sW0, nw16);
+  __syncthreads();
 
   ChunkCounts cnt = a.counts[(long long)st * D.nch];
   for (int ch = 0; ch < D.nch; ++ch) {
@@ -378,29 +459,51 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
     const int Cc = min(C, D.T - t0);
     const long long cidx = (long long)st * D.nch + ch;
     const unsigned char* greg = a.chunks + cidx * CL.bytes;
-    const ChunkCounts next = a.counts[ch + 1 < D.nch ? cidx + 1 : cidx];
+    const bool more = ch + 1 < D.nch;
+    const ChunkCounts next = a.counts[more ? cidx + 1 : cidx];
     const bool act = valid && gt < Cc;
-    // write terms and last-event codes
-    stage16<PREF>((const uint4*)greg, (uint4*)sReg, (int)((CL.wpairs_bytes + CL.wlast_bytes) >> 4));
-    __syncthreads();
-    // A1: held write rows
-    uint4 held[HOLD];
-    const int wbase = gt * W + part * tpw;
+    unsigned char* sWc = sW0 + (ch & 1) * WT;
+    unsigned char* sWn = sW0 + ((ch + 1) & 1) * WT;
+    const Pair* pw = (const Pair*)sWc;
+    const int32_t* wl = (const int32_t*)(sWc + align16((long long)C * W * 8));
+
+    // loads, oldest first ------------------------------------------------------------------------------------
+    // next chunk's write terms (into the other buffer, free since the previous chunk's scatter)
+    uint4 wpf[NWP];
+    {
+      const uint4* src = (const uint4*)(more ? greg + CL.bytes : greg);  // last chunk: loaded, never stored
 #pragma unroll
-    for (int u = 0; u < HOLD; ++u)
-      if (act && u < tpw) held[u] = *(const uint4*)(bank + (long long)pw[wbase + u].slot * D.ld + mycol);
-    // while they arrive: read terms, T and Q (lists in LDS if they fit), multi-event table, gates, value rows
+      for (int k = 0; k < NWP; ++k) wpf[k] = src[min(tid + k * LOOP_NT, nw16 - 1)];
+    }
+    // the group's read terms: lane q holds terms [8q, 8q + 8)
+    uint4 rp[HELD_RPL / 2];
+    {
+      const Pair* gp = (const Pair*)(greg + CL.rpairs) + gt * R + part * tpr + q * HELD_RPL;
+#pragma unroll
+      for (int k = 0; k < HELD_RPL / 2; ++k) rp[k] = *(const uint4*)(gp + 2 * k);  // inside the chunk region
+    }
+    // row pointers, T/Q lists (if they fit) and the multi-event table (if it fits)
     const long long lbytes = (long long)(cnt.nnzT + cnt.nnzQ) * 8;
     const bool llds = lbytes <= HELD_LISTS_LDS;
-    stage16<2>((const uint4*)(greg + CL.rpairs), (uint4*)(sReg + CL.rpairs),
-               (int)((CL.rpairs_bytes + CL.ptrs_bytes + (llds ? lbytes : 0) + 15) >> 4));
     const long long mbytes = (long long)cnt.nmseg * 16 + (long long)cnt.nmev * 8;
     const bool mlds = mbytes <= HELD_MULTI_LDS;
-    if (mlds) stage16<2>((const uint4*)(greg + CL.multi), (uint4*)msegs_lds, (int)((mbytes + 15) >> 4));
-    for (int t = tid; t < Cc; t += LOOP_NT) {
-      const long long g = ((long long)b * D.T + t0 + t) * D.H + h;
-      sA[t] = to_f<A>(alpha[g]);
-      sB[t] = to_f<A>(beta[g]);
+    const int n1 = (int)((ptrs_b + (llds ? lbytes : 0) + 15) >> 4);
+    const int n12 = n1 + (mlds ? (int)((mbytes + 15) >> 4) : 0);  // <= NST * LOOP_NT
+    const uint4* src1 = (const uint4*)(greg + CL.ptrs);
+    const uint4* src2 = (const uint4*)(greg + CL.multi) - n1;
+    uint4* dst1 = (uint4*)sLst;
+    uint4* dst2 = (uint4*)msegs_lds - n1;
+    uint4 stg[NST];
+#pragma unroll
+    for (int k = 0; k < NST; ++k) {
+      const int i = min(tid + k * LOOP_NT, n12 - 1);  // n12 >= 1: the row pointers are never empty
+      stg[k] = i < n1 ? src1[i] : src2[i];
+    }
+    float ga = 0.0f, gb = 0.0f;
+    if (tid < Cc) {
+      const long long g = ((long long)b * D.T + t0 + tid) * D.H + h;
+      ga = to_f<A>(alpha[g]);
+      gb = to_f<A>(beta[g]);
     }
     constexpr int VPT = (128 * COLS + LOOP_NT - 1) / LOOP_NT;
     float vreg[VPT];
@@ -414,6 +517,38 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
         vreg[k] = to_f<A>(values[g * D.d + col0 + c]);
       }
     }
+    // read rows: all 32 in flight (lanes without a term load row 0 and ignore it, so the count is fixed)
+    const long long ld = D.ld;
+    uint4 row[HOLD];
+    ReadBatch<0, HOLD>::load(row, rp, bank, ld, mycol, act, tpr);
+    // next write terms to the other buffer, staged words and gates to LDS (waits for the older loads only)
+#pragma unroll
+    for (int k = 0; k < NWP; ++k) {
+      const int i = tid + k * LOOP_NT;
+      if (more && i < nw16) ((uint4*)sWn)[i] = wpf[k];
+    }
+#pragma unroll
+    for (int k = 0; k < NST; ++k) {
+      const int i = tid + k * LOOP_NT;
+      if (i < n12) {
+        if (i < n1) dst1[i] = stg[k]; else dst2[i] = stg[k];
+      }
+    }
+    if (tid < Cc) {
+      sA[tid] = ga;
+      sB[tid] = gb;
+    }
+    // sliding window: consume read row u (oldest), then reuse its registers for held write row u
+    const int wbase = gt * W + part * tpw;
+    float gacc[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) gacc[e] = 0.0f;
+    Window<0, HOLD>::run(row, rp, gacc, pw + wbase, bank, ld, mycol, act, tpr, tpw);
+    if (gt < Cc) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) sGp[G * COLS + q * EPL + e] = gacc[e];
+    }
+    // H from the held rows
     {
       float acc[EPL];
 #pragma unroll
@@ -422,7 +557,7 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
       for (int u = 0; u < HOLD; ++u) {
         if (act && u < tpw) {
           float v[EPL];
-          Lane<Bk>::unpack(held[u], v);
+          Lane<Bk>::unpack(row[u], v);
           const float cf = pw[wbase + u].coef;
 #pragma unroll
           for (int e = 0; e < EPL; ++e) acc[e] += cf * v[e];
@@ -433,39 +568,8 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
         for (int e = 0; e < EPL; ++e) sHp[G * COLS + q * EPL + e] = acc[e];
       }
     }
-    __syncthreads();  // read terms, lists and multi-event table staged
-    const Ent* lists = llds ? (const Ent*)(sReg + lists_lds) : (const Ent*)(greg + CL.lists);
-    // A2: read terms
-    {
-      const Pair* pp = pr + gt * R + part * tpr;
-      float acc[EPL];
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
-      if (act) {
-        constexpr int GB = 8;
-        for (int i0 = 0; i0 < tpr; i0 += GB) {
-          uint4 raw[GB];
-#pragma unroll
-          for (int u = 0; u < GB; ++u)
-            if (i0 + u < tpr) raw[u] = *(const uint4*)(bank + (long long)pp[i0 + u].slot * D.ld + mycol);
-#pragma unroll
-          for (int u = 0; u < GB; ++u) {
-            if (i0 + u < tpr) {
-              float v[EPL];
-              Lane<Bk>::unpack(raw[u], v);
-              const float cf = pp[i0 + u].coef;
-#pragma unroll
-              for (int e = 0; e < EPL; ++e) acc[e] += cf * v[e];
-            }
-          }
-        }
-      }
-      if (gt < Cc) {
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) sGp[G * COLS + q * EPL + e] = acc[e];
-      }
-    }
-    __syncthreads();
+    __syncthreads();  // partial sums, gates, lists and multi-event table in LDS
+    const Ent* lists = llds ? (const Ent*)(sLst + ptrs_b) : (const Ent*)(greg + CL.lists);
     // B: U = beta v - alpha beta H (H = sum of the parts, in order), then delta = T U.
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
@@ -506,7 +610,7 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
           const int code = wl[wbase + u];
           if (code != -1) {
             float m[EPL];
-            Lane<Bk>::unpack(held[u], m);
+            Lane<Bk>::unpack(row[u], m);
             const Pair p = pw[wbase + u];
             if (code == -2) {  // the slot's only event: own token, own weight
               const float al = sA[gt];
@@ -540,10 +644,10 @@ static hipError_t launch_loop_t(const Dims& D, const LoopArgs& a, hipStream_t st
   const bool pow2 = (D.C & (D.C - 1)) == 0;
   const int gpt = 128 / D.C;
   const bool held_ok = pow2 && D.C <= 128 && D.W % gpt == 0 && D.R % gpt == 0 && D.W / gpt <= Hold<Bk>::N &&
-                       D.W >= gpt && D.R >= gpt;
+                       D.R / gpt <= 4 * HELD_RPL && (D.R / gpt) % 2 == 0 && D.W >= gpt && D.R >= gpt;
   if constexpr (sizeof(Bk) == 4) {
-    if (held_ok && loop_held_lds_bytes(D.C, D.W, D.R, COLS) <= 150 * 1024) {
-      const size_t lds = loop_held_lds_bytes(D.C, D.W, D.R, COLS);
+    if (held_ok && loop_held_lds_bytes(D.C, D.W, COLS) <= 160 * 1024) {
+      const size_t lds = loop_held_lds_bytes(D.C, D.W, COLS);
       (void)hipFuncSetAttribute((const void*)loop_held_kernel<A, Bk>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                 (int)lds);
       hipLaunchKernelGGL((loop_held_kernel<A, Bk>), dim3((unsigned)nblk), dim3(LOOP_NT), lds, st, D, a, nslices);
