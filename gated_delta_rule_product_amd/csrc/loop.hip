@@ -286,45 +286,38 @@ __global__ __launch_bounds__(LOOP_NT) void loop_kernel(Dims D, LoopArgs a, int n
 }
 
 // ------------------------------------------------------------------------------------------- held-row variant
-// For chunks with C a power of two and C * W <= 128 * 32 (float32 banks): the 128 lane groups split every token's
-// write terms, and its read terms, in gpt = 128 / C equal parts of at most 32; each group keeps its gathered write
-// rows M_0[S_ti] in registers, and the group holding a slot's last event of the chunk applies the slot's events to
-// that row and stores it (no second read of the bank). A slot written once needs only the holder's own term; slots
-// written more than once take their events from the plan's multi-event table. H and G are summed per part, then
-// over the parts in order (bitwise repeatable).
+// For chunks with C a power of two, 8 <= C <= 128, and at most 32 write and 32 read terms per part (float32
+// banks): the 128 lane groups split every token's write terms, and its read terms, in gpt = 128 / C equal parts;
+// each group keeps its gathered write rows M_0[S_ti] in registers, and the group holding a slot's last event of the
+// chunk applies the slot's events to that row and stores it (no second read of the bank). A slot written once needs
+// only the holder's own term; slots written more than once take their events from the plan's multi-event table.
+// H and G are summed per part, then over the parts in order (lane shuffles; bitwise repeatable); the part-0 group
+// of each token then computes its U, delta and output row slices.
 //
-// Memory pipeline per chunk: the write terms (slot, coefficient, last-event code) sit in one of two LDS buffers,
-// filled during the previous chunk; each lane reads 8 of its group's read terms straight into registers and the
-// group shares them with quad DPP broadcasts. Loads are issued oldest first: next chunk's write terms, read terms,
-// T/Q lists and multi-event table, gates, values, then held rows and read rows interleaved (16 held, 16 read,
-// 16 held, 16 read), so that each wait for a batch leaves the younger batches in flight. T/Q lists and multi-event
-// tables larger than their LDS areas are read from the plan region in HBM instead.
+// Memory pipeline per chunk: the write terms (slot, coefficient, int16 last-event code) and the read terms sit in
+// LDS, staged during the previous chunk (write terms double-buffered). The 32 read rows of a lane are issued first;
+// then a sliding window consumes read row u (the oldest load) into G and issues held write row u into the same
+// registers, so 32 row loads stay in flight per lane. T/Q lists and multi-event tables larger than their LDS areas are read from the
+// plan region in HBM instead.
 template <typename Bk> struct Hold { static constexpr int N = 32; };  // float32 banks only (see launch_loop_t)
 constexpr int HELD_LISTS_LDS = 12 * 1024;  // T and Q entries kept in LDS
 constexpr int HELD_MULTI_LDS = 12 * 1024;  // multi-event table kept in LDS
-constexpr int HELD_RPL = 8;                // read terms per lane (32 per group)
 
-// one LDS buffer of write terms: pairs [C * W], then last-event codes [C * W] (the plan region's first two sections)
+// one LDS buffer of write terms: pairs [C * W], then int16 last-event codes [C * W] (the plan region's first two
+// sections, same layout)
 __host__ __device__ inline long long held_wterm_bytes(int C, int W) {
-  return align16((long long)C * W * 8) + align16((long long)C * W * 4);
+  return align16((long long)C * W * 8) + align16((long long)C * W * 2);
 }
 
-__host__ __device__ inline long long held_sums_bytes(int C, int cols) {
-  const int gpt = 128 / C;
-  return align16((long long)2 * C * gpt * cols * 4 + (long long)2 * C * cols * 4 + (long long)C * 8);
+__host__ __device__ inline long long held_small_bytes(int C, int cols) {
+  return align16((long long)2 * C * cols * 4 + (long long)C * 8);
 }
 
-// LDS: partial H and G [C*gpt][cols], U and delta [C][cols], gates [C]; two write-term buffers; T/Q row pointers and
+// LDS: U and delta [C][cols], gates [C]; two write-term buffers; the read terms [C * R]; T/Q row pointers and
 // lists; the multi-event table.
-__host__ __device__ inline size_t loop_held_lds_bytes(int C, int W, int cols) {
-  return (size_t)(held_sums_bytes(C, cols) + 2 * held_wterm_bytes(C, W) + align16((long long)2 * (C + 1) * 4) +
-                  HELD_LISTS_LDS + HELD_MULTI_LDS);
-}
-
-// Value of `v` in lane K of each quad of lanes.
-template <int K>
-__device__ __forceinline__ int quad_bcast(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, K * 0x55, 0xF, 0xF, false);
+__host__ __device__ inline size_t loop_held_lds_bytes(int C, int W, int R, int cols) {
+  return (size_t)(held_small_bytes(C, cols) + 2 * held_wterm_bytes(C, W) + align16((long long)C * R * 8) +
+                  align16((long long)2 * (C + 1) * 4) + HELD_LISTS_LDS + HELD_MULTI_LDS);
 }
 
 // Copies n16 16-byte words from global to LDS, NB loads in flight per thread.
@@ -343,50 +336,17 @@ __device__ __forceinline__ void stage16(const uint4* __restrict__ src, uint4* ds
   }
 }
 
-// Read term u (0..31) of the lane's group: held by lane u / 8 of the quad, as pair u % 8 of its 4 words.
-template <int U>
-__device__ __forceinline__ Pair read_term(const uint4 (&rp)[HELD_RPL / 2]) {
-  constexpr int K = U / HELD_RPL, E = U % HELD_RPL;
-  const uint4 w = rp[E / 2];
-  Pair p;
-  p.slot = quad_bcast<K>((int)((E & 1) ? w.z : w.x));
-  p.coef = __int_as_float(quad_bcast<K>((int)((E & 1) ? w.w : w.y)));
-  return p;
-}
-
-template <int U0, int N>
-struct ReadBatch {
-  template <typename Bk>
-  __device__ __forceinline__ static void load(uint4 (&raw)[N], const uint4 (&rp)[HELD_RPL / 2], const Bk* bank,
-                                              long long ld, int mycol, bool act, int tpr) {
-    ReadBatch<U0, N - 1>::load(*(uint4(*)[N - 1]) & raw, rp, bank, ld, mycol, act, tpr);
-    const Pair p = read_term<U0 + N - 1>(rp);
-    const long long off = (act && U0 + N - 1 < tpr) ? (long long)p.slot * ld + mycol : 0;
-    raw[N - 1] = *(const uint4*)(bank + off);
-  }
-  __device__ __forceinline__ static void coefs(float (&cf)[N], const uint4 (&rp)[HELD_RPL / 2]) {
-    ReadBatch<U0, N - 1>::coefs(*(float(*)[N - 1]) & cf, rp);
-    cf[N - 1] = read_term<U0 + N - 1>(rp).coef;
-  }
-};
-template <int U0>
-struct ReadBatch<U0, 0> {
-  template <typename Bk>
-  __device__ __forceinline__ static void load(uint4 (&)[0], const uint4 (&)[HELD_RPL / 2], const Bk*, long long, int,
-                                              bool, int) {}
-  __device__ __forceinline__ static void coefs(float (&)[0], const uint4 (&)[HELD_RPL / 2]) {}
-};
-
 // Sliding window over the 32 row registers of a lane: step U consumes read row U (the oldest load in flight) into
-// G, then issues held write row U into the same registers, so 32 loads stay in flight with 32 registers of rows.
+// G, then issues held write row U into the same registers. Lanes without a term load row 0 and ignore it: the
+// number of loads in flight is fixed, which keeps the waits exact.
 template <int U, int N>
 struct Window {
   template <typename Bk>
-  __device__ __forceinline__ static void run(uint4 (&row)[N], const uint4 (&rp)[HELD_RPL / 2],
-                                             float (&g)[Lane<Bk>::EPL], const Pair* pw, const Bk* bank, long long ld,
-                                             int mycol, bool act, int tpr, int tpw) {
+  __device__ __forceinline__ static void run(uint4 (&row)[N], const Pair* pr, float (&g)[Lane<Bk>::EPL],
+                                             const Pair* pw, const Bk* bank, long long ld, int mycol, bool act,
+                                             int tpr, int tpw) {
     if (act && U < tpr) {
-      const float cf = read_term<U>(rp).coef;
+      const float cf = pr[U].coef;
       float v[Lane<Bk>::EPL];
       Lane<Bk>::unpack(row[U], v);
 #pragma unroll
@@ -394,35 +354,58 @@ struct Window {
     }
     const long long off = (act && U < tpw) ? (long long)pw[U].slot * ld + mycol : 0;
     row[U] = *(const uint4*)(bank + off);
-    Window<U + 1, N>::run(row, rp, g, pw, bank, ld, mycol, act, tpr, tpw);
+    Window<U + 1, N>::run(row, pr, g, pw, bank, ld, mycol, act, tpr, tpw);
   }
 };
 template <int N>
 struct Window<N, N> {
   template <typename Bk>
-  __device__ __forceinline__ static void run(uint4 (&)[N], const uint4 (&)[HELD_RPL / 2], float (&)[Lane<Bk>::EPL],
-                                             const Pair*, const Bk*, long long, int, bool, int, int) {}
+  __device__ __forceinline__ static void run(uint4 (&)[N], const Pair*, float (&)[Lane<Bk>::EPL], const Pair*,
+                                             const Bk*, long long, int, bool, int, int) {}
+};
+
+// Four activation elements as floats / from floats (value and output row slices of a lane).
+template <typename A> struct Act4;
+template <> struct Act4<float> {
+  __device__ static void load(const float* p, float (&v)[4]) {
+    const float4 x = *(const float4*)p;
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+  }
+  __device__ static void store(float* p, const float (&v)[4]) { *(float4*)p = make_float4(v[0], v[1], v[2], v[3]); }
+};
+template <> struct Act4<bf16_t> {
+  __device__ static void load(const bf16_t* p, float (&v)[4]) {
+    const uint2 x = *(const uint2*)p;
+    v[0] = __uint_as_float(x.x << 16); v[1] = __uint_as_float(x.x & 0xFFFF0000u);
+    v[2] = __uint_as_float(x.y << 16); v[3] = __uint_as_float(x.y & 0xFFFF0000u);
+  }
+  __device__ static void store(bf16_t* p, const float (&v)[4]) {
+    uint2 x;
+    x.x = (uint32_t)from_f<bf16_t>(v[0]) | ((uint32_t)from_f<bf16_t>(v[1]) << 16);
+    x.y = (uint32_t)from_f<bf16_t>(v[2]) | ((uint32_t)from_f<bf16_t>(v[3]) << 16);
+    *(uint2*)p = x;
+  }
 };
 
 template <typename A, typename Bk>
 __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, int nslices) {
   constexpr int EPL = Lane<Bk>::EPL;
+  static_assert(EPL == 4, "held rows are float32 row slices of 4 elements per lane");
   constexpr int COLS = 4 * EPL;
   constexpr int HOLD = Hold<Bk>::N;
   extern __shared__ __align__(16) unsigned char lds[];
   const int C = D.C, W = D.W, R = D.R;
   const int gpt = 128 / C;
   const int tpw = W / gpt, tpr = R / gpt;
-  float* sHp = (float*)lds;                 // [C * gpt][COLS] partial H
-  float* sGp = sHp + C * gpt * COLS;        // [C * gpt][COLS] partial G
-  float* sH = sGp + C * gpt * COLS;         // [C][COLS]  U
+  float* sH = (float*)lds;                  // [C][COLS]  U
   float* sD = sH + C * COLS;                // [C][COLS]  delta
   float* sA = sD + C * COLS;                // [C]
-  float* sB = sA + C;                       // [C]
   const ChunkLayout CL = chunk_layout(C, W, R);
   const long long WT = held_wterm_bytes(C, W);
-  unsigned char* sW0 = lds + held_sums_bytes(C, COLS);
-  unsigned char* sLst = sW0 + 2 * WT;       // T/Q row pointers, then lists (mirror of the plan region's layout)
+  unsigned char* sW0 = lds + held_small_bytes(C, COLS);
+  unsigned char* sR = sW0 + 2 * WT;                         // read terms [C * R]
+  const long long RT = align16((long long)C * R * 8);
+  unsigned char* sLst = sR + RT;                            // T/Q row pointers, then lists (plan region layout)
   const long long ptrs_b = align16((long long)2 * (C + 1) * 4);
   MSeg* msegs_lds = (MSeg*)(sLst + ptrs_b + HELD_LISTS_LDS);
   const int32_t* tptr = (const int32_t*)sLst;
@@ -441,16 +424,23 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
   const int mycol = col0 + q * EPL;
   const bool valid = mycol < D.d;
   Bk* bank = (Bk*)a.bank + (long long)st * D.rows * D.ld;
+  const long long ld = D.ld;
   const A* alpha = (const A*)a.alpha;
   const A* beta = (const A*)a.beta;
   const A* values = (const A*)a.values;
   A* out = (A*)a.out;
-  const int nw16 = (int)(WT >> 4);          // <= 3072: C * W <= 4096
-  constexpr int NWP = 6;                    // 16-byte words of the next write terms per thread
+  const int nw16 = (int)(WT >> 4);          // <= 2560: C * W <= 4096
+  const int nr16 = (int)(RT >> 4);          // <= 2048: C * R <= 4096
+  constexpr int NWP = 5;                    // 16-byte words of the next write terms per thread
+  constexpr int NRP = 4;                    // 16-byte words of the next read terms per thread
   constexpr int NST = 4;                    // 16-byte words of row pointers, lists and multi-event table per thread
 
-  // write terms of the first chunk
-  stage16<NWP>((const uint4*)(a.chunks + (long long)st * D.nch * CL.bytes), (uint4*)sW0, nw16);
+  // write and read terms of the first chunk
+  {
+    const unsigned char* g0 = a.chunks + (long long)st * D.nch * CL.bytes;
+    stage16<NWP>((const uint4*)g0, (uint4*)sW0, nw16);
+    stage16<NRP>((const uint4*)(g0 + CL.rpairs), (uint4*)sR, nr16);
+  }
   __syncthreads();
 
   ChunkCounts cnt = a.counts[(long long)st * D.nch];
@@ -462,156 +452,128 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
     const bool more = ch + 1 < D.nch;
     const ChunkCounts next = a.counts[more ? cidx + 1 : cidx];
     const bool act = valid && gt < Cc;
+    const bool lead = part == 0 && act;     // computes U, delta and the output of token gt's row slice
     unsigned char* sWc = sW0 + (ch & 1) * WT;
     unsigned char* sWn = sW0 + ((ch + 1) & 1) * WT;
-    const Pair* pw = (const Pair*)sWc;
-    const int32_t* wl = (const int32_t*)(sWc + align16((long long)C * W * 8));
+    const Pair* pw = (const Pair*)sWc + gt * W + part * tpw;
+    const int16_t* wl = (const int16_t*)(sWc + align16((long long)C * W * 8)) + gt * W + part * tpw;
 
-    // loads, oldest first ------------------------------------------------------------------------------------
-    // next chunk's write terms (into the other buffer, free since the previous chunk's scatter)
-    uint4 wpf[NWP];
-    {
-      const uint4* src = (const uint4*)(more ? greg + CL.bytes : greg);  // last chunk: loaded, never stored
+    // 1) read rows: terms from LDS, 32 loads in flight
+    const Pair* pr = (const Pair*)sR + gt * R + part * tpr;
+    uint4 row[HOLD];
 #pragma unroll
-      for (int k = 0; k < NWP; ++k) wpf[k] = src[min(tid + k * LOOP_NT, nw16 - 1)];
+    for (int u = 0; u < HOLD; ++u) {
+      const long long off = (act && u < tpr) ? (long long)pr[u].slot * ld + mycol : 0;
+      row[u] = *(const uint4*)(bank + off);
     }
-    // the group's read terms: lane q holds terms [8q, 8q + 8)
-    uint4 rp[HELD_RPL / 2];
-    {
-      const Pair* gp = (const Pair*)(greg + CL.rpairs) + gt * R + part * tpr + q * HELD_RPL;
+    // 2) gates and the value row slice of the token (its part-0 group)
+    const long long grow = ((long long)b * D.T + t0 + min(gt, Cc - 1)) * D.H + h;  // token gt's (b, t, h) row
+    float ga = 0.0f, gb = 0.0f, va[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (lead) {
+      ga = to_f<A>(alpha[grow]);
+      gb = to_f<A>(beta[grow]);
+      Act4<A>::load(values + grow * D.d + mycol, va);
+    }
+    float sa_t = 0.0f;
+    if (tid < Cc) sa_t = to_f<A>(alpha[((long long)b * D.T + t0 + tid) * D.H + h]);
+    // 3) window: read rows into G, held write rows into the same registers
+    float gacc[EPL], hacc[EPL];
 #pragma unroll
-      for (int k = 0; k < HELD_RPL / 2; ++k) rp[k] = *(const uint4*)(gp + 2 * k);  // inside the chunk region
-    }
-    // row pointers, T/Q lists (if they fit) and the multi-event table (if it fits)
+    for (int e = 0; e < EPL; ++e) gacc[e] = hacc[e] = 0.0f;
+    Window<0, HOLD>::run(row, pr, gacc, pw, bank, ld, mycol, act, tpr, tpw);
+    // 4) small loads behind the held rows: this chunk's row pointers, lists and multi-event table
     const long long lbytes = (long long)(cnt.nnzT + cnt.nnzQ) * 8;
     const bool llds = lbytes <= HELD_LISTS_LDS;
     const long long mbytes = (long long)cnt.nmseg * 16 + (long long)cnt.nmev * 8;
     const bool mlds = mbytes <= HELD_MULTI_LDS;
     const int n1 = (int)((ptrs_b + (llds ? lbytes : 0) + 15) >> 4);
     const int n12 = n1 + (mlds ? (int)((mbytes + 15) >> 4) : 0);  // <= NST * LOOP_NT
-    const uint4* src1 = (const uint4*)(greg + CL.ptrs);
-    const uint4* src2 = (const uint4*)(greg + CL.multi) - n1;
-    uint4* dst1 = (uint4*)sLst;
-    uint4* dst2 = (uint4*)msegs_lds - n1;
-    uint4 stg[NST];
-#pragma unroll
-    for (int k = 0; k < NST; ++k) {
+    const w16_t* src1 = (const w16_t*)(greg + CL.ptrs);
+    const w16_t* src2 = (const w16_t*)(greg + CL.multi) - n1;
+    w16_t stg[NST];
+    static_for<NST>([&](auto k) {
       const int i = min(tid + k * LOOP_NT, n12 - 1);  // n12 >= 1: the row pointers are never empty
       stg[k] = i < n1 ? src1[i] : src2[i];
-    }
-    float ga = 0.0f, gb = 0.0f;
-    if (tid < Cc) {
-      const long long g = ((long long)b * D.T + t0 + tid) * D.H + h;
-      ga = to_f<A>(alpha[g]);
-      gb = to_f<A>(beta[g]);
-    }
-    constexpr int VPT = (128 * COLS + LOOP_NT - 1) / LOOP_NT;
-    float vreg[VPT];
+    });
+    // 5) H from the held rows
 #pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-      const int idx = tid + k * LOOP_NT;
-      const int t = idx / COLS, c = idx % COLS;
-      vreg[k] = 0.0f;
-      if (t < Cc && col0 + c < D.d) {
-        const long long g = ((long long)b * D.T + t0 + t) * D.H + h;
-        vreg[k] = to_f<A>(values[g * D.d + col0 + c]);
+    for (int u = 0; u < HOLD; ++u) {
+      if (act && u < tpw) {
+        float v[EPL];
+        Lane<Bk>::unpack(row[u], v);
+        const float cf = pw[u].coef;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) hacc[e] += cf * v[e];
       }
     }
-    // read rows: all 32 in flight (lanes without a term load row 0 and ignore it, so the count is fixed)
-    const long long ld = D.ld;
-    uint4 row[HOLD];
-    ReadBatch<0, HOLD>::load(row, rp, bank, ld, mycol, act, tpr);
-    // next write terms to the other buffer, staged words and gates to LDS (waits for the older loads only)
+    // parts of a token are the gpt consecutive groups (4 gpt consecutive lanes of one wave): sum them in order
+    for (int p = 1; p < gpt; ++p) {
 #pragma unroll
-    for (int k = 0; k < NWP; ++k) {
-      const int i = tid + k * LOOP_NT;
-      if (more && i < nw16) ((uint4*)sWn)[i] = wpf[k];
-    }
-#pragma unroll
-    for (int k = 0; k < NST; ++k) {
-      const int i = tid + k * LOOP_NT;
-      if (i < n12) {
-        if (i < n1) dst1[i] = stg[k]; else dst2[i] = stg[k];
-      }
-    }
-    if (tid < Cc) {
-      sA[tid] = ga;
-      sB[tid] = gb;
-    }
-    // sliding window: consume read row u (oldest), then reuse its registers for held write row u
-    const int wbase = gt * W + part * tpw;
-    float gacc[EPL];
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) gacc[e] = 0.0f;
-    Window<0, HOLD>::run(row, rp, gacc, pw + wbase, bank, ld, mycol, act, tpr, tpw);
-    if (gt < Cc) {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) sGp[G * COLS + q * EPL + e] = gacc[e];
-    }
-    // H from the held rows
-    {
-      float acc[EPL];
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
-#pragma unroll
-      for (int u = 0; u < HOLD; ++u) {
-        if (act && u < tpw) {
-          float v[EPL];
-          Lane<Bk>::unpack(row[u], v);
-          const float cf = pw[wbase + u].coef;
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[e] += cf * v[e];
+      for (int e = 0; e < EPL; ++e) {
+        const float hx = __shfl_down(hacc[e], 4 * p, 64);
+        const float gx = __shfl_down(gacc[e], 4 * p, 64);
+        if (part == 0) {
+          hacc[e] += hx;
+          gacc[e] += gx;
         }
       }
-      if (gt < Cc) {
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) sHp[G * COLS + q * EPL + e] = acc[e];
-      }
     }
-    __syncthreads();  // partial sums, gates, lists and multi-event table in LDS
+    // 6) U = beta v - alpha beta H; staged words to LDS (the next write terms go to the free buffer)
+    if (lead) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) sH[gt * COLS + q * EPL + e] = gb * va[e] - ga * gb * hacc[e];
+    }
+    if (tid < Cc) sA[tid] = sa_t;
+    {
+      w16_t* dst1 = (w16_t*)sLst;
+      w16_t* dst2 = (w16_t*)msegs_lds - n1;
+      static_for<NST>([&](auto k) {
+        const int i = tid + k * LOOP_NT;
+        if (i < n12) {
+          if (i < n1) dst1[i] = stg[k]; else dst2[i] = stg[k];
+        }
+      });
+    }
+    __syncthreads();  // U, gates, lists and the multi-event table in LDS; every wave has taken its read terms
+    // next chunk's write and read terms (their LDS areas are free now)
+    w16_t wpf[NWP], rpf[NRP];
+    {
+      const unsigned char* gn = more ? greg + CL.bytes : greg;  // last chunk: loaded, never stored
+      static_for<NWP>([&](auto k) { wpf[k] = ((const w16_t*)gn)[min(tid + k * LOOP_NT, nw16 - 1)]; });
+      static_for<NRP>([&](auto k) { rpf[k] = ((const w16_t*)(gn + CL.rpairs))[min(tid + k * LOOP_NT, nr16 - 1)]; });
+    }
     const Ent* lists = llds ? (const Ent*)(sLst + ptrs_b) : (const Ent*)(greg + CL.lists);
-    // B: U = beta v - alpha beta H (H = sum of the parts, in order), then delta = T U.
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-      const int idx = tid + k * LOOP_NT;
-      const int t = idx / COLS, c = idx % COLS;
-      if (t < Cc) {
-        float hv = 0.0f;
-        for (int pp = 0; pp < gpt; ++pp) hv += sHp[(t * gpt + pp) * COLS + c];
-        sH[idx] = sB[t] * vreg[k] - sA[t] * sB[t] * hv;
+    // 7) delta = T U
+    if (lead) {
+      float d[EPL] = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int e = tptr[gt]; e < tptr[gt + 1]; ++e) {
+        const Ent x = lists[e];
+        const float4 u = *(const float4*)(sH + x.col * COLS + q * EPL);
+        d[0] += x.val * u.x; d[1] += x.val * u.y; d[2] += x.val * u.z; d[3] += x.val * u.w;
       }
+      *(float4*)(sD + gt * COLS + q * EPL) = make_float4(d[0], d[1], d[2], d[3]);
     }
-    __syncthreads();
-    for (int idx = tid; idx < Cc * COLS; idx += LOOP_NT) {
-      const int t = idx / COLS, c = idx % COLS;
-      float d = 0.0f;
-      for (int e = tptr[t]; e < tptr[t + 1]; ++e) d += lists[e].val * sH[lists[e].col * COLS + c];
-      sD[idx] = d;
-    }
-    __syncthreads();
-    // C: read output.
-    for (int idx = tid; idx < Cc * COLS; idx += LOOP_NT) {
-      const int t = idx / COLS, c = idx % COLS;
-      if (col0 + c < D.d) {
-        float o = 0.0f;
-        for (int pp = 0; pp < gpt; ++pp) o += sGp[(t * gpt + pp) * COLS + c];
-        for (int e = qptr[t]; e < qptr[t + 1]; ++e) o += lists[e].val * sD[lists[e].col * COLS + c];
-        const long long g = ((long long)b * D.T + t0 + t) * D.H + h;
-        out[g * D.d + col0 + c] = from_f<A>(o);
-      }
-    }
-    // D: the holder of each slot's last event applies the slot's events in token order and stores the row.
+    static_for<NWP>([&](auto k) {
+      const int i = tid + k * LOOP_NT;
+      if (more && i < nw16) ((w16_t*)sWn)[i] = wpf[k];
+    });
+    static_for<NRP>([&](auto k) {
+      const int i = tid + k * LOOP_NT;
+      if (more && i < nr16) ((w16_t*)sR)[i] = rpf[k];
+    });
+    __syncthreads();  // delta in LDS
+    // 8) scatter: the holder of each slot's last event applies the slot's events in token order and stores the row
     if (act) {
       const MSeg* msegs = mlds ? msegs_lds : (const MSeg*)(greg + CL.multi);
       const Ev* mev = (const Ev*)(msegs + cnt.nmseg);
 #pragma unroll
       for (int u = 0; u < HOLD; ++u) {
         if (u < tpw) {
-          const int code = wl[wbase + u];
+          const int code = wl[u];
           if (code != -1) {
             float m[EPL];
             Lane<Bk>::unpack(row[u], m);
-            const Pair p = pw[wbase + u];
+            const Pair p = pw[u];
             if (code == -2) {  // the slot's only event: own token, own weight
               const float al = sA[gt];
 #pragma unroll
@@ -625,10 +587,22 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
                 for (int k = 0; k < EPL; ++k) m[k] = al * m[k] + x.w * sD[x.tok * COLS + q * EPL + k];
               }
             }
-            Lane<Bk>::store(bank + (long long)p.slot * D.ld + mycol, m);
+            Lane<Bk>::store(bank + (long long)p.slot * ld + mycol, m);
           }
         }
       }
+    }
+    // 9) read output: out = G + Q delta
+    if (lead) {
+      float o[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[e] = gacc[e];
+      for (int e = qptr[gt]; e < qptr[gt + 1]; ++e) {
+        const Ent x = lists[e];
+        const float4 dd = *(const float4*)(sD + x.col * COLS + q * EPL);
+        o[0] += x.val * dd.x; o[1] += x.val * dd.y; o[2] += x.val * dd.z; o[3] += x.val * dd.w;
+      }
+      Act4<A>::store(out + grow * D.d + mycol, o);
     }
     cnt = next;
     __syncthreads();
@@ -643,11 +617,12 @@ static hipError_t launch_loop_t(const Dims& D, const LoopArgs& a, hipStream_t st
   const size_t staged = loop_lds_bytes(D.C, D.W, D.R, COLS, true);
   const bool pow2 = (D.C & (D.C - 1)) == 0;
   const int gpt = 128 / D.C;
-  const bool held_ok = pow2 && D.C <= 128 && D.W % gpt == 0 && D.R % gpt == 0 && D.W / gpt <= Hold<Bk>::N &&
-                       D.R / gpt <= 4 * HELD_RPL && (D.R / gpt) % 2 == 0 && D.W >= gpt && D.R >= gpt;
+  const bool held_ok = pow2 && D.C >= 8 && D.C <= 128 && D.W % gpt == 0 && D.R % gpt == 0 &&
+                       D.W / gpt <= Hold<Bk>::N && D.R / gpt <= Hold<Bk>::N &&
+                       D.W >= gpt && D.R >= gpt;
   if constexpr (sizeof(Bk) == 4) {
-    if (held_ok && loop_held_lds_bytes(D.C, D.W, COLS) <= 160 * 1024) {
-      const size_t lds = loop_held_lds_bytes(D.C, D.W, COLS);
+    if (held_ok && loop_held_lds_bytes(D.C, D.W, D.R, COLS) <= 160 * 1024) {
+      const size_t lds = loop_held_lds_bytes(D.C, D.W, D.R, COLS);
       (void)hipFuncSetAttribute((const void*)loop_held_kernel<A, Bk>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                 (int)lds);
       hipLaunchKernelGGL((loop_held_kernel<A, Bk>), dim3((unsigned)nblk), dim3(LOOP_NT), lds, st, D, a, nslices);

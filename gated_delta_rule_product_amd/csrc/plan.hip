@@ -88,7 +88,7 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
   unsigned char* reg = a.chunks + cidx * CL.bytes;
   Pair* pw = (Pair*)(reg + CL.wpairs);
   Pair* pr = (Pair*)(reg + CL.rpairs);
-  int32_t* wlast = (int32_t*)(reg + CL.wlast);
+  int16_t* wlast = (int16_t*)(reg + CL.wlast);
   int32_t* tptr = (int32_t*)(reg + CL.ptrs);
   int32_t* qptr = tptr + (C + 1);
   Ent* lists = (Ent*)(reg + CL.lists);
@@ -208,7 +208,7 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
         mev[me++] = x;
         if (last) msegs[m].end = me;
       }
-      wlast[evi] = !last ? -1 : (multi ? m : -2);
+      wlast[evi] = (int16_t)(!last ? -1 : (multi ? m : -2));
     }
   }
   __syncthreads();

@@ -3,6 +3,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
+#include <utility>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -72,8 +74,8 @@ struct Seg {
 
 // Per-chunk plan region (byte offsets; every part 16-byte aligned). Written by the plan kernel, read by the loop.
 //   wpairs [C*W] write gather terms (slot, a)                               (token-major, fixed size)
-//   wlast  [C*W] per write term: -1 if it is not its slot's last event in the chunk; -2 if it is the slot's only
-//          event; else the index of the slot in the multi-event table
+//   wlast  [C*W] int16 per write term: -1 if it is not its slot's last event in the chunk; -2 if it is the slot's
+//          only event; else the index of the slot in the multi-event table (< C W / 2 <= 4096)
 //   rpairs [C*R] read gather terms (slot, b)                                (token-major, fixed size)
 //   ptrs   tptr[C+1], qptr[C+1] row starts of the two lists                  (fixed size)
 //   lists  T entries [nnzT] immediately followed by Q entries [nnzQ]         (packed; capacity C(C+1))
@@ -89,7 +91,7 @@ __host__ __device__ inline ChunkLayout chunk_layout(int C, int W, int R) {
   L.wpairs = 0;
   L.wpairs_bytes = align16((long long)C * W * 8);
   L.wlast = L.wpairs + L.wpairs_bytes;
-  L.wlast_bytes = align16((long long)C * W * 4);
+  L.wlast_bytes = align16((long long)C * W * 2);
   L.rpairs = L.wlast + L.wlast_bytes;
   L.rpairs_bytes = align16((long long)C * R * 8);
   L.ptrs = L.rpairs + L.rpairs_bytes;
@@ -115,6 +117,22 @@ struct ChunkCounts {
 };
 
 // ------------------------------------------------------------------------------------------- device helpers
+// A 16-byte word as a native vector (plain loads and stores; HIP's uint4 struct is copied with memcpy, which can
+// keep arrays of it out of registers).
+typedef unsigned int w16_t __attribute__((ext_vector_type(4)));
+
+// Calls f(std::integral_constant<int, K>{}) for K = 0 .. N-1 in order: indices into register arrays stay compile-time
+// constants from the start (a plain unrolled loop is unrolled only after the arrays' promotion to registers is
+// attempted, and a barrier between their definition and use can then leave them in scratch memory).
+template <typename F, int... K>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, K...>) {
+  (f(std::integral_constant<int, K>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 __device__ __forceinline__ float bf16_to_f(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
 // float -> bfloat16, round to nearest even (finite inputs).
