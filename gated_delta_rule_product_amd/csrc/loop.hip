@@ -339,29 +339,32 @@ __device__ __forceinline__ void stage16(const uint4* __restrict__ src, uint4* ds
 // Sliding window over the 32 row registers of a lane: step U consumes read row U (the oldest load in flight) into
 // G, then issues held write row U into the same registers. Lanes without a term load row 0 and ignore it: the
 // number of loads in flight is fixed, which keeps the waits exact.
-template <int U, int N>
+template <int U, int N, bool FULL>
 struct Window {
   template <typename Bk>
   __device__ __forceinline__ static void run(uint4 (&row)[N], const Pair* pr, float (&g)[Lane<Bk>::EPL],
-                                             const Pair* pw, const Bk* bank, long long ld, int mycol, bool act,
-                                             int tpr, int tpw) {
-    if (act && U < tpr) {
-      const float cf = pr[U].coef;
+                                             const Pair* pw, const Bk* bank, uint32_t ld, int mycol, bool act,
+                                             uint32_t amask, int tpr, int tpw) {
+    // term slots are read unconditionally (inside the LDS areas) and masked to row 0 when not valid: no branch
+    const float cf = pr[U].coef;
+    const uint32_t m = amask & ((FULL || U < tpw) ? ~0u : 0u);
+    const uint64_t off = (uint64_t)((uint32_t)pw[U].slot & m) * ld + ((uint32_t)mycol & m);
+    if (FULL || (act && U < tpr)) {  // FULL: no branch (lanes without a token accumulate row 0, never used)
       float v[Lane<Bk>::EPL];
       Lane<Bk>::unpack(row[U], v);
 #pragma unroll
       for (int e = 0; e < Lane<Bk>::EPL; ++e) g[e] += cf * v[e];
     }
-    const long long off = (act && U < tpw) ? (long long)pw[U].slot * ld + mycol : 0;
     row[U] = *(const uint4*)(bank + off);
-    Window<U + 1, N>::run(row, pr, g, pw, bank, ld, mycol, act, tpr, tpw);
+    __builtin_amdgcn_sched_barrier(0);  // keep the steps in order: one row in, one row out
+    Window<U + 1, N, FULL>::run(row, pr, g, pw, bank, ld, mycol, act, amask, tpr, tpw);
   }
 };
-template <int N>
-struct Window<N, N> {
+template <int N, bool FULL>
+struct Window<N, N, FULL> {
   template <typename Bk>
   __device__ __forceinline__ static void run(uint4 (&)[N], const Pair*, float (&)[Lane<Bk>::EPL], const Pair*,
-                                             const Bk*, long long, int, bool, int, int) {}
+                                             const Bk*, uint32_t, int, bool, uint32_t, int, int) {}
 };
 
 // Four activation elements as floats / from floats (value and output row slices of a lane).
@@ -387,7 +390,8 @@ template <> struct Act4<bf16_t> {
   }
 };
 
-template <typename A, typename Bk>
+// FULL: every part has exactly 32 write and 32 read terms (no per-row term-count test).
+template <typename A, typename Bk, bool FULL>
 __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, int nslices) {
   constexpr int EPL = Lane<Bk>::EPL;
   static_assert(EPL == 4, "held rows are float32 row slices of 4 elements per lane");
@@ -424,7 +428,7 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
   const int mycol = col0 + q * EPL;
   const bool valid = mycol < D.d;
   Bk* bank = (Bk*)a.bank + (long long)st * D.rows * D.ld;
-  const long long ld = D.ld;
+  const uint32_t ld = (uint32_t)D.ld;
   const A* alpha = (const A*)a.alpha;
   const A* beta = (const A*)a.beta;
   const A* values = (const A*)a.values;
@@ -461,10 +465,13 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
     // 1) read rows: terms from LDS, 32 loads in flight
     const Pair* pr = (const Pair*)sR + gt * R + part * tpr;
     uint4 row[HOLD];
+    const uint32_t amask = act ? ~0u : 0u;
 #pragma unroll
     for (int u = 0; u < HOLD; ++u) {
-      const long long off = (act && u < tpr) ? (long long)pr[u].slot * ld + mycol : 0;
+      const uint32_t m = amask & ((FULL || u < tpr) ? ~0u : 0u);
+      const uint64_t off = (uint64_t)((uint32_t)pr[u].slot & m) * ld + ((uint32_t)mycol & m);
       row[u] = *(const uint4*)(bank + off);
+      if ((u & 7) == 7) __builtin_amdgcn_sched_barrier(0);
     }
     // 2) gates and the value row slice of the token (its part-0 group)
     const long long grow = ((long long)b * D.T + t0 + min(gt, Cc - 1)) * D.H + h;  // token gt's (b, t, h) row
@@ -480,7 +487,7 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
     float gacc[EPL], hacc[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) gacc[e] = hacc[e] = 0.0f;
-    Window<0, HOLD>::run(row, pr, gacc, pw, bank, ld, mycol, act, tpr, tpw);
+    Window<0, HOLD, FULL>::run(row, pr, gacc, pw, bank, ld, mycol, act, amask, tpr, tpw);
     // 4) small loads behind the held rows: this chunk's row pointers, lists and multi-event table
     const long long lbytes = (long long)(cnt.nnzT + cnt.nnzQ) * 8;
     const bool llds = lbytes <= HELD_LISTS_LDS;
@@ -498,10 +505,10 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
     // 5) H from the held rows
 #pragma unroll
     for (int u = 0; u < HOLD; ++u) {
-      if (act && u < tpw) {
+      const float cf = pw[u].coef;
+      if (FULL || (act && u < tpw)) {
         float v[EPL];
         Lane<Bk>::unpack(row[u], v);
-        const float cf = pw[u].coef;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) hacc[e] += cf * v[e];
       }
@@ -568,7 +575,7 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
       const Ev* mev = (const Ev*)(msegs + cnt.nmseg);
 #pragma unroll
       for (int u = 0; u < HOLD; ++u) {
-        if (u < tpw) {
+        if (FULL || u < tpw) {
           const int code = wl[u];
           if (code != -1) {
             float m[EPL];
@@ -587,7 +594,7 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
                 for (int k = 0; k < EPL; ++k) m[k] = al * m[k] + x.w * sD[x.tok * COLS + q * EPL + k];
               }
             }
-            Lane<Bk>::store(bank + (long long)p.slot * ld + mycol, m);
+            Lane<Bk>::store(bank + ((uint64_t)(uint32_t)p.slot * ld + (uint32_t)mycol), m);
           }
         }
       }
@@ -623,9 +630,17 @@ static hipError_t launch_loop_t(const Dims& D, const LoopArgs& a, hipStream_t st
   if constexpr (sizeof(Bk) == 4) {
     if (held_ok && loop_held_lds_bytes(D.C, D.W, D.R, COLS) <= 160 * 1024) {
       const size_t lds = loop_held_lds_bytes(D.C, D.W, D.R, COLS);
-      (void)hipFuncSetAttribute((const void*)loop_held_kernel<A, Bk>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)lds);
-      hipLaunchKernelGGL((loop_held_kernel<A, Bk>), dim3((unsigned)nblk), dim3(LOOP_NT), lds, st, D, a, nslices);
+      if (D.W / gpt == Hold<Bk>::N && D.R / gpt == Hold<Bk>::N) {
+        (void)hipFuncSetAttribute((const void*)loop_held_kernel<A, Bk, true>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        hipLaunchKernelGGL((loop_held_kernel<A, Bk, true>), dim3((unsigned)nblk), dim3(LOOP_NT), lds, st, D, a,
+                           nslices);
+      } else {
+        (void)hipFuncSetAttribute((const void*)loop_held_kernel<A, Bk, false>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        hipLaunchKernelGGL((loop_held_kernel<A, Bk, false>), dim3((unsigned)nblk), dim3(LOOP_NT), lds, st, D, a,
+                           nslices);
+      }
       return hipGetLastError();
     }
   }
