@@ -53,7 +53,9 @@ __global__ __launch_bounds__(TOPK_NT) void topk_kernel(Dims D, TopkArgs a) {
 // One wave scores QW query rows (same head and kind) against every sub-key with the fp64 FMA chain, each lane
 // owning NPL sub-keys (its rows read as 16-byte vectors and reused across the QW queries), selects each factor's
 // top min(k, n_f) exactly (wave_select_sorted), then merges the candidate tuples (CPL per lane) the same way.
-template <int NPL> struct WaveTile { static constexpr int QW = (32 / NPL) < 16 ? (32 / NPL < 1 ? 1 : 32 / NPL) : 16; };
+// Queries per wave for NPL sub-keys per lane (QW * NPL <= 16 keeps the fp64 accumulators at 32 registers).
+__host__ __device__ constexpr int wave_qw(int npl) { return 16 / npl < 1 ? 1 : 16 / npl; }
+template <int NPL> struct WaveTile { static constexpr int QW = wave_qw(NPL); };
 
 // Per-wave LDS: factor scores [QW][64 NPL] (float), kept factor lists [QW][F][kpmax] (float score + uint16 id),
 // selection scratch and sorted output [KS] each (uint64).
@@ -83,7 +85,7 @@ template <> struct Vec16<bf16_t> {
 };
 
 template <typename A, int NPL, int CPL>
-__global__ __launch_bounds__(256) void topk2_kernel(Dims D, TopkArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NPL <= 4 ? 4 : 1))) void topk2_kernel(Dims D, TopkArgs a) {
   constexpr int QW = WaveTile<NPL>::QW;
   constexpr int VEC = Vec16<A>::N;
   extern __shared__ __align__(16) unsigned char lds[];
@@ -255,7 +257,7 @@ static bool launch_topk2(const Dims& D, const TopkArgs& a, hipStream_t st) {
   if (ncand > 1024 || kpmax > 1024) return false;
   if ((D.dk * (int)sizeof(A)) % 16 != 0 || ((uintptr_t)a.subkeys) % 16 != 0) return false;
   const int cpl = ncand <= 512 ? 8 : 16;
-  const int QW = 32 / npl < 16 ? (32 / npl < 1 ? 1 : 32 / npl) : 16;
+  const int QW = wave_qw(npl);
   size_t lds = 0;
   for (int q = 0; q < a.nkinds; ++q) {
     const size_t l = 4 * topk2_wave_lds(D.F, a.plan[q].kpmax, a.plan[q].k, QW, npl);
