@@ -58,13 +58,13 @@ __host__ __device__ constexpr int wave_qw(int npl) { return 16 / npl < 1 ? 1 : 1
 template <int NPL> struct WaveTile { static constexpr int QW = wave_qw(NPL); };
 
 // Per-wave LDS: factor scores [QW][64 NPL] (float), kept factor lists [QW][F][kpmax] (float score + uint16 id),
-// selection scratch and sorted output [KS] each (uint64).
+// selection scratch [KS + 8] and sorted output [KS] (uint64).
 __host__ __device__ inline size_t topk2_wave_lds(int F, int kpmax, int k, int QW, int NPL) {
   const int KS = kpmax > k ? kpmax : k;
   size_t n = (size_t)QW * 64 * NPL * 4;
   n += (size_t)QW * F * kpmax * 6;
   n = (n + 7) & ~(size_t)7;
-  return n + (size_t)KS * 16;
+  return n + (size_t)(2 * KS + 8) * 8;
 }
 
 // 16 bytes of a sub-key row and element e of it as fp64 (exact widening).
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NPL <= 4 ? 
   uint16_t* fid = (uint16_t*)(fsc + QW * F * kpmax);        // [QW][F][kpmax]
   uint64_t* scratch =
       (uint64_t*)(wl + (((size_t)QW * 64 * NPL * 4 + (size_t)QW * F * kpmax * 6 + 7) & ~(size_t)7));
-  uint64_t* sorted = scratch + KS;
+  uint64_t* sorted = scratch + KS + 8;
   long long sumn = 0;
   for (int f = 0; f < F; ++f) sumn += D.widths[f];
   const A* sub = (const A*)a.subkeys + (long long)h * sumn * dk;
