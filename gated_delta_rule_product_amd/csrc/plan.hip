@@ -14,54 +14,152 @@
 // and each written row ends as the in-order application of M[j] <- alpha_s M[j] + w_sj delta_s over its events.
 // The kernel sorts the chunk's write events by (slot, token) and writes the chunk region of chunk_layout: the
 // gather terms (slot, a) and (slot, b), T and Q as row-sorted sparse lists, and the slot segments with their
-// events. T is solved in IEEE float32 by forward substitution, row after row. Every sum runs in a fixed order
-// (bitwise repeatable; no atomics).
+// events. T is solved in IEEE float32 by forward substitution, row after row, over the nonzero entries of each row
+// of diag(alpha beta) K only. Every floating-point sum runs in a fixed order (bitwise repeatable); the only atomics
+// are integer bit sets in LDS.
+//
+// Parallel structure (one 512-thread workgroup per chunk): gather terms are computed one thread per term; the few
+// terms that meet an earlier event of the same slot are flagged in per-token bit masks, and one thread per token
+// then adds their K and Q contributions in term order. Row nonzero masks, counts and offsets of the sparse T/Q lists
+// come from wave ballots and prefix sums.
 #include "sdm_internal.h"
 
 namespace sdm {
 
-__host__ __device__ inline size_t plan_lds_bytes(int C, int W) {
+// LDS layout of the plan kernel (16-byte aligned parts).
+struct PlanLds {
+  size_t keys, sslot, sev, pos, sA, sB, kmask, qmask, rmask, roff, tot, bytes;
+  int kwm, qwm;  // 64-bit words per token of the K / Q term masks
+};
+
+__host__ __device__ inline PlanLds plan_lds(int C, int W, int R) {
   const size_t CW = (size_t)C * W;
-  size_t keys = (size_t)pow2_ceil((int)CW) * 8;
-  const size_t dense = (size_t)C * C * 4;
-  if (dense > keys) keys = dense;
-  return keys + CW * 4 /*sslot*/ + CW * 2 /*sev*/ + CW * 2 /*pos*/ + (size_t)C * 12 /*alpha, beta, flags*/ +
-         (size_t)PLAN_NT * 4 * 3 /*scans*/ + 16;
+  PlanLds L;
+  size_t keys = (size_t)pow2_ceil((int)CW) * 8;             // sort keys; later write weights, then dense rows
+  if ((size_t)C * C * 4 > keys) keys = (size_t)C * C * 4;
+  L.kwm = (W + 63) / 64;
+  L.qwm = (R + 63) / 64;
+  size_t o = 0;
+  L.keys = o;  o += align16((long long)keys);
+  L.sslot = o; o += align16((long long)CW * 4);
+  L.sev = o;   o += align16((long long)CW * 2);
+  L.pos = o;   o += align16((long long)CW * 2);
+  L.sA = o;    o += align16((long long)C * 4);
+  L.sB = o;    o += align16((long long)C * 4);
+  L.kmask = o; o += align16((long long)C * L.kwm * 8);
+  L.qmask = o; o += align16((long long)C * L.qwm * 8);
+  L.rmask = o; o += align16((long long)C * 2 * 8);
+  L.roff = o;  o += align16((long long)(C + 1) * 4);
+  L.tot = o;   o += align16(3 * 8 * 4 + 16);
+  L.bytes = o;
+  return L;
 }
 
-// Row-sorted sparse compaction of the dense rows 0..Cc-1 (columns 0..t for row t) into ptr / out; returns nnz.
-// ptr[t] are absolute offsets (base + running count). All threads call; ends with a barrier.
-__device__ inline int compact_rows(const float* dense, int C, int Cc, int* scan, int32_t* ptr, Ent* out, int base) {
-  const int tid = threadIdx.x;
-  for (int t = tid; t < Cc; t += PLAN_NT) {
-    int n = 0;
-    for (int s = 0; s <= t; ++s) n += dense[t * C + s] != 0.0f;
-    scan[t] = n;
+__host__ __device__ inline size_t plan_lds_bytes(int C, int W, int R) { return plan_lds(C, W, R).bytes; }
+
+// Orders this wave's LDS accesses before and after it (program order within one wave).
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ uint64_t lanes_below() {
+  const int l = threadIdx.x & 63;
+  return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int x = __shfl_up(v, o, 64);
+    if (lane >= o) v += x;
+  }
+  return v;
+}
+
+// Exclusive prefix sums of three per-thread counts over the workgroup (thread order); totals in t0..t2.
+__device__ inline void block_excl_scan3(int& a, int& b, int& c, int* tot, int& t0, int& t1, int& t2) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int ia = wave_incl_scan(a), ib = wave_incl_scan(b), ic = wave_incl_scan(c);
+  if (lane == 63) {
+    tot[wv] = ia;
+    tot[8 + wv] = ib;
+    tot[16 + wv] = ic;
   }
   __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int t = 0; t < Cc; ++t) {
-      const int c = scan[t];
-      scan[t] = run;
-      ptr[t] = base + run;
-      run += c;
+  int ba = 0, bb = 0, bc = 0;
+  t0 = t1 = t2 = 0;
+  for (int w = 0; w < PLAN_NT / 64; ++w) {
+    if (w < wv) {
+      ba += tot[w];
+      bb += tot[8 + w];
+      bc += tot[16 + w];
     }
-    ptr[Cc] = base + run;
-    scan[PLAN_NT - 1] = run;
+    t0 += tot[w];
+    t1 += tot[8 + w];
+    t2 += tot[16 + w];
+  }
+  a = ba + ia - a;
+  b = bb + ib - b;
+  c = bc + ic - c;
+  __syncthreads();
+}
+
+// Lower bound of slot j in the sorted slots s[0..E).
+__device__ __forceinline__ int lower_bound_slot(const int32_t* s, int E, int j) {
+  int l = 0, r = E;
+  while (l < r) {
+    const int m = (l + r) >> 1;
+    if (s[m] < j) l = m + 1; else r = m;
+  }
+  return l;
+}
+
+// Row-sorted sparse compaction of the dense rows 0..Cc-1 (columns 0..t of row t, C <= 128) into ptr / out; returns
+// nnz. ptr[t] are absolute offsets (base + running count). Rows are counted with wave ballots (one wave per row),
+// offset by a wave prefix sum, and emitted in column order. All threads call; ends with a barrier.
+__device__ inline int compact_rows(const float* dense, int C, int Cc, uint64_t* rmask, int* roff, int* tot,
+                                   int32_t* ptr, Ent* out, int base) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  for (int t = wv; t < Cc; t += PLAN_NT / 64) {
+    const bool nz0 = lane < C && lane <= t && dense[t * C + lane] != 0.0f;
+    const bool nz1 = lane + 64 < C && lane + 64 <= t && dense[t * C + lane + 64] != 0.0f;
+    const uint64_t m0 = __ballot(nz0), m1 = __ballot(nz1);
+    if (lane == 0) {
+      rmask[2 * t] = m0;
+      rmask[2 * t + 1] = m1;
+    }
   }
   __syncthreads();
-  const int total = scan[PLAN_NT - 1];
-  for (int t = tid; t < Cc; t += PLAN_NT) {
-    int o = base + scan[t];
-    for (int s = 0; s <= t; ++s) {
-      const float v = dense[t * C + s];
-      if (v != 0.0f) {
-        Ent x;
-        x.col = s;
-        x.val = v;
-        out[o++] = x;
-      }
+  if (wv == 0) {  // row offsets: rows 2 lane and 2 lane + 1
+    const int r0 = 2 * lane, r1 = 2 * lane + 1;
+    const int c0 = r0 < Cc ? __popcll(rmask[2 * r0]) + __popcll(rmask[2 * r0 + 1]) : 0;
+    const int c1 = r1 < Cc ? __popcll(rmask[2 * r1]) + __popcll(rmask[2 * r1 + 1]) : 0;
+    const int incl = wave_incl_scan(c0 + c1);
+    const int ex = incl - c0 - c1;
+    if (r0 < Cc) { roff[r0] = ex; ptr[r0] = base + ex; }
+    if (r1 < Cc) { roff[r1] = ex + c0; ptr[r1] = base + ex + c0; }
+    if (lane == 63) { ptr[Cc] = base + incl; tot[0] = incl; }
+  }
+  __syncthreads();
+  const int total = tot[0];
+  const uint64_t below = lanes_below();
+  for (int t = wv; t < Cc; t += PLAN_NT / 64) {
+    const uint64_t m0 = rmask[2 * t], m1 = rmask[2 * t + 1];
+    const int o = base + roff[t];
+    if ((m0 >> lane) & 1) {
+      Ent x;
+      x.col = lane;
+      x.val = dense[t * C + lane];
+      out[o + __popcll(m0 & below)] = x;
+    }
+    if ((m1 >> lane) & 1) {
+      Ent x;
+      x.col = lane + 64;
+      x.val = dense[t * C + lane + 64];
+      out[o + __popcll(m0) + __popcll(m1 & below)] = x;
     }
   }
   __syncthreads();
@@ -71,7 +169,7 @@ __device__ inline int compact_rows(const float* dense, int C, int Cc, int* scan,
 template <typename A>
 __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int st = blockIdx.y;
   const int ch = blockIdx.x;
   const int b = st / D.H, h = st % D.H;
@@ -80,7 +178,6 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
   const int Cc = min(C, D.T - t0);
   const int E = Cc * W;
   const int Ep2 = pow2_ceil(E);
-  const long long CW = (long long)C * W;
   const long long cidx = (long long)st * D.nch + ch;
   const long long wbase = ((long long)st * D.T + t0) * W;  // [S][T][W] offset of the chunk's first event
   const long long rbase = ((long long)st * D.T + t0) * R;
@@ -93,24 +190,24 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
   int32_t* qptr = tptr + (C + 1);
   Ent* lists = (Ent*)(reg + CL.lists);
   Seg* segs = (Seg*)(reg + CL.scat);
-
-  size_t keys_bytes = (size_t)pow2_ceil((int)CW) * 8;
-  if ((size_t)C * C * 4 > keys_bytes) keys_bytes = (size_t)C * C * 4;
-  uint64_t* keys = (uint64_t*)lds;
-  float* dense = (float*)lds;
-  int32_t* sslot = (int32_t*)(lds + keys_bytes);
-  uint16_t* sev = (uint16_t*)(sslot + CW);
-  uint16_t* pos = sev + CW;
-  float* sA = (float*)(pos + CW + (CW & 1));
-  float* sB = sA + C;
-  int32_t* sHasL = (int32_t*)(sB + C);
-  int32_t* scan = sHasL + C;
-  int32_t* scanM = scan + PLAN_NT;   // multi-event segment starts per thread range
-  int32_t* scanE = scanM + PLAN_NT;  // multi-event events per thread range
-  __shared__ int s_nseg, s_nmseg;
   MSeg* msegs = (MSeg*)(reg + CL.multi);
 
-  // 1. write events -> sort keys (slot, event index); gates of the chunk.
+  const PlanLds PL = plan_lds(C, W, R);
+  uint64_t* keys = (uint64_t*)(lds + PL.keys);
+  float* sw = (float*)(lds + PL.keys);     // after the sort: write weights in sorted event order
+  float* dense = (float*)(lds + PL.keys);  // after the segments: K, T, Q rows
+  int32_t* sslot = (int32_t*)(lds + PL.sslot);
+  uint16_t* sev = (uint16_t*)(lds + PL.sev);
+  uint16_t* pos = (uint16_t*)(lds + PL.pos);
+  float* sA = (float*)(lds + PL.sA);
+  float* sB = (float*)(lds + PL.sB);
+  unsigned long long* kmask = (unsigned long long*)(lds + PL.kmask);
+  unsigned long long* qmask = (unsigned long long*)(lds + PL.qmask);
+  uint64_t* rmask = (uint64_t*)(lds + PL.rmask);
+  int* roff = (int*)(lds + PL.roff);
+  int* tot = (int*)(lds + PL.tot);
+
+  // 1. write events -> sort keys (slot, event index); gates of the chunk; empty term masks.
   for (int e = tid; e < Ep2; e += PLAN_NT) {
     uint64_t key = ~0ull;
     if (e < E) key = ((uint64_t)(uint32_t)a.widx[wbase + e] << 32) | (uint32_t)e;
@@ -125,8 +222,9 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
     }
     sA[t] = al;
     sB[t] = be;
-    sHasL[t] = 0;
   }
+  for (int i = tid; i < C * PL.kwm; i += PLAN_NT) kmask[i] = 0ull;
+  for (int i = tid; i < C * PL.qwm; i += PLAN_NT) qmask[i] = 0ull;
   __syncthreads();
   bitonic_sort_u64<PLAN_NT>(keys, Ep2);
   for (int e = tid; e < E; e += PLAN_NT) {
@@ -136,54 +234,39 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
     pos[k & 0xFFFF] = (uint16_t)e;
   }
   __syncthreads();
+  for (int e = tid; e < E; e += PLAN_NT) sw[e] = a.wwt[wbase + sev[e]];
 
-  // 2. segments (runs of equal slots) and the multi-event table: ids by block scans over contiguous ranges.
+  // 2. segments (runs of equal slots) and the multi-event table: ids by a workgroup prefix sum over contiguous
+  //    ranges of the sorted events.
   const int per = (E + PLAN_NT - 1) / PLAN_NT;
   const int lo = min(E, tid * per), hi = min(E, lo + per);
+  int g0 = 0, m0 = 0, me0 = 0, nseg = 0, nmseg = 0, nmev = 0;
   {
-    int cnt = 0, cm = 0, ce = 0;
     for (int e = lo; e < hi; ++e) {
       const bool first = e == 0 || sslot[e] != sslot[e - 1];
       const bool multi = !first || (e + 1 < E && sslot[e + 1] == sslot[e]);
-      cnt += first;
-      cm += first && multi;
-      ce += multi;
+      g0 += first;
+      m0 += first && multi;
+      me0 += multi;
     }
-    scan[tid] = cnt;
-    scanM[tid] = cm;
-    scanE[tid] = ce;
+    block_excl_scan3(g0, m0, me0, tot, nseg, nmseg, nmev);  // includes barriers (sw visible after it)
   }
-  __syncthreads();
   if (tid == 0) {
-    int run = 0, rm = 0, re = 0;
-    for (int i = 0; i < PLAN_NT; ++i) {
-      const int c = scan[i], m = scanM[i], x = scanE[i];
-      scan[i] = run;
-      scanM[i] = rm;
-      scanE[i] = re;
-      run += c;
-      rm += m;
-      re += x;
-    }
     ChunkCounts cc;
     cc.nnzT = cc.nnzQ = 0;
-    cc.nseg = run;
+    cc.nseg = nseg;
     cc.nev = E;
-    cc.nmseg = rm;
-    cc.nmev = re;
+    cc.nmseg = nmseg;
+    cc.nmev = nmev;
     cc.pad0 = cc.pad1 = 0;
     a.counts[cidx] = cc;
-    s_nseg = run;
-    s_nmseg = rm;
   }
-  __syncthreads();
-  const int nseg = s_nseg;
   Ev* ev = (Ev*)(segs + nseg);
-  Ev* mev = (Ev*)(msegs + s_nmseg);
+  Ev* mev = (Ev*)(msegs + nmseg);
   {
-    int g = scan[tid] - 1;   // segment id of the element before lo
-    int m = scanM[tid] - 1;  // multi-event segment id of the element before lo
-    int me = scanE[tid];     // next multi-event event slot
+    int g = g0 - 1;   // segment id of the element before lo
+    int m = m0 - 1;   // multi-event segment id of the element before lo
+    int me = me0;     // next multi-event event slot
     for (int e = lo; e < hi; ++e) {
       const bool first = e == 0 || sslot[e] != sslot[e - 1];
       const bool last = e == E - 1 || sslot[e + 1] != sslot[e];
@@ -201,7 +284,7 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
       if (last) segs[g].end = e + 1;
       const int evi = sev[e];
       Ev x;
-      x.w = a.wwt[wbase + evi];
+      x.w = sw[e];
       x.tok = evi / W;
       ev[e] = x;
       if (multi) {
@@ -213,85 +296,143 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
   }
   __syncthreads();
 
-  // 3. K (dense rows in LDS) and the write-gather terms (slot, a_ti); one thread per token, events in order.
+  // 3. write-gather terms (slot, a_ti), one thread per term; terms meeting an earlier event of their slot are
+  //    flagged. Then K (dense rows): one thread per token adds its flagged terms' contributions in term order.
   for (int i = tid; i < C * C; i += PLAN_NT) dense[i] = 0.0f;
+  for (int evi = tid; evi < E; evi += PLAN_NT) {
+    const int e = pos[evi];
+    const int slot = sslot[e];
+    const float wt = a.wwt[wbase + evi];
+    float prod = 1.0f;
+    bool has = false;
+    for (int e2 = e - 1; e2 >= 0 && sslot[e2] == slot; --e2) {
+      prod *= sA[sev[e2] / W];
+      has = true;
+    }
+    Pair p;
+    p.slot = slot;
+    p.coef = wt * prod;
+    pw[evi] = p;
+    if (has) {
+      const int t = evi / W, i = evi % W;
+      atomicOr(&kmask[t * PL.kwm + (i >> 6)], 1ull << (i & 63));
+    }
+  }
   __syncthreads();
   for (int t = tid; t < Cc; t += PLAN_NT) {
-    int has = 0;
-    for (int i = 0; i < W; ++i) {
-      const int evi = t * W + i;
-      const int e = pos[evi];
-      const int slot = sslot[e];
-      const float wt = a.wwt[wbase + evi];
-      float prod = 1.0f;
-      for (int e2 = e - 1; e2 >= 0 && sslot[e2] == slot; --e2) {
-        const int s = sev[e2] / W;
-        dense[t * C + s] += wt * a.wwt[wbase + sev[e2]] * prod;
-        prod *= sA[s];
-        has = 1;
+    for (int wd = 0; wd < PL.kwm; ++wd) {
+      uint64_t mk = kmask[t * PL.kwm + wd];
+      while (mk) {
+        const int i = wd * 64 + __ffsll((unsigned long long)mk) - 1;
+        mk &= mk - 1;
+        const int evi = t * W + i;
+        const int e = pos[evi];
+        const int slot = sslot[e];
+        const float wt = a.wwt[wbase + evi];
+        float prod = 1.0f;
+        for (int e2 = e - 1; e2 >= 0 && sslot[e2] == slot; --e2) {
+          const int s = sev[e2] / W;
+          dense[t * C + s] += wt * a.wwt[wbase + sev[e2]] * prod;
+          prod *= sA[s];
+        }
       }
-      Pair p;
-      p.slot = slot;
-      p.coef = wt * prod;
-      pw[evi] = p;
     }
-    sHasL[t] = has;
   }
   __syncthreads();
 
-  // 4. T = (I + L)^-1 with L = diag(alpha beta) K, in place, row after row (IEEE float32).
-  for (int i = tid; i < Cc * C; i += PLAN_NT) {
-    const int t = i / C, s = i % C;
-    if (s < t) dense[i] *= sA[t] * sB[t];
-    else if (s == t) dense[i] = 1.0f;
-  }
-  __syncthreads();
-  for (int t = 1; t < Cc; ++t) {
-    if (!sHasL[t]) continue;  // row t of T is e_t
-    const int s = tid;
-    float acc = 0.0f;
-    if (s < t) {
-      for (int m = s; m < t; ++m) {
-        const float l = dense[t * C + m];
-        if (l != 0.0f) acc += l * dense[m * C + s];
-      }
+  // 4. L = diag(alpha beta) K (unit diagonal) with the nonzero mask of each row (one wave per row), then
+  //    T = (I + L)^-1 in place, row after row, by wave 0 alone (lane s holds columns s and s + 64), summing over
+  //    the row's nonzero entries in increasing order. Meanwhile waves 1.. compute the read-gather terms
+  //    (slot, b_ti), one thread per term, flagging the terms that meet an earlier write of their slot.
+  for (int t = wv; t < Cc; t += PLAN_NT / 64) {
+    const float ab = sA[t] * sB[t];
+    bool nz0 = false, nz1 = false;
+    if (lane < C) {
+      float& x = dense[t * C + lane];
+      if (lane < t) { x *= ab; nz0 = x != 0.0f; }
+      else if (lane == t) x = 1.0f;
     }
-    __syncthreads();
-    if (s < t) dense[t * C + s] = -acc;
-    __syncthreads();
+    if (lane + 64 < C) {
+      float& x = dense[t * C + lane + 64];
+      if (lane + 64 < t) { x *= ab; nz1 = x != 0.0f; }
+      else if (lane + 64 == t) x = 1.0f;
+    }
+    const uint64_t m0 = __ballot(nz0), m1 = __ballot(nz1);
+    if (lane == 0) {
+      rmask[2 * t] = m0;
+      rmask[2 * t + 1] = m1;
+    }
   }
-  const int nnzT = compact_rows(dense, C, Cc, scan, tptr, lists, 0);
-
-  // 5. Q (dense rows) and the read-gather terms (slot, b_ti).
-  for (int i = tid; i < C * C; i += PLAN_NT) dense[i] = 0.0f;
   __syncthreads();
-  for (int t = tid; t < Cc; t += PLAN_NT) {
-    for (int i = 0; i < R; ++i) {
-      const int j = a.ridx[rbase + (long long)t * R + i];
-      const float rho = a.rwt[rbase + (long long)t * R + i];
-      int l = 0, r = E;  // lower bound of j in sslot
-      while (l < r) {
-        const int m = (l + r) >> 1;
-        if (sslot[m] < j) l = m + 1; else r = m;
+  if (wv == 0) {
+    for (int t = 1; t < Cc; ++t) {
+      const uint64_t mk0 = rmask[2 * t], mk1 = rmask[2 * t + 1];
+      if ((mk0 | mk1) == 0) continue;  // row t of T is e_t
+      float acc0 = 0.0f, acc1 = 0.0f;
+      for (int half = 0; half < 2; ++half) {
+        uint64_t mk = half ? mk1 : mk0;
+        while (mk) {
+          const int m = half * 64 + __ffsll((unsigned long long)mk) - 1;
+          mk &= mk - 1;
+          const float l = dense[t * C + m];
+          if (lane <= m) acc0 += l * dense[m * C + lane];
+          if (lane + 64 <= m) acc1 += l * dense[m * C + lane + 64];
+        }
       }
+      if (lane < t) dense[t * C + lane] = -acc0;
+      if (lane + 64 < t) dense[t * C + lane + 64] = -acc1;
+      wave_sync_lds();
+    }
+  } else {
+    const int nth = PLAN_NT - 64;
+    for (int x = tid - 64; x < Cc * R; x += nth) {
+      const int t = x / R;
+      const int j = a.ridx[rbase + x];
+      const float rho = a.rwt[rbase + x];
+      const int l = lower_bound_slot(sslot, E, j);
       float prod = 1.0f;
       if (l < E && sslot[l] == j && sev[l] / W <= t) {
         int e1 = l;
         while (e1 + 1 < E && sslot[e1 + 1] == j && sev[e1 + 1] / W <= t) ++e1;
+        for (int e2 = e1; e2 >= l; --e2) prod *= sA[sev[e2] / W];
+        const int i = x % R;
+        atomicOr(&qmask[t * PL.qwm + (i >> 6)], 1ull << (i & 63));
+      }
+      Pair p;
+      p.slot = j;
+      p.coef = rho * prod;
+      pr[x] = p;
+    }
+  }
+  __syncthreads();
+  const int nnzT = compact_rows(dense, C, Cc, rmask, roff, tot, tptr, lists, 0);
+
+  // 5. Q (dense rows): one thread per token adds its flagged read terms' contributions in term order.
+  for (int i = tid; i < C * C; i += PLAN_NT) dense[i] = 0.0f;
+  __syncthreads();
+  for (int t = tid; t < Cc; t += PLAN_NT) {
+    for (int wd = 0; wd < PL.qwm; ++wd) {
+      uint64_t mk = qmask[t * PL.qwm + wd];
+      while (mk) {
+        const int i = wd * 64 + __ffsll((unsigned long long)mk) - 1;
+        mk &= mk - 1;
+        const long long x = (long long)t * R + i;
+        const int j = a.ridx[rbase + x];
+        const float rho = a.rwt[rbase + x];
+        const int l = lower_bound_slot(sslot, E, j);
+        int e1 = l;
+        while (e1 + 1 < E && sslot[e1 + 1] == j && sev[e1 + 1] / W <= t) ++e1;
+        float prod = 1.0f;
         for (int e2 = e1; e2 >= l; --e2) {
           const int s = sev[e2] / W;
           dense[t * C + s] += rho * a.wwt[wbase + sev[e2]] * prod;
           prod *= sA[s];
         }
       }
-      Pair p;
-      p.slot = j;
-      p.coef = rho * prod;
-      pr[(long long)t * R + i] = p;
     }
   }
   __syncthreads();
-  const int nnzQ = compact_rows(dense, C, Cc, scan, qptr, lists, nnzT);
+  const int nnzQ = compact_rows(dense, C, Cc, rmask, roff, tot, qptr, lists, nnzT);
   if (tid == 0) {
     a.counts[cidx].nnzT = nnzT;
     a.counts[cidx].nnzQ = nnzQ;
@@ -300,7 +441,7 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
 
 hipError_t launch_plan(const Dims& D, const PlanArgs& a, hipStream_t st) {
   if (D.S == 0 || D.T == 0) return hipSuccess;
-  const size_t lds = plan_lds_bytes(D.C, D.W);
+  const size_t lds = plan_lds_bytes(D.C, D.W, D.R);
   dim3 grid((unsigned)D.nch, (unsigned)D.S);
   if (D.act == SDM_BF16) {
     (void)hipFuncSetAttribute((const void*)plan_kernel<bf16_t>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
