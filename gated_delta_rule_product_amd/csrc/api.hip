@@ -423,6 +423,7 @@ sdm_status sdm_write_read(const sdm_config* cfg, const void* write_keys, const v
   pa.beta = input_gate;
   pa.chunks = ws + L.chunks;
   pa.counts = (ChunkCounts*)(ws + L.counts);
+  pa.scat = loop_held_path(D) ? 0 : 1;
   TRY(hip_status(timed(SDM_K_PLAN, st, [&] { return launch_plan(D, pa, st); }), "chunk plan launch"));
   LoopArgs la;
   la.alpha = forget_gate;

@@ -616,19 +616,26 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
   }
 }
 
+// The held-row variant serves float32 banks whose chunk fits its lane-group split and LDS budget.
+bool loop_held_path(const Dims& D) {
+  if (D.bank != SDM_F32) return false;
+  constexpr int COLS = 4 * Lane<float>::EPL;
+  const bool pow2 = (D.C & (D.C - 1)) == 0;
+  if (!pow2 || D.C < 8 || D.C > 128) return false;
+  const int gpt = 128 / D.C;
+  return D.W % gpt == 0 && D.R % gpt == 0 && D.W / gpt <= Hold<float>::N && D.R / gpt <= Hold<float>::N &&
+         D.W >= gpt && D.R >= gpt && loop_held_lds_bytes(D.C, D.W, D.R, COLS) <= 160 * 1024;
+}
+
 template <typename A, typename Bk>
 static hipError_t launch_loop_t(const Dims& D, const LoopArgs& a, hipStream_t st) {
   constexpr int COLS = 4 * Lane<Bk>::EPL;
   const int nslices = (D.d + COLS - 1) / COLS;
   const long long nblk = (long long)D.S * nslices;
   const size_t staged = loop_lds_bytes(D.C, D.W, D.R, COLS, true);
-  const bool pow2 = (D.C & (D.C - 1)) == 0;
   const int gpt = 128 / D.C;
-  const bool held_ok = pow2 && D.C >= 8 && D.C <= 128 && D.W % gpt == 0 && D.R % gpt == 0 &&
-                       D.W / gpt <= Hold<Bk>::N && D.R / gpt <= Hold<Bk>::N &&
-                       D.W >= gpt && D.R >= gpt;
   if constexpr (sizeof(Bk) == 4) {
-    if (held_ok && loop_held_lds_bytes(D.C, D.W, D.R, COLS) <= 160 * 1024) {
+    if (loop_held_path(D)) {
       const size_t lds = loop_held_lds_bytes(D.C, D.W, D.R, COLS);
       if (D.W / gpt == Hold<Bk>::N && D.R / gpt == Hold<Bk>::N) {
         (void)hipFuncSetAttribute((const void*)loop_held_kernel<A, Bk, true>,

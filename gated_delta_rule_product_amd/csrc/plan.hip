@@ -26,16 +26,19 @@
 
 namespace sdm {
 
+// Number of keys the event sort works on: the chunk's events padded to 4096 or 8192 (C W <= 8192).
+__host__ __device__ inline int plan_sort_n(int CW) { return CW <= 4096 ? 4096 : 8192; }
+
 // LDS layout of the plan kernel (16-byte aligned parts).
 struct PlanLds {
-  size_t keys, sslot, sev, pos, sA, sB, kmask, qmask, rmask, roff, tot, bytes;
+  size_t keys, sslot, sev, pos, scode, sA, sB, kmask, qmask, rmask, roff, lev, loff, tot, bytes;
   int kwm, qwm;  // 64-bit words per token of the K / Q term masks
 };
 
 __host__ __device__ inline PlanLds plan_lds(int C, int W, int R) {
   const size_t CW = (size_t)C * W;
   PlanLds L;
-  size_t keys = (size_t)pow2_ceil((int)CW) * 8;             // sort keys; later write weights, then dense rows
+  size_t keys = (size_t)plan_sort_n((int)CW) * 8;           // sort keys; later write weights, then dense rows
   if ((size_t)C * C * 4 > keys) keys = (size_t)C * C * 4;
   L.kwm = (W + 63) / 64;
   L.qwm = (R + 63) / 64;
@@ -44,12 +47,15 @@ __host__ __device__ inline PlanLds plan_lds(int C, int W, int R) {
   L.sslot = o; o += align16((long long)CW * 4);
   L.sev = o;   o += align16((long long)CW * 2);
   L.pos = o;   o += align16((long long)CW * 2);
+  L.scode = o; o += align16((long long)CW * 2);
   L.sA = o;    o += align16((long long)C * 4);
   L.sB = o;    o += align16((long long)C * 4);
   L.kmask = o; o += align16((long long)C * L.kwm * 8);
   L.qmask = o; o += align16((long long)C * L.qwm * 8);
   L.rmask = o; o += align16((long long)C * 2 * 8);
   L.roff = o;  o += align16((long long)(C + 1) * 4);
+  L.lev = o;   o += align16((long long)C * 4);
+  L.loff = o;  o += align16((long long)(C + 2) * 4);
   L.tot = o;   o += align16(3 * 8 * 4 + 16);
   L.bytes = o;
   return L;
@@ -104,6 +110,99 @@ __device__ inline void block_excl_scan3(int& a, int& b, int& c, int* tot, int& t
   a = ba + ia - a;
   b = bb + ib - b;
   c = bc + ic - c;
+  __syncthreads();
+}
+
+// ------------------------------------------------------------------------------------------- event sort
+// Bitonic sort of NS = 512 * EPT 64-bit keys (ascending) held in LDS. Wave w owns the contiguous block of
+// BW = 64 * EPT keys [w BW, (w + 1) BW); lane l holds its keys j * 64 + l (j < EPT) in registers. Merge steps whose
+// partner lies in the same lane run on registers, steps with partner distance < 64 on lane shuffles, and only the
+// steps across wave blocks (distance >= BW) go through LDS with workgroup barriers (6 of the 78 steps for 4096 keys).
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
+  const int lo = __shfl_xor((int)(uint32_t)x, m, 64);
+  const int hi = __shfl_xor((int)(uint32_t)(x >> 32), m, 64);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+// One merge step (block size SIZE, partner distance STRIDE < BW) on the lane's registers.
+template <int EPT, int SIZE, int STRIDE>
+__device__ __forceinline__ void sort_step_reg(uint64_t (&v)[EPT], int gbase, int lane) {
+  if constexpr (STRIDE >= 64) {
+    constexpr int S = STRIDE / 64;
+    static_for<EPT>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      if constexpr ((j & S) == 0) {
+        const bool up = ((gbase + j * 64) & SIZE) == 0;
+        const uint64_t x = v[j], y = v[j | S];
+        const bool sw = (x > y) == up;
+        v[j] = sw ? y : x;
+        v[j | S] = sw ? x : y;
+      }
+    });
+  } else {
+    const bool lower = (lane & STRIDE) == 0;
+    static_for<EPT>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      const uint64_t x = v[j];
+      const uint64_t y = shfl_xor_u64(x, STRIDE);
+      const bool up = ((gbase + j * 64 + lane) & SIZE) == 0;
+      const bool keep_min = lower == up;
+      const bool xl = x < y;
+      v[j] = (keep_min == xl) ? x : y;
+    });
+  }
+}
+
+// All steps of block size SIZE with partner distance < BW, largest distance first.
+template <int EPT, int SIZE, int LST>
+__device__ __forceinline__ void sort_steps_reg(uint64_t (&v)[EPT], int gbase, int lane) {
+  sort_step_reg<EPT, SIZE, (1 << LST)>(v, gbase, lane);
+  if constexpr (LST > 0) sort_steps_reg<EPT, SIZE, LST - 1>(v, gbase, lane);
+}
+
+template <int N>
+constexpr int ilog2() { return N <= 1 ? 0 : 1 + ilog2<N / 2>(); }
+
+template <int EPT>
+__device__ void sort_keys(uint64_t* keys) {
+  constexpr int BW = 64 * EPT;
+  constexpr int NS = BW * (PLAN_NT / 64);
+  constexpr int LOG_BW = ilog2<BW>();
+  constexpr int LOG_NS = ilog2<NS>();
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int gbase = wv * BW;
+  uint64_t v[EPT];
+  static_for<EPT>([&](auto jc) { v[decltype(jc)::value] = keys[gbase + decltype(jc)::value * 64 + lane]; });
+  // block sizes 2 .. BW: inside the wave
+  static_for<LOG_BW>([&](auto a) {
+    constexpr int lsz = decltype(a)::value + 1;
+    sort_steps_reg<EPT, (1 << lsz), lsz - 1>(v, gbase, lane);
+  });
+  // block sizes 2 BW .. NS: distances >= BW through LDS, the rest in registers
+  static_for<LOG_NS - LOG_BW>([&](auto a) {
+    constexpr int lsz = LOG_BW + 1 + decltype(a)::value;
+    constexpr int size = 1 << lsz;
+    static_for<EPT>([&](auto jc) { keys[gbase + decltype(jc)::value * 64 + lane] = v[decltype(jc)::value]; });
+    __syncthreads();
+    for (int stride = size >> 1; stride >= BW; stride >>= 1) {
+      for (int i = threadIdx.x; i < NS / 2; i += PLAN_NT) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool up = (lo & size) == 0;
+        const uint64_t x = keys[lo], y = keys[hi];
+        if ((x > y) == up) {
+          keys[lo] = y;
+          keys[hi] = x;
+        }
+      }
+      __syncthreads();
+    }
+    static_for<EPT>([&](auto jc) { v[decltype(jc)::value] = keys[gbase + decltype(jc)::value * 64 + lane]; });
+    sort_steps_reg<EPT, size, LOG_BW - 1>(v, gbase, lane);
+  });
+  __syncthreads();  // every wave has read its block before the sorted keys overwrite it
+  static_for<EPT>([&](auto jc) { keys[gbase + decltype(jc)::value * 64 + lane] = v[decltype(jc)::value]; });
   __syncthreads();
 }
 
@@ -177,7 +276,7 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
   const int t0 = ch * C;
   const int Cc = min(C, D.T - t0);
   const int E = Cc * W;
-  const int Ep2 = pow2_ceil(E);
+  const int NS = plan_sort_n(C * W);
   const long long cidx = (long long)st * D.nch + ch;
   const long long wbase = ((long long)st * D.T + t0) * W;  // [S][T][W] offset of the chunk's first event
   const long long rbase = ((long long)st * D.T + t0) * R;
@@ -199,16 +298,19 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
   int32_t* sslot = (int32_t*)(lds + PL.sslot);
   uint16_t* sev = (uint16_t*)(lds + PL.sev);
   uint16_t* pos = (uint16_t*)(lds + PL.pos);
+  int16_t* scode = (int16_t*)(lds + PL.scode);  // last-event code per sorted event
   float* sA = (float*)(lds + PL.sA);
   float* sB = (float*)(lds + PL.sB);
   unsigned long long* kmask = (unsigned long long*)(lds + PL.kmask);
   unsigned long long* qmask = (unsigned long long*)(lds + PL.qmask);
   uint64_t* rmask = (uint64_t*)(lds + PL.rmask);
   int* roff = (int*)(lds + PL.roff);
+  int* lev = (int*)(lds + PL.lev);
+  int* loff = (int*)(lds + PL.loff);
   int* tot = (int*)(lds + PL.tot);
 
   // 1. write events -> sort keys (slot, event index); gates of the chunk; empty term masks.
-  for (int e = tid; e < Ep2; e += PLAN_NT) {
+  for (int e = tid; e < NS; e += PLAN_NT) {
     uint64_t key = ~0ull;
     if (e < E) key = ((uint64_t)(uint32_t)a.widx[wbase + e] << 32) | (uint32_t)e;
     keys[e] = key;
@@ -226,7 +328,7 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
   for (int i = tid; i < C * PL.kwm; i += PLAN_NT) kmask[i] = 0ull;
   for (int i = tid; i < C * PL.qwm; i += PLAN_NT) qmask[i] = 0ull;
   __syncthreads();
-  bitonic_sort_u64<PLAN_NT>(keys, Ep2);
+  if (NS == 4096) sort_keys<8>(keys); else sort_keys<16>(keys);
   for (int e = tid; e < E; e += PLAN_NT) {
     const uint64_t k = keys[e];
     sslot[e] = (int32_t)(k >> 32);
@@ -234,7 +336,20 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
     pos[k & 0xFFFF] = (uint16_t)e;
   }
   __syncthreads();
-  for (int e = tid; e < E; e += PLAN_NT) sw[e] = a.wwt[wbase + sev[e]];
+  {  // write weights in sorted event order (loads issued together: the flat loads may not pass the LDS stores)
+    constexpr int GB = 8;
+    for (int e0 = tid; e0 < E; e0 += PLAN_NT * GB) {
+      float wv8[GB];
+      static_for<GB>([&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        wv8[k] = a.wwt[wbase + sev[min(e0 + k * PLAN_NT, E - 1)]];
+      });
+      static_for<GB>([&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        if (e0 + k * PLAN_NT < E) sw[e0 + k * PLAN_NT] = wv8[k];
+      });
+    }
+  }
 
   // 2. segments (runs of equal slots) and the multi-event table: ids by a workgroup prefix sum over contiguous
   //    ranges of the sorted events.
@@ -273,7 +388,7 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
       const bool multi = !(first && last);
       if (first) {
         ++g;
-        segs[g].slot = sslot[e];
+        if (a.scat) segs[g].slot = sslot[e];
         if (multi) {
           ++m;
           msegs[m].slot = sslot[e];
@@ -281,17 +396,17 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
           msegs[m].pad = 0;
         }
       }
-      if (last) segs[g].end = e + 1;
+      if (last && a.scat) segs[g].end = e + 1;
       const int evi = sev[e];
       Ev x;
       x.w = sw[e];
       x.tok = evi / W;
-      ev[e] = x;
+      if (a.scat) ev[e] = x;
       if (multi) {
         mev[me++] = x;
         if (last) msegs[m].end = me;
       }
-      wlast[evi] = (int16_t)(!last ? -1 : (multi ? m : -2));
+      scode[e] = (int16_t)(!last ? -1 : (multi ? m : -2));
     }
   }
   __syncthreads();
@@ -299,23 +414,37 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
   // 3. write-gather terms (slot, a_ti), one thread per term; terms meeting an earlier event of their slot are
   //    flagged. Then K (dense rows): one thread per token adds its flagged terms' contributions in term order.
   for (int i = tid; i < C * C; i += PLAN_NT) dense[i] = 0.0f;
-  for (int evi = tid; evi < E; evi += PLAN_NT) {
-    const int e = pos[evi];
-    const int slot = sslot[e];
-    const float wt = a.wwt[wbase + evi];
-    float prod = 1.0f;
-    bool has = false;
-    for (int e2 = e - 1; e2 >= 0 && sslot[e2] == slot; --e2) {
-      prod *= sA[sev[e2] / W];
-      has = true;
-    }
-    Pair p;
-    p.slot = slot;
-    p.coef = wt * prod;
-    pw[evi] = p;
-    if (has) {
-      const int t = evi / W, i = evi % W;
-      atomicOr(&kmask[t * PL.kwm + (i >> 6)], 1ull << (i & 63));
+  {
+    constexpr int GB = 8;
+    for (int v0 = tid; v0 < E; v0 += PLAN_NT * GB) {
+      float wt8[GB];
+      static_for<GB>([&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        wt8[k] = a.wwt[wbase + min(v0 + k * PLAN_NT, E - 1)];
+      });
+      static_for<GB>([&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        const int evi = v0 + k * PLAN_NT;
+        if (evi < E) {
+          const int e = pos[evi];
+          const int slot = sslot[e];
+          float prod = 1.0f;
+          bool has = false;
+          for (int e2 = e - 1; e2 >= 0 && sslot[e2] == slot; --e2) {
+            prod *= sA[sev[e2] / W];
+            has = true;
+          }
+          Pair p;
+          p.slot = slot;
+          p.coef = wt8[k] * prod;
+          pw[evi] = p;
+          wlast[evi] = scode[e];
+          if (has) {
+            const int t = evi / W, i = evi % W;
+            atomicOr(&kmask[t * PL.kwm + (i >> 6)], 1ull << (i & 63));
+          }
+        }
+      });
     }
   }
   __syncthreads();
@@ -341,9 +470,9 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
   __syncthreads();
 
   // 4. L = diag(alpha beta) K (unit diagonal) with the nonzero mask of each row (one wave per row), then
-  //    T = (I + L)^-1 in place, row after row, by wave 0 alone (lane s holds columns s and s + 64), summing over
-  //    the row's nonzero entries in increasing order. Meanwhile waves 1.. compute the read-gather terms
-  //    (slot, b_ti), one thread per term, flagging the terms that meet an earlier write of their slot.
+  //    T = (I + L)^-1 in place by forward substitution, rows grouped by dependency level (a row after every row it
+  //    uses): one wave per row (lane s holds columns s and s + 64), summing over the row's nonzero entries in
+  //    increasing order.
   for (int t = wv; t < Cc; t += PLAN_NT / 64) {
     const float ab = sA[t] * sB[t];
     bool nz0 = false, nz1 = false;
@@ -364,10 +493,62 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
     }
   }
   __syncthreads();
+  // levels of the rows' dependency graph (row t needs the rows of its mask): wave 0, lane l holds rows l, l + 64
   if (wv == 0) {
-    for (int t = 1; t < Cc; ++t) {
+    const int r0 = lane, r1 = lane + 64;
+    const uint64_t a0 = r0 < Cc ? rmask[2 * r0] : 0ull, a1 = r0 < Cc ? rmask[2 * r0 + 1] : 0ull;
+    const uint64_t b0 = r1 < Cc ? rmask[2 * r1] : 0ull, b1 = r1 < Cc ? rmask[2 * r1 + 1] : 0ull;
+    if (r0 < C) lev[r0] = 0;
+    if (r1 < C) lev[r1] = 0;
+    wave_sync_lds();
+    for (int it = 0; it < C; ++it) {  // Jacobi sweeps: converges in (depth + 1) sweeps
+      int n0 = 0, n1 = 0;
+      for (int half = 0; half < 2; ++half) {
+        uint64_t m = half ? a1 : a0;
+        while (m) {
+          const int c = half * 64 + __ffsll((unsigned long long)m) - 1;
+          m &= m - 1;
+          n0 = max(n0, lev[c] + 1);
+        }
+        m = half ? b1 : b0;
+        while (m) {
+          const int c = half * 64 + __ffsll((unsigned long long)m) - 1;
+          m &= m - 1;
+          n1 = max(n1, lev[c] + 1);
+        }
+      }
+      const bool changed = (r0 < C && n0 != lev[r0]) || (r1 < C && n1 != lev[r1]);
+      wave_sync_lds();
+      if (r0 < C) lev[r0] = n0;
+      if (r1 < C) lev[r1] = n1;
+      wave_sync_lds();
+      if (__ballot(changed) == 0ull) break;
+    }
+    const int l0 = r0 < Cc ? lev[r0] : 0, l1 = r1 < Cc ? lev[r1] : 0;
+    int maxlev = max(l0, l1);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) maxlev = max(maxlev, __shfl_xor(maxlev, o, 64));
+    // rows of each level in increasing order: list roff[loff[v] .. loff[v + 1])
+    const uint64_t below = lanes_below();
+    int base = 0;
+    for (int v = 1; v <= maxlev; ++v) {
+      const uint64_t q0 = __ballot(l0 == v && r0 < Cc), q1 = __ballot(l1 == v && r1 < Cc);
+      if (l0 == v && r0 < Cc) roff[base + __popcll(q0 & below)] = r0;
+      if (l1 == v && r1 < Cc) roff[base + __popcll(q0) + __popcll(q1 & below)] = r1;
+      if (lane == 0) loff[v] = base;
+      base += __popcll(q0) + __popcll(q1);
+    }
+    if (lane == 0) {
+      loff[maxlev + 1] = base;
+      tot[0] = maxlev;
+    }
+  }
+  __syncthreads();
+  const int nlev = tot[0];
+  for (int v = 1; v <= nlev; ++v) {  // rows of one level are independent: one wave per row
+    for (int k = loff[v] + wv; k < loff[v + 1]; k += PLAN_NT / 64) {
+      const int t = roff[k];
       const uint64_t mk0 = rmask[2 * t], mk1 = rmask[2 * t + 1];
-      if ((mk0 | mk1) == 0) continue;  // row t of T is e_t
       float acc0 = 0.0f, acc1 = 0.0f;
       for (int half = 0; half < 2; ++half) {
         uint64_t mk = half ? mk1 : mk0;
@@ -379,29 +560,47 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
           if (lane + 64 <= m) acc1 += l * dense[m * C + lane + 64];
         }
       }
+      wave_sync_lds();
       if (lane < t) dense[t * C + lane] = -acc0;
       if (lane + 64 < t) dense[t * C + lane + 64] = -acc1;
-      wave_sync_lds();
     }
-  } else {
-    const int nth = PLAN_NT - 64;
-    for (int x = tid - 64; x < Cc * R; x += nth) {
-      const int t = x / R;
-      const int j = a.ridx[rbase + x];
-      const float rho = a.rwt[rbase + x];
-      const int l = lower_bound_slot(sslot, E, j);
-      float prod = 1.0f;
-      if (l < E && sslot[l] == j && sev[l] / W <= t) {
-        int e1 = l;
-        while (e1 + 1 < E && sslot[e1 + 1] == j && sev[e1 + 1] / W <= t) ++e1;
-        for (int e2 = e1; e2 >= l; --e2) prod *= sA[sev[e2] / W];
-        const int i = x % R;
-        atomicOr(&qmask[t * PL.qwm + (i >> 6)], 1ull << (i & 63));
-      }
-      Pair p;
-      p.slot = j;
-      p.coef = rho * prod;
-      pr[x] = p;
+    __syncthreads();
+  }
+  // read-gather terms (slot, b_ti), one thread per term, flagging the terms that meet an earlier write of their slot
+  {
+    constexpr int QB = 4;  // read terms per thread per batch (their loads issued together)
+    const int nth = PLAN_NT;
+    const int nx = Cc * R;
+    for (int x0 = tid; x0 < nx; x0 += nth * QB) {
+      int jj[QB];
+      float rr[QB];
+      static_for<QB>([&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        const int x = min(x0 + k * nth, nx - 1);
+        jj[k] = a.ridx[rbase + x];
+        rr[k] = a.rwt[rbase + x];
+      });
+      static_for<QB>([&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        const int x = x0 + k * nth;
+        if (x < nx) {
+          const int t = x / R;
+          const int j = jj[k];
+          const int l = lower_bound_slot(sslot, E, j);
+          float prod = 1.0f;
+          if (l < E && sslot[l] == j && sev[l] / W <= t) {
+            int e1 = l;
+            while (e1 + 1 < E && sslot[e1 + 1] == j && sev[e1 + 1] / W <= t) ++e1;
+            for (int e2 = e1; e2 >= l; --e2) prod *= sA[sev[e2] / W];
+            const int i = x % R;
+            atomicOr(&qmask[t * PL.qwm + (i >> 6)], 1ull << (i & 63));
+          }
+          Pair p;
+          p.slot = j;
+          p.coef = rr[k] * prod;
+          pr[x] = p;
+        }
+      });
     }
   }
   __syncthreads();

@@ -228,6 +228,7 @@ struct PlanArgs {
   const void* alpha; const void* beta;
   unsigned char* chunks;  // [S * nch] regions of chunk_layout(C, W, R).bytes
   ChunkCounts* counts;    // [S * nch]
+  int scat;               // also write the slot segments and their events (read by loop_kernel only)
 };
 hipError_t launch_plan(const Dims& D, const PlanArgs& a, hipStream_t st);
 
@@ -238,6 +239,8 @@ struct LoopArgs {
   void* bank; void* out;
 };
 hipError_t launch_loop(const Dims& D, const LoopArgs& a, hipStream_t st);
+// True if launch_loop runs the held-row variant (which reads last-event codes, not slot segments).
+bool loop_held_path(const Dims& D);
 
 struct DecodeArgs {
   const void* wkeys; const void* rq; const void* values; const void* alpha; const void* beta; const void* subkeys;
