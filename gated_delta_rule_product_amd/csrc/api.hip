@@ -183,6 +183,11 @@ WsLayout layout(const Dims& D, int op) {
     return r;
   };
   L.cand = take(2 * MAX_CAND * 8);
+  {
+    size_t sumn = 0;
+    for (int f = 0; f < D.F; ++f) sumn += (size_t)D.widths[f];
+    L.snorm = take((size_t)D.H * sumn * 4);
+  }
   if (op == SDM_OP_WRITE_READ) {
     const size_t nw = (size_t)D.S * D.T * D.W, nr = (size_t)D.S * D.T * D.R;
     const size_t nc = (size_t)D.S * D.nch;
@@ -347,6 +352,7 @@ sdm_status topk_product_keys(const sdm_config* cfg, const void* queries, const v
   a.stream_major = 0;
   a.ids[0] = idx;
   a.vals[0] = scores;
+  a.snorm = (float*)(ws + L.snorm);
   TRY(hip_status(timed(SDM_K_TOPK, st, [&] { return launch_topk(D, a, st); }), "top-k launch"));
   return ok();
 }
@@ -413,6 +419,7 @@ sdm_status sdm_write_read(const sdm_config* cfg, const void* write_keys, const v
   ta.vals[1] = (float*)(ws + L.rwt);
   ta.user_ids[0] = write_idx;
   ta.user_ids[1] = read_idx;
+  ta.snorm = (float*)(ws + L.snorm);
   TRY(hip_status(timed(SDM_K_TOPK, st, [&] { return launch_topk(D, ta, st); }), "top-k launch"));
   PlanArgs pa;
   pa.widx = (const int32_t*)(ws + L.widx);

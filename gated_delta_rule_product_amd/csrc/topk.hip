@@ -1,4 +1,7 @@
 // Exact product-key top-k kernels: the candidate table and the batched top-k (write keys and read queries).
+#include <cstdlib>
+#include <cstring>
+
 #include "sdm_internal.h"
 #include "topk_device.h"
 #include "topk_wave.h"
@@ -64,7 +67,41 @@ __host__ __device__ inline size_t topk2_wave_lds(int F, int kpmax, int k, int QW
   size_t n = (size_t)QW * 64 * NPL * 4;
   n += (size_t)QW * F * kpmax * 6;
   n = (n + 7) & ~(size_t)7;
-  return n + (size_t)(2 * KS + 8) * 8;
+  return n + (size_t)(2 * KS + 8) * 8 + (size_t)64 * NPL * 2;  // + kept-candidate list (filtered scoring)
+}
+
+// ------------------------------------------------------------------------------------------- filtered scoring
+// For bf16 activations the factor scores are first computed with bf16 MFMA (float32 accumulation) as a filter, and
+// only the sub-keys that can still be among a factor's top k_p are scored exactly (the fp64 chain that defines the
+// score). With s the defined score (float32 rounding of the fp64 chain) and s^ the MFMA score, every product of two
+// bf16 values is exact in float32, so |s - s^| <= E with
+//   E = (dk + 2) 2^-23 |x| |c| (1 + 2^-20) + dk 2^-125 (|x| + |c| + 1)
+// (x the query slice, c the sub-key row, |.| Euclidean norms): dk float32 additions in any order, truncating or
+// rounding, the final rounding of s, and flushed subnormal inputs or products. Let v be the smallest of the k_p
+// largest s^ and E_max the largest bound of the row: those k_p sub-keys have s >= s^ - E >= v - E_max, so the k_p-th
+// largest s is >= v - E_max, every member of the true top k_p has s >= v - E_max and therefore s^ + E >= v - E_max.
+// Keeping the sub-keys with s^ + E >= v - E_max loses none of them, and the exact selection among the kept ones
+// (usually k_p or a few more) equals the selection among all.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Euclidean norms of every sub-key row (fp64 sum of squares, rounded up to float32): snorm[h][sum n_f].
+__global__ __launch_bounds__(256) void subkey_norm_kernel(const bf16_t* __restrict__ sub, int total, int dk,
+                                                          float* __restrict__ snorm) {
+  const long long i = (long long)blockIdx.y * total + blockIdx.x * 256 + threadIdx.x;
+  if (blockIdx.x * 256 + threadIdx.x >= total) return;
+  const bf16_t* r = sub + i * dk;
+  double s2 = 0.0;
+  for (int c = 0; c < dk; ++c) {
+    const double y = (double)bf16_to_f(r[c]);
+    s2 = fma(y, y, s2);
+  }
+  snorm[i] = __double2float_ru(sqrt(s2) * (1.0 + 0x1p-40));
+}
+
+__device__ __forceinline__ bf16x8_t load_bf16x8(const bf16_t* p) {
+  const uint4 v = *(const uint4*)p;
+  return __builtin_bit_cast(bf16x8_t, v);
 }
 
 // 16 bytes of a sub-key row and element e of it as fp64 (exact widening).
@@ -84,7 +121,150 @@ template <> struct Vec16<bf16_t> {
   }
 };
 
-template <typename A, int NPL, int CPL>
+// One factor of the wave's QW queries by the filtered scoring: MFMA tiles of 16 queries (nq used) x 16 sub-keys,
+// bounds, threshold, exact fp64 re-score of the kept sub-keys, exact top-k_p. Writes fsc/fid like the direct path.
+// Requires n % 16 == 0 and dk % 32 == 0, dk <= 128.
+template <int NPL, int QW>
+__device__ void factor_topk_filtered(const Dims& D, const TopkArgs& a, int f, int n, long long nbase,
+                                     const bf16_t* tab, const bf16_t* qf, long long qstride, int nq, float* scs,
+                                     float* fsc, uint16_t* fid, uint64_t* scratch, uint64_t* sorted,
+                                     uint16_t* klist, int kpmax) {
+  constexpr int KBMAX = 4;
+  const int lane = threadIdx.x & 63;
+  const int dk = D.dk, F = D.F;
+  const int KB = dk / 32;
+  const int ql = lane & 15, pt = lane >> 4;
+  const int kind = blockIdx.y;
+  const int kp = a.plan[kind].kp[f];
+  // query fragments (A operand: row = query, 8 consecutive elements of a 32-wide block) and squared norms
+  bf16x8_t qa[KBMAX];
+  double nx2 = 0.0;
+  static_for<KBMAX>([&](auto kc) {
+    constexpr int kb = decltype(kc)::value;
+    if (kb < KB) {
+      if (ql < nq) {
+        qa[kb] = load_bf16x8(qf + ql * qstride + kb * 32 + pt * 8);
+        const uint4 w = __builtin_bit_cast(uint4, qa[kb]);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const double lo = (double)__uint_as_float(ws[e] << 16), hi = (double)__uint_as_float(ws[e] & 0xFFFF0000u);
+          nx2 = fma(lo, lo, nx2);
+          nx2 = fma(hi, hi, nx2);
+        }
+      } else {
+        qa[kb] = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
+      }
+    }
+  });
+  nx2 += __shfl_xor(nx2, 16, 64);
+  nx2 += __shfl_xor(nx2, 32, 64);
+  // MFMA scores of tile T: lane l holds queries 4 (l / 16) + r (r < 4) for sub-key 16 T + l % 16
+  for (int T = 0; T < n / 16; ++T) {
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    const bf16_t* row = tab + (long long)(T * 16 + ql) * dk + pt * 8;
+    static_for<KBMAX>([&](auto kc) {
+      constexpr int kb = decltype(kc)::value;
+      if (kb < KB) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kb], load_bf16x8(row + kb * 32), acc, 0, 0, 0);
+    });
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {  // D row 4 (lane / 16) + r = query, column lane % 16 = sub-key in the tile
+      const int qi = 4 * pt + r;
+      if (qi < nq) scs[qi * 64 * NPL + T * 16 + ql] = acc[r];
+    }
+  }
+  wave_sync();
+  const float* snorm = a.snorm + nbase;
+  const uint64_t below = lanes_below_mask();
+  for (int q = 0; q < nq; ++q) {
+    const double nx = sqrt(__shfl(nx2, q, 64)) * (1.0 + 0x1p-40);
+    // approximate keys, upper bounds and the largest error bound of the row
+    uint64_t key[NPL];
+    float hiv[NPL];
+    double emax = 0.0;
+    bool bad = false;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const int i = lane + 64 * j;
+      key[j] = ~0ull;
+      hiv[j] = -INFINITY;
+      if (i < n) {
+        const float sh = scs[q * 64 * NPL + i];
+        const double ni = (double)snorm[i];
+        const double e = (dk + 2) * 0x1p-23 * nx * ni * (1.0 + 0x1p-20) + dk * 0x1p-125 * (nx + ni + 1.0);
+        bad |= !(fabsf(sh) <= 3.4028234663852886e38f) || !(e <= 1e300);
+        emax = fmax(emax, e);
+        key[j] = ((uint64_t)desc_key(sh) << 32) | (uint32_t)i;
+        hiv[j] = __double2float_ru((double)sh + e);
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) emax = fmax(emax, __shfl_xor(emax, o, 64));
+    const bool anybad = __ballot(bad) != 0ull;
+    // the k_p best approximate scores (radix select, stopped once decided); v = the smallest of them
+    bool all[NPL];
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) all[j] = true;
+    int need = kp, shift = 0, csize = 64 * NPL;
+    const uint32_t res = radix_select32<NPL, true>(key, all, &need, &shift, &csize);
+    uint32_t kmax = 0;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const uint32_t hk = (uint32_t)(key[j] >> 32);
+      if ((hk >> shift) <= (res >> shift) && key[j] != ~0ull) kmax = max(kmax, hk);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+    // at least k_p sub-keys have a lower bound >= v - emax: keep every sub-key whose upper bound reaches it
+    const float thr = anybad ? -INFINITY : __double2float_rd((double)desc_key_value(kmax) - emax);
+    int m = 0;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const int i = lane + 64 * j;
+      const bool kept = i < n && (anybad || hiv[j] >= thr);
+      const uint64_t bm = __ballot(kept);
+      if (kept) klist[m + __popcll(bm & below)] = (uint16_t)i;
+      m += __popcll(bm);
+    }
+    wave_sync();
+    // exact scores of the kept sub-keys (the fp64 chain), then the exact top k_p among them
+    const bf16_t* xq = qf + q * qstride;
+    auto exact_key = [&](int r) -> uint64_t {
+      const int i = klist[r];
+      const bf16_t* y = tab + (long long)i * dk;
+      double acc = 0.0;
+      for (int c0 = 0; c0 < dk; c0 += 8) {
+        const uint4 xv = *(const uint4*)(xq + c0);
+        const uint4 yv = *(const uint4*)(y + c0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = fma(Vec16<bf16_t>::at(xv, e), Vec16<bf16_t>::at(yv, e), acc);
+      }
+      return ((uint64_t)desc_key((float)acc) << 32) | (uint32_t)i;
+    };
+    if (m <= 64) {
+      uint64_t ek[1] = {lane < m ? exact_key(lane) : ~0ull};
+      wave_select_sorted<1>(ek, kp, scratch, sorted);
+    } else if (m <= 128) {
+      uint64_t ek[2];
+      ek[0] = exact_key(lane);
+      ek[1] = lane + 64 < m ? exact_key(lane + 64) : ~0ull;
+      wave_select_sorted<2>(ek, kp, scratch, sorted);
+    } else {
+      uint64_t ek[NPL];
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) ek[j] = lane + 64 * j < m ? exact_key(lane + 64 * j) : ~0ull;
+      wave_select_sorted<NPL>(ek, kp, scratch, sorted);
+    }
+    for (int p = lane; p < kp; p += 64) {
+      const uint64_t kk = sorted[p];
+      fsc[(q * F + f) * kpmax + p] = desc_key_value((uint32_t)(kk >> 32));
+      fid[(q * F + f) * kpmax + p] = (uint16_t)(uint32_t)kk;
+    }
+    wave_sync();
+  }
+}
+
+template <typename A, int NPL, int CPL, bool MF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NPL <= 4 ? 4 : 1))) void topk2_kernel(Dims D, TopkArgs a) {
   constexpr int QW = WaveTile<NPL>::QW;
   constexpr int VEC = Vec16<A>::N;
@@ -105,6 +285,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NPL <= 4 ? 
   uint64_t* scratch =
       (uint64_t*)(wl + (((size_t)QW * 64 * NPL * 4 + (size_t)QW * F * kpmax * 6 + 7) & ~(size_t)7));
   uint64_t* sorted = scratch + KS + 8;
+  uint16_t* klist = (uint16_t*)(sorted + KS);               // [64 NPL] kept candidates (filtered scoring)
   long long sumn = 0;
   for (int f = 0; f < F; ++f) sumn += D.widths[f];
   const A* sub = (const A*)a.subkeys + (long long)h * sumn * dk;
@@ -118,6 +299,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NPL <= 4 ? 
   for (int f = 0; f < F; ++f) {
     const int n = D.widths[f];
     const A* tab = sub + off * dk;
+    if constexpr (MF) {
+      factor_topk_filtered<NPL, QW>(D, a, f, n, (long long)h * sumn + off, (const bf16_t*)tab,
+                                    (const bf16_t*)qbase + f * dk, qstride, nq, scs, fsc, fid, scratch, sorted,
+                                    klist, kpmax);
+      off += n;
+      continue;
+    }
     double acc[QW][NPL];
 #pragma unroll
     for (int q = 0; q < QW; ++q)
@@ -223,22 +411,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NPL <= 4 ? 
   }
 }
 
+template <typename A, int NPL, int CPL, bool MF>
+static void launch_topk2_k(dim3 grid, size_t lds, hipStream_t st, const Dims& D, const TopkArgs& a) {
+  (void)hipFuncSetAttribute((const void*)topk2_kernel<A, NPL, CPL, MF>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)lds);
+  hipLaunchKernelGGL((topk2_kernel<A, NPL, CPL, MF>), grid, dim3(256), lds, st, D, a);
+}
+
 template <typename A, int NPL>
-static bool launch_topk2_npl(const Dims& D, const TopkArgs& a, hipStream_t st, int cpl, size_t lds) {
+static bool launch_topk2_npl(const Dims& D, const TopkArgs& a, hipStream_t st, int cpl, size_t lds, bool mf) {
   constexpr int QW = WaveTile<NPL>::QW;
   const long long BT = (long long)D.B * D.T;
   const long long tiles = (BT + QW - 1) / QW;
   dim3 grid((unsigned)((tiles + 3) / 4), (unsigned)a.nkinds, (unsigned)D.H);
-  if (cpl == 8) {
-    (void)hipFuncSetAttribute((const void*)topk2_kernel<A, NPL, 8>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)lds);
-    hipLaunchKernelGGL((topk2_kernel<A, NPL, 8>), grid, dim3(256), lds, st, D, a);
-  } else {
-    (void)hipFuncSetAttribute((const void*)topk2_kernel<A, NPL, 16>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)lds);
-    hipLaunchKernelGGL((topk2_kernel<A, NPL, 16>), grid, dim3(256), lds, st, D, a);
+  if constexpr (sizeof(A) == 2) {
+    if (mf) {
+      if (cpl == 8) launch_topk2_k<A, NPL, 8, true>(grid, lds, st, D, a);
+      else launch_topk2_k<A, NPL, 16, true>(grid, lds, st, D, a);
+      return true;
+    }
   }
+  if (cpl == 8) launch_topk2_k<A, NPL, 8, false>(grid, lds, st, D, a);
+  else launch_topk2_k<A, NPL, 16, false>(grid, lds, st, D, a);
   return true;
+}
+
+// The filtered (MFMA) scoring serves bf16 activations with factor widths that are multiples of 16 and
+// dk in {32, 64, 96, 128}, when a factor has at least 512 sub-keys: below that the direct fp64 chain over every
+// sub-key costs no more than the filter's extra selection and re-scoring (measured: 256 and 64 sub-keys per factor
+// are as fast or faster direct; 1024 sub-keys are about twice as fast filtered). SDM_TOPK_SCORING=filtered or
+// =direct in the environment overrides the choice (tests exercise both on the same inputs).
+static bool topk_filtered(const Dims& D, const TopkArgs& a) {
+  if (D.act != SDM_BF16 || a.snorm == nullptr) return false;
+  if (D.dk % 32 != 0 || D.dk > 128) return false;
+  int nmax = 0;
+  for (int f = 0; f < D.F; ++f) {
+    if (D.widths[f] % 16 != 0) return false;
+    nmax = D.widths[f] > nmax ? D.widths[f] : nmax;
+  }
+  for (int q = 0; q < a.nkinds; ++q)
+    if (((uintptr_t)a.queries[q]) % 16 != 0) return false;
+  const char* env = getenv("SDM_TOPK_SCORING");
+  if (env && strcmp(env, "direct") == 0) return false;
+  if (env && strcmp(env, "filtered") == 0) return true;
+  return nmax >= 512;
 }
 
 template <typename A>
@@ -264,12 +480,19 @@ static bool launch_topk2(const Dims& D, const TopkArgs& a, hipStream_t st) {
     lds = l > lds ? l : lds;
   }
   if (lds > 128 * 1024) return false;
+  const bool mf = topk_filtered(D, a);
+  if (mf) {
+    int sumn = 0;
+    for (int f = 0; f < D.F; ++f) sumn += D.widths[f];
+    dim3 g((unsigned)((sumn + 255) / 256), (unsigned)D.H);
+    hipLaunchKernelGGL(subkey_norm_kernel, g, dim3(256), 0, st, (const bf16_t*)a.subkeys, sumn, D.dk, a.snorm);
+  }
   switch (npl) {
-    case 1: return launch_topk2_npl<A, 1>(D, a, st, cpl, lds);
-    case 2: return launch_topk2_npl<A, 2>(D, a, st, cpl, lds);
-    case 4: return launch_topk2_npl<A, 4>(D, a, st, cpl, lds);
-    case 8: return launch_topk2_npl<A, 8>(D, a, st, cpl, lds);
-    default: return launch_topk2_npl<A, 16>(D, a, st, cpl, lds);
+    case 1: return launch_topk2_npl<A, 1>(D, a, st, cpl, lds, mf);
+    case 2: return launch_topk2_npl<A, 2>(D, a, st, cpl, lds, mf);
+    case 4: return launch_topk2_npl<A, 4>(D, a, st, cpl, lds, mf);
+    case 8: return launch_topk2_npl<A, 8>(D, a, st, cpl, lds, mf);
+    default: return launch_topk2_npl<A, 16>(D, a, st, cpl, lds, mf);
   }
 }
 

@@ -111,6 +111,37 @@ def test_topk_exact(widths, dk, k, kind, act):
     _topk_case(widths, dk, k, act, kind)
 
 
+@pytest.mark.parametrize("widths,dk,k", [((32, 32), 32, 64), ((64, 32, 16), 64, 64), ((16,), 32, 9),
+                                         ((256, 256), 64, 64), ((48, 16), 96, 33), ((32, 32), 128, 17)])
+@pytest.mark.parametrize("kind", ["random", "ternary", "dup"])
+@pytest.mark.parametrize("scoring", ["filtered", "direct"])
+def test_topk_exact_filtered(widths, dk, k, kind, scoring, monkeypatch):
+    """bf16 shapes the MFMA-filtered scoring can serve (widths multiples of 16, dk a multiple of 32 up to 128), with
+    each scoring forced: ids and scores bit-exact, including the many exact ties of ternary inputs and duplicated
+    sub-keys."""
+    monkeypatch.setenv("SDM_TOPK_SCORING", scoring)
+    print(f"topk {scoring} widths={widths} dk={dk} k={k} kind={kind}", flush=True)
+    _topk_case(widths, dk, k, "bf16", kind, T=40)
+
+
+@pytest.mark.parametrize("name", ["layer_65k", "large_1m"])
+def test_topk_filtered_equals_direct(name, monkeypatch):
+    """The filtered (MFMA) scoring and the direct fp64 scoring return identical ids and scores at full size."""
+    s = synth.WORKLOADS[name]
+    x = synth.make_step_inputs(s.with_(tokens=256))
+    q = to_dev(x["wkeys"], torch.bfloat16)
+    sub = to_dev(synth.make_subkeys(s), torch.bfloat16)
+    print(f"topk filtered vs direct, {name} T=256", flush=True)
+    monkeypatch.setenv("SDM_TOPK_SCORING", "filtered")
+    ids_f, sc_f = binding.topk_product_keys(q, sub, s.widths, s.num_writes)
+    torch.cuda.synchronize()
+    monkeypatch.setenv("SDM_TOPK_SCORING", "direct")
+    ids_d, sc_d = binding.topk_product_keys(q, sub, s.widths, s.num_writes)
+    torch.cuda.synchronize()
+    assert torch.equal(ids_f, ids_d)
+    assert torch.equal(sc_f, sc_d)
+
+
 def test_topk_zero_query_tie_order():
     q = np.zeros((1, 1, 1, 2 * 8), np.float32)
     sub = np.random.default_rng(0).standard_normal((1, 64, 8)).astype(np.float32)
