@@ -141,6 +141,27 @@ def make_bank(s: Shape, seed: int = 0, threads: int = 8) -> np.ndarray:
     return out
 
 
+def fill_bank_stream_device(rows_view, s: Shape, b: int, h: int, seed: int = 0) -> None:
+    """Fills the device bank rows [rows, d] of stream (b, h) (torch view, any row pitch) with N(0, 0.02^2) drawn by
+    torch's device generator seeded with seed * 1000003 + b * heads + h, rounded to the view's dtype.
+
+    For banks too large to draw on the host (the 1,048,576-slot workload: 32 GiB); the same seed always gives the
+    same values on the same device type."""
+    import torch
+
+    g = torch.Generator(device=rows_view.device)
+    g.manual_seed(int(seed) * 1000003 + b * s.heads + h)
+    z = torch.randn(tuple(rows_view.shape), generator=g, device=rows_view.device, dtype=torch.float32)
+    rows_view.copy_((z * 0.02).to(rows_view.dtype))
+
+
+def fill_bank_device(bank, s: Shape, seed: int = 0) -> None:
+    """Fills a device bank view [B, H, rows, d] stream by stream (fill_bank_stream_device)."""
+    for b in range(bank.shape[0]):
+        for h in range(bank.shape[1]):
+            fill_bank_stream_device(bank[b, h], s, b, h, seed)
+
+
 def make_inputs(s: Shape, seed: int = 0) -> dict:
     d = make_step_inputs(s, seed)
     d["subkeys"] = make_subkeys(s, seed)

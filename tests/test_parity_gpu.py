@@ -354,3 +354,100 @@ def test_layer_65k_full_size():
     ref = run_oracle(s, x)
     e = check_parity(s, gpu, ref)
     print("full-size layer_65k errors", e, flush=True)
+
+
+def _sub(x, lo, hi):
+    """Per-token inputs restricted to tokens [lo, hi)."""
+    return {k: (v[:, lo:hi] if k in ("wkeys", "rq", "values", "alpha", "beta") else v) for k, v in x.items()}
+
+
+@pytest.mark.slow
+def test_three_factor_65k_full_size():
+    """Three-factor workload at full size (B 1, T 32768, H 4, d 256, factors 64 x 32 x 32, W = R = 64, chunk 128,
+    bf16 bank). The oracle runs on the first 2048 tokens (outputs there depend on nothing later); at full size:
+    ids of sampled tokens against the oracle's top-k, and a run split at token 2048 equal bit for bit to one run."""
+    s = synth.WORKLOADS["three_factor_65k"]
+    P = 2048
+    print("full-size three_factor_65k: generating inputs", flush=True)
+    x = synth.make_inputs(s)
+    print("full-size three_factor_65k: GPU, whole sequence", flush=True)
+    out, bank, widx, ridx = run_gpu(s, x)
+    print("full-size three_factor_65k: oracle on the prefix", flush=True)
+    sp = s.with_(tokens=P)
+    ref = run_oracle(sp, _sub(x, 0, P))
+    assert np.array_equal(widx[:, :P], ref["widx"]) and np.array_equal(ridx[:, :P], ref["ridx"])
+    e_out = rowwise_rel(out[:, :P], ref["out"])
+    assert e_out <= RTOL["bf16"], f"out rel err {e_out}"
+    rng = np.random.default_rng(5)
+    ts = np.sort(rng.choice(s.tokens, 64, replace=False))
+    for key, got in (("wkeys", widx), ("rq", ridx)):
+        rid, _ = oracle.topk(x[key][:, ts], x["subkeys"], s.widths, s.num_writes)
+        assert np.array_equal(got[:, ts], rid), f"{key}: sampled ids differ"
+    print("full-size three_factor_65k: GPU prefix and remainder", flush=True)
+    out_p, bank_p, _, _ = run_gpu(sp, _sub(x, 0, P))
+    e_bank = rowwise_rel(bank_p, ref["bank"])
+    assert e_bank <= RTOL["bf16"], f"prefix bank rel err {e_bank}"
+    assert np.array_equal(out_p, out[:, :P])
+    out_r, bank_r, _, _ = run_gpu(s.with_(tokens=s.tokens - P), _sub(x, P, s.tokens), bank=bank_p)
+    assert np.array_equal(out_r, out[:, P:]) and np.array_equal(bank_r, bank)
+    print("full-size three_factor_65k errors", e_out, e_bank, flush=True)
+
+
+@pytest.mark.slow
+def test_large_1m_full_size():
+    """1,048,576-slot workload at full size (B 4, T 8192, H 4, d 512, W = R = 64, chunk 64, bf16 on a 32 GiB float32
+    bank, padded pitch, int64 offsets). Oracle on the first 256 tokens of batch row 0 (its 4 streams); at full
+    size: a run split at token 256 equal bit for bit to one run, sampled ids against the oracle's top-k."""
+    s = synth.WORKLOADS["large_1m"]
+    P = 256
+    at = torch.bfloat16
+    pitch = binding.bank_pitch(s.head_dim, torch.float32)
+    print("full-size large_1m: generating inputs", flush=True)
+    x = synth.make_step_inputs(s)
+    x["subkeys"] = synth.make_subkeys(s)
+    t = {k: to_dev(x[k], at) for k in ("wkeys", "rq", "values", "alpha", "beta", "subkeys")}
+    kw = dict(widths=s.widths, num_writes=s.num_writes, num_reads=s.num_reads, chunk_size=s.chunk_size)
+
+    def call(bank, lo, hi):
+        out, wi, ri = binding.sdm_write_read(*(t[k][:, lo:hi].contiguous() for k in ("wkeys", "rq", "values",
+                                                                                      "alpha", "beta")),
+                                             t["subkeys"], bank, want_index=True, **kw)
+        torch.cuda.synchronize()
+        return out, wi, ri
+
+    bank = binding.alloc_bank(s.batch, s.heads, s.rows, s.head_dim, torch.float32, DEV, pitch=pitch)
+    synth.fill_bank_device(bank, s)
+    print("full-size large_1m: GPU, whole sequence", flush=True)
+    out, widx, ridx = call(bank, 0, s.tokens)
+    print("full-size large_1m: split run", flush=True)
+    bank2 = binding.alloc_bank(s.batch, s.heads, s.rows, s.head_dim, torch.float32, DEV, pitch=pitch)
+    synth.fill_bank_device(bank2, s)
+    out_p, wp, rp = call(bank2, 0, P)
+    assert torch.equal(out_p, out[:, :P]) and torch.equal(wp, widx[:, :P]) and torch.equal(rp, ridx[:, :P])
+    # the rows the prefix wrote in batch row 0, for the oracle comparison
+    touched = [torch.unique(wp[0, :, h].reshape(-1).long()) for h in range(s.heads)]
+    got_rows = [bank2[0, h][touched[h]].float().cpu().numpy() for h in range(s.heads)]
+    out_r, _, _ = call(bank2, P, s.tokens)
+    assert torch.equal(out_r, out[:, P:]), "split run outputs differ"
+    assert torch.equal(bank2, bank), "split run bank differs"
+    del bank2, out_r
+    print("full-size large_1m: oracle on the prefix of batch row 0", flush=True)
+    b0 = np.empty((1, s.heads, s.rows, s.head_dim), np.float32)
+    tmp = torch.empty((s.rows, s.head_dim), dtype=torch.float32, device=DEV)
+    for h in range(s.heads):
+        synth.fill_bank_stream_device(tmp, s, 0, h)
+        b0[0, h] = tmp.cpu().numpy()
+    del tmp
+    xp = {k: x[k][0:1, :P] for k in ("wkeys", "rq", "values", "alpha", "beta")}
+    ref = oracle.write_read(xp["wkeys"], xp["rq"], xp["values"], xp["alpha"], xp["beta"], x["subkeys"], b0,
+                            s.widths, s.num_writes, s.num_reads, act_bf16=True)
+    assert np.array_equal(to_np(widx[0:1, :P]), ref["widx"]) and np.array_equal(to_np(ridx[0:1, :P]), ref["ridx"])
+    e_out = rowwise_rel(to_np(out[0:1, :P]), ref["out"])
+    assert e_out <= RTOL["bf16"], f"out rel err {e_out}"
+    e_bank = max(rowwise_rel(got_rows[h], ref["bank"][0, h][touched[h].cpu().numpy()]) for h in range(s.heads))
+    assert e_bank <= RTOL["f32"], f"prefix bank rel err {e_bank}"
+    rng = np.random.default_rng(6)
+    ts = np.sort(rng.choice(s.tokens, 16, replace=False))
+    rid, _ = oracle.topk(x["wkeys"][:, ts], x["subkeys"], s.widths, s.num_writes)
+    assert np.array_equal(to_np(widx[:, ts]), rid), "sampled write ids differ"
+    print("full-size large_1m errors", e_out, e_bank, flush=True)
