@@ -136,6 +136,61 @@ def bench_write_read(args, torch, binding, synth):
     }
 
 
+def bench_other(args, torch, binding, synth):
+    """The three-factor (65,536 slots, bf16 bank, chunk 128) and 1,048,576-slot (32 GiB float32 bank) workloads at
+    full size: tokens/s and the chunk loop's algorithmic bandwidth. Context lines, not the headline value."""
+    res = {}
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16}
+    dev = torch.device("cuda:0")
+    for name in ("three_factor_65k", "large_1m"):
+        s = synth.WORKLOADS[name]
+        log(f"[bench] {name}: inputs")
+        x = synth.make_step_inputs(s)
+        x["subkeys"] = synth.make_subkeys(s)
+        t = {k: torch.from_numpy(x[k]).to(dev).to(dt[s.act]) for k in ("wkeys", "rq", "values", "alpha", "beta",
+                                                                        "subkeys")}
+        del x
+        pitch = binding.bank_pitch(s.head_dim, dt[s.bank])
+        bank = binding.alloc_bank(s.batch, s.heads, s.rows, s.head_dim, dt[s.bank], dev, pitch=pitch)
+        synth.fill_bank_device(bank, s)
+        cfg = binding.make_config(s.batch, s.tokens, s.heads, s.widths, s.subkey_dim, s.head_dim, s.num_writes,
+                                  s.num_reads, s.chunk_size, binding.SDM_BF16 if s.act == "bf16" else binding.SDM_F32,
+                                  binding.SDM_BF16 if s.bank == "bf16" else binding.SDM_F32, s.rows, pitch)
+        ws = torch.empty(binding.workspace_size(cfg, binding.SDM_OP_WRITE_READ), dtype=torch.uint8, device=dev)
+        out = torch.empty((s.batch, s.tokens, s.heads, s.head_dim), dtype=dt[s.act], device=dev)
+
+        def step():
+            binding.sdm_write_read(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"], t["subkeys"], bank,
+                                   widths=s.widths, num_writes=s.num_writes, num_reads=s.num_reads,
+                                   chunk_size=s.chunk_size, out=out, workspace=ws)
+
+        step()
+        torch.cuda.synchronize()
+        binding.profile_enable(True)
+        n = max(1, args.other_steps)
+        t0 = time.perf_counter()
+        for _ in range(n):
+            step()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        prof = binding.profile_read()
+        binding.profile_enable(False)
+        ms = (t1 - t0) * 1e3 / n
+        loop_ms = prof["loop"][0] / prof["loop"][1]
+        alg = loop_algorithmic_bytes(s, s.batch * s.tokens * s.heads)
+        res[name] = {"tokens_per_s": round(s.batch * s.tokens / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
+                     "steps": n, "kernels_avg_ms": {k: round(v[0] / v[1], 4) for k, v in prof.items() if v[1]},
+                     "loop_algorithmic_bytes": alg, "loop_achieved_GBps": round(alg / (loop_ms * 1e-3) / 1e9, 1),
+                     "loop_frac_of_8TBps": round(alg / (loop_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "bank_bytes": s.batch * s.heads * s.rows * s.head_dim * (2 if s.bank == "bf16" else 4),
+                     "config": f"B{s.batch} T{s.tokens} H{s.heads} d{s.head_dim} widths {s.widths} dk {s.subkey_dim} "
+                               f"W=R={s.num_writes} chunk {s.chunk_size} {s.act} act / {s.bank} bank"}
+        log(f"[bench] {name}: {res[name]['tokens_per_s']} tokens/s, loop {loop_ms:.3f} ms")
+        del bank, ws, out, t
+        torch.cuda.empty_cache()
+    return res
+
+
 def bench_decode(args, torch, binding, synth):
     s = synth.WORKLOADS["decode_b128"]
     dev = torch.device("cuda:0")
@@ -238,6 +293,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=64)
     ap.add_argument("--decode-warmup", type=int, default=8)
     ap.add_argument("--cpu-tokens", type=int, default=0, help="tokens of the oracle sample (0: the whole workload)")
+    ap.add_argument("--other-steps", type=int, default=3, help="timed calls of each context workload (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -255,6 +311,7 @@ def main():
     binding.load()
     wr = bench_write_read(args, torch, binding, synth)
     dec = bench_decode(args, torch, binding, synth)
+    other = bench_other(args, torch, binding, synth) if args.other_steps > 0 else None
     s = wr["shape"]
     line = {
         "metric": METRIC, "value": round(wr["tokens_per_s"], 1), "unit": "tokens/s", "n_gpus": 1,
@@ -271,6 +328,7 @@ def main():
         "kernels_avg_ms": wr["kernels_avg_ms"],
         "roofline": wr["roofline"],
         "decode": dec,
+        "other_workloads": other,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args, s, synth)
