@@ -160,71 +160,138 @@ __device__ void factor_topk_filtered(const Dims& D, const TopkArgs& a, int f, in
   nx2 += __shfl_xor(nx2, 16, 64);
   nx2 += __shfl_xor(nx2, 32, 64);
   // MFMA scores of tile T: lane l holds queries 4 (l / 16) + r (r < 4) for sub-key 16 T + l % 16
-  for (int T = 0; T < n / 16; ++T) {
-    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    const bf16_t* row = tab + (long long)(T * 16 + ql) * dk + pt * 8;
-    static_for<KBMAX>([&](auto kc) {
-      constexpr int kb = decltype(kc)::value;
-      if (kb < KB) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kb], load_bf16x8(row + kb * 32), acc, 0, 0, 0);
+  // tiles in batches of TB whose B-operand loads are issued together (the table sits in L2: latency, not bandwidth)
+  constexpr int TB = NPL >= 8 ? 8 : 2;
+  const int ntile = n / 16;
+  for (int T0 = 0; T0 < ntile; T0 += TB) {
+    bf16x8_t bv[TB][2];
+    static_for<TB>([&](auto tc) {
+      constexpr int u = decltype(tc)::value;
+      const bf16_t* row = tab + (long long)(min(T0 + u, ntile - 1) * 16 + ql) * dk + pt * 8;
+      bv[u][0] = load_bf16x8(row);
+      if (KB > 1) bv[u][1] = load_bf16x8(row + 32);
     });
+    static_for<TB>([&](auto tc) {
+      constexpr int u = decltype(tc)::value;
+      const int T = T0 + u;
+      if (T < ntile) {
+        const bf16_t* row = tab + (long long)(T * 16 + ql) * dk + pt * 8;
+        f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0], bv[u][0], acc, 0, 0, 0);
+        if (KB > 1) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[1], bv[u][1], acc, 0, 0, 0);
+        static_for<KBMAX - 2>([&](auto kc) {  // dk = 96, 128: the remaining blocks, loaded here
+          constexpr int kb = decltype(kc)::value + 2;
+          if (kb < KB) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kb], load_bf16x8(row + kb * 32), acc, 0, 0, 0);
+        });
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {  // D row 4 (lane / 16) + r = query, column lane % 16 = sub-key in the tile
-      const int qi = 4 * pt + r;
-      if (qi < nq) scs[qi * 64 * NPL + T * 16 + ql] = acc[r];
-    }
+        for (int r = 0; r < 4; ++r) {  // D row 4 (lane / 16) + r = query, column lane % 16 = sub-key in the tile
+          const int qi = 4 * pt + r;
+          if (qi < nq) scs[qi * 64 * NPL + T * 16 + ql] = acc[r];
+        }
+      }
+    });
   }
   wave_sync();
   const float* snorm = a.snorm + nbase;
   const uint64_t below = lanes_below_mask();
   for (int q = 0; q < nq; ++q) {
     const double nx = sqrt(__shfl(nx2, q, 64)) * (1.0 + 0x1p-40);
-    // approximate keys, upper bounds and the largest error bound of the row
-    uint64_t key[NPL];
-    float hiv[NPL];
+    auto bound = [&](float sh, int i) -> double {
+      const double ni = (double)snorm[i];
+      return (dk + 2) * 0x1p-23 * nx * ni * (1.0 + 0x1p-20) + dk * 0x1p-125 * (nx + ni + 1.0);
+    };
     double emax = 0.0;
     bool bad = false;
+    float lmax = -INFINITY;
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
       const int i = lane + 64 * j;
-      key[j] = ~0ull;
-      hiv[j] = -INFINITY;
       if (i < n) {
         const float sh = scs[q * 64 * NPL + i];
-        const double ni = (double)snorm[i];
-        const double e = (dk + 2) * 0x1p-23 * nx * ni * (1.0 + 0x1p-20) + dk * 0x1p-125 * (nx + ni + 1.0);
+        const double e = bound(sh, i);
         bad |= !(fabsf(sh) <= 3.4028234663852886e38f) || !(e <= 1e300);
         emax = fmax(emax, e);
-        key[j] = ((uint64_t)desc_key(sh) << 32) | (uint32_t)i;
-        hiv[j] = __double2float_ru((double)sh + e);
+        lmax = fmaxf(lmax, sh);
       }
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) emax = fmax(emax, __shfl_xor(emax, o, 64));
     const bool anybad = __ballot(bad) != 0ull;
-    // the k_p best approximate scores (radix select, stopped once decided); v = the smallest of them
-    bool all[NPL];
+    // Wide factors first keep only the sub-keys that can reach the k_p-th largest lane maximum of s^ (k_p <= 64
+    // lanes hold a value at least that large): usually a small fraction of the factor.
+    int mA = n;
+    if constexpr (NPL >= 8) {
+      uint64_t lk[1] = {((uint64_t)desc_key(lmax) << 32) | (uint32_t)lane};
+      bool in1[1] = {true};
+      int need1 = kp, sh1 = 0, cs1 = 64;
+      const uint32_t r1 = radix_select32<1, true>(lk, in1, &need1, &sh1, &cs1);
+      uint32_t km1 = ((uint32_t)(lk[0] >> 32) >> sh1) <= (r1 >> sh1) ? (uint32_t)(lk[0] >> 32) : 0u;
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) all[j] = true;
-    int need = kp, shift = 0, csize = 64 * NPL;
-    const uint32_t res = radix_select32<NPL, true>(key, all, &need, &shift, &csize);
-    uint32_t kmax = 0;
+      for (int o = 32; o >= 1; o >>= 1) km1 = max(km1, (uint32_t)__shfl_xor((int)km1, o, 64));
+      const float thrA = (anybad || kp > 64) ? -INFINITY : __double2float_rd((double)desc_key_value(km1) - emax);
+      mA = 0;
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) {
-      const uint32_t hk = (uint32_t)(key[j] >> 32);
-      if ((hk >> shift) <= (res >> shift) && key[j] != ~0ull) kmax = max(kmax, hk);
+      for (int j = 0; j < NPL; ++j) {
+        const int i = lane + 64 * j;
+        bool kept = false;
+        if (i < n) {
+          const float sh = scs[q * 64 * NPL + i];
+          kept = anybad || __double2float_ru((double)sh + bound(sh, i)) >= thrA;
+        }
+        const uint64_t bm = __ballot(kept);
+        if (kept) klist[mA + __popcll(bm & below)] = (uint16_t)i;
+        mA += __popcll(bm);
+      }
+      wave_sync();
     }
+    // approximate keys of the candidates, the k_p best approximate scores (radix select, stopped once decided),
+    // v = the smallest of them; keep every candidate whose upper bound reaches v - E_max
+    auto stage_b = [&](auto nsc) -> int {
+      constexpr int NS = decltype(nsc)::value;
+      uint64_t key[NS];
+      float hiv[NS];
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
-    // at least k_p sub-keys have a lower bound >= v - emax: keep every sub-key whose upper bound reaches it
-    const float thr = anybad ? -INFINITY : __double2float_rd((double)desc_key_value(kmax) - emax);
-    int m = 0;
+      for (int j = 0; j < NS; ++j) {
+        const int r = lane + 64 * j;
+        key[j] = ~0ull;
+        hiv[j] = -INFINITY;
+        if (r < mA) {
+          const int i = NPL >= 8 ? (int)klist[r] : r;
+          const float sh = scs[q * 64 * NPL + i];
+          key[j] = ((uint64_t)desc_key(sh) << 32) | (uint32_t)i;
+          hiv[j] = __double2float_ru((double)sh + bound(sh, i));
+        }
+      }
+      bool all[NS];
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) {
-      const int i = lane + 64 * j;
-      const bool kept = i < n && (anybad || hiv[j] >= thr);
-      const uint64_t bm = __ballot(kept);
-      if (kept) klist[m + __popcll(bm & below)] = (uint16_t)i;
-      m += __popcll(bm);
+      for (int j = 0; j < NS; ++j) all[j] = true;
+      int need = kp, shift = 0, csize = 64 * NS;
+      const uint32_t res = radix_select32<NS, true>(key, all, &need, &shift, &csize);
+      uint32_t kmax = 0;
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        const uint32_t hk = (uint32_t)(key[j] >> 32);
+        if ((hk >> shift) <= (res >> shift) && key[j] != ~0ull) kmax = max(kmax, hk);
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+      const float thr = anybad ? -INFINITY : __double2float_rd((double)desc_key_value(kmax) - emax);
+      wave_sync();  // every lane has read its candidates before the kept list overwrites them
+      int m = 0;
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        const bool kept = key[j] != ~0ull && (anybad || hiv[j] >= thr);
+        const uint64_t bm = __ballot(kept);
+        if (kept) klist[m + __popcll(bm & below)] = (uint16_t)(uint32_t)key[j];
+        m += __popcll(bm);
+      }
+      return m;
+    };
+    int m;
+    if constexpr (NPL >= 8) {
+      m = mA <= 256 ? stage_b(std::integral_constant<int, 4>{}) : stage_b(std::integral_constant<int, NPL>{});
+    } else {
+      m = stage_b(std::integral_constant<int, NPL>{});
     }
     wave_sync();
     // exact scores of the kept sub-keys (the fp64 chain), then the exact top k_p among them
