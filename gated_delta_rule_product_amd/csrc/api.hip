@@ -188,6 +188,13 @@ WsLayout layout(const Dims& D, int op) {
     for (int f = 0; f < D.F; ++f) sumn += (size_t)D.widths[f];
     L.snorm = take((size_t)D.H * sumn * 4);
   }
+  if (op == SDM_OP_DECODE) {
+    const size_t nw = (size_t)D.S * D.W, nr = (size_t)D.S * D.R;
+    L.widx = take(nw * 4);
+    L.wwt = take(nw * 4);
+    L.ridx = take(nr * 4);
+    L.rwt = take(nr * 4);
+  }
   if (op == SDM_OP_WRITE_READ) {
     const size_t nw = (size_t)D.S * D.T * D.W, nr = (size_t)D.S * D.T * D.R;
     const size_t nc = (size_t)D.S * D.nch;
@@ -490,28 +497,40 @@ sdm_status sdm_decode_step(const sdm_config* cfg, const void* write_keys, const 
   if (rows == 0) return ok();
   hipStream_t st = (hipStream_t)stream;
   unsigned char* ws = (unsigned char*)workspace;
-  const TopkPlan plans[2] = {pw, pr};
-  TRY(hip_status(timed(SDM_K_CAND, st, [&] { return launch_cand_tables(plans, 2, D.F, (uint64_t*)(ws + L.cand), st); }),
-                 "candidate table launch"));
   if (!donated)
     TRY(hip_status(timed(SDM_K_COPY, st, [&] { return launch_copy(bank_in, bank_out, bank_bytes, st); }),
                    "successor copy launch"));
+  TopkArgs ta;
+  memset(&ta, 0, sizeof ta);
+  ta.queries[0] = write_keys;
+  ta.queries[1] = read_queries;
+  ta.subkeys = subkeys;
+  ta.cand[0] = (const uint64_t*)(ws + L.cand);
+  ta.cand[1] = (const uint64_t*)(ws + L.cand) + MAX_CAND;
+  ta.plan[0] = pw;
+  ta.plan[1] = pr;
+  ta.nkinds = 2;
+  ta.stream_major = 1;
+  ta.ids[0] = (int32_t*)(ws + L.widx);
+  ta.ids[1] = (int32_t*)(ws + L.ridx);
+  ta.vals[0] = (float*)(ws + L.wwt);
+  ta.vals[1] = (float*)(ws + L.rwt);
+  ta.user_ids[0] = write_idx;
+  ta.user_ids[1] = read_idx;
+  ta.snorm = (float*)(ws + L.snorm);
+  ta.one_query_per_wave = 1;
+  TRY(hip_status(timed(SDM_K_TOPK, st, [&] { return launch_topk(D, ta, st); }), "top-k launch"));
   DecodeArgs a;
-  a.wkeys = write_keys;
-  a.rq = read_queries;
   a.values = values;
   a.alpha = forget_gate;
   a.beta = input_gate;
-  a.subkeys = subkeys;
   a.bank_in = bank_in;
   a.bank_out = bank_out;
   a.out = out;
-  a.widx = write_idx;
-  a.ridx = read_idx;
-  a.cand[0] = (const uint64_t*)(ws + L.cand);
-  a.cand[1] = (const uint64_t*)(ws + L.cand) + MAX_CAND;
-  a.plan[0] = pw;
-  a.plan[1] = pr;
+  a.wid = (const int32_t*)(ws + L.widx);
+  a.wwt = (const float*)(ws + L.wwt);
+  a.rid = (const int32_t*)(ws + L.ridx);
+  a.rwt = (const float*)(ws + L.rwt);
   TRY(hip_status(timed(SDM_K_DECODE, st, [&] { return launch_decode(D, a, st); }), "decode launch"));
   return ok();
 }

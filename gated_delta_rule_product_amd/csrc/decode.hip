@@ -1,5 +1,7 @@
-// Single-token decode step: one workgroup per stream (b, h) does both exact top-k selections, the gated
-// delta-rule update of the W write rows and the read of the R read rows.
+// Single-token decode step, after the step's exact top-k (the wave-level top-k kernel, one query per wave): the
+// gated delta-rule update of the W write rows and the read of the R read rows. One workgroup per (stream, 64-byte
+// column slice); its 64 lane groups of 4 lanes hold one row slice each (16 bytes per lane), so a step spreads over
+// streams x slices workgroups.
 //
 // Successor bank (lumen PR #29, "Donating is a permission, not a demand"): bank_out == bank_in writes the successor
 // in place; a distinct bank_out first receives a copy of bank_in (launch_copy, same stream) and then the same body
@@ -7,7 +9,6 @@
 // the read takes its rows from bank_out. Both forms therefore execute identical arithmetic on identical values
 // and produce identical bits. Per-token work is O((W + R) d) as in the pages' cost model; the copy is O(N d).
 #include "sdm_internal.h"
-#include "topk_device.h"
 
 namespace sdm {
 
@@ -39,148 +40,127 @@ template <> struct DLane<bf16_t> {
   }
 };
 
-__host__ __device__ inline size_t decode_lds_bytes(const Dims& D, const TopkPlan& pw, const TopkPlan& pr, int EPL) {
-  size_t t = topk_lds_bytes(D.F, D.dk, pw);
-  const size_t t2 = topk_lds_bytes(D.F, D.dk, pr);
-  if (t2 > t) t = t2;
-  t = (t + 15) & ~(size_t)15;
-  t += (size_t)(D.W + D.R) * 8;             // ids + weights
-  t += (size_t)DECODE_NT * EPL * 4;         // partial sums
-  t += (size_t)DECODE_NT * EPL * 4;         // delta of one column pass
-  return t + 16;
+
+// Sums the 64 lane groups' partial rows in a fixed order: each wave's 16 groups in order into part4[wave], then
+// (by the caller) the 4 wave sums in order. Starts and ends with a barrier.
+template <int COLS>
+__device__ __forceinline__ void reduce_groups(float (*part)[COLS], float (*part4)[COLS]) {
+  __syncthreads();
+  const int tid = threadIdx.x;
+  if (tid < 4 * COLS) {
+    const int w = tid / COLS, c = tid % COLS;
+    float s = 0.0f;
+    for (int gg = 16 * w; gg < 16 * w + 16; ++gg) s += part[gg][c];
+    part4[w][c] = s;
+  }
+  __syncthreads();
 }
 
-template <typename A, typename Bk>
-__global__ __launch_bounds__(DECODE_NT) void decode_kernel(Dims D, DecodeArgs a) {
+// RPG = rows per lane group (W, R <= 64 RPG).
+template <typename A, typename Bk, int RPG>
+__global__ __launch_bounds__(DECODE_NT) void decode_update_kernel(Dims D, DecodeArgs a) {
   constexpr int EPL = DLane<Bk>::EPL;
-  extern __shared__ __align__(16) unsigned char lds[];
+  constexpr int COLS = 4 * EPL;
+  constexpr int NG = DECODE_NT / 4;
+  __shared__ float part[NG][COLS];
+  __shared__ float part4[DECODE_NT / 64][COLS];
+  __shared__ float sdel[COLS];
   const int tid = threadIdx.x;
-  const int st = blockIdx.x;  // stream b * H + h; with one token the [B, 1, H] row index equals st
-  const int h = st % D.H;
-  const long long row = st;
-  long long sumn = 0;
-  for (int f = 0; f < D.F; ++f) sumn += D.widths[f];
-  const A* sub = (const A*)a.subkeys + (long long)h * sumn * D.dk;
-  const int Fdk = D.F * D.dk;
-
-  size_t tb = topk_lds_bytes(D.F, D.dk, a.plan[0]);
-  const size_t tb2 = topk_lds_bytes(D.F, D.dk, a.plan[1]);
-  if (tb2 > tb) tb = tb2;
-  tb = (tb + 15) & ~(size_t)15;
-  int32_t* sWid = (int32_t*)(lds + tb);
-  float* sWw = (float*)(sWid + D.W);
-  int32_t* sRid = (int32_t*)(sWw + D.W);
-  float* sRw = (float*)(sRid + D.R);
-  float* part = (float*)(((uintptr_t)(sRw + D.R) + 15) & ~(uintptr_t)15);
-  float* sdel = part + DECODE_NT * EPL;
-
-  // 1. addressing (bank-independent)
-  {
-    TopkLds L = topk_lds_carve(lds, D.F, D.dk, a.plan[0]);
-    topk_query<A, DECODE_NT>((const A*)a.wkeys + row * Fdk, sub, D.widths, D.F, D.dk, a.plan[0], a.cand[0], L);
-    for (int r = tid; r < D.W; r += DECODE_NT) {
-      sWid[r] = L.rid[r];
-      if (a.widx) a.widx[row * D.W + r] = L.rid[r];
-    }
-    topk_softmax<DECODE_NT>(L, D.W, sWw);
-  }
-  {
-    TopkLds L = topk_lds_carve(lds, D.F, D.dk, a.plan[1]);
-    topk_query<A, DECODE_NT>((const A*)a.rq + row * Fdk, sub, D.widths, D.F, D.dk, a.plan[1], a.cand[1], L);
-    for (int r = tid; r < D.R; r += DECODE_NT) {
-      sRid[r] = L.rid[r];
-      if (a.ridx) a.ridx[row * D.R + r] = L.rid[r];
-    }
-    topk_softmax<DECODE_NT>(L, D.R, sRw);
-  }
-  const float al = to_f<A>(((const A*)a.alpha)[row]);
-  const float be = to_f<A>(((const A*)a.beta)[row]);
-  const A* v = (const A*)a.values + row * D.d;
-  A* out = (A*)a.out + row * D.d;
+  const int g = tid >> 2, q = tid & 3;
+  const int st = blockIdx.y;  // stream b * H + h; with one token the [B, 1, H] row index equals st
+  const int col0 = blockIdx.x * COLS;
+  const int col = col0 + q * EPL;
+  const bool valid = col < D.d;
   const long long rowsd = D.rows * D.ld;
   const Bk* bin = (const Bk*)a.bank_in + (long long)st * rowsd;
   Bk* bout = (Bk*)a.bank_out + (long long)st * rowsd;
+  const int32_t* wid = a.wid + (long long)st * D.W;
+  const float* wwt = a.wwt + (long long)st * D.W;
+  const int32_t* rid = a.rid + (long long)st * D.R;
+  const float* rwt = a.rwt + (long long)st * D.R;
+  const float al = to_f<A>(((const A*)a.alpha)[st]);
+  const float be = to_f<A>(((const A*)a.beta)[st]);
 
-  // 2. column passes: lanes of EPL columns; RG row groups of LPR lanes each.
-  const int nlane = D.d / EPL;
-  const int LPR = nlane < DECODE_NT ? nlane : DECODE_NT;
-  const int RG = DECODE_NT / LPR;
-  const int cl = tid % LPR, rg = tid / LPR;
-  const bool act = rg < RG;
-  for (int lane0 = 0; lane0 < nlane; lane0 += LPR) {
-    const int ln = lane0 + cl;
-    const bool on = act && ln < nlane;
-    const int col = ln * EPL;
-    // r = sum_i w_i M[S_i]
-    float acc[EPL];
+  // r = sum_i w_i M[S_i]: group g takes rows g, g + 64, ... (kept in registers for the update)
+  float m[RPG][EPL];
+  float acc[EPL];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
-    if (on) {
-      for (int i = rg; i < D.W; i += RG) {
-        float m[EPL];
-        DLane<Bk>::load(bin + (long long)sWid[i] * D.ld + col, m);
-        const float wi = sWw[i];
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] += wi * m[e];
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) part[(rg * LPR + cl) * EPL + e] = acc[e];
-    __syncthreads();
-    if (rg == 0 && on) {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        float r = 0.0f;
-        for (int g = 0; g < RG; ++g) r += part[(g * LPR + cl) * EPL + e];
-        sdel[cl * EPL + e] = be * (to_f<A>(v[col + e]) - al * r);
-      }
-    }
-    __syncthreads();
-    // M[S_i] <- alpha M[S_i] + w_i delta, rounded to the bank dtype, into the successor
-    if (on) {
-      for (int i = rg; i < D.W; i += RG) {
-        const long long o = (long long)sWid[i] * D.ld + col;
-        float m[EPL];
-        DLane<Bk>::load(bin + o, m);
-        const float wi = sWw[i];
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) m[e] = al * m[e] + wi * sdel[cl * EPL + e];
-        DLane<Bk>::store(bout + o, m);
-      }
-    }
-    __syncthreads();
-    // out = sum_i rho_i M'[R_i], read from the successor after the write
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
-    if (on) {
-      for (int i = rg; i < D.R; i += RG) {
-        float m[EPL];
-        DLane<Bk>::load(bout + (long long)sRid[i] * D.ld + col, m);
-        const float ri = sRw[i];
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] += ri * m[e];
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) part[(rg * LPR + cl) * EPL + e] = acc[e];
-    __syncthreads();
-    if (rg == 0 && on) {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        float o = 0.0f;
-        for (int g = 0; g < RG; ++g) o += part[(g * LPR + cl) * EPL + e];
-        out[col + e] = from_f<A>(o);
-      }
-    }
-    __syncthreads();
+  for (int u = 0; u < RPG; ++u) {
+    const int i = g + NG * u;
+    if (valid && i < D.W) DLane<Bk>::load(bin + (long long)wid[i] * D.ld + col, m[u]);
   }
+#pragma unroll
+  for (int u = 0; u < RPG; ++u) {
+    const int i = g + NG * u;
+    if (valid && i < D.W) {
+      const float wi = wwt[i];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] += wi * m[u][e];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) part[g][q * EPL + e] = acc[e];
+  reduce_groups<COLS>(part, part4);
+  if (tid < COLS && col0 + tid < D.d) {  // delta = beta (v - alpha r)
+    const float r = part4[0][tid] + part4[1][tid] + part4[2][tid] + part4[3][tid];
+    sdel[tid] = be * (to_f<A>(((const A*)a.values)[(long long)st * D.d + col0 + tid]) - al * r);
+  }
+  __syncthreads();
+  // M[S_i] <- alpha M[S_i] + w_i delta, rounded to the bank dtype, into the successor
+#pragma unroll
+  for (int u = 0; u < RPG; ++u) {
+    const int i = g + NG * u;
+    if (valid && i < D.W) {
+      const float wi = wwt[i];
+      float y[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) y[e] = al * m[u][e] + wi * sdel[q * EPL + e];
+      DLane<Bk>::store(bout + (long long)wid[i] * D.ld + col, y);
+    }
+  }
+  __syncthreads();  // the updated rows are visible to the read below
+  // out = sum_i rho_i M'[R_i], read from the successor after the write
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
+#pragma unroll
+  for (int u = 0; u < RPG; ++u) {
+    const int i = g + NG * u;
+    if (valid && i < D.R) DLane<Bk>::load(bout + (long long)rid[i] * D.ld + col, m[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < RPG; ++u) {
+    const int i = g + NG * u;
+    if (valid && i < D.R) {
+      const float ri = rwt[i];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] += ri * m[u][e];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) part[g][q * EPL + e] = acc[e];
+  reduce_groups<COLS>(part, part4);
+  if (tid < COLS && col0 + tid < D.d) {
+    const float o = part4[0][tid] + part4[1][tid] + part4[2][tid] + part4[3][tid];
+    ((A*)a.out)[(long long)st * D.d + col0 + tid] = from_f<A>(o);
+  }
+}
+
+template <typename A, typename Bk, int RPG>
+static void launch_decode_r(const Dims& D, const DecodeArgs& a, hipStream_t st) {
+  constexpr int COLS = 4 * DLane<Bk>::EPL;
+  dim3 grid((unsigned)((D.d + COLS - 1) / COLS), (unsigned)D.S);
+  hipLaunchKernelGGL((decode_update_kernel<A, Bk, RPG>), grid, dim3(DECODE_NT), 0, st, D, a);
 }
 
 template <typename A, typename Bk>
 static hipError_t launch_decode_t(const Dims& D, const DecodeArgs& a, hipStream_t st) {
-  const size_t lds = decode_lds_bytes(D, a.plan[0], a.plan[1], DLane<Bk>::EPL);
-  (void)hipFuncSetAttribute((const void*)decode_kernel<A, Bk>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  hipLaunchKernelGGL((decode_kernel<A, Bk>), dim3((unsigned)D.S), dim3(DECODE_NT), lds, st, D, a);
+  const int rows = D.W > D.R ? D.W : D.R;  // <= MAX_K = 512
+  if (rows <= 64) launch_decode_r<A, Bk, 1>(D, a, st);
+  else if (rows <= 128) launch_decode_r<A, Bk, 2>(D, a, st);
+  else if (rows <= 256) launch_decode_r<A, Bk, 4>(D, a, st);
+  else launch_decode_r<A, Bk, 8>(D, a, st);
   return hipGetLastError();
 }
 

@@ -222,6 +222,7 @@ struct TopkArgs {
   float* vals[2];        // stream-major weights (softmax) or user scores (may be NULL)
   int32_t* user_ids[2];  // optional user ids [B,T,H,k] in stream-major mode
   float* snorm;          // workspace [H][sum n_f]: sub-key norms for the filtered (MFMA) scoring, or NULL
+  int one_query_per_wave;  // few rows (a decode step): one query per wave
 };
 hipError_t launch_topk(const Dims& D, const TopkArgs& a, hipStream_t st);
 
@@ -245,10 +246,10 @@ hipError_t launch_loop(const Dims& D, const LoopArgs& a, hipStream_t st);
 bool loop_held_path(const Dims& D);
 
 struct DecodeArgs {
-  const void* wkeys; const void* rq; const void* values; const void* alpha; const void* beta; const void* subkeys;
-  const void* bank_in; void* bank_out; void* out; int32_t* widx; int32_t* ridx;
-  const uint64_t* cand[2];
-  TopkPlan plan[2];
+  const void* values; const void* alpha; const void* beta;
+  const void* bank_in; void* bank_out; void* out;
+  const int32_t* wid; const float* wwt;  // [S][W] write slots and weights (top-k of the step)
+  const int32_t* rid; const float* rwt;  // [S][R] read slots and weights
 };
 hipError_t launch_decode(const Dims& D, const DecodeArgs& a, hipStream_t st);
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t st);

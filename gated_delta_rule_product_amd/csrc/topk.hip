@@ -331,9 +331,10 @@ __device__ void factor_topk_filtered(const Dims& D, const TopkArgs& a, int f, in
   }
 }
 
-template <typename A, int NPL, int CPL, bool MF>
+// QW1: one query per wave (few rows, e.g. a decode step: parallelism over queries rather than reuse of sub-key rows).
+template <typename A, int NPL, int CPL, bool MF, bool QW1>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NPL <= 4 ? 4 : 1))) void topk2_kernel(Dims D, TopkArgs a) {
-  constexpr int QW = WaveTile<NPL>::QW;
+  constexpr int QW = QW1 ? 1 : WaveTile<NPL>::QW;
   constexpr int VEC = Vec16<A>::N;
   extern __shared__ __align__(16) unsigned char lds[];
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -343,6 +344,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NPL <= 4 ? 
   const int F = D.F, dk = D.dk, k = P.k, kpmax = P.kpmax;
   const long long BT = (long long)D.B * D.T;
   const long long bt0 = ((long long)blockIdx.x * 4 + wv) * QW;
+  const uint64_t* cand = a.cand[kind];
+  if constexpr (QW1) {  // few rows: the block builds its kind's candidate table itself (no separate launch)
+    uint64_t* ctab = (uint64_t*)(lds + 4 * topk2_wave_lds(F, kpmax, k, QW, NPL));
+    build_cand_table<256>(P, F, ctab, (int*)(ctab + P.ncand));
+    cand = ctab;
+  }
   if (bt0 >= BT) return;  // no block-wide barriers below: idle waves may leave
   const int KS = kpmax > k ? kpmax : k;
   unsigned char* wl = lds + (size_t)wv * topk2_wave_lds(F, kpmax, k, QW, NPL);
@@ -419,7 +426,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NPL <= 4 ? 
     off += n;
   }
 
-  const uint64_t* cand = a.cand[kind];
   for (int q = 0; q < nq; ++q) {
     uint64_t ck[CPL];
 #pragma unroll
@@ -478,28 +484,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NPL <= 4 ? 
   }
 }
 
-template <typename A, int NPL, int CPL, bool MF>
+template <typename A, int NPL, int CPL, bool MF, bool QW1>
 static void launch_topk2_k(dim3 grid, size_t lds, hipStream_t st, const Dims& D, const TopkArgs& a) {
-  (void)hipFuncSetAttribute((const void*)topk2_kernel<A, NPL, CPL, MF>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)lds);
-  hipLaunchKernelGGL((topk2_kernel<A, NPL, CPL, MF>), grid, dim3(256), lds, st, D, a);
+  (void)hipFuncSetAttribute((const void*)topk2_kernel<A, NPL, CPL, MF, QW1>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipLaunchKernelGGL((topk2_kernel<A, NPL, CPL, MF, QW1>), grid, dim3(256), lds, st, D, a);
 }
 
 template <typename A, int NPL>
 static bool launch_topk2_npl(const Dims& D, const TopkArgs& a, hipStream_t st, int cpl, size_t lds, bool mf) {
-  constexpr int QW = WaveTile<NPL>::QW;
+  const int QW = a.one_query_per_wave ? 1 : WaveTile<NPL>::QW;
   const long long BT = (long long)D.B * D.T;
   const long long tiles = (BT + QW - 1) / QW;
   dim3 grid((unsigned)((tiles + 3) / 4), (unsigned)a.nkinds, (unsigned)D.H);
+  if (a.one_query_per_wave) {
+    if (cpl == 8) launch_topk2_k<A, NPL, 8, false, true>(grid, lds, st, D, a);
+    else launch_topk2_k<A, NPL, 16, false, true>(grid, lds, st, D, a);
+    return true;
+  }
   if constexpr (sizeof(A) == 2) {
     if (mf) {
-      if (cpl == 8) launch_topk2_k<A, NPL, 8, true>(grid, lds, st, D, a);
-      else launch_topk2_k<A, NPL, 16, true>(grid, lds, st, D, a);
+      if (cpl == 8) launch_topk2_k<A, NPL, 8, true, false>(grid, lds, st, D, a);
+      else launch_topk2_k<A, NPL, 16, true, false>(grid, lds, st, D, a);
       return true;
     }
   }
-  if (cpl == 8) launch_topk2_k<A, NPL, 8, false>(grid, lds, st, D, a);
-  else launch_topk2_k<A, NPL, 16, false>(grid, lds, st, D, a);
+  if (cpl == 8) launch_topk2_k<A, NPL, 8, false, false>(grid, lds, st, D, a);
+  else launch_topk2_k<A, NPL, 16, false, false>(grid, lds, st, D, a);
   return true;
 }
 
@@ -540,14 +551,15 @@ static bool launch_topk2(const Dims& D, const TopkArgs& a, hipStream_t st) {
   if (ncand > 1024 || kpmax > 1024) return false;
   if ((D.dk * (int)sizeof(A)) % 16 != 0 || ((uintptr_t)a.subkeys) % 16 != 0) return false;
   const int cpl = ncand <= 512 ? 8 : 16;
-  const int QW = wave_qw(npl);
+  const int QW = a.one_query_per_wave ? 1 : wave_qw(npl);
   size_t lds = 0;
   for (int q = 0; q < a.nkinds; ++q) {
-    const size_t l = 4 * topk2_wave_lds(D.F, a.plan[q].kpmax, a.plan[q].k, QW, npl);
+    size_t l = 4 * topk2_wave_lds(D.F, a.plan[q].kpmax, a.plan[q].k, QW, npl);
+    if (a.one_query_per_wave) l += (size_t)a.plan[q].ncand * 8 + (size_t)(a.plan[q].kp[0] + 1) * 4;
     lds = l > lds ? l : lds;
   }
   if (lds > 128 * 1024) return false;
-  const bool mf = topk_filtered(D, a);
+  const bool mf = !a.one_query_per_wave && topk_filtered(D, a);
   if (mf) {
     int sumn = 0;
     for (int f = 0; f < D.F; ++f) sumn += D.widths[f];
@@ -568,6 +580,10 @@ hipError_t launch_topk(const Dims& D, const TopkArgs& a, hipStream_t st) {
   if (rows == 0) return hipSuccess;
   const bool done = D.act == SDM_BF16 ? launch_topk2<bf16_t>(D, a, st) : launch_topk2<float>(D, a, st);
   if (done) return hipGetLastError();
+  if (a.one_query_per_wave) {  // the block-level kernel reads the candidate tables from the workspace
+    const hipError_t e = launch_cand_tables(a.plan, a.nkinds, D.F, (uint64_t*)a.cand[0], st);
+    if (e != hipSuccess) return e;
+  }
   size_t lds = 0;
   for (int q = 0; q < a.nkinds; ++q) {
     size_t l = topk_lds_bytes(D.F, D.dk, a.plan[q]);
