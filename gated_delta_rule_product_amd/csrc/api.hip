@@ -437,7 +437,8 @@ sdm_status sdm_write_read(const sdm_config* cfg, const void* write_keys, const v
   pa.beta = input_gate;
   pa.chunks = ws + L.chunks;
   pa.counts = (ChunkCounts*)(ws + L.counts);
-  pa.scat = loop_held_path(D) ? 0 : 1;
+  pa.scat = loop_held_path(D) || loop_narrow_path(D) ? 0 : 1;
+  pa.lanemajor = !loop_held_path(D) && loop_narrow_lanemajor(D) ? 1 : 0;
   TRY(hip_status(timed(SDM_K_PLAN, st, [&] { return launch_plan(D, pa, st); }), "chunk plan launch"));
   LoopArgs la;
   la.alpha = forget_gate;

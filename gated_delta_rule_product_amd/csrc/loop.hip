@@ -616,6 +616,482 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
   }
 }
 
+// ------------------------------------------------------------------------------------------- narrow variant
+// One lane per 16-byte row piece and one workgroup per (stream, 16-byte column slice): four times the workgroups
+// of the 64-byte slices, for streams whose rows are short (bf16 banks, small head_dim) or whose chunk gives a
+// 64-byte lane group more terms than it can hold. The gpt = 512 / C consecutive lanes of a token split its W write
+// and R read terms (at most 16 of each per lane). A lane keeps its own terms in registers (they are not shared
+// with other lanes): the next chunk's read terms are loaded during the delta phase; a chunk's write terms and read
+// rows are issued first, then a sliding window turns each consumed read row's registers into a held write row. H and G are
+// summed over the parts of a token in order by lane shuffles, the token's first lane computes U, delta and the
+// output piece, and the lane holding a slot's last event of the chunk applies the slot's events and stores it.
+constexpr int NARROW_HOLD = 16;
+constexpr int NARROW_NST = 8;                // 16-byte words of row pointers, lists and multi-event table per thread
+constexpr int NARROW_STAGE_LDS = NARROW_NST * LOOP_NT * 16;  // their LDS area, filled by direct global-to-LDS loads
+constexpr int NARROW_MROWS = 1024;           // held rows of multi-event slots kept in LDS (16 bytes each)
+
+__host__ __device__ inline long long narrow_small_bytes(int C, int epl) {
+  return align16((long long)2 * C * epl * 4 + (long long)C * 4);
+}
+
+// LDS: U and delta [C][epl], gates [C]; T/Q row pointers, lists and the multi-event table (one contiguous area);
+// held rows of slots written more than once.
+__host__ __device__ inline size_t loop_narrow_lds_bytes(int C, int epl) {
+  return (size_t)(narrow_small_bytes(C, epl) + NARROW_STAGE_LDS + NARROW_MROWS * 16);
+}
+
+// EPL activation elements (4 or 8) as floats / from floats.
+template <typename A, int EPL>
+__device__ __forceinline__ void act_load(const A* p, float (&v)[EPL]) {
+  static_for<EPL / 4>([&](auto k) {
+    float t[4];
+    Act4<A>::load(p + 4 * k, t);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[4 * k + e] = t[e];
+  });
+}
+template <typename A, int EPL>
+__device__ __forceinline__ void act_store(A* p, const float (&v)[EPL]) {
+  static_for<EPL / 4>([&](auto k) {
+    float t[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) t[e] = v[4 * k + e];
+    Act4<A>::store(p + 4 * k, t);
+  });
+}
+
+// Word 3 of a raw buffer resource on gfx9 (32-bit data format, no swizzle, offsets in bytes).
+constexpr int BUF_RSRC_WORD3 = 0x00020000;
+// A byte offset past every buffer range used here (ranges are kept below it): an access there is dropped by the
+// hardware range check (a store writes nothing), also with 16 or 32 bytes added.
+constexpr uint32_t BUF_OOB = 0xFFFFFF00u;
+
+// EPL activation elements of a row as raw words (one 16- or 32-byte load), converted to floats later.
+template <typename A, int EPL>
+struct ActRaw {
+  static constexpr int NW = (EPL * (int)sizeof(A) + 15) / 16;
+  static_assert(EPL * sizeof(A) == 16 || EPL * sizeof(A) == 32 || EPL * sizeof(A) == 8, "row piece of 8, 16 or 32 bytes");
+  w16_t w[NW];
+  __device__ __forceinline__ void load(const A* p) {
+    if constexpr (EPL * sizeof(A) == 8) {
+      const uint2 x = *(const uint2*)p;
+      w[0] = w16_t{x.x, x.y, 0u, 0u};
+    } else {
+#pragma unroll
+      for (int i = 0; i < NW; ++i) w[i] = ((const w16_t*)p)[i];
+    }
+  }
+  __device__ __forceinline__ void pack(const float (&v)[EPL]) {
+    if constexpr (sizeof(A) == 4) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) w[e / 4][e % 4] = __float_as_uint(v[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; e += 2)
+        w[e / 8][(e % 8) / 2] = (uint32_t)f_to_bf16(v[e]) | ((uint32_t)f_to_bf16(v[e + 1]) << 16);
+    }
+  }
+  // buffer store of the words at byte offset off (one 8-, 16- or two 16-byte stores)
+  __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t off) const {
+    if constexpr (EPL * sizeof(A) == 8) {
+      __builtin_amdgcn_raw_buffer_store_b64((unsigned int __attribute__((ext_vector_type(2)))){w[0].x, w[0].y}, r,
+                                            (int)off, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NW; ++i) __builtin_amdgcn_raw_buffer_store_b128(w[i], r, (int)(off + 16 * i), 0, 0);
+    }
+  }
+  __device__ __forceinline__ void unpack(float (&v)[EPL]) const {
+    if constexpr (sizeof(A) == 4) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) v[e] = __uint_as_float(w[e / 4][e % 4]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const uint32_t x = w[e / 8][(e % 8) / 2];
+        v[e] = __uint_as_float((e & 1) ? (x & 0xFFFF0000u) : (x << 16));
+      }
+    }
+  }
+};
+
+// A lane's gather terms of one chunk: NARROW_HOLD (slot, coefficient) pairs, and for write terms their int16
+// last-event codes. FULL: exactly NARROW_HOLD terms, stored lane-major (term_pos, code_pos): word k of the lane is
+// word k * 512 + lane of the section, one coalesced load; pp and cp are the sections. Otherwise pp and cp point at
+// the lane's first term (token-major) and n terms are loaded one by one, the rest repeating the last.
+struct NarrowTerms {
+  w16_t p[NARROW_HOLD / 2];  // pairs (slot, coef bits) two per word
+  w16_t c[2];                // int16 codes, eight per word (write terms only)
+};
+template <bool FULL, bool CODES>
+__device__ __forceinline__ void narrow_load_terms(NarrowTerms& t, const Pair* pp, const int16_t* cp, int n) {
+  if (FULL) {
+    static_for<NARROW_HOLD / 2>([&](auto k) { t.p[k] = ((const w16_t*)pp)[k * LOOP_NT + threadIdx.x]; });
+    if (CODES) static_for<2>([&](auto k) { t.c[k] = ((const w16_t*)cp)[k * LOOP_NT + threadIdx.x]; });
+  } else {
+    static_for<NARROW_HOLD / 2>([&](auto k) {
+      const uint2 a = *(const uint2*)(pp + min(2 * (int)k, n - 1));
+      const uint2 b = *(const uint2*)(pp + min(2 * (int)k + 1, n - 1));
+      t.p[k] = w16_t{a.x, a.y, b.x, b.y};
+    });
+    if (CODES)
+      static_for<2>([&](auto k) {
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t lo = (uint16_t)cp[min(8 * (int)k + 2 * j, n - 1)];
+          const uint32_t hi = (uint16_t)cp[min(8 * (int)k + 2 * j + 1, n - 1)];
+          w[j] = lo | (hi << 16);
+        }
+        t.c[k] = w16_t{w[0], w[1], w[2], w[3]};
+      });
+  }
+}
+template <int U> __device__ __forceinline__ uint32_t term_slot(const NarrowTerms& t) { return t.p[U / 2][(U & 1) * 2]; }
+template <int U> __device__ __forceinline__ float term_coef(const NarrowTerms& t) {
+  return __uint_as_float(t.p[U / 2][(U & 1) * 2 + 1]);
+}
+template <int U> __device__ __forceinline__ int term_code(const NarrowTerms& t) {
+  return (int)(int16_t)(uint16_t)(t.c[U / 8][(U & 7) / 2] >> (16 * (U & 1)));
+}
+
+// A 16-byte row piece held as a native vector, as floats.
+template <typename Bk> __device__ __forceinline__ void unpack_w(const w16_t& x, float* v);
+template <> __device__ __forceinline__ void unpack_w<float>(const w16_t& x, float* v) {
+  v[0] = __uint_as_float(x.x); v[1] = __uint_as_float(x.y); v[2] = __uint_as_float(x.z); v[3] = __uint_as_float(x.w);
+}
+template <> __device__ __forceinline__ void unpack_w<bf16_t>(const w16_t& x, float* v) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(x[i] << 16);
+    v[2 * i + 1] = __uint_as_float(x[i] & 0xFFFF0000u);
+  }
+}
+
+template <typename Bk> __device__ __forceinline__ w16_t pack_w(const float* v);
+template <> __device__ __forceinline__ w16_t pack_w<float>(const float* v) {
+  return w16_t{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+}
+template <> __device__ __forceinline__ w16_t pack_w<bf16_t>(const float* v) {
+  w16_t x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = (uint32_t)f_to_bf16(v[2 * i]) | ((uint32_t)f_to_bf16(v[2 * i + 1]) << 16);
+  return x;
+}
+
+
+template <typename A, typename Bk, bool FULL>
+__global__ __launch_bounds__(LOOP_NT) void loop_narrow_kernel(Dims D, LoopArgs a, int nslices) {
+  constexpr int EPL = Lane<Bk>::EPL;
+  constexpr int HOLD = NARROW_HOLD;
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int C = D.C, W = D.W, R = D.R;
+  const int lg = __builtin_ctz(LOOP_NT / C);  // log2 of gpt
+  const int gpt = 1 << lg;
+  const int tpw = W >> lg, tpr = R >> lg;
+  float* sU = (float*)lds;   // [C][EPL]
+  float* sD = sU + C * EPL;  // [C][EPL]
+  float* sA = sD + C * EPL;  // [C]
+  const ChunkLayout CL = chunk_layout(C, W, R);
+  unsigned char* sLst = lds + narrow_small_bytes(C, EPL);  // T/Q row pointers, lists, then the multi-event table
+  const long long ptrs_b = align16((long long)2 * (C + 1) * 4);
+  w16_t* sM = (w16_t*)(sLst + NARROW_STAGE_LDS);           // held rows of multi-event slots
+  const int32_t* tptr = (const int32_t*)sLst;
+  const int32_t* qptr = tptr + (C + 1);
+
+  const int nblk = gridDim.x;
+  int w = blockIdx.x;
+  if ((nblk & 7) == 0) w = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+  const int st = w / nslices, slice = w % nslices;
+  const int b = st / D.H, h = st % D.H;
+  const int tid = threadIdx.x;
+  const int gt = tid >> lg, part = tid & (gpt - 1);  // token and part of this lane
+  const int mycol = slice * EPL;
+  const bool valid = mycol < D.d;
+  // the stream's bank as a buffer resource: 32-bit byte offsets (the path requires < 4 GiB per stream), and any
+  // access beyond the stream's rows is dropped by the hardware range check
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)((Bk*)a.bank + (long long)st * D.rows * D.ld), (short)0,
+      (int)(uint32_t)((unsigned long long)D.rows * D.ld * sizeof(Bk)), BUF_RSRC_WORD3);
+  const uint32_t ldb = (uint32_t)(D.ld * sizeof(Bk));
+  const uint32_t colb = (uint32_t)(mycol * sizeof(Bk));
+  const A* alpha = (const A*)a.alpha;
+  const A* beta = (const A*)a.beta;
+  const A* values = (const A*)a.values;
+  A* out = (A*)a.out;
+  const long long woff = FULL ? 0 : (long long)gt * W + part * tpw;  // this lane's first write term (token-major)
+  const long long roff = FULL ? 0 : (long long)gt * R + part * tpr;
+
+  NarrowTerms rt;
+  {
+    const unsigned char* g0 = a.chunks + (long long)st * D.nch * CL.bytes;
+    narrow_load_terms<FULL, false>(rt, (const Pair*)(g0 + CL.rpairs) + roff, nullptr, tpr);
+#pragma unroll
+    for (int i = 0; i < NARROW_HOLD / 2; ++i) asm volatile("" : "+v"(rt.p[i]));  // arrived before the loop
+  }
+
+  ChunkCounts cnt = a.counts[(long long)st * D.nch];
+  for (int ch = 0; ch < D.nch; ++ch) {
+    const int t0 = ch * C;
+    const int Cc = min(C, D.T - t0);
+    const long long cidx = (long long)st * D.nch + ch;
+    const unsigned char* greg = a.chunks + cidx * CL.bytes;
+    const bool more = ch + 1 < D.nch;
+    const ChunkCounts next = a.counts[more ? cidx + 1 : cidx];
+    const bool act = valid && gt < Cc;
+    const bool lead = part == 0 && act;
+    const uint32_t amask = act ? ~0u : 0u;
+
+    // 1) write terms (needed from the first window step on), then the read rows, all in flight
+    NarrowTerms wt;
+    narrow_load_terms<FULL, true>(wt, (const Pair*)greg + woff, (const int16_t*)(greg + CL.wlast) + woff, tpw);
+    w16_t row[HOLD];
+    static_for<HOLD>([&](auto u) {
+      const uint32_t m = amask & ((FULL || u < tpr) ? ~0u : 0u);
+      row[u] = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)((term_slot<decltype(u)::value>(rt) & m) * ldb + (colb & m)), 0, 0);
+    });
+    // 2) window: read row u into G, then held write row u into its registers
+    float gacc[EPL], hacc[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) gacc[e] = hacc[e] = 0.0f;
+    static_for<HOLD>([&](auto u) {
+      if (FULL || (act && u < tpr)) {
+        const float cf = term_coef<decltype(u)::value>(rt);
+        float v[EPL];
+        unpack_w<Bk>(row[u], v);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) gacc[e] += cf * v[e];
+      }
+      // pin G here: the read row's registers are free before the held row is loaded into them
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) asm volatile("" : "+v"(gacc[e]));
+      const uint32_t m = amask & ((FULL || u < tpw) ? ~0u : 0u);
+      row[u] = __builtin_amdgcn_raw_buffer_load_b128(rb, (int)((term_slot<decltype(u)::value>(wt) & m) * ldb + (colb & m)), 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    // 3) behind the held rows: gates and the value piece of the token (its first lane), loaded by every lane without
+    //    a branch and converted only after H, so that no wait for them is placed ahead of the held rows
+    const long long grow = ((long long)b * D.T + t0 + min(gt, Cc - 1)) * D.H + h;
+    const A raw_a = alpha[grow], raw_b = beta[grow];
+    ActRaw<A, EPL> raw_v;
+    raw_v.load(values + grow * D.d + mycol);
+    const A raw_sa = alpha[((long long)b * D.T + t0 + min(tid, Cc - 1)) * D.H + h];
+    // 4) this chunk's row pointers, lists and multi-event table into LDS by direct loads, issued behind the held
+    //    rows: a direct load still in flight makes the compiler wait for every load before the next use of a
+    //    loaded register, which here is H's first held row, which the direct loads follow. Word i of the area:
+    //    row pointers and lists for i < n1, then the multi-event table. Each wave fills 64 consecutive words per
+    //    step (the LDS address of a step is uniform over the wave); lanes past n12 repeat the last word inside the
+    //    area.
+    const long long lbytes = (long long)(cnt.nnzT + cnt.nnzQ) * 8;
+    const bool llds = ptrs_b + lbytes <= NARROW_STAGE_LDS;
+    const int n1 = (int)((ptrs_b + (llds ? lbytes : 0) + 15) >> 4);
+    const long long mbytes = (long long)cnt.nmseg * 16 + (long long)cnt.nmev * 8;
+    const bool mlds = (long long)n1 * 16 + mbytes <= NARROW_STAGE_LDS;
+    const int n12 = n1 + (mlds ? (int)((mbytes + 15) >> 4) : 0);  // <= NARROW_NST * LOOP_NT
+    {
+      const w16_t* src1 = (const w16_t*)(greg + CL.ptrs);
+      const w16_t* src2 = (const w16_t*)(greg + CL.multi) - n1;
+      const int wbase = tid & ~63;
+#pragma unroll
+      for (int k = 0; k < NARROW_NST; ++k) {
+        const int i = min(tid + k * LOOP_NT, n12 - 1);  // n12 >= 1: the row pointers are never empty
+        const w16_t* src = i < n1 ? src1 + i : src2 + i;
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                         (__attribute__((address_space(3))) void*)(sLst + (k * LOOP_NT + wbase) * 16),
+                                         16, 0, 0);
+      }
+    }
+    // 5) H from the held rows; the parts of a token summed by a fixed shuffle tree
+    static_for<HOLD>([&](auto u) {
+      if (FULL || (act && u < tpw)) {
+        const float cf = term_coef<decltype(u)::value>(wt);
+        float v[EPL];
+        unpack_w<Bk>(row[u], v);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) hacc[e] += cf * v[e];
+      }
+      // keep the row packed until the scatter (its unpacked values are not carried over)
+      asm volatile("" : "+v"(row[u]));
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    for (int o = gpt >> 1; o > 0; o >>= 1) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        hacc[e] += __shfl_down(hacc[e], o, 64);
+        gacc[e] += __shfl_down(gacc[e], o, 64);
+      }
+    }
+    // 6) U = beta v - alpha beta H
+    if (lead) {
+      const float ga = to_f<A>(raw_a), gb = to_f<A>(raw_b);
+      float va[EPL];
+      raw_v.unpack(va);
+      float u4[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) u4[e] = gb * va[e] - ga * gb * hacc[e];
+      static_for<EPL / 4>([&](auto k) {
+        *(float4*)(sU + gt * EPL + 4 * k) = make_float4(u4[4 * k], u4[4 * k + 1], u4[4 * k + 2], u4[4 * k + 3]);
+      });
+    }
+    if (tid < Cc) sA[tid] = to_f<A>(raw_sa);
+    __syncthreads();  // U, gates, lists and the multi-event table in LDS (the barrier waits for the direct loads)
+    // next chunk's read terms (last chunk: this chunk's again, never used)
+    NarrowTerms rn;
+    {
+      const unsigned char* gn = more ? greg + CL.bytes : greg;
+      narrow_load_terms<FULL, false>(rn, (const Pair*)(gn + CL.rpairs) + roff, nullptr, tpr);
+    }
+    // lists and the multi-event table are read through typed pointers (LDS, or the plan region when they did not
+    // fit): a pointer that may be either would compile to flat loads, whose waits also cover every global load
+    const Ent* lists_l = (const Ent*)(sLst + ptrs_b);
+    const Ent* lists_g = (const Ent*)(greg + CL.lists);
+    // 7) delta = T U: the gpt lanes of a token take every gpt-th entry of its row, then a fixed shuffle tree
+    {
+      float d[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) d[e] = 0.0f;
+      auto trow = [&](const Ent* lists) {
+        const int e1 = tptr[gt + 1];
+        for (int e = tptr[gt] + part; e < e1; e += gpt) {
+          const Ent x = lists[e];
+          static_for<EPL / 4>([&](auto k) {
+            const float4 u = *(const float4*)(sU + x.col * EPL + 4 * k);
+            d[4 * k] += x.val * u.x; d[4 * k + 1] += x.val * u.y; d[4 * k + 2] += x.val * u.z; d[4 * k + 3] += x.val * u.w;
+          });
+        }
+      };
+      if (act) {
+        if (llds) trow(lists_l); else trow(lists_g);
+      }
+      for (int o = gpt >> 1; o > 0; o >>= 1) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) d[e] += __shfl_down(d[e], o, 64);
+      }
+      if (lead)
+        static_for<EPL / 4>([&](auto k) {
+          *(float4*)(sD + gt * EPL + 4 * k) = make_float4(d[4 * k], d[4 * k + 1], d[4 * k + 2], d[4 * k + 3]);
+        });
+    }
+    // the next read terms have arrived by now (they were issued before the delta products): taking them here, ahead
+    // of the stores, lets the next chunk start its row loads without waiting for this chunk's stores
+#pragma unroll
+    for (int i = 0; i < NARROW_HOLD / 2; ++i) asm volatile("" : "+v"(rn.p[i]));
+    __syncthreads();  // delta in LDS
+    // 8) scatter: a slot's only event is applied by its holder; the held rows of slots written more than once go to
+    //    LDS (when they fit) and are finished below, one slot per thread. Every lane issues the same number of
+    //    stores: a store that must not happen goes to an offset past the buffer's range, which the hardware drops
+    //    (so the compiler can count the loads and stores in flight exactly and never has to wait for all of them).
+    const bool mrows = cnt.nmseg <= NARROW_MROWS;
+    const MSeg* msegs_lds = (const MSeg*)(sLst + (long long)n1 * 16);
+    const MSeg* msegs_g = (const MSeg*)(greg + CL.multi);
+    {
+      float dg[EPL];
+#pragma unroll
+      for (int k = 0; k < EPL; ++k) dg[k] = sD[gt * EPL + k];
+      const float ag = sA[gt];
+      static_for<HOLD>([&](auto u) {
+        constexpr int U = decltype(u)::value;
+        const bool has = act && (FULL || U < tpw);
+        const int code = has ? term_code<U>(wt) : -1;
+        float m[EPL];
+        unpack_w<Bk>(row[u], m);
+        if (code >= 0 && !mrows) {  // rare (many multi-event slots): events read from the plan region
+          const MSeg sg = msegs_g[code];
+          const Ev* mev = (const Ev*)(msegs_g + cnt.nmseg);
+          for (int e = sg.beg; e < sg.end; ++e) {
+            const Ev x = mev[e];
+            const float al = sA[x.tok];
+#pragma unroll
+            for (int k = 0; k < EPL; ++k) m[k] = al * m[k] + x.w * sD[x.tok * EPL + k];
+          }
+        } else {  // own token, own weight (used when the slot's only event is this one)
+          const float wgt = term_coef<U>(wt);
+#pragma unroll
+          for (int k = 0; k < EPL; ++k) m[k] = ag * m[k] + wgt * dg[k];
+          if (code >= 0) sM[code] = row[u];
+        }
+        const bool st = code == -2 || (code >= 0 && !mrows);
+        const uint32_t off = st ? term_slot<U>(wt) * ldb + colb : BUF_OOB;
+        __builtin_amdgcn_raw_buffer_store_b128(pack_w<Bk>(m), rb, (int)off, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    }
+    // 9) read output: out = G + Q delta (every lane stores; only a token's first lane inside the range)
+    {
+      float o[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[e] = gacc[e];
+      auto qrow = [&](const Ent* lists) {
+        for (int e = qptr[gt]; e < qptr[gt + 1]; ++e) {
+          const Ent x = lists[e];
+          static_for<EPL / 4>([&](auto k) {
+            const float4 dd = *(const float4*)(sD + x.col * EPL + 4 * k);
+            o[4 * k] += x.val * dd.x; o[4 * k + 1] += x.val * dd.y; o[4 * k + 2] += x.val * dd.z; o[4 * k + 3] += x.val * dd.w;
+          });
+        }
+      };
+      if (lead) {
+        if (llds) qrow(lists_l); else qrow(lists_g);
+      }
+      // rows of this chunk and head: token t at byte (t H d + mycol) * sizeof(A) from the chunk's first row
+      const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(out + (((long long)b * D.T + t0) * D.H + h) * D.d), (short)0,
+          (int)(uint32_t)((unsigned long long)Cc * D.H * D.d * sizeof(A)), BUF_RSRC_WORD3);
+      const uint32_t oo = lead ? (uint32_t)(((long long)gt * D.H * D.d + mycol) * sizeof(A)) : BUF_OOB;
+      ActRaw<A, EPL> ov;
+      ov.pack(o);
+      ov.store(ro, oo);
+    }
+    // 10) slots written more than once: events in token order on the held row, one store (a fixed number of
+    //     iterations per thread; the rows past nmseg are not stored)
+    if (mrows && valid) {
+      __syncthreads();  // held rows in LDS
+      auto finish = [&](const MSeg* msegs) {
+        const Ev* mev = (const Ev*)(msegs + cnt.nmseg);
+#pragma unroll
+        for (int r = 0; r < NARROW_MROWS / LOOP_NT; ++r) {
+          const int i = tid + r * LOOP_NT;
+          const bool in = i < cnt.nmseg;
+          const MSeg sg = msegs[in ? i : 0];
+          float m[EPL];
+          unpack_w<Bk>(sM[i], m);
+          const int e1 = in ? sg.end : sg.beg;
+          for (int e = sg.beg; e < e1; ++e) {
+            const Ev x = mev[e];
+            const float al = sA[x.tok];
+#pragma unroll
+            for (int k = 0; k < EPL; ++k) m[k] = al * m[k] + x.w * sD[x.tok * EPL + k];
+          }
+          const uint32_t off = in ? (uint32_t)sg.slot * ldb + colb : BUF_OOB;
+          __builtin_amdgcn_raw_buffer_store_b128(pack_w<Bk>(m), rb, (int)off, 0, 0);
+        }
+      };
+      if (mlds) finish(msegs_lds); else finish(msegs_g);
+    }
+    rt = rn;
+    cnt = next;
+    __syncthreads();
+  }
+}
+
+// The narrow variant: chunk a power of two in [8, 128], every token's terms split evenly over gpt = 512 / C lanes
+// with at most 16 of each kind per lane.
+bool loop_narrow_path(const Dims& D) {
+  const bool pow2 = (D.C & (D.C - 1)) == 0;
+  if (!pow2 || D.C < 8 || D.C > 128) return false;
+  const int gpt = LOOP_NT / D.C;
+  const int epl = D.bank == SDM_BF16 ? 8 : 4;
+  const unsigned long long bytes = (unsigned long long)D.rows * D.ld * (D.bank == SDM_BF16 ? 2 : 4);
+  const unsigned long long obytes = (unsigned long long)D.C * D.H * D.d * (D.act == SDM_BF16 ? 2 : 4);
+  return bytes < BUF_OOB && obytes < BUF_OOB && D.d % epl == 0 && D.W % gpt == 0 && D.R % gpt == 0 && D.W >= gpt && D.R >= gpt &&
+         D.W / gpt <= NARROW_HOLD && D.R / gpt <= NARROW_HOLD && loop_narrow_lds_bytes(D.C, epl) <= 160 * 1024;
+}
+
+bool loop_narrow_lanemajor(const Dims& D) {
+  const int gpt = LOOP_NT / D.C;
+  return loop_narrow_path(D) && D.W == NARROW_HOLD * gpt && D.R == NARROW_HOLD * gpt;
+}
+
 // The held-row variant serves float32 banks whose chunk fits its lane-group split and LDS budget.
 bool loop_held_path(const Dims& D) {
   if (D.bank != SDM_F32) return false;
@@ -650,6 +1126,22 @@ static hipError_t launch_loop_t(const Dims& D, const LoopArgs& a, hipStream_t st
       }
       return hipGetLastError();
     }
+  }
+  if (loop_narrow_path(D)) {
+    const size_t lds = loop_narrow_lds_bytes(D.C, Lane<Bk>::EPL);
+    const int ns = D.d / Lane<Bk>::EPL;
+    const long long nb = (long long)D.S * ns;
+    const int g = LOOP_NT / D.C;
+    if (loop_narrow_lanemajor(D)) {  // the plan wrote the terms lane-major
+      (void)hipFuncSetAttribute((const void*)loop_narrow_kernel<A, Bk, true>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      hipLaunchKernelGGL((loop_narrow_kernel<A, Bk, true>), dim3((unsigned)nb), dim3(LOOP_NT), lds, st, D, a, ns);
+    } else {
+      (void)hipFuncSetAttribute((const void*)loop_narrow_kernel<A, Bk, false>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      hipLaunchKernelGGL((loop_narrow_kernel<A, Bk, false>), dim3((unsigned)nb), dim3(LOOP_NT), lds, st, D, a, ns);
+    }
+    return hipGetLastError();
   }
   if (staged <= 150 * 1024) {
     (void)hipFuncSetAttribute((const void*)loop_kernel<A, Bk, true>, hipFuncAttributeMaxDynamicSharedMemorySize,

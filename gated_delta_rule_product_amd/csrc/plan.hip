@@ -437,8 +437,8 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
           Pair p;
           p.slot = slot;
           p.coef = wt8[k] * prod;
-          pw[evi] = p;
-          wlast[evi] = scode[e];
+          pw[term_pos(evi / W, evi % W, W, a.lanemajor)] = p;
+          wlast[code_pos(evi / W, evi % W, W, a.lanemajor)] = scode[e];
           if (has) {
             const int t = evi / W, i = evi % W;
             atomicOr(&kmask[t * PL.kwm + (i >> 6)], 1ull << (i & 63));
@@ -598,7 +598,7 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
           Pair p;
           p.slot = j;
           p.coef = rr[k] * prod;
-          pr[x] = p;
+          pr[term_pos(t, x % R, R, a.lanemajor)] = p;
         }
       });
     }

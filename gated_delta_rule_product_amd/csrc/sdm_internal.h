@@ -232,7 +232,25 @@ struct PlanArgs {
   unsigned char* chunks;  // [S * nch] regions of chunk_layout(C, W, R).bytes
   ChunkCounts* counts;    // [S * nch]
   int scat;               // also write the slot segments and their events (read by loop_kernel only)
+  int lanemajor;          // write the gather terms lane-major for the narrow loop (term_pos)
 };
+
+// Position of gather term i (of n per token) of chunk-local token t in a chunk's term section. Token-major: t n + i.
+// Lane-major (the narrow chunk loop with 16 terms of each kind per lane): lane L = t gpt + i / 16 (gpt = n / 16)
+// keeps its terms j = i % 16 as 8 words of two (slot, coefficient) pairs, and word k of all 512 lanes is
+// contiguous, so a lane's k-th load is one coalesced 16-byte word: pair index (k * 512 + L) * 2 + j % 2.
+__host__ __device__ inline int term_pos(int t, int i, int n, bool lanemajor) {
+  if (!lanemajor) return t * n + i;
+  const int L = t * (n >> 4) + (i >> 4), j = i & 15;
+  return (((j >> 1) * LOOP_NT + L) << 1) + (j & 1);
+}
+// Position of the int16 last-event code of write term i of token t: token-major t n + i; lane-major as 2 words of
+// 8 codes per lane, word k of all lanes contiguous: ((j / 8) * 512 + L) * 8 + j % 8.
+__host__ __device__ inline int code_pos(int t, int i, int n, bool lanemajor) {
+  if (!lanemajor) return t * n + i;
+  const int L = t * (n >> 4) + (i >> 4), j = i & 15;
+  return (((j >> 3) * LOOP_NT + L) << 3) + (j & 7);
+}
 hipError_t launch_plan(const Dims& D, const PlanArgs& a, hipStream_t st);
 
 struct LoopArgs {
@@ -244,6 +262,10 @@ struct LoopArgs {
 hipError_t launch_loop(const Dims& D, const LoopArgs& a, hipStream_t st);
 // True if launch_loop runs the held-row variant (which reads last-event codes, not slot segments).
 bool loop_held_path(const Dims& D);
+// True if launch_loop runs the narrow variant (16-byte column slices; also reads last-event codes).
+bool loop_narrow_path(const Dims& D);
+// True if it runs the narrow variant with 16 terms of each kind per lane, which reads lane-major terms.
+bool loop_narrow_lanemajor(const Dims& D);
 
 struct DecodeArgs {
   const void* values; const void* alpha; const void* beta;

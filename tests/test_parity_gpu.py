@@ -214,6 +214,58 @@ def test_write_read_three_factors_small():
     check_parity(s, run_gpu(s, x), run_oracle(s, x))
 
 
+# Shapes served by the 16-byte-slice chunk loop: gpt = 512 / C lanes per token share its W write and R read terms
+# (at most 16 of each per lane); bf16 banks, and float32 banks whose chunk gives a 64-byte slice too many terms.
+NARROW = [
+    # act, bank, chunk, W, R, widths, tokens
+    ("bf16", "bf16", 128, 64, 64, (16, 8, 8), 300),   # the three-factor workload's chunk split (16 terms per lane)
+    ("bf16", "f32", 128, 64, 64, (32, 32), 200),      # float32 bank, 16 terms per lane
+    ("f32", "bf16", 64, 32, 24, (32, 32), 150),       # 4 and 3 terms per lane
+    ("bf16", "bf16", 32, 16, 32, (16, 16), 100),      # 1 and 2 terms per lane
+    ("f32", "bf16", 8, 64, 128, (16, 16), 37),        # one wave per token
+]
+
+
+@pytest.mark.parametrize("act,bank,chunk,W,R,widths,T", NARROW)
+def test_write_read_narrow_slices(act, bank, chunk, W, R, widths, T):
+    s = synth.Shape(2, T, 2, widths, 8, 64, W, R, chunk, act, bank, name="narrow")
+    x = synth.make_inputs(s, seed=21)
+    print(f"write/read narrow act={act} bank={bank} C={chunk} W={W} R={R} T={T}", flush=True)
+    got = run_gpu(s, x)
+    check_parity(s, got, run_oracle(s, x))
+    again = run_gpu(s, x)
+    for u, v in zip(got, again):
+        assert np.array_equal(u, v)
+
+
+def test_write_read_narrow_collisions_and_split():
+    """64 slots, W = R = 16, chunk 64, bf16 bank: most writes collide; a split call is bitwise equal."""
+    s = synth.Shape(1, 192, 2, (8, 8), 4, 32, 16, 16, 64, "bf16", "bf16", name="collide_narrow")
+    x = synth.make_inputs(s, seed=22)
+    print("write/read narrow collisions", flush=True)
+    full = run_gpu(s, x)
+    check_parity(s, full, run_oracle(s, x))
+    h = 128
+    first = {k: (v[:, :h] if k in ("wkeys", "rq", "values", "alpha", "beta") else v) for k, v in x.items()}
+    second = {k: (v[:, h:] if k in ("wkeys", "rq", "values", "alpha", "beta") else v) for k, v in x.items()}
+    o1, b1, _, _ = run_gpu(s.with_(tokens=h), first)
+    o2, b2, _, _ = run_gpu(s.with_(tokens=192 - h), second, bank=b1)
+    assert np.array_equal(np.concatenate([o1, o2], 1), full[0])
+    assert np.array_equal(b2, full[1])
+
+
+@pytest.mark.parametrize("pitch", [72, 128])
+def test_write_read_narrow_padded_pitch(pitch):
+    s = synth.Shape(2, 130, 2, (16, 16), 8, 64, 32, 32, 64, "bf16", "bf16", name="narrow_pitch")
+    x = synth.make_inputs(s, seed=23)
+    print(f"write/read narrow pitch={pitch}", flush=True)
+    got = run_gpu(s, x, pitch=pitch)
+    check_parity(s, got, run_oracle(s, x))
+    same = run_gpu(s, x)
+    for u, v in zip(got, same):
+        assert np.array_equal(u, v)
+
+
 def test_write_read_bank_rows_padding():
     """bank_rows > N: rows past N are never touched."""
     s = synth.WORKLOADS["tiny_1k"].with_(tokens=64, bank_rows=1100)
