@@ -285,6 +285,61 @@ __global__ __launch_bounds__(LOOP_NT) void loop_kernel(Dims D, LoopArgs a, int n
   }
 }
 
+// Word 3 of a raw buffer resource on gfx9 (32-bit data format, no swizzle, offsets in bytes).
+constexpr int BUF_RSRC_WORD3 = 0x00020000;
+// A byte offset past every buffer range used here (ranges are kept below it): an access there is dropped by the
+// hardware range check (a store writes nothing), also with 16 or 32 bytes added.
+constexpr uint32_t BUF_OOB = 0xFFFFFF00u;
+
+// EPL activation elements of a row as raw words (one 16- or 32-byte load), converted to floats later.
+template <typename A, int EPL>
+struct ActRaw {
+  static constexpr int NW = (EPL * (int)sizeof(A) + 15) / 16;
+  static_assert(EPL * sizeof(A) == 16 || EPL * sizeof(A) == 32 || EPL * sizeof(A) == 8, "row piece of 8, 16 or 32 bytes");
+  w16_t w[NW];
+  __device__ __forceinline__ void load(const A* p) {
+    if constexpr (EPL * sizeof(A) == 8) {
+      const uint2 x = *(const uint2*)p;
+      w[0] = w16_t{x.x, x.y, 0u, 0u};
+    } else {
+#pragma unroll
+      for (int i = 0; i < NW; ++i) w[i] = ((const w16_t*)p)[i];
+    }
+  }
+  __device__ __forceinline__ void pack(const float (&v)[EPL]) {
+    if constexpr (sizeof(A) == 4) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) w[e / 4][e % 4] = __float_as_uint(v[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; e += 2)
+        w[e / 8][(e % 8) / 2] = (uint32_t)f_to_bf16(v[e]) | ((uint32_t)f_to_bf16(v[e + 1]) << 16);
+    }
+  }
+  // buffer store of the words at byte offset off (one 8-, 16- or two 16-byte stores)
+  __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t off) const {
+    if constexpr (EPL * sizeof(A) == 8) {
+      __builtin_amdgcn_raw_buffer_store_b64((unsigned int __attribute__((ext_vector_type(2)))){w[0].x, w[0].y}, r,
+                                            (int)off, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NW; ++i) __builtin_amdgcn_raw_buffer_store_b128(w[i], r, (int)(off + 16 * i), 0, 0);
+    }
+  }
+  __device__ __forceinline__ void unpack(float (&v)[EPL]) const {
+    if constexpr (sizeof(A) == 4) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) v[e] = __uint_as_float(w[e / 4][e % 4]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const uint32_t x = w[e / 8][(e % 8) / 2];
+        v[e] = __uint_as_float((e & 1) ? (x & 0xFFFF0000u) : (x << 16));
+      }
+    }
+  }
+};
+
 // ------------------------------------------------------------------------------------------- held-row variant
 // For chunks with C a power of two, 8 <= C <= 128, and at most 32 write and 32 read terms per part (float32
 // banks): the 128 lane groups split every token's write terms, and its read terms, in gpt = 128 / C equal parts;
@@ -300,8 +355,9 @@ __global__ __launch_bounds__(LOOP_NT) void loop_kernel(Dims D, LoopArgs a, int n
 // registers, so 32 row loads stay in flight per lane. T/Q lists and multi-event tables larger than their LDS areas are read from the
 // plan region in HBM instead.
 template <typename Bk> struct Hold { static constexpr int N = 32; };  // float32 banks only (see launch_loop_t)
-constexpr int HELD_LISTS_LDS = 12 * 1024;  // T and Q entries kept in LDS
-constexpr int HELD_MULTI_LDS = 12 * 1024;  // multi-event table kept in LDS
+constexpr int HELD_LISTS_LDS = 8 * 1024;   // T and Q entries kept in LDS
+constexpr int HELD_MULTI_LDS = 8 * 1024;   // multi-event table kept in LDS
+constexpr int HELD_MROWS = 256;            // held row slices (64 bytes) of multi-event slots kept in LDS
 
 // one LDS buffer of write terms: pairs [C * W], then int16 last-event codes [C * W] (the plan region's first two
 // sections, same layout)
@@ -314,10 +370,10 @@ __host__ __device__ inline long long held_small_bytes(int C, int cols) {
 }
 
 // LDS: U and delta [C][cols], gates [C]; two write-term buffers; the read terms [C * R]; T/Q row pointers and
-// lists; the multi-event table.
+// lists; the multi-event table; held row slices of slots written more than once.
 __host__ __device__ inline size_t loop_held_lds_bytes(int C, int W, int R, int cols) {
   return (size_t)(held_small_bytes(C, cols) + 2 * held_wterm_bytes(C, W) + align16((long long)C * R * 8) +
-                  align16((long long)2 * (C + 1) * 4) + HELD_LISTS_LDS + HELD_MULTI_LDS);
+                  align16((long long)2 * (C + 1) * 4) + HELD_LISTS_LDS + HELD_MULTI_LDS + HELD_MROWS * 64);
 }
 
 // Copies n16 16-byte words from global to LDS, NB loads in flight per thread.
@@ -412,6 +468,7 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
   unsigned char* sLst = sR + RT;                            // T/Q row pointers, then lists (plan region layout)
   const long long ptrs_b = align16((long long)2 * (C + 1) * 4);
   MSeg* msegs_lds = (MSeg*)(sLst + ptrs_b + HELD_LISTS_LDS);
+  w16_t* sM = (w16_t*)((unsigned char*)msegs_lds + HELD_MULTI_LDS);  // [HELD_MROWS][4] held rows of multi slots
   const int32_t* tptr = (const int32_t*)sLst;
   const int32_t* qptr = tptr + (C + 1);
 
@@ -473,16 +530,13 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
       row[u] = *(const uint4*)(bank + off);
       if ((u & 7) == 7) __builtin_amdgcn_sched_barrier(0);
     }
-    // 2) gates and the value row slice of the token (its part-0 group)
+    // 2) gates and the value row slice of the token (used by its part-0 group), loaded by every lane without a
+    //    branch and converted only after H: a use right after the load would wait for every row load before it
     const long long grow = ((long long)b * D.T + t0 + min(gt, Cc - 1)) * D.H + h;  // token gt's (b, t, h) row
-    float ga = 0.0f, gb = 0.0f, va[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (lead) {
-      ga = to_f<A>(alpha[grow]);
-      gb = to_f<A>(beta[grow]);
-      Act4<A>::load(values + grow * D.d + mycol, va);
-    }
-    float sa_t = 0.0f;
-    if (tid < Cc) sa_t = to_f<A>(alpha[((long long)b * D.T + t0 + tid) * D.H + h]);
+    const A raw_a = alpha[grow], raw_b = beta[grow];
+    ActRaw<A, 4> raw_v;
+    raw_v.load(values + grow * D.d + mycol);
+    const A raw_sa = alpha[((long long)b * D.T + t0 + min(tid, Cc - 1)) * D.H + h];
     // 3) window: read rows into G, held write rows into the same registers
     float gacc[EPL], hacc[EPL];
 #pragma unroll
@@ -527,10 +581,13 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
     }
     // 6) U = beta v - alpha beta H; staged words to LDS (the next write terms go to the free buffer)
     if (lead) {
+      const float ga = to_f<A>(raw_a), gb = to_f<A>(raw_b);
+      float va[4];
+      raw_v.unpack(va);
 #pragma unroll
       for (int e = 0; e < EPL; ++e) sH[gt * COLS + q * EPL + e] = gb * va[e] - ga * gb * hacc[e];
     }
-    if (tid < Cc) sA[tid] = sa_t;
+    if (tid < Cc) sA[tid] = to_f<A>(raw_sa);
     {
       w16_t* dst1 = (w16_t*)sLst;
       w16_t* dst2 = (w16_t*)msegs_lds - n1;
@@ -549,15 +606,21 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
       static_for<NWP>([&](auto k) { wpf[k] = ((const w16_t*)gn)[min(tid + k * LOOP_NT, nw16 - 1)]; });
       static_for<NRP>([&](auto k) { rpf[k] = ((const w16_t*)(gn + CL.rpairs))[min(tid + k * LOOP_NT, nr16 - 1)]; });
     }
-    const Ent* lists = llds ? (const Ent*)(sLst + ptrs_b) : (const Ent*)(greg + CL.lists);
+    // lists and the multi-event table through typed pointers (LDS, or the plan region when they did not fit): a
+    // pointer that may be either compiles to flat loads, whose waits also cover every global load and store
+    const Ent* lists_l = (const Ent*)(sLst + ptrs_b);
+    const Ent* lists_g = (const Ent*)(greg + CL.lists);
     // 7) delta = T U
     if (lead) {
       float d[EPL] = {0.0f, 0.0f, 0.0f, 0.0f};
-      for (int e = tptr[gt]; e < tptr[gt + 1]; ++e) {
-        const Ent x = lists[e];
-        const float4 u = *(const float4*)(sH + x.col * COLS + q * EPL);
-        d[0] += x.val * u.x; d[1] += x.val * u.y; d[2] += x.val * u.z; d[3] += x.val * u.w;
-      }
+      auto trow = [&](const Ent* lists) {
+        for (int e = tptr[gt]; e < tptr[gt + 1]; ++e) {
+          const Ent x = lists[e];
+          const float4 u = *(const float4*)(sH + x.col * COLS + q * EPL);
+          d[0] += x.val * u.x; d[1] += x.val * u.y; d[2] += x.val * u.z; d[3] += x.val * u.w;
+        }
+      };
+      if (llds) trow(lists_l); else trow(lists_g);
       *(float4*)(sD + gt * COLS + q * EPL) = make_float4(d[0], d[1], d[2], d[3]);
     }
     static_for<NWP>([&](auto k) {
@@ -569,32 +632,40 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
       if (more && i < nr16) ((w16_t*)sR)[i] = rpf[k];
     });
     __syncthreads();  // delta in LDS
-    // 8) scatter: the holder of each slot's last event applies the slot's events in token order and stores the row
+    // 8) scatter: a slot's only event is applied by its holder and stored; the held row slices of slots written more
+    //    than once go to LDS (when they fit) and are finished in step 10, one slot per lane group
+    const bool mrows = cnt.nmseg <= HELD_MROWS;
+    const MSeg* msegs_g = (const MSeg*)(greg + CL.multi);
     if (act) {
-      const MSeg* msegs = mlds ? msegs_lds : (const MSeg*)(greg + CL.multi);
-      const Ev* mev = (const Ev*)(msegs + cnt.nmseg);
+      const float4 dg = *(const float4*)(sD + gt * COLS + q * EPL);
+      const float ag = sA[gt];
 #pragma unroll
       for (int u = 0; u < HOLD; ++u) {
         if (FULL || u < tpw) {
           const int code = wl[u];
-          if (code != -1) {
+          if (code == -2) {  // the slot's only event: own token, own weight
             float m[EPL];
             Lane<Bk>::unpack(row[u], m);
             const Pair p = pw[u];
-            if (code == -2) {  // the slot's only event: own token, own weight
-              const float al = sA[gt];
-#pragma unroll
-              for (int k = 0; k < EPL; ++k) m[k] = al * m[k] + p.coef * sD[gt * COLS + q * EPL + k];
-            } else {
-              const MSeg sg = msegs[code];
+            m[0] = ag * m[0] + p.coef * dg.x; m[1] = ag * m[1] + p.coef * dg.y;
+            m[2] = ag * m[2] + p.coef * dg.z; m[3] = ag * m[3] + p.coef * dg.w;
+            Lane<Bk>::store(bank + ((uint64_t)(uint32_t)p.slot * ld + (uint32_t)mycol), m);
+          } else if (code >= 0) {
+            if (mrows) {
+              sM[code * 4 + q] = w16_t{row[u].x, row[u].y, row[u].z, row[u].w};
+            } else {  // rare (many multi-event slots): events read from the plan region
+              float m[EPL];
+              Lane<Bk>::unpack(row[u], m);
+              const MSeg sg = msegs_g[code];
+              const Ev* mev = (const Ev*)(msegs_g + cnt.nmseg);
               for (int e = sg.beg; e < sg.end; ++e) {
                 const Ev x = mev[e];
                 const float al = sA[x.tok];
 #pragma unroll
                 for (int k = 0; k < EPL; ++k) m[k] = al * m[k] + x.w * sD[x.tok * COLS + q * EPL + k];
               }
+              Lane<Bk>::store(bank + ((uint64_t)(uint32_t)pw[u].slot * ld + (uint32_t)mycol), m);
             }
-            Lane<Bk>::store(bank + ((uint64_t)(uint32_t)p.slot * ld + (uint32_t)mycol), m);
           }
         }
       }
@@ -604,12 +675,36 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
       float o[EPL];
 #pragma unroll
       for (int e = 0; e < EPL; ++e) o[e] = gacc[e];
-      for (int e = qptr[gt]; e < qptr[gt + 1]; ++e) {
-        const Ent x = lists[e];
-        const float4 dd = *(const float4*)(sD + x.col * COLS + q * EPL);
-        o[0] += x.val * dd.x; o[1] += x.val * dd.y; o[2] += x.val * dd.z; o[3] += x.val * dd.w;
-      }
+      auto qrow = [&](const Ent* lists) {
+        for (int e = qptr[gt]; e < qptr[gt + 1]; ++e) {
+          const Ent x = lists[e];
+          const float4 dd = *(const float4*)(sD + x.col * COLS + q * EPL);
+          o[0] += x.val * dd.x; o[1] += x.val * dd.y; o[2] += x.val * dd.z; o[3] += x.val * dd.w;
+        }
+      };
+      if (llds) qrow(lists_l); else qrow(lists_g);
       Act4<A>::store(out + grow * D.d + mycol, o);
+    }
+    // 10) slots written more than once: their events in token order on the held row slice, one store
+    if (mrows) {
+      __syncthreads();  // held row slices in LDS
+      auto finish = [&](const MSeg* msegs) {
+        const Ev* mev = (const Ev*)(msegs + cnt.nmseg);
+        for (int i = G; i < cnt.nmseg; i += 128) {
+          const MSeg sg = msegs[i];
+          const w16_t x0 = sM[i * 4 + q];
+          float m[EPL] = {__uint_as_float(x0.x), __uint_as_float(x0.y), __uint_as_float(x0.z), __uint_as_float(x0.w)};
+          for (int e = sg.beg; e < sg.end; ++e) {
+            const Ev x = mev[e];
+            const float al = sA[x.tok];
+            const float4 dd = *(const float4*)(sD + x.tok * COLS + q * EPL);
+            m[0] = al * m[0] + x.w * dd.x; m[1] = al * m[1] + x.w * dd.y;
+            m[2] = al * m[2] + x.w * dd.z; m[3] = al * m[3] + x.w * dd.w;
+          }
+          if (valid) Lane<Bk>::store(bank + ((uint64_t)(uint32_t)sg.slot * ld + (uint32_t)mycol), m);
+        }
+      };
+      if (mlds) finish(msegs_lds); else finish(msegs_g);
     }
     cnt = next;
     __syncthreads();
@@ -659,61 +754,6 @@ __device__ __forceinline__ void act_store(A* p, const float (&v)[EPL]) {
     Act4<A>::store(p + 4 * k, t);
   });
 }
-
-// Word 3 of a raw buffer resource on gfx9 (32-bit data format, no swizzle, offsets in bytes).
-constexpr int BUF_RSRC_WORD3 = 0x00020000;
-// A byte offset past every buffer range used here (ranges are kept below it): an access there is dropped by the
-// hardware range check (a store writes nothing), also with 16 or 32 bytes added.
-constexpr uint32_t BUF_OOB = 0xFFFFFF00u;
-
-// EPL activation elements of a row as raw words (one 16- or 32-byte load), converted to floats later.
-template <typename A, int EPL>
-struct ActRaw {
-  static constexpr int NW = (EPL * (int)sizeof(A) + 15) / 16;
-  static_assert(EPL * sizeof(A) == 16 || EPL * sizeof(A) == 32 || EPL * sizeof(A) == 8, "row piece of 8, 16 or 32 bytes");
-  w16_t w[NW];
-  __device__ __forceinline__ void load(const A* p) {
-    if constexpr (EPL * sizeof(A) == 8) {
-      const uint2 x = *(const uint2*)p;
-      w[0] = w16_t{x.x, x.y, 0u, 0u};
-    } else {
-#pragma unroll
-      for (int i = 0; i < NW; ++i) w[i] = ((const w16_t*)p)[i];
-    }
-  }
-  __device__ __forceinline__ void pack(const float (&v)[EPL]) {
-    if constexpr (sizeof(A) == 4) {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) w[e / 4][e % 4] = __float_as_uint(v[e]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < EPL; e += 2)
-        w[e / 8][(e % 8) / 2] = (uint32_t)f_to_bf16(v[e]) | ((uint32_t)f_to_bf16(v[e + 1]) << 16);
-    }
-  }
-  // buffer store of the words at byte offset off (one 8-, 16- or two 16-byte stores)
-  __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t off) const {
-    if constexpr (EPL * sizeof(A) == 8) {
-      __builtin_amdgcn_raw_buffer_store_b64((unsigned int __attribute__((ext_vector_type(2)))){w[0].x, w[0].y}, r,
-                                            (int)off, 0, 0);
-    } else {
-#pragma unroll
-      for (int i = 0; i < NW; ++i) __builtin_amdgcn_raw_buffer_store_b128(w[i], r, (int)(off + 16 * i), 0, 0);
-    }
-  }
-  __device__ __forceinline__ void unpack(float (&v)[EPL]) const {
-    if constexpr (sizeof(A) == 4) {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) v[e] = __uint_as_float(w[e / 4][e % 4]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        const uint32_t x = w[e / 8][(e % 8) / 2];
-        v[e] = __uint_as_float((e & 1) ? (x & 0xFFFF0000u) : (x << 16));
-      }
-    }
-  }
-};
 
 // A lane's gather terms of one chunk: NARROW_HOLD (slot, coefficient) pairs, and for write terms their int16
 // last-event codes. FULL: exactly NARROW_HOLD terms, stored lane-major (term_pos, code_pos): word k of the lane is
