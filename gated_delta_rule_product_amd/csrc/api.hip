@@ -501,6 +501,25 @@ sdm_status sdm_decode_step(const sdm_config* cfg, const void* write_keys, const 
   if (!donated)
     TRY(hip_status(timed(SDM_K_COPY, st, [&] { return launch_copy(bank_in, bank_out, bank_bytes, st); }),
                    "successor copy launch"));
+  DecodeArgs a;
+  memset(&a, 0, sizeof a);
+  a.queries[0] = write_keys;
+  a.queries[1] = read_queries;
+  a.subkeys = subkeys;
+  a.plan[0] = pw;
+  a.plan[1] = pr;
+  a.user_ids[0] = write_idx;
+  a.user_ids[1] = read_idx;
+  a.values = values;
+  a.alpha = forget_gate;
+  a.beta = input_gate;
+  a.bank_in = bank_in;
+  a.bank_out = bank_out;
+  a.out = out;
+  if (decode_step_fits(D, a)) {  // top-k, update and read in one launch
+    TRY(hip_status(timed(SDM_K_DECODE, st, [&] { return launch_decode_step(D, a, st); }), "decode step launch"));
+    return ok();
+  }
   TopkArgs ta;
   memset(&ta, 0, sizeof ta);
   ta.queries[0] = write_keys;
@@ -521,13 +540,6 @@ sdm_status sdm_decode_step(const sdm_config* cfg, const void* write_keys, const 
   ta.snorm = (float*)(ws + L.snorm);
   ta.one_query_per_wave = 1;
   TRY(hip_status(timed(SDM_K_TOPK, st, [&] { return launch_topk(D, ta, st); }), "top-k launch"));
-  DecodeArgs a;
-  a.values = values;
-  a.alpha = forget_gate;
-  a.beta = input_gate;
-  a.bank_in = bank_in;
-  a.bank_out = bank_out;
-  a.out = out;
   a.wid = (const int32_t*)(ws + L.widx);
   a.wwt = (const float*)(ws + L.wwt);
   a.rid = (const int32_t*)(ws + L.ridx);

@@ -9,6 +9,8 @@
 // the read takes its rows from bank_out. Both forms therefore execute identical arithmetic on identical values
 // and produce identical bits. Per-token work is O((W + R) d) as in the pages' cost model; the copy is O(N d).
 #include "sdm_internal.h"
+#include "topk_device.h"
+#include "topk_wave.h"
 
 namespace sdm {
 
@@ -169,6 +171,256 @@ hipError_t launch_decode(const Dims& D, const DecodeArgs& a, hipStream_t st) {
   if (D.act == SDM_BF16)
     return D.bank == SDM_BF16 ? launch_decode_t<bf16_t, bf16_t>(D, a, st) : launch_decode_t<bf16_t, float>(D, a, st);
   return D.bank == SDM_BF16 ? launch_decode_t<float, bf16_t>(D, a, st) : launch_decode_t<float, float>(D, a, st);
+}
+
+// ------------------------------------------------------------------------------------------- one-launch step
+// The step in one workgroup per stream (b, h): the block builds both candidate tables in LDS, waves 0 and 1
+// compute the write and read top-k (wave_topk_single), then all four waves gather, update and read the rows in
+// column passes of 64 lanes x 16 bytes: wave w takes write rows and read rows w, w + 4, ... (W, R <= 64). All row
+// loads of a pass come from bank_in and complete before any row of the pass is written; a read row whose slot is
+// also written this step is updated in registers with the same arithmetic and rounding as the stored row, so the
+// read sees the successor's values (write then read, as the per-token recurrence) and a donated step equals a
+// copied one bit for bit. r and out are summed per wave in row order, then over the waves in order.
+struct StepLds {
+  uint64_t* ctab[2];
+  int* cscratch;
+  float* fsc[2];
+  uint16_t* fid[2];
+  uint64_t* scratch[2];
+  uint64_t* sorted[2];
+  int32_t *wid, *rid, *rmatch;
+  float *wwt, *rwt;
+  float* part;  // [4][64 EPL]
+  size_t bytes;
+};
+
+__host__ __device__ inline StepLds step_lds(unsigned char* base, const Dims& D, const TopkPlan* P, int epl) {
+  StepLds L;
+  size_t o = 0;
+  auto take = [&](size_t b) {
+    unsigned char* p = base + o;
+    o = (o + b + 15) & ~(size_t)15;
+    return p;
+  };
+  const int nc = P[0].ncand > P[1].ncand ? P[0].ncand : P[1].ncand;
+  const int kp0 = P[0].kp[0] > P[1].kp[0] ? P[0].kp[0] : P[1].kp[0];
+  for (int q = 0; q < 2; ++q) L.ctab[q] = (uint64_t*)take((size_t)nc * 8);
+  L.cscratch = (int*)take((size_t)(kp0 + 1) * 4);
+  for (int q = 0; q < 2; ++q) {
+    const int KS = P[q].kpmax > P[q].k ? P[q].kpmax : P[q].k;
+    L.fsc[q] = (float*)take((size_t)D.F * P[q].kpmax * 4);
+    L.fid[q] = (uint16_t*)take((size_t)D.F * P[q].kpmax * 2);
+    L.scratch[q] = (uint64_t*)take((size_t)(KS + 8) * 8);
+    L.sorted[q] = (uint64_t*)take((size_t)KS * 8);
+  }
+  L.wid = (int32_t*)take((size_t)D.W * 4);
+  L.wwt = (float*)take((size_t)D.W * 4);
+  L.rid = (int32_t*)take((size_t)D.R * 4);
+  L.rwt = (float*)take((size_t)D.R * 4);
+  L.rmatch = (int32_t*)take((size_t)D.R * 4);
+  L.part = (float*)take((size_t)4 * 64 * epl * 4);
+  L.bytes = o;
+  return L;
+}
+
+// A float rounded to the bank dtype and back (the value a stored row holds).
+template <typename Bk> __device__ __forceinline__ float bank_round(float v);
+template <> __device__ __forceinline__ float bank_round<float>(float v) { return v; }
+template <> __device__ __forceinline__ float bank_round<bf16_t>(float v) { return bf16_to_f(f_to_bf16(v)); }
+
+// A 16-byte row piece (EPL elements of the bank dtype) as floats.
+template <typename Bk> __device__ __forceinline__ void piece_unpack(const w16_t& x, float* v);
+template <> __device__ __forceinline__ void piece_unpack<float>(const w16_t& x, float* v) {
+  v[0] = __uint_as_float(x.x); v[1] = __uint_as_float(x.y); v[2] = __uint_as_float(x.z); v[3] = __uint_as_float(x.w);
+}
+template <> __device__ __forceinline__ void piece_unpack<bf16_t>(const w16_t& x, float* v) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(x[i] << 16);
+    v[2 * i + 1] = __uint_as_float(x[i] & 0xFFFF0000u);
+  }
+}
+
+constexpr int STEP_NT = 256;
+constexpr int STEP_RPW = 16;  // rows of each kind per wave: W, R <= 64
+
+template <typename A, typename Bk, int NPL, int CPL>
+__global__ __launch_bounds__(STEP_NT) void decode_step_kernel(Dims D, DecodeArgs a) {
+  constexpr int EPL = DLane<Bk>::EPL;
+  constexpr int COLW = 64 * EPL;
+  extern __shared__ __align__(16) unsigned char lds[];
+  const StepLds L = step_lds(lds, D, a.plan, EPL);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int st = blockIdx.x;  // stream b * H + h; with one token the [B, 1, H] row index equals st
+  const int h = st % D.H;
+  build_cand_table<STEP_NT>(a.plan[0], D.F, L.ctab[0], L.cscratch);
+  build_cand_table<STEP_NT>(a.plan[1], D.F, L.ctab[1], L.cscratch);
+  if (wv < 2) {
+    const int kind = wv;
+    long long sumn = 0;
+    for (int f = 0; f < D.F; ++f) sumn += D.widths[f];
+    const A* qv = (const A*)(kind ? a.queries[1] : a.queries[0]) + (long long)st * D.F * D.dk;
+    const A* sub = (const A*)a.subkeys + (long long)h * sumn * D.dk;
+    int32_t* ids = kind ? L.rid : L.wid;
+    float* wts = kind ? L.rwt : L.wwt;
+    // (members selected by kind, not indexed: a runtime index into a struct's array puts the struct in scratch)
+    const TopkPlan& P = kind ? a.plan[1] : a.plan[0];
+    wave_topk_single<A, NPL, CPL>(D, P, kind ? L.ctab[1] : L.ctab[0], qv, sub, kind ? L.fsc[1] : L.fsc[0],
+                                  kind ? L.fid[1] : L.fid[0], kind ? L.scratch[1] : L.scratch[0],
+                                  kind ? L.sorted[1] : L.sorted[0], ids, wts);
+    int32_t* uid = kind ? a.user_ids[1] : a.user_ids[0];
+    if (uid)
+      for (int r = lane; r < P.k; r += 64) uid[(long long)st * P.k + r] = ids[r];
+  }
+  __syncthreads();
+  // read slots that are also written this step (the slots of one top-k are distinct)
+  for (int j = tid; j < D.R; j += STEP_NT) {
+    const int s = L.rid[j];
+    int mi = -1;
+    for (int i = 0; i < D.W; ++i) mi = L.wid[i] == s ? i : mi;
+    L.rmatch[j] = mi;
+  }
+  __syncthreads();
+  const float al = to_f<A>(((const A*)a.alpha)[st]);
+  const float be = to_f<A>(((const A*)a.beta)[st]);
+  const long long rowsd = D.rows * D.ld;
+  const Bk* bin = (const Bk*)a.bank_in + (long long)st * rowsd;
+  Bk* bout = (Bk*)a.bank_out + (long long)st * rowsd;
+  float* part = L.part;
+  for (int c0 = 0; c0 < D.d; c0 += COLW) {
+    const int col = c0 + lane * EPL;
+    const bool valid = col < D.d;
+    w16_t wr[STEP_RPW], rr[STEP_RPW];
+    static_for<STEP_RPW>([&](auto u) {
+      const int i = wv + 4 * u;
+      wr[u] = w16_t{0u, 0u, 0u, 0u};
+      if (valid && i < D.W) wr[u] = *(const w16_t*)(bin + (long long)L.wid[i] * D.ld + col);
+    });
+    static_for<STEP_RPW>([&](auto u) {
+      const int j = wv + 4 * u;
+      rr[u] = w16_t{0u, 0u, 0u, 0u};
+      if (valid && j < D.R) rr[u] = *(const w16_t*)(bin + (long long)L.rid[j] * D.ld + col);
+    });
+    // r = sum_i w_i M[S_i]: this wave's rows in order
+    float acc[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
+    static_for<STEP_RPW>([&](auto u) {
+      const int i = wv + 4 * u;
+      if (i < D.W) {
+        const float wi = L.wwt[i];
+        float m[EPL];
+        piece_unpack<Bk>(wr[u], m);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] += wi * m[e];
+      }
+    });
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) part[wv * COLW + lane * EPL + e] = acc[e];
+    // every read row of this pass has arrived before the barrier, so no row written below can reach it
+#pragma unroll
+    for (int u = 0; u < STEP_RPW; ++u) asm volatile("" ::"v"(rr[u]));
+    __syncthreads();
+    // delta = beta (v - alpha r) for this lane's columns (the same in every wave)
+    float dl[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const int c = lane * EPL + e;
+      const float r = part[c] + part[COLW + c] + part[2 * COLW + c] + part[3 * COLW + c];
+      dl[e] = valid ? be * (to_f<A>(((const A*)a.values)[(long long)st * D.d + col + e]) - al * r) : 0.0f;
+    }
+    __syncthreads();  // every wave has read the partial sums
+    // M[S_i] <- alpha M[S_i] + w_i delta, rounded to the bank dtype, into the successor
+    static_for<STEP_RPW>([&](auto u) {
+      const int i = wv + 4 * u;
+      if (valid && i < D.W) {
+        const float wi = L.wwt[i];
+        float m[EPL];
+        piece_unpack<Bk>(wr[u], m);
+        float y[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) y[e] = fmaf(wi, dl[e], al * m[e]);
+        DLane<Bk>::store(bout + (long long)L.wid[i] * D.ld + col, y);
+      }
+    });
+    // out = sum_j rho_j M'[R_j], M' the successor (rows written this step updated as above)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
+    static_for<STEP_RPW>([&](auto u) {
+      const int j = wv + 4 * u;
+      if (j < D.R) {
+        float m[EPL];
+        piece_unpack<Bk>(rr[u], m);
+        const int mi = L.rmatch[j];
+        if (mi >= 0) {
+          const float wi = L.wwt[mi];
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) m[e] = bank_round<Bk>(fmaf(wi, dl[e], al * m[e]));
+        }
+        const float rj = L.rwt[j];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] += rj * m[e];
+      }
+    });
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) part[wv * COLW + lane * EPL + e] = acc[e];
+    __syncthreads();
+    if (wv == 0 && valid) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const int c = lane * EPL + e;
+        const float o = part[c] + part[COLW + c] + part[2 * COLW + c] + part[3 * COLW + c];
+        ((A*)a.out)[(long long)st * D.d + col + e] = from_f<A>(o);
+      }
+    }
+    __syncthreads();  // the partial sums are reused by the next pass
+  }
+}
+
+static void step_shape(const Dims& D, const DecodeArgs& a, int* npl, int* cpl) {
+  int nfmax = 0;
+  for (int f = 0; f < D.F; ++f) nfmax = D.widths[f] > nfmax ? D.widths[f] : nfmax;
+  *npl = 1;
+  while (*npl * 64 < nfmax) *npl <<= 1;
+  const int nc = a.plan[0].ncand > a.plan[1].ncand ? a.plan[0].ncand : a.plan[1].ncand;
+  *cpl = nc <= 512 ? 8 : 16;
+}
+
+bool decode_step_fits(const Dims& D, const DecodeArgs& a) {
+  int npl, cpl;
+  step_shape(D, a, &npl, &cpl);
+  const int epl = D.bank == SDM_BF16 ? 8 : 4;
+  if (npl > 4 || D.W > 4 * STEP_RPW || D.R > 4 * STEP_RPW) return false;
+  for (int q = 0; q < 2; ++q)
+    if (a.plan[q].ncand > 64 * cpl || a.plan[q].kpmax > 1024) return false;
+  const int esz = D.act == SDM_BF16 ? 2 : 4;
+  if ((D.dk * esz) % 16 != 0 || ((uintptr_t)a.subkeys) % 16 != 0) return false;
+  return step_lds(nullptr, D, a.plan, epl).bytes <= 64 * 1024;
+}
+
+template <typename A, typename Bk, int NPL, int CPL>
+static void launch_step_k(const Dims& D, const DecodeArgs& a, size_t lds, hipStream_t st) {
+  (void)hipFuncSetAttribute((const void*)decode_step_kernel<A, Bk, NPL, CPL>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipLaunchKernelGGL((decode_step_kernel<A, Bk, NPL, CPL>), dim3((unsigned)D.S), dim3(STEP_NT), lds, st, D, a);
+}
+
+template <typename A, typename Bk>
+static hipError_t launch_step_t(const Dims& D, const DecodeArgs& a, hipStream_t st) {
+  int npl, cpl;
+  step_shape(D, a, &npl, &cpl);
+  const size_t lds = step_lds(nullptr, D, a.plan, DLane<Bk>::EPL).bytes;
+  if (npl == 1) cpl == 8 ? launch_step_k<A, Bk, 1, 8>(D, a, lds, st) : launch_step_k<A, Bk, 1, 16>(D, a, lds, st);
+  else if (npl == 2) cpl == 8 ? launch_step_k<A, Bk, 2, 8>(D, a, lds, st) : launch_step_k<A, Bk, 2, 16>(D, a, lds, st);
+  else cpl == 8 ? launch_step_k<A, Bk, 4, 8>(D, a, lds, st) : launch_step_k<A, Bk, 4, 16>(D, a, lds, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_step(const Dims& D, const DecodeArgs& a, hipStream_t st) {
+  if (D.S == 0) return hipSuccess;
+  if (D.act == SDM_BF16)
+    return D.bank == SDM_BF16 ? launch_step_t<bf16_t, bf16_t>(D, a, st) : launch_step_t<bf16_t, float>(D, a, st);
+  return D.bank == SDM_BF16 ? launch_step_t<float, bf16_t>(D, a, st) : launch_step_t<float, float>(D, a, st);
 }
 
 __global__ __launch_bounds__(256) void copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, size_t n) {

@@ -272,8 +272,17 @@ struct DecodeArgs {
   const void* bank_in; void* bank_out; void* out;
   const int32_t* wid; const float* wwt;  // [S][W] write slots and weights (top-k of the step)
   const int32_t* rid; const float* rwt;  // [S][R] read slots and weights
+  // the one-launch step computes the top-k itself from these
+  const void* queries[2];                // write keys, read queries [S][F dk]
+  const void* subkeys;
+  TopkPlan plan[2];
+  int32_t* user_ids[2];                  // optional [S][W|R] slot ids
 };
 hipError_t launch_decode(const Dims& D, const DecodeArgs& a, hipStream_t st);
+// The whole step (top-k, update, read) in one launch, one workgroup per stream; false if the shape does not fit
+// (then nothing is launched).
+bool decode_step_fits(const Dims& D, const DecodeArgs& a);
+hipError_t launch_decode_step(const Dims& D, const DecodeArgs& a, hipStream_t st);
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t st);
 
 

@@ -56,9 +56,16 @@ __global__ __launch_bounds__(TOPK_NT) void topk_kernel(Dims D, TopkArgs a) {
 // One wave scores QW query rows (same head and kind) against every sub-key with the fp64 FMA chain, each lane
 // owning NPL sub-keys (its rows read as 16-byte vectors and reused across the QW queries), selects each factor's
 // top min(k, n_f) exactly (wave_select_sorted), then merges the candidate tuples (CPL per lane) the same way.
-// Queries per wave for NPL sub-keys per lane (QW * NPL <= 16 keeps the fp64 accumulators at 32 registers).
-__host__ __device__ constexpr int wave_qw(int npl) { return 16 / npl < 1 ? 1 : 16 / npl; }
-template <int NPL> struct WaveTile { static constexpr int QW = wave_qw(NPL); };
+// Queries per wave for NPL sub-keys per lane (QW * NPL <= 16 keeps the fp64 accumulators at 32 registers). Narrow
+// factors (NPL <= 2) take 4 queries: the per-wave LDS of 16 (the factor lists of every query are kept until the
+// merge) allowed only one 4-wave block per CU, and the selections, which are latency-bound, ran at one wave per
+// SIMD (three-factor workload: 1.87 -> 0.65 ms per kind). The filtered scoring of wide factors (NPL >= 8) takes 2:
+// its MFMA tiles reload the factor's sub-key table per wave, so a second query halves that traffic, while 4 would
+// cost occupancy (1,048,576 slots: 1.46 -> 1.03 ms per 32,768 queries; 4 queries: 1.36 ms).
+__host__ __device__ constexpr int wave_qw(int npl, bool mf = false) {
+  return (mf && npl >= 8) ? 2 : npl <= 2 ? 4 : 16 / npl < 1 ? 1 : 16 / npl;
+}
+template <int NPL, bool MF = false> struct WaveTile { static constexpr int QW = wave_qw(NPL, MF); };
 
 // Per-wave LDS: factor scores [QW][64 NPL] (float), kept factor lists [QW][F][kpmax] (float score + uint16 id),
 // selection scratch [KS + 8] and sorted output [KS] (uint64).
@@ -103,23 +110,6 @@ __device__ __forceinline__ bf16x8_t load_bf16x8(const bf16_t* p) {
   const uint4 v = *(const uint4*)p;
   return __builtin_bit_cast(bf16x8_t, v);
 }
-
-// 16 bytes of a sub-key row and element e of it as fp64 (exact widening).
-template <typename A> struct Vec16;
-template <> struct Vec16<float> {
-  static constexpr int N = 4;
-  __device__ static double at(const uint4& x, int e) {
-    const uint32_t w = e == 0 ? x.x : e == 1 ? x.y : e == 2 ? x.z : x.w;
-    return (double)__uint_as_float(w);
-  }
-};
-template <> struct Vec16<bf16_t> {
-  static constexpr int N = 8;
-  __device__ static double at(const uint4& x, int e) {
-    const uint32_t w = (e >> 1) == 0 ? x.x : (e >> 1) == 1 ? x.y : (e >> 1) == 2 ? x.z : x.w;
-    return (double)__uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
-  }
-};
 
 // One factor of the wave's QW queries by the filtered scoring: MFMA tiles of 16 queries (nq used) x 16 sub-keys,
 // bounds, threshold, exact fp64 re-score of the kept sub-keys, exact top-k_p. Writes fsc/fid like the direct path.
@@ -334,7 +324,7 @@ __device__ void factor_topk_filtered(const Dims& D, const TopkArgs& a, int f, in
 // QW1: one query per wave (few rows, e.g. a decode step: parallelism over queries rather than reuse of sub-key rows).
 template <typename A, int NPL, int CPL, bool MF, bool QW1>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NPL <= 4 ? 4 : 1))) void topk2_kernel(Dims D, TopkArgs a) {
-  constexpr int QW = QW1 ? 1 : WaveTile<NPL>::QW;
+  constexpr int QW = QW1 ? 1 : WaveTile<NPL, MF>::QW;
   constexpr int VEC = Vec16<A>::N;
   extern __shared__ __align__(16) unsigned char lds[];
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -493,7 +483,7 @@ static void launch_topk2_k(dim3 grid, size_t lds, hipStream_t st, const Dims& D,
 
 template <typename A, int NPL>
 static bool launch_topk2_npl(const Dims& D, const TopkArgs& a, hipStream_t st, int cpl, size_t lds, bool mf) {
-  const int QW = a.one_query_per_wave ? 1 : WaveTile<NPL>::QW;
+  const int QW = a.one_query_per_wave ? 1 : (mf ? WaveTile<NPL, true>::QW : WaveTile<NPL>::QW);
   const long long BT = (long long)D.B * D.T;
   const long long tiles = (BT + QW - 1) / QW;
   dim3 grid((unsigned)((tiles + 3) / 4), (unsigned)a.nkinds, (unsigned)D.H);
@@ -551,7 +541,8 @@ static bool launch_topk2(const Dims& D, const TopkArgs& a, hipStream_t st) {
   if (ncand > 1024 || kpmax > 1024) return false;
   if ((D.dk * (int)sizeof(A)) % 16 != 0 || ((uintptr_t)a.subkeys) % 16 != 0) return false;
   const int cpl = ncand <= 512 ? 8 : 16;
-  const int QW = a.one_query_per_wave ? 1 : wave_qw(npl);
+  const bool mf = !a.one_query_per_wave && topk_filtered(D, a);
+  const int QW = a.one_query_per_wave ? 1 : wave_qw(npl, mf);
   size_t lds = 0;
   for (int q = 0; q < a.nkinds; ++q) {
     size_t l = 4 * topk2_wave_lds(D.F, a.plan[q].kpmax, a.plan[q].k, QW, npl);
@@ -559,7 +550,6 @@ static bool launch_topk2(const Dims& D, const TopkArgs& a, hipStream_t st) {
     lds = l > lds ? l : lds;
   }
   if (lds > 128 * 1024) return false;
-  const bool mf = !a.one_query_per_wave && topk_filtered(D, a);
   if (mf) {
     int sumn = 0;
     for (int f = 0; f < D.F; ++f) sumn += D.widths[f];

@@ -17,6 +17,23 @@ __device__ __forceinline__ void wave_sync() {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// 16 bytes of a sub-key row and element e of it as fp64 (exact widening).
+template <typename A> struct Vec16;
+template <> struct Vec16<float> {
+  static constexpr int N = 4;
+  __device__ static double at(const uint4& x, int e) {
+    const uint32_t w = e == 0 ? x.x : e == 1 ? x.y : e == 2 ? x.z : x.w;
+    return (double)__uint_as_float(w);
+  }
+};
+template <> struct Vec16<bf16_t> {
+  static constexpr int N = 8;
+  __device__ static double at(const uint4& x, int e) {
+    const uint32_t w = (e >> 1) == 0 ? x.x : (e >> 1) == 1 ? x.y : (e >> 1) == 2 ? x.z : x.w;
+    return (double)__uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+  }
+};
+
 __device__ __forceinline__ uint64_t lanes_below_mask() {
   const int l = lane_id();
   return l == 0 ? 0ull : (~0ull >> (64 - l));
@@ -109,6 +126,92 @@ __device__ void wave_select_sorted(const uint64_t (&key)[N], int k, uint64_t* sc
     }
     out[r] = v;
   }
+  wave_sync();
+}
+
+// Exact top-k of one query by one wave (the method and its exactness: topk_device.h). Factor scores: the fp64 FMA
+// chain in coordinate order, rounded to float32, for every sub-key (NPL per lane, lane l owns l + 64 j); each
+// factor's top k_p by wave selection; then the candidate tuples of `cand` (CPL per lane) with their float32 slot
+// scores summed left to right, selected by (score, position sum, candidate index). Writes ids[r] (slot ids, best
+// first) and wts[r] (softmax of the k slot scores: fp64 exponentials, per-lane partial sums in a fixed order and a
+// fixed butterfly) to LDS. fsc/fid: [F][kpmax] LDS; scratch and sorted: this wave's selection buffers.
+template <typename A, int NPL, int CPL>
+__device__ void wave_topk_single(const Dims& D, const TopkPlan& P, const uint64_t* cand, const A* qv, const A* sub,
+                                 float* fsc, uint16_t* fid, uint64_t* scratch, uint64_t* sorted, int32_t* ids,
+                                 float* wts) {
+  constexpr int VEC = Vec16<A>::N;
+  const int lane = lane_id();
+  const int F = D.F, dk = D.dk, k = P.k, kpmax = P.kpmax;
+  long long off = 0;
+  for (int f = 0; f < F; ++f) {
+    const int n = D.widths[f];
+    const A* tab = sub + off * dk;
+    double acc[NPL];
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) acc[j] = 0.0;
+    for (int c0 = 0; c0 < dk; c0 += VEC) {
+      uint4 rv[NPL];
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) {
+        const int i = lane + 64 * j;
+        rv[j] = i < n ? *(const uint4*)(tab + (long long)i * dk + c0) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const double x = to_d<A>(qv[f * dk + c0 + e]);
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) acc[j] = fma(x, Vec16<A>::at(rv[j], e), acc[j]);
+      }
+    }
+    uint64_t key[NPL];
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const int i = lane + 64 * j;
+      key[j] = i < n ? (((uint64_t)desc_key((float)acc[j]) << 32) | (uint32_t)i) : ~0ull;
+    }
+    wave_select_sorted<NPL>(key, P.kp[f], scratch, sorted);
+    for (int p = lane; p < P.kp[f]; p += 64) {
+      const uint64_t kk = sorted[p];
+      fsc[f * kpmax + p] = desc_key_value((uint32_t)(kk >> 32));
+      fid[f * kpmax + p] = (uint16_t)(uint32_t)kk;
+    }
+    wave_sync();
+    off += n;
+  }
+  uint64_t ck[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int c = lane + 64 * j;
+    uint64_t key = ~0ull;
+    if (c < P.ncand) {
+      const uint64_t tup = cand[c];
+      int p = (int)(tup & 0xFFFF);
+      float S = fsc[p];
+      int ps = p;
+      for (int f = 1; f < F; ++f) {
+        p = (int)((tup >> (16 * f)) & 0xFFFF);
+        S = S + fsc[f * kpmax + p];  // float32 sum, left to right
+        ps += p;
+      }
+      key = ((uint64_t)desc_key(S) << 32) | ((uint64_t)ps << 20) | (uint64_t)c;
+    }
+    ck[j] = key;
+  }
+  wave_select_sorted<CPL>(ck, k, scratch, sorted);
+  const double m = (double)desc_key_value((uint32_t)(sorted[0] >> 32));
+  double zpart = 0.0;
+  for (int r = lane; r < k; r += 64) {
+    const uint64_t kk = sorted[r];
+    const uint64_t tup = cand[(int)(kk & 0xFFFFF)];
+    long long id = 0;
+    for (int f = 0; f < F; ++f) id = id * D.widths[f] + fid[f * kpmax + (int)((tup >> (16 * f)) & 0xFFFF)];
+    ids[r] = (int32_t)id;
+    zpart += exp((double)desc_key_value((uint32_t)(kk >> 32)) - m);
+  }
+  double z = zpart;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) z += __shfl_xor(z, o);
+  for (int r = lane; r < k; r += 64) wts[r] = (float)(exp((double)desc_key_value((uint32_t)(sorted[r] >> 32)) - m) / z);
   wave_sync();
 }
 
