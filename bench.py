@@ -227,18 +227,64 @@ def bench_decode(args, torch, binding, synth):
         for i in range(args.decode_warmup):
             one(i)
         torch.cuda.synchronize()
-        binding.profile_enable(True)
         t0 = time.perf_counter()
         for i in range(args.decode_warmup, nsteps):
             one(i)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
+        ms = (t1 - t0) * 1e3 / args.decode_steps
+        outs[mode] = (out.clone(), (banks[0] if mode == "donated" else banks[cur]).clone())
+        # kernel times: the same steps again with timing events on (not part of the steps/s above)
+        banks[0].copy_(bank0)
+        cur = 0
+        torch.cuda.synchronize()
+        binding.profile_enable(True)
+        for i in range(args.decode_warmup, nsteps):
+            one(i)
+        torch.cuda.synchronize()
         prof = binding.profile_read()
         binding.profile_enable(False)
-        ms = (t1 - t0) * 1e3 / args.decode_steps
         res[mode] = {"steps_per_s": round(1e3 / ms, 1), "ms_per_step": round(ms, 4),
                      "kernels_avg_ms": {k: round(v[0] / v[1], 4) for k, v in prof.items() if v[1]}}
-        outs[mode] = (out.clone(), banks[0] if mode == "donated" else banks[cur])
+    # graph replay (donated): the timed steps captured once into a HIP graph and replayed; checked bit for bit
+    # against the same steps run eagerly from the same bank
+    g_bank = bank0.clone()
+    g_out = torch.empty((s.batch, 1, s.heads, s.head_dim), dtype=torch.float32, device=dev)
+
+    def eager_step(i):
+        a = steps[i]
+        binding.sdm_decode_step(a["wkeys"], a["rq"], a["values"], a["alpha"], a["beta"], sub, g_bank, out=g_out,
+                                **kw)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(3):
+            eager_step(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(args.decode_warmup, nsteps):
+            eager_step(i)
+    g_bank.copy_(bank0)
+    for i in range(args.decode_warmup, nsteps):
+        eager_step(i)
+    torch.cuda.synchronize()
+    ref_out, ref_bank = g_out.clone(), g_bank.clone()
+    g_bank.copy_(bank0)
+    graph.replay()
+    torch.cuda.synchronize()
+    graph_equal = bool(torch.equal(g_out, ref_out) and torch.equal(g_bank, ref_bank))
+    g_bank.copy_(bank0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    graph.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    res["graph"] = {"steps_per_s": round(args.decode_steps / (t1 - t0), 1),
+                    "ms_per_step": round((t1 - t0) * 1e3 / args.decode_steps, 4), "equals_eager_bitwise": graph_equal}
+    del graph
     equal = bool(torch.equal(outs["donated"][0], outs["copied"][0]) and torch.equal(outs["donated"][1],
                                                                                     outs["copied"][1]))
     sb = 4
@@ -247,7 +293,9 @@ def bench_decode(args, torch, binding, synth):
     return {
         "workload": "decode_b128: B128 streams x 1 token, H2 d256 N1024 (2x32) W=R=64, fp32 bank",
         "steps_per_s": res["donated"]["steps_per_s"], "steps_per_s_copied": res["copied"]["steps_per_s"],
-        "donated": res["donated"], "copied": res["copied"], "donated_equals_copied_bitwise": equal,
+        "steps_per_s_graph_replay": res["graph"]["steps_per_s"],
+        "donated": res["donated"], "copied": res["copied"], "graph_replay": res["graph"],
+        "donated_equals_copied_bitwise": equal,
         "warmup": args.decode_warmup, "steps": args.decode_steps,
         "decode_kernel_hbm_frac": round(per_step / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if dms else None,
     }

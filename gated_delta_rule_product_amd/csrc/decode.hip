@@ -174,8 +174,9 @@ hipError_t launch_decode(const Dims& D, const DecodeArgs& a, hipStream_t st) {
 }
 
 // ------------------------------------------------------------------------------------------- one-launch step
-// The step in one workgroup per stream (b, h): the block builds both candidate tables in LDS, waves 0 and 1
-// compute the write and read top-k (wave_topk_single), then all four waves gather, update and read the rows in
+// The step in one workgroup per stream (b, h): the block builds both candidate tables in LDS, the four waves
+// score and select the factors of both queries, waves 0 and 1 merge them into the write and read top-k, then all
+// four waves gather, update and read the rows in
 // column passes of 64 lanes x 16 bytes: wave w takes write rows and read rows w, w + 4, ... (W, R <= 64). All row
 // loads of a pass come from bank_in and complete before any row of the pass is written; a read row whose slot is
 // also written this step is updated in registers with the same arithmetic and rounding as the stored row, so the
@@ -183,11 +184,11 @@ hipError_t launch_decode(const Dims& D, const DecodeArgs& a, hipStream_t st) {
 // copied one bit for bit. r and out are summed per wave in row order, then over the waves in order.
 struct StepLds {
   uint64_t* ctab[2];
-  int* cscratch;
+  int* offs[2];
   float* fsc[2];
   uint16_t* fid[2];
-  uint64_t* scratch[2];
-  uint64_t* sorted[2];
+  uint64_t* scratch[4];  // per wave
+  uint64_t* sorted[4];
   int32_t *wid, *rid, *rmatch;
   float *wwt, *rwt;
   float* part;  // [4][64 EPL]
@@ -202,16 +203,18 @@ __host__ __device__ inline StepLds step_lds(unsigned char* base, const Dims& D, 
     o = (o + b + 15) & ~(size_t)15;
     return p;
   };
-  const int nc = P[0].ncand > P[1].ncand ? P[0].ncand : P[1].ncand;
-  const int kp0 = P[0].kp[0] > P[1].kp[0] ? P[0].kp[0] : P[1].kp[0];
-  for (int q = 0; q < 2; ++q) L.ctab[q] = (uint64_t*)take((size_t)nc * 8);
-  L.cscratch = (int*)take((size_t)(kp0 + 1) * 4);
+  int KS = 0;
   for (int q = 0; q < 2; ++q) {
-    const int KS = P[q].kpmax > P[q].k ? P[q].kpmax : P[q].k;
+    L.ctab[q] = (uint64_t*)take((size_t)P[q].ncand * 8);
+    L.offs[q] = (int*)take((size_t)(P[q].kp[0] + 1) * 4);
     L.fsc[q] = (float*)take((size_t)D.F * P[q].kpmax * 4);
     L.fid[q] = (uint16_t*)take((size_t)D.F * P[q].kpmax * 2);
-    L.scratch[q] = (uint64_t*)take((size_t)(KS + 8) * 8);
-    L.sorted[q] = (uint64_t*)take((size_t)KS * 8);
+    const int ks = P[q].kpmax > P[q].k ? P[q].kpmax : P[q].k;
+    KS = ks > KS ? ks : KS;
+  }
+  for (int w = 0; w < 4; ++w) {
+    L.scratch[w] = (uint64_t*)take((size_t)(KS + 8) * 8);
+    L.sorted[w] = (uint64_t*)take((size_t)KS * 8);
   }
   L.wid = (int32_t*)take((size_t)D.W * 4);
   L.wwt = (float*)take((size_t)D.W * 4);
@@ -253,22 +256,41 @@ __global__ __launch_bounds__(STEP_NT) void decode_step_kernel(Dims D, DecodeArgs
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int st = blockIdx.x;  // stream b * H + h; with one token the [B, 1, H] row index equals st
   const int h = st % D.H;
-  build_cand_table<STEP_NT>(a.plan[0], D.F, L.ctab[0], L.cscratch);
-  build_cand_table<STEP_NT>(a.plan[1], D.F, L.ctab[1], L.cscratch);
-  if (wv < 2) {
-    const int kind = wv;
-    long long sumn = 0;
-    for (int f = 0; f < D.F; ++f) sumn += D.widths[f];
-    const A* qv = (const A*)(kind ? a.queries[1] : a.queries[0]) + (long long)st * D.F * D.dk;
-    const A* sub = (const A*)a.subkeys + (long long)h * sumn * D.dk;
-    int32_t* ids = kind ? L.rid : L.wid;
-    float* wts = kind ? L.rwt : L.wwt;
-    // (members selected by kind, not indexed: a runtime index into a struct's array puts the struct in scratch)
+  // (members picked by kind or wave with conditionals, not indexed: a runtime index into a struct's array puts the
+  // struct in scratch memory)
+  auto pick2 = [](auto x0, auto x1, int i) { return i ? x1 : x0; };
+  auto pick4 = [](auto x0, auto x1, auto x2, auto x3, int i) { return i < 2 ? (i ? x1 : x0) : (i == 2 ? x2 : x3); };
+  // candidate tables: threads 0-127 build the write table, 128-255 the read table
+  {
+    const int kind = tid >> 7, t = tid & 127;
     const TopkPlan& P = kind ? a.plan[1] : a.plan[0];
-    wave_topk_single<A, NPL, CPL>(D, P, kind ? L.ctab[1] : L.ctab[0], qv, sub, kind ? L.fsc[1] : L.fsc[0],
-                                  kind ? L.fid[1] : L.fid[0], kind ? L.scratch[1] : L.scratch[0],
-                                  kind ? L.sorted[1] : L.sorted[0], ids, wts);
-    int32_t* uid = kind ? a.user_ids[1] : a.user_ids[0];
+    cand_offsets(P, D.F, pick2(L.offs[0], L.offs[1], kind), t, 128);
+    __syncthreads();
+    cand_emit(P, D.F, pick2(L.offs[0], L.offs[1], kind), pick2(L.ctab[0], L.ctab[1], kind), t, 128);
+  }
+  // factor top-k of both queries: task kind * F + f on wave task % 4
+  uint64_t* wscr = pick4(L.scratch[0], L.scratch[1], L.scratch[2], L.scratch[3], wv);
+  uint64_t* wsrt = pick4(L.sorted[0], L.sorted[1], L.sorted[2], L.sorted[3], wv);
+  long long sumn = 0;
+  for (int f = 0; f < D.F; ++f) sumn += D.widths[f];
+  const A* subh = (const A*)a.subkeys + (long long)h * sumn * D.dk;
+  for (int task = wv; task < 2 * D.F; task += 4) {
+    const int kind = task / D.F, f = task % D.F;
+    long long off = 0;
+    for (int g = 0; g < f; ++g) off += D.widths[g];
+    const TopkPlan& P = kind ? a.plan[1] : a.plan[0];
+    const A* qv = (const A*)pick2(a.queries[0], a.queries[1], kind) + (long long)st * D.F * D.dk;
+    wave_factor_topk<A, NPL>(D, P, f, qv, subh + off * D.dk, pick2(L.fsc[0], L.fsc[1], kind),
+                             pick2(L.fid[0], L.fid[1], kind), wscr, wsrt);
+  }
+  __syncthreads();  // factor lists and candidate tables complete
+  if (wv < 2) {  // merges: wave 0 the write query, wave 1 the read query
+    const int kind = wv;
+    const TopkPlan& P = kind ? a.plan[1] : a.plan[0];
+    int32_t* ids = kind ? L.rid : L.wid;
+    wave_merge_topk<CPL>(D, P, pick2(L.ctab[0], L.ctab[1], kind), pick2(L.fsc[0], L.fsc[1], kind),
+                         pick2(L.fid[0], L.fid[1], kind), wscr, wsrt, ids, kind ? L.rwt : L.wwt);
+    int32_t* uid = pick2(a.user_ids[0], a.user_ids[1], kind);
     if (uid)
       for (int r = lane; r < P.k; r += 64) uid[(long long)st * P.k + r] = ids[r];
   }

@@ -90,6 +90,50 @@ __device__ void build_cand_table(const TopkPlan& P, int F, uint64_t* out, int* s
   __syncthreads();
 }
 
+// The same table built by NT threads without a serial step, in two phases with a block barrier between them
+// (the caller's). Phase 1: thread t computes the output offset of first positions p_0 = t, t + NT, ... as the sum
+// of the counts of the smaller first positions, offs[p_0], and offs[kp[0]] = ncand. Phase 2: two factors, every
+// entry e by one thread (its first position found by binary search in offs); otherwise every first position's
+// tuples by one thread. offs: >= kp[0] + 1 ints (LDS).
+// With kp[0] <= 64 the first wave of the NT threads (t < 64) does phase 1 alone: one count per lane and a wave
+// prefix sum (lane shuffles).
+__device__ inline void cand_offsets(const TopkPlan& P, int F, int* offs, int t, int NT) {
+  if (P.kp[0] <= 64) {
+    if (t < 64) {
+      int c = t < P.kp[0] ? cand_count_rest(P, F, P.k / (t + 1)) : 0;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(c, o, 64);
+        if (t >= o) c += y;
+      }
+      if (t < P.kp[0]) offs[t + 1] = c;  // inclusive sum of first positions <= t = offset of t + 1
+      if (t == 0) offs[0] = 0;
+    }
+    return;
+  }
+  for (int p0 = t; p0 < P.kp[0]; p0 += NT) {
+    int o = 0;
+    for (int q = 0; q < p0; ++q) o += cand_count_rest(P, F, P.k / (q + 1));
+    offs[p0] = o;
+  }
+  if (t == 0) offs[P.kp[0]] = P.ncand;
+}
+__device__ inline void cand_emit(const TopkPlan& P, int F, const int* offs, uint64_t* out, int t, int NT) {
+  if (F == 2) {
+    for (int e = t; e < P.ncand; e += NT) {
+      int lo = 0, hi = P.kp[0];  // the last p0 with offs[p0] <= e (counts are >= 1, offsets increase)
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (offs[mid] <= e) lo = mid; else hi = mid;
+      }
+      out[e] = (uint64_t)lo | ((uint64_t)(e - offs[lo]) << 16);
+    }
+    return;
+  }
+  for (int p0 = t; p0 < P.kp[0]; p0 += NT)
+    if (offs[p0] < MAX_CAND) cand_emit_rest(P, F, p0, P.k / (p0 + 1), out + offs[p0], MAX_CAND - offs[p0]);
+}
+
 // LDS bytes of one topk_query workspace (8-byte aligned regions).
 __host__ __device__ inline size_t topk_lds_bytes(int F, int dk, const TopkPlan& P) {
   size_t n = 0;

@@ -129,55 +129,56 @@ __device__ void wave_select_sorted(const uint64_t (&key)[N], int k, uint64_t* sc
   wave_sync();
 }
 
-// Exact top-k of one query by one wave (the method and its exactness: topk_device.h). Factor scores: the fp64 FMA
-// chain in coordinate order, rounded to float32, for every sub-key (NPL per lane, lane l owns l + 64 j); each
-// factor's top k_p by wave selection; then the candidate tuples of `cand` (CPL per lane) with their float32 slot
-// scores summed left to right, selected by (score, position sum, candidate index). Writes ids[r] (slot ids, best
-// first) and wts[r] (softmax of the k slot scores: fp64 exponentials, per-lane partial sums in a fixed order and a
-// fixed butterfly) to LDS. fsc/fid: [F][kpmax] LDS; scratch and sorted: this wave's selection buffers.
-template <typename A, int NPL, int CPL>
-__device__ void wave_topk_single(const Dims& D, const TopkPlan& P, const uint64_t* cand, const A* qv, const A* sub,
-                                 float* fsc, uint16_t* fid, uint64_t* scratch, uint64_t* sorted, int32_t* ids,
-                                 float* wts) {
+// Exact top-k of one query (the method and its exactness: topk_device.h), in two parts that may run on different
+// waves. wave_factor_topk: factor f's scores (the fp64 FMA chain in coordinate order, rounded to float32) for every
+// sub-key (NPL per lane, lane l owns l + 64 j) and its top k_p by wave selection, into fsc/fid[f * kpmax + p].
+// wave_merge_topk: the candidate tuples of `cand` (CPL per lane) with float32 slot scores summed left to right,
+// selected by (score, position sum, candidate index); writes ids[r] (slot ids, best first) and wts[r] (softmax of
+// the k slot scores: fp64 exponentials, per-lane partial sums in a fixed order and a fixed butterfly) to LDS.
+// scratch and sorted: the calling wave's selection buffers.
+template <typename A, int NPL>
+__device__ void wave_factor_topk(const Dims& D, const TopkPlan& P, int f, const A* qv, const A* tab, float* fsc,
+                                 uint16_t* fid, uint64_t* scratch, uint64_t* sorted) {
   constexpr int VEC = Vec16<A>::N;
   const int lane = lane_id();
-  const int F = D.F, dk = D.dk, k = P.k, kpmax = P.kpmax;
-  long long off = 0;
-  for (int f = 0; f < F; ++f) {
-    const int n = D.widths[f];
-    const A* tab = sub + off * dk;
-    double acc[NPL];
+  const int dk = D.dk, n = D.widths[f], kpmax = P.kpmax;
+  double acc[NPL];
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) acc[j] = 0.0;
-    for (int c0 = 0; c0 < dk; c0 += VEC) {
-      uint4 rv[NPL];
-#pragma unroll
-      for (int j = 0; j < NPL; ++j) {
-        const int i = lane + 64 * j;
-        rv[j] = i < n ? *(const uint4*)(tab + (long long)i * dk + c0) : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const double x = to_d<A>(qv[f * dk + c0 + e]);
-#pragma unroll
-        for (int j = 0; j < NPL; ++j) acc[j] = fma(x, Vec16<A>::at(rv[j], e), acc[j]);
-      }
-    }
-    uint64_t key[NPL];
+  for (int j = 0; j < NPL; ++j) acc[j] = 0.0;
+  for (int c0 = 0; c0 < dk; c0 += VEC) {
+    uint4 rv[NPL];
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
       const int i = lane + 64 * j;
-      key[j] = i < n ? (((uint64_t)desc_key((float)acc[j]) << 32) | (uint32_t)i) : ~0ull;
+      rv[j] = i < n ? *(const uint4*)(tab + (long long)i * dk + c0) : make_uint4(0, 0, 0, 0);
     }
-    wave_select_sorted<NPL>(key, P.kp[f], scratch, sorted);
-    for (int p = lane; p < P.kp[f]; p += 64) {
-      const uint64_t kk = sorted[p];
-      fsc[f * kpmax + p] = desc_key_value((uint32_t)(kk >> 32));
-      fid[f * kpmax + p] = (uint16_t)(uint32_t)kk;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const double x = to_d<A>(qv[f * dk + c0 + e]);
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) acc[j] = fma(x, Vec16<A>::at(rv[j], e), acc[j]);
     }
-    wave_sync();
-    off += n;
   }
+  uint64_t key[NPL];
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) {
+    const int i = lane + 64 * j;
+    key[j] = i < n ? (((uint64_t)desc_key((float)acc[j]) << 32) | (uint32_t)i) : ~0ull;
+  }
+  wave_select_sorted<NPL>(key, P.kp[f], scratch, sorted);
+  for (int p = lane; p < P.kp[f]; p += 64) {
+    const uint64_t kk = sorted[p];
+    fsc[f * kpmax + p] = desc_key_value((uint32_t)(kk >> 32));
+    fid[f * kpmax + p] = (uint16_t)(uint32_t)kk;
+  }
+  wave_sync();
+}
+
+template <int CPL>
+__device__ void wave_merge_topk(const Dims& D, const TopkPlan& P, const uint64_t* cand, const float* fsc,
+                                const uint16_t* fid, uint64_t* scratch, uint64_t* sorted, int32_t* ids, float* wts) {
+  const int lane = lane_id();
+  const int F = D.F, k = P.k, kpmax = P.kpmax;
   uint64_t ck[CPL];
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {

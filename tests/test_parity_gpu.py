@@ -397,6 +397,86 @@ def test_decode_shapes(d, W, R, widths, dk, act, bank):
         ref_bank = ref["bank"]
 
 
+def test_decode_graph_replay_equals_eager():
+    """Decode steps captured into a HIP graph (the C ABI allocates nothing and never synchronises) replay to the
+    same bits as the eager calls; several replays with eager work and synchronisations between them."""
+    s = synth.WORKLOADS["decode_b128"].with_(batch=8)
+    sub = to_dev(synth.make_subkeys(s), torch.float32)
+    bank0 = to_dev(synth.make_bank(s), torch.float32)
+    steps = [_decode_inputs(s, i)[0] for i in range(4)]
+    cfg = binding.make_config(s.batch, 1, s.heads, s.widths, s.subkey_dim, s.head_dim, s.num_writes, s.num_reads, 1)
+    ws = torch.empty(binding.workspace_size(cfg, binding.SDM_OP_DECODE), dtype=torch.uint8, device=DEV)
+    bank = bank0.clone()
+    out = torch.empty((s.batch, 1, s.heads, s.head_dim), dtype=torch.float32, device=DEV)
+    kw = dict(widths=s.widths, num_writes=s.num_writes, num_reads=s.num_reads, out=out, workspace=ws)
+
+    def run(lo, hi):
+        for t in steps[lo:hi]:
+            binding.sdm_decode_step(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"], sub, bank, **kw)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(0, 1)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(1, 4)
+    bank.copy_(bank0)
+    run(1, 4)
+    torch.cuda.synchronize()
+    ref_out, ref_bank = out.clone(), bank.clone()
+    for rep in range(3):
+        bank.copy_(bank0)
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(bank, ref_bank), f"replay {rep} differs"
+        run(0, 1)  # eager work between replays
+        torch.cuda.synchronize()
+
+
+def test_write_read_graph_replay_equals_eager():
+    s = synth.WORKLOADS["tiny_1k"].with_(tokens=160, batch=2, heads=2, chunk_size=32, act="bf16")
+    x = synth.make_inputs(s, seed=15)
+    t = {k: to_dev(x[k], torch.bfloat16) for k in ("wkeys", "rq", "values", "alpha", "beta", "subkeys")}
+    bank0 = to_dev(x["bank"], torch.float32)
+    cfg = binding.make_config(s.batch, s.tokens, s.heads, s.widths, s.subkey_dim, s.head_dim, s.num_writes,
+                              s.num_reads, s.chunk_size, binding.SDM_BF16, binding.SDM_F32)
+    ws = torch.empty(binding.workspace_size(cfg, binding.SDM_OP_WRITE_READ), dtype=torch.uint8, device=DEV)
+    bank = bank0.clone()
+    out = torch.empty((s.batch, s.tokens, s.heads, s.head_dim), dtype=torch.bfloat16, device=DEV)
+
+    def run():
+        binding.sdm_write_read(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"], t["subkeys"], bank,
+                               widths=s.widths, num_writes=s.num_writes, num_reads=s.num_reads,
+                               chunk_size=s.chunk_size, out=out, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    bank.copy_(bank0)
+    run()
+    torch.cuda.synchronize()
+    ref_out, ref_bank = out.clone(), bank.clone()
+    for rep in range(3):
+        bank.copy_(bank0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(bank, ref_bank), f"replay {rep} differs"
+        run()  # eager work between replays (advances the bank)
+        torch.cuda.synchronize()
+
+
 def test_decode_padded_pitch_donated_equals_copied():
     s = synth.WORKLOADS["decode_b128"].with_(batch=8)
     x = synth.make_inputs(s, seed=13)
