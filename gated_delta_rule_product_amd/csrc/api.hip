@@ -183,11 +183,7 @@ WsLayout layout(const Dims& D, int op) {
     return r;
   };
   L.cand = take(2 * MAX_CAND * 8);
-  {
-    size_t sumn = 0;
-    for (int f = 0; f < D.F; ++f) sumn += (size_t)D.widths[f];
-    L.snorm = take((size_t)D.H * sumn * 4);
-  }
+  L.snorm = take((size_t)D.H * D.F * 4);
   if (op == SDM_OP_DECODE) {
     const size_t nw = (size_t)D.S * D.W, nr = (size_t)D.S * D.R;
     L.widx = take(nw * 4);

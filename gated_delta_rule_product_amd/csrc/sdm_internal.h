@@ -196,7 +196,7 @@ __host__ __device__ inline int pow2_ceil(int x) {
 // ------------------------------------------------------------------------------------------- workspace layout
 struct WsLayout {
   size_t cand;                                 // uint64 [2][MAX_CAND]: write then read candidate tables
-  size_t snorm;                                // float [H][sum n_f]: sub-key norms
+  size_t snorm;                                // float [H][F]: largest sub-key norm of each factor
   size_t widx, wwt, ridx, rwt;                 // [S][T][W|R] slot ids and softmax weights, stream-major
   size_t chunks;                               // [S * nch] chunk plan regions (chunk_layout)
   size_t counts;                               // [S * nch] ChunkCounts
@@ -221,7 +221,7 @@ struct TopkArgs {
   int32_t* ids[2];       // stream-major ids or user ids
   float* vals[2];        // stream-major weights (softmax) or user scores (may be NULL)
   int32_t* user_ids[2];  // optional user ids [B,T,H,k] in stream-major mode
-  float* snorm;          // workspace [H][sum n_f]: sub-key norms for the filtered (MFMA) scoring, or NULL
+  float* snorm;          // workspace [H][F]: largest sub-key norms for the filtered (MFMA) scoring, or NULL
   int one_query_per_wave;  // few rows (a decode step): one query per wave
 };
 hipError_t launch_topk(const Dims& D, const TopkArgs& a, hipStream_t st);

@@ -92,18 +92,33 @@ __host__ __device__ inline size_t topk2_wave_lds(int F, int kpmax, int k, int QW
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-// Euclidean norms of every sub-key row (fp64 sum of squares, rounded up to float32): snorm[h][sum n_f].
-__global__ __launch_bounds__(256) void subkey_norm_kernel(const bf16_t* __restrict__ sub, int total, int dk,
-                                                          float* __restrict__ snorm) {
-  const long long i = (long long)blockIdx.y * total + blockIdx.x * 256 + threadIdx.x;
-  if (blockIdx.x * 256 + threadIdx.x >= total) return;
-  const bf16_t* r = sub + i * dk;
-  double s2 = 0.0;
-  for (int c = 0; c < dk; ++c) {
-    const double y = (double)bf16_to_f(r[c]);
-    s2 = fma(y, y, s2);
+// Largest Euclidean norm of the sub-key rows of each factor (fp64 sum of squares, rounded up to float32):
+// snmax[h][f]. One block per (factor, head); the maximum is order independent.
+__global__ __launch_bounds__(256) void subkey_maxnorm_kernel(const bf16_t* __restrict__ sub, Dims D,
+                                                             float* __restrict__ snmax) {
+  __shared__ float wmax[4];
+  const int f = blockIdx.x, h = blockIdx.y, dk = D.dk;
+  long long off = 0, sumn = 0;
+  for (int g = 0; g < D.F; ++g) {
+    if (g < f) off += D.widths[g];
+    sumn += D.widths[g];
   }
-  snorm[i] = __double2float_ru(sqrt(s2) * (1.0 + 0x1p-40));
+  const bf16_t* tab = sub + ((long long)h * sumn + off) * dk;
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < D.widths[f]; i += 256) {
+    const bf16_t* r = tab + (long long)i * dk;
+    double s2 = 0.0;
+    for (int c = 0; c < dk; ++c) {
+      const double y = (double)bf16_to_f(r[c]);
+      s2 = fma(y, y, s2);
+    }
+    m = fmaxf(m, __double2float_ru(sqrt(s2) * (1.0 + 0x1p-40)));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) snmax[h * D.F + f] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
 }
 
 __device__ __forceinline__ bf16x8_t load_bf16x8(const bf16_t* p) {
@@ -112,7 +127,8 @@ __device__ __forceinline__ bf16x8_t load_bf16x8(const bf16_t* p) {
 }
 
 // One factor of the wave's QW queries by the filtered scoring: MFMA tiles of 16 queries (nq used) x 16 sub-keys,
-// bounds, threshold, exact fp64 re-score of the kept sub-keys, exact top-k_p. Writes fsc/fid like the direct path.
+// one error bound per query (from the query norm and the factor's largest sub-key norm), thresholds, exact fp64
+// re-score of the kept sub-keys, exact top-k_p. Writes fsc/fid like the direct path.
 // Requires n % 16 == 0 and dk % 32 == 0, dk <= 128.
 template <int NPL, int QW>
 __device__ void factor_topk_filtered(const Dims& D, const TopkArgs& a, int f, int n, long long nbase,
@@ -182,30 +198,25 @@ __device__ void factor_topk_filtered(const Dims& D, const TopkArgs& a, int f, in
     });
   }
   wave_sync();
-  const float* snorm = a.snorm + nbase;
+  // E bounds |s - s^| for every sub-key of the factor (its norm <= the factor's largest norm): a true top-k_p
+  // member j has s_j >= (k_p-th largest s) >= L - E for any L with k_p sub-keys at s^ >= L, hence s^_j >= L - 2E;
+  // any sub-key below that threshold has s < L - E and is not a member (ties included)
+  const double cmax = (double)a.snorm[(long long)blockIdx.z * F + f];
   const uint64_t below = lanes_below_mask();
   for (int q = 0; q < nq; ++q) {
     const double nx = sqrt(__shfl(nx2, q, 64)) * (1.0 + 0x1p-40);
-    auto bound = [&](float sh, int i) -> double {
-      const double ni = (double)snorm[i];
-      return (dk + 2) * 0x1p-23 * nx * ni * (1.0 + 0x1p-20) + dk * 0x1p-125 * (nx + ni + 1.0);
-    };
-    double emax = 0.0;
-    bool bad = false;
+    const double E = (dk + 2) * 0x1p-23 * nx * cmax * (1.0 + 0x1p-20) + dk * 0x1p-125 * (nx + cmax + 1.0);
+    bool bad = !(E <= 1e300);
     float lmax = -INFINITY;
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
       const int i = lane + 64 * j;
       if (i < n) {
         const float sh = scs[q * 64 * NPL + i];
-        const double e = bound(sh, i);
-        bad |= !(fabsf(sh) <= 3.4028234663852886e38f) || !(e <= 1e300);
-        emax = fmax(emax, e);
+        bad |= !(fabsf(sh) <= 3.4028234663852886e38f);
         lmax = fmaxf(lmax, sh);
       }
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) emax = fmax(emax, __shfl_xor(emax, o, 64));
     const bool anybad = __ballot(bad) != 0ull;
     // Wide factors first keep only the sub-keys that can reach the k_p-th largest lane maximum of s^ (k_p <= 64
     // lanes hold a value at least that large): usually a small fraction of the factor.
@@ -218,16 +229,13 @@ __device__ void factor_topk_filtered(const Dims& D, const TopkArgs& a, int f, in
       uint32_t km1 = ((uint32_t)(lk[0] >> 32) >> sh1) <= (r1 >> sh1) ? (uint32_t)(lk[0] >> 32) : 0u;
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) km1 = max(km1, (uint32_t)__shfl_xor((int)km1, o, 64));
-      const float thrA = (anybad || kp > 64) ? -INFINITY : __double2float_rd((double)desc_key_value(km1) - emax);
+      const float thrA =
+          (anybad || kp > 64) ? -INFINITY : __double2float_rd((double)desc_key_value(km1) - 2.0 * E);
       mA = 0;
 #pragma unroll
       for (int j = 0; j < NPL; ++j) {
         const int i = lane + 64 * j;
-        bool kept = false;
-        if (i < n) {
-          const float sh = scs[q * 64 * NPL + i];
-          kept = anybad || __double2float_ru((double)sh + bound(sh, i)) >= thrA;
-        }
+        const bool kept = i < n && (anybad || scs[q * 64 * NPL + i] >= thrA);
         const uint64_t bm = __ballot(kept);
         if (kept) klist[mA + __popcll(bm & below)] = (uint16_t)i;
         mA += __popcll(bm);
@@ -235,21 +243,17 @@ __device__ void factor_topk_filtered(const Dims& D, const TopkArgs& a, int f, in
       wave_sync();
     }
     // approximate keys of the candidates, the k_p best approximate scores (radix select, stopped once decided),
-    // v = the smallest of them; keep every candidate whose upper bound reaches v - E_max
+    // v = the smallest of them; keep every candidate with s^ >= v - 2E
     auto stage_b = [&](auto nsc) -> int {
       constexpr int NS = decltype(nsc)::value;
       uint64_t key[NS];
-      float hiv[NS];
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
         const int r = lane + 64 * j;
         key[j] = ~0ull;
-        hiv[j] = -INFINITY;
         if (r < mA) {
           const int i = NPL >= 8 ? (int)klist[r] : r;
-          const float sh = scs[q * 64 * NPL + i];
-          key[j] = ((uint64_t)desc_key(sh) << 32) | (uint32_t)i;
-          hiv[j] = __double2float_ru((double)sh + bound(sh, i));
+          key[j] = ((uint64_t)desc_key(scs[q * 64 * NPL + i]) << 32) | (uint32_t)i;
         }
       }
       bool all[NS];
@@ -265,12 +269,12 @@ __device__ void factor_topk_filtered(const Dims& D, const TopkArgs& a, int f, in
       }
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
-      const float thr = anybad ? -INFINITY : __double2float_rd((double)desc_key_value(kmax) - emax);
+      const float thr = anybad ? -INFINITY : __double2float_rd((double)desc_key_value(kmax) - 2.0 * E);
       wave_sync();  // every lane has read its candidates before the kept list overwrites them
       int m = 0;
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
-        const bool kept = key[j] != ~0ull && (anybad || hiv[j] >= thr);
+        const bool kept = key[j] != ~0ull && (anybad || desc_key_value((uint32_t)(key[j] >> 32)) >= thr);
         const uint64_t bm = __ballot(kept);
         if (kept) klist[m + __popcll(bm & below)] = (uint16_t)(uint32_t)key[j];
         m += __popcll(bm);
@@ -551,10 +555,8 @@ static bool launch_topk2(const Dims& D, const TopkArgs& a, hipStream_t st) {
   }
   if (lds > 128 * 1024) return false;
   if (mf) {
-    int sumn = 0;
-    for (int f = 0; f < D.F; ++f) sumn += D.widths[f];
-    dim3 g((unsigned)((sumn + 255) / 256), (unsigned)D.H);
-    hipLaunchKernelGGL(subkey_norm_kernel, g, dim3(256), 0, st, (const bf16_t*)a.subkeys, sumn, D.dk, a.snorm);
+    hipLaunchKernelGGL(subkey_maxnorm_kernel, dim3((unsigned)D.F, (unsigned)D.H), dim3(256), 0, st,
+                       (const bf16_t*)a.subkeys, D, a.snorm);
   }
   switch (npl) {
     case 1: return launch_topk2_npl<A, 1>(D, a, st, cpl, lds, mf);
