@@ -405,7 +405,7 @@ static void step_shape(const Dims& D, const DecodeArgs& a, int* npl, int* cpl) {
   *npl = 1;
   while (*npl * 64 < nfmax) *npl <<= 1;
   const int nc = a.plan[0].ncand > a.plan[1].ncand ? a.plan[0].ncand : a.plan[1].ncand;
-  *cpl = nc <= 512 ? 8 : 16;
+  *cpl = nc <= 256 ? 4 : nc <= 512 ? 8 : 16;
 }
 
 bool decode_step_fits(const Dims& D, const DecodeArgs& a) {
@@ -432,9 +432,15 @@ static hipError_t launch_step_t(const Dims& D, const DecodeArgs& a, hipStream_t 
   int npl, cpl;
   step_shape(D, a, &npl, &cpl);
   const size_t lds = step_lds(nullptr, D, a.plan, DLane<Bk>::EPL).bytes;
-  if (npl == 1) cpl == 8 ? launch_step_k<A, Bk, 1, 8>(D, a, lds, st) : launch_step_k<A, Bk, 1, 16>(D, a, lds, st);
-  else if (npl == 2) cpl == 8 ? launch_step_k<A, Bk, 2, 8>(D, a, lds, st) : launch_step_k<A, Bk, 2, 16>(D, a, lds, st);
-  else cpl == 8 ? launch_step_k<A, Bk, 4, 8>(D, a, lds, st) : launch_step_k<A, Bk, 4, 16>(D, a, lds, st);
+  auto go = [&](auto nplc) {
+    constexpr int NPL = decltype(nplc)::value;
+    if (cpl == 4) launch_step_k<A, Bk, NPL, 4>(D, a, lds, st);
+    else if (cpl == 8) launch_step_k<A, Bk, NPL, 8>(D, a, lds, st);
+    else launch_step_k<A, Bk, NPL, 16>(D, a, lds, st);
+  };
+  if (npl == 1) go(std::integral_constant<int, 1>{});
+  else if (npl == 2) go(std::integral_constant<int, 2>{});
+  else go(std::integral_constant<int, 4>{});
   return hipGetLastError();
 }
 

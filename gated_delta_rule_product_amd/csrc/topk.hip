@@ -491,20 +491,23 @@ static bool launch_topk2_npl(const Dims& D, const TopkArgs& a, hipStream_t st, i
   const long long BT = (long long)D.B * D.T;
   const long long tiles = (BT + QW - 1) / QW;
   dim3 grid((unsigned)((tiles + 3) / 4), (unsigned)a.nkinds, (unsigned)D.H);
+  auto go = [&](auto mfc, auto qw1c) {
+    constexpr bool MFV = decltype(mfc)::value, QW1V = decltype(qw1c)::value;
+    if (cpl == 4) launch_topk2_k<A, NPL, 4, MFV, QW1V>(grid, lds, st, D, a);
+    else if (cpl == 8) launch_topk2_k<A, NPL, 8, MFV, QW1V>(grid, lds, st, D, a);
+    else launch_topk2_k<A, NPL, 16, MFV, QW1V>(grid, lds, st, D, a);
+  };
   if (a.one_query_per_wave) {
-    if (cpl == 8) launch_topk2_k<A, NPL, 8, false, true>(grid, lds, st, D, a);
-    else launch_topk2_k<A, NPL, 16, false, true>(grid, lds, st, D, a);
+    go(std::false_type{}, std::true_type{});
     return true;
   }
   if constexpr (sizeof(A) == 2) {
     if (mf) {
-      if (cpl == 8) launch_topk2_k<A, NPL, 8, true, false>(grid, lds, st, D, a);
-      else launch_topk2_k<A, NPL, 16, true, false>(grid, lds, st, D, a);
+      go(std::true_type{}, std::false_type{});
       return true;
     }
   }
-  if (cpl == 8) launch_topk2_k<A, NPL, 8, false, false>(grid, lds, st, D, a);
-  else launch_topk2_k<A, NPL, 16, false, false>(grid, lds, st, D, a);
+  go(std::false_type{}, std::false_type{});
   return true;
 }
 
@@ -544,7 +547,7 @@ static bool launch_topk2(const Dims& D, const TopkArgs& a, hipStream_t st) {
   }
   if (ncand > 1024 || kpmax > 1024) return false;
   if ((D.dk * (int)sizeof(A)) % 16 != 0 || ((uintptr_t)a.subkeys) % 16 != 0) return false;
-  const int cpl = ncand <= 512 ? 8 : 16;
+  const int cpl = ncand <= 256 ? 4 : ncand <= 512 ? 8 : 16;
   const bool mf = !a.one_query_per_wave && topk_filtered(D, a);
   const int QW = a.one_query_per_wave ? 1 : wave_qw(npl, mf);
   size_t lds = 0;

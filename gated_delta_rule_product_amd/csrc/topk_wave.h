@@ -74,30 +74,39 @@ __device__ __forceinline__ uint32_t radix_select32(const uint64_t (&key)[N], con
   return res;
 }
 
-// Selects the k smallest of the wave's keys (key[j] of every lane; unused slots hold ~0ull, k <= number of used
-// slots), writes them ascending to out[0..k). scratch: >= k + 8 entries of this wave's LDS, not overlapping out.
-// Wave-uniform k.
+// Selects the k smallest of the wave's keys (key[j] of every lane; unused slots hold ~0ull, which no used key
+// equals; k <= number of used slots), writes them ascending to out[0..k). scratch: >= k + 8 entries of this wave's
+// LDS, not overlapping out. Wave-uniform k.
 template <int N>
 __device__ void wave_select_sorted(const uint64_t (&key)[N], int k, uint64_t* scratch, uint64_t* out) {
   bool all[N];
+  int nused = 0;
 #pragma unroll
-  for (int j = 0; j < N; ++j) all[j] = true;
+  for (int j = 0; j < N; ++j) {
+    all[j] = true;
+    nused += __popcll(__ballot(key[j] != ~0ull));
+  }
   int need = k, shift = 0, csize = 64 * N;
-  const uint32_t hi = radix_select32<N, true>(key, all, &need, &shift, &csize);
   bool sel[N];
-  if (csize == need) {  // decided on the high halves
+  if (nused == k) {  // every used key is selected (e.g. k_p = n_f): only the order is left to find
 #pragma unroll
-    for (int j = 0; j < N; ++j) sel[j] = ((uint32_t)(key[j] >> 32) >> shift) <= (hi >> shift);
-  } else {              // equal high halves straddle the cut: select among them on the low halves
-    bool tie[N];
+    for (int j = 0; j < N; ++j) sel[j] = key[j] != ~0ull;
+  } else {
+    const uint32_t hi = radix_select32<N, true>(key, all, &need, &shift, &csize);
+    if (csize == need) {  // decided on the high halves
 #pragma unroll
-    for (int j = 0; j < N; ++j) tie[j] = (uint32_t)(key[j] >> 32) == hi;
-    int need2 = need, shift2 = 0, csize2 = csize;
-    const uint32_t lo = radix_select32<N, false>(key, tie, &need2, &shift2, &csize2);
+      for (int j = 0; j < N; ++j) sel[j] = ((uint32_t)(key[j] >> 32) >> shift) <= (hi >> shift);
+    } else {              // equal high halves straddle the cut: select among them on the low halves
+      bool tie[N];
 #pragma unroll
-    for (int j = 0; j < N; ++j) {
-      const uint32_t h = (uint32_t)(key[j] >> 32);
-      sel[j] = h < hi || (h == hi && ((uint32_t)key[j] >> shift2) <= (lo >> shift2));
+      for (int j = 0; j < N; ++j) tie[j] = (uint32_t)(key[j] >> 32) == hi;
+      int need2 = need, shift2 = 0, csize2 = csize;
+      const uint32_t lo = radix_select32<N, false>(key, tie, &need2, &shift2, &csize2);
+#pragma unroll
+      for (int j = 0; j < N; ++j) {
+        const uint32_t h = (uint32_t)(key[j] >> 32);
+        sel[j] = h < hi || (h == hi && ((uint32_t)key[j] >> shift2) <= (lo >> shift2));
+      }
     }
   }
   // compaction
