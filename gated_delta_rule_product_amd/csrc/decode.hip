@@ -295,12 +295,16 @@ __global__ __launch_bounds__(STEP_NT) void decode_step_kernel(Dims D, DecodeArgs
       for (int r = lane; r < P.k; r += 64) uid[(long long)st * P.k + r] = ids[r];
   }
   __syncthreads();
-  // read slots that are also written this step (the slots of one top-k are distinct)
-  for (int j = tid; j < D.R; j += STEP_NT) {
-    const int s = L.rid[j];
+  // read slots that are also written this step (the slots of one top-k are distinct): read slot j is compared
+  // with the write slots by the 4 consecutive threads 4 j .. 4 j + 3, each scanning a quarter, then combined
+  for (int j0 = 0; j0 < D.R; j0 += STEP_NT / 4) {
+    const int j = j0 + (tid >> 2), qt = tid & 3;
+    const int s = j < D.R ? L.rid[j] : -1;
     int mi = -1;
-    for (int i = 0; i < D.W; ++i) mi = L.wid[i] == s ? i : mi;
-    L.rmatch[j] = mi;
+    for (int i = qt; i < D.W; i += 4) mi = L.wid[i] == s ? i : mi;
+    mi = max(mi, __shfl_xor(mi, 1, 64));
+    mi = max(mi, __shfl_xor(mi, 2, 64));
+    if (qt == 0 && j < D.R) L.rmatch[j] = mi;
   }
   __syncthreads();
   const float al = to_f<A>(((const A*)a.alpha)[st]);
@@ -312,6 +316,10 @@ __global__ __launch_bounds__(STEP_NT) void decode_step_kernel(Dims D, DecodeArgs
   for (int c0 = 0; c0 < D.d; c0 += COLW) {
     const int col = c0 + lane * EPL;
     const bool valid = col < D.d;
+    // the value piece first (used after the barrier below; loaded now so that its latency hides behind the rows)
+    float va[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) va[e] = valid ? to_f<A>(((const A*)a.values)[(long long)st * D.d + col + e]) : 0.0f;
     w16_t wr[STEP_RPW], rr[STEP_RPW];
     static_for<STEP_RPW>([&](auto u) {
       const int i = wv + 4 * u;
@@ -349,7 +357,7 @@ __global__ __launch_bounds__(STEP_NT) void decode_step_kernel(Dims D, DecodeArgs
     for (int e = 0; e < EPL; ++e) {
       const int c = lane * EPL + e;
       const float r = part[c] + part[COLW + c] + part[2 * COLW + c] + part[3 * COLW + c];
-      dl[e] = valid ? be * (to_f<A>(((const A*)a.values)[(long long)st * D.d + col + e]) - al * r) : 0.0f;
+      dl[e] = valid ? be * (va[e] - al * r) : 0.0f;
     }
     __syncthreads();  // every wave has read the partial sums
     // M[S_i] <- alpha M[S_i] + w_i delta, rounded to the bank dtype, into the successor
