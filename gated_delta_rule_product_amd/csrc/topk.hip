@@ -69,9 +69,9 @@ template <int NPL, bool MF = false> struct WaveTile { static constexpr int QW = 
 
 // Per-wave LDS: factor scores [QW][64 NPL] (float), kept factor lists [QW][F][kpmax] (float score + uint16 id),
 // selection scratch [KS + 8] and sorted output [KS] (uint64).
-__host__ __device__ inline size_t topk2_wave_lds(int F, int kpmax, int k, int QW, int NPL) {
+__host__ __device__ inline size_t topk2_wave_lds(int F, int kpmax, int k, int QW, int NPL, bool shared_scores = false) {
   const int KS = kpmax > k ? kpmax : k;
-  size_t n = (size_t)QW * 64 * NPL * 4;
+  size_t n = shared_scores ? 0 : (size_t)QW * 64 * NPL * 4;
   n += (size_t)QW * F * kpmax * 6;
   n = (n + 7) & ~(size_t)7;
   return n + (size_t)(2 * KS + 8) * 8 + (size_t)64 * NPL * 2;  // + kept-candidate list (filtered scoring)
@@ -130,26 +130,35 @@ __device__ __forceinline__ bf16x8_t load_bf16x8(const bf16_t* p) {
 // one error bound per query (from the query norm and the factor's largest sub-key norm), thresholds, exact fp64
 // re-score of the kept sub-keys, exact top-k_p. Writes fsc/fid like the direct path.
 // Requires n % 16 == 0 and dk % 32 == 0, dk <= 128.
-template <int NPL, int QW>
-__device__ void factor_topk_filtered(const Dims& D, const TopkArgs& a, int f, int n, long long nbase,
-                                     const bf16_t* tab, const bf16_t* qf, long long qstride, int nq, float* scs,
-                                     float* fsc, uint16_t* fid, uint64_t* scratch, uint64_t* sorted,
-                                     uint16_t* klist, int kpmax) {
+//
+// Block mode (NW > 1): the NW waves of the workgroup hold NW * QW <= 16 consecutive queries, the rows of one MFMA
+// tile; wave w computes tiles w, w + NW, ... for all of them (each sub-key tile is read once per workgroup) into
+// the shared score buffer scs [16][64 NPL]; qb/nqb are the workgroup's first query and query count, row0 the
+// wave's first row, and qf/nq the wave's own queries. Every wave calls this (nq may be 0): it has two barriers.
+template <int NPL, int QW, int NW = 1>
+__device__ void factor_topk_filtered(const Dims& D, const TopkArgs& a, int f, int n, const bf16_t* tab,
+                                     const bf16_t* qf, long long qstride, int nq, float* scs, float* fsc,
+                                     uint16_t* fid, uint64_t* scratch, uint64_t* sorted, uint16_t* klist, int kpmax,
+                                     const bf16_t* qb = nullptr, int nqb = 0, int row0 = 0) {
   constexpr int KBMAX = 4;
+  constexpr bool BLK = NW > 1;
   const int lane = threadIdx.x & 63;
   const int dk = D.dk, F = D.F;
   const int KB = dk / 32;
   const int ql = lane & 15, pt = lane >> 4;
   const int kind = blockIdx.y;
   const int kp = a.plan[kind].kp[f];
+  const int wv = BLK ? (int)(threadIdx.x >> 6) : 0;
+  const bf16_t* qa_base = BLK ? qb : qf;  // the MFMA rows: the workgroup's queries or the wave's
+  const int nqa = BLK ? nqb : nq;
   // query fragments (A operand: row = query, 8 consecutive elements of a 32-wide block) and squared norms
   bf16x8_t qa[KBMAX];
   double nx2 = 0.0;
   static_for<KBMAX>([&](auto kc) {
     constexpr int kb = decltype(kc)::value;
     if (kb < KB) {
-      if (ql < nq) {
-        qa[kb] = load_bf16x8(qf + ql * qstride + kb * 32 + pt * 8);
+      if (ql < nqa) {
+        qa[kb] = load_bf16x8(qa_base + ql * qstride + kb * 32 + pt * 8);
         const uint4 w = __builtin_bit_cast(uint4, qa[kb]);
         const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
@@ -167,19 +176,19 @@ __device__ void factor_topk_filtered(const Dims& D, const TopkArgs& a, int f, in
   nx2 += __shfl_xor(nx2, 32, 64);
   // MFMA scores of tile T: lane l holds queries 4 (l / 16) + r (r < 4) for sub-key 16 T + l % 16
   // tiles in batches of TB whose B-operand loads are issued together (the table sits in L2: latency, not bandwidth)
-  constexpr int TB = NPL >= 8 ? 8 : 2;
+  constexpr int TB = BLK ? 4 : NPL >= 8 ? 8 : 2;
   const int ntile = n / 16;
-  for (int T0 = 0; T0 < ntile; T0 += TB) {
+  for (int T0 = 0; T0 < ntile; T0 += TB * NW) {
     bf16x8_t bv[TB][2];
     static_for<TB>([&](auto tc) {
       constexpr int u = decltype(tc)::value;
-      const bf16_t* row = tab + (long long)(min(T0 + u, ntile - 1) * 16 + ql) * dk + pt * 8;
+      const bf16_t* row = tab + (long long)(min(T0 + u * NW + wv, ntile - 1) * 16 + ql) * dk + pt * 8;
       bv[u][0] = load_bf16x8(row);
       if (KB > 1) bv[u][1] = load_bf16x8(row + 32);
     });
     static_for<TB>([&](auto tc) {
       constexpr int u = decltype(tc)::value;
-      const int T = T0 + u;
+      const int T = T0 + u * NW + wv;
       if (T < ntile) {
         const bf16_t* row = tab + (long long)(T * 16 + ql) * dk + pt * 8;
         f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -192,19 +201,24 @@ __device__ void factor_topk_filtered(const Dims& D, const TopkArgs& a, int f, in
 #pragma unroll
         for (int r = 0; r < 4; ++r) {  // D row 4 (lane / 16) + r = query, column lane % 16 = sub-key in the tile
           const int qi = 4 * pt + r;
-          if (qi < nq) scs[qi * 64 * NPL + T * 16 + ql] = acc[r];
+          if (qi < nqa) scs[qi * 64 * NPL + T * 16 + ql] = acc[r];
         }
       }
     });
   }
-  wave_sync();
+  if constexpr (BLK) {
+    __syncthreads();  // every tile's scores in LDS
+    scs += row0 * 64 * NPL;  // this wave's queries
+  } else {
+    wave_sync();
+  }
   // E bounds |s - s^| for every sub-key of the factor (its norm <= the factor's largest norm): a true top-k_p
   // member j has s_j >= (k_p-th largest s) >= L - E for any L with k_p sub-keys at s^ >= L, hence s^_j >= L - 2E;
   // any sub-key below that threshold has s < L - E and is not a member (ties included)
   const double cmax = (double)a.snorm[(long long)blockIdx.z * F + f];
   const uint64_t below = lanes_below_mask();
   for (int q = 0; q < nq; ++q) {
-    const double nx = sqrt(__shfl(nx2, q, 64)) * (1.0 + 0x1p-40);
+    const double nx = sqrt(__shfl(nx2, row0 + q, 64)) * (1.0 + 0x1p-40);
     const double E = (dk + 2) * 0x1p-23 * nx * cmax * (1.0 + 0x1p-20) + dk * 0x1p-125 * (nx + cmax + 1.0);
     bool bad = !(E <= 1e300);
     float lmax = -INFINITY;
@@ -323,12 +337,20 @@ __device__ void factor_topk_filtered(const Dims& D, const TopkArgs& a, int f, in
     }
     wave_sync();
   }
+  if constexpr (BLK) __syncthreads();  // the next factor's tiles overwrite the shared scores
 }
+
+// Waves per workgroup: 4; the filtered scoring of wide factors uses 8 waves of 2 queries, so that one MFMA tile of 16
+// queries covers the workgroup and each sub-key tile is read once per workgroup (block mode of
+// factor_topk_filtered, scores in a shared LDS buffer).
+template <int NPL, bool MF> struct Topk2Waves { static constexpr int NW = (MF && WaveTile<NPL, true>::QW * 8 == 16) ? 8 : 4; };
 
 // QW1: one query per wave (few rows, e.g. a decode step: parallelism over queries rather than reuse of sub-key rows).
 template <typename A, int NPL, int CPL, bool MF, bool QW1>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NPL <= 4 ? 4 : 1))) void topk2_kernel(Dims D, TopkArgs a) {
+__global__ __launch_bounds__((64 * Topk2Waves<NPL, MF>::NW)) __attribute__((amdgpu_waves_per_eu(NPL <= 4 ? 4 : 1))) void topk2_kernel(Dims D, TopkArgs a) {
   constexpr int QW = QW1 ? 1 : WaveTile<NPL, MF>::QW;
+  constexpr int NW = QW1 ? 4 : Topk2Waves<NPL, MF>::NW;
+  constexpr bool BLK = NW == 8;  // block mode of the filtered scoring
   constexpr int VEC = Vec16<A>::N;
   extern __shared__ __align__(16) unsigned char lds[];
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -337,28 +359,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NPL <= 4 ? 
   const TopkPlan& P = a.plan[kind];
   const int F = D.F, dk = D.dk, k = P.k, kpmax = P.kpmax;
   const long long BT = (long long)D.B * D.T;
-  const long long bt0 = ((long long)blockIdx.x * 4 + wv) * QW;
+  const long long bt0 = ((long long)blockIdx.x * NW + wv) * QW;
   const uint64_t* cand = a.cand[kind];
+  const size_t shared_scs = BLK ? (size_t)16 * 64 * NPL * 4 : 0;  // block mode: [16][64 NPL] scores
   if constexpr (QW1) {  // few rows: the block builds its kind's candidate table itself (no separate launch)
     uint64_t* ctab = (uint64_t*)(lds + 4 * topk2_wave_lds(F, kpmax, k, QW, NPL));
     build_cand_table<256>(P, F, ctab, (int*)(ctab + P.ncand));
     cand = ctab;
   }
-  if (bt0 >= BT) return;  // no block-wide barriers below: idle waves may leave
+  if (!BLK && bt0 >= BT) return;  // no block-wide barriers below: idle waves may leave
   const int KS = kpmax > k ? kpmax : k;
-  unsigned char* wl = lds + (size_t)wv * topk2_wave_lds(F, kpmax, k, QW, NPL);
-  float* scs = (float*)wl;                                  // [QW][64 NPL]
-  float* fsc = scs + QW * 64 * NPL;                         // [QW][F][kpmax]
+  unsigned char* wl = lds + shared_scs + (size_t)wv * topk2_wave_lds(F, kpmax, k, QW, NPL, BLK);
+  float* scs = BLK ? (float*)lds : (float*)wl;              // [QW][64 NPL] (block mode: the shared buffer)
+  float* fsc = (float*)(wl + (BLK ? 0 : (size_t)QW * 64 * NPL * 4));  // [QW][F][kpmax]
   uint16_t* fid = (uint16_t*)(fsc + QW * F * kpmax);        // [QW][F][kpmax]
-  uint64_t* scratch =
-      (uint64_t*)(wl + (((size_t)QW * 64 * NPL * 4 + (size_t)QW * F * kpmax * 6 + 7) & ~(size_t)7));
+  uint64_t* scratch = (uint64_t*)(wl + (((BLK ? 0 : (size_t)QW * 64 * NPL * 4) + (size_t)QW * F * kpmax * 6 + 7) &
+                                        ~(size_t)7));
   uint64_t* sorted = scratch + KS + 8;
   uint16_t* klist = (uint16_t*)(sorted + KS);               // [64 NPL] kept candidates (filtered scoring)
   long long sumn = 0;
   for (int f = 0; f < F; ++f) sumn += D.widths[f];
   const A* sub = (const A*)a.subkeys + (long long)h * sumn * dk;
   const int Fdk = F * dk;
-  const int nq = (int)min((long long)QW, BT - bt0);
+  const int nq = (int)max(0LL, min((long long)QW, BT - bt0));
   // rows (b, t) = bt0 + q are consecutive: row index (bt0 + q) * H + h
   const A* qbase = (const A*)a.queries[kind] + ((long long)bt0 * D.H + h) * Fdk;
   const long long qstride = (long long)D.H * Fdk;
@@ -367,8 +390,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NPL <= 4 ? 
   for (int f = 0; f < F; ++f) {
     const int n = D.widths[f];
     const A* tab = sub + off * dk;
-    if constexpr (MF) {
-      factor_topk_filtered<NPL, QW>(D, a, f, n, (long long)h * sumn + off, (const bf16_t*)tab,
+    if constexpr (MF && BLK) {
+      const long long bb = (long long)blockIdx.x * NW * QW;  // the workgroup's first row
+      const bf16_t* qb = (const bf16_t*)a.queries[kind] + ((long long)bb * D.H + h) * Fdk + f * dk;
+      factor_topk_filtered<NPL, QW, NW>(D, a, f, n, (const bf16_t*)tab, (const bf16_t*)qbase + f * dk, qstride, nq,
+                                        scs, fsc, fid, scratch, sorted, klist, kpmax, qb,
+                                        (int)max(0LL, min((long long)NW * QW, BT - bb)), wv * QW);
+      off += n;
+      continue;
+    } else if constexpr (MF) {
+      factor_topk_filtered<NPL, QW>(D, a, f, n, (const bf16_t*)tab,
                                     (const bf16_t*)qbase + f * dk, qstride, nq, scs, fsc, fid, scratch, sorted,
                                     klist, kpmax);
       off += n;
@@ -482,7 +513,8 @@ template <typename A, int NPL, int CPL, bool MF, bool QW1>
 static void launch_topk2_k(dim3 grid, size_t lds, hipStream_t st, const Dims& D, const TopkArgs& a) {
   (void)hipFuncSetAttribute((const void*)topk2_kernel<A, NPL, CPL, MF, QW1>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  hipLaunchKernelGGL((topk2_kernel<A, NPL, CPL, MF, QW1>), grid, dim3(256), lds, st, D, a);
+  constexpr int NW = QW1 ? 4 : Topk2Waves<NPL, MF>::NW;
+  hipLaunchKernelGGL((topk2_kernel<A, NPL, CPL, MF, QW1>), grid, dim3(64 * NW), lds, st, D, a);
 }
 
 template <typename A, int NPL>
@@ -490,7 +522,8 @@ static bool launch_topk2_npl(const Dims& D, const TopkArgs& a, hipStream_t st, i
   const int QW = a.one_query_per_wave ? 1 : (mf ? WaveTile<NPL, true>::QW : WaveTile<NPL>::QW);
   const long long BT = (long long)D.B * D.T;
   const long long tiles = (BT + QW - 1) / QW;
-  dim3 grid((unsigned)((tiles + 3) / 4), (unsigned)a.nkinds, (unsigned)D.H);
+  const int NW = (!a.one_query_per_wave && mf) ? Topk2Waves<NPL, true>::NW : 4;
+  dim3 grid((unsigned)((tiles + NW - 1) / NW), (unsigned)a.nkinds, (unsigned)D.H);
   auto go = [&](auto mfc, auto qw1c) {
     constexpr bool MFV = decltype(mfc)::value, QW1V = decltype(qw1c)::value;
     if (cpl == 4) launch_topk2_k<A, NPL, 4, MFV, QW1V>(grid, lds, st, D, a);
@@ -550,9 +583,12 @@ static bool launch_topk2(const Dims& D, const TopkArgs& a, hipStream_t st) {
   const int cpl = ncand <= 256 ? 4 : ncand <= 512 ? 8 : 16;
   const bool mf = !a.one_query_per_wave && topk_filtered(D, a);
   const int QW = a.one_query_per_wave ? 1 : wave_qw(npl, mf);
+  // block mode of the filtered scoring (8 waves of 2 queries, shared [16][64 npl] scores) for wide factors
+  const bool blk = mf && QW * 8 == 16;
   size_t lds = 0;
   for (int q = 0; q < a.nkinds; ++q) {
-    size_t l = 4 * topk2_wave_lds(D.F, a.plan[q].kpmax, a.plan[q].k, QW, npl);
+    size_t l = blk ? (size_t)16 * 64 * npl * 4 + 8 * topk2_wave_lds(D.F, a.plan[q].kpmax, a.plan[q].k, QW, npl, true)
+                   : 4 * topk2_wave_lds(D.F, a.plan[q].kpmax, a.plan[q].k, QW, npl);
     if (a.one_query_per_wave) l += (size_t)a.plan[q].ncand * 8 + (size_t)(a.plan[q].kp[0] + 1) * 4;
     lds = l > lds ? l : lds;
   }

@@ -112,7 +112,8 @@ def test_topk_exact(widths, dk, k, kind, act):
 
 
 @pytest.mark.parametrize("widths,dk,k", [((32, 32), 32, 64), ((64, 32, 16), 64, 64), ((16,), 32, 9),
-                                         ((256, 256), 64, 64), ((48, 16), 96, 33), ((32, 32), 128, 17)])
+                                         ((256, 256), 64, 64), ((48, 16), 96, 33), ((32, 32), 128, 17),
+                                         ((512, 16), 32, 64), ((1024, 32), 64, 40)])
 @pytest.mark.parametrize("kind", ["random", "ternary", "dup"])
 @pytest.mark.parametrize("scoring", ["filtered", "direct"])
 def test_topk_exact_filtered(widths, dk, k, kind, scoring, monkeypatch):
