@@ -191,7 +191,7 @@ struct StepLds {
   uint64_t* sorted[4];
   int32_t *wid, *rid, *rmatch;
   float *wwt, *rwt;
-  float* part;  // [4][64 EPL]
+  float* part;  // [2][4][64 EPL]: the waves' partial sums of r, then of out
   size_t bytes;
 };
 
@@ -221,7 +221,7 @@ __host__ __device__ inline StepLds step_lds(unsigned char* base, const Dims& D, 
   L.rid = (int32_t*)take((size_t)D.R * 4);
   L.rwt = (float*)take((size_t)D.R * 4);
   L.rmatch = (int32_t*)take((size_t)D.R * 4);
-  L.part = (float*)take((size_t)4 * 64 * epl * 4);
+  L.part = (float*)take((size_t)2 * 4 * 64 * epl * 4);
   L.bytes = o;
   return L;
 }
@@ -359,7 +359,6 @@ __global__ __launch_bounds__(STEP_NT) void decode_step_kernel(Dims D, DecodeArgs
       const float r = part[c] + part[COLW + c] + part[2 * COLW + c] + part[3 * COLW + c];
       dl[e] = valid ? be * (va[e] - al * r) : 0.0f;
     }
-    __syncthreads();  // every wave has read the partial sums
     // M[S_i] <- alpha M[S_i] + w_i delta, rounded to the bank dtype, into the successor
     static_for<STEP_RPW>([&](auto u) {
       const int i = wv + 4 * u;
@@ -392,18 +391,19 @@ __global__ __launch_bounds__(STEP_NT) void decode_step_kernel(Dims D, DecodeArgs
         for (int e = 0; e < EPL; ++e) acc[e] += rj * m[e];
       }
     });
+    float* opart = part + 4 * COLW;  // a second buffer: no barrier needed between reading r's parts and this
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) part[wv * COLW + lane * EPL + e] = acc[e];
+    for (int e = 0; e < EPL; ++e) opart[wv * COLW + lane * EPL + e] = acc[e];
     __syncthreads();
     if (wv == 0 && valid) {
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
         const int c = lane * EPL + e;
-        const float o = part[c] + part[COLW + c] + part[2 * COLW + c] + part[3 * COLW + c];
+        const float o = opart[c] + opart[COLW + c] + opart[2 * COLW + c] + opart[3 * COLW + c];
         ((A*)a.out)[(long long)st * D.d + col + e] = from_f<A>(o);
       }
     }
-    __syncthreads();  // the partial sums are reused by the next pass
+    if (c0 + COLW < D.d) __syncthreads();  // the partial sums are reused by the next pass
   }
 }
 
