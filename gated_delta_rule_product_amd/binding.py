@@ -40,11 +40,13 @@ class SdmConfig(ctypes.Structure):
         ("head_dim", ctypes.c_int32), ("num_writes", ctypes.c_int32), ("num_reads", ctypes.c_int32),
         ("chunk_size", ctypes.c_int32), ("act_dtype", ctypes.c_int32), ("bank_dtype", ctypes.c_int32),
         ("bank_rows", ctypes.c_int64), ("bank_row_stride", ctypes.c_int64),
+        ("shared_bank", ctypes.c_int32), ("reserved", ctypes.c_int32),
     ]
 
 
 def make_config(batch, tokens, heads, widths, subkey_dim, head_dim=1, num_writes=1, num_reads=1, chunk_size=1,
-                act_dtype=SDM_F32, bank_dtype=SDM_F32, bank_rows=None, bank_row_stride=0) -> SdmConfig:
+                act_dtype=SDM_F32, bank_dtype=SDM_F32, bank_rows=None, bank_row_stride=0,
+                shared_bank=False) -> SdmConfig:
     c = SdmConfig()
     c.batch, c.tokens, c.heads = int(batch), int(tokens), int(heads)
     c.num_factors = len(widths)
@@ -58,6 +60,7 @@ def make_config(batch, tokens, heads, widths, subkey_dim, head_dim=1, num_writes
         n *= int(w)
     c.bank_rows = int(bank_rows) if bank_rows is not None else n
     c.bank_row_stride = int(bank_row_stride)
+    c.shared_bank = 1 if shared_bank else 0
     return c
 
 
@@ -112,6 +115,8 @@ def load():
             lib.sdm_write_read.argtypes = [cfgp] + [_vp] * 11 + [ctypes.c_size_t, _vp]
             lib.sdm_decode_step.restype = ctypes.c_int
             lib.sdm_decode_step.argtypes = [cfgp] + [_vp] * 12 + [ctypes.c_size_t, _vp]
+            lib.sdm_shared_bank_check.restype = ctypes.c_int
+            lib.sdm_shared_bank_check.argtypes = [cfgp, _vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int32), _vp]
             lib.sdm_profile_enable.restype = ctypes.c_int
             lib.sdm_profile_enable.argtypes = [ctypes.c_int32]
             lib.sdm_profile_read.restype = ctypes.c_int
@@ -214,9 +219,17 @@ def topk_product_keys(queries: torch.Tensor, subkeys: torch.Tensor, widths, k: i
     return ids, scores
 
 
+class SlotConflictError(ValueError):
+    """A shared-bank write/read whose streams address a common slot (the call wrote neither the bank nor out)."""
+
+
 def sdm_write_read(write_keys, read_queries, values, forget_gate, input_gate, subkeys, bank, *, widths, num_writes,
-                   num_reads, chunk_size, want_index=False, out=None, workspace=None):
-    """Chunked SDM write/read. bank [B, H, bank_rows, d] advances in place. Returns (out, write_idx, read_idx)."""
+                   num_reads, chunk_size, want_index=False, out=None, workspace=None, shared_bank=False):
+    """Chunked SDM write/read. bank [B, H, bank_rows, d] advances in place. Returns (out, write_idx, read_idx).
+
+    shared_bank=True: bank is [H, bank_rows, d], shared by the B streams of each head, whose slots must be disjoint;
+    the library checks this on the device and this function waits for the check (it synchronises the stream) and
+    raises SlotConflictError if it failed."""
     B, T, H, Fdk = write_keys.shape
     F = len(widths)
     dk = Fdk // F
@@ -226,11 +239,18 @@ def sdm_write_read(write_keys, read_queries, values, forget_gate, input_gate, su
                          ("values", values, (B, T, H, d)), ("forget_gate", forget_gate, (B, T, H)),
                          ("input_gate", input_gate, (B, T, H)), ("subkeys", subkeys, (H, sum(widths), dk))):
         _need(t, name, shp, act)
-    if bank.dim() != 4 or bank.shape[0] != B or bank.shape[1] != H or bank.shape[3] != d:
-        raise ValueError(f"bank has shape {tuple(bank.shape)}, expected ({B}, {H}, bank_rows, {d})")
-    ld = _bank_ld(bank, "bank")
+    if shared_bank:
+        if bank.dim() != 3 or bank.shape[0] != H or bank.shape[2] != d:
+            raise ValueError(f"shared bank has shape {tuple(bank.shape)}, expected ({H}, bank_rows, {d})")
+        ld = _bank_ld(bank.unsqueeze(0), "bank")
+        rows = bank.shape[1]
+    else:
+        if bank.dim() != 4 or bank.shape[0] != B or bank.shape[1] != H or bank.shape[3] != d:
+            raise ValueError(f"bank has shape {tuple(bank.shape)}, expected ({B}, {H}, bank_rows, {d})")
+        ld = _bank_ld(bank, "bank")
+        rows = bank.shape[2]
     cfg = make_config(B, T, H, widths, dk, d, num_writes, num_reads, chunk_size, _dt(write_keys), _dt(bank),
-                      bank.shape[2], ld)
+                      rows, ld, shared_bank)
     ws = _workspace(workspace_size(cfg, SDM_OP_WRITE_READ), bank.device, workspace)
     if out is None:
         out = torch.empty((B, T, H, d), dtype=act, device=bank.device)
@@ -242,6 +262,13 @@ def sdm_write_read(write_keys, read_queries, values, forget_gate, input_gate, su
                                  _ptr(forget_gate), _ptr(input_gate), _ptr(subkeys), _ptr(bank), _ptr(out),
                                  _ptr(widx), _ptr(ridx), _ptr(ws), 0 if ws is None else ws.numel(),
                                  _stream(bank.device)))
+    if shared_bank:
+        conflict = ctypes.c_int32(0)
+        _check(load().sdm_shared_bank_check(ctypes.byref(cfg), _ptr(ws), 0 if ws is None else ws.numel(),
+                                            ctypes.byref(conflict), _stream(bank.device)))
+        if conflict.value:
+            raise SlotConflictError("shared_bank=True but the streams of a head address a common slot "
+                                    "(the bank and out were not written)")
     return out, widx, ridx
 
 

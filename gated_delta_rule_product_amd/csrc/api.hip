@@ -118,6 +118,11 @@ sdm_status validate(const sdm_config* cfg, int op, int k, Dims* D, TopkPlan* pw,
   D->B = cfg->batch; D->T = cfg->tokens; D->H = cfg->heads; D->F = F; D->dk = cfg->subkey_dim;
   D->act = act; D->bank = bank; D->N = N; D->S = cfg->batch * cfg->heads;
   if (op == SDM_OP_TOPK) return make_plan(*D, k, "k", pw);
+  if (cfg->shared_bank != 0 && cfg->shared_bank != 1)
+    return fail(SDM_ERR_RANGE, "shared_bank = %d must be 0 or 1", cfg->shared_bank);
+  if (cfg->shared_bank && op != SDM_OP_WRITE_READ)
+    return fail(SDM_ERR_RANGE, "shared_bank applies to sdm_write_read only (a decode step's streams own their banks)");
+  D->shared = cfg->shared_bank;
 
   const int d = cfg->head_dim;
   if (d < 1 || d > (1 << 20)) return fail(SDM_ERR_RANGE, "head_dim = %d out of range [1, 2^20]", d);
@@ -200,6 +205,10 @@ WsLayout layout(const Dims& D, int op) {
     L.rwt = take(nr * 4);
     L.chunks = take(nc * (size_t)chunk_layout(D.C, D.W, D.R).bytes);
     L.counts = take(nc * sizeof(ChunkCounts));
+    if (D.shared) {
+      L.owner = take((size_t)D.H * (size_t)D.N * 4);
+      L.conflict = take(4);
+    }
   }
   L.total = o;
   return L;
@@ -371,7 +380,7 @@ sdm_status sdm_write_read(const sdm_config* cfg, const void* write_keys, const v
   long long sumn = 0;
   for (int f = 0; f < D.F; ++f) sumn += D.widths[f];
   const size_t ea = esize(D.act), eb = esize(D.bank);
-  const size_t bank_bytes = (size_t)D.S * (size_t)D.rows * (size_t)D.ld * eb;
+  const size_t bank_bytes = (size_t)(D.shared ? D.H : D.S) * (size_t)D.rows * (size_t)D.ld * eb;
   if (rows > 0) {
     TRY(need(write_keys, "write_keys"));
     TRY(need(read_queries, "read_queries"));
@@ -424,7 +433,15 @@ sdm_status sdm_write_read(const sdm_config* cfg, const void* write_keys, const v
   ta.user_ids[1] = read_idx;
   ta.snorm = (float*)(ws + L.snorm);
   TRY(hip_status(timed(SDM_K_TOPK, st, [&] { return launch_topk(D, ta, st); }), "top-k launch"));
+  const int32_t* abort = nullptr;
+  if (D.shared) {  // the streams of a head must address disjoint slots; if not, the plan and the loop do nothing
+    TRY(hip_status(launch_shared_check(D, (const int32_t*)(ws + L.widx), (const int32_t*)(ws + L.ridx),
+                                       (int32_t*)(ws + L.owner), (int32_t*)(ws + L.conflict), st),
+                   "shared-bank check launch"));
+    abort = (const int32_t*)(ws + L.conflict);
+  }
   PlanArgs pa;
+  pa.abort = abort;
   pa.widx = (const int32_t*)(ws + L.widx);
   pa.wwt = (const float*)(ws + L.wwt);
   pa.ridx = (const int32_t*)(ws + L.ridx);
@@ -444,7 +461,28 @@ sdm_status sdm_write_read(const sdm_config* cfg, const void* write_keys, const v
   la.counts = pa.counts;
   la.bank = bank;
   la.out = out;
+  la.abort = abort;
   TRY(hip_status(timed(SDM_K_LOOP, st, [&] { return launch_loop(D, la, st); }), "chunk loop launch"));
+  return ok();
+}
+
+sdm_status sdm_shared_bank_check(const sdm_config* cfg, const void* workspace, size_t workspace_bytes,
+                                 int32_t* conflict, void* stream) {
+  Dims D;
+  TopkPlan pw, pr;
+  TRY(validate(cfg, SDM_OP_WRITE_READ, 0, &D, &pw, &pr));
+  if (!conflict) return fail(SDM_ERR_NULL, "conflict is NULL");
+  if (!D.shared) return fail(SDM_ERR_RANGE, "cfg.shared_bank is 0: there is no shared-bank check to read");
+  const WsLayout L = layout(D, SDM_OP_WRITE_READ);
+  TRY(check_ws(workspace, workspace_bytes, L.total));
+  TRY(check_device());
+  *conflict = 0;
+  if ((long long)D.B * D.T * D.H == 0) return ok();  // the op did no work
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return fail(SDM_ERR_HIP, "hipStreamSynchronize failed");
+  int32_t flag = 0;
+  if (hipMemcpy(&flag, (const unsigned char*)workspace + L.conflict, 4, hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(SDM_ERR_HIP, "reading the shared-bank flag failed");
+  *conflict = flag != 0;
   return ok();
 }
 

@@ -76,6 +76,7 @@ __host__ __device__ inline size_t loop_lds_bytes(int C, int W, int R, int cols, 
 
 template <typename A, typename Bk, bool STAGED>
 __global__ __launch_bounds__(LOOP_NT) void loop_kernel(Dims D, LoopArgs a, int nslices) {
+  if (a.abort && *a.abort) return;  // shared-bank conflict: no work (uniform over the grid)
   constexpr int EPL = Lane<Bk>::EPL;
   constexpr int COLS = 4 * EPL;  // columns per 64-byte slice
   constexpr int NW = LOOP_NT / 64;
@@ -100,7 +101,7 @@ __global__ __launch_bounds__(LOOP_NT) void loop_kernel(Dims D, LoopArgs a, int n
   const int mycol = col0 + q * EPL;
   const bool valid = mycol < D.d;
   const long long rowsd = D.rows * D.ld;
-  Bk* bank = (Bk*)a.bank + (long long)st * rowsd;
+  Bk* bank = (Bk*)a.bank + bank_of(D, st) * rowsd;
   const A* alpha = (const A*)a.alpha;
   const A* beta = (const A*)a.beta;
   const A* values = (const A*)a.values;
@@ -449,6 +450,7 @@ template <> struct Act4<bf16_t> {
 // FULL: every part has exactly 32 write and 32 read terms (no per-row term-count test).
 template <typename A, typename Bk, bool FULL>
 __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, int nslices) {
+  if (a.abort && *a.abort) return;  // shared-bank conflict: no work (uniform over the grid)
   constexpr int EPL = Lane<Bk>::EPL;
   static_assert(EPL == 4, "held rows are float32 row slices of 4 elements per lane");
   constexpr int COLS = 4 * EPL;
@@ -484,7 +486,7 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
   const int col0 = slice * COLS;
   const int mycol = col0 + q * EPL;
   const bool valid = mycol < D.d;
-  Bk* bank = (Bk*)a.bank + (long long)st * D.rows * D.ld;
+  Bk* bank = (Bk*)a.bank + bank_of(D, st) * D.rows * D.ld;
   const uint32_t ld = (uint32_t)D.ld;
   const A* alpha = (const A*)a.alpha;
   const A* beta = (const A*)a.beta;
@@ -822,6 +824,7 @@ template <> __device__ __forceinline__ w16_t pack_w<bf16_t>(const float* v) {
 
 template <typename A, typename Bk, bool FULL>
 __global__ __launch_bounds__(LOOP_NT) void loop_narrow_kernel(Dims D, LoopArgs a, int nslices) {
+  if (a.abort && *a.abort) return;  // shared-bank conflict: no work (uniform over the grid)
   constexpr int EPL = Lane<Bk>::EPL;
   constexpr int HOLD = NARROW_HOLD;
   extern __shared__ __align__(16) unsigned char lds[];
@@ -851,7 +854,7 @@ __global__ __launch_bounds__(LOOP_NT) void loop_narrow_kernel(Dims D, LoopArgs a
   // the stream's bank as a buffer resource: 32-bit byte offsets (the path requires < 4 GiB per stream), and any
   // access beyond the stream's rows is dropped by the hardware range check
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)((Bk*)a.bank + (long long)st * D.rows * D.ld), (short)0,
+      (void*)((Bk*)a.bank + bank_of(D, st) * D.rows * D.ld), (short)0,
       (int)(uint32_t)((unsigned long long)D.rows * D.ld * sizeof(Bk)), BUF_RSRC_WORD3);
   const uint32_t ldb = (uint32_t)(D.ld * sizeof(Bk));
   const uint32_t colb = (uint32_t)(mycol * sizeof(Bk));

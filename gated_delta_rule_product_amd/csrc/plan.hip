@@ -267,6 +267,7 @@ __device__ inline int compact_rows(const float* dense, int C, int Cc, uint64_t* 
 
 template <typename A>
 __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
+  if (a.abort && *a.abort) return;  // shared-bank conflict: no work (uniform over the grid)
   extern __shared__ __align__(16) unsigned char lds[];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int st = blockIdx.y;

@@ -36,7 +36,11 @@ struct Dims {
   long long ld;         // bank row stride (elements)
   int nch;              // chunks per stream
   int S;                // streams = B * H
+  int shared;           // the B streams of a head share one bank (bank [H, rows, ld])
 };
+
+// Bank index of stream st = b * H + h: st itself, or h with a shared bank.
+__host__ __device__ inline long long bank_of(const Dims& D, int st) { return D.shared ? st % D.H : st; }
 
 // Per-query-kind top-k plan: kept positions per factor and the candidate table.
 struct TopkPlan {
@@ -200,6 +204,7 @@ struct WsLayout {
   size_t widx, wwt, ridx, rwt;                 // [S][T][W|R] slot ids and softmax weights, stream-major
   size_t chunks;                               // [S * nch] chunk plan regions (chunk_layout)
   size_t counts;                               // [S * nch] ChunkCounts
+  size_t owner, conflict;                      // shared bank: int32 [H][N] first stream of each slot; int32 flag
   size_t total;
 };
 
@@ -233,6 +238,7 @@ struct PlanArgs {
   ChunkCounts* counts;    // [S * nch]
   int scat;               // also write the slot segments and their events (read by loop_kernel only)
   int lanemajor;          // write the gather terms lane-major for the narrow loop (term_pos)
+  const int32_t* abort;   // if not NULL and *abort != 0: do nothing (shared-bank conflict)
 };
 
 // Position of gather term i (of n per token) of chunk-local token t in a chunk's term section. Token-major: t n + i.
@@ -258,6 +264,7 @@ struct LoopArgs {
   const unsigned char* chunks;
   const ChunkCounts* counts;
   void* bank; void* out;
+  const int32_t* abort;   // if not NULL and *abort != 0: do nothing (shared-bank conflict)
 };
 hipError_t launch_loop(const Dims& D, const LoopArgs& a, hipStream_t st);
 // True if launch_loop runs the held-row variant (which reads last-event codes, not slot segments).
@@ -284,6 +291,10 @@ hipError_t launch_decode(const Dims& D, const DecodeArgs& a, hipStream_t st);
 bool decode_step_fits(const Dims& D, const DecodeArgs& a);
 hipError_t launch_decode_step(const Dims& D, const DecodeArgs& a, hipStream_t st);
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t st);
+// Shared bank: owner[h][slot] = -1 for every slot, flag = 0; then every addressed slot is claimed by its stream and
+// a slot claimed by two streams of a head sets the flag.
+hipError_t launch_shared_check(const Dims& D, const int32_t* widx, const int32_t* ridx, int32_t* owner,
+                               int32_t* flag, hipStream_t st);
 
 
 }  // namespace sdm

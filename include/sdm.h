@@ -32,7 +32,8 @@
  *   values, out                          [B, T, H, d]      act dtype
  *   forget_gate, input_gate              [B, T, H]         act dtype
  *   bank                                 [B, H, bank_rows, d] bank dtype, row pitch bank_row_stride elements (padding
- *                                        columns are never read or written); rows >= N are never read or written
+ *                                        columns are never read or written); rows >= N are never read or written;
+ *                                        [H, bank_rows, d] with cfg.shared_bank (sdm_write_read)
  *   write_idx, read_idx (optional)       [B, T, H, W] / [B, T, H, R] int32 slot ids, best first
  *
  * Ownership and streams: the caller owns every buffer. The library never allocates or frees memory (temporary
@@ -88,6 +89,9 @@ typedef struct {
   int64_t bank_row_stride;  /* elements from one bank row to the next (0: head_dim); >= head_dim, 16-byte multiple.
                                A pitch that is not a power of two (e.g. head_dim + 128 bytes) spreads the rows over
                                HBM channels evenly when rows are gathered in column slices. */
+  int32_t shared_bank;      /* sdm_write_read only (0 elsewhere): 1 = the B streams of a head share one bank,
+                               bank [H, bank_rows, d], and must address disjoint slots (see sdm_shared_bank_check) */
+  int32_t reserved;         /* 0 */
 } sdm_config;
 
 enum { SDM_OP_TOPK = 0, SDM_OP_WRITE_READ = 1, SDM_OP_DECODE = 2 };
@@ -117,6 +121,18 @@ sdm_status sdm_write_read(const sdm_config* cfg, const void* write_keys, const v
                           const void* values, const void* forget_gate, const void* input_gate, const void* subkeys,
                           void* bank, void* out, int32_t* write_idx, int32_t* read_idx, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/* Shared bank (CHANGELOG 2.0.0, "Behavior changes": a direct write/read call that runs several streams over one
+ * shared bank must say so, which asserts that the streams' slots are disjoint). With cfg.shared_bank = 1,
+ * sdm_write_read takes bank [H, bank_rows, d]: the streams (0, h) ... (B-1, h) all advance bank h. Reading taken
+ * here: the streams' slots are disjoint when no slot addressed (written or read) in this call by stream (b, h) is
+ * addressed by another stream (b', h); then the streams touch disjoint rows and the result equals running them one
+ * after the other. The call checks this on the device after the top-k; if it fails, the call writes neither the
+ * bank nor out (the ids may be written) and records the conflict in the workspace. sdm_shared_bank_check waits for
+ * `stream` (it synchronises) and sets *conflict to 1 if the last shared-bank sdm_write_read that used this
+ * workspace on this stream found a conflict, else 0. cfg and the workspace must be those of that call. */
+sdm_status sdm_shared_bank_check(const sdm_config* cfg, const void* workspace, size_t workspace_bytes,
+                                 int32_t* conflict, void* stream);
 
 /* Single-token decode step (CHANGELOG 2.0.0 "New": a single-token decode kernel; lumen PR #29: donate). cfg.tokens
  * must be 1; every stream (b, h) takes one token. bank_out == bank_in: donated, the successor is written in place.

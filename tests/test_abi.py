@@ -89,6 +89,23 @@ def test_refusals(lib, kw, status):
     assert B.last_error() != ""
 
 
+def test_shared_bank_settings(lib):
+    s0, n0 = _status(_cfg())
+    s1, n1 = _status(_cfg(shared_bank=True))
+    assert s0 == B.SDM_OK and s1 == B.SDM_OK
+    assert n1 >= n0 + 2 * 1024 * 4  # the owner table: one int32 per (head, slot)
+    cfg = _cfg(tokens=1, shared_bank=True)
+    assert _status(cfg, B.SDM_OP_DECODE)[0] == B.SDM_ERR_RANGE  # a decode step's streams own their banks
+    assert "shared_bank" in B.last_error()
+    cfg = _cfg()
+    cfg.shared_bank = 2
+    assert _status(cfg)[0] == B.SDM_ERR_RANGE
+    # the check entry point refuses a config without a shared bank and a NULL result pointer
+    c = ctypes.c_int32(0)
+    assert lib.sdm_shared_bank_check(ctypes.byref(_cfg()), None, 0, ctypes.byref(c), None) == B.SDM_ERR_RANGE
+    assert lib.sdm_shared_bank_check(ctypes.byref(_cfg(shared_bank=True)), None, 0, None, None) == B.SDM_ERR_NULL
+
+
 def test_padded_pitch_accepted_and_sized(lib):
     s0, n0 = _status(_cfg(bank_row_stride=0))
     s1, n1 = _status(_cfg(bank_row_stride=96))

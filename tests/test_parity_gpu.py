@@ -290,6 +290,151 @@ def test_write_read_padded_bank_pitch(bank_dt, pitch):
         assert np.array_equal(u, v)  # the pitch does not change the arithmetic
 
 
+# ------------------------------------------------------------------------------------------------ shared bank
+def _disjoint_streams(s, seed):
+    """Inputs whose B streams address disjoint slots of each head: factor 0's sub-keys fall into B groups, group g
+    near 10 * u_g (u_g = +-e_0, +-e_1, ...), and every query of stream b points along 5 * u_b in factor 0, so the
+    best factor-0 score of any tuple outside group b is about 50 below every tuple inside it (the other factors'
+    scores are a few units wide). Every written or read slot of stream b then has its factor-0 index in group b."""
+    x = synth.make_inputs(s, seed=seed)
+    B, dk, n0 = s.batch, s.subkey_dim, s.widths[0]
+    assert n0 % B == 0 and B <= 2 * dk
+    rng = np.random.default_rng(seed)
+    u = np.zeros((B, dk), np.float32)
+    for g in range(B):
+        u[g, g // 2] = 1.0 if g % 2 == 0 else -1.0
+    g = n0 // B
+    sub = x["subkeys"].copy()
+    for grp in range(B):
+        sub[:, grp * g:(grp + 1) * g] = 10.0 * u[grp] + 0.1 * rng.standard_normal((s.heads, g, dk))
+    for key in ("wkeys", "rq"):
+        q = x[key].copy()
+        q[..., :dk] = 5.0 * u[:, None, None, :] + 0.3 * rng.standard_normal(q[..., :dk].shape)
+        x[key] = q
+    if s.act == "bf16":
+        sub = synth.round_bf16_rne(sub)
+        x["wkeys"], x["rq"] = synth.round_bf16_rne(x["wkeys"]), synth.round_bf16_rne(x["rq"])
+    x["subkeys"] = sub.astype(np.float32)
+    x["shared"] = x["bank"][0].copy()  # [H, rows, d]
+    return x
+
+
+def run_gpu_shared(s, x, bank=None, pitch=None, out_fill=None):
+    at, bt = TORCH_DT[s.act], TORCH_DT[s.bank]
+    t = {k: to_dev(x[k], at) for k in ("wkeys", "rq", "values", "alpha", "beta", "subkeys")}
+    src = x["shared"] if bank is None else bank
+    g_bank = to_dev(src, bt) if pitch is None else padded_bank(src[None], bt, pitch)[0]
+    out = None
+    if out_fill is not None:
+        out = torch.full((s.batch, s.tokens, s.heads, s.head_dim), out_fill, dtype=at, device=DEV)
+    try:
+        out, widx, ridx = binding.sdm_write_read(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"],
+                                                 t["subkeys"], g_bank, widths=s.widths, num_writes=s.num_writes,
+                                                 num_reads=s.num_reads, chunk_size=s.chunk_size, want_index=True,
+                                                 out=out, shared_bank=True)
+    finally:
+        torch.cuda.synchronize()
+    if pitch is not None and pitch > s.head_dim:
+        assert bool((g_bank._base[..., s.head_dim:] == SENTINEL).all()), "padding columns of the bank were written"
+    return to_np(out), to_np(g_bank), to_np(widx), to_np(ridx)
+
+
+def oracle_shared(s, x):
+    """The streams of each head run one after another on the one bank (stream 0 first); with disjoint slots the
+    order is immaterial."""
+    M = x["shared"][None]
+    outs, widx, ridx = [], [], []
+    for b in range(s.batch):
+        xb = {k: x[k][b:b + 1] for k in ("wkeys", "rq", "values", "alpha", "beta")}
+        ref = oracle.write_read(xb["wkeys"], xb["rq"], xb["values"], xb["alpha"], xb["beta"], x["subkeys"], M,
+                                s.widths, s.num_writes, s.num_reads, bank_bf16=s.bank == "bf16",
+                                act_bf16=s.act == "bf16")
+        M = ref["bank"]
+        outs.append(ref["out"])
+        widx.append(ref["widx"])
+        ridx.append(ref["ridx"])
+    return {"out": np.concatenate(outs), "bank": M[0], "widx": np.concatenate(widx), "ridx": np.concatenate(ridx)}
+
+
+# act, bank, chunk, W, R, streams: the held-row loop (float32 bank, pow2 chunk), the 16-byte-slice loop (bf16
+# bank), and the general loop (chunk 7, ragged)
+SHARED = [
+    ("f32", "f32", 16, 8, 8, 4),
+    ("bf16", "f32", 64, 64, 64, 2),
+    ("bf16", "bf16", 32, 16, 16, 4),
+    ("f32", "bf16", 64, 32, 24, 2),
+    ("f32", "f32", 7, 5, 6, 4),
+]
+
+
+@pytest.mark.parametrize("act,bank,chunk,W,R,B", SHARED)
+def test_shared_bank_disjoint_streams(act, bank, chunk, W, R, B):
+    s = synth.Shape(B, 75, 2, (32, 32), 8, 64, W, R, chunk, act, bank, name="shared")
+    x = _disjoint_streams(s, seed=31)
+    print(f"shared bank act={act} bank={bank} C={chunk} W={W} R={R} B={B}", flush=True)
+    ref = oracle_shared(s, x)
+    grp = s.widths[0] // B
+    for key in ("widx", "ridx"):
+        f0 = ref[key] // s.widths[1]
+        assert np.array_equal(f0 // grp, np.broadcast_to(np.arange(B)[:, None, None, None], f0.shape)), \
+            "the construction did not give disjoint streams"
+    got = run_gpu_shared(s, x)
+    check_parity(s, got, ref)
+    again = run_gpu_shared(s, x)
+    for u, v in zip(got, again):
+        assert np.array_equal(u, v)
+
+
+def test_shared_bank_padded_pitch():
+    s = synth.Shape(2, 60, 2, (32, 32), 8, 64, 16, 16, 32, "bf16", "bf16", name="shared_pitch")
+    x = _disjoint_streams(s, seed=32)
+    print("shared bank pitch 72", flush=True)
+    got = run_gpu_shared(s, x, pitch=72)
+    check_parity(s, got, oracle_shared(s, x))
+
+
+def test_shared_bank_one_stream_equals_private():
+    """B = 1: the shared layout [H, rows, d] is the private one without its batch axis; results are bitwise equal."""
+    s = synth.WORKLOADS["tiny_1k"].with_(tokens=100, batch=1, heads=2, chunk_size=32)
+    x = synth.make_inputs(s, seed=33)
+    x["shared"] = x["bank"][0].copy()
+    print("shared bank B=1", flush=True)
+    priv = run_gpu(s, x)
+    shr = run_gpu_shared(s, x)
+    for u, v in zip(priv, shr):
+        assert np.array_equal(u.reshape(v.shape), v)
+
+
+def test_shared_bank_conflict_leaves_bank_and_out_untouched():
+    """Random keys over 1024 slots collide across streams: the check fails, SlotConflictError is raised, and neither
+    the bank nor out was written. A following disjoint call on the same library state succeeds (the flag and the
+    owner table start clear on every call)."""
+    s = synth.WORKLOADS["tiny_1k"].with_(tokens=64, batch=2, heads=2, chunk_size=32)
+    x = synth.make_inputs(s, seed=34)
+    x["shared"] = x["bank"][0].copy()
+    ref = oracle.write_read(x["wkeys"], x["rq"], x["values"], x["alpha"], x["beta"], x["subkeys"], x["bank"],
+                            s.widths, s.num_writes, s.num_reads)
+    a = set(ref["widx"][0, :, 0].ravel()) | set(ref["ridx"][0, :, 0].ravel())
+    b = set(ref["widx"][1, :, 0].ravel()) | set(ref["ridx"][1, :, 0].ravel())
+    assert a & b, "the random streams were expected to share a slot"
+    print("shared bank conflict", flush=True)
+    at, bt = TORCH_DT[s.act], TORCH_DT[s.bank]
+    t = {k: to_dev(x[k], at) for k in ("wkeys", "rq", "values", "alpha", "beta", "subkeys")}
+    g_bank = to_dev(x["shared"], bt)
+    before = g_bank.clone()
+    out = torch.full((s.batch, s.tokens, s.heads, s.head_dim), SENTINEL, dtype=at, device=DEV)
+    with pytest.raises(binding.SlotConflictError):
+        binding.sdm_write_read(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"], t["subkeys"], g_bank,
+                               widths=s.widths, num_writes=s.num_writes, num_reads=s.num_reads,
+                               chunk_size=s.chunk_size, out=out, shared_bank=True)
+    torch.cuda.synchronize()
+    assert torch.equal(g_bank, before)
+    assert bool((out == SENTINEL).all())
+    s2 = synth.Shape(2, 40, 2, (32, 32), 8, 64, 8, 8, 16, name="shared_after")
+    x2 = _disjoint_streams(s2, seed=35)
+    check_parity(s2, run_gpu_shared(s2, x2), oracle_shared(s2, x2))
+
+
 def test_write_read_bitwise_repeatable():
     s = synth.WORKLOADS["tiny_1k"].with_(tokens=192, batch=2, heads=2)
     x = synth.make_inputs(s, seed=9)
