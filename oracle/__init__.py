@@ -12,4 +12,5 @@ from .sdm_oracle import (  # noqa: F401
     topk,
     topk_one,
     write_read,
+    write_read_backward,
 )

@@ -35,7 +35,9 @@
  *
  * Parity pins: the factor score against exact rational arithmetic; brute force top-k against an independent Python
  * enumeration; tie closed forms; F = 1 textbook top-k; no-op gates; single-write closed form; the dense Gated
- * DeltaNet limit (W = R = N); linearity. See tests/test_oracle_pins.py.
+ * DeltaNet limit (W = R = N); linearity. See tests/test_oracle_pins.py. The backward (oracle_write_read_backward) is
+ * pinned by central finite differences of its fp64-state forward along random directions in every input, on banks
+ * small enough that slots collide across tokens; see tests/test_oracle_backward_pins.py.
  */
 #include <math.h>
 #include <pthread.h>
@@ -343,5 +345,241 @@ int oracle_write_read(int B, int T, int H, int F, const int* widths, int dk, int
     if (!started[i]) wr_worker(j);
   }
   for (int i = 0; i < nthreads; ++i) { if (started[i]) pthread_join(th[i], NULL); err |= jobs[i].err; }
+  return err ? -1 : 0;
+}
+
+/* ---------------------------------------------------------------------------------------------------------------
+ * Backward of the write/read: the reverse-mode derivative of the per-token recurrence above, one stream at a time.
+ *
+ * The pages ask for gradients of every input, computed deterministically, with the bank restored in place by the
+ * backward ([CL] 2.0.0, "Deterministic", "New", "Known limitations"); they print no formula. This is the plain
+ * chain rule applied to the recurrence of oracle_write_read, token by token in reverse. With P_i = M[S_i] before
+ * the token's write, r = sum_i w_i P_i, delta = beta (v - alpha r), M[S_i] <- alpha P_i + w_i delta and
+ * out = sum_j rho_j M[R_j] after the write, and G the adjoint of the bank after the token:
+ *   reads:   d rho_j = <dout, M[R_j]>,  G[R_j] += rho_j dout
+ *   writes:  g_i = G[S_i];  D = sum_i w_i g_i (the adjoint of delta);  dv = beta D;
+ *            d beta = <D, v - alpha r>;  d alpha = sum_i <g_i, P_i> - beta <D, r>;
+ *            d w_i = <g_i, delta> - alpha beta <D, P_i>;  G[S_i] <- alpha g_i - alpha beta w_i D
+ *   weights: softmax derivative, d s_i = w_i (d w_i - sum_k w_k d w_k)
+ *   scores:  a slot score is the sum of its factor scores <x^(f), C_f[i_f]>, so d x^(f) += d s C_f[i_f] and
+ *            d C_f[i_f] += d s x^(f) (rounding of the float32 scores is taken as exact: it has no derivative).
+ * After the first token G is the gradient of the bank before the call. Every sum is fp64 in a fixed order.
+ * exact = 1 keeps the bank states in fp64 (no rounding to the bank dtype): the smooth function that the finite-
+ * difference pins differentiate. exact = 0 rounds them after every token exactly as oracle_write_read does.
+ * ------------------------------------------------------------------------------------------------------------- */
+
+typedef struct {
+  int B, T, H, F, dk, d, W, R, bank_bf16, exact;
+  const int* widths;
+  const float *wkeys, *rq, *values, *alpha, *beta, *sub, *bank, *dout, *dbank;
+  int64_t bank_rows, sumn;
+  double *d_wkeys, *d_rq, *d_values, *d_alpha, *d_beta, *d_sub_stream, *d_bank, *out64, *bank64;
+  int s_begin, s_end;
+  int err;
+} bwd_job_t;
+
+static void score_backward(int F, const int* widths, int dk, int64_t id, double ds, const float* x, const float* sub,
+                           double* dx, double* dsub) {
+  int dig[ORACLE_MAX_F];
+  for (int f = F - 1; f >= 0; --f) { dig[f] = (int)(id % widths[f]); id /= widths[f]; }
+  int64_t off = 0;
+  for (int f = 0; f < F; ++f) {
+    const float* c = sub + (off + dig[f]) * dk;
+    double* dc = dsub + (off + dig[f]) * dk;
+    for (int e = 0; e < dk; ++e) {
+      dx[(int64_t)f * dk + e] += ds * (double)c[e];
+      dc[e] += ds * (double)x[(int64_t)f * dk + e];
+    }
+    off += widths[f];
+  }
+}
+
+static void* bwd_worker(void* arg) {
+  bwd_job_t* j = (bwd_job_t*)arg;
+  const int F = j->F, dk = j->dk, d = j->d, W = j->W, R = j->R, H = j->H, T = j->T;
+  const int64_t rows = j->bank_rows;
+  int32_t* S = (int32_t*)malloc(sizeof(int32_t) * (size_t)T * W);
+  int32_t* Rd = (int32_t*)malloc(sizeof(int32_t) * (size_t)T * R);
+  float* sc = (float*)malloc(sizeof(float) * (size_t)(W > R ? W : R));
+  double* w = (double*)malloc(sizeof(double) * (size_t)T * W);
+  double* rho = (double*)malloc(sizeof(double) * (size_t)T * R);
+  double* P = (double*)malloc(sizeof(double) * (size_t)T * W * d);
+  double* Vr = (double*)malloc(sizeof(double) * (size_t)T * R * d);
+  double* rr = (double*)malloc(sizeof(double) * (size_t)T * d);
+  double* del = (double*)malloc(sizeof(double) * (size_t)T * d);
+  double* M = (double*)malloc(sizeof(double) * (size_t)rows * d);
+  double* G = (double*)malloc(sizeof(double) * (size_t)rows * d);
+  double* g = (double*)malloc(sizeof(double) * (size_t)W * d);
+  double* D = (double*)malloc(sizeof(double) * (size_t)d);
+  double* dw = (double*)malloc(sizeof(double) * (size_t)(W > R ? W : R));
+  if (!S || !Rd || !sc || !w || !rho || !P || !Vr || !rr || !del || !M || !G || !g || !D || !dw) { j->err = 1; goto done; }
+  for (int st = j->s_begin; st < j->s_end; ++st) {
+    const int b = st / H, h = st % H;
+    const float* sub = j->sub + (int64_t)h * j->sumn * dk;
+    double* dsub = j->d_sub_stream + (int64_t)st * j->sumn * dk;
+    for (int64_t i = 0; i < rows * d; ++i) M[i] = (double)j->bank[(int64_t)st * rows * d + i];
+    /* forward, keeping what the backward reads */
+    for (int t = 0; t < T; ++t) {
+      const int64_t row = ((int64_t)b * T + t) * H + h;
+      int32_t* St = S + (int64_t)t * W;
+      int32_t* Rt = Rd + (int64_t)t * R;
+      if (oracle_topk_one(F, j->widths, dk, j->wkeys + row * F * dk, sub, W, St, sc) != 0) { j->err = 1; goto done; }
+      softmax64(W, sc, w + (int64_t)t * W);
+      if (oracle_topk_one(F, j->widths, dk, j->rq + row * F * dk, sub, R, Rt, sc) != 0) { j->err = 1; goto done; }
+      softmax64(R, sc, rho + (int64_t)t * R);
+      const double a = j->alpha[row], be = j->beta[row];
+      const float* v = j->values + row * d;
+      double* r = rr + (int64_t)t * d;
+      double* dl = del + (int64_t)t * d;
+      for (int c = 0; c < d; ++c) r[c] = 0.0;
+      for (int i = 0; i < W; ++i) {
+        const double* m = M + (int64_t)St[i] * d;
+        double* p = P + ((int64_t)t * W + i) * d;
+        for (int c = 0; c < d; ++c) { p[c] = m[c]; r[c] += w[(int64_t)t * W + i] * m[c]; }
+      }
+      for (int c = 0; c < d; ++c) dl[c] = be * ((double)v[c] - a * r[c]);
+      for (int i = 0; i < W; ++i) {
+        double* m = M + (int64_t)St[i] * d;
+        const double wi = w[(int64_t)t * W + i];
+        for (int c = 0; c < d; ++c) {
+          const double x = a * m[c] + wi * dl[c];
+          m[c] = j->exact ? x : (double)round_to(x, j->bank_bf16);
+        }
+      }
+      for (int i = 0; i < R; ++i) {
+        const double* m = M + (int64_t)Rt[i] * d;
+        double* q = Vr + ((int64_t)t * R + i) * d;
+        for (int c = 0; c < d; ++c) q[c] = m[c];
+      }
+      if (j->out64) {
+        double* o = j->out64 + row * d;
+        for (int c = 0; c < d; ++c) o[c] = 0.0;
+        for (int i = 0; i < R; ++i)
+          for (int c = 0; c < d; ++c) o[c] += rho[(int64_t)t * R + i] * Vr[((int64_t)t * R + i) * d + c];
+      }
+    }
+    if (j->bank64)
+      for (int64_t i = 0; i < rows * d; ++i) j->bank64[(int64_t)st * rows * d + i] = M[i];
+    /* reverse sweep */
+    for (int64_t i = 0; i < rows * d; ++i) G[i] = j->dbank ? (double)j->dbank[(int64_t)st * rows * d + i] : 0.0;
+    for (int t = T - 1; t >= 0; --t) {
+      const int64_t row = ((int64_t)b * T + t) * H + h;
+      const int32_t* St = S + (int64_t)t * W;
+      const int32_t* Rt = Rd + (int64_t)t * R;
+      const double* wt = w + (int64_t)t * W;
+      const double* rt = rho + (int64_t)t * R;
+      const float* dout = j->dout + row * d;
+      const double a = j->alpha[row], be = j->beta[row];
+      const float* v = j->values + row * d;
+      const double* r = rr + (int64_t)t * d;
+      const double* dl = del + (int64_t)t * d;
+      /* the read */
+      double sum = 0.0;
+      for (int i = 0; i < R; ++i) {
+        const double* q = Vr + ((int64_t)t * R + i) * d;
+        double acc = 0.0;
+        for (int c = 0; c < d; ++c) acc += (double)dout[c] * q[c];
+        dw[i] = acc;
+        double* Gr = G + (int64_t)Rt[i] * d;
+        for (int c = 0; c < d; ++c) Gr[c] += rt[i] * (double)dout[c];
+      }
+      for (int i = 0; i < R; ++i) sum += rt[i] * dw[i];
+      for (int i = 0; i < R; ++i)
+        score_backward(F, j->widths, dk, Rt[i], rt[i] * (dw[i] - sum), j->rq + row * F * dk, sub,
+                       j->d_rq + row * F * dk, dsub);
+      /* the write */
+      for (int i = 0; i < W; ++i)
+        for (int c = 0; c < d; ++c) g[(int64_t)i * d + c] = G[(int64_t)St[i] * d + c];
+      for (int c = 0; c < d; ++c) {
+        double acc = 0.0;
+        for (int i = 0; i < W; ++i) acc += wt[i] * g[(int64_t)i * d + c];
+        D[c] = acc;
+      }
+      double dbe = 0.0, dal = 0.0, rD = 0.0;
+      for (int c = 0; c < d; ++c) {
+        j->d_values[row * d + c] = be * D[c];
+        dbe += D[c] * ((double)v[c] - a * r[c]);
+        rD += D[c] * r[c];
+      }
+      for (int i = 0; i < W; ++i) {
+        const double* p = P + ((int64_t)t * W + i) * d;
+        const double* gi = g + (int64_t)i * d;
+        double gp = 0.0, gd = 0.0, Dp = 0.0;
+        for (int c = 0; c < d; ++c) { gp += gi[c] * p[c]; gd += gi[c] * dl[c]; Dp += D[c] * p[c]; }
+        dal += gp;
+        dw[i] = gd - a * be * Dp;
+      }
+      dal -= be * rD;
+      j->d_alpha[row] = dal;
+      j->d_beta[row] = dbe;
+      for (int i = 0; i < W; ++i) {
+        double* Gw = G + (int64_t)St[i] * d;
+        const double* gi = g + (int64_t)i * d;
+        for (int c = 0; c < d; ++c) Gw[c] = a * gi[c] - a * be * wt[i] * D[c];
+      }
+      sum = 0.0;
+      for (int i = 0; i < W; ++i) sum += wt[i] * dw[i];
+      for (int i = 0; i < W; ++i)
+        score_backward(F, j->widths, dk, St[i], wt[i] * (dw[i] - sum), j->wkeys + row * F * dk, sub,
+                       j->d_wkeys + row * F * dk, dsub);
+    }
+    for (int64_t i = 0; i < rows * d; ++i) j->d_bank[(int64_t)st * rows * d + i] = G[i];
+  }
+done:
+  free(S); free(Rd); free(sc); free(w); free(rho); free(P); free(Vr); free(rr); free(del); free(M); free(G);
+  free(g); free(D); free(dw);
+  return NULL;
+}
+
+/* Inputs as for oracle_write_read (bank = the bank BEFORE the call, not modified), plus
+ *   dout  [B, T, H, d]            gradient of the loss with respect to out
+ *   dbank [B, H, bank_rows, d]    gradient with respect to the bank after the call (NULL = zero)
+ * Outputs (fp64, zero-initialised here): d_wkeys, d_rq [B, T, H, F*dk], d_values [B, T, H, d], d_alpha, d_beta
+ * [B, T, H], d_subkeys [H, sum n_f, dk] (summed over the batch in order b = 0, 1, ...), d_bank [B, H, bank_rows, d]
+ * (the gradient with respect to the bank before the call); optional out64 [B, T, H, d] and bank64 (the forward's
+ * outputs in fp64, unrounded, NULL to skip). Returns 0 or -1. */
+int oracle_write_read_backward(int B, int T, int H, int F, const int* widths, int dk, int d, int W, int R,
+                               int bank_bf16, int exact, const float* wkeys, const float* rq, const float* values,
+                               const float* alpha, const float* beta, const float* subkeys, const float* bank,
+                               int64_t bank_rows, const float* dout, const float* dbank, double* d_wkeys,
+                               double* d_rq, double* d_values, double* d_alpha, double* d_beta, double* d_subkeys,
+                               double* d_bank, double* out64, double* bank64, int nthreads) {
+  int64_t sumn = 0, N = 1;
+  for (int f = 0; f < F; ++f) { sumn += widths[f]; N *= widths[f]; }
+  if (F < 1 || F > ORACLE_MAX_F || W < 1 || R < 1 || W > N || R > N || bank_rows < N) return -1;
+  const int streams = B * H;
+  memset(d_wkeys, 0, sizeof(double) * (size_t)B * T * H * F * dk);
+  memset(d_rq, 0, sizeof(double) * (size_t)B * T * H * F * dk);
+  memset(d_subkeys, 0, sizeof(double) * (size_t)H * sumn * dk);
+  double* dsub_stream = (double*)calloc((size_t)(streams > 0 ? streams : 1) * sumn * dk, sizeof(double));
+  if (!dsub_stream) return -1;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > streams) nthreads = streams > 0 ? streams : 1;
+  if (nthreads > 256) nthreads = 256;
+  pthread_t th[256];
+  int started[256];
+  bwd_job_t jobs[256];
+  int err = 0;
+  for (int i = 0; i < nthreads; ++i) {
+    bwd_job_t* j = &jobs[i];
+    j->B = B; j->T = T; j->H = H; j->F = F; j->dk = dk; j->d = d; j->W = W; j->R = R;
+    j->bank_bf16 = bank_bf16; j->exact = exact; j->widths = widths; j->wkeys = wkeys; j->rq = rq;
+    j->values = values; j->alpha = alpha; j->beta = beta; j->sub = subkeys; j->bank = bank; j->dout = dout;
+    j->dbank = dbank; j->bank_rows = bank_rows; j->sumn = sumn; j->d_wkeys = d_wkeys; j->d_rq = d_rq;
+    j->d_values = d_values; j->d_alpha = d_alpha; j->d_beta = d_beta; j->d_sub_stream = dsub_stream;
+    j->d_bank = d_bank; j->out64 = out64; j->bank64 = bank64; j->err = 0;
+    j->s_begin = (int)((int64_t)streams * i / nthreads);
+    j->s_end = (int)((int64_t)streams * (i + 1) / nthreads);
+    started[i] = pthread_create(&th[i], NULL, bwd_worker, j) == 0;
+    if (!started[i]) bwd_worker(j);
+  }
+  for (int i = 0; i < nthreads; ++i) { if (started[i]) pthread_join(th[i], NULL); err |= jobs[i].err; }
+  for (int b = 0; b < B; ++b)
+    for (int h = 0; h < H; ++h) {
+      const double* src = dsub_stream + ((int64_t)b * H + h) * sumn * dk;
+      double* dst = d_subkeys + (int64_t)h * sumn * dk;
+      for (int64_t i = 0; i < sumn * dk; ++i) dst[i] += src[i];
+    }
+  free(dsub_stream);
   return err ? -1 : 0;
 }

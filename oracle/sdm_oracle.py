@@ -64,6 +64,12 @@ def _load():
                 ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                 _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, ctypes.c_int64, _f32p,
                 vp, vp, vp, vp, ctypes.c_int]
+            lib.oracle_write_read_backward.restype = ctypes.c_int
+            lib.oracle_write_read_backward.argtypes = [
+                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, ctypes.c_int, ctypes.c_int,
+                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, ctypes.c_int64, _f32p, vp,
+                _f64p, _f64p, _f64p, _f64p, _f64p, _f64p, _f64p, vp, vp, ctypes.c_int]
             _lib = lib
     return _lib
 
@@ -162,4 +168,41 @@ def write_read(wkeys, rq, values, alpha, beta, subkeys, bank, widths, num_writes
                                    ptrs[0], ptrs[1], ptrs[2], ptrs[3], nt)
     if rc != 0:
         raise ValueError("oracle_write_read rejected its arguments")
+    return res
+
+
+def write_read_backward(wkeys, rq, values, alpha, beta, subkeys, bank, dout, dbank, widths, num_writes, num_reads,
+                        *, bank_bf16=False, exact=False, want_forward=False, nthreads: int | None = None):
+    """Gradients of the write/read (the chain rule through the per-token recurrence, in reverse; sdm_oracle.c).
+
+    bank is the bank before the call [B, H, bank_rows, d]; dout [B, T, H, d] and dbank (same shape as bank, or None
+    for zero) are the gradients of the loss with respect to out and to the bank after the call. exact=True keeps
+    the bank states in fp64 (no rounding to the bank dtype). Returns fp64 arrays d_wkeys, d_rq, d_values, d_alpha,
+    d_beta, d_subkeys, d_bank (with respect to the bank before the call), and with want_forward=True also out and
+    bank (the forward in fp64, rounded to the bank dtype after every token unless exact).
+    """
+    wk, rqa, v, al, be, sub = (_f32(x) for x in (wkeys, rq, values, alpha, beta, subkeys))
+    M = _f32(bank)
+    g_out = _f32(dout)
+    g_bank = None if dbank is None else _f32(dbank)
+    B, T, H, Fdk = wk.shape
+    d = v.shape[-1]
+    widths = np.ascontiguousarray(np.asarray(widths, dtype=np.int32))
+    dk = sub.shape[2]
+    W, R = int(num_writes), int(num_reads)
+    res = {"d_wkeys": np.zeros(wk.shape), "d_rq": np.zeros(rqa.shape), "d_values": np.zeros(v.shape),
+           "d_alpha": np.zeros(al.shape), "d_beta": np.zeros(be.shape), "d_subkeys": np.zeros(sub.shape),
+           "d_bank": np.zeros(M.shape)}
+    fwd = [None, None]
+    if want_forward:
+        res["out"] = np.zeros((B, T, H, d))
+        res["bank"] = np.zeros(M.shape)
+        fwd = [res["out"].ctypes.data, res["bank"].ctypes.data]
+    nt = nthreads or min(os.cpu_count() or 1, 16)
+    rc = _load().oracle_write_read_backward(
+        B, T, H, len(widths), widths, dk, d, W, R, int(bool(bank_bf16)), int(bool(exact)), wk, rqa, v, al, be, sub,
+        M, M.shape[2], g_out, None if g_bank is None else g_bank.ctypes.data, res["d_wkeys"], res["d_rq"],
+        res["d_values"], res["d_alpha"], res["d_beta"], res["d_subkeys"], res["d_bank"], fwd[0], fwd[1], nt)
+    if rc != 0:
+        raise ValueError("oracle_write_read_backward rejected its arguments")
     return res
