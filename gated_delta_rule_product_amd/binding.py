@@ -22,7 +22,7 @@ SDM_ERR_LAYOUT, SDM_ERR_WORKSPACE, SDM_ERR_DEVICE, SDM_ERR_HIP, SDM_ERR_NULL = 5
 STATUS_NAMES = {0: "SDM_OK", 1: "SDM_ERR_DTYPE", 2: "SDM_ERR_RANGE", 3: "SDM_ERR_BANK_TOO_SMALL", 4: "SDM_ERR_ALIAS",
                 5: "SDM_ERR_LAYOUT", 6: "SDM_ERR_WORKSPACE", 7: "SDM_ERR_DEVICE", 8: "SDM_ERR_HIP", 9: "SDM_ERR_NULL"}
 SDM_F32, SDM_BF16, SDM_F16 = 0, 1, 2
-SDM_OP_TOPK, SDM_OP_WRITE_READ, SDM_OP_DECODE = 0, 1, 2
+SDM_OP_TOPK, SDM_OP_WRITE_READ, SDM_OP_DECODE, SDM_OP_BACKWARD = 0, 1, 2, 3
 
 
 class UnsupportedConfigurationError(ValueError):
@@ -113,6 +113,10 @@ def load():
             lib.topk_product_keys.argtypes = [cfgp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp, ctypes.c_size_t, _vp]
             lib.sdm_write_read.restype = ctypes.c_int
             lib.sdm_write_read.argtypes = [cfgp] + [_vp] * 11 + [ctypes.c_size_t, _vp]
+            lib.sdm_write_read_save.restype = ctypes.c_int
+            lib.sdm_write_read_save.argtypes = [cfgp] + [_vp] * 12 + [ctypes.c_size_t, _vp]
+            lib.sdm_write_read_backward.restype = ctypes.c_int
+            lib.sdm_write_read_backward.argtypes = [cfgp] + [_vp] * 17 + [ctypes.c_size_t, _vp]
             lib.sdm_decode_step.restype = ctypes.c_int
             lib.sdm_decode_step.argtypes = [cfgp] + [_vp] * 12 + [ctypes.c_size_t, _vp]
             lib.sdm_shared_bank_check.restype = ctypes.c_int
@@ -148,7 +152,7 @@ def workspace_size(cfg: SdmConfig, op: int, k: int = 0) -> int:
     return n.value
 
 
-KERNELS = ("cand", "topk", "plan", "loop", "decode", "copy")
+KERNELS = ("cand", "topk", "plan", "loop", "decode", "copy", "bwd")
 
 
 def profile_enable(on: bool = True):
@@ -270,6 +274,87 @@ def sdm_write_read(write_keys, read_queries, values, forget_gate, input_gate, su
             raise SlotConflictError("shared_bank=True but the streams of a head address a common slot "
                                     "(the bank and out were not written)")
     return out, widx, ridx
+
+
+def sdm_write_read_save(write_keys, read_queries, values, forget_gate, input_gate, subkeys, bank, *, widths,
+                        num_writes, num_reads, chunk_size, want_index=False, out=None, snapshot=None, workspace=None):
+    """sdm_write_read that also saves the backward's snapshot [B, H, T, W, d] (bank dtype): the row of every write
+    event before it. Returns (out, write_idx, read_idx, snapshot)."""
+    B, T, H, Fdk = write_keys.shape
+    F = len(widths)
+    dk = Fdk // F
+    d = values.shape[-1]
+    act = write_keys.dtype
+    for name, t, shp in (("write_keys", write_keys, (B, T, H, Fdk)), ("read_queries", read_queries, (B, T, H, Fdk)),
+                         ("values", values, (B, T, H, d)), ("forget_gate", forget_gate, (B, T, H)),
+                         ("input_gate", input_gate, (B, T, H)), ("subkeys", subkeys, (H, sum(widths), dk))):
+        _need(t, name, shp, act)
+    if bank.dim() != 4 or bank.shape[0] != B or bank.shape[1] != H or bank.shape[3] != d:
+        raise ValueError(f"bank has shape {tuple(bank.shape)}, expected ({B}, {H}, bank_rows, {d})")
+    ld = _bank_ld(bank, "bank")
+    cfg = make_config(B, T, H, widths, dk, d, num_writes, num_reads, chunk_size, _dt(write_keys), _dt(bank),
+                      bank.shape[2], ld)
+    ws = _workspace(workspace_size(cfg, SDM_OP_WRITE_READ), bank.device, workspace)
+    if out is None:
+        out = torch.empty((B, T, H, d), dtype=act, device=bank.device)
+    else:
+        _need(out, "out", (B, T, H, d), act)
+    if snapshot is None:
+        snapshot = torch.empty((B, H, T, num_writes, d), dtype=bank.dtype, device=bank.device)
+    else:
+        _need(snapshot, "snapshot", (B, H, T, num_writes, d), bank.dtype)
+    widx = torch.empty((B, T, H, num_writes), dtype=torch.int32, device=bank.device) if want_index else None
+    ridx = torch.empty((B, T, H, num_reads), dtype=torch.int32, device=bank.device) if want_index else None
+    _check(load().sdm_write_read_save(ctypes.byref(cfg), _ptr(write_keys), _ptr(read_queries), _ptr(values),
+                                      _ptr(forget_gate), _ptr(input_gate), _ptr(subkeys), _ptr(bank), _ptr(out),
+                                      _ptr(snapshot), _ptr(widx), _ptr(ridx), _ptr(ws),
+                                      0 if ws is None else ws.numel(), _stream(bank.device)))
+    return out, widx, ridx, snapshot
+
+
+def sdm_write_read_backward(write_keys, read_queries, values, forget_gate, input_gate, subkeys, bank, snapshot,
+                            grad_out, grad_bank=None, *, widths, num_writes, num_reads, chunk_size, workspace=None):
+    """Backward of sdm_write_read_save. bank (as the forward left it) steps back to its state before the forward.
+    grad_bank: float32 with the bank's shape and row stride, the gradient w.r.t. the bank after the forward (None:
+    zeros), replaced in place by the gradient w.r.t. the bank before it. Returns a dict of float32 gradients:
+    write_keys, read_queries, values, forget_gate, input_gate, subkeys, bank."""
+    B, T, H, Fdk = write_keys.shape
+    F = len(widths)
+    dk = Fdk // F
+    d = values.shape[-1]
+    act = write_keys.dtype
+    for name, t, shp in (("write_keys", write_keys, (B, T, H, Fdk)), ("read_queries", read_queries, (B, T, H, Fdk)),
+                         ("values", values, (B, T, H, d)), ("forget_gate", forget_gate, (B, T, H)),
+                         ("input_gate", input_gate, (B, T, H)), ("subkeys", subkeys, (H, sum(widths), dk)),
+                         ("grad_out", grad_out, (B, T, H, d))):
+        _need(t, name, shp, act)
+    if bank.dim() != 4 or bank.shape[0] != B or bank.shape[1] != H or bank.shape[3] != d:
+        raise ValueError(f"bank has shape {tuple(bank.shape)}, expected ({B}, {H}, bank_rows, {d})")
+    ld = _bank_ld(bank, "bank")
+    _need(snapshot, "snapshot", (B, H, T, num_writes, d), bank.dtype)
+    dev = bank.device
+    if grad_bank is None:
+        grad_bank = torch.zeros((B, H, bank.shape[2], ld), dtype=torch.float32, device=dev)[..., :d]
+    if grad_bank.dtype != torch.float32 or tuple(grad_bank.shape) != tuple(bank.shape) or \
+            grad_bank.stride() != bank.stride():
+        raise ValueError("grad_bank must be float32 with the bank's shape and strides")
+    cfg = make_config(B, T, H, widths, dk, d, num_writes, num_reads, chunk_size, _dt(write_keys), _dt(bank),
+                      bank.shape[2], ld)
+    ws = _workspace(workspace_size(cfg, SDM_OP_BACKWARD), dev, workspace)
+    f32 = torch.float32
+    g = {"write_keys": torch.empty((B, T, H, Fdk), dtype=f32, device=dev),
+         "read_queries": torch.empty((B, T, H, Fdk), dtype=f32, device=dev),
+         "values": torch.empty((B, T, H, d), dtype=f32, device=dev),
+         "forget_gate": torch.empty((B, T, H), dtype=f32, device=dev),
+         "input_gate": torch.empty((B, T, H), dtype=f32, device=dev),
+         "subkeys": torch.empty((H, sum(widths), dk), dtype=f32, device=dev),
+         "bank": grad_bank}
+    _check(load().sdm_write_read_backward(
+        ctypes.byref(cfg), _ptr(write_keys), _ptr(read_queries), _ptr(values), _ptr(forget_gate), _ptr(input_gate),
+        _ptr(subkeys), _ptr(bank), _ptr(snapshot), _ptr(grad_out), _ptr(grad_bank), _ptr(g["write_keys"]),
+        _ptr(g["read_queries"]), _ptr(g["values"]), _ptr(g["forget_gate"]), _ptr(g["input_gate"]),
+        _ptr(g["subkeys"]), _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev)))
+    return g
 
 
 def sdm_decode_step(write_keys, read_queries, values, forget_gate, input_gate, subkeys, bank_in, bank_out=None, *,

@@ -82,10 +82,11 @@ sdm_status make_plan(const Dims& D, int k, const char* what, TopkPlan* P) {
   return SDM_OK;
 }
 
-// op: SDM_OP_TOPK (k given), SDM_OP_WRITE_READ, SDM_OP_DECODE
+// op: SDM_OP_TOPK (k given), SDM_OP_WRITE_READ, SDM_OP_DECODE, SDM_OP_BACKWARD (the write/read's config)
 sdm_status validate(const sdm_config* cfg, int op, int k, Dims* D, TopkPlan* pw, TopkPlan* pr) {
   if (!cfg) return fail(SDM_ERR_NULL, "cfg is NULL");
-  if (op < SDM_OP_TOPK || op > SDM_OP_DECODE) return fail(SDM_ERR_RANGE, "unknown op %d", op);
+  if (op < SDM_OP_TOPK || op > SDM_OP_BACKWARD) return fail(SDM_ERR_RANGE, "unknown op %d", op);
+  const bool chunked = op == SDM_OP_WRITE_READ || op == SDM_OP_BACKWARD;
   const int act = cfg->act_dtype, bank = cfg->bank_dtype;
   if (act == SDM_F16 || (op != SDM_OP_TOPK && bank == SDM_F16))
     return fail(SDM_ERR_DTYPE, "float16 is not supported (use float32 or bfloat16)");
@@ -95,7 +96,7 @@ sdm_status validate(const sdm_config* cfg, int op, int k, Dims* D, TopkPlan* pw,
     return fail(SDM_ERR_RANGE, "batch, tokens and heads must be >= 0");
   if (op == SDM_OP_DECODE && cfg->tokens != 1)
     return fail(SDM_ERR_RANGE, "sdm_decode_step takes exactly one token per stream (tokens = %d)", cfg->tokens);
-  if ((long long)cfg->batch * cfg->heads > 65535 && op == SDM_OP_WRITE_READ)
+  if ((long long)cfg->batch * cfg->heads > 65535 && chunked)
     return fail(SDM_ERR_RANGE, "batch * heads = %lld exceeds 65535 streams", (long long)cfg->batch * cfg->heads);
   if ((long long)cfg->batch * cfg->heads > 0x7FFFFFFFLL)
     return fail(SDM_ERR_RANGE, "batch * heads exceeds 2^31 - 1");
@@ -142,7 +143,10 @@ sdm_status validate(const sdm_config* cfg, int op, int k, Dims* D, TopkPlan* pw,
   if (ld < d || (ld * (bank == SDM_BF16 ? 2 : 4)) % 16 != 0)
     return fail(SDM_ERR_LAYOUT, "bank_row_stride = %lld must be >= head_dim = %d and a multiple of 16 bytes", ld, d);
   D->ld = ld;
-  if (op == SDM_OP_WRITE_READ) {
+  if (op == SDM_OP_BACKWARD && (long long)D->S * D->T * D->W >= (1LL << 31))
+    return fail(SDM_ERR_RANGE, "the backward snapshot would hold batch * heads * tokens * num_writes = %lld rows "
+                "(2^31 or more)", (long long)D->S * D->T * D->W);
+  if (chunked) {
     const int C = cfg->chunk_size;
     if (C < 1 || C > MAX_CHUNK) return fail(SDM_ERR_RANGE, "chunk_size = %d out of range [1, %d]", C, MAX_CHUNK);
     if ((long long)C * D->W > MAX_CHUNK_EVENTS)
@@ -209,6 +213,18 @@ WsLayout layout(const Dims& D, int op) {
       L.owner = take((size_t)D.H * (size_t)D.N * 4);
       L.conflict = take(4);
     }
+  }
+  if (op == SDM_OP_BACKWARD) {
+    const size_t nw = (size_t)D.S * D.T * D.W, nr = (size_t)D.S * D.T * D.R;
+    long long sumn = 0;
+    for (int f = 0; f < D.F; ++f) sumn += D.widths[f];
+    L.widx = take(nw * 4);
+    L.wwt = take(nw * 4);
+    L.ridx = take(nr * 4);
+    L.rwt = take(nr * 4);
+    L.part = take((size_t)bwd_slices(D) * D.S * D.T * (D.W + D.R + 2) * 4);
+    L.ds = take((size_t)D.S * D.T * (D.W + D.R) * 4);
+    L.sgpart = take((size_t)bwd_row_blocks(D) * D.H * sumn * D.dk * 4);
   }
   L.total = o;
   return L;
@@ -369,13 +385,22 @@ sdm_status topk_product_keys(const sdm_config* cfg, const void* queries, const v
   return ok();
 }
 
-sdm_status sdm_write_read(const sdm_config* cfg, const void* write_keys, const void* read_queries,
-                          const void* values, const void* forget_gate, const void* input_gate, const void* subkeys,
-                          void* bank, void* out, int32_t* write_idx, int32_t* read_idx, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+// The write/read; with a snapshot (not NULL) also the backward's snapshot, through the segmented chunk loop.
+static sdm_status write_read_impl(const sdm_config* cfg, const void* write_keys, const void* read_queries,
+                           const void* values, const void* forget_gate, const void* input_gate, const void* subkeys,
+                           void* bank, void* out, void* snapshot, int32_t* write_idx, int32_t* read_idx,
+                           void* workspace, size_t workspace_bytes, void* stream) {
   Dims D;
   TopkPlan pw, pr;
   TRY(validate(cfg, SDM_OP_WRITE_READ, 0, &D, &pw, &pr));
+  const size_t snap_bytes = (size_t)D.S * D.T * D.W * D.d * esize(D.bank);
+  if (snapshot || cfg->shared_bank) {
+    if (cfg->shared_bank && snapshot)
+      return fail(SDM_ERR_RANGE, "a shared bank has no backward (sdm_write_read_save refuses shared_bank)");
+    if (snapshot && (long long)D.S * D.T * D.W >= (1LL << 31))
+      return fail(SDM_ERR_RANGE, "the backward snapshot would hold batch * heads * tokens * num_writes = %lld rows "
+                  "(2^31 or more)", (long long)D.S * D.T * D.W);
+  }
   const long long rows = (long long)D.B * D.T * D.H;
   long long sumn = 0;
   for (int f = 0; f < D.F; ++f) sumn += D.widths[f];
@@ -392,6 +417,7 @@ sdm_status sdm_write_read(const sdm_config* cfg, const void* write_keys, const v
     TRY(need(out, "out"));
   }
   TRY(aligned(bank, 16, "bank"));
+  if (snapshot) TRY(aligned(snapshot, 16, "snapshot"));
   const WsLayout L = layout(D, SDM_OP_WRITE_READ);
   TRY(check_ws(workspace, workspace_bytes, L.total));
   const size_t qb = (size_t)rows * D.F * D.dk * ea;
@@ -405,8 +431,9 @@ sdm_status sdm_write_read(const sdm_config* cfg, const void* write_keys, const v
                         {out, (size_t)rows * D.d * ea, "out"},
                         {write_idx, (size_t)rows * D.W * 4, "write_idx"},
                         {read_idx, (size_t)rows * D.R * 4, "read_idx"},
-                        {workspace, L.total, "workspace"}};
-  TRY(check_alias(outs, 5, ins, 6));
+                        {workspace, L.total, "workspace"},
+                        {snapshot, snap_bytes, "snapshot"}};
+  TRY(check_alias(outs, 6, ins, 6));
   TRY(check_device());
   if (rows == 0) return ok();
   hipStream_t st = (hipStream_t)stream;
@@ -450,8 +477,9 @@ sdm_status sdm_write_read(const sdm_config* cfg, const void* write_keys, const v
   pa.beta = input_gate;
   pa.chunks = ws + L.chunks;
   pa.counts = (ChunkCounts*)(ws + L.counts);
-  pa.scat = loop_held_path(D) || loop_narrow_path(D) ? 0 : 1;
-  pa.lanemajor = !loop_held_path(D) && loop_narrow_lanemajor(D) ? 1 : 0;
+  pa.scat = !snapshot && (loop_held_path(D) || loop_narrow_path(D)) ? 0 : 1;
+  pa.lanemajor = !snapshot && !loop_held_path(D) && loop_narrow_lanemajor(D) ? 1 : 0;
+  pa.evcode = snapshot ? 1 : 0;
   TRY(hip_status(timed(SDM_K_PLAN, st, [&] { return launch_plan(D, pa, st); }), "chunk plan launch"));
   LoopArgs la;
   la.alpha = forget_gate;
@@ -462,7 +490,128 @@ sdm_status sdm_write_read(const sdm_config* cfg, const void* write_keys, const v
   la.bank = bank;
   la.out = out;
   la.abort = abort;
+  la.snap = snapshot;
   TRY(hip_status(timed(SDM_K_LOOP, st, [&] { return launch_loop(D, la, st); }), "chunk loop launch"));
+  return ok();
+}
+
+sdm_status sdm_write_read(const sdm_config* cfg, const void* write_keys, const void* read_queries,
+                          const void* values, const void* forget_gate, const void* input_gate, const void* subkeys,
+                          void* bank, void* out, int32_t* write_idx, int32_t* read_idx, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return write_read_impl(cfg, write_keys, read_queries, values, forget_gate, input_gate, subkeys, bank, out, nullptr,
+                         write_idx, read_idx, workspace, workspace_bytes, stream);
+}
+
+sdm_status sdm_write_read_save(const sdm_config* cfg, const void* write_keys, const void* read_queries,
+                               const void* values, const void* forget_gate, const void* input_gate,
+                               const void* subkeys, void* bank, void* out, void* snapshot, int32_t* write_idx,
+                               int32_t* read_idx, void* workspace, size_t workspace_bytes, void* stream) {
+  if (cfg && (long long)cfg->batch * cfg->tokens * cfg->heads > 0 && !snapshot)
+    return fail(SDM_ERR_NULL, "snapshot is NULL");
+  if (cfg && cfg->shared_bank)
+    return fail(SDM_ERR_RANGE, "a shared bank has no backward (sdm_write_read_save refuses shared_bank)");
+  return write_read_impl(cfg, write_keys, read_queries, values, forget_gate, input_gate, subkeys, bank, out,
+                         snapshot, write_idx, read_idx, workspace, workspace_bytes, stream);
+}
+
+sdm_status sdm_write_read_backward(const sdm_config* cfg, const void* write_keys, const void* read_queries,
+                                   const void* values, const void* forget_gate, const void* input_gate,
+                                   const void* subkeys, void* bank, const void* snapshot, const void* grad_out,
+                                   float* grad_bank, float* grad_write_keys, float* grad_read_queries,
+                                   float* grad_values, float* grad_forget_gate, float* grad_input_gate,
+                                   float* grad_subkeys, void* workspace, size_t workspace_bytes, void* stream) {
+  Dims D;
+  TopkPlan pw, pr;
+  TRY(validate(cfg, SDM_OP_BACKWARD, 0, &D, &pw, &pr));
+  const long long rows = (long long)D.B * D.T * D.H;
+  long long sumn = 0;
+  for (int f = 0; f < D.F; ++f) sumn += D.widths[f];
+  const size_t ea = esize(D.act), eb = esize(D.bank);
+  const size_t nbank = (size_t)D.S * (size_t)D.rows * (size_t)D.ld;
+  if (rows > 0) {
+    const void* ptrs[] = {write_keys, read_queries, values, forget_gate, input_gate, subkeys, bank, snapshot,
+                          grad_out, grad_bank, grad_write_keys, grad_read_queries, grad_values, grad_forget_gate,
+                          grad_input_gate, grad_subkeys};
+    const char* names[] = {"write_keys", "read_queries", "values", "forget_gate", "input_gate", "subkeys", "bank",
+                           "snapshot", "grad_out", "grad_bank", "grad_write_keys", "grad_read_queries",
+                           "grad_values", "grad_forget_gate", "grad_input_gate", "grad_subkeys"};
+    for (int i = 0; i < 16; ++i) TRY(need(ptrs[i], names[i]));
+  }
+  TRY(aligned(bank, 16, "bank"));
+  TRY(aligned(snapshot, 16, "snapshot"));
+  TRY(aligned(grad_bank, 16, "grad_bank"));
+  TRY(aligned(grad_values, 16, "grad_values"));
+  const WsLayout L = layout(D, SDM_OP_BACKWARD);
+  TRY(check_ws(workspace, workspace_bytes, L.total));
+  const size_t qb = (size_t)rows * D.F * D.dk;
+  const Range ins[] = {{write_keys, qb * ea, "write_keys"},
+                       {read_queries, qb * ea, "read_queries"},
+                       {values, (size_t)rows * D.d * ea, "values"},
+                       {forget_gate, (size_t)rows * ea, "forget_gate"},
+                       {input_gate, (size_t)rows * ea, "input_gate"},
+                       {subkeys, (size_t)D.H * sumn * D.dk * ea, "subkeys"},
+                       {snapshot, (size_t)D.S * D.T * D.W * D.d * eb, "snapshot"},
+                       {grad_out, (size_t)rows * D.d * ea, "grad_out"}};
+  const Range outs[] = {{bank, nbank * eb, "bank"},
+                        {grad_bank, nbank * 4, "grad_bank"},
+                        {grad_write_keys, qb * 4, "grad_write_keys"},
+                        {grad_read_queries, qb * 4, "grad_read_queries"},
+                        {grad_values, (size_t)rows * D.d * 4, "grad_values"},
+                        {grad_forget_gate, (size_t)rows * 4, "grad_forget_gate"},
+                        {grad_input_gate, (size_t)rows * 4, "grad_input_gate"},
+                        {grad_subkeys, (size_t)D.H * sumn * D.dk * 4, "grad_subkeys"},
+                        {workspace, L.total, "workspace"}};
+  TRY(check_alias(outs, 9, ins, 8));
+  TRY(check_device());
+  if (rows == 0) return ok();
+  hipStream_t st = (hipStream_t)stream;
+  unsigned char* ws = (unsigned char*)workspace;
+  const TopkPlan plans[2] = {pw, pr};
+  TRY(hip_status(timed(SDM_K_CAND, st, [&] { return launch_cand_tables(plans, 2, D.F, (uint64_t*)(ws + L.cand), st); }),
+                 "candidate table launch"));
+  TopkArgs ta;
+  memset(&ta, 0, sizeof ta);
+  ta.queries[0] = write_keys;
+  ta.queries[1] = read_queries;
+  ta.subkeys = subkeys;
+  ta.cand[0] = (const uint64_t*)(ws + L.cand);
+  ta.cand[1] = (const uint64_t*)(ws + L.cand) + MAX_CAND;
+  ta.plan[0] = pw;
+  ta.plan[1] = pr;
+  ta.nkinds = 2;
+  ta.stream_major = 1;
+  ta.ids[0] = (int32_t*)(ws + L.widx);
+  ta.ids[1] = (int32_t*)(ws + L.ridx);
+  ta.vals[0] = (float*)(ws + L.wwt);
+  ta.vals[1] = (float*)(ws + L.rwt);
+  ta.snorm = (float*)(ws + L.snorm);
+  TRY(hip_status(timed(SDM_K_TOPK, st, [&] { return launch_topk(D, ta, st); }), "top-k launch"));
+  BwdArgs ba;
+  ba.widx = (const int32_t*)(ws + L.widx);
+  ba.wwt = (const float*)(ws + L.wwt);
+  ba.ridx = (const int32_t*)(ws + L.ridx);
+  ba.rwt = (const float*)(ws + L.rwt);
+  ba.wkeys = write_keys;
+  ba.rq = read_queries;
+  ba.subkeys = subkeys;
+  ba.alpha = forget_gate;
+  ba.beta = input_gate;
+  ba.values = values;
+  ba.gout = grad_out;
+  ba.bank = bank;
+  ba.snap = snapshot;
+  ba.gbank = grad_bank;
+  ba.gwkeys = grad_write_keys;
+  ba.grq = grad_read_queries;
+  ba.gvalues = grad_values;
+  ba.galpha = grad_forget_gate;
+  ba.gbeta = grad_input_gate;
+  ba.gsub = grad_subkeys;
+  ba.part = (float*)(ws + L.part);
+  ba.ds = (float*)(ws + L.ds);
+  ba.sgpart = (float*)(ws + L.sgpart);
+  TRY(hip_status(timed(SDM_K_BWD, st, [&] { return launch_bwd(D, ba, st); }), "backward launch"));
   return ok();
 }
 

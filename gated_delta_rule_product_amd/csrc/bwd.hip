@@ -1,0 +1,342 @@
+// Backward of the write/read: gradients of the write keys, read queries, values, both gates, the sub-keys and the
+// bank before the call; the bank itself steps back to its state before the call. sparse-delta-memory CHANGELOG.md
+// 2.0.0: "Deterministic" (every gradient bitwise repeatable, no float atomics), "New" (exact product-key top-k with
+// a deterministic sparse backward), "Known limitations" (the first backward restores the bank in place).
+//
+// The reverse-mode derivative of the per-token recurrence (write: r = sum_i w_i P_i, delta = beta (v - alpha r),
+// M[S_i] <- alpha P_i + w_i delta; then the read out = sum_j rho_j M[R_j]), tokens in reverse, with G the adjoint
+// of the bank (the gradient buffer, updated in place):
+//   read:   d rho_j = <dout, M[R_j]>,  G[R_j] += rho_j dout
+//   write:  g_i = G[S_i],  D = sum_i w_i g_i,  dv = beta D,  d beta = <D, v - alpha r>,
+//           d alpha = sum_i <g_i, P_i> - beta <D, r>,  d w_i = <g_i, delta> - alpha beta <D, P_i>,
+//           G[S_i] <- alpha g_i - alpha beta w_i D,  M[S_i] <- P_i  (the bank steps back one token)
+//   weights: softmax derivative d s_i = w_i (d w_i - sum_k w_k d w_k); scores: a slot score is the sum of its factor
+//           scores <x^(f), C_f[i_f]>, so d x^(f) = sum_i d s_i C_f[i_f] and d C_f[i] = sum d s x^(f) over the terms
+//           whose factor-f sub-key is i.
+// P_i (the row of S_i before the token's write) is the forward's snapshot. G, M and D are column-local, so one
+// workgroup runs one (stream, 16-column slice) over every token; only the dot products cross slices: each slice
+// writes its partial sums and a second kernel adds them over the slices in order. Every sum has a fixed order.
+#include "sdm_internal.h"
+
+namespace sdm {
+
+constexpr int BWD_NT = 512;
+constexpr int BWD_COLS = 16;  // columns per slice: 128 groups of 4 lanes, 4 columns per lane
+
+// Four consecutive bank elements: raw bits (for the restore) and floats.
+template <typename Bk> struct Raw4;
+template <> struct Raw4<float> {
+  typedef w16_t T;
+  __device__ static T load(const float* p) { return *(const w16_t*)p; }
+  __device__ static void store(float* p, T x) { *(w16_t*)p = x; }
+  __device__ static void unpack(T x, float* v) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = __uint_as_float(x[k]);
+  }
+};
+template <> struct Raw4<bf16_t> {
+  typedef uint2 T;
+  __device__ static T load(const bf16_t* p) { return *(const uint2*)p; }
+  __device__ static void store(bf16_t* p, T x) { *(uint2*)p = x; }
+  __device__ static void unpack(T x, float* v) {
+    v[0] = __uint_as_float(x.x << 16);
+    v[1] = __uint_as_float(x.x & 0xFFFF0000u);
+    v[2] = __uint_as_float(x.y << 16);
+    v[3] = __uint_as_float(x.y & 0xFFFF0000u);
+  }
+};
+
+__device__ __forceinline__ float sum4_lanes(float x) {  // over the 4 lanes of a group; equal on all four
+  x += __shfl_xor(x, 1);
+  x += __shfl_xor(x, 2);
+  return x;
+}
+
+__host__ __device__ inline size_t bwd_sweep_lds(int W) { return (size_t)W * (2 * BWD_COLS + 2) * 4 + 8 * BWD_COLS * 4; }
+
+template <typename A, typename Bk>
+__global__ __launch_bounds__(BWD_NT) void bwd_sweep_kernel(Dims D, BwdArgs a, int nsl) {
+  extern __shared__ __align__(16) float lds_f[];
+  const int W = D.W, R = D.R, T = D.T, d = D.d;
+  float* sG = lds_f;                      // [W][16] g_i
+  float* sP = sG + W * BWD_COLS;          // [W][16] P_i
+  float* sW = sP + W * BWD_COLS;          // [W] w_i
+  float* sGP = sW + W;                    // [W] slice partial <g_i, P_i>
+  float* sDel = sGP + W;                  // [16] D
+  float* sRr = sDel + BWD_COLS;           // [16] r
+  float* sDt = sRr + BWD_COLS;            // [16] delta
+  float* sSc = sDt + BWD_COLS;            // [2]  slice partials of d alpha and d beta
+
+  const int nblk = gridDim.x;
+  int wk = blockIdx.x;
+  if ((nblk & 7) == 0) wk = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);  // XCD-aware: slices of a stream together
+  const int st = wk / nsl, slice = wk % nsl;
+  const int b = st / D.H, h = st % D.H;
+  const int tid = threadIdx.x, grp = tid >> 2, q = tid & 3;
+  const int col = slice * BWD_COLS + q * 4;
+  const bool valid = col < d;  // d % 4 == 0: a lane's four columns are all inside or all outside
+  const int P = W + R + 2;
+  Bk* bank = (Bk*)a.bank + (long long)st * D.rows * D.ld;
+  float* gbank = a.gbank + (long long)st * D.rows * D.ld;
+  const Bk* snap = (const Bk*)a.snap + (long long)st * T * W * d;
+  const A* gout = (const A*)a.gout;
+  const A* values = (const A*)a.values;
+
+  for (int t = T - 1; t >= 0; --t) {
+    const long long so = (long long)st * T + t;             // stream-major token index
+    const long long row = ((long long)b * T + t) * D.H + h;  // [B, T, H] row
+    const float al = to_f<A>(((const A*)a.alpha)[row]);
+    const float be = to_f<A>(((const A*)a.beta)[row]);
+    float* part = a.part + ((long long)slice * D.S * T + so) * P;
+    float dout[4] = {0.f, 0.f, 0.f, 0.f};
+    if (valid) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) dout[k] = to_f<A>(gout[row * d + col + k]);
+    }
+    // the read: d rho partials, G[R_j] += rho_j dout
+    for (int j = grp; j < R; j += BWD_NT / 4) {
+      const int slot = a.ridx[so * R + j];
+      const float rho = a.rwt[so * R + j];
+      float m[4] = {0.f, 0.f, 0.f, 0.f};
+      if (valid) {
+        Raw4<Bk>::unpack(Raw4<Bk>::load(bank + (long long)slot * D.ld + col), m);
+        float* gp = gbank + (long long)slot * D.ld + col;
+        float4 g = *(float4*)gp;
+        g.x += rho * dout[0]; g.y += rho * dout[1]; g.z += rho * dout[2]; g.w += rho * dout[3];
+        *(float4*)gp = g;
+      }
+      const float dot = sum4_lanes(((dout[0] * m[0] + dout[1] * m[1]) + dout[2] * m[2]) + dout[3] * m[3]);
+      if (q == 0) part[W + j] = dot;
+    }
+    __syncthreads();
+    // the write, first half: g_i and P_i of the slice into LDS
+    for (int i = grp; i < W; i += BWD_NT / 4) {
+      const int slot = a.widx[so * W + i];
+      float g[4] = {0.f, 0.f, 0.f, 0.f}, p[4] = {0.f, 0.f, 0.f, 0.f};
+      if (valid) {
+        const float4 gv = *(const float4*)(gbank + (long long)slot * D.ld + col);
+        g[0] = gv.x; g[1] = gv.y; g[2] = gv.z; g[3] = gv.w;
+        Raw4<Bk>::unpack(Raw4<Bk>::load(snap + ((long long)t * W + i) * d + col), p);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        sG[i * BWD_COLS + q * 4 + k] = g[k];
+        sP[i * BWD_COLS + q * 4 + k] = p[k];
+      }
+      const float gp = sum4_lanes(((g[0] * p[0] + g[1] * p[1]) + g[2] * p[2]) + g[3] * p[3]);
+      if (q == 0) {
+        sGP[i] = gp;
+        sW[i] = a.wwt[so * W + i];
+      }
+    }
+    __syncthreads();
+    // D and r per column, sum of <g_i, P_i>, each in term order
+    if (tid < BWD_COLS) {
+      float s = 0.f;
+      for (int i = 0; i < W; ++i) s += sW[i] * sG[i * BWD_COLS + tid];
+      sDel[tid] = s;
+    } else if (tid < 2 * BWD_COLS) {
+      const int c = tid - BWD_COLS;
+      float s = 0.f;
+      for (int i = 0; i < W; ++i) s += sW[i] * sP[i * BWD_COLS + c];
+      sRr[c] = s;
+    } else if (tid == 2 * BWD_COLS) {
+      float s = 0.f;
+      for (int i = 0; i < W; ++i) s += sGP[i];
+      sSc[0] = s;
+    }
+    __syncthreads();
+    // delta, dv and the gate partials (one wave: columns on lanes 0..15)
+    if (tid < 64) {
+      const int c = tid & (BWD_COLS - 1);
+      const int cc = slice * BWD_COLS + c;
+      const bool cv = tid < BWD_COLS && cc < d;
+      const float Dl = sDel[c], r = sRr[c];
+      const float v = cv ? to_f<A>(values[row * d + cc]) : 0.f;
+      const float e = v - al * r;  // v - alpha r
+      float db = cv ? Dl * e : 0.f;
+      float rd = cv ? Dl * r : 0.f;
+      if (cv) {
+        sDt[c] = be * e;
+        a.gvalues[row * d + cc] = be * Dl;
+      } else if (tid < BWD_COLS) {
+        sDt[c] = 0.f;
+      }
+#pragma unroll
+      for (int o = 8; o >= 1; o >>= 1) {  // fixed tree over the 16 columns
+        db += __shfl_xor(db, o);
+        rd += __shfl_xor(rd, o);
+      }
+      if (tid == 0) {
+        part[W + R] = sSc[0] - be * rd;
+        part[W + R + 1] = db;
+      }
+    }
+    __syncthreads();
+    // the write, second half: d w_i partials, G[S_i] <- alpha g_i - alpha beta w_i D, M[S_i] <- P_i
+    const float ab = al * be;
+    for (int i = grp; i < W; i += BWD_NT / 4) {
+      float g[4], p[4], dl[4], Dl[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        g[k] = sG[i * BWD_COLS + q * 4 + k];
+        p[k] = sP[i * BWD_COLS + q * 4 + k];
+        dl[k] = sDt[q * 4 + k];
+        Dl[k] = sDel[q * 4 + k];
+      }
+      const float gd = sum4_lanes(((g[0] * dl[0] + g[1] * dl[1]) + g[2] * dl[2]) + g[3] * dl[3]);
+      const float Dp = sum4_lanes(((Dl[0] * p[0] + Dl[1] * p[1]) + Dl[2] * p[2]) + Dl[3] * p[3]);
+      if (q == 0) part[i] = gd - ab * Dp;
+      if (valid) {
+        const int slot = a.widx[so * W + i];
+        const float cw = ab * sW[i];
+        *(float4*)(gbank + (long long)slot * D.ld + col) =
+            make_float4(al * g[0] - cw * Dl[0], al * g[1] - cw * Dl[1], al * g[2] - cw * Dl[2], al * g[3] - cw * Dl[3]);
+        Raw4<Bk>::store(bank + (long long)slot * D.ld + col, Raw4<Bk>::load(snap + ((long long)t * W + i) * d + col));
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// One workgroup per token row (stream-major): slice sums, gate gradients, softmax derivative (slot-score gradients
+// into the workspace), and the key and query gradients d x^(f) = sum_i d s_i C_f[i_f] (terms in order).
+template <typename A>
+__global__ __launch_bounds__(256) void bwd_token_kernel(Dims D, BwdArgs a, int nsl) {
+  __shared__ float sd[MAX_K * 2 + 2];
+  __shared__ float sm[2];
+  const long long so = blockIdx.x;
+  const int T = D.T, W = D.W, R = D.R, P = W + R + 2;
+  const int st = (int)(so / T), t = (int)(so % T);
+  const int b = st / D.H, h = st % D.H;
+  const long long row = ((long long)b * T + t) * D.H + h;
+  for (int p = threadIdx.x; p < P; p += 256) {
+    float s = 0.f;
+    for (int sl = 0; sl < nsl; ++sl) s += a.part[((long long)sl * D.S * T + so) * P + p];
+    sd[p] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    a.galpha[row] = sd[W + R];
+    a.gbeta[row] = sd[W + R + 1];
+    float m = 0.f;
+    for (int i = 0; i < W; ++i) m += a.wwt[so * W + i] * sd[i];
+    sm[0] = m;
+  } else if (threadIdx.x == 64) {
+    float m = 0.f;
+    for (int j = 0; j < R; ++j) m += a.rwt[so * R + j] * sd[W + j];
+    sm[1] = m;
+  }
+  __syncthreads();
+  float* ds = a.ds + so * (W + R);
+  for (int i = threadIdx.x; i < W + R; i += 256) {
+    const bool wr = i < W;
+    const float wt = wr ? a.wwt[so * W + i] : a.rwt[so * R + (i - W)];
+    const float v = wt * (sd[i] - sm[wr ? 0 : 1]);
+    sd[i] = v;
+    ds[i] = v;
+  }
+  __syncthreads();
+  long long sumn = 0;
+  for (int f = 0; f < D.F; ++f) sumn += D.widths[f];
+  const A* sub = (const A*)a.subkeys + (long long)h * sumn * D.dk;
+  const int Fdk = D.F * D.dk;
+  for (int x = threadIdx.x; x < 2 * Fdk; x += 256) {
+    const int kind = x >= Fdk;
+    const int fc = x - kind * Fdk;
+    const int f = fc / D.dk, c = fc % D.dk;
+    long long stride = 1, off = 0;
+    for (int g = D.F - 1; g > f; --g) stride *= D.widths[g];
+    for (int g = 0; g < f; ++g) off += D.widths[g];
+    const int n = kind ? R : W;
+    const int32_t* ids = kind ? a.ridx + so * R : a.widx + so * W;
+    const float* dsk = sd + (kind ? W : 0);
+    float acc = 0.f;
+    for (int i = 0; i < n; ++i) {
+      const int sf = (int)((ids[i] / stride) % D.widths[f]);
+      acc += dsk[i] * to_f<A>(sub[(off + sf) * D.dk + c]);
+    }
+    (kind ? a.grq : a.gwkeys)[row * Fdk + fc] = acc;
+  }
+}
+
+// Sub-key partial sums of one block of 128 token rows of head h (rows ordered b-major), factor f, `cb` columns:
+// one wave, lane c owns column c of every sub-key of the factor (LDS accumulators), terms in order.
+template <typename A>
+__global__ __launch_bounds__(64) void bwd_subkey_kernel(Dims D, BwdArgs a, int cb, int ncb) {
+  extern __shared__ __align__(16) float acc[];  // [n_f][cb]
+  const int rb = blockIdx.x, h = blockIdx.y, f = blockIdx.z / ncb, cblk = blockIdx.z % ncb;
+  const int n = D.widths[f], lane = threadIdx.x;
+  const int c = cblk * cb + lane;
+  const bool on = lane < cb && c < D.dk;
+  for (int i = lane; i < n * cb; i += 64) acc[i] = 0.f;
+  __syncthreads();
+  long long stride = 1, off = 0, sumn = 0;
+  for (int g = D.F - 1; g > f; --g) stride *= D.widths[g];
+  for (int g = 0; g < f; ++g) off += D.widths[g];
+  for (int g = 0; g < D.F; ++g) sumn += D.widths[g];
+  const int W = D.W, R = D.R, T = D.T, Fdk = D.F * D.dk;
+  const int r0 = rb * 128, r1 = min(r0 + 128, D.B * T);
+  for (int r = r0; r < r1; ++r) {
+    const int b = r / T, t = r % T;
+    const long long so = ((long long)b * D.H + h) * T + t;
+    const long long row = ((long long)b * T + t) * D.H + h;
+    const float xw = on ? to_f<A>(((const A*)a.wkeys)[row * Fdk + f * D.dk + c]) : 0.f;
+    const float xr = on ? to_f<A>(((const A*)a.rq)[row * Fdk + f * D.dk + c]) : 0.f;
+    const float* ds = a.ds + so * (W + R);
+    for (int i = 0; i < W + R; ++i) {
+      const int slot = i < W ? a.widx[so * W + i] : a.ridx[so * R + (i - W)];
+      const int sf = (int)((slot / stride) % n);
+      if (on) acc[sf * cb + lane] += ds[i] * (i < W ? xw : xr);
+    }
+  }
+  __syncthreads();
+  if (on)
+    for (int i = 0; i < n; ++i) a.sgpart[(((long long)rb * D.H + h) * sumn + off + i) * D.dk + c] = acc[i * cb + lane];
+}
+
+__global__ __launch_bounds__(256) void bwd_subkey_sum_kernel(const float* __restrict__ sgpart, float* __restrict__ gsub,
+                                                             long long n, int nrb) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.f;
+  for (int rb = 0; rb < nrb; ++rb) s += sgpart[(long long)rb * n + i];
+  gsub[i] = s;
+}
+
+template <typename A, typename Bk>
+static hipError_t launch_bwd_t(const Dims& D, const BwdArgs& a, hipStream_t st) {
+  const int nsl = bwd_slices(D);
+  const size_t lds = bwd_sweep_lds(D.W);
+  (void)hipFuncSetAttribute((const void*)bwd_sweep_kernel<A, Bk>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipLaunchKernelGGL((bwd_sweep_kernel<A, Bk>), dim3((unsigned)((long long)D.S * nsl)), dim3(BWD_NT), lds, st, D, a,
+                     nsl);
+  hipLaunchKernelGGL((bwd_token_kernel<A>), dim3((unsigned)((long long)D.S * D.T)), dim3(256), 0, st, D, a, nsl);
+  const int nrb = bwd_row_blocks(D);
+  long long sumn = 0;
+  int nmax = 0;
+  for (int f = 0; f < D.F; ++f) {
+    sumn += D.widths[f];
+    nmax = max(nmax, D.widths[f]);
+  }
+  int cb = 64;
+  while (cb > 1 && (size_t)nmax * cb * 4 > 64 * 1024) cb >>= 1;
+  const int ncb = (D.dk + cb - 1) / cb;
+  const size_t slds = (size_t)nmax * cb * 4;
+  (void)hipFuncSetAttribute((const void*)bwd_subkey_kernel<A>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)slds);
+  hipLaunchKernelGGL((bwd_subkey_kernel<A>), dim3((unsigned)nrb, (unsigned)D.H, (unsigned)(D.F * ncb)), dim3(64), slds,
+                     st, D, a, cb, ncb);
+  const long long n = (long long)D.H * sumn * D.dk;
+  hipLaunchKernelGGL(bwd_subkey_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.sgpart, a.gsub, n,
+                     nrb);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(const Dims& D, const BwdArgs& a, hipStream_t st) {
+  if (D.S == 0 || D.T == 0) return hipSuccess;
+  if (D.act == SDM_BF16)
+    return D.bank == SDM_BF16 ? launch_bwd_t<bf16_t, bf16_t>(D, a, st) : launch_bwd_t<bf16_t, float>(D, a, st);
+  return D.bank == SDM_BF16 ? launch_bwd_t<float, bf16_t>(D, a, st) : launch_bwd_t<float, float>(D, a, st);
+}
+
+}  // namespace sdm

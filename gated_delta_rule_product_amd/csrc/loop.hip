@@ -248,6 +248,8 @@ __global__ __launch_bounds__(LOOP_NT) void loop_kernel(Dims D, LoopArgs a, int n
       segs = (const Seg*)sReg;
     }
     const Ev* ev = (const Ev*)(segs + cnt.nseg);
+    // snapshot rows of this stream's chunk: row (t, i) = [t * W + i] * d
+    Bk* snap = a.snap ? (Bk*)a.snap + ((long long)st * D.T + t0) * D.W * D.d + mycol : nullptr;
     if (valid) {
       constexpr int UB = 8;
       for (int sg0 = wv * 16 + grp; sg0 < cnt.nseg; sg0 += NW * 16 * UB) {
@@ -272,9 +274,11 @@ __global__ __launch_bounds__(LOOP_NT) void loop_kernel(Dims D, LoopArgs a, int n
           if (p[u]) {
             for (int e = beg[u]; e < end[u]; ++e) {
               const Ev x = ev[e];
-              const float al = sA[x.tok];
+              const int tk = x.tok & 0xFFFF;
+              if (snap) Lane<Bk>::store(snap + ((long long)tk * D.W + (x.tok >> 16)) * D.d, m[u]);
+              const float al = sA[tk];
 #pragma unroll
-              for (int k = 0; k < EPL; ++k) m[u][k] = al * m[u][k] + x.w * sD[x.tok * COLS + q * EPL + k];
+              for (int k = 0; k < EPL; ++k) m[u][k] = al * m[u][k] + x.w * sD[tk * COLS + q * EPL + k];
             }
             Lane<Bk>::store(p[u], m[u]);
           }
@@ -1154,7 +1158,7 @@ static hipError_t launch_loop_t(const Dims& D, const LoopArgs& a, hipStream_t st
   const size_t staged = loop_lds_bytes(D.C, D.W, D.R, COLS, true);
   const int gpt = 128 / D.C;
   if constexpr (sizeof(Bk) == 4) {
-    if (loop_held_path(D)) {
+    if (loop_held_path(D) && !a.snap) {
       const size_t lds = loop_held_lds_bytes(D.C, D.W, D.R, COLS);
       if (D.W / gpt == Hold<Bk>::N && D.R / gpt == Hold<Bk>::N) {
         (void)hipFuncSetAttribute((const void*)loop_held_kernel<A, Bk, true>,
@@ -1170,7 +1174,7 @@ static hipError_t launch_loop_t(const Dims& D, const LoopArgs& a, hipStream_t st
       return hipGetLastError();
     }
   }
-  if (loop_narrow_path(D)) {
+  if (loop_narrow_path(D) && !a.snap) {
     const size_t lds = loop_narrow_lds_bytes(D.C, Lane<Bk>::EPL);
     const int ns = D.d / Lane<Bk>::EPL;
     const long long nb = (long long)D.S * ns;

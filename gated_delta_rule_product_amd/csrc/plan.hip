@@ -402,6 +402,7 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
       Ev x;
       x.w = sw[e];
       x.tok = evi / W;
+      if (a.evcode) x.tok |= (evi % W) << 16;
       if (a.scat) ev[e] = x;
       if (multi) {
         mev[me++] = x;

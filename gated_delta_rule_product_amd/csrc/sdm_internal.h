@@ -55,7 +55,7 @@ struct TopkPlan {
 // One scatter event of a chunk: (weight, chunk-local token), sorted by (slot, token).
 struct Ev {
   float w;
-  int32_t tok;
+  int32_t tok;  // chunk-local token; with PlanArgs::evcode also the event's term index in bits 16..31
 };
 
 // One sparse entry (column, value) of a row-sorted list: T = (I + diag(alpha beta) K)^-1 or the read coupling Q.
@@ -205,6 +205,9 @@ struct WsLayout {
   size_t chunks;                               // [S * nch] chunk plan regions (chunk_layout)
   size_t counts;                               // [S * nch] ChunkCounts
   size_t owner, conflict;                      // shared bank: int32 [H][N] first stream of each slot; int32 flag
+  size_t part;                                 // backward: float [slices][S][T][W + R + 2] per-slice dot products
+  size_t ds;                                   // backward: float [S][T][W + R] slot-score gradients
+  size_t sgpart;                               // backward: float [row blocks][H][sum n_f][dk] sub-key partial sums
   size_t total;
 };
 
@@ -239,6 +242,7 @@ struct PlanArgs {
   int scat;               // also write the slot segments and their events (read by loop_kernel only)
   int lanemajor;          // write the gather terms lane-major for the narrow loop (term_pos)
   const int32_t* abort;   // if not NULL and *abort != 0: do nothing (shared-bank conflict)
+  int evcode;             // events also carry their term index (Ev::tok bits 16..31), for the snapshot
 };
 
 // Position of gather term i (of n per token) of chunk-local token t in a chunk's term section. Token-major: t n + i.
@@ -265,6 +269,8 @@ struct LoopArgs {
   const ChunkCounts* counts;
   void* bank; void* out;
   const int32_t* abort;   // if not NULL and *abort != 0: do nothing (shared-bank conflict)
+  void* snap;             // if not NULL: [S][T][W][d] bank dtype, the row of every write event before it (the
+                          // segmented loop_kernel writes it; needs PlanArgs::evcode)
 };
 hipError_t launch_loop(const Dims& D, const LoopArgs& a, hipStream_t st);
 // True if launch_loop runs the held-row variant (which reads last-event codes, not slot segments).
@@ -273,6 +279,22 @@ bool loop_held_path(const Dims& D);
 bool loop_narrow_path(const Dims& D);
 // True if it runs the narrow variant with 16 terms of each kind per lane, which reads lane-major terms.
 bool loop_narrow_lanemajor(const Dims& D);
+
+// Backward of the write/read (bwd.hip). Ids and weights are the forward's (recomputed top-k, stream-major).
+struct BwdArgs {
+  const int32_t* widx; const float* wwt; const int32_t* ridx; const float* rwt;  // [S][T][W|R]
+  const void* wkeys; const void* rq; const void* subkeys;                         // activation dtype
+  const void* alpha; const void* beta; const void* values; const void* gout;      // activation dtype
+  void* bank;             // [S][rows][ld] bank dtype: after the forward on entry, before it on return
+  const void* snap;       // [S][T][W][d] bank dtype
+  float* gbank;           // [S][rows][ld]: gradient w.r.t. the bank after the call in, before the call out
+  float* gwkeys; float* grq; float* gvalues; float* galpha; float* gbeta; float* gsub;
+  float* part; float* ds; float* sgpart;  // workspace
+};
+// Slices of 16 columns the backward sweep splits a row into, and the row blocks of the sub-key sums.
+inline int bwd_slices(const Dims& D) { return (D.d + 15) / 16; }
+inline int bwd_row_blocks(const Dims& D) { return (D.B * D.T + 127) / 128; }
+hipError_t launch_bwd(const Dims& D, const BwdArgs& a, hipStream_t st);
 
 struct DecodeArgs {
   const void* values; const void* alpha; const void* beta;

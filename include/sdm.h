@@ -94,7 +94,7 @@ typedef struct {
   int32_t reserved;         /* 0 */
 } sdm_config;
 
-enum { SDM_OP_TOPK = 0, SDM_OP_WRITE_READ = 1, SDM_OP_DECODE = 2 };
+enum { SDM_OP_TOPK = 0, SDM_OP_WRITE_READ = 1, SDM_OP_DECODE = 2, SDM_OP_BACKWARD = 3 };
 
 /* Message for the last non-OK status returned on the calling thread ("" if none). Valid until the next call. */
 const char* sdm_last_error(void);
@@ -121,6 +121,35 @@ sdm_status sdm_write_read(const sdm_config* cfg, const void* write_keys, const v
                           const void* values, const void* forget_gate, const void* input_gate, const void* subkeys,
                           void* bank, void* out, int32_t* write_idx, int32_t* read_idx, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/* Training forward (CHANGELOG 2.0.0: training saves a backward snapshot; "Known limitations": the backward restores
+ * the bank in place). sdm_write_read, plus `snapshot` [B, H, T, W, d] in the bank dtype (dense rows, caller-owned):
+ * row (b, h, t, i) receives the row of slot write_idx[b, t, h, i] as it was just before token t's write (i in top-k
+ * order, best first). The workspace is sdm_write_read's (SDM_OP_WRITE_READ). Refused (SDM_ERR_RANGE) with
+ * shared_bank, or when B * H * T * W reaches 2^31 rows (CHANGELOG 2.0.0, "New": a snapshot of 2^31 rows is refused
+ * before any work). Results equal sdm_write_read's up to rounding (this call always runs the segmented chunk loop). */
+sdm_status sdm_write_read_save(const sdm_config* cfg, const void* write_keys, const void* read_queries,
+                               const void* values, const void* forget_gate, const void* input_gate,
+                               const void* subkeys, void* bank, void* out, void* snapshot, int32_t* write_idx,
+                               int32_t* read_idx, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Deterministic backward of the write/read (CHANGELOG 2.0.0, "Deterministic": every gradient bitwise repeatable;
+ * "New": exact product-key top-k with a deterministic sparse backward; "Known limitations": the first backward
+ * restores the bank in place). Inputs are the forward's (same cfg, keys, queries, values, gates, sub-keys), `bank`
+ * as the forward left it, the forward's `snapshot`, and grad_out [B, T, H, d] (act dtype). On return `bank` is the
+ * bank before the forward, bit for bit. grad_bank (float32, [B, H, bank_rows, bank_row_stride], the bank's row
+ * layout) holds the gradient w.r.t. the bank after the forward on entry (zeros if none) and the gradient w.r.t. the
+ * bank before it on return. Written (float32, overwritten): grad_write_keys, grad_read_queries [B, T, H, F*dk],
+ * grad_values [B, T, H, d], grad_forget_gate, grad_input_gate [B, T, H], grad_subkeys [H, sum n_f, dk] (summed over
+ * the batch). The selection itself has no gradient; the gradient reaches keys, queries and sub-keys through the
+ * softmax weights of the selected slots, whose scores are sums of factor scores. Workspace: SDM_OP_BACKWARD. The
+ * bank and the snapshot are consumed: a second backward of the same forward needs the forward run again. */
+sdm_status sdm_write_read_backward(const sdm_config* cfg, const void* write_keys, const void* read_queries,
+                                   const void* values, const void* forget_gate, const void* input_gate,
+                                   const void* subkeys, void* bank, const void* snapshot, const void* grad_out,
+                                   float* grad_bank, float* grad_write_keys, float* grad_read_queries,
+                                   float* grad_values, float* grad_forget_gate, float* grad_input_gate,
+                                   float* grad_subkeys, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Shared bank (CHANGELOG 2.0.0, "Behavior changes": a direct write/read call that runs several streams over one
  * shared bank must say so, which asserts that the streams' slots are disjoint). With cfg.shared_bank = 1,
@@ -156,7 +185,8 @@ typedef enum {
   SDM_K_LOOP = 3,   /* chunk loop: gather, solve, read, scatter */
   SDM_K_DECODE = 4, /* decode step */
   SDM_K_COPY = 5,   /* successor copy */
-  SDM_K_COUNT = 6
+  SDM_K_BWD = 6,    /* backward: reverse sweep, token sums, sub-key sums */
+  SDM_K_COUNT = 7
 } sdm_kernel;
 sdm_status sdm_profile_enable(int32_t on);
 sdm_status sdm_profile_read(double* ms, int64_t* launches);

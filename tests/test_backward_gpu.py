@@ -1,0 +1,156 @@
+"""GPU parity of the backward (sdm_write_read_save + sdm_write_read_backward, through the C ABI) against the oracle's
+backward (fp64, bank states rounded like the forward after every token).
+
+Checked: every gradient (write keys, read queries, values, both gates, sub-keys, the bank before the call) within the
+tolerances below; the bank stepped back to its state before the forward bit for bit; the snapshot's rows of each
+stream's first token equal the initial bank rows bit for bit; repeated backward calls give the same bits.
+
+Tolerances (row-wise infinity-norm relative error; a gate gradient row is the H values of a token): the backward
+accumulates in float32 over the token sweep where the oracle uses fp64, and it differentiates the forward the GPU
+ran (bank rounded once per chunk) where the oracle differentiates its own (rounded after every token); activations
+enter both sides with the same values and every gradient is float32, so the tolerance follows the bank dtype. Float32
+banks: 1e-4 (the adjoint of a row passes through a few hundred float32 operations over the tokens that touch it;
+measured 1e-7 to 2e-5). Bfloat16 banks: 3e-2 (the bf16 tolerance of the forward, 2e-2, plus the spread of rounding
+points; measured up to 1e-2).
+A row's scale is at least 1e-3 of the tensor's largest value: gradient rows are sums whose terms can cancel (the
+softmax derivative sums to zero over a token's terms, so a sub-key shared by all of them gets an exact zero in fp64
+and float32 rounding residue on the GPU); their error is bounded by the terms' size, not by the sum's.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_delta_rule_product_amd import binding, synth
+
+DEV = torch.device("cuda:0")
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+pytestmark = pytest.mark.gpu
+
+
+def rowwise_rel(got, ref, floor=0.0):
+    """max over rows of |got - ref|_inf / max(|ref row|_inf, floor * |ref|_inf)."""
+    got = np.asarray(got, np.float64).reshape(-1, got.shape[-1])
+    ref = np.asarray(ref, np.float64).reshape(-1, ref.shape[-1])
+    err = np.abs(got - ref).max(axis=1)
+    scale = np.maximum(np.abs(ref).max(axis=1), max(floor * float(np.abs(ref).max()), 1e-30))
+    return float((err / scale).max())
+
+
+def to_dev(x, dtype):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV).to(dtype)
+
+
+FLOOR = 1e-3
+
+
+def _tol(s):
+    return 1e-4 if s.bank == "f32" else 3e-2
+
+
+def _upstream(s, seed, with_bank_grad):
+    rng = np.random.default_rng(seed)
+    dout = rng.standard_normal((s.batch, s.tokens, s.heads, s.head_dim)).astype(np.float32)
+    if s.act == "bf16":
+        dout = synth.round_bf16_rne(dout)
+    dbank = rng.standard_normal((s.batch, s.heads, s.rows, s.head_dim)).astype(np.float32) if with_bank_grad else None
+    return dout, dbank
+
+
+def run_gpu(s, x, dout, dbank, pitch=None):
+    at, bt = TORCH_DT[s.act], TORCH_DT[s.bank]
+    t = {k: to_dev(x[k], at) for k in ("wkeys", "rq", "values", "alpha", "beta", "subkeys")}
+    if pitch is None:
+        bank = to_dev(x["bank"], bt)
+    else:
+        buf = torch.zeros((s.batch, s.heads, s.rows, pitch), dtype=bt, device=DEV)
+        bank = buf[..., :s.head_dim]
+        bank.copy_(to_dev(x["bank"], bt))
+    bank0 = bank.clone()
+    kw = dict(widths=s.widths, num_writes=s.num_writes, num_reads=s.num_reads, chunk_size=s.chunk_size)
+    out, widx, _, snap = binding.sdm_write_read_save(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"],
+                                                     t["subkeys"], bank, want_index=True, **kw)
+    gbank = None
+    if dbank is not None:
+        ld = bank.stride(2)
+        gbank = torch.zeros((s.batch, s.heads, s.rows, ld), dtype=torch.float32, device=DEV)[..., :s.head_dim]
+        gbank.copy_(to_dev(dbank, torch.float32))
+    g = binding.sdm_write_read_backward(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"], t["subkeys"], bank,
+                                        snap, to_dev(dout, at), gbank, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(bank, bank0), "the backward did not restore the bank bit for bit"
+    # the first token's snapshot rows are initial bank rows
+    w0 = widx[:, 0].long()  # [B, H, W]
+    first = torch.stack([torch.stack([bank0[b, h, w0[b, h]] for h in range(s.heads)]) for b in range(s.batch)])
+    assert torch.equal(snap[:, :, 0], first)
+    return {k: v.cpu().numpy() for k, v in g.items()}, out.float().cpu().numpy()
+
+
+def run_oracle(s, x, dout, dbank):
+    return oracle.write_read_backward(x["wkeys"], x["rq"], x["values"], x["alpha"], x["beta"], x["subkeys"],
+                                      x["bank"], dout, dbank, s.widths, s.num_writes, s.num_reads,
+                                      bank_bf16=s.bank == "bf16")
+
+
+NAMES = {"write_keys": "d_wkeys", "read_queries": "d_rq", "values": "d_values", "subkeys": "d_subkeys",
+         "bank": "d_bank"}
+
+
+def check(s, got, ref, tol):
+    errs = {}
+    for k, r in NAMES.items():
+        errs[k] = rowwise_rel(got[k], ref[r], FLOOR)
+    for k, r in (("forget_gate", "d_alpha"), ("input_gate", "d_beta")):
+        errs[k] = rowwise_rel(got[k], ref[r], FLOOR)
+    print("gradient errors", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, f"gradients beyond {tol}: {bad}"
+
+
+CASES = [
+    # name, shape, with a bank gradient
+    ("tiny", synth.WORKLOADS["tiny_1k"].with_(tokens=96, batch=2, heads=2, chunk_size=32), True),
+    ("ragged_c7", synth.WORKLOADS["tiny_1k"].with_(tokens=50, batch=1, heads=2, chunk_size=7), False),
+    ("collide", synth.Shape(1, 64, 2, (8, 8), 4, 32, 16, 16, 16, name="collide"), True),
+    ("three_factors", synth.Shape(1, 40, 2, (8, 4, 4), 8, 32, 16, 12, 16, name="f3"), True),
+    ("bf16_act", synth.Shape(2, 48, 2, (16, 16), 8, 64, 8, 8, 16, "bf16", "f32", name="bf16a"), True),
+    ("bf16_bank", synth.Shape(1, 48, 2, (16, 16), 8, 64, 8, 8, 16, "bf16", "bf16", name="bf16b"), True),
+    ("wide_w", synth.Shape(1, 24, 1, (16, 16), 8, 48, 160, 136, 8, name="wide"), True),
+]
+
+
+@pytest.mark.parametrize("name,s,bank_grad", CASES, ids=[c[0] for c in CASES])
+def test_backward_matches_oracle(name, s, bank_grad):
+    x = synth.make_inputs(s, seed=41)
+    dout, dbank = _upstream(s, 42, bank_grad)
+    print(f"backward {name}: {s}", flush=True)
+    got, _ = run_gpu(s, x, dout, dbank)
+    check(s, got, run_oracle(s, x, dout, dbank), _tol(s))
+
+
+def test_backward_padded_pitch_and_repeatable():
+    s = synth.WORKLOADS["tiny_1k"].with_(tokens=64, batch=1, heads=2, chunk_size=16)
+    x = synth.make_inputs(s, seed=43)
+    dout, dbank = _upstream(s, 44, True)
+    print("backward pitch 80 / repeat", flush=True)
+    a, out_a = run_gpu(s, x, dout, dbank, pitch=80)
+    b, out_b = run_gpu(s, x, dout, dbank)
+    assert np.array_equal(out_a, out_b)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), f"{k} differs between calls"
+    check(s, a, run_oracle(s, x, dout, dbank), _tol(s))
+
+
+def test_save_forward_matches_plain_forward_within_rounding():
+    """The saving forward runs the segmented loop; its outputs equal the plain forward's up to rounding."""
+    s = synth.WORKLOADS["tiny_1k"].with_(tokens=80, batch=2, heads=2, chunk_size=16)
+    x = synth.make_inputs(s, seed=45)
+    t = {k: to_dev(x[k], torch.float32) for k in ("wkeys", "rq", "values", "alpha", "beta", "subkeys")}
+    kw = dict(widths=s.widths, num_writes=s.num_writes, num_reads=s.num_reads, chunk_size=s.chunk_size)
+    b1, b2 = to_dev(x["bank"], torch.float32), to_dev(x["bank"], torch.float32)
+    o1, _, _ = binding.sdm_write_read(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"], t["subkeys"], b1, **kw)
+    o2, _, _, _ = binding.sdm_write_read_save(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"], t["subkeys"],
+                                              b2, **kw)
+    torch.cuda.synchronize()
+    assert rowwise_rel(o2.cpu().numpy(), o1.cpu().numpy()) <= 1e-5
+    assert rowwise_rel(b2.cpu().numpy(), b1.cpu().numpy()) <= 1e-5
