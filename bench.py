@@ -136,6 +136,70 @@ def bench_write_read(args, torch, binding, synth):
     }
 
 
+def bench_train(args, torch, binding, synth):
+    """Training step of the layer workload: the snapshot-saving forward, then the backward (which steps the bank
+    back, so every step starts from the same bank). Context line, not the headline value."""
+    s = synth.WORKLOADS["layer_65k"]
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16}
+    dev = torch.device("cuda:0")
+    log("[bench] train: inputs")
+    x = synth.make_inputs(s)
+    t = {k: torch.from_numpy(x[k]).to(dev).to(dt[s.act]) for k in ("wkeys", "rq", "values", "alpha", "beta",
+                                                                    "subkeys")}
+    pitch = binding.bank_pitch(s.head_dim, dt[s.bank])
+    bank = binding.alloc_bank(s.batch, s.heads, s.rows, s.head_dim, dt[s.bank], dev, pitch=pitch)
+    bank.copy_(torch.from_numpy(x["bank"]).to(dev).to(dt[s.bank]))
+    del x
+    bank0 = bank.clone()
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    gout = torch.randn((s.batch, s.tokens, s.heads, s.head_dim), generator=gen, device=dev).to(dt[s.act])
+    gbank = torch.zeros((s.batch, s.heads, s.rows, pitch), dtype=torch.float32, device=dev)[..., :s.head_dim]
+    kw = dict(widths=s.widths, num_writes=s.num_writes, num_reads=s.num_reads, chunk_size=s.chunk_size)
+    out, _, _, snap = binding.sdm_write_read_save(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"],
+                                                  t["subkeys"], bank, **kw)
+    cfg = binding.make_config(s.batch, s.tokens, s.heads, s.widths, s.subkey_dim, s.head_dim, s.num_writes,
+                              s.num_reads, s.chunk_size, binding.SDM_BF16 if s.act == "bf16" else binding.SDM_F32,
+                              binding.SDM_BF16 if s.bank == "bf16" else binding.SDM_F32, s.rows, pitch)
+    wsf = torch.empty(binding.workspace_size(cfg, binding.SDM_OP_WRITE_READ), dtype=torch.uint8, device=dev)
+    wsb = torch.empty(binding.workspace_size(cfg, binding.SDM_OP_BACKWARD), dtype=torch.uint8, device=dev)
+    g = binding.sdm_write_read_backward(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"], t["subkeys"], bank,
+                                        snap, gout, gbank, workspace=wsb, **kw)
+    torch.cuda.synchronize()
+    restored = bool(torch.equal(bank, bank0))
+    del bank0
+    n = max(1, min(args.steps, 5))
+    tf = tb = 0.0
+    binding.profile_enable(True)
+    log(f"[bench] train: {n} steps")
+    for _ in range(n):
+        gbank.zero_()
+        torch.cuda.synchronize()
+        a = time.perf_counter()
+        binding.sdm_write_read_save(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"], t["subkeys"], bank,
+                                    out=out, snapshot=snap, workspace=wsf, **kw)
+        torch.cuda.synchronize()
+        b = time.perf_counter()
+        binding.sdm_write_read_backward(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"], t["subkeys"], bank,
+                                        snap, gout, gbank, workspace=wsb, **kw)
+        torch.cuda.synchronize()
+        c = time.perf_counter()
+        tf += b - a
+        tb += c - b
+    prof = binding.profile_read()
+    binding.profile_enable(False)
+    ms_f, ms_b = tf * 1e3 / n, tb * 1e3 / n
+    res = {"tokens_per_s": round(s.batch * s.tokens / ((ms_f + ms_b) * 1e-3), 1),
+           "ms_forward_save": round(ms_f, 4), "ms_backward": round(ms_b, 4), "steps": n,
+           "kernels_avg_ms": {k: round(v[0] / v[1], 4) for k, v in prof.items() if v[1]},
+           "snapshot_bytes": snap.numel() * snap.element_size(), "bank_restored_bitwise": restored,
+           "config": "layer_65k (as the headline), grad_out ~ N(0,1), float32 gradients"}
+    log(f"[bench] train: forward+snapshot {ms_f:.3f} ms, backward {ms_b:.3f} ms")
+    del g, snap, gbank, bank, wsf, wsb, out, t, gout
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_other(args, torch, binding, synth):
     """The three-factor (65,536 slots, bf16 bank, chunk 128) and 1,048,576-slot (32 GiB float32 bank) workloads at
     full size: tokens/s and the chunk loop's algorithmic bandwidth. Context lines, not the headline value."""
@@ -343,6 +407,7 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=0, help="tokens of the oracle sample (0: the whole workload)")
     ap.add_argument("--other-steps", type=int, default=3, help="timed calls of each context workload (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-train", dest="train", action="store_false", help="skip the training-step context line")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -359,6 +424,7 @@ def main():
     binding.load()
     wr = bench_write_read(args, torch, binding, synth)
     dec = bench_decode(args, torch, binding, synth)
+    train = bench_train(args, torch, binding, synth) if args.train else None
     other = bench_other(args, torch, binding, synth) if args.other_steps > 0 else None
     s = wr["shape"]
     line = {
@@ -376,6 +442,7 @@ def main():
         "kernels_avg_ms": wr["kernels_avg_ms"],
         "roofline": wr["roofline"],
         "decode": dec,
+        "train": train,
         "other_workloads": other,
     }
     if not args.no_cpu_baseline:
