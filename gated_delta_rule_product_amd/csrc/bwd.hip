@@ -34,15 +34,31 @@ template <> struct Raw4<float> {
     for (int k = 0; k < 4; ++k) v[k] = __uint_as_float(x[k]);
   }
 };
+typedef unsigned int w8_t __attribute__((ext_vector_type(2)));  // 8 bytes as a native vector (not a struct)
 template <> struct Raw4<bf16_t> {
-  typedef uint2 T;
-  __device__ static T load(const bf16_t* p) { return *(const uint2*)p; }
-  __device__ static void store(bf16_t* p, T x) { *(uint2*)p = x; }
+  typedef w8_t T;
+  __device__ static T load(const bf16_t* p) { return *(const w8_t*)p; }
+  __device__ static void store(bf16_t* p, T x) { *(w8_t*)p = x; }
   __device__ static void unpack(T x, float* v) {
-    v[0] = __uint_as_float(x.x << 16);
-    v[1] = __uint_as_float(x.x & 0xFFFF0000u);
-    v[2] = __uint_as_float(x.y << 16);
-    v[3] = __uint_as_float(x.y & 0xFFFF0000u);
+    v[0] = __uint_as_float(x[0] << 16);
+    v[1] = __uint_as_float(x[0] & 0xFFFF0000u);
+    v[2] = __uint_as_float(x[1] << 16);
+    v[3] = __uint_as_float(x[1] & 0xFFFF0000u);
+  }
+};
+
+// An activation element through a 32-bit word: the float itself, or for bfloat16 the aligned 4-byte word that
+// contains it (never crossing a page), its half picked where the value is used. A 16-bit value kept in a
+// loop-carried register gets re-masked by the compiler right after its load, which makes it wait for that load.
+template <typename A> struct Word;
+template <> struct Word<float> {
+  __device__ static uint32_t load(const float* p) { return __float_as_uint(*p); }
+  __device__ static float get(uint32_t w, const float*) { return __uint_as_float(w); }
+};
+template <> struct Word<bf16_t> {
+  __device__ static uint32_t load(const bf16_t* p) { return *(const uint32_t*)((uintptr_t)p & ~(uintptr_t)3); }
+  __device__ static float get(uint32_t w, const bf16_t* p) {
+    return __uint_as_float(((uintptr_t)p & 2) ? (w & 0xFFFF0000u) : (w << 16));
   }
 };
 
@@ -199,6 +215,228 @@ __global__ __launch_bounds__(BWD_NT) void bwd_sweep_kernel(Dims D, BwdArgs a, in
   }
 }
 
+// The same sweep for W, R <= 128 (one write and one read term per 4-lane group), with one HBM round trip per token:
+// the read rows, their G rows and the write terms' G rows of token t are loaded together, with the snapshot rows,
+// gates and output gradient of token t - 1 and the ids of token t - 2 (read-only data, loaded ahead). A write slot
+// that token t also reads gets the read's G update (rho_j dout) added in registers: its loaded G row predates that
+// update; the read terms' slots go to a small LDS hash (slot -> rho) for that lookup. Sums over the write terms: a
+// fixed shuffle tree inside each wave, then the 8 wave partials in order. The loads of token t - 1's rows follow the
+// end-of-token barrier, after every store of token t in the workgroup's program order (one CU: its vector memory
+// pipeline keeps that order).
+constexpr int BWD_HASH = 256;
+
+__device__ __forceinline__ int bwd_hash(int slot) { return (int)(((uint32_t)slot * 2654435761u) >> 24); }
+
+template <typename A, typename Bk>
+__global__ __launch_bounds__(BWD_NT) void bwd_sweep_fast_kernel(Dims D, BwdArgs a, int nsl) {
+  __shared__ float sRedD[8][BWD_COLS], sRedR[8][BWD_COLS], sRedGP[8];
+  __shared__ float sDel[BWD_COLS], sDt[BWD_COLS];
+  __shared__ uint32_t hkey[BWD_HASH];
+  __shared__ float hrho[BWD_HASH];
+  typedef typename Raw4<Bk>::T RawT;
+  typedef typename Raw4<A>::T ARaw;
+  const int W = D.W, R = D.R, T = D.T, d = D.d;
+  const int nblk = gridDim.x;
+  int wk = blockIdx.x;
+  if ((nblk & 7) == 0) wk = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+  const int st = wk / nsl, slice = wk % nsl;
+  const int b = st / D.H, h = st % D.H;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, grp = tid >> 2, q = tid & 3;
+  const int col = slice * BWD_COLS + q * 4;
+  const bool valid = col < d;
+  const bool hasR = grp < R, hasW = grp < W;
+  const int P = W + R + 2;
+  Bk* bank = (Bk*)a.bank + (long long)st * D.rows * D.ld;
+  float* gbank = a.gbank + (long long)st * D.rows * D.ld;
+  const Bk* snap = (const Bk*)a.snap + (long long)st * T * W * d;
+  const A* gout = (const A*)a.gout;
+  const A* values = (const A*)a.values;
+  const A* alpha = (const A*)a.alpha;
+  const A* beta = (const A*)a.beta;
+  for (int i = tid; i < BWD_HASH; i += BWD_NT) hkey[i] = 0u;
+
+  // Inputs of a token loaded ahead are kept raw and converted where they are used: a conversion next to its load
+  // would make the compiler wait for every load issued before it (this token's rows included). The gates are uniform
+  // over the workgroup; through the scalar cache they would count against the LDS counter that every barrier
+  // drains, so they take the vector path (zero is 0 on every lane but not provably uniform).
+  // (separate variables, not a struct: a struct copy becomes a byte-wise memcpy that needs the loaded data at once)
+  const int zero = (int)__builtin_amdgcn_mbcnt_lo(0u, 0u);
+  const int vcol = min(slice * BWD_COLS + (tid & (BWD_COLS - 1)), d - 1);  // in range for every thread
+  const int dcol = valid ? col : 0;
+  auto load_ids = [&](int t, int& rs, float& rho, int& ws, float& w) {
+    const long long so = (long long)st * T + t;
+    rs = hasR ? a.ridx[so * R + grp] : 0;
+    rho = hasR ? a.rwt[so * R + grp] : 0.f;
+    ws = hasW ? a.widx[so * W + grp] : 0;
+    w = hasW ? a.wwt[so * W + grp] : 0.f;
+  };
+  auto load_tok = [&](int t, uint32_t& al_, uint32_t& be_, uint32_t& v_, ARaw& dout_, RawT& sp_) {
+    const long long row = ((long long)b * T + t) * D.H + h;
+    al_ = Word<A>::load(alpha + row + zero);
+    be_ = Word<A>::load(beta + row + zero);
+    dout_ = Raw4<A>::load(gout + row * d + dcol);
+    v_ = Word<A>::load(values + row * d + vcol);
+    // unconditional (a load under a branch merged with a default value costs a wait): other lanes read element 0
+    sp_ = Raw4<Bk>::load(snap + (hasW && valid ? ((long long)t * W + grp) * d + col : 0));
+  };
+
+  int rs, ws, rs1 = 0, ws1 = 0;
+  float rho, w, rho1 = 0.f, w1 = 0.f;
+  uint32_t c_al, c_be, c_v;
+  ARaw c_dout;
+  RawT c_sp;
+  load_ids(T - 1, rs, rho, ws, w);
+  if (T >= 2) load_ids(T - 2, rs1, rho1, ws1, w1);
+  load_tok(T - 1, c_al, c_be, c_v, c_dout, c_sp);
+  __syncthreads();  // hash table cleared
+
+  for (int t = T - 1; t >= 0; --t) {
+    const long long so = (long long)st * T + t;
+    const long long row = ((long long)b * T + t) * D.H + h;
+    float* part = a.part + ((long long)slice * D.S * T + so) * P;
+    // this token's rows
+    RawT rb;
+    memset(&rb, 0, sizeof rb);
+    float4 rg = make_float4(0.f, 0.f, 0.f, 0.f), wg = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (valid && hasR) {
+      rb = Raw4<Bk>::load(bank + (long long)rs * D.ld + col);
+      rg = *(const float4*)(gbank + (long long)rs * D.ld + col);
+    }
+    if (valid && hasW) wg = *(const float4*)(gbank + (long long)ws * D.ld + col);
+    // ahead: token t - 1's inputs and snapshot rows, token t - 2's ids
+    // (unconditional, token index clamped at 0: a branch around them would merge registers still in flight)
+    uint32_t n_al, n_be, n_v;
+    ARaw n_dout;
+    RawT n_sp;
+    int rs2, ws2;
+    float rho2, w2;
+    load_tok(max(t - 1, 0), n_al, n_be, n_v, n_dout, n_sp);
+    load_ids(max(t - 2, 0), rs2, rho2, ws2, w2);
+    // read slots into the hash
+    int hslot = -1;
+    if (hasR && q == 0) {
+      int hh = bwd_hash(rs);
+      while (atomicCAS(&hkey[hh], 0u, (uint32_t)rs + 1u) != 0u) hh = (hh + 1) & (BWD_HASH - 1);
+      hrho[hh] = rho;
+      hslot = hh;
+    }
+    __syncthreads();
+    // keep the conversions of the looked-ahead inputs (and the wait for them) below the barrier
+    asm volatile("" : "+v"(c_dout), "+v"(c_sp), "+v"(c_al), "+v"(c_be), "+v"(c_v));
+    const float al = Word<A>::get(c_al, alpha + row), be = Word<A>::get(c_be, beta + row);
+    float dout[4];
+    Raw4<A>::unpack(c_dout, dout);
+    if (!valid) dout[0] = dout[1] = dout[2] = dout[3] = 0.f;
+    // the read
+    float m[4];
+    Raw4<Bk>::unpack(rb, m);
+    if (hasR) {
+      const float dot = sum4_lanes(((dout[0] * m[0] + dout[1] * m[1]) + dout[2] * m[2]) + dout[3] * m[3]);
+      if (q == 0) part[W + grp] = dot;
+      if (valid) {
+        rg.x += rho * dout[0]; rg.y += rho * dout[1]; rg.z += rho * dout[2]; rg.w += rho * dout[3];
+        *(float4*)(gbank + (long long)rs * D.ld + col) = rg;
+      }
+    }
+    // the write: g_i (with this token's read update if its slot is also read), P_i
+    float g[4] = {wg.x, wg.y, wg.z, wg.w}, pp[4];
+    Raw4<Bk>::unpack(c_sp, pp);
+    if (!valid) pp[0] = pp[1] = pp[2] = pp[3] = 0.f;
+    if (hasW) {
+      int hh = bwd_hash(ws);
+      uint32_t key;
+      while ((key = hkey[hh]) != 0u && key != (uint32_t)ws + 1u) hh = (hh + 1) & (BWD_HASH - 1);
+      if (key != 0u) {
+        const float rj = hrho[hh];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) g[k] += rj * dout[k];
+      }
+    }
+    // sums over the write terms: D = sum w g, r = sum w P, sum <g, P>
+    float cD[4], cR[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      cD[k] = hasW ? w * g[k] : 0.f;
+      cR[k] = hasW ? w * pp[k] : 0.f;
+    }
+    float gp = hasW ? sum4_lanes(((g[0] * pp[0] + g[1] * pp[1]) + g[2] * pp[2]) + g[3] * pp[3]) : 0.f;
+#pragma unroll
+    for (int o = 4; o <= 32; o <<= 1) {  // over the 16 groups of the wave (fixed tree; lanes 0..3 keep the sum)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        cD[k] += __shfl_xor(cD[k], o);
+        cR[k] += __shfl_xor(cR[k], o);
+      }
+      gp += __shfl_xor(gp, o);
+    }
+    if (lane < 4) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        sRedD[wv][lane * 4 + k] = cD[k];
+        sRedR[wv][lane * 4 + k] = cR[k];
+      }
+      if (lane == 0) sRedGP[wv] = gp;
+    }
+    __syncthreads();
+    // delta, dv and the gate partials (lanes 0..15 of wave 0, one column each)
+    if (tid < 64) {
+      const int c = tid & (BWD_COLS - 1);
+      const int cc = slice * BWD_COLS + c;
+      const bool cv = tid < BWD_COLS && cc < d;
+      float Dl = 0.f, r = 0.f, gps = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        Dl += sRedD[k][c];
+        r += sRedR[k][c];
+        gps += sRedGP[k];
+      }
+      const float e = Word<A>::get(c_v, values + row * d + vcol) - al * r;
+      float db = cv ? Dl * e : 0.f;
+      float rd = cv ? Dl * r : 0.f;
+      if (tid < BWD_COLS) {
+        sDel[c] = Dl;
+        sDt[c] = cv ? be * e : 0.f;
+        if (cv) a.gvalues[row * d + cc] = be * Dl;
+      }
+#pragma unroll
+      for (int o = 8; o >= 1; o >>= 1) {
+        db += __shfl_xor(db, o);
+        rd += __shfl_xor(rd, o);
+      }
+      if (tid == 0) {
+        part[W + R] = gps - be * rd;
+        part[W + R + 1] = db;
+      }
+    }
+    __syncthreads();
+    // d w partials, G[S_i] <- alpha g_i - alpha beta w_i D, M[S_i] <- P_i; clear the hash
+    if (hasW) {
+      const float ab = al * be;
+      float dl[4], Dl[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        dl[k] = sDt[q * 4 + k];
+        Dl[k] = sDel[q * 4 + k];
+      }
+      const float gd = sum4_lanes(((g[0] * dl[0] + g[1] * dl[1]) + g[2] * dl[2]) + g[3] * dl[3]);
+      const float Dp = sum4_lanes(((Dl[0] * pp[0] + Dl[1] * pp[1]) + Dl[2] * pp[2]) + Dl[3] * pp[3]);
+      if (q == 0) part[grp] = gd - ab * Dp;
+      if (valid) {
+        const float cw = ab * w;
+        *(float4*)(gbank + (long long)ws * D.ld + col) = make_float4(
+            al * g[0] - cw * Dl[0], al * g[1] - cw * Dl[1], al * g[2] - cw * Dl[2], al * g[3] - cw * Dl[3]);
+        Raw4<Bk>::store(bank + (long long)ws * D.ld + col, c_sp);
+      }
+    }
+    if (hslot >= 0) hkey[hslot] = 0u;
+    // next token
+    rs = rs1; rho = rho1; ws = ws1; w = w1;
+    rs1 = rs2; rho1 = rho2; ws1 = ws2; w1 = w2;
+    c_al = n_al; c_be = n_be; c_v = n_v; c_dout = n_dout; c_sp = n_sp;
+    __syncthreads();
+  }
+}
+
 // One workgroup per token row (stream-major): slice sums, gate gradients, softmax derivative (slot-score gradients
 // into the workspace), and the key and query gradients d x^(f) = sum_i d s_i C_f[i_f] (terms in order).
 template <typename A>
@@ -307,10 +545,16 @@ __global__ __launch_bounds__(256) void bwd_subkey_sum_kernel(const float* __rest
 template <typename A, typename Bk>
 static hipError_t launch_bwd_t(const Dims& D, const BwdArgs& a, hipStream_t st) {
   const int nsl = bwd_slices(D);
-  const size_t lds = bwd_sweep_lds(D.W);
-  (void)hipFuncSetAttribute((const void*)bwd_sweep_kernel<A, Bk>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  hipLaunchKernelGGL((bwd_sweep_kernel<A, Bk>), dim3((unsigned)((long long)D.S * nsl)), dim3(BWD_NT), lds, st, D, a,
-                     nsl);
+  if (D.W <= BWD_NT / 4 && D.R <= BWD_NT / 4) {
+    hipLaunchKernelGGL((bwd_sweep_fast_kernel<A, Bk>), dim3((unsigned)((long long)D.S * nsl)), dim3(BWD_NT), 0, st, D,
+                       a, nsl);
+  } else {
+    const size_t lds = bwd_sweep_lds(D.W);
+    (void)hipFuncSetAttribute((const void*)bwd_sweep_kernel<A, Bk>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)lds);
+    hipLaunchKernelGGL((bwd_sweep_kernel<A, Bk>), dim3((unsigned)((long long)D.S * nsl)), dim3(BWD_NT), lds, st, D, a,
+                       nsl);
+  }
   hipLaunchKernelGGL((bwd_token_kernel<A>), dim3((unsigned)((long long)D.S * D.T)), dim3(256), 0, st, D, a, nsl);
   const int nrb = bwd_row_blocks(D);
   long long sumn = 0;
