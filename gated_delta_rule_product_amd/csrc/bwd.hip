@@ -443,6 +443,7 @@ template <typename A>
 __global__ __launch_bounds__(256) void bwd_token_kernel(Dims D, BwdArgs a, int nsl) {
   __shared__ float sd[MAX_K * 2 + 2];
   __shared__ float sm[2];
+  __shared__ uint16_t ssub[MAX_K * 2][MAX_F];  // factor sub-key of every term (n_f <= 4096)
   const long long so = blockIdx.x;
   const int T = D.T, W = D.W, R = D.R, P = W + R + 2;
   const int st = (int)(so / T), t = (int)(so % T);
@@ -473,6 +474,11 @@ __global__ __launch_bounds__(256) void bwd_token_kernel(Dims D, BwdArgs a, int n
     const float v = wt * (sd[i] - sm[wr ? 0 : 1]);
     sd[i] = v;
     ds[i] = v;
+    long long id = wr ? a.widx[so * W + i] : a.ridx[so * R + (i - W)];
+    for (int f = D.F - 1; f >= 0; --f) {  // mixed radix, factor 0 most significant
+      ssub[i][f] = (uint16_t)(id % D.widths[f]);
+      id /= D.widths[f];
+    }
   }
   __syncthreads();
   long long sumn = 0;
@@ -483,49 +489,67 @@ __global__ __launch_bounds__(256) void bwd_token_kernel(Dims D, BwdArgs a, int n
     const int kind = x >= Fdk;
     const int fc = x - kind * Fdk;
     const int f = fc / D.dk, c = fc % D.dk;
-    long long stride = 1, off = 0;
-    for (int g = D.F - 1; g > f; --g) stride *= D.widths[g];
+    long long off = 0;
     for (int g = 0; g < f; ++g) off += D.widths[g];
-    const int n = kind ? R : W;
-    const int32_t* ids = kind ? a.ridx + so * R : a.widx + so * W;
-    const float* dsk = sd + (kind ? W : 0);
+    const int n = kind ? R : W, i0 = kind ? W : 0;
     float acc = 0.f;
-    for (int i = 0; i < n; ++i) {
-      const int sf = (int)((ids[i] / stride) % D.widths[f]);
-      acc += dsk[i] * to_f<A>(sub[(off + sf) * D.dk + c]);
-    }
+    for (int i = 0; i < n; ++i) acc += sd[i0 + i] * to_f<A>(sub[(off + ssub[i0 + i][f]) * D.dk + c]);
     (kind ? a.grq : a.gwkeys)[row * Fdk + fc] = acc;
   }
 }
 
-// Sub-key partial sums of one block of 128 token rows of head h (rows ordered b-major), factor f, `cb` columns:
-// one wave, lane c owns column c of every sub-key of the factor (LDS accumulators), terms in order.
+// Sub-key partial sums of one block of token rows of head h (rows ordered b-major; bwd_row_block_rows each),
+// factor f, `cb` columns: one wave, lane c owns column c of every sub-key of the factor (LDS accumulators), terms in
+// order. The factor-f sub-key of every term and the slot-score gradients of 16 rows at a time are staged in LDS.
+constexpr int BWD_SK_ROWS = 16;
+
 template <typename A>
-__global__ __launch_bounds__(64) void bwd_subkey_kernel(Dims D, BwdArgs a, int cb, int ncb) {
-  extern __shared__ __align__(16) float acc[];  // [n_f][cb]
+__global__ __launch_bounds__(64) void bwd_subkey_kernel(Dims D, BwdArgs a, int cb, int ncb, int rows_per_block) {
+  extern __shared__ __align__(16) float acc[];  // [n_f][cb], then ids [16][W + R] and ds [16][W + R]
   const int rb = blockIdx.x, h = blockIdx.y, f = blockIdx.z / ncb, cblk = blockIdx.z % ncb;
   const int n = D.widths[f], lane = threadIdx.x;
+  const int W = D.W, R = D.R, T = D.T, Fdk = D.F * D.dk, K = W + R;
+  int32_t* sid = (int32_t*)(acc + (size_t)n * cb);
+  float* sds = (float*)(sid + BWD_SK_ROWS * K);
   const int c = cblk * cb + lane;
   const bool on = lane < cb && c < D.dk;
   for (int i = lane; i < n * cb; i += 64) acc[i] = 0.f;
-  __syncthreads();
   long long stride = 1, off = 0, sumn = 0;
   for (int g = D.F - 1; g > f; --g) stride *= D.widths[g];
   for (int g = 0; g < f; ++g) off += D.widths[g];
   for (int g = 0; g < D.F; ++g) sumn += D.widths[g];
-  const int W = D.W, R = D.R, T = D.T, Fdk = D.F * D.dk;
-  const int r0 = rb * 128, r1 = min(r0 + 128, D.B * T);
-  for (int r = r0; r < r1; ++r) {
-    const int b = r / T, t = r % T;
-    const long long so = ((long long)b * D.H + h) * T + t;
-    const long long row = ((long long)b * T + t) * D.H + h;
-    const float xw = on ? to_f<A>(((const A*)a.wkeys)[row * Fdk + f * D.dk + c]) : 0.f;
-    const float xr = on ? to_f<A>(((const A*)a.rq)[row * Fdk + f * D.dk + c]) : 0.f;
-    const float* ds = a.ds + so * (W + R);
-    for (int i = 0; i < W + R; ++i) {
+  const int r0 = rb * rows_per_block, r1 = min(r0 + rows_per_block, D.B * T);
+  for (int q0 = r0; q0 < r1; q0 += BWD_SK_ROWS) {
+    const int nr = min(BWD_SK_ROWS, r1 - q0);
+    __syncthreads();  // the previous rows' staging is consumed
+    for (int e = lane; e < nr * K; e += 64) {
+      const int rr = e / K, i = e % K;
+      const int r = q0 + rr, b = r / T, t = r % T;
+      const long long so = ((long long)b * D.H + h) * T + t;
       const int slot = i < W ? a.widx[so * W + i] : a.ridx[so * R + (i - W)];
-      const int sf = (int)((slot / stride) % n);
-      if (on) acc[sf * cb + lane] += ds[i] * (i < W ? xw : xr);
+      sid[e] = (int)((slot / stride) % n);  // the factor-f sub-key (divisions here, in parallel, not in the serial sums)
+      sds[e] = a.ds[so * K + i];
+    }
+    float xw[BWD_SK_ROWS], xr[BWD_SK_ROWS];
+#pragma unroll
+    for (int rr = 0; rr < BWD_SK_ROWS; ++rr) {
+      xw[rr] = xr[rr] = 0.f;
+      if (rr < nr && on) {
+        const int r = q0 + rr, b = r / T, t = r % T;
+        const long long row = ((long long)b * T + t) * D.H + h;
+        xw[rr] = to_f<A>(((const A*)a.wkeys)[row * Fdk + f * D.dk + c]);
+        xr[rr] = to_f<A>(((const A*)a.rq)[row * Fdk + f * D.dk + c]);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rr = 0; rr < BWD_SK_ROWS; ++rr) {
+      if (rr < nr) {
+        for (int i = 0; i < K; ++i) {
+          const int sf = sid[rr * K + i];
+          if (on) acc[sf * cb + lane] += sds[rr * K + i] * (i < W ? xw[rr] : xr[rr]);
+        }
+      }
     }
   }
   __syncthreads();
@@ -556,20 +580,22 @@ static hipError_t launch_bwd_t(const Dims& D, const BwdArgs& a, hipStream_t st) 
                        nsl);
   }
   hipLaunchKernelGGL((bwd_token_kernel<A>), dim3((unsigned)((long long)D.S * D.T)), dim3(256), 0, st, D, a, nsl);
-  const int nrb = bwd_row_blocks(D);
+  const int nrb = bwd_row_blocks(D), rpb = bwd_row_block_rows(D);
   long long sumn = 0;
   int nmax = 0;
   for (int f = 0; f < D.F; ++f) {
     sumn += D.widths[f];
     nmax = max(nmax, D.widths[f]);
   }
+  const size_t stage = (size_t)BWD_SK_ROWS * (D.W + D.R) * 8;  // <= 128 KiB (W, R <= 512)
+  const size_t budget = 150 * 1024 - stage;                     // >= 22 KiB: n_f * 4 <= 16 KiB always fits
   int cb = 64;
-  while (cb > 1 && (size_t)nmax * cb * 4 > 64 * 1024) cb >>= 1;
+  while (cb > 1 && (size_t)nmax * cb * 4 > budget) cb >>= 1;
   const int ncb = (D.dk + cb - 1) / cb;
-  const size_t slds = (size_t)nmax * cb * 4;
+  const size_t slds = (size_t)nmax * cb * 4 + stage;
   (void)hipFuncSetAttribute((const void*)bwd_subkey_kernel<A>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)slds);
   hipLaunchKernelGGL((bwd_subkey_kernel<A>), dim3((unsigned)nrb, (unsigned)D.H, (unsigned)(D.F * ncb)), dim3(64), slds,
-                     st, D, a, cb, ncb);
+                     st, D, a, cb, ncb, rpb);
   const long long n = (long long)D.H * sumn * D.dk;
   hipLaunchKernelGGL(bwd_subkey_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.sgpart, a.gsub, n,
                      nrb);

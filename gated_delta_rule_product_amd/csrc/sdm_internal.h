@@ -293,7 +293,15 @@ struct BwdArgs {
 };
 // Slices of 16 columns the backward sweep splits a row into, and the row blocks of the sub-key sums.
 inline int bwd_slices(const Dims& D) { return (D.d + 15) / 16; }
-inline int bwd_row_blocks(const Dims& D) { return (D.B * D.T + 127) / 128; }
+// Token rows per block of the sub-key sums: a multiple of 16 giving about 256 blocks per head (at least 16 rows).
+inline int bwd_row_block_rows(const Dims& D) {
+  const int want = (D.B * D.T + 255) / 256;
+  return want <= 16 ? 16 : (want + 15) / 16 * 16;
+}
+inline int bwd_row_blocks(const Dims& D) {
+  const int r = bwd_row_block_rows(D);
+  return (D.B * D.T + r - 1) / r;
+}
 hipError_t launch_bwd(const Dims& D, const BwdArgs& a, hipStream_t st);
 
 struct DecodeArgs {
