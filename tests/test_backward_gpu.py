@@ -9,8 +9,10 @@ Tolerances (row-wise infinity-norm relative error; a gate gradient row is the H 
 accumulates in float32 over the token sweep where the oracle uses fp64, and it differentiates the forward the GPU
 ran (bank rounded once per chunk) where the oracle differentiates its own (rounded after every token); activations
 enter both sides with the same values and every gradient is float32, so the tolerance follows the bank dtype. Float32
-banks: 1e-4 (the adjoint of a row passes through a few hundred float32 operations over the tokens that touch it;
-measured 1e-7 to 2e-5). Bfloat16 banks: 3e-2 (the bf16 tolerance of the forward, 2e-2, plus the spread of rounding
+banks: 1e-4 for the row gradients (values, bank, sub-keys: the adjoint of a row passes through a few hundred float32
+operations over the tokens that touch it; measured 1e-7 to 5e-6), 1e-3 for the score-path gradients (keys, queries,
+gates: dot products over the head dim, d = 1024 at full size, that the softmax derivative then centres, so float32
+gives up to about d 2^-24 = 6e-5 relative times the cancellation of the centring; measured up to 1.4e-4). Bfloat16 banks: 3e-2 (the bf16 tolerance of the forward, 2e-2, plus the spread of rounding
 points; measured up to 1e-2).
 A row's scale is at least 1e-3 of the tensor's largest value: gradient rows are sums whose terms can cancel (the
 softmax derivative sums to zero over a token's terms, so a sub-key shared by all of them gets an exact zero in fp64
@@ -44,8 +46,16 @@ def to_dev(x, dtype):
 FLOOR = 1e-3
 
 
+SCORE_PATH = ("write_keys", "read_queries", "forget_gate", "input_gate")
+
+
 def _tol(s):
-    return 1e-4 if s.bank == "f32" else 3e-2
+    """{gradient: tolerance} for the shape's bank dtype."""
+    if s.bank == "bf16":
+        return {k: 3e-2 for k in list(NAMES) + ["forget_gate", "input_gate"]}
+    t = {k: 1e-4 for k in NAMES}
+    t.update({k: 1e-3 for k in SCORE_PATH})
+    return t
 
 
 def _upstream(s, seed, with_bank_grad):
@@ -103,8 +113,8 @@ def check(s, got, ref, tol):
     for k, r in (("forget_gate", "d_alpha"), ("input_gate", "d_beta")):
         errs[k] = rowwise_rel(got[k], ref[r], FLOOR)
     print("gradient errors", {k: f"{v:.2e}" for k, v in errs.items()}, flush=True)
-    bad = {k: v for k, v in errs.items() if not v <= tol}
-    assert not bad, f"gradients beyond {tol}: {bad}"
+    bad = {k: v for k, v in errs.items() if not v <= tol[k]}
+    assert not bad, f"gradients beyond their tolerance {tol}: {bad}"
 
 
 CASES = [
@@ -154,3 +164,17 @@ def test_save_forward_matches_plain_forward_within_rounding():
     torch.cuda.synchronize()
     assert rowwise_rel(o2.cpu().numpy(), o1.cpu().numpy()) <= 1e-5
     assert rowwise_rel(b2.cpu().numpy(), b1.cpu().numpy()) <= 1e-5
+
+
+def test_backward_layer_65k_full_size():
+    """The 65,536-slot layer workload at full size (B 2, T 4096, H 2, d 1024, W = R = 64, chunk 64, bf16 activations
+    on a float32 bank, padded row pitch): every gradient against the oracle's backward, bank restored bit for bit."""
+    s = synth.WORKLOADS["layer_65k"]
+    print("full-size backward: inputs", flush=True)
+    x = synth.make_inputs(s)
+    dout, dbank = _upstream(s, 46, True)
+    print("full-size backward: GPU", flush=True)
+    got, _ = run_gpu(s, x, dout, dbank, pitch=binding.bank_pitch(s.head_dim, torch.float32))
+    print("full-size backward: oracle", flush=True)
+    ref = run_oracle(s, x, dout, dbank)
+    check(s, got, ref, _tol(s))
