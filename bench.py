@@ -242,7 +242,17 @@ def bench_other(args, torch, binding, synth):
         ms = (t1 - t0) * 1e3 / n
         loop_ms = prof["loop"][0] / prof["loop"][1]
         alg = loop_algorithmic_bytes(s, s.batch * s.tokens * s.heads)
+        topk_ms = prof["topk"][0] / prof["topk"][1]
+        # factor scoring as a dense contraction: both kinds, every query against every sub-key of every factor
+        flops = 2 * s.batch * s.tokens * s.heads * sum(s.widths) * s.subkey_dim * 2
+        filtered = s.act == "bf16" and min(s.widths) >= 512
+        res_mfma = {"kernel": "topk2_kernel (%s factor scoring + exact selection)" % (
+                        "bf16 MFMA-filtered" if filtered else "fp64 direct"),
+                    "bound": "latency (selection chains)", "scoring_flops_per_launch": flops,
+                    "achieved": round(flops / (topk_ms * 1e-3) / 1e12, 2), "peak": 2500.0, "unit": "TFLOP/s",
+                    "frac": round(flops / (topk_ms * 1e-3) / 1e12 / 2500.0, 5), "avg_launch_ms": round(topk_ms, 4)}
         res[name] = {"tokens_per_s": round(s.batch * s.tokens / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
+                     "topk_scoring_mfma": res_mfma,
                      "steps": n, "kernels_avg_ms": {k: round(v[0] / v[1], 4) for k, v in prof.items() if v[1]},
                      "loop_algorithmic_bytes": alg, "loop_achieved_GBps": round(alg / (loop_ms * 1e-3) / 1e9, 1),
                      "loop_frac_of_8TBps": round(alg / (loop_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -323,7 +333,7 @@ def bench_decode(args, torch, binding, synth):
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        for i in range(3):
+        for i in range(min(3, nsteps)):
             eager_step(i)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
