@@ -225,6 +225,8 @@ WsLayout layout(const Dims& D, int op) {
     L.part = take((size_t)bwd_slices(D) * D.S * D.T * (D.W + D.R + 2) * 4);
     L.ds = take((size_t)D.S * D.T * (D.W + D.R) * 4);
     L.sgpart = take((size_t)bwd_row_blocks(D) * D.H * sumn * D.dk * 4);
+    L.mrho = take(nw * 4);
+    L.mread = take(nr * 4);
   }
   L.total = o;
   return L;
@@ -611,6 +613,8 @@ sdm_status sdm_write_read_backward(const sdm_config* cfg, const void* write_keys
   ba.part = (float*)(ws + L.part);
   ba.ds = (float*)(ws + L.ds);
   ba.sgpart = (float*)(ws + L.sgpart);
+  ba.mrho = (float*)(ws + L.mrho);
+  ba.mread = (float*)(ws + L.mread);
   TRY(hip_status(timed(SDM_K_BWD, st, [&] { return launch_bwd(D, ba, st); }), "backward launch"));
   return ok();
 }

@@ -215,24 +215,53 @@ __global__ __launch_bounds__(BWD_NT) void bwd_sweep_kernel(Dims D, BwdArgs a, in
   }
 }
 
-// The same sweep for W, R <= 128 (one write and one read term per 4-lane group), with one HBM round trip per token:
-// the read rows, their G rows and the write terms' G rows of token t are loaded together, with the snapshot rows,
-// gates and output gradient of token t - 1 and the ids of token t - 2 (read-only data, loaded ahead). A write slot
-// that token t also reads gets the read's G update (rho_j dout) added in registers: its loaded G row predates that
-// update; the read terms' slots go to a small LDS hash (slot -> rho) for that lookup. Sums over the write terms: a
-// fixed shuffle tree inside each wave, then the 8 wave partials in order. The loads of token t - 1's rows follow the
-// end-of-token barrier, after every store of token t in the workgroup's program order (one CU: its vector memory
-// pipeline keeps that order).
-constexpr int BWD_HASH = 256;
+// For every write term (t, i): the weight rho_j of the read term of the same token with the same slot, or 0; for
+// every read term: 1 if the token also writes its slot (slots are distinct within one token's writes and within its
+// reads, so there is at most one match). One wave per token.
+__global__ __launch_bounds__(64) void bwd_match_kernel(Dims D, BwdArgs a) {
+  __shared__ int32_t srs[MAX_K], sws[MAX_K];
+  __shared__ float srho[MAX_K];
+  const long long so = blockIdx.x;
+  const int W = D.W, R = D.R;
+  for (int j = threadIdx.x; j < R; j += 64) {
+    srs[j] = a.ridx[so * R + j];
+    srho[j] = a.rwt[so * R + j];
+  }
+  for (int i = threadIdx.x; i < W; i += 64) sws[i] = a.widx[so * W + i];
+  __syncthreads();
+  for (int i = threadIdx.x; i < W; i += 64) {
+    const int slot = sws[i];
+    float r = 0.f;
+    for (int j = 0; j < R; ++j)
+      if (srs[j] == slot) r = srho[j];
+    a.mrho[so * W + i] = r;
+  }
+  for (int j = threadIdx.x; j < R; j += 64) {
+    const int slot = srs[j];
+    float f = 0.f;
+    for (int i = 0; i < W; ++i)
+      if (sws[i] == slot) f = 1.f;
+    a.mread[so * R + j] = f;
+  }
+}
 
-__device__ __forceinline__ int bwd_hash(int slot) { return (int)(((uint32_t)slot * 2654435761u) >> 24); }
-
+// The same sweep for W, R <= 128 (one write and one read term per 4-lane group), two barriers and one HBM load
+// round trip per token: the read rows, their G rows and the write terms' G rows of token t are loaded together; the snapshot rows, gates, output gradient and values of token t - 1 and the ids of token
+// t - 2 are loaded a token ahead (read-only data) and kept raw until used (a conversion next to its load would make
+// the compiler wait for every earlier load). A write slot that the token also reads gets the read's G update
+// (rho_j dout, rho_j from bwd_match_kernel) added in registers, since its loaded G row predates that update. Sums
+// over the write terms: a fixed shuffle tree inside each wave, then every lane adds the 8 wave partials of its own
+// columns in order (the same sums on every lane, so no barrier for a broadcast). Every store of a token comes after
+// its last use of loaded data: loads and stores share one memory counter, and a wait for a load issued before a
+// store would also wait for the store. So the read's G update is stored with the write's, and not at all when the
+// token also writes that slot (the write's G row includes it). The loads of token t - 1's rows
+// follow the end-of-token barrier, after every store of token t in the workgroup's program order (one CU: its
+// vector memory pipeline keeps that order).
 template <typename A, typename Bk>
 __global__ __launch_bounds__(BWD_NT) void bwd_sweep_fast_kernel(Dims D, BwdArgs a, int nsl) {
-  __shared__ float sRedD[8][BWD_COLS], sRedR[8][BWD_COLS], sRedGP[8];
-  __shared__ float sDel[BWD_COLS], sDt[BWD_COLS];
-  __shared__ uint32_t hkey[BWD_HASH];
-  __shared__ float hrho[BWD_HASH];
+  __shared__ __align__(16) float sRedD[8][BWD_COLS];
+  __shared__ __align__(16) float sRedR[8][BWD_COLS];
+  __shared__ float sRedGP[8];
   typedef typename Raw4<Bk>::T RawT;
   typedef typename Raw4<A>::T ARaw;
   const int W = D.W, R = D.R, T = D.T, d = D.d;
@@ -245,6 +274,7 @@ __global__ __launch_bounds__(BWD_NT) void bwd_sweep_fast_kernel(Dims D, BwdArgs 
   const int col = slice * BWD_COLS + q * 4;
   const bool valid = col < d;
   const bool hasR = grp < R, hasW = grp < W;
+  const int jr = min(grp, R - 1), jw = min(grp, W - 1);  // clamped term indices: every lane loads in range
   const int P = W + R + 2;
   Bk* bank = (Bk*)a.bank + (long long)st * D.rows * D.ld;
   float* gbank = a.gbank + (long long)st * D.rows * D.ld;
@@ -253,105 +283,76 @@ __global__ __launch_bounds__(BWD_NT) void bwd_sweep_fast_kernel(Dims D, BwdArgs 
   const A* values = (const A*)a.values;
   const A* alpha = (const A*)a.alpha;
   const A* beta = (const A*)a.beta;
-  for (int i = tid; i < BWD_HASH; i += BWD_NT) hkey[i] = 0u;
-
-  // Inputs of a token loaded ahead are kept raw and converted where they are used: a conversion next to its load
-  // would make the compiler wait for every load issued before it (this token's rows included). The gates are uniform
-  // over the workgroup; through the scalar cache they would count against the LDS counter that every barrier
-  // drains, so they take the vector path (zero is 0 on every lane but not provably uniform).
-  // (separate variables, not a struct: a struct copy becomes a byte-wise memcpy that needs the loaded data at once)
-  const int zero = (int)__builtin_amdgcn_mbcnt_lo(0u, 0u);
-  const int vcol = min(slice * BWD_COLS + (tid & (BWD_COLS - 1)), d - 1);  // in range for every thread
+  const int zero = (int)__builtin_amdgcn_mbcnt_lo(0u, 0u);  // 0, not provably uniform: keeps the gate loads vector
   const int dcol = valid ? col : 0;
-  auto load_ids = [&](int t, int& rs, float& rho, int& ws, float& w) {
+
+  auto load_ids = [&](int t, int& rs, float& rho, int& ws, float& w, float& mr, float& mw) {
     const long long so = (long long)st * T + t;
-    rs = hasR ? a.ridx[so * R + grp] : 0;
-    rho = hasR ? a.rwt[so * R + grp] : 0.f;
-    ws = hasW ? a.widx[so * W + grp] : 0;
-    w = hasW ? a.wwt[so * W + grp] : 0.f;
+    rs = a.ridx[so * R + jr];
+    rho = a.rwt[so * R + jr];
+    ws = a.widx[so * W + jw];
+    w = a.wwt[so * W + jw];
+    mr = a.mrho[so * W + jw];
+    mw = a.mread[so * R + jr];
   };
-  auto load_tok = [&](int t, uint32_t& al_, uint32_t& be_, uint32_t& v_, ARaw& dout_, RawT& sp_) {
+  // (separate variables, not a struct: a struct copy becomes a byte-wise memcpy that needs the loaded data at once;
+  // 16-bit values in 32-bit words: kept in 16 bits the compiler re-masks them right after their load)
+  auto load_tok = [&](int t, uint32_t& al_, uint32_t& be_, ARaw& v_, ARaw& dout_, RawT& sp_) {
     const long long row = ((long long)b * T + t) * D.H + h;
     al_ = Word<A>::load(alpha + row + zero);
     be_ = Word<A>::load(beta + row + zero);
     dout_ = Raw4<A>::load(gout + row * d + dcol);
-    v_ = Word<A>::load(values + row * d + vcol);
-    // unconditional (a load under a branch merged with a default value costs a wait): other lanes read element 0
-    sp_ = Raw4<Bk>::load(snap + (hasW && valid ? ((long long)t * W + grp) * d + col : 0));
+    v_ = Raw4<A>::load(values + row * d + dcol);
+    sp_ = Raw4<Bk>::load(snap + ((long long)t * W + jw) * d + dcol);
   };
 
-  int rs, ws, rs1 = 0, ws1 = 0;
-  float rho, w, rho1 = 0.f, w1 = 0.f;
-  uint32_t c_al, c_be, c_v;
-  ARaw c_dout;
+  int rs, ws, rs1, ws1;
+  float rho, w, mr, mw, rho1, w1, mr1, mw1;
+  uint32_t c_al, c_be;
+  ARaw c_v, c_dout;
   RawT c_sp;
-  load_ids(T - 1, rs, rho, ws, w);
-  if (T >= 2) load_ids(T - 2, rs1, rho1, ws1, w1);
+  load_ids(T - 1, rs, rho, ws, w, mr, mw);
+  load_ids(max(T - 2, 0), rs1, rho1, ws1, w1, mr1, mw1);
   load_tok(T - 1, c_al, c_be, c_v, c_dout, c_sp);
-  __syncthreads();  // hash table cleared
+  // the loop's first values in before it starts: a load still in flight on the way in would make the loop head wait
+  // for everything outstanding, the previous token's stores included, on every token
+  asm volatile("" ::"v"(rs), "v"(ws), "v"(rho), "v"(w), "v"(mr), "v"(mw), "v"(rs1), "v"(ws1), "v"(rho1), "v"(w1),
+               "v"(mr1), "v"(mw1), "v"(c_al), "v"(c_be), "v"(c_v), "v"(c_dout), "v"(c_sp));
 
   for (int t = T - 1; t >= 0; --t) {
     const long long so = (long long)st * T + t;
     const long long row = ((long long)b * T + t) * D.H + h;
     float* part = a.part + ((long long)slice * D.S * T + so) * P;
-    // this token's rows
-    RawT rb;
-    memset(&rb, 0, sizeof rb);
-    float4 rg = make_float4(0.f, 0.f, 0.f, 0.f), wg = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (valid && hasR) {
-      rb = Raw4<Bk>::load(bank + (long long)rs * D.ld + col);
-      rg = *(const float4*)(gbank + (long long)rs * D.ld + col);
-    }
-    if (valid && hasW) wg = *(const float4*)(gbank + (long long)ws * D.ld + col);
-    // ahead: token t - 1's inputs and snapshot rows, token t - 2's ids
-    // (unconditional, token index clamped at 0: a branch around them would merge registers still in flight)
-    uint32_t n_al, n_be, n_v;
-    ARaw n_dout;
+    // this token's rows (clamped ids: in range on every lane)
+    const RawT rb = Raw4<Bk>::load(bank + (long long)rs * D.ld + dcol);
+    float4 rg = *(const float4*)(gbank + (long long)rs * D.ld + dcol);
+    const float4 wg = *(const float4*)(gbank + (long long)ws * D.ld + dcol);
+    // ahead: token t - 1's inputs and snapshot rows, token t - 2's ids (token indices clamped at 0)
+    uint32_t n_al, n_be;
+    ARaw n_v, n_dout;
     RawT n_sp;
     int rs2, ws2;
-    float rho2, w2;
+    float rho2, w2, mr2, mw2;
     load_tok(max(t - 1, 0), n_al, n_be, n_v, n_dout, n_sp);
-    load_ids(max(t - 2, 0), rs2, rho2, ws2, w2);
-    // read slots into the hash
-    int hslot = -1;
-    if (hasR && q == 0) {
-      int hh = bwd_hash(rs);
-      while (atomicCAS(&hkey[hh], 0u, (uint32_t)rs + 1u) != 0u) hh = (hh + 1) & (BWD_HASH - 1);
-      hrho[hh] = rho;
-      hslot = hh;
-    }
-    __syncthreads();
-    // keep the conversions of the looked-ahead inputs (and the wait for them) below the barrier
-    asm volatile("" : "+v"(c_dout), "+v"(c_sp), "+v"(c_al), "+v"(c_be), "+v"(c_v));
+    load_ids(max(t - 2, 0), rs2, rho2, ws2, w2, mr2, mw2);
     const float al = Word<A>::get(c_al, alpha + row), be = Word<A>::get(c_be, beta + row);
-    float dout[4];
+    float dout[4], v[4];
     Raw4<A>::unpack(c_dout, dout);
-    if (!valid) dout[0] = dout[1] = dout[2] = dout[3] = 0.f;
-    // the read
+    Raw4<A>::unpack(c_v, v);
+    if (!valid) dout[0] = dout[1] = dout[2] = dout[3] = v[0] = v[1] = v[2] = v[3] = 0.f;
+    // the read: d rho partial, G[R_j] += rho_j dout (stored at the end of the token)
     float m[4];
     Raw4<Bk>::unpack(rb, m);
-    if (hasR) {
-      const float dot = sum4_lanes(((dout[0] * m[0] + dout[1] * m[1]) + dout[2] * m[2]) + dout[3] * m[3]);
-      if (q == 0) part[W + grp] = dot;
-      if (valid) {
-        rg.x += rho * dout[0]; rg.y += rho * dout[1]; rg.z += rho * dout[2]; rg.w += rho * dout[3];
-        *(float4*)(gbank + (long long)rs * D.ld + col) = rg;
-      }
-    }
-    // the write: g_i (with this token's read update if its slot is also read), P_i
-    float g[4] = {wg.x, wg.y, wg.z, wg.w}, pp[4];
+    const float rdot = sum4_lanes(((dout[0] * m[0] + dout[1] * m[1]) + dout[2] * m[2]) + dout[3] * m[3]);
+    rg.x += rho * dout[0]; rg.y += rho * dout[1]; rg.z += rho * dout[2]; rg.w += rho * dout[3];
+    // the write: g_i (plus this token's read update of the same slot), P_i
+    float g[4] = {wg.x + mr * dout[0], wg.y + mr * dout[1], wg.z + mr * dout[2], wg.w + mr * dout[3]}, pp[4];
     Raw4<Bk>::unpack(c_sp, pp);
     if (!valid) pp[0] = pp[1] = pp[2] = pp[3] = 0.f;
-    if (hasW) {
-      int hh = bwd_hash(ws);
-      uint32_t key;
-      while ((key = hkey[hh]) != 0u && key != (uint32_t)ws + 1u) hh = (hh + 1) & (BWD_HASH - 1);
-      if (key != 0u) {
-        const float rj = hrho[hh];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) g[k] += rj * dout[k];
-      }
-    }
+    // the looked-ahead values are in (issued before this token's rows, which were just waited for): take them
+    // here, before any store, so that moving them into place at the end of the token waits for nothing
+    asm volatile("" ::"v"(rs2), "v"(ws2), "v"(rho2), "v"(w2), "v"(mr2), "v"(mw2), "v"(n_al), "v"(n_be), "v"(n_v),
+                 "v"(n_dout), "v"(n_sp));
     // sums over the write terms: D = sum w g, r = sum w P, sum <g, P>
     float cD[4], cR[4];
 #pragma unroll
@@ -370,54 +371,47 @@ __global__ __launch_bounds__(BWD_NT) void bwd_sweep_fast_kernel(Dims D, BwdArgs 
       gp += __shfl_xor(gp, o);
     }
     if (lane < 4) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        sRedD[wv][lane * 4 + k] = cD[k];
-        sRedR[wv][lane * 4 + k] = cR[k];
-      }
+      *(float4*)&sRedD[wv][lane * 4] = make_float4(cD[0], cD[1], cD[2], cD[3]);
+      *(float4*)&sRedR[wv][lane * 4] = make_float4(cR[0], cR[1], cR[2], cR[3]);
       if (lane == 0) sRedGP[wv] = gp;
     }
     __syncthreads();
-    // delta, dv and the gate partials (lanes 0..15 of wave 0, one column each)
-    if (tid < 64) {
-      const int c = tid & (BWD_COLS - 1);
-      const int cc = slice * BWD_COLS + c;
-      const bool cv = tid < BWD_COLS && cc < d;
-      float Dl = 0.f, r = 0.f, gps = 0.f;
+    // D, r and delta of this lane's four columns (the 8 wave partials in order, on every lane alike)
+    float Dl[4] = {0.f, 0.f, 0.f, 0.f}, r[4] = {0.f, 0.f, 0.f, 0.f}, dl[4];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        Dl += sRedD[k][c];
-        r += sRedR[k][c];
-        gps += sRedGP[k];
-      }
-      const float e = Word<A>::get(c_v, values + row * d + vcol) - al * r;
-      float db = cv ? Dl * e : 0.f;
-      float rd = cv ? Dl * r : 0.f;
-      if (tid < BWD_COLS) {
-        sDel[c] = Dl;
-        sDt[c] = cv ? be * e : 0.f;
-        if (cv) a.gvalues[row * d + cc] = be * Dl;
-      }
+    for (int k = 0; k < 8; ++k) {
+      const float4 x = *(const float4*)&sRedD[k][q * 4];
+      const float4 y = *(const float4*)&sRedR[k][q * 4];
+      Dl[0] += x.x; Dl[1] += x.y; Dl[2] += x.z; Dl[3] += x.w;
+      r[0] += y.x; r[1] += y.y; r[2] += y.z; r[3] += y.w;
+    }
+    float e[4];
 #pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) {
-        db += __shfl_xor(db, o);
-        rd += __shfl_xor(rd, o);
-      }
-      if (tid == 0) {
+    for (int k = 0; k < 4; ++k) {
+      e[k] = v[k] - al * r[k];  // v - alpha r
+      dl[k] = be * e[k];
+    }
+    if (grp == 0) {  // dv, and the slice partials of d alpha and d beta (4 lanes x 4 columns)
+      if (valid)
+        *(float4*)(a.gvalues + row * d + col) = make_float4(be * Dl[0], be * Dl[1], be * Dl[2], be * Dl[3]);
+      const float db = sum4_lanes(((Dl[0] * e[0] + Dl[1] * e[1]) + Dl[2] * e[2]) + Dl[3] * e[3]);
+      const float rd = sum4_lanes(((Dl[0] * r[0] + Dl[1] * r[1]) + Dl[2] * r[2]) + Dl[3] * r[3]);
+      if (q == 0) {
+        float gps = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) gps += sRedGP[k];
         part[W + R] = gps - be * rd;
         part[W + R + 1] = db;
       }
     }
-    __syncthreads();
-    // d w partials, G[S_i] <- alpha g_i - alpha beta w_i D, M[S_i] <- P_i; clear the hash
+    // the read's stores (its G row only if the token does not also write the slot)
+    if (hasR) {
+      if (q == 0) part[W + grp] = rdot;
+      if (valid && mw == 0.f) *(float4*)(gbank + (long long)rs * D.ld + col) = rg;
+    }
+    // d w partials, G[S_i] <- alpha g_i - alpha beta w_i D, M[S_i] <- P_i
     if (hasW) {
       const float ab = al * be;
-      float dl[4], Dl[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        dl[k] = sDt[q * 4 + k];
-        Dl[k] = sDel[q * 4 + k];
-      }
       const float gd = sum4_lanes(((g[0] * dl[0] + g[1] * dl[1]) + g[2] * dl[2]) + g[3] * dl[3]);
       const float Dp = sum4_lanes(((Dl[0] * pp[0] + Dl[1] * pp[1]) + Dl[2] * pp[2]) + Dl[3] * pp[3]);
       if (q == 0) part[grp] = gd - ab * Dp;
@@ -428,10 +422,9 @@ __global__ __launch_bounds__(BWD_NT) void bwd_sweep_fast_kernel(Dims D, BwdArgs 
         Raw4<Bk>::store(bank + (long long)ws * D.ld + col, c_sp);
       }
     }
-    if (hslot >= 0) hkey[hslot] = 0u;
     // next token
-    rs = rs1; rho = rho1; ws = ws1; w = w1;
-    rs1 = rs2; rho1 = rho2; ws1 = ws2; w1 = w2;
+    rs = rs1; rho = rho1; ws = ws1; w = w1; mr = mr1; mw = mw1;
+    rs1 = rs2; rho1 = rho2; ws1 = ws2; w1 = w2; mr1 = mr2; mw1 = mw2;
     c_al = n_al; c_be = n_be; c_v = n_v; c_dout = n_dout; c_sp = n_sp;
     __syncthreads();
   }
@@ -570,6 +563,7 @@ template <typename A, typename Bk>
 static hipError_t launch_bwd_t(const Dims& D, const BwdArgs& a, hipStream_t st) {
   const int nsl = bwd_slices(D);
   if (D.W <= BWD_NT / 4 && D.R <= BWD_NT / 4) {
+    hipLaunchKernelGGL(bwd_match_kernel, dim3((unsigned)((long long)D.S * D.T)), dim3(64), 0, st, D, a);
     hipLaunchKernelGGL((bwd_sweep_fast_kernel<A, Bk>), dim3((unsigned)((long long)D.S * nsl)), dim3(BWD_NT), 0, st, D,
                        a, nsl);
   } else {

@@ -206,6 +206,8 @@ struct WsLayout {
   size_t counts;                               // [S * nch] ChunkCounts
   size_t owner, conflict;                      // shared bank: int32 [H][N] first stream of each slot; int32 flag
   size_t part;                                 // backward: float [slices][S][T][W + R + 2] per-slice dot products
+  size_t mrho;                                 // backward: float [S][T][W] read weight of the same slot, or 0
+  size_t mread;                                // backward: float [S][T][R] 1 if the read slot is also written
   size_t ds;                                   // backward: float [S][T][W + R] slot-score gradients
   size_t sgpart;                               // backward: float [row blocks][H][sum n_f][dk] sub-key partial sums
   size_t total;
@@ -290,6 +292,8 @@ struct BwdArgs {
   float* gbank;           // [S][rows][ld]: gradient w.r.t. the bank after the call in, before the call out
   float* gwkeys; float* grq; float* gvalues; float* galpha; float* gbeta; float* gsub;
   float* part; float* ds; float* sgpart;  // workspace
+  float* mrho;            // workspace [S][T][W]: rho of the read term of the same token and slot as write term i, or 0
+  float* mread;           // workspace [S][T][R]: 1 if read term j's slot is also written by the token, else 0
 };
 // Slices of 16 columns the backward sweep splits a row into, and the row blocks of the sub-key sums.
 inline int bwd_slices(const Dims& D) { return (D.d + 15) / 16; }
