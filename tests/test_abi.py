@@ -161,3 +161,48 @@ def test_decode_partial_overlap_refused(lib):
     p[7] = _fake(base + 6 * step + 256)  # bank_out starts inside bank_in
     st = lib.sdm_decode_step(ctypes.byref(cfg), *p, _fake(base + 20 * step), n.value, None)
     assert st == B.SDM_ERR_ALIAS and "bank_out" in B.last_error()
+
+
+def test_backward_settings_and_refusals(lib):
+    s0, n0 = _status(_cfg(), B.SDM_OP_BACKWARD)
+    assert s0 == B.SDM_OK and n0 > 0
+    assert _status(_cfg(tokens=512), B.SDM_OP_BACKWARD)[1] > n0  # partial sums grow with the tokens
+    assert _status(_cfg(shared_bank=True), B.SDM_OP_BACKWARD)[0] == B.SDM_ERR_RANGE
+    # a snapshot of 2^31 rows (batch * heads * tokens * num_writes) is refused before any work
+    big = _cfg(batch=64, heads=64, tokens=4096, num_writes=128)
+    assert _status(big, B.SDM_OP_BACKWARD)[0] == B.SDM_ERR_RANGE and "snapshot" in B.last_error()
+    assert _status(_cfg(batch=64, heads=64, tokens=4096, num_writes=64), B.SDM_OP_BACKWARD)[0] == B.SDM_OK
+    assert _status(_cfg(), 4)[0] == B.SDM_ERR_RANGE  # no op 4
+
+
+def test_save_and_backward_refuse_before_device_work(lib):
+    cfg = _cfg()
+    n = ctypes.c_size_t(0)
+    assert lib.sdm_workspace_size(ctypes.byref(cfg), B.SDM_OP_WRITE_READ, 0, ctypes.byref(n)) == B.SDM_OK
+    base, step = 1 << 40, 1 << 36  # fake, never dereferenced: every check below fails before any HIP call
+    p = [_fake(base + i * step) for i in range(12)]
+    ws = _fake(base + 40 * step)
+    # the saving forward: NULL snapshot, shared bank, snapshot overlapping the bank
+    q = list(p)
+    q[9] = None
+    assert lib.sdm_write_read_save(ctypes.byref(cfg), *q, ws, n.value, None) == B.SDM_ERR_NULL
+    assert "snapshot" in B.last_error()
+    shared = _cfg(shared_bank=True)
+    assert lib.sdm_write_read_save(ctypes.byref(shared), *p, ws, n.value, None) == B.SDM_ERR_RANGE
+    q = list(p)
+    q[9] = _fake(base + 7 * step + 4096)  # inside the bank
+    assert lib.sdm_write_read_save(ctypes.byref(cfg), *q, ws, n.value, None) == B.SDM_ERR_ALIAS
+    # the backward: NULL gradient, misaligned grad_bank, a gradient overlapping an input
+    nb = ctypes.c_size_t(0)
+    assert lib.sdm_workspace_size(ctypes.byref(cfg), B.SDM_OP_BACKWARD, 0, ctypes.byref(nb)) == B.SDM_OK
+    g = [_fake(base + i * step) for i in range(17)]
+    q = list(g)
+    q[11] = None  # grad_read_queries
+    assert lib.sdm_write_read_backward(ctypes.byref(cfg), *q, ws, nb.value, None) == B.SDM_ERR_NULL
+    q = list(g)
+    q[9] = _fake(base + 9 * step + 4)  # grad_bank
+    assert lib.sdm_write_read_backward(ctypes.byref(cfg), *q, ws, nb.value, None) == B.SDM_ERR_LAYOUT
+    q = list(g)
+    q[12] = q[2]  # grad_values = values
+    assert lib.sdm_write_read_backward(ctypes.byref(cfg), *q, ws, nb.value, None) == B.SDM_ERR_ALIAS
+    assert lib.sdm_write_read_backward(ctypes.byref(cfg), *g, ws, nb.value - 1, None) == B.SDM_ERR_WORKSPACE
