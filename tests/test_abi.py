@@ -180,22 +180,24 @@ def test_save_and_backward_refuse_before_device_work(lib):
     n = ctypes.c_size_t(0)
     assert lib.sdm_workspace_size(ctypes.byref(cfg), B.SDM_OP_WRITE_READ, 0, ctypes.byref(n)) == B.SDM_OK
     base, step = 1 << 40, 1 << 36  # fake, never dereferenced: every check below fails before any HIP call
-    p = [_fake(base + i * step) for i in range(12)]
+    # keys, queries, values, gates (2), sub-keys, bank, out, snapshot, write ids, read ids
+    p = [_fake(base + i * step) for i in range(11)]
     ws = _fake(base + 40 * step)
     # the saving forward: NULL snapshot, shared bank, snapshot overlapping the bank
     q = list(p)
-    q[9] = None
+    q[8] = None
     assert lib.sdm_write_read_save(ctypes.byref(cfg), *q, ws, n.value, None) == B.SDM_ERR_NULL
     assert "snapshot" in B.last_error()
     shared = _cfg(shared_bank=True)
     assert lib.sdm_write_read_save(ctypes.byref(shared), *p, ws, n.value, None) == B.SDM_ERR_RANGE
     q = list(p)
-    q[9] = _fake(base + 7 * step + 4096)  # inside the bank
+    q[8] = _fake(base + 6 * step + 4096)  # inside the bank
     assert lib.sdm_write_read_save(ctypes.byref(cfg), *q, ws, n.value, None) == B.SDM_ERR_ALIAS
     # the backward: NULL gradient, misaligned grad_bank, a gradient overlapping an input
     nb = ctypes.c_size_t(0)
     assert lib.sdm_workspace_size(ctypes.byref(cfg), B.SDM_OP_BACKWARD, 0, ctypes.byref(nb)) == B.SDM_OK
-    g = [_fake(base + i * step) for i in range(17)]
+    # inputs (6), bank, snapshot, grad_out, grad_bank, then the six gradients
+    g = [_fake(base + i * step) for i in range(16)]
     q = list(g)
     q[11] = None  # grad_read_queries
     assert lib.sdm_write_read_backward(ctypes.byref(cfg), *q, ws, nb.value, None) == B.SDM_ERR_NULL
