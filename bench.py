@@ -280,6 +280,9 @@ def bench_decode(args, torch, binding, synth):
                               binding.SDM_F32, binding.SDM_F32, s.rows)
     ws = torch.empty(binding.workspace_size(cfg, binding.SDM_OP_DECODE), dtype=torch.uint8, device=dev)
     kw = dict(widths=s.widths, num_writes=s.num_writes, num_reads=s.num_reads, workspace=ws)
+    # the prepared step (config and workspace made once): what a serving loop calls per token
+    step_fn = binding.DecodeStep(s.batch, s.heads, s.widths, s.subkey_dim, s.head_dim, s.num_writes, s.num_reads,
+                                 torch.float32, torch.float32, s.rows, dev, workspace=ws)
     res = {}
     outs = {}
     for mode in ("donated", "copied"):
@@ -291,11 +294,10 @@ def bench_decode(args, torch, binding, synth):
             nonlocal cur
             a = steps[i]
             if mode == "donated":
-                binding.sdm_decode_step(a["wkeys"], a["rq"], a["values"], a["alpha"], a["beta"], sub, banks[0],
-                                        out=out, **kw)
+                step_fn(a["wkeys"], a["rq"], a["values"], a["alpha"], a["beta"], sub, banks[0], out=out)
             else:
-                binding.sdm_decode_step(a["wkeys"], a["rq"], a["values"], a["alpha"], a["beta"], sub, banks[cur],
-                                        banks[1 - cur], out=out, **kw)
+                step_fn(a["wkeys"], a["rq"], a["values"], a["alpha"], a["beta"], sub, banks[cur], banks[1 - cur],
+                        out=out)
                 cur = 1 - cur
 
         for i in range(args.decode_warmup):

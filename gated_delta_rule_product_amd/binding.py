@@ -390,3 +390,35 @@ def sdm_decode_step(write_keys, read_queries, values, forget_gate, input_gate, s
                                   _ptr(out), _ptr(widx), _ptr(ridx), _ptr(ws), 0 if ws is None else ws.numel(),
                                   _stream(bank_in.device)))
     return out, widx, ridx, bank_out
+
+
+class DecodeStep:
+    """A prepared single-token decode step for fixed shapes (serving loops): the config and the workspace are made
+    once, and a call only hands the tensors' pointers to sdm_decode_step (which still validates the config, the
+    ranges and the aliasing on every call). Tensors must have the shapes, dtypes and bank layout given here
+    (contiguous inputs [batch, 1, heads, ...]; bank [batch, heads, bank_rows, head_dim] with row stride
+    bank_row_stride). Returns out [batch, 1, heads, head_dim]."""
+
+    def __init__(self, batch, heads, widths, subkey_dim, head_dim, num_writes, num_reads, act_dtype, bank_dtype,
+                 bank_rows, device, bank_row_stride=0, workspace=None):
+        self._cfg = make_config(batch, 1, heads, widths, subkey_dim, head_dim, num_writes, num_reads, 1,
+                                _DT[act_dtype], _DT[bank_dtype], bank_rows, bank_row_stride)
+        self._cfgp = ctypes.byref(self._cfg)
+        self._ws = _workspace(workspace_size(self._cfg, SDM_OP_DECODE), device, workspace)
+        self._wsp = _ptr(self._ws)
+        self._wsn = 0 if self._ws is None else self._ws.numel()
+        self._fn = load().sdm_decode_step
+        self._device = device
+        self._out_shape = (batch, 1, heads, head_dim)
+        self._act = act_dtype
+
+    def __call__(self, write_keys, read_queries, values, forget_gate, input_gate, subkeys, bank_in, bank_out=None,
+                 out=None, write_idx=None, read_idx=None):
+        if out is None:
+            out = torch.empty(self._out_shape, dtype=self._act, device=self._device)
+        _check(self._fn(self._cfgp, write_keys.data_ptr(), read_queries.data_ptr(), values.data_ptr(),
+                        forget_gate.data_ptr(), input_gate.data_ptr(), subkeys.data_ptr(), bank_in.data_ptr(),
+                        (bank_out if bank_out is not None else bank_in).data_ptr(), out.data_ptr(),
+                        _ptr(write_idx), _ptr(read_idx), self._wsp, self._wsn,
+                        torch.cuda.current_stream(self._device).cuda_stream))
+        return out

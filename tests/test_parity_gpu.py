@@ -543,6 +543,30 @@ def test_decode_shapes(d, W, R, widths, dk, act, bank):
         ref_bank = ref["bank"]
 
 
+def test_prepared_decode_step_equals_decode_step():
+    """binding.DecodeStep (config and workspace made once) gives the bits of sdm_decode_step, donated and copied."""
+    s = synth.WORKLOADS["decode_b128"].with_(batch=8)
+    sub = to_dev(synth.make_subkeys(s, seed=15), torch.float32)
+    bank0 = to_dev(synth.make_bank(s, seed=15), torch.float32)
+    step = binding.DecodeStep(s.batch, s.heads, s.widths, s.subkey_dim, s.head_dim, s.num_writes, s.num_reads,
+                              torch.float32, torch.float32, s.rows, DEV)
+    kw = dict(widths=s.widths, num_writes=s.num_writes, num_reads=s.num_reads)
+    b_ref, b_new, b_cp = bank0.clone(), bank0.clone(), bank0.clone()
+    print("prepared decode step", flush=True)
+    for i in range(3):
+        x = synth.make_step_inputs(s, seed=15, step=i)
+        t = {k: to_dev(v, torch.float32) for k, v in x.items()}
+        args = (t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"], sub)
+        o_ref, _, _, _ = binding.sdm_decode_step(*args, b_ref, **kw)
+        o_new = step(*args, b_new)
+        succ = torch.empty_like(b_cp)
+        o_cp = step(*args, b_cp, succ)
+        b_cp = succ
+        torch.cuda.synchronize()
+        assert torch.equal(o_ref, o_new) and torch.equal(o_ref, o_cp)
+        assert torch.equal(b_ref, b_new) and torch.equal(b_ref, b_cp)
+
+
 def test_decode_graph_replay_equals_eager():
     """Decode steps captured into a HIP graph (the C ABI allocates nothing and never synchronises) replay to the
     same bits as the eager calls; several replays with eager work and synchronisations between them."""
