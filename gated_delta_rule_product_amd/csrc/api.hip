@@ -479,8 +479,12 @@ static sdm_status write_read_impl(const sdm_config* cfg, const void* write_keys,
   pa.beta = input_gate;
   pa.chunks = ws + L.chunks;
   pa.counts = (ChunkCounts*)(ws + L.counts);
-  pa.scat = !snapshot && (loop_held_path(D) || loop_narrow_path(D)) ? 0 : 1;
-  pa.lanemajor = !snapshot && !loop_held_path(D) && loop_narrow_lanemajor(D) ? 1 : 0;
+  // the loop that runs: held-row (also with a snapshot), narrow (not with a snapshot) or segmented; only the
+  // segmented loop reads the slot segments, only the narrow one lane-major terms
+  const bool held = snapshot ? loop_held_snap_ok(D) : loop_held_path(D);
+  const bool narrow = !held && !snapshot && loop_narrow_path(D);
+  pa.scat = held || narrow ? 0 : 1;
+  pa.lanemajor = narrow && loop_narrow_lanemajor(D) ? 1 : 0;
   pa.evcode = snapshot ? 1 : 0;
   TRY(hip_status(timed(SDM_K_PLAN, st, [&] { return launch_plan(D, pa, st); }), "chunk plan launch"));
   LoopArgs la;

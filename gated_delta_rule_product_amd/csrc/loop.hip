@@ -451,8 +451,11 @@ template <> struct Act4<bf16_t> {
   }
 };
 
-// FULL: every part has exactly 32 write and 32 read terms (no per-row term-count test).
-template <typename A, typename Bk, bool FULL>
+// FULL: every part has exactly 32 write and 32 read terms (no per-row term-count test). SNAP: also the backward's
+// snapshot (a.snap; the plan tagged every event with its term index): a slot's only event stores its held row (the
+// chunk-start row, the row before that event), and a slot written more than once stores its running row before
+// each of its events.
+template <typename A, typename Bk, bool FULL, bool SNAP>
 __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, int nslices) {
   if (a.abort && *a.abort) return;  // shared-bank conflict: no work (uniform over the grid)
   constexpr int EPL = Lane<Bk>::EPL;
@@ -642,6 +645,16 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
     //    than once go to LDS (when they fit) and are finished in step 10, one slot per lane group
     const bool mrows = cnt.nmseg <= HELD_MROWS;
     const MSeg* msegs_g = (const MSeg*)(greg + CL.multi);
+    // snapshot rows of this stream: row (t, i) at (t * W + i) * d, through a buffer resource (base in scalar
+    // registers, 32-bit lane offsets: the held rows leave few vector registers)
+    __amdgpu_buffer_rsrc_t rsnap;
+    if constexpr (SNAP)
+      rsnap = __builtin_amdgcn_make_buffer_rsrc((void*)((Bk*)a.snap + (long long)st * D.T * D.W * D.d), (short)0,
+                                                (int)(uint32_t)((unsigned long long)D.T * D.W * D.d * sizeof(Bk)),
+                                                BUF_RSRC_WORD3);
+    auto snap_off = [&](int t, int i) -> uint32_t {
+      return (uint32_t)((((uint32_t)(t0 + t) * (uint32_t)W + (uint32_t)i) * (uint32_t)D.d + (uint32_t)mycol) * 4u);
+    };
     if (act) {
       const float4 dg = *(const float4*)(sD + gt * COLS + q * EPL);
       const float ag = sA[gt];
@@ -650,6 +663,9 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
         if (FULL || u < tpw) {
           const int code = wl[u];
           if (code == -2) {  // the slot's only event: own token, own weight
+            if constexpr (SNAP)
+              __builtin_amdgcn_raw_buffer_store_b128(w16_t{row[u].x, row[u].y, row[u].z, row[u].w}, rsnap,
+                                                     (int)snap_off(gt, part * tpw + u), 0, 0);
             float m[EPL];
             Lane<Bk>::unpack(row[u], m);
             const Pair p = pw[u];
@@ -666,9 +682,14 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
               const Ev* mev = (const Ev*)(msegs_g + cnt.nmseg);
               for (int e = sg.beg; e < sg.end; ++e) {
                 const Ev x = mev[e];
-                const float al = sA[x.tok];
+                const int tk = SNAP ? (x.tok & 0xFFFF) : x.tok;
+                if constexpr (SNAP)
+                  __builtin_amdgcn_raw_buffer_store_b128(
+                      w16_t{__float_as_uint(m[0]), __float_as_uint(m[1]), __float_as_uint(m[2]), __float_as_uint(m[3])},
+                      rsnap, (int)snap_off(tk, x.tok >> 16), 0, 0);
+                const float al = sA[tk];
 #pragma unroll
-                for (int k = 0; k < EPL; ++k) m[k] = al * m[k] + x.w * sD[x.tok * COLS + q * EPL + k];
+                for (int k = 0; k < EPL; ++k) m[k] = al * m[k] + x.w * sD[tk * COLS + q * EPL + k];
               }
               Lane<Bk>::store(bank + ((uint64_t)(uint32_t)pw[u].slot * ld + (uint32_t)mycol), m);
             }
@@ -702,8 +723,14 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
           float m[EPL] = {__uint_as_float(x0.x), __uint_as_float(x0.y), __uint_as_float(x0.z), __uint_as_float(x0.w)};
           for (int e = sg.beg; e < sg.end; ++e) {
             const Ev x = mev[e];
-            const float al = sA[x.tok];
-            const float4 dd = *(const float4*)(sD + x.tok * COLS + q * EPL);
+            const int tk = SNAP ? (x.tok & 0xFFFF) : x.tok;
+            if constexpr (SNAP)
+              if (valid)
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    w16_t{__float_as_uint(m[0]), __float_as_uint(m[1]), __float_as_uint(m[2]), __float_as_uint(m[3])},
+                    rsnap, (int)snap_off(tk, x.tok >> 16), 0, 0);
+            const float al = sA[tk];
+            const float4 dd = *(const float4*)(sD + tk * COLS + q * EPL);
             m[0] = al * m[0] + x.w * dd.x; m[1] = al * m[1] + x.w * dd.y;
             m[2] = al * m[2] + x.w * dd.z; m[3] = al * m[3] + x.w * dd.w;
           }
@@ -1150,6 +1177,11 @@ bool loop_held_path(const Dims& D) {
          D.W >= gpt && D.R >= gpt && loop_held_lds_bytes(D.C, D.W, D.R, COLS) <= 160 * 1024;
 }
 
+// The held-row variant can also write the snapshot when a stream's snapshot fits 32-bit byte offsets.
+bool loop_held_snap_ok(const Dims& D) {
+  return loop_held_path(D) && (unsigned long long)D.T * D.W * D.d * 4 < BUF_OOB;
+}
+
 template <typename A, typename Bk>
 static hipError_t launch_loop_t(const Dims& D, const LoopArgs& a, hipStream_t st) {
   constexpr int COLS = 4 * Lane<Bk>::EPL;
@@ -1158,18 +1190,17 @@ static hipError_t launch_loop_t(const Dims& D, const LoopArgs& a, hipStream_t st
   const size_t staged = loop_lds_bytes(D.C, D.W, D.R, COLS, true);
   const int gpt = 128 / D.C;
   if constexpr (sizeof(Bk) == 4) {
-    if (loop_held_path(D) && !a.snap) {
+    if (a.snap ? loop_held_snap_ok(D) : loop_held_path(D)) {
       const size_t lds = loop_held_lds_bytes(D.C, D.W, D.R, COLS);
-      if (D.W / gpt == Hold<Bk>::N && D.R / gpt == Hold<Bk>::N) {
-        (void)hipFuncSetAttribute((const void*)loop_held_kernel<A, Bk, true>,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        hipLaunchKernelGGL((loop_held_kernel<A, Bk, true>), dim3((unsigned)nblk), dim3(LOOP_NT), lds, st, D, a,
-                           nslices);
+      const bool full = D.W / gpt == Hold<Bk>::N && D.R / gpt == Hold<Bk>::N;
+      auto go = [&](auto kern) {
+        (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(LOOP_NT), lds, st, D, a, nslices);
+      };
+      if (a.snap) {
+        if (full) go(loop_held_kernel<A, Bk, true, true>); else go(loop_held_kernel<A, Bk, false, true>);
       } else {
-        (void)hipFuncSetAttribute((const void*)loop_held_kernel<A, Bk, false>,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        hipLaunchKernelGGL((loop_held_kernel<A, Bk, false>), dim3((unsigned)nblk), dim3(LOOP_NT), lds, st, D, a,
-                           nslices);
+        if (full) go(loop_held_kernel<A, Bk, true, false>); else go(loop_held_kernel<A, Bk, false, false>);
       }
       return hipGetLastError();
     }

@@ -272,11 +272,13 @@ struct LoopArgs {
   void* bank; void* out;
   const int32_t* abort;   // if not NULL and *abort != 0: do nothing (shared-bank conflict)
   void* snap;             // if not NULL: [S][T][W][d] bank dtype, the row of every write event before it (the
-                          // segmented loop_kernel writes it; needs PlanArgs::evcode)
+                          // held-row or the segmented loop writes it; needs PlanArgs::evcode)
 };
 hipError_t launch_loop(const Dims& D, const LoopArgs& a, hipStream_t st);
 // True if launch_loop runs the held-row variant (which reads last-event codes, not slot segments).
 bool loop_held_path(const Dims& D);
+// True if launch_loop runs the held-row variant for a call that writes the snapshot.
+bool loop_held_snap_ok(const Dims& D);
 // True if launch_loop runs the narrow variant (16-byte column slices; also reads last-event codes).
 bool loop_narrow_path(const Dims& D);
 // True if it runs the narrow variant with 16 terms of each kind per lane, which reads lane-major terms.
