@@ -126,6 +126,9 @@ CASES = [
     ("bf16_act", synth.Shape(2, 48, 2, (16, 16), 8, 64, 8, 8, 16, "bf16", "f32", name="bf16a"), True),
     ("bf16_bank", synth.Shape(1, 48, 2, (16, 16), 8, 64, 8, 8, 16, "bf16", "bf16", name="bf16b"), True),
     ("wide_w", synth.Shape(1, 24, 1, (16, 16), 8, 48, 160, 136, 8, name="wide"), True),
+    # held-row loop with more slots written several times per chunk than its LDS keeps (~300 of 512 slots): the
+    # events of those slots are applied, and their snapshot rows stored, from the plan region
+    ("held_many_multi", synth.Shape(1, 96, 1, (16, 32), 8, 32, 32, 32, 32, name="multi"), True),
 ]
 
 
