@@ -181,3 +181,62 @@ def test_backward_layer_65k_full_size():
     print("full-size backward: oracle", flush=True)
     ref = run_oracle(s, x, dout, dbank)
     check(s, got, ref, _tol(s))
+
+
+def test_training_step_graph_replay_equals_eager():
+    """The saving forward and the backward captured into one HIP graph (the gradient bank reset by a fill kernel
+    inside it) and replayed several times, with eager work and synchronisations between the replays: every replay
+    gives the eager outputs and gradients bit for bit, and leaves the bank as it found it."""
+    s = synth.WORKLOADS["tiny_1k"].with_(tokens=96, batch=2, heads=2, chunk_size=32)
+    x = synth.make_inputs(s, seed=47)
+    dout, _ = _upstream(s, 48, False)
+    t = {k: to_dev(x[k], torch.float32) for k in ("wkeys", "rq", "values", "alpha", "beta", "subkeys")}
+    g_out = to_dev(dout, torch.float32)
+    kw = dict(widths=s.widths, num_writes=s.num_writes, num_reads=s.num_reads, chunk_size=s.chunk_size)
+    cfg = binding.make_config(s.batch, s.tokens, s.heads, s.widths, s.subkey_dim, s.head_dim, s.num_writes,
+                              s.num_reads, s.chunk_size, binding.SDM_F32, binding.SDM_F32, s.rows)
+    wsf = torch.empty(binding.workspace_size(cfg, binding.SDM_OP_WRITE_READ), dtype=torch.uint8, device=DEV)
+    wsb = torch.empty(binding.workspace_size(cfg, binding.SDM_OP_BACKWARD), dtype=torch.uint8, device=DEV)
+    bank = to_dev(x["bank"], torch.float32)
+    bank0 = bank.clone()
+    out = torch.empty((s.batch, s.tokens, s.heads, s.head_dim), device=DEV)
+    snap = torch.empty((s.batch, s.heads, s.tokens, s.num_writes, s.head_dim), device=DEV)
+    gbank = torch.zeros_like(bank)
+    grads = {}
+
+    def step():
+        gbank.zero_()
+        binding.sdm_write_read_save(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"], t["subkeys"], bank,
+                                    out=out, snapshot=snap, workspace=wsf, **kw)
+        grads.update(binding.sdm_write_read_backward(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"],
+                                                     t["subkeys"], bank, snap, g_out, gbank, workspace=wsb, **kw))
+
+    print("training step graph replay", flush=True)
+    step()
+    torch.cuda.synchronize()
+    ref_out = out.clone()
+    ref = {k: v.clone() for k, v in grads.items()}
+    assert torch.equal(bank, bank0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    captured = dict(grads)  # the gradient tensors the graph writes
+    for r in range(3):
+        out.fill_(float("nan"))
+        for v in captured.values():
+            v.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out), f"replay {r}: out differs"
+        for k, v in captured.items():
+            assert torch.equal(v, ref[k]), f"replay {r}: gradient {k} differs"
+        assert torch.equal(bank, bank0), f"replay {r}: bank not restored"
+        step()  # eager work between replays
+        torch.cuda.synchronize()
