@@ -213,7 +213,7 @@ __host__ __device__ inline StepLds step_lds(unsigned char* base, const Dims& D, 
     KS = ks > KS ? ks : KS;
   }
   for (int w = 0; w < 4; ++w) {
-    L.scratch[w] = (uint64_t*)take((size_t)(KS + 8) * 8);
+    L.scratch[w] = (uint64_t*)take((size_t)(KS + MERGE_RB) * 8);
     L.sorted[w] = (uint64_t*)take((size_t)KS * 8);
   }
   L.wid = (int32_t*)take((size_t)D.W * 4);
@@ -253,35 +253,54 @@ __global__ __launch_bounds__(STEP_NT) void decode_step_kernel(Dims D, DecodeArgs
   constexpr int COLW = 64 * EPL;
   extern __shared__ __align__(16) unsigned char lds[];
   const StepLds L = step_lds(lds, D, a.plan, EPL);
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  // the wave index as a scalar: plan fields picked by wave then load as scalar loads (a vector load of them would
+  // queue behind the sub-key loads issued early below and wait for them)
+  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int st = blockIdx.x;  // stream b * H + h; with one token the [B, 1, H] row index equals st
   const int h = st % D.H;
   // (members picked by kind or wave with conditionals, not indexed: a runtime index into a struct's array puts the
   // struct in scratch memory)
   auto pick2 = [](auto x0, auto x1, int i) { return i ? x1 : x0; };
   auto pick4 = [](auto x0, auto x1, auto x2, auto x3, int i) { return i < 2 ? (i ? x1 : x0) : (i == 2 ? x2 : x3); };
+  // factor top-k of both queries: task kind * F + f on wave task % 4. Each wave issues the loads of its first
+  // task's first block now; they arrive while the candidate tables are built.
+  long long sumn = 0;
+  for (int f = 0; f < D.F; ++f) sumn += D.widths[f];
+  const A* subh = (const A*)a.subkeys + (long long)h * sumn * D.dk;
+  auto task_in = [&](int task, int* f, const A** qv, const A** tab) {
+    const int kind = task / D.F;
+    *f = task % D.F;
+    long long off = 0;
+    for (int g = 0; g < *f; ++g) off += D.widths[g];
+    *qv = (const A*)pick2(a.queries[0], a.queries[1], kind) + (long long)st * D.F * D.dk;
+    *tab = subh + off * D.dk;
+  };
+  FactorBlock<A, NPL> fb;
+  if (wv < 2 * D.F) {
+    int f;
+    const A *qv, *tab;
+    task_in(wv, &f, &qv, &tab);
+    factor_load<A, NPL>(D, f, qv, tab, 0, fb);
+  }
   // candidate tables: threads 0-127 build the write table, 128-255 the read table
   {
-    const int kind = tid >> 7, t = tid & 127;
+    const int kind = wv >> 1, t = tid & 127;
     const TopkPlan& P = kind ? a.plan[1] : a.plan[0];
     cand_offsets(P, D.F, pick2(L.offs[0], L.offs[1], kind), t, 128);
     __syncthreads();
     cand_emit(P, D.F, pick2(L.offs[0], L.offs[1], kind), pick2(L.ctab[0], L.ctab[1], kind), t, 128);
   }
-  // factor top-k of both queries: task kind * F + f on wave task % 4
   uint64_t* wscr = pick4(L.scratch[0], L.scratch[1], L.scratch[2], L.scratch[3], wv);
   uint64_t* wsrt = pick4(L.sorted[0], L.sorted[1], L.sorted[2], L.sorted[3], wv);
-  long long sumn = 0;
-  for (int f = 0; f < D.F; ++f) sumn += D.widths[f];
-  const A* subh = (const A*)a.subkeys + (long long)h * sumn * D.dk;
   for (int task = wv; task < 2 * D.F; task += 4) {
-    const int kind = task / D.F, f = task % D.F;
-    long long off = 0;
-    for (int g = 0; g < f; ++g) off += D.widths[g];
+    const int kind = task / D.F;
+    int f;
+    const A *qv, *tab;
+    task_in(task, &f, &qv, &tab);
+    if (task != wv) factor_load<A, NPL>(D, f, qv, tab, 0, fb);
     const TopkPlan& P = kind ? a.plan[1] : a.plan[0];
-    const A* qv = (const A*)pick2(a.queries[0], a.queries[1], kind) + (long long)st * D.F * D.dk;
-    wave_factor_topk<A, NPL>(D, P, f, qv, subh + off * D.dk, pick2(L.fsc[0], L.fsc[1], kind),
-                             pick2(L.fid[0], L.fid[1], kind), wscr, wsrt);
+    wave_factor_topk<A, NPL>(D, P, f, qv, tab, pick2(L.fsc[0], L.fsc[1], kind), pick2(L.fid[0], L.fid[1], kind),
+                             wscr, wsrt, fb);
   }
   __syncthreads();  // factor lists and candidate tables complete
   if (wv < 2) {  // merges: wave 0 the write query, wave 1 the read query
@@ -293,18 +312,6 @@ __global__ __launch_bounds__(STEP_NT) void decode_step_kernel(Dims D, DecodeArgs
     int32_t* uid = pick2(a.user_ids[0], a.user_ids[1], kind);
     if (uid)
       for (int r = lane; r < P.k; r += 64) uid[(long long)st * P.k + r] = ids[r];
-  }
-  __syncthreads();
-  // read slots that are also written this step (the slots of one top-k are distinct): read slot j is compared
-  // with the write slots by the 4 consecutive threads 4 j .. 4 j + 3, each scanning a quarter, then combined
-  for (int j0 = 0; j0 < D.R; j0 += STEP_NT / 4) {
-    const int j = j0 + (tid >> 2), qt = tid & 3;
-    const int s = j < D.R ? L.rid[j] : -1;
-    int mi = -1;
-    for (int i = qt; i < D.W; i += 4) mi = L.wid[i] == s ? i : mi;
-    mi = max(mi, __shfl_xor(mi, 1, 64));
-    mi = max(mi, __shfl_xor(mi, 2, 64));
-    if (qt == 0 && j < D.R) L.rmatch[j] = mi;
   }
   __syncthreads();
   const float al = to_f<A>(((const A*)a.alpha)[st]);
@@ -331,6 +338,20 @@ __global__ __launch_bounds__(STEP_NT) void decode_step_kernel(Dims D, DecodeArgs
       rr[u] = w16_t{0u, 0u, 0u, 0u};
       if (valid && j < D.R) rr[u] = *(const w16_t*)(bin + (long long)L.rid[j] * D.ld + col);
     });
+    if (c0 == 0) {
+      // while the rows load: read slots that are also written this step (the slots of one top-k are distinct);
+      // read slot j is compared with the write slots by the 4 consecutive threads 4 j .. 4 j + 3, each scanning a
+      // quarter, then combined. Read after the barrier below, in the output.
+      for (int j0 = 0; j0 < D.R; j0 += STEP_NT / 4) {
+        const int j = j0 + (tid >> 2), qt = tid & 3;
+        const int s = j < D.R ? L.rid[j] : -1;
+        int mi = -1;
+        for (int i = qt; i < D.W; i += 4) mi = L.wid[i] == s ? i : mi;
+        mi = max(mi, __shfl_xor(mi, 1, 64));
+        mi = max(mi, __shfl_xor(mi, 2, 64));
+        if (qt == 0 && j < D.R) L.rmatch[j] = mi;
+      }
+    }
     // r = sum_i w_i M[S_i]: this wave's rows in order
     float acc[EPL];
 #pragma unroll
@@ -425,6 +446,7 @@ bool decode_step_fits(const Dims& D, const DecodeArgs& a) {
     if (a.plan[q].ncand > 64 * cpl || a.plan[q].kpmax > 1024) return false;
   const int esz = D.act == SDM_BF16 ? 2 : 4;
   if ((D.dk * esz) % 16 != 0 || ((uintptr_t)a.subkeys) % 16 != 0) return false;
+  if (((uintptr_t)a.queries[0]) % 16 != 0 || ((uintptr_t)a.queries[1]) % 16 != 0) return false;
   return step_lds(nullptr, D, a.plan, epl).bytes <= 64 * 1024;
 }
 

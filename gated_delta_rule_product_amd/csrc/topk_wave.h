@@ -45,12 +45,14 @@ __device__ __forceinline__ uint64_t lanes_below_mask() {
 // field, shifted right by *shift, is <= res >> *shift, and the loop stops (about log2 of the key count bits for
 // distinct values instead of 32). If the loop runs to bit 0 the class is the keys whose field equals res and
 // *need is the number of them still to take.
+// The search may start below bit 31: bits above `top` are then res0's (zero at and below top), every flagged key
+// at or below that prefix shares it, and *csize counts the keys with it.
 template <int N, bool HIGH>
 __device__ __forceinline__ uint32_t radix_select32(const uint64_t (&key)[N], const bool (&in)[N], int* need,
-                                                   int* shift, int* csize) {
-  uint32_t res = 0;
+                                                   int* shift, int* csize, int top = 31, uint32_t res0 = 0) {
+  uint32_t res = res0;
   int nd = *need, cs = *csize, sh = 0;
-  for (int bit = 31; bit >= 0; --bit) {
+  for (int bit = top; bit >= 0; --bit) {
     int cnt = 0;
 #pragma unroll
     for (int j = 0; j < N; ++j) {
@@ -74,10 +76,14 @@ __device__ __forceinline__ uint32_t radix_select32(const uint64_t (&key)[N], con
   return res;
 }
 
+extern "C" __device__ __attribute__((const)) unsigned int __ockl_wfred_and_u32(unsigned int);
+extern "C" __device__ __attribute__((const)) unsigned int __ockl_wfred_or_u32(unsigned int);
+
 // Selects the k smallest of the wave's keys (key[j] of every lane; unused slots hold ~0ull, which no used key
-// equals; k <= number of used slots), writes them ascending to out[0..k). scratch: >= k + 8 entries of this wave's
-// LDS, not overlapping out. Wave-uniform k.
-template <int N>
+// equals; k <= number of used slots), writes them ascending to out[0..k). RB: selected keys read per batch in the
+// rank placement (more reads in flight, a larger pad). scratch: >= k + RB entries of this wave's LDS, not
+// overlapping out. Wave-uniform k.
+template <int N, int RB = 8>
 __device__ void wave_select_sorted(const uint64_t (&key)[N], int k, uint64_t* scratch, uint64_t* out) {
   bool all[N];
   int nused = 0;
@@ -92,7 +98,40 @@ __device__ void wave_select_sorted(const uint64_t (&key)[N], int k, uint64_t* sc
 #pragma unroll
     for (int j = 0; j < N; ++j) sel[j] = key[j] != ~0ull;
   } else {
-    const uint32_t hi = radix_select32<N, true>(key, all, &need, &shift, &csize);
+    // A bound on the k-th smallest high half: when at least k lanes hold a used key, the largest lane minimum is
+    // one (each of those lanes holds a key at or below it). Keys above it are never selected, so the high bits
+    // shared by every used key at or below it (wave AND == wave OR) decide nothing: the search starts below them.
+    uint32_t lmin = ~0u;
+    bool has = false;
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      if (key[j] != ~0ull) {
+        lmin = min(lmin, (uint32_t)(key[j] >> 32));
+        has = true;
+      }
+    }
+    const uint32_t bound = __popcll(__ballot(has)) >= k ? __ockl_wfred_max_u32(has ? lmin : 0u) : ~0u;
+    uint32_t andv = ~0u, orv = 0u;
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const uint32_t h = (uint32_t)(key[j] >> 32);
+      if (key[j] != ~0ull && h <= bound) { andv &= h; orv |= h; }
+    }
+    andv = __ockl_wfred_and_u32(andv);
+    orv = __ockl_wfred_or_u32(orv);
+    const uint32_t diff = andv ^ orv;
+    int top = 31;
+    uint32_t res0 = 0;
+    if (diff == 0 || (diff >> 31) == 0) {
+      top = diff ? 31 - __clz(diff) : -1;  // highest differing bit (-1: all used keys share the high half)
+      const int s = top + 1;               // 1..31, or 0
+      res0 = andv & ~((1u << s) - 1u);     // the shared prefix, zero at and below top
+      int cs = 0;                          // keys with that prefix (every key at or below the bound, maybe more)
+#pragma unroll
+      for (int j = 0; j < N; ++j) cs += __popcll(__ballot(((uint32_t)(key[j] >> 32) >> s) == (res0 >> s)));
+      csize = cs;
+    }
+    const uint32_t hi = radix_select32<N, true>(key, all, &need, &shift, &csize, top, res0);
     if (csize == need) {  // decided on the high halves
 #pragma unroll
       for (int j = 0; j < N; ++j) sel[j] = ((uint32_t)(key[j] >> 32) >> shift) <= (hi >> shift);
@@ -118,20 +157,20 @@ __device__ void wave_select_sorted(const uint64_t (&key)[N], int k, uint64_t* sc
     if (sel[j]) scratch[base + __popcll(m & below)] = key[j];
     base += __popcll(m);
   }
-  // pad to a multiple of 8 with the largest key (never below a selected one)
-  const int kpad = (k + 7) & ~7;
+  // pad to a multiple of RB with the largest key (never below a selected one)
+  const int kpad = (k + RB - 1) & ~(RB - 1);
   for (int i = k + lane_id(); i < kpad; i += 64) scratch[i] = ~0ull;
   wave_sync();
-  // rank placement: each selected key's rank is the number of selected keys below it (8 reads in flight)
+  // rank placement: each selected key's rank is the number of selected keys below it (RB reads in flight)
   for (int i = lane_id(); i < k; i += 64) {
     const uint64_t v = scratch[i];
     int r = 0;
-    for (int m = 0; m < kpad; m += 8) {
-      uint64_t x[8];
+    for (int m = 0; m < kpad; m += RB) {
+      uint64_t x[RB];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) x[u] = scratch[m + u];
+      for (int u = 0; u < RB; ++u) x[u] = scratch[m + u];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) r += x[u] < v;
+      for (int u = 0; u < RB; ++u) r += x[u] < v;
     }
     out[r] = v;
   }
@@ -145,27 +184,60 @@ __device__ void wave_select_sorted(const uint64_t (&key)[N], int k, uint64_t* sc
 // selected by (score, position sum, candidate index); writes ids[r] (slot ids, best first) and wts[r] (softmax of
 // the k slot scores: fp64 exponentials, per-lane partial sums in a fixed order and a fixed butterfly) to LDS.
 // scratch and sorted: the calling wave's selection buffers.
+
+// One block of factor f's coordinates, loaded ahead of its use: PB pieces of 16 bytes (VEC coordinates) of each of
+// this lane's sub-key rows and the same pieces of the query (every lane holds them). The loads are unconditional
+// (row and coordinate clamped into the tables) so that no select waits on them; a piece past dk is loaded from the
+// last valid coordinates and skipped where it is used. A caller may issue the first block early and do other work
+// while it arrives.
+template <typename A, int NPL> struct FactorBlock {
+  static constexpr int PB = NPL >= 4 ? 2 : 8 / NPL;
+  uint4 rv[PB][NPL];
+  uint4 qx[PB];
+};
+
+// Requires dk a multiple of VEC (16-byte rows) and 16-byte aligned tab and qv.
+template <typename A, int NPL>
+__device__ __forceinline__ void factor_load(const Dims& D, int f, const A* qv, const A* tab, int c0,
+                                            FactorBlock<A, NPL>& B) {
+  constexpr int VEC = Vec16<A>::N;
+  const int lane = lane_id(), dk = D.dk, n = D.widths[f];
+  // 0 in every lane but not known uniform: the query pieces load as vector loads (counted with the row loads)
+  const int zero = (int)__builtin_amdgcn_mbcnt_lo(0u, 0u);
+#pragma unroll
+  for (int p = 0; p < FactorBlock<A, NPL>::PB; ++p) {
+    const int c = min(c0 + p * VEC, dk - VEC);
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const int i = min(lane + 64 * j, n - 1);
+      B.rv[p][j] = *(const uint4*)(tab + (long long)i * dk + c);
+    }
+    B.qx[p] = *(const uint4*)(qv + f * dk + c + zero);
+  }
+}
+
+// B holds factor f's first block (factor_load at c0 = 0).
 template <typename A, int NPL>
 __device__ void wave_factor_topk(const Dims& D, const TopkPlan& P, int f, const A* qv, const A* tab, float* fsc,
-                                 uint16_t* fid, uint64_t* scratch, uint64_t* sorted) {
-  constexpr int VEC = Vec16<A>::N;
+                                 uint16_t* fid, uint64_t* scratch, uint64_t* sorted, FactorBlock<A, NPL>& B) {
+  constexpr int VEC = Vec16<A>::N, PB = FactorBlock<A, NPL>::PB;
   const int lane = lane_id();
   const int dk = D.dk, n = D.widths[f], kpmax = P.kpmax;
   double acc[NPL];
 #pragma unroll
   for (int j = 0; j < NPL; ++j) acc[j] = 0.0;
-  for (int c0 = 0; c0 < dk; c0 += VEC) {
-    uint4 rv[NPL];
+  for (int c0 = 0; c0 < dk; c0 += PB * VEC) {
+    if (c0 > 0) factor_load<A, NPL>(D, f, qv, tab, c0, B);
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) {
-      const int i = lane + 64 * j;
-      rv[j] = i < n ? *(const uint4*)(tab + (long long)i * dk + c0) : make_uint4(0, 0, 0, 0);
-    }
+    for (int p = 0; p < PB; ++p) {
+      if (c0 + p * VEC < dk) {
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      const double x = to_d<A>(qv[f * dk + c0 + e]);
+        for (int e = 0; e < VEC; ++e) {
+          const double x = Vec16<A>::at(B.qx[p], e);
 #pragma unroll
-      for (int j = 0; j < NPL; ++j) acc[j] = fma(x, Vec16<A>::at(rv[j], e), acc[j]);
+          for (int j = 0; j < NPL; ++j) acc[j] = fma(x, Vec16<A>::at(B.rv[p][j], e), acc[j]);
+        }
+      }
     }
   }
   uint64_t key[NPL];
@@ -183,45 +255,67 @@ __device__ void wave_factor_topk(const Dims& D, const TopkPlan& P, int f, const 
   wave_sync();
 }
 
+constexpr int MERGE_RB = 32;  // rank-placement batch of the merge's selection (its scratch: >= k + MERGE_RB)
+
 template <int CPL>
 __device__ void wave_merge_topk(const Dims& D, const TopkPlan& P, const uint64_t* cand, const float* fsc,
                                 const uint16_t* fid, uint64_t* scratch, uint64_t* sorted, int32_t* ids, float* wts) {
   const int lane = lane_id();
   const int F = D.F, k = P.k, kpmax = P.kpmax;
+  // every candidate's tuple, then the factor scores one factor at a time over all of them (the LDS reads of a
+  // step in flight together); each slot score is still the float32 sum over factors left to right
+  uint64_t tup[CPL];
+  float S[CPL];
+  int ps[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) tup[j] = cand[min(lane + 64 * j, P.ncand - 1)];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    ps[j] = (int)(tup[j] & 0xFFFF);
+    S[j] = fsc[ps[j]];
+  }
+  for (int f = 1; f < F; ++f) {
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int p = (int)((tup[j] >> (16 * f)) & 0xFFFF);
+      S[j] = S[j] + fsc[f * kpmax + p];
+      ps[j] += p;
+    }
+  }
   uint64_t ck[CPL];
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
     const int c = lane + 64 * j;
-    uint64_t key = ~0ull;
-    if (c < P.ncand) {
-      const uint64_t tup = cand[c];
-      int p = (int)(tup & 0xFFFF);
-      float S = fsc[p];
-      int ps = p;
-      for (int f = 1; f < F; ++f) {
-        p = (int)((tup >> (16 * f)) & 0xFFFF);
-        S = S + fsc[f * kpmax + p];  // float32 sum, left to right
-        ps += p;
-      }
-      key = ((uint64_t)desc_key(S) << 32) | ((uint64_t)ps << 20) | (uint64_t)c;
-    }
-    ck[j] = key;
+    ck[j] = c < P.ncand ? ((uint64_t)desc_key(S[j]) << 32) | ((uint64_t)ps[j] << 20) | (uint64_t)c : ~0ull;
   }
-  wave_select_sorted<CPL>(ck, k, scratch, sorted);
+  wave_select_sorted<CPL, MERGE_RB>(ck, k, scratch, sorted);
   const double m = (double)desc_key_value((uint32_t)(sorted[0] >> 32));
+  // rank r = lane + 64 u (u < MAX_K / 64): its exponential is kept for the weight
+  constexpr int RPL = MAX_K / 64;
+  double ex[RPL];
   double zpart = 0.0;
-  for (int r = lane; r < k; r += 64) {
-    const uint64_t kk = sorted[r];
-    const uint64_t tup = cand[(int)(kk & 0xFFFFF)];
-    long long id = 0;
-    for (int f = 0; f < F; ++f) id = id * D.widths[f] + fid[f * kpmax + (int)((tup >> (16 * f)) & 0xFFFF)];
-    ids[r] = (int32_t)id;
-    zpart += exp((double)desc_key_value((uint32_t)(kk >> 32)) - m);
+#pragma unroll
+  for (int u = 0; u < RPL; ++u) {
+    const int r = lane + 64 * u;
+    ex[u] = 0.0;
+    if (64 * u < k && r < k) {
+      const uint64_t kk = sorted[r];
+      const uint64_t t = cand[(int)(kk & 0xFFFFF)];
+      long long id = 0;
+      for (int f = 0; f < F; ++f) id = id * D.widths[f] + fid[f * kpmax + (int)((t >> (16 * f)) & 0xFFFF)];
+      ids[r] = (int32_t)id;
+      ex[u] = exp((double)desc_key_value((uint32_t)(kk >> 32)) - m);
+      zpart += ex[u];
+    }
   }
   double z = zpart;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) z += __shfl_xor(z, o);
-  for (int r = lane; r < k; r += 64) wts[r] = (float)(exp((double)desc_key_value((uint32_t)(sorted[r] >> 32)) - m) / z);
+#pragma unroll
+  for (int u = 0; u < RPL; ++u) {
+    const int r = lane + 64 * u;
+    if (64 * u < k && r < k) wts[r] = (float)(ex[u] / z);
+  }
   wave_sync();
 }
 
