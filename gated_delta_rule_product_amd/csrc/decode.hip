@@ -282,13 +282,17 @@ __global__ __launch_bounds__(STEP_NT) void decode_step_kernel(Dims D, DecodeArgs
     task_in(wv, &f, &qv, &tab);
     factor_load<A, NPL>(D, f, qv, tab, 0, fb);
   }
-  // candidate tables: threads 0-127 build the write table, 128-255 the read table
+  // candidate tables: threads 0-127 build the write table, 128-255 the read table (small tables: waves 0 and 2)
   {
     const int kind = wv >> 1, t = tid & 127;
     const TopkPlan& P = kind ? a.plan[1] : a.plan[0];
-    cand_offsets(P, D.F, pick2(L.offs[0], L.offs[1], kind), t, 128);
-    __syncthreads();
-    cand_emit(P, D.F, pick2(L.offs[0], L.offs[1], kind), pick2(L.ctab[0], L.ctab[1], kind), t, 128);
+    if (cand_one_wave(a.plan[0], D.F) && cand_one_wave(a.plan[1], D.F)) {
+      if (t < 64) cand_table_wave(P, pick2(L.ctab[0], L.ctab[1], kind), lane);
+    } else {
+      cand_offsets(P, D.F, pick2(L.offs[0], L.offs[1], kind), t, 128);
+      __syncthreads();
+      cand_emit(P, D.F, pick2(L.offs[0], L.offs[1], kind), pick2(L.ctab[0], L.ctab[1], kind), t, 128);
+    }
   }
   uint64_t* wscr = pick4(L.scratch[0], L.scratch[1], L.scratch[2], L.scratch[3], wv);
   uint64_t* wsrt = pick4(L.sorted[0], L.sorted[1], L.sorted[2], L.sorted[3], wv);

@@ -134,6 +134,31 @@ __device__ inline void cand_emit(const TopkPlan& P, int F, const int* offs, uint
     if (offs[p0] < MAX_CAND) cand_emit_rest(P, F, p0, P.k / (p0 + 1), out + offs[p0], MAX_CAND - offs[p0]);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts right by 1, 2, 4 and 8 lanes inside each
+// row of 16 (lanes shifted in from outside the row read 0), then the last lane of row 0 and of row 2 added to rows
+// 1 and 3, then the last lane of row 1 added to rows 2 and 3. All lanes active.
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1 and 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+// Two factors with kp[0] <= 64 and at most 64 tuples after any first position: one wave builds the whole table,
+// with no barrier and no search. Lane p_0 counts its tuples, the wave prefix sum gives its output offset, and it
+// writes them (lexicographic order, the same table as cand_offsets + cand_emit).
+__device__ inline bool cand_one_wave(const TopkPlan& P, int F) {
+  return F == 2 && P.kp[0] <= 64 && min(P.kp[1], P.k) <= 64;
+}
+__device__ inline void cand_table_wave(const TopkPlan& P, uint64_t* out, int lane) {
+  const int c = lane < P.kp[0] ? min(P.kp[1], P.k / (lane + 1)) : 0;
+  const int o = wave_inclusive_sum(c) - c;
+  for (int p1 = 0; p1 < c; ++p1) out[o + p1] = (uint64_t)lane | ((uint64_t)p1 << 16);
+}
+
 // LDS bytes of one topk_query workspace (8-byte aligned regions).
 __host__ __device__ inline size_t topk_lds_bytes(int F, int dk, const TopkPlan& P) {
   size_t n = 0;
