@@ -17,6 +17,7 @@ import numpy as np
 
 # tensor ids of the Philox key
 _T_WKEYS, _T_RQ, _T_VALUES, _T_ALPHA, _T_BETA, _T_SUBKEYS, _T_BANK = 1, 2, 3, 4, 5, 6, 7
+_T_X, _T_WIN, _T_WOUT, _T_ALOG, _T_DT = 8, 9, 10, 11, 12
 
 
 @dataclass(frozen=True)
@@ -167,3 +168,26 @@ def make_inputs(s: Shape, seed: int = 0) -> dict:
     d["subkeys"] = make_subkeys(s, seed)
     d["bank"] = make_bank(s, seed)
     return d
+
+
+def make_layer_inputs(s: Shape, model_dim: int, seed: int = 0) -> dict:
+    """Inputs of the layer around the op (all bf16 values as float32 except the per-head gate parameters):
+    x [B, T, Dm] ~ N(0, 1); w_in [2 H F dk + H d + 2 H, Dm] and w_out [Dm, H d] ~ N(0, 1 / fan_in) (so projections
+    and outputs are O(1)); the gate parameters drawn as in FLA's Gated DeltaNet initialisation: A ~ U(0, 16),
+    a_log = log A; dt = exp(U(log 0.001, log 0.1)) clamped at 1e-4, dt_bias = dt + log(-expm1(-dt)) (the inverse of
+    softplus at dt); sub-keys ~ N(0, 1); the initial bank as for the op."""
+    B, T, H, F = s.batch, s.tokens, s.heads, len(s.widths)
+    n_in = 2 * H * F * s.subkey_dim + H * s.head_dim + 2 * H
+    Dm = int(model_dim)
+    u = _rng(seed, _T_ALOG).uniform(0.0, 16.0, size=H)
+    dt = np.exp(_rng(seed, _T_DT).uniform(np.log(0.001), np.log(0.1), size=H))
+    dt = np.maximum(dt, 1e-4)
+    return {
+        "x": round_bf16_rne(_normal(seed, _T_X, (B, T, Dm))),
+        "w_in": round_bf16_rne(_normal(seed, _T_WIN, (n_in, Dm), scale=1.0 / np.sqrt(Dm))),
+        "w_out": round_bf16_rne(_normal(seed, _T_WOUT, (Dm, H * s.head_dim), scale=1.0 / np.sqrt(H * s.head_dim))),
+        "a_log": np.log(u).astype(np.float32),
+        "dt_bias": (dt + np.log(-np.expm1(-dt))).astype(np.float32),
+        "subkeys": make_subkeys(s, seed),
+        "bank": make_bank(s, seed),
+    }
