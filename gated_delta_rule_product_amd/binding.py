@@ -44,6 +44,10 @@ class SdmConfig(ctypes.Structure):
     ]
 
 
+class SdmLayerConfig(ctypes.Structure):
+    _fields_ = [("op", SdmConfig), ("model_dim", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
 def make_config(batch, tokens, heads, widths, subkey_dim, head_dim=1, num_writes=1, num_reads=1, chunk_size=1,
                 act_dtype=SDM_F32, bank_dtype=SDM_F32, bank_rows=None, bank_row_stride=0,
                 shared_bank=False) -> SdmConfig:
@@ -122,6 +126,11 @@ def load():
             lib.sdm_shared_bank_check.restype = ctypes.c_int
             lib.sdm_shared_bank_check.argtypes = [cfgp, _vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int32), _vp]
             lib.sdm_profile_enable.restype = ctypes.c_int
+            lcfgp = ctypes.POINTER(SdmLayerConfig)
+            lib.sdm_layer_workspace_size.argtypes = [lcfgp, ctypes.POINTER(ctypes.c_size_t)]
+            lib.sdm_layer_workspace_size.restype = ctypes.c_int
+            lib.sdm_layer_forward.argtypes = [lcfgp] + [_vp] * 11 + [ctypes.c_size_t, _vp]
+            lib.sdm_layer_forward.restype = ctypes.c_int
             lib.sdm_profile_enable.argtypes = [ctypes.c_int32]
             lib.sdm_profile_read.restype = ctypes.c_int
             lib.sdm_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
@@ -152,7 +161,7 @@ def workspace_size(cfg: SdmConfig, op: int, k: int = 0) -> int:
     return n.value
 
 
-KERNELS = ("cand", "topk", "plan", "loop", "decode", "copy", "bwd")
+KERNELS = ("cand", "topk", "plan", "loop", "decode", "copy", "bwd", "dense")
 
 
 def profile_enable(on: bool = True):
@@ -274,6 +283,66 @@ def sdm_write_read(write_keys, read_queries, values, forget_gate, input_gate, su
             raise SlotConflictError("shared_bank=True but the streams of a head address a common slot "
                                     "(the bank and out were not written)")
     return out, widx, ridx
+
+
+def layer_in_features(heads, widths, subkey_dim, head_dim) -> int:
+    """Rows of the layer's input map: write keys and read queries (H F dk each), values (H d), two gate inputs (2 H)."""
+    return 2 * heads * len(widths) * subkey_dim + heads * head_dim + 2 * heads
+
+
+def sdm_layer_forward(x, w_in, a_log, dt_bias, w_out, subkeys, bank, *, heads, widths, num_writes, num_reads,
+                      chunk_size, want_index=False, y=None, workspace=None, return_workspace=False):
+    """The layer's forward: projections of x [B, T, Dm] (bf16) by w_in, gates, the write/read op on bank
+    [B, H, bank_rows, d] (advances in place), output projection by w_out [Dm, H d]. Returns (y, write_idx,
+    read_idx), plus the workspace (uint8) with return_workspace (its first regions: layer_workspace_views)."""
+    B, T, Dm = x.shape
+    H = int(heads)
+    dk = subkeys.shape[-1]
+    d = bank.shape[-1]
+    _need(x, "x", None, torch.bfloat16)
+    _need(w_in, "w_in", (layer_in_features(H, widths, dk, d), Dm), torch.bfloat16)
+    _need(a_log, "a_log", (H,), torch.float32)
+    _need(dt_bias, "dt_bias", (H,), torch.float32)
+    _need(w_out, "w_out", (Dm, H * d), torch.bfloat16)
+    _need(subkeys, "subkeys", (H, sum(widths), dk), torch.bfloat16)
+    if bank.dim() != 4 or bank.shape[0] != B or bank.shape[1] != H:
+        raise ValueError(f"bank has shape {tuple(bank.shape)}, expected ({B}, {H}, bank_rows, d)")
+    ld = _bank_ld(bank, "bank")
+    lc = SdmLayerConfig()
+    lc.op = make_config(B, T, H, widths, dk, d, num_writes, num_reads, chunk_size, SDM_BF16, _dt(bank),
+                        bank.shape[2], ld)
+    lc.model_dim = int(Dm)
+    n = ctypes.c_size_t(0)
+    _check(load().sdm_layer_workspace_size(ctypes.byref(lc), ctypes.byref(n)))
+    ws = _workspace(n.value, x.device, workspace)
+    if y is None:
+        y = torch.empty((B, T, Dm), dtype=torch.bfloat16, device=x.device)
+    else:
+        _need(y, "y", (B, T, Dm), torch.bfloat16)
+    widx = torch.empty((B, T, H, num_writes), dtype=torch.int32, device=x.device) if want_index else None
+    ridx = torch.empty((B, T, H, num_reads), dtype=torch.int32, device=x.device) if want_index else None
+    _check(load().sdm_layer_forward(ctypes.byref(lc), _ptr(x), _ptr(w_in), _ptr(a_log), _ptr(dt_bias), _ptr(w_out),
+                                    _ptr(subkeys), _ptr(bank), _ptr(y), _ptr(widx), _ptr(ridx), _ptr(ws),
+                                    0 if ws is None else ws.numel(), _stream(x.device)))
+    return (y, widx, ridx, ws) if return_workspace else (y, widx, ridx)
+
+
+def layer_workspace_views(x_shape, heads, widths, subkey_dim, head_dim, ws):
+    """Views of the projections and gates the last sdm_layer_forward left in its workspace `ws` (bf16 tensors):
+    write keys, read queries [B, T, H, F dk], values [B, T, H, d], gate inputs [B, T, 2 H], alpha, beta [B, T, H],
+    o [B, T, H, d] (the layout of the layer's workspace, in order, each region 256-byte aligned)."""
+    B, T, _ = x_shape
+    H, P, d = int(heads), len(widths) * int(subkey_dim), int(head_dim)
+    shapes = [("keys", (B, T, H, P)), ("queries", (B, T, H, P)), ("values", (B, T, H, d)), ("gin", (B, T, 2 * H)),
+              ("alpha", (B, T, H)), ("beta", (B, T, H)), ("o", (B, T, H, d))]
+    out, off = {}, 0
+    for name, shp in shapes:
+        n = 1
+        for v in shp:
+            n *= v
+        out[name] = ws[off:off + 2 * n].view(torch.bfloat16).view(shp)
+        off = (off + 2 * n + 255) // 256 * 256
+    return out
 
 
 def sdm_write_read_save(write_keys, read_queries, values, forget_gate, input_gate, subkeys, bank, *, widths,

@@ -13,6 +13,7 @@
 #include <string>
 #include <vector>
 
+#include "layer.h"
 #include "sdm_internal.h"
 
 using namespace sdm;
@@ -736,6 +737,141 @@ sdm_status sdm_decode_step(const sdm_config* cfg, const void* write_keys, const 
   a.rid = (const int32_t*)(ws + L.ridx);
   a.rwt = (const float*)(ws + L.rwt);
   TRY(hip_status(timed(SDM_K_DECODE, st, [&] { return launch_decode(D, a, st); }), "decode launch"));
+  return ok();
+}
+
+// ------------------------------------------------------------------------------------------- layer (forward)
+namespace {
+struct LayerWs {
+  size_t keys, queries, values, gin, alpha, beta, o, op, total;
+};
+sdm_status layer_layout(const sdm_layer_config* cfg, LayerWs* L) {
+  if (!cfg) return fail(SDM_ERR_NULL, "cfg must not be NULL");
+  if (cfg->reserved != 0) return fail(SDM_ERR_RANGE, "sdm_layer_config.reserved must be 0");
+  if (cfg->op.shared_bank) return fail(SDM_ERR_RANGE, "the layer does not take a shared bank");
+  size_t opws = 0;
+  TRY(sdm_workspace_size(&cfg->op, SDM_OP_WRITE_READ, 0, &opws));
+  if (cfg->op.act_dtype != SDM_BF16)
+    return fail(SDM_ERR_DTYPE, "the layer computes in bfloat16 (act_dtype must be SDM_BF16)");
+  const long long Dm = cfg->model_dim, H = cfg->op.heads, d = cfg->op.head_dim;
+  if (Dm < 32 || Dm > 65536 || Dm % 32 != 0)
+    return fail(SDM_ERR_RANGE, "model_dim = %lld must be a multiple of 32 in [32, 65536]", Dm);
+  if ((H * d) % 32 != 0) return fail(SDM_ERR_RANGE, "heads * head_dim = %lld must be a multiple of 32", H * d);
+  const long long M = (long long)cfg->op.batch * cfg->op.tokens;
+  const long long P = (long long)cfg->op.num_factors * cfg->op.subkey_dim;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t r = o;
+    o = (o + bytes + 255) & ~(size_t)255;
+    return r;
+  };
+  L->keys = take((size_t)(M * H * P * 2));
+  L->queries = take((size_t)(M * H * P * 2));
+  L->values = take((size_t)(M * H * d * 2));
+  L->gin = take((size_t)(M * 2 * H * 2));
+  L->alpha = take((size_t)(M * H * 2));
+  L->beta = take((size_t)(M * H * 2));
+  L->o = take((size_t)(M * H * d * 2));
+  L->op = take(opws);
+  L->total = o;
+  return SDM_OK;
+}
+}  // namespace
+
+sdm_status sdm_layer_workspace_size(const sdm_layer_config* cfg, size_t* bytes) {
+  if (!bytes) return fail(SDM_ERR_NULL, "bytes must not be NULL");
+  LayerWs L;
+  TRY(layer_layout(cfg, &L));
+  *bytes = L.total;
+  return ok();
+}
+
+sdm_status sdm_layer_forward(const sdm_layer_config* cfg, const void* x, const void* w_in, const float* a_log,
+                             const float* dt_bias, const void* w_out, const void* subkeys, void* bank, void* y,
+                             int32_t* write_idx, int32_t* read_idx, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  LayerWs L;
+  TRY(layer_layout(cfg, &L));
+  const sdm_config& oc = cfg->op;
+  const long long M = (long long)oc.batch * oc.tokens, H = oc.heads, d = oc.head_dim, Dm = cfg->model_dim;
+  const long long P = (long long)oc.num_factors * oc.subkey_dim;
+  const long long nin = 2 * H * P + H * d + 2 * H;
+  if (M > 0) {
+    TRY(need(x, "x"));
+    TRY(need(w_in, "w_in"));
+    TRY(need(a_log, "a_log"));
+    TRY(need(dt_bias, "dt_bias"));
+    TRY(need(w_out, "w_out"));
+    TRY(need(y, "y"));
+  }
+  if (M > 0) {
+    TRY(need(subkeys, "subkeys"));
+    TRY(need(bank, "bank"));
+  }
+  const void* al[] = {x, w_in, a_log, dt_bias, w_out, y, subkeys, bank};
+  const char* an[] = {"x", "w_in", "a_log", "dt_bias", "w_out", "y", "subkeys", "bank"};
+  for (int i = 0; i < 8; ++i) TRY(aligned(al[i], 16, an[i]));
+  TRY(check_ws(workspace, workspace_bytes, L.total));
+  // the op's own checks (bank rows, pitch, ...) run here too, before any launch: a refused call does no work
+  size_t opws = 0;
+  TRY(sdm_workspace_size(&oc, SDM_OP_WRITE_READ, 0, &opws));
+  long long sumn = 0;
+  for (int f = 0; f < oc.num_factors; ++f) sumn += oc.factor_widths[f];
+  const size_t eb = oc.bank_dtype == SDM_BF16 ? 2 : 4;
+  const long long ld = oc.bank_row_stride ? oc.bank_row_stride : d;
+  const size_t bank_bytes = (size_t)(oc.batch * H) * (size_t)oc.bank_rows * (size_t)ld * eb;
+  const Range ins[] = {{x, (size_t)(M * Dm * 2), "x"},
+                       {w_in, (size_t)(nin * Dm * 2), "w_in"},
+                       {a_log, (size_t)H * 4, "a_log"},
+                       {dt_bias, (size_t)H * 4, "dt_bias"},
+                       {w_out, (size_t)(Dm * H * d * 2), "w_out"},
+                       {subkeys, (size_t)(H * sumn * oc.subkey_dim * 2), "subkeys"}};
+  const Range outs[] = {{y, (size_t)(M * Dm * 2), "y"},
+                        {workspace, L.total, "workspace"},
+                        {bank, bank_bytes, "bank"},
+                        {write_idx, (size_t)(M * H * oc.num_writes * 4), "write_idx"},
+                        {read_idx, (size_t)(M * H * oc.num_reads * 4), "read_idx"}};
+  TRY(check_alias(outs, 5, ins, 6));
+  TRY(check_device());
+  if (M == 0 || H == 0) return ok();
+  hipStream_t st = (hipStream_t)stream;
+  unsigned char* ws = (unsigned char*)workspace;
+  bf16_t* keys = (bf16_t*)(ws + L.keys);
+  bf16_t* queries = (bf16_t*)(ws + L.queries);
+  bf16_t* values = (bf16_t*)(ws + L.values);
+  bf16_t* gin = (bf16_t*)(ws + L.gin);
+  bf16_t* alpha = (bf16_t*)(ws + L.alpha);
+  bf16_t* beta = (bf16_t*)(ws + L.beta);
+  bf16_t* o = (bf16_t*)(ws + L.o);
+  GemmArgs g;
+  memset(&g, 0, sizeof g);
+  g.x = (const bf16_t*)x;
+  g.w = (const bf16_t*)w_in;
+  g.M = (int)M;
+  g.N = (int)nin;
+  g.K = (int)Dm;
+  g.nseg = 4;
+  g.seg[0] = {(int)(H * P), keys, (int)(H * P)};
+  g.seg[1] = {(int)(2 * H * P), queries, (int)(H * P)};
+  g.seg[2] = {(int)(2 * H * P + H * d), values, (int)(H * d)};
+  g.seg[3] = {(int)nin, gin, (int)(2 * H)};
+  TRY(hip_status(timed(SDM_K_DENSE, st, [&] { return launch_gemm_bf16(g, st); }), "projection launch"));
+  TRY(hip_status(timed(SDM_K_DENSE, st, [&] {
+                   return launch_gates(gin, gin + H, (int)(2 * H), a_log, dt_bias, M * H, (int)H, alpha, beta, st);
+                 }),
+                 "gates launch"));
+  TRY(write_read_impl(&oc, keys, queries, values, alpha, beta, subkeys, bank, o, nullptr, write_idx, read_idx,
+                      ws + L.op, workspace_bytes - L.op, stream));
+  GemmArgs go;
+  memset(&go, 0, sizeof go);
+  go.x = o;
+  go.w = (const bf16_t*)w_out;
+  go.M = (int)M;
+  go.N = (int)Dm;
+  go.K = (int)(H * d);
+  go.nseg = 1;
+  go.seg[0] = {(int)Dm, (bf16_t*)y, (int)Dm};
+  TRY(hip_status(timed(SDM_K_DENSE, st, [&] { return launch_gemm_bf16(go, st); }), "output projection launch"));
   return ok();
 }
 

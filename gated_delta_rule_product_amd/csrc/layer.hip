@@ -1,0 +1,120 @@
+// The layer around the write/read op: its dense maps (projections in, output projection out) and its gates.
+//
+// Dense maps (sparse-delta-memory README.md, usage example and "Behavior changes": a layer call runs the
+// projections, the top-k and the bank copy before the op): Y = X W^T with X [M, K] and W [N, K] bfloat16,
+// row-major (the weight in out-features x in-features order), float32 accumulation on the matrix cores, the result
+// rounded to bfloat16. The output columns are split into up to GEMM_MAXSEG contiguous destinations (write keys,
+// read queries, values, gate inputs), so one launch feeds the op's separate input tensors directly.
+//
+// Gates (README "ideas": the gated delta rule of Gated DeltaNet, with FLA's A/dt parameterisation): per (token,
+// head) the forget gate alpha = exp(-exp(A_log[h]) * softplus(a + dt_bias[h])) and the input gate
+// beta = sigmoid(b), from the two gate inputs a and b of the projection, in float32, rounded to bfloat16.
+#include "layer.h"
+
+namespace sdm {
+
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short gemm_bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float gemm_f32x4_t;
+
+// One workgroup (4 waves) per 128 x 128 output tile; wave (wm, wn) computes rows 64 wm .. + 64 and columns
+// 64 wn .. + 64 as 4 x 4 MFMA tiles of 16 x 16 (v_mfma_f32_16x16x32_bf16). Operand fragments come straight from
+// global memory (16 bytes per lane: 8 consecutive K elements of one row), the next K step's fragments loaded while
+// the current step multiplies. Rows and columns past M or N load row M - 1 or N - 1 (never stored). K % 32 == 0.
+//
+// MFMA 16x16x32 bf16 lane layout: A lane l holds row l % 16, K elements 8 (l / 16) .. + 8 of the 32-wide step; B
+// lane l holds column l % 16, the same K elements; the result lane l holds column l % 16, rows 4 (l / 16) + r.
+constexpr int GEMM_NT = 256;
+__global__ __launch_bounds__(GEMM_NT) void gemm_bf16_kernel(GemmArgs g) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int m0 = blockIdx.y * 128 + (wv & 1) * 64, n0 = blockIdx.x * 128 + (wv >> 1) * 64;
+  const int ql = lane & 15, kq = (lane >> 4) * 8;
+  const bf16_t* ap[4];
+  const bf16_t* bp[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ap[i] = g.x + (long long)min(m0 + 16 * i + ql, g.M - 1) * g.K + kq;
+    bp[i] = g.w + (long long)min(n0 + 16 * i + ql, g.N - 1) * g.K + kq;
+  }
+  gemm_f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = gemm_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  gemm_bf16x8_t a[4], b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = *(const gemm_bf16x8_t*)ap[i];
+    b[i] = *(const gemm_bf16x8_t*)bp[i];
+  }
+  for (int k = 32; k <= g.K; k += 32) {
+    gemm_bf16x8_t an[4], bn[4];
+    const int kk = k < g.K ? k : 0;  // the last step reloads step 0 (in bounds, unused)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      an[i] = *(const gemm_bf16x8_t*)(ap[i] + kk);
+      bn[i] = *(const gemm_bf16x8_t*)(bp[i] + kk);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = an[i];
+      b[i] = bn[i];
+    }
+  }
+  // store: column n of the output goes to the segment whose range holds it
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = n0 + 16 * j + ql;
+    if (n >= g.N) continue;
+    int s = 0, start = 0;
+    while (n >= g.seg[s].end) {
+      start = g.seg[s].end;
+      ++s;
+    }
+    bf16_t* dst = g.seg[s].dst + (n - start);
+    const long long ld = g.seg[s].ld;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + 16 * i + 4 * (lane >> 4) + r;
+        if (m < g.M) dst[(long long)m * ld] = f_to_bf16(acc[i][j][r]);
+      }
+  }
+}
+
+hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t st) {
+  if (g.M == 0 || g.N == 0) return hipSuccess;
+  dim3 grid((unsigned)((g.N + 127) / 128), (unsigned)((g.M + 127) / 128));
+  hipLaunchKernelGGL(gemm_bf16_kernel, grid, dim3(GEMM_NT), 0, st, g);
+  return hipGetLastError();
+}
+
+// softplus(x) = log(1 + e^x), for large x equal to x in float32
+__device__ __forceinline__ float softplus_f(float x) { return x > 20.0f ? x : log1pf(expf(x)); }
+
+__global__ __launch_bounds__(256) void gates_kernel(const bf16_t* ga, const bf16_t* gb, int ldg, const float* a_log,
+                                                    const float* dt_bias, long long S, int H, bf16_t* alpha,
+                                                    bf16_t* beta) {
+  const long long s = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (s >= S) return;
+  const long long row = s / H;
+  const int h = (int)(s - row * H);
+  const float a = bf16_to_f(ga[row * ldg + h]), b = bf16_to_f(gb[row * ldg + h]);
+  const float decay = expf(a_log[h]) * softplus_f(a + dt_bias[h]);
+  alpha[s] = f_to_bf16(expf(-decay));
+  beta[s] = f_to_bf16(1.0f / (1.0f + expf(-b)));
+}
+
+hipError_t launch_gates(const bf16_t* ga, const bf16_t* gb, int ldg, const float* a_log, const float* dt_bias,
+                        long long S, int H, bf16_t* alpha, bf16_t* beta, hipStream_t st) {
+  if (S == 0) return hipSuccess;
+  hipLaunchKernelGGL(gates_kernel, dim3((unsigned)((S + 255) / 256)), dim3(256), 0, st, ga, gb, ldg, a_log, dt_bias,
+                     S, H, alpha, beta);
+  return hipGetLastError();
+}
+
+}  // namespace sdm

@@ -173,6 +173,37 @@ sdm_status sdm_decode_step(const sdm_config* cfg, const void* write_keys, const 
                            const void* bank_in, void* bank_out, void* out, int32_t* write_idx, int32_t* read_idx,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* The layer around the op (README usage example: SparseDeltaMemoryArgs(dim, num_heads, slots_per_head, num_writes,
+ * num_reads, chunk_size); CHANGELOG 2.0.0, "Behavior changes": a layer call runs the projections, the top-k and the
+ * bank copy, then the op; README "ideas": gates of Gated DeltaNet with FLA's A/dt parameterisation). Forward only.
+ * With M = B * T rows, Dm = model_dim, P = F * dk and cfg.op the write/read settings:
+ *   [keys | queries | values | a | b] = x w_in^T          x [B, T, Dm], w_in [2 H P + H d + 2 H, Dm]: rows
+ *                                                         [0, H P) write keys (head-major, [H, P] per token), then
+ *                                                         H P read queries, H d values, H forget inputs a, H input
+ *                                                         inputs b
+ *   alpha = exp(-exp(a_log[h]) * softplus(a + dt_bias[h])),  beta = sigmoid(b)       (float32, rounded to bf16)
+ *   o = the write/read op (sdm_write_read) on keys, queries, values, alpha, beta, subkeys and bank
+ *   y = o w_out^T                                         o [B, T, H d], w_out [Dm, H d], y [B, T, Dm]
+ * Dense maps accumulate in float32 on the matrix cores and round to bfloat16. x, w_in, w_out, subkeys and y are
+ * bfloat16 (cfg.op.act_dtype must be SDM_BF16, else SDM_ERR_DTYPE); a_log and dt_bias are float32 [H]. The bank
+ * advances in place like sdm_write_read's (shared_bank not allowed). Dm and H * d must be multiples of 32 (the
+ * matrix-core step), Dm <= 65536, and every buffer 16-byte aligned (SDM_ERR_RANGE / SDM_ERR_LAYOUT). write_idx /
+ * read_idx as in sdm_write_read. The workspace (sdm_layer_workspace_size) holds, in this order and each region
+ * starting at a 256-byte multiple: keys [B, T, H, P], queries [B, T, H, P], values [B, T, H, d], gate inputs
+ * [B, T, 2 H] (a then b), alpha [B, T, H], beta [B, T, H], o [B, T, H, d] (all bfloat16; left there by the call),
+ * then the op's own workspace. */
+typedef struct {
+  sdm_config op;      /* write/read settings of the op inside the layer */
+  int32_t model_dim;  /* Dm, the width of x and y */
+  int32_t reserved;   /* 0 */
+} sdm_layer_config;
+
+sdm_status sdm_layer_workspace_size(const sdm_layer_config* cfg, size_t* bytes);
+sdm_status sdm_layer_forward(const sdm_layer_config* cfg, const void* x, const void* w_in, const float* a_log,
+                             const float* dt_bias, const void* w_out, const void* subkeys, void* bank, void* y,
+                             int32_t* write_idx, int32_t* read_idx, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
 /* Kernel timing (diagnostics, not part of the method). While enabled, every kernel launch of this library is
  * bracketed by a pair of HIP events recorded on the call's stream. sdm_profile_read waits for the recorded events
  * and returns, per kernel family, the summed milliseconds (ms) and the number of launches (launches) since timing
@@ -186,7 +217,8 @@ typedef enum {
   SDM_K_DECODE = 4, /* decode step */
   SDM_K_COPY = 5,   /* successor copy */
   SDM_K_BWD = 6,    /* backward: reverse sweep, token sums, sub-key sums */
-  SDM_K_COUNT = 7
+  SDM_K_DENSE = 7,  /* layer: dense maps (projections, output projection) and gates */
+  SDM_K_COUNT = 8
 } sdm_kernel;
 sdm_status sdm_profile_enable(int32_t on);
 sdm_status sdm_profile_read(double* ms, int64_t* launches);

@@ -208,3 +208,56 @@ def test_save_and_backward_refuse_before_device_work(lib):
     q[12] = q[2]  # grad_values = values
     assert lib.sdm_write_read_backward(ctypes.byref(cfg), *q, ws, nb.value, None) == B.SDM_ERR_ALIAS
     assert lib.sdm_write_read_backward(ctypes.byref(cfg), *g, ws, nb.value - 1, None) == B.SDM_ERR_WORKSPACE
+
+
+def _layer_cfg(model_dim=256, **kw):
+    base = dict(act_dtype=B.SDM_BF16)
+    base.update(kw)
+    lc = B.SdmLayerConfig()
+    lc.op = _cfg(**base)
+    lc.model_dim = model_dim
+    return lc
+
+
+def _layer_ws(lc):
+    n = ctypes.c_size_t(0)
+    return B.load().sdm_layer_workspace_size(ctypes.byref(lc), ctypes.byref(n)), n.value
+
+
+def test_layer_settings_and_refusals(lib):
+    s, n = _layer_ws(_layer_cfg())
+    assert s == B.SDM_OK
+    op_s, op_n = _status(_layer_cfg().op)
+    assert op_s == B.SDM_OK and n > op_n  # the projections, gates and o come before the op's workspace
+    assert _layer_ws(_layer_cfg(act_dtype=B.SDM_F32))[0] == B.SDM_ERR_DTYPE
+    assert _layer_ws(_layer_cfg(model_dim=48))[0] == B.SDM_ERR_RANGE
+    assert _layer_ws(_layer_cfg(model_dim=0))[0] == B.SDM_ERR_RANGE
+    assert _layer_ws(_layer_cfg(shared_bank=True))[0] == B.SDM_ERR_RANGE
+    assert _layer_ws(_layer_cfg(head_dim=72, heads=1))[0] == B.SDM_ERR_RANGE  # H d = 72: not a multiple of 32
+    lc = _layer_cfg()
+    lc.reserved = 1
+    assert _layer_ws(lc)[0] == B.SDM_ERR_RANGE
+    assert _layer_ws(_layer_cfg(widths=(32, 32), bank_rows=100))[0] == B.SDM_ERR_BANK_TOO_SMALL
+
+
+def test_layer_refuses_before_device_work(lib):
+    lc = _layer_cfg()
+    s, n = _layer_ws(lc)
+    assert s == B.SDM_OK
+    base = 1 << 40  # fake, never dereferenced: every check below fails before any HIP call
+    step = 1 << 32
+    p = [_fake(base + i * step) for i in range(11)]  # x w_in a_log dt_bias w_out subkeys bank y widx ridx ws
+    call = lambda q, wsn=n: lib.sdm_layer_forward(ctypes.byref(lc), *q[:10], q[10], wsn, None)
+    q = list(p)
+    q[6] = None  # bank
+    assert call(q) == B.SDM_ERR_NULL
+    q = list(p)
+    q[7] = _fake(base + 6 * step + 64)  # y inside the bank
+    assert call(q) == B.SDM_ERR_ALIAS
+    q = list(p)
+    q[8] = p[0]  # write ids over x
+    assert call(q) == B.SDM_ERR_ALIAS
+    q = list(p)
+    q[5] = _fake(base + 5 * step + 8)  # misaligned sub-keys
+    assert call(q) == B.SDM_ERR_LAYOUT
+    assert call(list(p), n - 1) == B.SDM_ERR_WORKSPACE
