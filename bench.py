@@ -265,6 +265,55 @@ def bench_other(args, torch, binding, synth):
     return res
 
 
+def bench_layer(args, torch, binding, synth):
+    """The layer's forward at the layer_65k op shapes and model width 2048 (x [2, 4096, 2048] bf16): input map,
+    gates, the op, output map. Context line (tokens/s of the whole layer; the dense maps' MFMA roofline)."""
+    s = synth.WORKLOADS["layer_65k"]
+    Dm = 2048
+    dev = torch.device("cuda:0")
+    log("[bench] layer: inputs")
+    x = synth.make_layer_inputs(s, Dm)
+    t = {k: torch.from_numpy(x[k]).to(dev).to(torch.bfloat16) for k in ("x", "w_in", "w_out", "subkeys")}
+    g = {k: torch.from_numpy(x[k]).to(dev) for k in ("a_log", "dt_bias")}
+    pitch = binding.bank_pitch(s.head_dim, torch.float32)
+    bank = binding.alloc_bank(s.batch, s.heads, s.rows, s.head_dim, torch.float32, dev, pitch=pitch)
+    bank.copy_(torch.from_numpy(x["bank"]).to(dev))
+    del x
+    kw = dict(heads=s.heads, widths=s.widths, num_writes=s.num_writes, num_reads=s.num_reads,
+              chunk_size=s.chunk_size)
+    y, _, _, ws = binding.sdm_layer_forward(t["x"], t["w_in"], g["a_log"], g["dt_bias"], t["w_out"], t["subkeys"],
+                                            bank, return_workspace=True, **kw)
+    torch.cuda.synchronize()
+    n = max(1, args.other_steps)
+    binding.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(n):
+        binding.sdm_layer_forward(t["x"], t["w_in"], g["a_log"], g["dt_bias"], t["w_out"], t["subkeys"], bank,
+                                  y=y, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    prof = binding.profile_read()
+    binding.profile_enable(False)
+    ms = (t1 - t0) * 1e3 / n
+    M = s.batch * s.tokens
+    n_in = binding.layer_in_features(s.heads, s.widths, s.subkey_dim, s.head_dim)
+    flops = 2 * M * Dm * n_in + 2 * M * s.heads * s.head_dim * Dm
+    dense_ms = prof["dense"][0] / n  # both dense maps and the gates, per call
+    res = {"tokens_per_s": round(M / (ms * 1e-3), 1), "ms_per_step": round(ms, 4), "steps": n,
+           "kernels_ms_per_call": {k: round(v[0] / n, 4) for k, v in prof.items() if v[1]},
+           "dense_mfma": {"kernel": "gemm_bf16_kernel (input and output maps) + gates_kernel", "bound": "mfma",
+                          "flops_per_call": flops, "achieved": round(flops / (dense_ms * 1e-3) / 1e12, 1),
+                          "peak": 2500.0, "unit": "TFLOP/s",
+                          "frac": round(flops / (dense_ms * 1e-3) / 1e12 / 2500.0, 4),
+                          "ms_per_call": round(dense_ms, 4)},
+           "config": f"x [{s.batch}, {s.tokens}, {Dm}] bf16, w_in [{n_in}, {Dm}], w_out [{Dm}, "
+                     f"{s.heads * s.head_dim}], op as layer_65k (f32 bank)"}
+    log(f"[bench] layer: {res['tokens_per_s']} tokens/s, dense {dense_ms:.3f} ms per call")
+    del bank, ws, y, t, g
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_decode(args, torch, binding, synth):
     s = synth.WORKLOADS["decode_b128"]
     dev = torch.device("cuda:0")
@@ -438,6 +487,7 @@ def main():
     dec = bench_decode(args, torch, binding, synth)
     train = bench_train(args, torch, binding, synth) if args.train else None
     other = bench_other(args, torch, binding, synth) if args.other_steps > 0 else None
+    layer = bench_layer(args, torch, binding, synth) if args.other_steps > 0 else None
     s = wr["shape"]
     line = {
         "metric": METRIC, "value": round(wr["tokens_per_s"], 1), "unit": "tokens/s", "n_gpus": 1,
@@ -456,6 +506,7 @@ def main():
         "decode": dec,
         "train": train,
         "other_workloads": other,
+        "layer": layer,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args, s, synth)

@@ -13,7 +13,7 @@
 
 namespace sdm {
 
-typedef __attribute__((__vector_size__(8 * sizeof(short)))) short gemm_bf16x8_t;
+typedef __bf16 gemm_bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float gemm_f32x4_t;
 
 // One workgroup (4 waves) per 128 x 128 output tile; wave (wm, wn) computes rows 64 wm .. + 64 and columns
@@ -43,16 +43,16 @@ __global__ __launch_bounds__(GEMM_NT) void gemm_bf16_kernel(GemmArgs g) {
   gemm_bf16x8_t a[4], b[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    a[i] = *(const gemm_bf16x8_t*)ap[i];
-    b[i] = *(const gemm_bf16x8_t*)bp[i];
+    a[i] = __builtin_bit_cast(gemm_bf16x8_t, *(const uint4*)ap[i]);
+    b[i] = __builtin_bit_cast(gemm_bf16x8_t, *(const uint4*)bp[i]);
   }
   for (int k = 32; k <= g.K; k += 32) {
     gemm_bf16x8_t an[4], bn[4];
     const int kk = k < g.K ? k : 0;  // the last step reloads step 0 (in bounds, unused)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      an[i] = *(const gemm_bf16x8_t*)(ap[i] + kk);
-      bn[i] = *(const gemm_bf16x8_t*)(bp[i] + kk);
+      an[i] = __builtin_bit_cast(gemm_bf16x8_t, *(const uint4*)(ap[i] + kk));
+      bn[i] = __builtin_bit_cast(gemm_bf16x8_t, *(const uint4*)(bp[i] + kk));
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
