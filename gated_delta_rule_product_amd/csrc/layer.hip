@@ -23,6 +23,35 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float gemm_f32x4_t;
 //
 // MFMA 16x16x32 bf16 lane layout: A lane l holds row l % 16, K elements 8 (l / 16) .. + 8 of the 32-wide step; B
 // lane l holds column l % 16, the same K elements; the result lane l holds column l % 16, rows 4 (l / 16) + r.
+// The epilogue shared by both dense-map kernels: acc[i][j][r] is the element at row m0 + 16 i + 4 (lane / 16) + r,
+// column n0 + 16 j + lane % 16; column n goes to the segment whose range holds it.
+__device__ __forceinline__ void gemm_store(const GemmArgs& g, const gemm_f32x4_t (&acc)[4][4], int m0, int n0,
+                                           int lane) {
+  const int ql = lane & 15;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = n0 + 16 * j + ql;
+    if (n >= g.N) continue;
+    // the segment holding column n, picked with constant indices (a runtime index into the argument's array
+    // would copy it to scratch memory)
+    bf16_t* dst = g.seg[0].dst + n;
+    long long ld = g.seg[0].ld;
+#pragma unroll
+    for (int q = 1; q < GEMM_MAXSEG; ++q)
+      if (q < g.nseg && n >= g.seg[q - 1].end) {
+        dst = g.seg[q].dst + (n - g.seg[q - 1].end);
+        ld = g.seg[q].ld;
+      }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + 16 * i + 4 * (lane >> 4) + r;
+        if (m < g.M) dst[(long long)m * ld] = f_to_bf16(acc[i][j][r]);
+      }
+  }
+}
+
 constexpr int GEMM_NT = 256;
 __global__ __launch_bounds__(GEMM_NT) void gemm_bf16_kernel(GemmArgs g) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -64,32 +93,89 @@ __global__ __launch_bounds__(GEMM_NT) void gemm_bf16_kernel(GemmArgs g) {
       b[i] = bn[i];
     }
   }
-  // store: column n of the output goes to the segment whose range holds it
+  gemm_store(g, acc, m0, n0, lane);
+}
+
+// LDS-tiled dense map (K % 64 == 0): one workgroup per 128 x 128 output tile, K in steps of 64. Each step the
+// 256 threads copy the A and B tiles (128 rows x 64 K elements each, 16 bytes per thread and load, 8 threads per
+// 128-byte row segment) from registers into LDS, then issue the next step's global loads into registers and run
+// the step's MFMAs from LDS (wave (wm, wn): rows 64 wm .., columns 64 wn .., 4 x 4 tiles of 16 x 16, two 32-wide K
+// halves). LDS rows are 72 elements apart (144 bytes), which spreads a fragment read's 16 rows over all banks.
+// Rows past M or N load row M - 1 or N - 1 and are never stored. Workgroups map to tiles so that the tiles on one
+// XCD (workgroup id mod 8) are consecutive in row-major tile order, so they share A rows in that XCD's L2.
+constexpr int GT_LD = 72;
+__global__ __launch_bounds__(GEMM_NT) void gemm_bf16_lds_kernel(GemmArgs g) {
+  __shared__ __align__(16) bf16_t As[128 * GT_LD];
+  __shared__ __align__(16) bf16_t Bs[128 * GT_LD];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int ntn = gridDim.x, total = gridDim.x * gridDim.y;
+  int tile = blockIdx.x + ntn * blockIdx.y;
+  if (total % 8 == 0) tile = (tile % 8) * (total / 8) + tile / 8;
+  const int bm = (tile / ntn) * 128, bn = (tile % ntn) * 128;
+  // this thread's 4 copy chunks per operand: chunk c = tid + 256 u -> row c / 8, K piece (c % 8) * 8
+  const bf16_t* ag[4];
+  const bf16_t* bg[4];
+  int lds_off[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int n = n0 + 16 * j + ql;
-    if (n >= g.N) continue;
-    int s = 0, start = 0;
-    while (n >= g.seg[s].end) {
-      start = g.seg[s].end;
-      ++s;
-    }
-    bf16_t* dst = g.seg[s].dst + (n - start);
-    const long long ld = g.seg[s].ld;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + 16 * i + 4 * (lane >> 4) + r;
-        if (m < g.M) dst[(long long)m * ld] = f_to_bf16(acc[i][j][r]);
-      }
+  for (int u = 0; u < 4; ++u) {
+    const int c = tid + 256 * u, row = c >> 3, kp = (c & 7) * 8;
+    ag[u] = g.x + (long long)min(bm + row, g.M - 1) * g.K + kp;
+    bg[u] = g.w + (long long)min(bn + row, g.N - 1) * g.K + kp;
+    lds_off[u] = row * GT_LD + kp;
   }
+  gemm_bf16x8_t ar[4], br[4];  // native vectors: a union-based uint4 array carried across steps lands in scratch
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    ar[u] = *(const gemm_bf16x8_t*)ag[u];
+    br[u] = *(const gemm_bf16x8_t*)bg[u];
+  }
+  gemm_f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = gemm_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  const int wm = (wv & 1) * 64, wn = (wv >> 1) * 64;
+  const int ql = lane & 15, kq = (lane >> 4) * 8;
+  for (int k0 = 0; k0 < g.K; k0 += 64) {
+    __syncthreads();  // the previous step's fragment reads are done
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      *(gemm_bf16x8_t*)&As[lds_off[u]] = ar[u];
+      *(gemm_bf16x8_t*)&Bs[lds_off[u]] = br[u];
+    }
+    __syncthreads();
+    const int kn = k0 + 64 < g.K ? k0 + 64 : k0;  // the last step reloads its own tile (in bounds, unused)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      ar[u] = *(const gemm_bf16x8_t*)(ag[u] + kn);
+      br[u] = *(const gemm_bf16x8_t*)(bg[u] + kn);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // the next step's loads go out before this step's MFMAs
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      gemm_bf16x8_t a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = *(const gemm_bf16x8_t*)&As[(wm + 16 * i + ql) * GT_LD + 32 * h + kq];
+        b[i] = *(const gemm_bf16x8_t*)&Bs[(wn + 16 * i + ql) * GT_LD + 32 * h + kq];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  }
+  gemm_store(g, acc, bm + wm, bn + wn, lane);
 }
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t st) {
   if (g.M == 0 || g.N == 0) return hipSuccess;
   dim3 grid((unsigned)((g.N + 127) / 128), (unsigned)((g.M + 127) / 128));
-  hipLaunchKernelGGL(gemm_bf16_kernel, grid, dim3(GEMM_NT), 0, st, g);
+  if (g.K % 64 == 0)
+    hipLaunchKernelGGL(gemm_bf16_lds_kernel, grid, dim3(GEMM_NT), 0, st, g);
+  else
+    hipLaunchKernelGGL(gemm_bf16_kernel, grid, dim3(GEMM_NT), 0, st, g);
   return hipGetLastError();
 }
 
