@@ -13,6 +13,7 @@
 #include <string>
 #include <vector>
 
+#include "bwd_shape.h"
 #include "layer.h"
 #include "sdm_internal.h"
 
@@ -223,7 +224,7 @@ WsLayout layout(const Dims& D, int op) {
     L.wwt = take(nw * 4);
     L.ridx = take(nr * 4);
     L.rwt = take(nr * 4);
-    L.part = take((size_t)bwd_slices(D) * D.S * D.T * (D.W + D.R + 2) * 4);
+    L.part = take((size_t)bwd_nsl(D) * D.S * D.T * (D.W + D.R + 2) * 4);
     L.ds = take((size_t)D.S * D.T * (D.W + D.R) * 4);
     L.sgpart = take((size_t)bwd_row_blocks(D) * D.H * sumn * D.dk * 4);
     L.mrho = take(nw * 4);

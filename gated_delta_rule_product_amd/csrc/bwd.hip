@@ -16,6 +16,7 @@
 // P_i (the row of S_i before the token's write) is the forward's snapshot. G, M and D are column-local, so one
 // workgroup runs one (stream, 16-column slice) over every token; only the dot products cross slices: each slice
 // writes its partial sums and a second kernel adds them over the slices in order. Every sum has a fixed order.
+#include "bwd_shape.h"
 #include "sdm_internal.h"
 
 namespace sdm {
@@ -65,6 +66,11 @@ template <> struct Word<bf16_t> {
 __device__ __forceinline__ float sum4_lanes(float x) {  // over the 4 lanes of a group; equal on all four
   x += __shfl_xor(x, 1);
   x += __shfl_xor(x, 2);
+  return x;
+}
+template <int L> __device__ __forceinline__ float sum_group_lanes(float x) {  // over the L lanes of a group
+#pragma unroll
+  for (int o = 1; o < L; o <<= 1) x += __shfl_xor(x, o);
   return x;
 }
 
@@ -257,11 +263,13 @@ __global__ __launch_bounds__(64) void bwd_match_kernel(Dims D, BwdArgs a) {
 // token also writes that slot (the write's G row includes it). The loads of token t - 1's rows
 // follow the end-of-token barrier, after every store of token t in the workgroup's program order (one CU: its
 // vector memory pipeline keeps that order).
-template <typename A, typename Bk>
-__global__ __launch_bounds__(BWD_NT) void bwd_sweep_fast_kernel(Dims D, BwdArgs a, int nsl) {
-  __shared__ __align__(16) float sRedD[8][BWD_COLS];
-  __shared__ __align__(16) float sRedR[8][BWD_COLS];
-  __shared__ float sRedGP[8];
+// LPG lanes per term group (4 columns each): slices of 4 LPG columns, 128 groups, 128 LPG threads (2 LPG waves).
+template <typename A, typename Bk, int LPG>
+__global__ __launch_bounds__(128 * LPG) void bwd_sweep_fast_kernel(Dims D, BwdArgs a, int nsl) {
+  constexpr int COLS = 4 * LPG, NW = 2 * LPG;
+  __shared__ __align__(16) float sRedD[NW][COLS];
+  __shared__ __align__(16) float sRedR[NW][COLS];
+  __shared__ float sRedGP[NW];
   typedef typename Raw4<Bk>::T RawT;
   typedef typename Raw4<A>::T ARaw;
   const int W = D.W, R = D.R, T = D.T, d = D.d;
@@ -270,8 +278,8 @@ __global__ __launch_bounds__(BWD_NT) void bwd_sweep_fast_kernel(Dims D, BwdArgs 
   if ((nblk & 7) == 0) wk = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
   const int st = wk / nsl, slice = wk % nsl;
   const int b = st / D.H, h = st % D.H;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, grp = tid >> 2, q = tid & 3;
-  const int col = slice * BWD_COLS + q * 4;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, grp = tid / LPG, q = tid % LPG;
+  const int col = slice * COLS + q * 4;
   const bool valid = col < d;
   const bool hasR = grp < R, hasW = grp < W;
   const int jr = min(grp, R - 1), jw = min(grp, W - 1);  // clamped term indices: every lane loads in range
@@ -343,7 +351,7 @@ __global__ __launch_bounds__(BWD_NT) void bwd_sweep_fast_kernel(Dims D, BwdArgs 
     // the read: d rho partial, G[R_j] += rho_j dout (stored at the end of the token)
     float m[4];
     Raw4<Bk>::unpack(rb, m);
-    const float rdot = sum4_lanes(((dout[0] * m[0] + dout[1] * m[1]) + dout[2] * m[2]) + dout[3] * m[3]);
+    const float rdot = sum_group_lanes<LPG>(((dout[0] * m[0] + dout[1] * m[1]) + dout[2] * m[2]) + dout[3] * m[3]);
     rg.x += rho * dout[0]; rg.y += rho * dout[1]; rg.z += rho * dout[2]; rg.w += rho * dout[3];
     // the write: g_i (plus this token's read update of the same slot), P_i
     float g[4] = {wg.x + mr * dout[0], wg.y + mr * dout[1], wg.z + mr * dout[2], wg.w + mr * dout[3]}, pp[4];
@@ -360,9 +368,9 @@ __global__ __launch_bounds__(BWD_NT) void bwd_sweep_fast_kernel(Dims D, BwdArgs 
       cD[k] = hasW ? w * g[k] : 0.f;
       cR[k] = hasW ? w * pp[k] : 0.f;
     }
-    float gp = hasW ? sum4_lanes(((g[0] * pp[0] + g[1] * pp[1]) + g[2] * pp[2]) + g[3] * pp[3]) : 0.f;
+    float gp = hasW ? sum_group_lanes<LPG>(((g[0] * pp[0] + g[1] * pp[1]) + g[2] * pp[2]) + g[3] * pp[3]) : 0.f;
 #pragma unroll
-    for (int o = 4; o <= 32; o <<= 1) {  // over the 16 groups of the wave (fixed tree; lanes 0..3 keep the sum)
+    for (int o = LPG; o <= 32; o <<= 1) {  // over the groups of the wave (fixed tree; lanes 0..LPG-1 keep the sum)
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         cD[k] += __shfl_xor(cD[k], o);
@@ -370,16 +378,16 @@ __global__ __launch_bounds__(BWD_NT) void bwd_sweep_fast_kernel(Dims D, BwdArgs 
       }
       gp += __shfl_xor(gp, o);
     }
-    if (lane < 4) {
+    if (lane < LPG) {
       *(float4*)&sRedD[wv][lane * 4] = make_float4(cD[0], cD[1], cD[2], cD[3]);
       *(float4*)&sRedR[wv][lane * 4] = make_float4(cR[0], cR[1], cR[2], cR[3]);
       if (lane == 0) sRedGP[wv] = gp;
     }
     __syncthreads();
-    // D, r and delta of this lane's four columns (the 8 wave partials in order, on every lane alike)
+    // D, r and delta of this lane's four columns (the NW wave partials in order, on every lane alike)
     float Dl[4] = {0.f, 0.f, 0.f, 0.f}, r[4] = {0.f, 0.f, 0.f, 0.f}, dl[4];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < NW; ++k) {
       const float4 x = *(const float4*)&sRedD[k][q * 4];
       const float4 y = *(const float4*)&sRedR[k][q * 4];
       Dl[0] += x.x; Dl[1] += x.y; Dl[2] += x.z; Dl[3] += x.w;
@@ -391,15 +399,15 @@ __global__ __launch_bounds__(BWD_NT) void bwd_sweep_fast_kernel(Dims D, BwdArgs 
       e[k] = v[k] - al * r[k];  // v - alpha r
       dl[k] = be * e[k];
     }
-    if (grp == 0) {  // dv, and the slice partials of d alpha and d beta (4 lanes x 4 columns)
+    if (grp == 0) {  // dv, and the slice partials of d alpha and d beta (LPG lanes x 4 columns)
       if (valid)
         *(float4*)(a.gvalues + row * d + col) = make_float4(be * Dl[0], be * Dl[1], be * Dl[2], be * Dl[3]);
-      const float db = sum4_lanes(((Dl[0] * e[0] + Dl[1] * e[1]) + Dl[2] * e[2]) + Dl[3] * e[3]);
-      const float rd = sum4_lanes(((Dl[0] * r[0] + Dl[1] * r[1]) + Dl[2] * r[2]) + Dl[3] * r[3]);
+      const float db = sum_group_lanes<LPG>(((Dl[0] * e[0] + Dl[1] * e[1]) + Dl[2] * e[2]) + Dl[3] * e[3]);
+      const float rd = sum_group_lanes<LPG>(((Dl[0] * r[0] + Dl[1] * r[1]) + Dl[2] * r[2]) + Dl[3] * r[3]);
       if (q == 0) {
         float gps = 0.f;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) gps += sRedGP[k];
+        for (int k = 0; k < NW; ++k) gps += sRedGP[k];
         part[W + R] = gps - be * rd;
         part[W + R + 1] = db;
       }
@@ -412,8 +420,8 @@ __global__ __launch_bounds__(BWD_NT) void bwd_sweep_fast_kernel(Dims D, BwdArgs 
     // d w partials, G[S_i] <- alpha g_i - alpha beta w_i D, M[S_i] <- P_i
     if (hasW) {
       const float ab = al * be;
-      const float gd = sum4_lanes(((g[0] * dl[0] + g[1] * dl[1]) + g[2] * dl[2]) + g[3] * dl[3]);
-      const float Dp = sum4_lanes(((Dl[0] * pp[0] + Dl[1] * pp[1]) + Dl[2] * pp[2]) + Dl[3] * pp[3]);
+      const float gd = sum_group_lanes<LPG>(((g[0] * dl[0] + g[1] * dl[1]) + g[2] * dl[2]) + g[3] * dl[3]);
+      const float Dp = sum_group_lanes<LPG>(((Dl[0] * pp[0] + Dl[1] * pp[1]) + Dl[2] * pp[2]) + Dl[3] * pp[3]);
       if (q == 0) part[grp] = gd - ab * Dp;
       if (valid) {
         const float cw = ab * w;
@@ -561,11 +569,15 @@ __global__ __launch_bounds__(256) void bwd_subkey_sum_kernel(const float* __rest
 
 template <typename A, typename Bk>
 static hipError_t launch_bwd_t(const Dims& D, const BwdArgs& a, hipStream_t st) {
-  const int nsl = bwd_slices(D);
-  if (D.W <= BWD_NT / 4 && D.R <= BWD_NT / 4) {
+  const int nsl = bwd_nsl(D);
+  if (bwd_fast(D)) {
     hipLaunchKernelGGL(bwd_match_kernel, dim3((unsigned)((long long)D.S * D.T)), dim3(64), 0, st, D, a);
-    hipLaunchKernelGGL((bwd_sweep_fast_kernel<A, Bk>), dim3((unsigned)((long long)D.S * nsl)), dim3(BWD_NT), 0, st, D,
-                       a, nsl);
+    if (bwd_cols(D) == 8)
+      hipLaunchKernelGGL((bwd_sweep_fast_kernel<A, Bk, 2>), dim3((unsigned)((long long)D.S * nsl)), dim3(256), 0, st,
+                         D, a, nsl);
+    else
+      hipLaunchKernelGGL((bwd_sweep_fast_kernel<A, Bk, 4>), dim3((unsigned)((long long)D.S * nsl)), dim3(512), 0, st,
+                         D, a, nsl);
   } else {
     const size_t lds = bwd_sweep_lds(D.W);
     (void)hipFuncSetAttribute((const void*)bwd_sweep_kernel<A, Bk>, hipFuncAttributeMaxDynamicSharedMemorySize,

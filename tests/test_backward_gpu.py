@@ -129,6 +129,9 @@ CASES = [
     # held-row loop with more slots written several times per chunk than its LDS keeps (~300 of 512 slots): the
     # events of those slots are applied, and their snapshot rows stored, from the plan region
     ("held_many_multi", synth.Shape(1, 96, 1, (16, 32), 8, 32, 32, 32, 32, name="multi"), True),
+    # enough streams x 16-column slices (32 x 16 = 512) that the sweep keeps 16-column slices; the shapes above take
+    # 8-column slices (two token chains per CU)
+    ("slices16", synth.Shape(8, 24, 4, (16, 16), 8, 256, 16, 12, 8, name="s16"), True),
 ]
 
 
