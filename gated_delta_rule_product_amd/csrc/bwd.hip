@@ -68,9 +68,26 @@ __device__ __forceinline__ float sum4_lanes(float x) {  // over the 4 lanes of a
   x += __shfl_xor(x, 2);
   return x;
 }
+// DPP lane moves (VALU, no LDS round trip): within quads (quad_perm) and rotations within rows of 16 lanes.
+template <int CTRL> __device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int DPP_QUAD_XOR1 = 0xB1, DPP_QUAD_XOR2 = 0x4E, DPP_ROW_ROR4 = 0x124, DPP_ROW_ROR8 = 0x128;
+
 template <int L> __device__ __forceinline__ float sum_group_lanes(float x) {  // over the L lanes of a group
-#pragma unroll
-  for (int o = 1; o < L; o <<= 1) x += __shfl_xor(x, o);
+  if (L >= 2) x += dpp_f<DPP_QUAD_XOR1>(x);
+  if (L >= 4) x += dpp_f<DPP_QUAD_XOR2>(x);
+  return x;
+}
+
+// Over the groups of a wave, per column quad: the sum of the lanes with this lane's index mod L (L = 2 or 4 lanes
+// per group), in a fixed order; every lane ends with its class's sum.
+template <int L> __device__ __forceinline__ float sum_wave_groups(float x) {
+  if (L == 2) x += dpp_f<DPP_QUAD_XOR2>(x);  // the other group of the quad
+  x += dpp_f<DPP_ROW_ROR4>(x);               // the row's other quads
+  x += dpp_f<DPP_ROW_ROR8>(x);
+  x += __shfl_xor(x, 16);                    // the other rows
+  x += __shfl_xor(x, 32);
   return x;
 }
 
@@ -370,14 +387,11 @@ __global__ __launch_bounds__(128 * LPG) void bwd_sweep_fast_kernel(Dims D, BwdAr
     }
     float gp = hasW ? sum_group_lanes<LPG>(((g[0] * pp[0] + g[1] * pp[1]) + g[2] * pp[2]) + g[3] * pp[3]) : 0.f;
 #pragma unroll
-    for (int o = LPG; o <= 32; o <<= 1) {  // over the groups of the wave (fixed tree; lanes 0..LPG-1 keep the sum)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        cD[k] += __shfl_xor(cD[k], o);
-        cR[k] += __shfl_xor(cR[k], o);
-      }
-      gp += __shfl_xor(gp, o);
+    for (int k = 0; k < 4; ++k) {  // over the groups of the wave (fixed order; lanes 0..LPG-1 are used)
+      cD[k] = sum_wave_groups<LPG>(cD[k]);
+      cR[k] = sum_wave_groups<LPG>(cR[k]);
     }
+    gp = sum_wave_groups<LPG>(gp);
     if (lane < LPG) {
       *(float4*)&sRedD[wv][lane * 4] = make_float4(cD[0], cD[1], cD[2], cD[3]);
       *(float4*)&sRedR[wv][lane * 4] = make_float4(cR[0], cR[1], cR[2], cR[3]);
