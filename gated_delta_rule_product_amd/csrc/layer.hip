@@ -96,17 +96,20 @@ __global__ __launch_bounds__(GEMM_NT) void gemm_bf16_kernel(GemmArgs g) {
   gemm_store(g, acc, m0, n0, lane);
 }
 
-// LDS-tiled dense map (K % 64 == 0): one workgroup per 128 x 128 output tile, K in steps of 64. Each step the
-// 256 threads copy the A and B tiles (128 rows x 64 K elements each, 16 bytes per thread and load, 8 threads per
-// 128-byte row segment) from registers into LDS, then issue the next step's global loads into registers and run
-// the step's MFMAs from LDS (wave (wm, wn): rows 64 wm .., columns 64 wn .., 4 x 4 tiles of 16 x 16, two 32-wide K
-// halves). LDS rows are 72 elements apart (144 bytes), which spreads a fragment read's 16 rows over all banks.
-// Rows past M or N load row M - 1 or N - 1 and are never stored. Workgroups map to tiles so that the tiles on one
-// XCD (workgroup id mod 8) are consecutive in row-major tile order, so they share A rows in that XCD's L2.
+// LDS-tiled dense map (K % 64 == 0): one workgroup per 128 x 128 output tile, K in steps of 64, two LDS buffers.
+// Step k multiplies buffer k % 2 while the tile of step k + 1, loaded from global memory into registers during step
+// k - 1, is written into the other buffer, and the loads of step k + 2 are issued; one barrier per step separates a
+// buffer's reads from its next writes. Tiles: 128 rows x 64 K elements of A and of B, 16 bytes per thread and load
+// (8 threads per 128-byte row segment); wave (wm, wn) owns rows 64 wm .., columns 64 wn .. as 4 x 4 MFMA tiles of
+// 16 x 16, two 32-wide K halves per step. LDS rows are 72 elements apart (144 bytes), which spreads a fragment
+// read's 16 rows over all banks. Rows past M or N load row M - 1 or N - 1 and are never stored. Workgroups map to
+// tiles so that the tiles on one XCD (workgroup id mod 8) are consecutive in row-major tile order, sharing A rows
+// in that XCD's L2.
 constexpr int GT_LD = 72;
+constexpr int GT_BUF = 128 * GT_LD;  // elements of one operand tile
+constexpr size_t GEMM_LDS = (size_t)4 * GT_BUF * sizeof(bf16_t);  // A and B, two buffers each: 73,728 bytes
 __global__ __launch_bounds__(GEMM_NT) void gemm_bf16_lds_kernel(GemmArgs g) {
-  __shared__ __align__(16) bf16_t As[128 * GT_LD];
-  __shared__ __align__(16) bf16_t Bs[128 * GT_LD];
+  extern __shared__ __align__(16) bf16_t gsm[];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int ntn = gridDim.x, total = gridDim.x * gridDim.y;
   int tile = blockIdx.x + ntn * blockIdx.y;
@@ -124,10 +127,22 @@ __global__ __launch_bounds__(GEMM_NT) void gemm_bf16_lds_kernel(GemmArgs g) {
     lds_off[u] = row * GT_LD + kp;
   }
   gemm_bf16x8_t ar[4], br[4];  // native vectors: a union-based uint4 array carried across steps lands in scratch
+  // step 0's tile straight into buffer 0, step 1's into registers
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     ar[u] = *(const gemm_bf16x8_t*)ag[u];
     br[u] = *(const gemm_bf16x8_t*)bg[u];
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    *(gemm_bf16x8_t*)&gsm[lds_off[u]] = ar[u];
+    *(gemm_bf16x8_t*)&gsm[2 * GT_BUF + lds_off[u]] = br[u];
+  }
+  const int k1 = 64 < g.K ? 64 : 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    ar[u] = *(const gemm_bf16x8_t*)(ag[u] + k1);
+    br[u] = *(const gemm_bf16x8_t*)(bg[u] + k1);
   }
   gemm_f32x4_t acc[4][4];
 #pragma unroll
@@ -136,21 +151,26 @@ __global__ __launch_bounds__(GEMM_NT) void gemm_bf16_lds_kernel(GemmArgs g) {
     for (int j = 0; j < 4; ++j) acc[i][j] = gemm_f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   const int wm = (wv & 1) * 64, wn = (wv >> 1) * 64;
   const int ql = lane & 15, kq = (lane >> 4) * 8;
+  int cur = 0;
   for (int k0 = 0; k0 < g.K; k0 += 64) {
-    __syncthreads();  // the previous step's fragment reads are done
+    __syncthreads();  // buffer cur is written; the other buffer's last reads (step k0 - 64) are done
+    const int nxt = cur ^ 1;
+    if (k0 + 64 < g.K) {  // step k0 + 64's tile into the other buffer, then step k0 + 128's loads
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      *(gemm_bf16x8_t*)&As[lds_off[u]] = ar[u];
-      *(gemm_bf16x8_t*)&Bs[lds_off[u]] = br[u];
-    }
-    __syncthreads();
-    const int kn = k0 + 64 < g.K ? k0 + 64 : k0;  // the last step reloads its own tile (in bounds, unused)
+      for (int u = 0; u < 4; ++u) {
+        *(gemm_bf16x8_t*)&gsm[nxt * GT_BUF + lds_off[u]] = ar[u];
+        *(gemm_bf16x8_t*)&gsm[(2 + nxt) * GT_BUF + lds_off[u]] = br[u];
+      }
+      const int kn = k0 + 128 < g.K ? k0 + 128 : k0;  // past the end: reload a tile in bounds (unused)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      ar[u] = *(const gemm_bf16x8_t*)(ag[u] + kn);
-      br[u] = *(const gemm_bf16x8_t*)(bg[u] + kn);
+      for (int u = 0; u < 4; ++u) {
+        ar[u] = *(const gemm_bf16x8_t*)(ag[u] + kn);
+        br[u] = *(const gemm_bf16x8_t*)(bg[u] + kn);
+      }
     }
-    __builtin_amdgcn_sched_barrier(0);  // the next step's loads go out before this step's MFMAs
+    __builtin_amdgcn_sched_barrier(0);  // the copies and loads go out before this step's MFMAs
+    const bf16_t* As = gsm + cur * GT_BUF;
+    const bf16_t* Bs = gsm + (2 + cur) * GT_BUF;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       gemm_bf16x8_t a[4], b[4];
@@ -165,6 +185,7 @@ __global__ __launch_bounds__(GEMM_NT) void gemm_bf16_lds_kernel(GemmArgs g) {
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
+    cur = nxt;
   }
   gemm_store(g, acc, bm + wm, bn + wn, lane);
 }
@@ -172,8 +193,11 @@ __global__ __launch_bounds__(GEMM_NT) void gemm_bf16_lds_kernel(GemmArgs g) {
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t st) {
   if (g.M == 0 || g.N == 0) return hipSuccess;
   dim3 grid((unsigned)((g.N + 127) / 128), (unsigned)((g.M + 127) / 128));
-  if (g.K % 64 == 0)
-    hipLaunchKernelGGL(gemm_bf16_lds_kernel, grid, dim3(GEMM_NT), 0, st, g);
+  if (g.K % 64 == 0) {
+    (void)hipFuncSetAttribute((const void*)gemm_bf16_lds_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)GEMM_LDS);
+    hipLaunchKernelGGL(gemm_bf16_lds_kernel, grid, dim3(GEMM_NT), GEMM_LDS, st, g);
+  }
   else
     hipLaunchKernelGGL(gemm_bf16_kernel, grid, dim3(GEMM_NT), 0, st, g);
   return hipGetLastError();
