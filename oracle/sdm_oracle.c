@@ -369,7 +369,7 @@ int oracle_write_read(int B, int T, int H, int F, const int* widths, int dk, int
  * ------------------------------------------------------------------------------------------------------------- */
 
 typedef struct {
-  int B, T, H, F, dk, d, W, R, bank_bf16, exact;
+  int B, T, H, F, dk, d, W, R, bank_bf16, exact, snap_bf16;
   const int* widths;
   const float *wkeys, *rq, *values, *alpha, *beta, *sub, *bank, *dout, *dbank;
   int64_t bank_rows, sumn;
@@ -412,7 +412,11 @@ static void* bwd_worker(void* arg) {
   double* g = (double*)malloc(sizeof(double) * (size_t)W * d);
   double* D = (double*)malloc(sizeof(double) * (size_t)d);
   double* dw = (double*)malloc(sizeof(double) * (size_t)(W > R ? W : R));
-  if (!S || !Rd || !sc || !w || !rho || !P || !Vr || !rr || !del || !M || !G || !g || !D || !dw) { j->err = 1; goto done; }
+  unsigned char* later = (unsigned char*)malloc((size_t)rows);
+  if (!S || !Rd || !sc || !w || !rho || !P || !Vr || !rr || !del || !M || !G || !g || !D || !dw || !later) {
+    j->err = 1;
+    goto done;
+  }
   for (int st = j->s_begin; st < j->s_end; ++st) {
     const int b = st / H, h = st % H;
     const float* sub = j->sub + (int64_t)h * j->sumn * dk;
@@ -460,6 +464,26 @@ static void* bwd_worker(void* arg) {
     }
     if (j->bank64)
       for (int64_t i = 0; i < rows * d; ++i) j->bank64[(int64_t)st * rows * d + i] = M[i];
+    /* bfloat16 snapshot (CHANGELOG 2.0.0, "New"): the backward sees every pre-write row rounded to bfloat16, and r
+     * and delta rebuilt from those rows; a row read at token t whose slot a later token writes was restored in place
+     * from such a row, so it is rounded too (marked in `later` as the sweep goes back) */
+    if (j->snap_bf16) {
+      for (int64_t i = 0; i < (int64_t)T * W * d; ++i) P[i] = (double)round_to(P[i], 1);
+      for (int t = 0; t < T; ++t) {
+        const int64_t row = ((int64_t)b * T + t) * H + h;
+        const double a = j->alpha[row], be = j->beta[row];
+        const float* v = j->values + row * d;
+        double* r = rr + (int64_t)t * d;
+        double* dl = del + (int64_t)t * d;
+        for (int c = 0; c < d; ++c) {
+          double acc = 0.0;
+          for (int i = 0; i < W; ++i) acc += w[(int64_t)t * W + i] * P[((int64_t)t * W + i) * d + c];
+          r[c] = acc;
+          dl[c] = be * ((double)v[c] - a * acc);
+        }
+      }
+    }
+    for (int64_t i = 0; i < rows; ++i) later[i] = 0;
     /* reverse sweep */
     for (int64_t i = 0; i < rows * d; ++i) G[i] = j->dbank ? (double)j->dbank[(int64_t)st * rows * d + i] : 0.0;
     for (int t = T - 1; t >= 0; --t) {
@@ -477,8 +501,9 @@ static void* bwd_worker(void* arg) {
       double sum = 0.0;
       for (int i = 0; i < R; ++i) {
         const double* q = Vr + ((int64_t)t * R + i) * d;
+        const int rounded = j->snap_bf16 && later[Rt[i]];
         double acc = 0.0;
-        for (int c = 0; c < d; ++c) acc += (double)dout[c] * q[c];
+        for (int c = 0; c < d; ++c) acc += (double)dout[c] * (rounded ? (double)round_to(q[c], 1) : q[c]);
         dw[i] = acc;
         double* Gr = G + (int64_t)Rt[i] * d;
         for (int c = 0; c < d; ++c) Gr[c] += rt[i] * (double)dout[c];
@@ -516,6 +541,7 @@ static void* bwd_worker(void* arg) {
         double* Gw = G + (int64_t)St[i] * d;
         const double* gi = g + (int64_t)i * d;
         for (int c = 0; c < d; ++c) Gw[c] = a * gi[c] - a * be * wt[i] * D[c];
+        later[St[i]] = 1;
       }
       sum = 0.0;
       for (int i = 0; i < W; ++i) sum += wt[i] * dw[i];
@@ -527,7 +553,7 @@ static void* bwd_worker(void* arg) {
   }
 done:
   free(S); free(Rd); free(sc); free(w); free(rho); free(P); free(Vr); free(rr); free(del); free(M); free(G);
-  free(g); free(D); free(dw);
+  free(g); free(D); free(dw); free(later);
   return NULL;
 }
 
@@ -539,7 +565,8 @@ done:
  * (the gradient with respect to the bank before the call); optional out64 [B, T, H, d] and bank64 (the forward's
  * outputs in fp64, unrounded, NULL to skip). Returns 0 or -1. */
 int oracle_write_read_backward(int B, int T, int H, int F, const int* widths, int dk, int d, int W, int R,
-                               int bank_bf16, int exact, const float* wkeys, const float* rq, const float* values,
+                               int bank_bf16, int exact, int snap_bf16, const float* wkeys, const float* rq,
+                               const float* values,
                                const float* alpha, const float* beta, const float* subkeys, const float* bank,
                                int64_t bank_rows, const float* dout, const float* dbank, double* d_wkeys,
                                double* d_rq, double* d_values, double* d_alpha, double* d_beta, double* d_subkeys,
@@ -563,7 +590,7 @@ int oracle_write_read_backward(int B, int T, int H, int F, const int* widths, in
   for (int i = 0; i < nthreads; ++i) {
     bwd_job_t* j = &jobs[i];
     j->B = B; j->T = T; j->H = H; j->F = F; j->dk = dk; j->d = d; j->W = W; j->R = R;
-    j->bank_bf16 = bank_bf16; j->exact = exact; j->widths = widths; j->wkeys = wkeys; j->rq = rq;
+    j->bank_bf16 = bank_bf16; j->exact = exact; j->snap_bf16 = snap_bf16; j->widths = widths; j->wkeys = wkeys; j->rq = rq;
     j->values = values; j->alpha = alpha; j->beta = beta; j->sub = subkeys; j->bank = bank; j->dout = dout;
     j->dbank = dbank; j->bank_rows = bank_rows; j->sumn = sumn; j->d_wkeys = d_wkeys; j->d_rq = d_rq;
     j->d_values = d_values; j->d_alpha = d_alpha; j->d_beta = d_beta; j->d_sub_stream = dsub_stream;

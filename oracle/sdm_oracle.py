@@ -67,7 +67,7 @@ def _load():
             lib.oracle_write_read_backward.restype = ctypes.c_int
             lib.oracle_write_read_backward.argtypes = [
                 ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, ctypes.c_int, ctypes.c_int,
-                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                 _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, ctypes.c_int64, _f32p, vp,
                 _f64p, _f64p, _f64p, _f64p, _f64p, _f64p, _f64p, vp, vp, ctypes.c_int]
             _lib = lib
@@ -172,14 +172,18 @@ def write_read(wkeys, rq, values, alpha, beta, subkeys, bank, widths, num_writes
 
 
 def write_read_backward(wkeys, rq, values, alpha, beta, subkeys, bank, dout, dbank, widths, num_writes, num_reads,
-                        *, bank_bf16=False, exact=False, want_forward=False, nthreads: int | None = None):
+                        *, bank_bf16=False, exact=False, snap_bf16=False, want_forward=False,
+                        nthreads: int | None = None):
     """Gradients of the write/read (the chain rule through the per-token recurrence, in reverse; sdm_oracle.c).
 
     bank is the bank before the call [B, H, bank_rows, d]; dout [B, T, H, d] and dbank (same shape as bank, or None
     for zero) are the gradients of the loss with respect to out and to the bank after the call. exact=True keeps
     the bank states in fp64 (no rounding to the bank dtype). Returns fp64 arrays d_wkeys, d_rq, d_values, d_alpha,
     d_beta, d_subkeys, d_bank (with respect to the bank before the call), and with want_forward=True also out and
-    bank (the forward in fp64, rounded to the bank dtype after every token unless exact).
+    bank (the forward in fp64, rounded to the bank dtype after every token unless exact). snap_bf16=True: the
+    backward of a bfloat16 snapshot (CHANGELOG 2.0.0, "New"): every pre-write row it reads rounded to bfloat16 (r and
+    delta rebuilt from them), and a row read at token t whose slot a later token writes rounded too (the bank is
+    restored in place from the snapshot as the sweep goes back).
     """
     wk, rqa, v, al, be, sub = (_f32(x) for x in (wkeys, rq, values, alpha, beta, subkeys))
     M = _f32(bank)
@@ -200,7 +204,8 @@ def write_read_backward(wkeys, rq, values, alpha, beta, subkeys, bank, dout, dba
         fwd = [res["out"].ctypes.data, res["bank"].ctypes.data]
     nt = nthreads or min(os.cpu_count() or 1, 16)
     rc = _load().oracle_write_read_backward(
-        B, T, H, len(widths), widths, dk, d, W, R, int(bool(bank_bf16)), int(bool(exact)), wk, rqa, v, al, be, sub,
+        B, T, H, len(widths), widths, dk, d, W, R, int(bool(bank_bf16)), int(bool(exact)), int(bool(snap_bf16)),
+        wk, rqa, v, al, be, sub,
         M, M.shape[2], g_out, None if g_bank is None else g_bank.ctypes.data, res["d_wkeys"], res["d_rq"],
         res["d_values"], res["d_alpha"], res["d_beta"], res["d_subkeys"], res["d_bank"], fwd[0], fwd[1], nt)
     if rc != 0:

@@ -143,3 +143,91 @@ def test_zero_upstream_gradient_gives_zero_and_bank_gradient_passes_untouched_ro
     untouched = [s for s in range(64) if s not in touched]
     assert untouched
     assert np.array_equal(r["d_bank"][0, 0, untouched], u_bank[0, 0, untouched].astype(np.float64))
+
+
+# ------------------------------------------------------------------ bfloat16 snapshot (CHANGELOG 2.0.0, "New")
+def _bwd(x, dout, dbank, widths, W, R, **kw):
+    return oracle.write_read_backward(x["wkeys"], x["rq"], x["values"], x["alpha"], x["beta"], x["subkeys"],
+                                      x["bank"], dout, dbank, widths, W, R, nthreads=1, **kw)
+
+
+def _rbf16(a):
+    return np.vectorize(oracle.round_bf16)(np.asarray(a, dtype=np.float64))
+
+
+def test_bf16_snapshot_leaves_value_and_bank_gradients_alone():
+    """The rounded rows feed only the key, gate and query gradients: d_values and d_bank use no row."""
+    x = _case(7, 1, 12, 2, (4, 4), 3, 5, 3, 2)[0]
+    rng = np.random.default_rng(8)
+    dout = rng.standard_normal(x["values"].shape).astype(np.float32)
+    dbank = rng.standard_normal(x["bank"].shape).astype(np.float32)
+    a = _bwd(x, dout, dbank, (4, 4), 3, 2)
+    b = _bwd(x, dout, dbank, (4, 4), 3, 2, snap_bf16=True)
+    np.testing.assert_array_equal(a["d_values"], b["d_values"])
+    np.testing.assert_array_equal(a["d_bank"], b["d_bank"])
+    assert not np.array_equal(a["d_alpha"], b["d_alpha"])  # the rows are not bf16-exact here
+
+
+def test_bf16_snapshot_of_exact_rows_changes_nothing():
+    """Rows that are bfloat16 values already (a bf16 bank that never changes: alpha = 1, beta = 0) round to
+    themselves: every gradient equals the float32 snapshot's."""
+    x = _case(9, 1, 10, 1, (4, 4), 3, 6, 3, 3)[0]
+    x["bank"] = _rbf16(x["bank"]).astype(np.float32)
+    x["alpha"][:] = 1.0
+    x["beta"][:] = 0.0
+    rng = np.random.default_rng(10)
+    dout = rng.standard_normal(x["values"].shape).astype(np.float32)
+    a = _bwd(x, dout, None, (4, 4), 3, 3)
+    b = _bwd(x, dout, None, (4, 4), 3, 3, snap_bf16=True)
+    for k in a:
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+
+
+def test_bf16_snapshot_one_token_gate_gradients_by_hand():
+    """One token, one slot written and read (the same key and query): g = dout, D = dout, r = P, so
+    d alpha = (1 - beta) <dout, P~> and d beta = <dout, v - alpha P~> with P~ the row rounded to bfloat16."""
+    rng = np.random.default_rng(11)
+    widths, dk, d = (4,), 2, 6
+    q = rng.standard_normal((1, 1, 1, dk)).astype(np.float32)
+    x = {"wkeys": q, "rq": q.copy(), "values": rng.standard_normal((1, 1, 1, d)).astype(np.float32),
+         "alpha": np.array([[[0.7]]], np.float32), "beta": np.array([[[0.3]]], np.float32),
+         "subkeys": rng.standard_normal((1, 4, dk)).astype(np.float32),
+         "bank": (rng.standard_normal((1, 1, 4, d)) / 3).astype(np.float32)}
+    dout = rng.standard_normal((1, 1, 1, d)).astype(np.float32)
+    ids, _ = oracle.topk(q, x["subkeys"], widths, 1)
+    P = x["bank"][0, 0, ids[0, 0, 0, 0]].astype(np.float64)
+    Pq = _rbf16(P)
+    assert not np.array_equal(P, Pq)
+    a, be = np.float64(x["alpha"][0, 0, 0]), np.float64(x["beta"][0, 0, 0])
+    g = dout[0, 0, 0].astype(np.float64)
+    v = x["values"][0, 0, 0].astype(np.float64)
+    for Prow, kw in ((P, {}), (Pq, {"snap_bf16": True})):
+        r = _bwd(x, dout, None, widths, 1, 1, **kw)
+        assert abs(r["d_alpha"][0, 0, 0] - (1 - be) * (g @ Prow)) <= 1e-12
+        assert abs(r["d_beta"][0, 0, 0] - g @ (v - a * Prow)) <= 1e-12
+
+
+def test_bf16_snapshot_rounds_a_read_row_only_if_a_later_token_writes_its_slot():
+    """Token 0 reads slot s; token 1 writes s (and token 0 does not). Rounding the row read at token 0 is what
+    the in-place restore from a bfloat16 snapshot gives; with one token (nothing later) the read gradient matches
+    the float32 snapshot's exactly."""
+    rng = np.random.default_rng(12)
+    widths, dk, d = (4,), 2, 5
+    sub = np.zeros((1, 4, dk), np.float32)
+    sub[0, :, 0] = [3.0, 2.0, 1.0, 0.0]  # query (1, 0) ranks slots 0, 1, 2, 3; query (-1, 0) ranks 3, 2, 1, 0
+    q_best0 = np.array([1.0, 0.0], np.float32)
+    q_best3 = np.array([-1.0, 0.0], np.float32)
+    x = {"wkeys": np.stack([q_best3, q_best0])[None, :, None, :],    # writes: token 0 slot 3, token 1 slot 0
+         "rq": np.stack([q_best0, q_best3])[None, :, None, :],       # reads (R = 2): token 0 slots 0, 1
+         "values": rng.standard_normal((1, 2, 1, d)).astype(np.float32),
+         "alpha": np.array([[[0.9], [0.8]]], np.float32), "beta": np.array([[[0.4], [0.6]]], np.float32),
+         "subkeys": sub, "bank": (rng.standard_normal((1, 1, 4, d)) / 3).astype(np.float32)}
+    dout = rng.standard_normal((1, 2, 1, d)).astype(np.float32)
+    a = _bwd(x, dout, None, widths, 1, 2)
+    b = _bwd(x, dout, None, widths, 1, 2, snap_bf16=True)
+    assert not np.array_equal(a["d_rq"][0, 0], b["d_rq"][0, 0])  # token 0 read slot 0, which token 1 rewrites
+    one = {k: v[:, :1] for k, v in x.items() if k not in ("subkeys", "bank")}
+    one.update(subkeys=x["subkeys"], bank=x["bank"])
+    a1 = _bwd(one, dout[:, :1], None, widths, 1, 2)
+    b1 = _bwd(one, dout[:, :1], None, widths, 1, 2, snap_bf16=True)
+    np.testing.assert_array_equal(a1["d_rq"], b1["d_rq"])
