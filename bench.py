@@ -189,10 +189,34 @@ def bench_train(args, torch, binding, synth):
     prof = binding.profile_read()
     binding.profile_enable(False)
     ms_f, ms_b = tf * 1e3 / n, tb * 1e3 / n
+    # the same step with a bfloat16 snapshot (half the snapshot bytes; the bank comes back rounded where written)
+    del snap
+    snap_q = torch.empty((s.batch, s.heads, s.tokens, s.num_writes, s.head_dim), dtype=torch.bfloat16, device=dev)
+    tqf = tqb = 0.0
+    for _ in range(n):
+        gbank.zero_()
+        torch.cuda.synchronize()
+        a = time.perf_counter()
+        binding.sdm_write_read_save(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"], t["subkeys"], bank,
+                                    out=out, snapshot=snap_q, workspace=wsf, snapshot_quant="bf16", **kw)
+        torch.cuda.synchronize()
+        b = time.perf_counter()
+        binding.sdm_write_read_backward(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"], t["subkeys"], bank,
+                                        snap_q, gout, gbank, workspace=wsb, snapshot_quant="bf16", **kw)
+        torch.cuda.synchronize()
+        c = time.perf_counter()
+        tqf += b - a
+        tqb += c - b
+    snap = snap_q
+    ms_qf, ms_qb = tqf * 1e3 / n, tqb * 1e3 / n
     res = {"tokens_per_s": round(s.batch * s.tokens / ((ms_f + ms_b) * 1e-3), 1),
            "ms_forward_save": round(ms_f, 4), "ms_backward": round(ms_b, 4), "steps": n,
            "kernels_avg_ms": {k: round(v[0] / v[1], 4) for k, v in prof.items() if v[1]},
-           "snapshot_bytes": snap.numel() * snap.element_size(), "bank_restored_bitwise": restored,
+           "snapshot_bytes": s.batch * s.heads * s.tokens * s.num_writes * s.head_dim * 4,
+           "bank_restored_bitwise": restored,
+           "bf16_snapshot": {"tokens_per_s": round(s.batch * s.tokens / ((ms_qf + ms_qb) * 1e-3), 1),
+                             "ms_forward_save": round(ms_qf, 4), "ms_backward": round(ms_qb, 4),
+                             "snapshot_bytes": snap_q.numel() * snap_q.element_size()},
            "config": "layer_65k (as the headline), grad_out ~ N(0,1), float32 gradients"}
     log(f"[bench] train: forward+snapshot {ms_f:.3f} ms, backward {ms_b:.3f} ms")
     del g, snap, gbank, bank, wsf, wsb, out, t, gout

@@ -40,7 +40,7 @@ class SdmConfig(ctypes.Structure):
         ("head_dim", ctypes.c_int32), ("num_writes", ctypes.c_int32), ("num_reads", ctypes.c_int32),
         ("chunk_size", ctypes.c_int32), ("act_dtype", ctypes.c_int32), ("bank_dtype", ctypes.c_int32),
         ("bank_rows", ctypes.c_int64), ("bank_row_stride", ctypes.c_int64),
-        ("shared_bank", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("shared_bank", ctypes.c_int32), ("snapshot_dtype", ctypes.c_int32),
     ]
 
 
@@ -50,7 +50,7 @@ class SdmLayerConfig(ctypes.Structure):
 
 def make_config(batch, tokens, heads, widths, subkey_dim, head_dim=1, num_writes=1, num_reads=1, chunk_size=1,
                 act_dtype=SDM_F32, bank_dtype=SDM_F32, bank_rows=None, bank_row_stride=0,
-                shared_bank=False) -> SdmConfig:
+                shared_bank=False, snapshot_dtype=0) -> SdmConfig:
     c = SdmConfig()
     c.batch, c.tokens, c.heads = int(batch), int(tokens), int(heads)
     c.num_factors = len(widths)
@@ -65,7 +65,18 @@ def make_config(batch, tokens, heads, widths, subkey_dim, head_dim=1, num_writes
     c.bank_rows = int(bank_rows) if bank_rows is not None else n
     c.bank_row_stride = int(bank_row_stride)
     c.shared_bank = 1 if shared_bank else 0
+    c.snapshot_dtype = int(snapshot_dtype)
     return c
+
+
+_SNAP = {"none": 0, "bf16": SDM_BF16}
+
+
+def _snapshot_dtype(snapshot_quant: str, bank: torch.Tensor):
+    """(config code, torch dtype) of the backward snapshot: "none" = the bank dtype, "bf16" = bfloat16."""
+    if snapshot_quant not in _SNAP:
+        raise ValueError(f"snapshot_quant must be one of {sorted(_SNAP)}, not {snapshot_quant!r}")
+    return _SNAP[snapshot_quant], (torch.bfloat16 if snapshot_quant == "bf16" else bank.dtype)
 
 
 def bank_pitch(head_dim: int, dtype: torch.dtype) -> int:
@@ -346,9 +357,10 @@ def layer_workspace_views(x_shape, heads, widths, subkey_dim, head_dim, ws):
 
 
 def sdm_write_read_save(write_keys, read_queries, values, forget_gate, input_gate, subkeys, bank, *, widths,
-                        num_writes, num_reads, chunk_size, want_index=False, out=None, snapshot=None, workspace=None):
-    """sdm_write_read that also saves the backward's snapshot [B, H, T, W, d] (bank dtype): the row of every write
-    event before it. Returns (out, write_idx, read_idx, snapshot)."""
+                        num_writes, num_reads, chunk_size, want_index=False, out=None, snapshot=None, workspace=None,
+                        snapshot_quant="none"):
+    """sdm_write_read that also saves the backward's snapshot [B, H, T, W, d] (bank dtype, or bfloat16 with
+    snapshot_quant="bf16"): the row of every write event before it. Returns (out, write_idx, read_idx, snapshot)."""
     B, T, H, Fdk = write_keys.shape
     F = len(widths)
     dk = Fdk // F
@@ -361,17 +373,18 @@ def sdm_write_read_save(write_keys, read_queries, values, forget_gate, input_gat
     if bank.dim() != 4 or bank.shape[0] != B or bank.shape[1] != H or bank.shape[3] != d:
         raise ValueError(f"bank has shape {tuple(bank.shape)}, expected ({B}, {H}, bank_rows, {d})")
     ld = _bank_ld(bank, "bank")
+    scode, sdt = _snapshot_dtype(snapshot_quant, bank)
     cfg = make_config(B, T, H, widths, dk, d, num_writes, num_reads, chunk_size, _dt(write_keys), _dt(bank),
-                      bank.shape[2], ld)
+                      bank.shape[2], ld, snapshot_dtype=scode)
     ws = _workspace(workspace_size(cfg, SDM_OP_WRITE_READ), bank.device, workspace)
     if out is None:
         out = torch.empty((B, T, H, d), dtype=act, device=bank.device)
     else:
         _need(out, "out", (B, T, H, d), act)
     if snapshot is None:
-        snapshot = torch.empty((B, H, T, num_writes, d), dtype=bank.dtype, device=bank.device)
+        snapshot = torch.empty((B, H, T, num_writes, d), dtype=sdt, device=bank.device)
     else:
-        _need(snapshot, "snapshot", (B, H, T, num_writes, d), bank.dtype)
+        _need(snapshot, "snapshot", (B, H, T, num_writes, d), sdt)
     widx = torch.empty((B, T, H, num_writes), dtype=torch.int32, device=bank.device) if want_index else None
     ridx = torch.empty((B, T, H, num_reads), dtype=torch.int32, device=bank.device) if want_index else None
     _check(load().sdm_write_read_save(ctypes.byref(cfg), _ptr(write_keys), _ptr(read_queries), _ptr(values),
@@ -382,8 +395,10 @@ def sdm_write_read_save(write_keys, read_queries, values, forget_gate, input_gat
 
 
 def sdm_write_read_backward(write_keys, read_queries, values, forget_gate, input_gate, subkeys, bank, snapshot,
-                            grad_out, grad_bank=None, *, widths, num_writes, num_reads, chunk_size, workspace=None):
-    """Backward of sdm_write_read_save. bank (as the forward left it) steps back to its state before the forward.
+                            grad_out, grad_bank=None, *, widths, num_writes, num_reads, chunk_size, workspace=None,
+                            snapshot_quant="none"):
+    """Backward of sdm_write_read_save (the same snapshot_quant). bank (as the forward left it) steps back to its
+    state before the forward (with a bfloat16 snapshot of a float32 bank, written rows come back rounded).
     grad_bank: float32 with the bank's shape and row stride, the gradient w.r.t. the bank after the forward (None:
     zeros), replaced in place by the gradient w.r.t. the bank before it. Returns a dict of float32 gradients:
     write_keys, read_queries, values, forget_gate, input_gate, subkeys, bank."""
@@ -400,7 +415,8 @@ def sdm_write_read_backward(write_keys, read_queries, values, forget_gate, input
     if bank.dim() != 4 or bank.shape[0] != B or bank.shape[1] != H or bank.shape[3] != d:
         raise ValueError(f"bank has shape {tuple(bank.shape)}, expected ({B}, {H}, bank_rows, {d})")
     ld = _bank_ld(bank, "bank")
-    _need(snapshot, "snapshot", (B, H, T, num_writes, d), bank.dtype)
+    scode, sdt = _snapshot_dtype(snapshot_quant, bank)
+    _need(snapshot, "snapshot", (B, H, T, num_writes, d), sdt)
     dev = bank.device
     if grad_bank is None:
         grad_bank = torch.zeros((B, H, bank.shape[2], ld), dtype=torch.float32, device=dev)[..., :d]
@@ -408,7 +424,7 @@ def sdm_write_read_backward(write_keys, read_queries, values, forget_gate, input
             grad_bank.stride() != bank.stride():
         raise ValueError("grad_bank must be float32 with the bank's shape and strides")
     cfg = make_config(B, T, H, widths, dk, d, num_writes, num_reads, chunk_size, _dt(write_keys), _dt(bank),
-                      bank.shape[2], ld)
+                      bank.shape[2], ld, snapshot_dtype=scode)
     ws = _workspace(workspace_size(cfg, SDM_OP_BACKWARD), dev, workspace)
     f32 = torch.float32
     g = {"write_keys": torch.empty((B, T, H, Fdk), dtype=f32, device=dev),

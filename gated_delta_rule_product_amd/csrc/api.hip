@@ -331,6 +331,23 @@ sdm_status hip_status(hipError_t e, const char* what) {
     if (_s != SDM_OK) return _s;      \
   } while (0)
 
+// The backward snapshot's element: the bank dtype (snapshot_dtype 0), or bfloat16 (SDM_BF16; the same as 0 on a
+// bfloat16 bank) [CHANGELOG 2.0.0, "New": bf16 snapshots on a float32 bank]. A bfloat16 snapshot of a float32
+// bank has native kernels when the held-row loop writes the snapshot and the fast reverse sweep (W, R <= 128) reads
+// it; other training calls are refused before any work, as the pages refuse snapshot routes they lack.
+sdm_status snapshot_kind(const sdm_config* cfg, const Dims& D, bool* bf16_snap) {
+  *bf16_snap = false;
+  if (cfg->snapshot_dtype == 0 || (cfg->snapshot_dtype == SDM_BF16 && D.bank == SDM_BF16)) return SDM_OK;
+  if (cfg->snapshot_dtype != SDM_BF16)
+    return fail(SDM_ERR_DTYPE, "snapshot_dtype = %d (0: the bank dtype, or SDM_BF16)", cfg->snapshot_dtype);
+  if (!loop_held_snap_ok(D) || !bwd_fast(D))
+    return fail(SDM_ERR_RANGE, "no native route for a bfloat16 snapshot of a float32 bank at these settings (it "
+                "needs the held-row loop: chunk a power of two in [8, 128], at most 32 terms per lane group, and "
+                "num_writes, num_reads <= 128): use snapshot_dtype 0");
+  *bf16_snap = true;
+  return SDM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -397,7 +414,9 @@ static sdm_status write_read_impl(const sdm_config* cfg, const void* write_keys,
   Dims D;
   TopkPlan pw, pr;
   TRY(validate(cfg, SDM_OP_WRITE_READ, 0, &D, &pw, &pr));
-  const size_t snap_bytes = (size_t)D.S * D.T * D.W * D.d * esize(D.bank);
+  bool bf16_snap = false;
+  if (snapshot) TRY(snapshot_kind(cfg, D, &bf16_snap));
+  const size_t snap_bytes = (size_t)D.S * D.T * D.W * D.d * (bf16_snap ? 2 : esize(D.bank));
   if (snapshot || cfg->shared_bank) {
     if (cfg->shared_bank && snapshot)
       return fail(SDM_ERR_RANGE, "a shared bank has no backward (sdm_write_read_save refuses shared_bank)");
@@ -499,6 +518,7 @@ static sdm_status write_read_impl(const sdm_config* cfg, const void* write_keys,
   la.out = out;
   la.abort = abort;
   la.snap = snapshot;
+  la.snap_bf16 = bf16_snap ? 1 : 0;
   TRY(hip_status(timed(SDM_K_LOOP, st, [&] { return launch_loop(D, la, st); }), "chunk loop launch"));
   return ok();
 }
@@ -532,6 +552,8 @@ sdm_status sdm_write_read_backward(const sdm_config* cfg, const void* write_keys
   Dims D;
   TopkPlan pw, pr;
   TRY(validate(cfg, SDM_OP_BACKWARD, 0, &D, &pw, &pr));
+  bool bf16_snap = false;
+  TRY(snapshot_kind(cfg, D, &bf16_snap));
   const long long rows = (long long)D.B * D.T * D.H;
   long long sumn = 0;
   for (int f = 0; f < D.F; ++f) sumn += D.widths[f];
@@ -559,7 +581,7 @@ sdm_status sdm_write_read_backward(const sdm_config* cfg, const void* write_keys
                        {forget_gate, (size_t)rows * ea, "forget_gate"},
                        {input_gate, (size_t)rows * ea, "input_gate"},
                        {subkeys, (size_t)D.H * sumn * D.dk * ea, "subkeys"},
-                       {snapshot, (size_t)D.S * D.T * D.W * D.d * eb, "snapshot"},
+                       {snapshot, (size_t)D.S * D.T * D.W * D.d * (bf16_snap ? 2 : eb), "snapshot"},
                        {grad_out, (size_t)rows * D.d * ea, "grad_out"}};
   const Range outs[] = {{bank, nbank * eb, "bank"},
                         {grad_bank, nbank * 4, "grad_bank"},
@@ -609,6 +631,7 @@ sdm_status sdm_write_read_backward(const sdm_config* cfg, const void* write_keys
   ba.gout = grad_out;
   ba.bank = bank;
   ba.snap = snapshot;
+  ba.snap_bf16 = bf16_snap ? 1 : 0;
   ba.gbank = grad_bank;
   ba.gwkeys = grad_write_keys;
   ba.grq = grad_read_queries;

@@ -281,13 +281,15 @@ __global__ __launch_bounds__(64) void bwd_match_kernel(Dims D, BwdArgs a) {
 // follow the end-of-token barrier, after every store of token t in the workgroup's program order (one CU: its
 // vector memory pipeline keeps that order).
 // LPG lanes per term group (4 columns each): slices of 4 LPG columns, 128 groups, 128 LPG threads (2 LPG waves).
-template <typename A, typename Bk, int LPG>
+// Sk: the snapshot's element type (Bk, or bfloat16 rows of a float32 bank, which restore the bank widened).
+template <typename A, typename Bk, int LPG, typename Sk = Bk>
 __global__ __launch_bounds__(128 * LPG) void bwd_sweep_fast_kernel(Dims D, BwdArgs a, int nsl) {
   constexpr int COLS = 4 * LPG, NW = 2 * LPG;
   __shared__ __align__(16) float sRedD[NW][COLS];
   __shared__ __align__(16) float sRedR[NW][COLS];
   __shared__ float sRedGP[NW];
   typedef typename Raw4<Bk>::T RawT;
+  typedef typename Raw4<Sk>::T RawS;
   typedef typename Raw4<A>::T ARaw;
   const int W = D.W, R = D.R, T = D.T, d = D.d;
   const int nblk = gridDim.x;
@@ -303,7 +305,7 @@ __global__ __launch_bounds__(128 * LPG) void bwd_sweep_fast_kernel(Dims D, BwdAr
   const int P = W + R + 2;
   Bk* bank = (Bk*)a.bank + (long long)st * D.rows * D.ld;
   float* gbank = a.gbank + (long long)st * D.rows * D.ld;
-  const Bk* snap = (const Bk*)a.snap + (long long)st * T * W * d;
+  const Sk* snap = (const Sk*)a.snap + (long long)st * T * W * d;
   const A* gout = (const A*)a.gout;
   const A* values = (const A*)a.values;
   const A* alpha = (const A*)a.alpha;
@@ -322,20 +324,20 @@ __global__ __launch_bounds__(128 * LPG) void bwd_sweep_fast_kernel(Dims D, BwdAr
   };
   // (separate variables, not a struct: a struct copy becomes a byte-wise memcpy that needs the loaded data at once;
   // 16-bit values in 32-bit words: kept in 16 bits the compiler re-masks them right after their load)
-  auto load_tok = [&](int t, uint32_t& al_, uint32_t& be_, ARaw& v_, ARaw& dout_, RawT& sp_) {
+  auto load_tok = [&](int t, uint32_t& al_, uint32_t& be_, ARaw& v_, ARaw& dout_, RawS& sp_) {
     const long long row = ((long long)b * T + t) * D.H + h;
     al_ = Word<A>::load(alpha + row + zero);
     be_ = Word<A>::load(beta + row + zero);
     dout_ = Raw4<A>::load(gout + row * d + dcol);
     v_ = Raw4<A>::load(values + row * d + dcol);
-    sp_ = Raw4<Bk>::load(snap + ((long long)t * W + jw) * d + dcol);
+    sp_ = Raw4<Sk>::load(snap + ((long long)t * W + jw) * d + dcol);
   };
 
   int rs, ws, rs1, ws1;
   float rho, w, mr, mw, rho1, w1, mr1, mw1;
   uint32_t c_al, c_be;
   ARaw c_v, c_dout;
-  RawT c_sp;
+  RawS c_sp;
   load_ids(T - 1, rs, rho, ws, w, mr, mw);
   load_ids(max(T - 2, 0), rs1, rho1, ws1, w1, mr1, mw1);
   load_tok(T - 1, c_al, c_be, c_v, c_dout, c_sp);
@@ -355,7 +357,7 @@ __global__ __launch_bounds__(128 * LPG) void bwd_sweep_fast_kernel(Dims D, BwdAr
     // ahead: token t - 1's inputs and snapshot rows, token t - 2's ids (token indices clamped at 0)
     uint32_t n_al, n_be;
     ARaw n_v, n_dout;
-    RawT n_sp;
+    RawS n_sp;
     int rs2, ws2;
     float rho2, w2, mr2, mw2;
     load_tok(max(t - 1, 0), n_al, n_be, n_v, n_dout, n_sp);
@@ -372,7 +374,7 @@ __global__ __launch_bounds__(128 * LPG) void bwd_sweep_fast_kernel(Dims D, BwdAr
     rg.x += rho * dout[0]; rg.y += rho * dout[1]; rg.z += rho * dout[2]; rg.w += rho * dout[3];
     // the write: g_i (plus this token's read update of the same slot), P_i
     float g[4] = {wg.x + mr * dout[0], wg.y + mr * dout[1], wg.z + mr * dout[2], wg.w + mr * dout[3]}, pp[4];
-    Raw4<Bk>::unpack(c_sp, pp);
+    Raw4<Sk>::unpack(c_sp, pp);
     if (!valid) pp[0] = pp[1] = pp[2] = pp[3] = 0.f;
     // the looked-ahead values are in (issued before this token's rows, which were just waited for): take them
     // here, before any store, so that moving them into place at the end of the token waits for nothing
@@ -441,7 +443,10 @@ __global__ __launch_bounds__(128 * LPG) void bwd_sweep_fast_kernel(Dims D, BwdAr
         const float cw = ab * w;
         *(float4*)(gbank + (long long)ws * D.ld + col) = make_float4(
             al * g[0] - cw * Dl[0], al * g[1] - cw * Dl[1], al * g[2] - cw * Dl[2], al * g[3] - cw * Dl[3]);
-        Raw4<Bk>::store(bank + (long long)ws * D.ld + col, c_sp);
+        if constexpr (std::is_same<Sk, Bk>::value)
+          Raw4<Bk>::store(bank + (long long)ws * D.ld + col, c_sp);
+        else  // a float32 bank from bfloat16 snapshot rows (pp: the widened values)
+          *(float4*)(bank + (long long)ws * D.ld + col) = make_float4(pp[0], pp[1], pp[2], pp[3]);
       }
     }
     // next token
@@ -586,12 +591,18 @@ static hipError_t launch_bwd_t(const Dims& D, const BwdArgs& a, hipStream_t st) 
   const int nsl = bwd_nsl(D);
   if (bwd_fast(D)) {
     hipLaunchKernelGGL(bwd_match_kernel, dim3((unsigned)((long long)D.S * D.T)), dim3(64), 0, st, D, a);
-    if (bwd_cols(D) == 8)
-      hipLaunchKernelGGL((bwd_sweep_fast_kernel<A, Bk, 2>), dim3((unsigned)((long long)D.S * nsl)), dim3(256), 0, st,
-                         D, a, nsl);
+    const dim3 grid((unsigned)((long long)D.S * nsl));
+    auto fast = [&](auto sk) {  // sk: a value of the snapshot's element type
+      using Sk = decltype(sk);
+      if (bwd_cols(D) == 8)
+        hipLaunchKernelGGL((bwd_sweep_fast_kernel<A, Bk, 2, Sk>), grid, dim3(256), 0, st, D, a, nsl);
+      else
+        hipLaunchKernelGGL((bwd_sweep_fast_kernel<A, Bk, 4, Sk>), grid, dim3(512), 0, st, D, a, nsl);
+    };
+    if (std::is_same<Bk, float>::value && a.snap_bf16)
+      fast(bf16_t{});  // bfloat16 snapshot rows of a float32 bank
     else
-      hipLaunchKernelGGL((bwd_sweep_fast_kernel<A, Bk, 4>), dim3((unsigned)((long long)D.S * nsl)), dim3(512), 0, st,
-                         D, a, nsl);
+      fast(Bk{});
   } else {
     const size_t lds = bwd_sweep_lds(D.W);
     (void)hipFuncSetAttribute((const void*)bwd_sweep_kernel<A, Bk>, hipFuncAttributeMaxDynamicSharedMemorySize,

@@ -455,7 +455,7 @@ template <> struct Act4<bf16_t> {
 // snapshot (a.snap; the plan tagged every event with its term index): a slot's only event stores its held row (the
 // chunk-start row, the row before that event), and a slot written more than once stores its running row before
 // each of its events.
-template <typename A, typename Bk, bool FULL, bool SNAP>
+template <typename A, typename Bk, bool FULL, bool SNAP, bool SB = false>
 __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, int nslices) {
   if (a.abort && *a.abort) return;  // shared-bank conflict: no work (uniform over the grid)
   constexpr int EPL = Lane<Bk>::EPL;
@@ -646,14 +646,26 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
     const bool mrows = cnt.nmseg <= HELD_MROWS;
     const MSeg* msegs_g = (const MSeg*)(greg + CL.multi);
     // snapshot rows of this stream: row (t, i) at (t * W + i) * d, through a buffer resource (base in scalar
-    // registers, 32-bit lane offsets: the held rows leave few vector registers)
+    // registers, 32-bit lane offsets: the held rows leave few vector registers); SB: bfloat16 rows (each float
+    // rounded to nearest even), 8 bytes per lane instead of 16
+    constexpr uint32_t SES = SB ? 2u : 4u;  // bytes per snapshot element
     __amdgpu_buffer_rsrc_t rsnap;
     if constexpr (SNAP)
-      rsnap = __builtin_amdgcn_make_buffer_rsrc((void*)((Bk*)a.snap + (long long)st * D.T * D.W * D.d), (short)0,
-                                                (int)(uint32_t)((unsigned long long)D.T * D.W * D.d * sizeof(Bk)),
+      rsnap = __builtin_amdgcn_make_buffer_rsrc((void*)((char*)a.snap + (long long)st * D.T * D.W * D.d * SES),
+                                                (short)0, (int)(uint32_t)((unsigned long long)D.T * D.W * D.d * SES),
                                                 BUF_RSRC_WORD3);
     auto snap_off = [&](int t, int i) -> uint32_t {
-      return (uint32_t)((((uint32_t)(t0 + t) * (uint32_t)W + (uint32_t)i) * (uint32_t)D.d + (uint32_t)mycol) * 4u);
+      return (uint32_t)((((uint32_t)(t0 + t) * (uint32_t)W + (uint32_t)i) * (uint32_t)D.d + (uint32_t)mycol) * SES);
+    };
+    auto snap_store = [&](uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3, uint32_t off) {
+      if constexpr (SB) {
+        const uint32_t lo = (uint32_t)f_to_bf16(__uint_as_float(x0)) | ((uint32_t)f_to_bf16(__uint_as_float(x1)) << 16);
+        const uint32_t hi = (uint32_t)f_to_bf16(__uint_as_float(x2)) | ((uint32_t)f_to_bf16(__uint_as_float(x3)) << 16);
+        typedef unsigned int u32x2_t __attribute__((__vector_size__(2 * sizeof(unsigned int))));
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{lo, hi}, rsnap, (int)off, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b128(w16_t{x0, x1, x2, x3}, rsnap, (int)off, 0, 0);
+      }
     };
     if (act) {
       const float4 dg = *(const float4*)(sD + gt * COLS + q * EPL);
@@ -663,9 +675,7 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
         if (FULL || u < tpw) {
           const int code = wl[u];
           if (code == -2) {  // the slot's only event: own token, own weight
-            if constexpr (SNAP)
-              __builtin_amdgcn_raw_buffer_store_b128(w16_t{row[u].x, row[u].y, row[u].z, row[u].w}, rsnap,
-                                                     (int)snap_off(gt, part * tpw + u), 0, 0);
+            if constexpr (SNAP) snap_store(row[u].x, row[u].y, row[u].z, row[u].w, snap_off(gt, part * tpw + u));
             float m[EPL];
             Lane<Bk>::unpack(row[u], m);
             const Pair p = pw[u];
@@ -684,9 +694,8 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
                 const Ev x = mev[e];
                 const int tk = SNAP ? (x.tok & 0xFFFF) : x.tok;
                 if constexpr (SNAP)
-                  __builtin_amdgcn_raw_buffer_store_b128(
-                      w16_t{__float_as_uint(m[0]), __float_as_uint(m[1]), __float_as_uint(m[2]), __float_as_uint(m[3])},
-                      rsnap, (int)snap_off(tk, x.tok >> 16), 0, 0);
+                  snap_store(__float_as_uint(m[0]), __float_as_uint(m[1]), __float_as_uint(m[2]), __float_as_uint(m[3]),
+                             snap_off(tk, x.tok >> 16));
                 const float al = sA[tk];
 #pragma unroll
                 for (int k = 0; k < EPL; ++k) m[k] = al * m[k] + x.w * sD[tk * COLS + q * EPL + k];
@@ -726,9 +735,8 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
             const int tk = SNAP ? (x.tok & 0xFFFF) : x.tok;
             if constexpr (SNAP)
               if (valid)
-                __builtin_amdgcn_raw_buffer_store_b128(
-                    w16_t{__float_as_uint(m[0]), __float_as_uint(m[1]), __float_as_uint(m[2]), __float_as_uint(m[3])},
-                    rsnap, (int)snap_off(tk, x.tok >> 16), 0, 0);
+                snap_store(__float_as_uint(m[0]), __float_as_uint(m[1]), __float_as_uint(m[2]), __float_as_uint(m[3]),
+                           snap_off(tk, x.tok >> 16));
             const float al = sA[tk];
             const float4 dd = *(const float4*)(sD + tk * COLS + q * EPL);
             m[0] = al * m[0] + x.w * dd.x; m[1] = al * m[1] + x.w * dd.y;
@@ -1197,7 +1205,9 @@ static hipError_t launch_loop_t(const Dims& D, const LoopArgs& a, hipStream_t st
         (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(LOOP_NT), lds, st, D, a, nslices);
       };
-      if (a.snap) {
+      if (a.snap && a.snap_bf16) {
+        if (full) go(loop_held_kernel<A, Bk, true, true, true>); else go(loop_held_kernel<A, Bk, false, true, true>);
+      } else if (a.snap) {
         if (full) go(loop_held_kernel<A, Bk, true, true>); else go(loop_held_kernel<A, Bk, false, true>);
       } else {
         if (full) go(loop_held_kernel<A, Bk, true, false>); else go(loop_held_kernel<A, Bk, false, false>);

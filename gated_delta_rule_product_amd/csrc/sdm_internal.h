@@ -273,6 +273,7 @@ struct LoopArgs {
   const int32_t* abort;   // if not NULL and *abort != 0: do nothing (shared-bank conflict)
   void* snap;             // if not NULL: [S][T][W][d] bank dtype, the row of every write event before it (the
                           // held-row or the segmented loop writes it; needs PlanArgs::evcode)
+  int snap_bf16;          // the snapshot in bfloat16 (float32 bank, held-row loop only), rounded to nearest even
 };
 hipError_t launch_loop(const Dims& D, const LoopArgs& a, hipStream_t st);
 // True if launch_loop runs the held-row variant (which reads last-event codes, not slot segments).
@@ -291,6 +292,7 @@ struct BwdArgs {
   const void* alpha; const void* beta; const void* values; const void* gout;      // activation dtype
   void* bank;             // [S][rows][ld] bank dtype: after the forward on entry, before it on return
   const void* snap;       // [S][T][W][d] bank dtype
+  int snap_bf16;          // the snapshot holds bfloat16 rows (a float32 bank restored from them)
   float* gbank;           // [S][rows][ld]: gradient w.r.t. the bank after the call in, before the call out
   float* gwkeys; float* grq; float* gvalues; float* galpha; float* gbeta; float* gsub;
   float* part; float* ds; float* sgpart;  // workspace

@@ -91,7 +91,9 @@ typedef struct {
                                HBM channels evenly when rows are gathered in column slices. */
   int32_t shared_bank;      /* sdm_write_read only (0 elsewhere): 1 = the B streams of a head share one bank,
                                bank [H, bank_rows, d], and must address disjoint slots (see sdm_shared_bank_check) */
-  int32_t reserved;         /* 0 */
+  int32_t snapshot_dtype;   /* read by sdm_write_read_save and sdm_write_read_backward only: 0 = the backward
+                               snapshot in the bank dtype, SDM_BF16 = in bfloat16 (on a float32 bank: half the
+                               bytes; each row rounded to nearest even; on a bfloat16 bank the same as 0) */
 } sdm_config;
 
 enum { SDM_OP_TOPK = 0, SDM_OP_WRITE_READ = 1, SDM_OP_DECODE = 2, SDM_OP_BACKWARD = 3 };

@@ -243,3 +243,65 @@ def test_training_step_graph_replay_equals_eager():
         assert torch.equal(bank, bank0), f"replay {r}: bank not restored"
         step()  # eager work between replays
         torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ bfloat16 snapshot of a float32 bank
+SNAP_CASES = [
+    ("tiny", synth.WORKLOADS["tiny_1k"].with_(tokens=96, batch=2, heads=2, chunk_size=32), True),
+    ("collide", synth.Shape(1, 64, 2, (8, 8), 4, 32, 16, 16, 16, name="collide"), True),
+    ("bf16_act", synth.Shape(2, 48, 2, (16, 16), 8, 64, 8, 8, 16, "bf16", "f32", name="bf16a"), False),
+]
+
+
+@pytest.mark.parametrize("name,s,bank_grad", SNAP_CASES, ids=[c[0] for c in SNAP_CASES])
+def test_bf16_snapshot(name, s, bank_grad):
+    """CHANGELOG 2.0.0, "New" (bf16 snapshots on a float32 bank): the saving forward with a bfloat16 snapshot
+    equals the float32 snapshot's forward bit for bit, its snapshot is that snapshot rounded to nearest even, the
+    backward matches the oracle's bfloat16-snapshot backward, and the bank comes back with exactly the rows the
+    forward wrote rounded to bfloat16 (it is restored from the rounded rows)."""
+    x = synth.make_inputs(s, seed=51)
+    dout, dbank = _upstream(s, 52, bank_grad)
+    at = TORCH_DT[s.act]
+    t = {k: to_dev(x[k], at) for k in ("wkeys", "rq", "values", "alpha", "beta", "subkeys")}
+    kw = dict(widths=s.widths, num_writes=s.num_writes, num_reads=s.num_reads, chunk_size=s.chunk_size)
+    bank0 = to_dev(x["bank"], torch.float32)
+    b_none, b_q = bank0.clone(), bank0.clone()
+    o1, w1, _, snap_none = binding.sdm_write_read_save(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"],
+                                                       t["subkeys"], b_none, want_index=True, **kw)
+    o2, w2, _, snap_q = binding.sdm_write_read_save(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"],
+                                                    t["subkeys"], b_q, want_index=True, snapshot_quant="bf16", **kw)
+    torch.cuda.synchronize()
+    assert snap_q.dtype == torch.bfloat16
+    assert torch.equal(o1, o2) and torch.equal(b_none, b_q) and torch.equal(w1, w2)
+    assert torch.equal(snap_q, snap_none.to(torch.bfloat16))
+    gbank = None
+    if dbank is not None:
+        gbank = to_dev(dbank, torch.float32)
+    g = binding.sdm_write_read_backward(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"], t["subkeys"], b_q,
+                                        snap_q, to_dev(dout, at), gbank, snapshot_quant="bf16", **kw)
+    torch.cuda.synchronize()
+    written = torch.zeros((s.batch, s.heads, s.rows), dtype=torch.bool, device=DEV)
+    for b in range(s.batch):
+        for h in range(s.heads):
+            written[b, h, w1[b, :, h].reshape(-1).long()] = True
+    expect = torch.where(written[..., None], bank0.to(torch.bfloat16).float(), bank0)
+    assert torch.equal(b_q, expect), "the bank is not the rounded restore"
+    ref = oracle.write_read_backward(x["wkeys"], x["rq"], x["values"], x["alpha"], x["beta"], x["subkeys"],
+                                     x["bank"], dout, dbank, s.widths, s.num_writes, s.num_reads, snap_bf16=True)
+    check(s, {k: v.cpu().numpy() for k, v in g.items()}, ref, _tol(s))
+
+
+def test_bf16_snapshot_refused_without_a_native_route():
+    """A bfloat16 snapshot of a float32 bank needs the held-row loop (chunk 7 is not a power of two): refused
+    before any work, like the pages' training calls that have no native route."""
+    s = synth.WORKLOADS["tiny_1k"].with_(tokens=50, batch=1, heads=2, chunk_size=7)
+    x = synth.make_inputs(s, seed=1)
+    t = {k: to_dev(x[k], torch.float32) for k in ("wkeys", "rq", "values", "alpha", "beta", "subkeys")}
+    bank = to_dev(x["bank"], torch.float32)
+    bank0 = bank.clone()
+    with pytest.raises(binding.UnsupportedConfigurationError, match="no native route"):
+        binding.sdm_write_read_save(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"], t["subkeys"], bank,
+                                    widths=s.widths, num_writes=s.num_writes, num_reads=s.num_reads,
+                                    chunk_size=s.chunk_size, snapshot_quant="bf16")
+    torch.cuda.synchronize()
+    assert torch.equal(bank, bank0)
