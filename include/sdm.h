@@ -125,11 +125,15 @@ sdm_status sdm_write_read(const sdm_config* cfg, const void* write_keys, const v
                           size_t workspace_bytes, void* stream);
 
 /* Training forward (CHANGELOG 2.0.0: training saves a backward snapshot; "Known limitations": the backward restores
- * the bank in place). sdm_write_read, plus `snapshot` [B, H, T, W, d] in the bank dtype (dense rows, caller-owned):
+ * the bank in place). sdm_write_read, plus `snapshot` [B, H, T, W, d] in the bank dtype, or bfloat16 with
+ * cfg.snapshot_dtype = SDM_BF16 (CHANGELOG 2.0.0, "New": bf16 snapshots on a float32 bank) (dense rows, caller-owned):
  * row (b, h, t, i) receives the row of slot write_idx[b, t, h, i] as it was just before token t's write (i in top-k
  * order, best first). The workspace is sdm_write_read's (SDM_OP_WRITE_READ). Refused (SDM_ERR_RANGE) with
  * shared_bank, or when B * H * T * W reaches 2^31 rows (CHANGELOG 2.0.0, "New": a snapshot of 2^31 rows is refused
- * before any work). Results equal sdm_write_read's up to rounding (this call always runs the segmented chunk loop). */
+ * before any work). A bfloat16 snapshot of a float32 bank needs the held-row loop (chunk a power of two in [8, 128],
+ * at most 32 terms per lane group) and num_writes, num_reads <= 128, else SDM_ERR_RANGE before any work; its rows are
+ * the float32 rows rounded to nearest even, and out and the bank equal the float32 snapshot's bit for bit. Results
+ * equal sdm_write_read's up to rounding. */
 sdm_status sdm_write_read_save(const sdm_config* cfg, const void* write_keys, const void* read_queries,
                                const void* values, const void* forget_gate, const void* input_gate,
                                const void* subkeys, void* bank, void* out, void* snapshot, int32_t* write_idx,
@@ -138,8 +142,11 @@ sdm_status sdm_write_read_save(const sdm_config* cfg, const void* write_keys, co
 /* Deterministic backward of the write/read (CHANGELOG 2.0.0, "Deterministic": every gradient bitwise repeatable;
  * "New": exact product-key top-k with a deterministic sparse backward; "Known limitations": the first backward
  * restores the bank in place). Inputs are the forward's (same cfg, keys, queries, values, gates, sub-keys), `bank`
- * as the forward left it, the forward's `snapshot`, and grad_out [B, T, H, d] (act dtype). On return `bank` is the
- * bank before the forward, bit for bit. grad_bank (float32, [B, H, bank_rows, bank_row_stride], the bank's row
+ * as the forward left it, the forward's `snapshot` (same cfg.snapshot_dtype), and grad_out [B, T, H, d] (act dtype).
+ * On return `bank` is the bank before the forward, bit for bit; with a bfloat16 snapshot of a float32 bank, the rows
+ * the forward wrote come back rounded to bfloat16 (restored from the snapshot), and every row the backward reads
+ * from the snapshot or the restored bank is the rounded one (it enters the key, query, gate and sub-key gradients,
+ * not grad_values or grad_bank). grad_bank (float32, [B, H, bank_rows, bank_row_stride], the bank's row
  * layout) holds the gradient w.r.t. the bank after the forward on entry (zeros if none) and the gradient w.r.t. the
  * bank before it on return. Written (float32, overwritten): grad_write_keys, grad_read_queries [B, T, H, F*dk],
  * grad_values [B, T, H, d], grad_forget_gate, grad_input_gate [B, T, H], grad_subkeys [H, sum n_f, dk] (summed over
