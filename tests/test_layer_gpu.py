@@ -141,3 +141,25 @@ def test_layer_65k_width_2048_sampled():
         assert np.array_equal(got[ids].reshape(-1, 1, H, k)[rows], rid), f"{ids} differ on sampled rows"
     r = dense_ok(got["y"].reshape(-1, Dm)[rows], got["o"].reshape(-1, H * d)[rows], x["w_out"])
     assert r <= 1.0, f"y: error {r} x the bound"
+
+
+def test_layer_padded_bank_pitch():
+    """A bank whose rows are padded (the pitch the bench uses for 4 KiB rows): the same bits as a dense bank, and
+    the padding never written."""
+    s, Dm = CASES["small"]
+    x = synth.make_layer_inputs(s, Dm, seed=6)
+    args = [to_dev(x["x"], torch.bfloat16), to_dev(x["w_in"], torch.bfloat16), to_dev(x["a_log"], torch.float32),
+            to_dev(x["dt_bias"], torch.float32), to_dev(x["w_out"], torch.bfloat16),
+            to_dev(x["subkeys"], torch.bfloat16)]
+    kw = dict(heads=s.heads, widths=s.widths, num_writes=s.num_writes, num_reads=s.num_reads,
+              chunk_size=s.chunk_size)
+    dense = to_dev(x["bank"], torch.float32)
+    pitch = s.head_dim + 32
+    buf = torch.full((s.batch, s.heads, s.rows, pitch), 1234.5, dtype=torch.float32, device=DEV)
+    padded = buf[..., :s.head_dim]
+    padded.copy_(dense)
+    y1, _, _ = binding.sdm_layer_forward(*args, dense, **kw)
+    y2, _, _ = binding.sdm_layer_forward(*args, padded, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(dense, padded)
+    assert bool((buf[..., s.head_dim:] == 1234.5).all())
