@@ -182,7 +182,7 @@ __device__ void wave_select_sorted(const uint64_t (&key)[N], int k, uint64_t* sc
 // sub-key (NPL per lane, lane l owns l + 64 j) and its top k_p by wave selection, into fsc/fid[f * kpmax + p].
 // wave_merge_topk: the candidate tuples of `cand` (CPL per lane) with float32 slot scores summed left to right,
 // selected by (score, position sum, candidate index); writes ids[r] (slot ids, best first) and wts[r] (softmax of
-// the k slot scores: fp64 exponentials, per-lane partial sums in a fixed order and a fixed butterfly) to LDS.
+// the k slot scores: fp64 exponentials, per-lane partial sums in a fixed order, then a fixed cross-lane order) to LDS.
 // scratch and sorted: the calling wave's selection buffers.
 
 // One block of factor f's coordinates, loaded ahead of its use: PB pieces of 16 bytes (VEC coordinates) of each of
@@ -257,6 +257,30 @@ __device__ void wave_factor_topk(const Dims& D, const TopkPlan& P, int f, const 
 
 constexpr int MERGE_RB = 32;  // rank-placement batch of the merge's selection (its scratch: >= k + MERGE_RB)
 
+// A double moved between lanes by a DPP control (two 32-bit moves; all lanes active).
+template <int CTRL> __device__ __forceinline__ double dpp_d(double x) {
+  const uint64_t u = __double_as_longlong(x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xf, 0xf, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xf, 0xf, false);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+// Lane l's double, as a wave-uniform value (constant l).
+template <int L> __device__ __forceinline__ double readlane_d(double x) {
+  const uint64_t u = __double_as_longlong(x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, L);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), L);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+// The sum of the 64 lanes' values in a fixed order, the same on every lane: inside each row of 16 lanes by DPP
+// moves (pairs, quads, then rotations by 4 and 8), then the row sums of lanes 0, 16, 32 and 48 in row order.
+__device__ __forceinline__ double wave_sum_d(double x) {
+  x += dpp_d<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  x += dpp_d<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  x += dpp_d<0x124>(x);  // row_ror:4
+  x += dpp_d<0x128>(x);  // row_ror:8
+  return ((readlane_d<0>(x) + readlane_d<16>(x)) + readlane_d<32>(x)) + readlane_d<48>(x);
+}
+
 template <int CPL>
 __device__ void wave_merge_topk(const Dims& D, const TopkPlan& P, const uint64_t* cand, const float* fsc,
                                 const uint16_t* fid, uint64_t* scratch, uint64_t* sorted, int32_t* ids, float* wts) {
@@ -308,9 +332,7 @@ __device__ void wave_merge_topk(const Dims& D, const TopkPlan& P, const uint64_t
       zpart += ex[u];
     }
   }
-  double z = zpart;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) z += __shfl_xor(z, o);
+  const double z = wave_sum_d(zpart);
 #pragma unroll
   for (int u = 0; u < RPL; ++u) {
     const int r = lane + 64 * u;
