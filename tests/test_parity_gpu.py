@@ -793,3 +793,36 @@ def test_large_1m_full_size():
     rid, _ = oracle.topk(x["wkeys"][:, ts], x["subkeys"], s.widths, s.num_writes)
     assert np.array_equal(to_np(widx[:, ts]), rid), "sampled write ids differ"
     print("full-size large_1m errors", e_out, e_bank, flush=True)
+
+
+@pytest.mark.parametrize("kind", ["ternary", "zero_query"])
+def test_decode_exact_ties(kind):
+    """Decode steps whose slot scores tie exactly (ternary queries and sub-keys; or all-zero queries, where every
+    slot scores 0 and the order is by position sums): the one-launch step's merge (radix select started below the
+    high bits shared by the keys it can select, tie branch on the low halves) must give the oracle's ids."""
+    s = synth.WORKLOADS["decode_b128"].with_(batch=8)
+    rng = np.random.default_rng(21 if kind == "ternary" else 22)
+    F = len(s.widths)
+    sub_np = rng.integers(-1, 2, (s.heads, sum(s.widths), s.subkey_dim)).astype(np.float32)
+    sub = to_dev(sub_np, torch.float32)
+    bank_np = synth.make_bank(s)
+    bank = to_dev(bank_np, torch.float32)
+    shape = (s.batch, 1, s.heads, F * s.subkey_dim)
+    if kind == "ternary":
+        wk = rng.integers(-1, 2, shape).astype(np.float32)
+        rq = rng.integers(-1, 2, shape).astype(np.float32)
+    else:
+        wk = np.zeros(shape, np.float32)
+        rq = np.zeros(shape, np.float32)
+    x = synth.make_step_inputs(s, seed=5, step=1)
+    x["wkeys"], x["rq"] = wk, rq
+    t = {k: to_dev(v, torch.float32) for k, v in x.items()}
+    o, w, r, b = binding.sdm_decode_step(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"], sub, bank,
+                                         widths=s.widths, num_writes=s.num_writes, num_reads=s.num_reads,
+                                         want_index=True)
+    torch.cuda.synchronize()
+    ref = oracle.write_read(x["wkeys"], x["rq"], x["values"], x["alpha"], x["beta"], sub_np, bank_np, s.widths,
+                            s.num_writes, s.num_reads)
+    assert np.array_equal(w.cpu().numpy(), ref["widx"]) and np.array_equal(r.cpu().numpy(), ref["ridx"])
+    assert rowwise_rel(to_np(o), ref["out"]) <= RTOL["f32"]
+    assert rowwise_rel(to_np(b), ref["bank"]) <= RTOL["f32"]
