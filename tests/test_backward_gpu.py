@@ -253,19 +253,38 @@ SNAP_CASES = [
 ]
 
 
-@pytest.mark.parametrize("name,s,bank_grad", SNAP_CASES, ids=[c[0] for c in SNAP_CASES])
-def test_bf16_snapshot(name, s, bank_grad):
-    """CHANGELOG 2.0.0, "New" (bf16 snapshots on a float32 bank): the saving forward with a bfloat16 snapshot
-    equals the float32 snapshot's forward bit for bit, its snapshot is that snapshot rounded to nearest even, the
-    backward matches the oracle's bfloat16-snapshot backward, and the bank comes back with exactly the rows the
-    forward wrote rounded to bfloat16 (it is restored from the rounded rows)."""
+def _padded(arr, pitch):
+    """A float32 bank view [B, H, rows, d] on rows `pitch` elements apart (pitch None: dense)."""
+    if pitch is None:
+        return to_dev(arr, torch.float32)
+    B, H, rows, d = arr.shape
+    v = torch.zeros((B, H, rows, pitch), dtype=torch.float32, device=DEV)[..., :d]
+    v.copy_(to_dev(arr, torch.float32))
+    return v
+
+
+def _tol_bf16_snapshot(s):
+    """Tolerances with a bfloat16 snapshot of a float32 bank: d values and d bank read no row and keep the float32
+    ones; the gradients that read rows (keys, queries, sub-keys, gates) get 1e-2. Derivation: the GPU's pre-write
+    rows come from the chunked closed form and the oracle's from the per-token recurrence, about one float32 ulp
+    apart; where such a pair straddles a bfloat16 rounding boundary the two snapshots differ by one bfloat16 ulp
+    (2^-8 relative) in that element, which the gate gradient's difference of two sums (sum <g, P> - beta <D, r>)
+    can amplify. Measured at full layer_65k: 2.3e-3 for the forget gate (1.6e-5 with a float32 snapshot on the same
+    inputs), 7.9e-4 for the read queries."""
+    t = _tol(s)
+    for k in ("write_keys", "read_queries", "subkeys", "forget_gate", "input_gate"):
+        t[k] = max(t[k], 1e-2)
+    return t
+
+
+def _bf16_snapshot_case(s, bank_grad, pitch=None):
     x = synth.make_inputs(s, seed=51)
     dout, dbank = _upstream(s, 52, bank_grad)
     at = TORCH_DT[s.act]
     t = {k: to_dev(x[k], at) for k in ("wkeys", "rq", "values", "alpha", "beta", "subkeys")}
     kw = dict(widths=s.widths, num_writes=s.num_writes, num_reads=s.num_reads, chunk_size=s.chunk_size)
-    bank0 = to_dev(x["bank"], torch.float32)
-    b_none, b_q = bank0.clone(), bank0.clone()
+    bank0 = _padded(x["bank"], pitch)
+    b_none, b_q = _padded(x["bank"], pitch), _padded(x["bank"], pitch)
     o1, w1, _, snap_none = binding.sdm_write_read_save(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"],
                                                        t["subkeys"], b_none, want_index=True, **kw)
     o2, w2, _, snap_q = binding.sdm_write_read_save(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"],
@@ -274,9 +293,11 @@ def test_bf16_snapshot(name, s, bank_grad):
     assert snap_q.dtype == torch.bfloat16
     assert torch.equal(o1, o2) and torch.equal(b_none, b_q) and torch.equal(w1, w2)
     assert torch.equal(snap_q, snap_none.to(torch.bfloat16))
+    del snap_none
     gbank = None
     if dbank is not None:
-        gbank = to_dev(dbank, torch.float32)
+        gbank = torch.zeros((s.batch, s.heads, s.rows, b_q.stride(2)), dtype=torch.float32, device=DEV)[..., :s.head_dim]
+        gbank.copy_(to_dev(dbank, torch.float32))
     g = binding.sdm_write_read_backward(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"], t["subkeys"], b_q,
                                         snap_q, to_dev(dout, at), gbank, snapshot_quant="bf16", **kw)
     torch.cuda.synchronize()
@@ -288,7 +309,23 @@ def test_bf16_snapshot(name, s, bank_grad):
     assert torch.equal(b_q, expect), "the bank is not the rounded restore"
     ref = oracle.write_read_backward(x["wkeys"], x["rq"], x["values"], x["alpha"], x["beta"], x["subkeys"],
                                      x["bank"], dout, dbank, s.widths, s.num_writes, s.num_reads, snap_bf16=True)
-    check(s, {k: v.cpu().numpy() for k, v in g.items()}, ref, _tol(s))
+    check(s, {k: v.cpu().numpy() for k, v in g.items()}, ref, _tol_bf16_snapshot(s))
+
+
+@pytest.mark.parametrize("name,s,bank_grad", SNAP_CASES, ids=[c[0] for c in SNAP_CASES])
+def test_bf16_snapshot(name, s, bank_grad):
+    """CHANGELOG 2.0.0, "New" (bf16 snapshots on a float32 bank): the saving forward with a bfloat16 snapshot
+    equals the float32 snapshot's forward bit for bit, its snapshot is that snapshot rounded to nearest even, the
+    backward matches the oracle's bfloat16-snapshot backward, and the bank comes back with exactly the rows the
+    forward wrote rounded to bfloat16 (it is restored from the rounded rows)."""
+    _bf16_snapshot_case(s, bank_grad)
+
+
+def test_bf16_snapshot_layer_65k_full_size():
+    """The same at the full layer_65k workload (2 GiB bfloat16 snapshot, padded row pitch, 8-column sweep)."""
+    s = synth.WORKLOADS["layer_65k"]
+    print("full-size bf16 snapshot", flush=True)
+    _bf16_snapshot_case(s, True, pitch=binding.bank_pitch(s.head_dim, torch.float32))
 
 
 def test_bf16_snapshot_refused_without_a_native_route():
