@@ -23,6 +23,7 @@ STATUS_NAMES = {0: "SDM_OK", 1: "SDM_ERR_DTYPE", 2: "SDM_ERR_RANGE", 3: "SDM_ERR
                 5: "SDM_ERR_LAYOUT", 6: "SDM_ERR_WORKSPACE", 7: "SDM_ERR_DEVICE", 8: "SDM_ERR_HIP", 9: "SDM_ERR_NULL"}
 SDM_F32, SDM_BF16, SDM_F16 = 0, 1, 2
 SDM_OP_TOPK, SDM_OP_WRITE_READ, SDM_OP_DECODE, SDM_OP_BACKWARD = 0, 1, 2, 3
+SCORING = {"auto": 0, "direct": 1, "filtered": 2}
 
 
 class UnsupportedConfigurationError(ValueError):
@@ -40,7 +41,7 @@ class SdmConfig(ctypes.Structure):
         ("head_dim", ctypes.c_int32), ("num_writes", ctypes.c_int32), ("num_reads", ctypes.c_int32),
         ("chunk_size", ctypes.c_int32), ("act_dtype", ctypes.c_int32), ("bank_dtype", ctypes.c_int32),
         ("bank_rows", ctypes.c_int64), ("bank_row_stride", ctypes.c_int64),
-        ("shared_bank", ctypes.c_int32), ("snapshot_dtype", ctypes.c_int32),
+        ("shared_bank", ctypes.c_int32), ("snapshot_dtype", ctypes.c_int32), ("topk_scoring", ctypes.c_int32),
     ]
 
 
@@ -50,7 +51,7 @@ class SdmLayerConfig(ctypes.Structure):
 
 def make_config(batch, tokens, heads, widths, subkey_dim, head_dim=1, num_writes=1, num_reads=1, chunk_size=1,
                 act_dtype=SDM_F32, bank_dtype=SDM_F32, bank_rows=None, bank_row_stride=0,
-                shared_bank=False, snapshot_dtype=0) -> SdmConfig:
+                shared_bank=False, snapshot_dtype=0, topk_scoring=0) -> SdmConfig:
     c = SdmConfig()
     c.batch, c.tokens, c.heads = int(batch), int(tokens), int(heads)
     c.num_factors = len(widths)
@@ -66,6 +67,7 @@ def make_config(batch, tokens, heads, widths, subkey_dim, head_dim=1, num_writes
     c.bank_row_stride = int(bank_row_stride)
     c.shared_bank = 1 if shared_bank else 0
     c.snapshot_dtype = int(snapshot_dtype)
+    c.topk_scoring = SCORING[topk_scoring] if isinstance(topk_scoring, str) else int(topk_scoring)
     return c
 
 
@@ -227,14 +229,15 @@ def _workspace(nbytes: int, device, workspace=None):
 
 
 def topk_product_keys(queries: torch.Tensor, subkeys: torch.Tensor, widths, k: int, want_scores=True,
-                      workspace=None):
-    """queries [B, T, H, F*dk], subkeys [H, sum n_f, dk] (same dtype) -> (ids int32 [B,T,H,k], scores f32 or None)."""
+                      workspace=None, scoring="auto"):
+    """queries [B, T, H, F*dk], subkeys [H, sum n_f, dk] (same dtype) -> (ids int32 [B,T,H,k], scores f32 or None).
+    scoring: "auto", "direct" or "filtered" (the factor-scoring kernel; the results are the same)."""
     B, T, H, Fdk = queries.shape
     F = len(widths)
     dk = Fdk // F
     _need(queries, "queries")
     _need(subkeys, "subkeys", (H, sum(widths), dk), queries.dtype)
-    cfg = make_config(B, T, H, widths, dk, act_dtype=_dt(queries))
+    cfg = make_config(B, T, H, widths, dk, act_dtype=_dt(queries), topk_scoring=scoring)
     ws = _workspace(workspace_size(cfg, SDM_OP_TOPK, k), queries.device, workspace)
     ids = torch.empty((B, T, H, k), dtype=torch.int32, device=queries.device)
     scores = torch.empty((B, T, H, k), dtype=torch.float32, device=queries.device) if want_scores else None

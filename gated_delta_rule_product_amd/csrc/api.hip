@@ -120,6 +120,9 @@ sdm_status validate(const sdm_config* cfg, int op, int k, Dims* D, TopkPlan* pw,
                 cfg->subkey_dim, MAX_FDK);
   D->B = cfg->batch; D->T = cfg->tokens; D->H = cfg->heads; D->F = F; D->dk = cfg->subkey_dim;
   D->act = act; D->bank = bank; D->N = N; D->S = cfg->batch * cfg->heads;
+  if (cfg->topk_scoring < SDM_SCORING_AUTO || cfg->topk_scoring > SDM_SCORING_FILTERED)
+    return fail(SDM_ERR_RANGE, "topk_scoring = %d (0 auto, 1 direct, 2 filtered)", cfg->topk_scoring);
+  D->scoring = cfg->topk_scoring;
   if (op == SDM_OP_TOPK) return make_plan(*D, k, "k", pw);
   if (cfg->shared_bank != 0 && cfg->shared_bank != 1)
     return fail(SDM_ERR_RANGE, "shared_bank = %d must be 0 or 1", cfg->shared_bank);

@@ -37,6 +37,7 @@ struct Dims {
   int nch;              // chunks per stream
   int S;                // streams = B * H
   int shared;           // the B streams of a head share one bank (bank [H, rows, ld])
+  int scoring;          // SDM_SCORING_*: which factor-scoring kernel the batched top-k uses
 };
 
 // Bank index of stream st = b * H + h: st itself, or h with a shared bank.

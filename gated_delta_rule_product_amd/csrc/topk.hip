@@ -545,11 +545,12 @@ static bool launch_topk2_npl(const Dims& D, const TopkArgs& a, hipStream_t st, i
 }
 
 // The filtered (MFMA) scoring serves bf16 activations with factor widths that are multiples of 16 and
-// dk in {32, 64, 96, 128}, when a factor has at least 512 sub-keys: below that the direct fp64 chain over every
-// sub-key costs no more than the filter's extra selection and re-scoring (measured: 256 and 64 sub-keys per factor
-// are as fast or faster direct; 1024 sub-keys are about twice as fast filtered). SDM_TOPK_SCORING=filtered or
-// =direct in the environment overrides the choice (tests exercise both on the same inputs).
+// dk in {32, 64, 96, 128}. By default (SDM_SCORING_AUTO) it runs when a factor has at least 512 sub-keys: below that
+// the direct fp64 chain over every sub-key costs no more than the filter's extra selection and re-scoring (measured:
+// 256 and 64 sub-keys per factor are as fast or faster direct; 1024 sub-keys are about twice as fast filtered).
+// The config's topk_scoring forces either kernel; both return the same ids and scores.
 static bool topk_filtered(const Dims& D, const TopkArgs& a) {
+  if (D.scoring == SDM_SCORING_DIRECT) return false;
   if (D.act != SDM_BF16 || a.snorm == nullptr) return false;
   if (D.dk % 32 != 0 || D.dk > 128) return false;
   int nmax = 0;
@@ -559,9 +560,7 @@ static bool topk_filtered(const Dims& D, const TopkArgs& a) {
   }
   for (int q = 0; q < a.nkinds; ++q)
     if (((uintptr_t)a.queries[q]) % 16 != 0) return false;
-  const char* env = getenv("SDM_TOPK_SCORING");
-  if (env && strcmp(env, "direct") == 0) return false;
-  if (env && strcmp(env, "filtered") == 0) return true;
+  if (D.scoring == SDM_SCORING_FILTERED) return true;
   return nmax >= 512;
 }
 

@@ -26,7 +26,7 @@
  *   read           out = sum_i rho_i M[R_i], after the update
  * alpha (forget gate) and beta (input gate) are one scalar each per (token, head), given by the caller.
  *
- * Layouts (row-major, contiguous, no strides):
+ * Layouts (row-major; every tensor is dense except the bank, whose rows may be padded to bank_row_stride):
  *   queries / write_keys / read_queries  [B, T, H, F*dk]   act dtype; factor f uses columns [f*dk, (f+1)*dk)
  *   subkeys                              [H, sum_f n_f, dk] act dtype; factor tables stacked in factor order
  *   values, out                          [B, T, H, d]      act dtype
@@ -87,14 +87,26 @@ typedef struct {
   int32_t bank_dtype;       /* sdm_dtype of the bank: F32 or BF16 */
   int64_t bank_rows;        /* rows per stream in the bank buffer, >= N */
   int64_t bank_row_stride;  /* elements from one bank row to the next (0: head_dim); >= head_dim, 16-byte multiple.
-                               A pitch that is not a power of two (e.g. head_dim + 128 bytes) spreads the rows over
-                               HBM channels evenly when rows are gathered in column slices. */
+                               Performance note: with a row size that is a multiple of 512 bytes, a dense pitch puts
+                               the same column slice of every row in one group of HBM channels, and the chunk loop's
+                               row gathers then run about 20 % slower (65,536 slots x 1024 float32 columns: 3.3 ms
+                               dense vs 2.6 ms per call). A pitch of head_dim + 128 bytes (an odd multiple of
+                               128 bytes past the row) spreads the rows over all channels; the library's bandwidth
+                               figures are quoted with it. */
   int32_t shared_bank;      /* sdm_write_read only (0 elsewhere): 1 = the B streams of a head share one bank,
                                bank [H, bank_rows, d], and must address disjoint slots (see sdm_shared_bank_check) */
   int32_t snapshot_dtype;   /* read by sdm_write_read_save and sdm_write_read_backward only: 0 = the backward
                                snapshot in the bank dtype, SDM_BF16 = in bfloat16 (on a float32 bank: half the
                                bytes; each row rounded to nearest even; on a bfloat16 bank the same as 0) */
+  int32_t topk_scoring;     /* factor-scoring kernel of the batched top-k (ids and scores are identical for every
+                               value; only the speed differs): SDM_SCORING_AUTO (0) = the bf16 matrix-core filter
+                               where a factor has >= 512 sub-keys, else the fp64 chain over every sub-key;
+                               SDM_SCORING_DIRECT = the fp64 chain everywhere; SDM_SCORING_FILTERED = the filter
+                               wherever it applies (bf16 activations, factor widths multiples of 16, subkey_dim a
+                               multiple of 32 up to 128, 16-byte aligned queries; not the decode step's top-k) */
 } sdm_config;
+
+enum { SDM_SCORING_AUTO = 0, SDM_SCORING_DIRECT = 1, SDM_SCORING_FILTERED = 2 };
 
 enum { SDM_OP_TOPK = 0, SDM_OP_WRITE_READ = 1, SDM_OP_DECODE = 2, SDM_OP_BACKWARD = 3 };
 

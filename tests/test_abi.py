@@ -78,6 +78,8 @@ def test_workspace_sizes(lib):
     (dict(bank_row_stride=60), B.SDM_ERR_LAYOUT),                          # pitch below head_dim
     (dict(bank_row_stride=66), B.SDM_ERR_LAYOUT),                          # pitch not a 16-byte multiple
     (dict(tokens=-1), B.SDM_ERR_RANGE),
+    (dict(topk_scoring=3), B.SDM_ERR_RANGE),
+    (dict(topk_scoring=-1), B.SDM_ERR_RANGE),
 ])
 def test_refusals(lib, kw, status):
     if kw.get("widths") == (4096, 4096):

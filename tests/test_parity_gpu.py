@@ -80,7 +80,7 @@ def check_parity(s, gpu, ref):
 
 
 # ------------------------------------------------------------------------------------------------ top-k
-def _topk_case(widths, dk, k, act, kind, B=1, T=24, H=2, seed=0):
+def _topk_case(widths, dk, k, act, kind, B=1, T=24, H=2, seed=0, scoring="auto"):
     rng = np.random.default_rng(seed)
     F = len(widths)
     if kind == "ternary":
@@ -95,7 +95,8 @@ def _topk_case(widths, dk, k, act, kind, B=1, T=24, H=2, seed=0):
                 sub[:, j] = sub[:, i]
     if act == "bf16":
         q, sub = synth.round_bf16_rne(q), synth.round_bf16_rne(sub)
-    ids, sc = binding.topk_product_keys(to_dev(q, TORCH_DT[act]), to_dev(sub, TORCH_DT[act]), widths, k)
+    ids, sc = binding.topk_product_keys(to_dev(q, TORCH_DT[act]), to_dev(sub, TORCH_DT[act]), widths, k,
+                                        scoring=scoring)
     torch.cuda.synchronize()
     rid, rsc = oracle.topk(q, sub, widths, k)
     assert np.array_equal(ids.cpu().numpy(), rid)
@@ -116,28 +117,25 @@ def test_topk_exact(widths, dk, k, kind, act):
                                          ((512, 16), 32, 64), ((1024, 32), 64, 40)])
 @pytest.mark.parametrize("kind", ["random", "ternary", "dup"])
 @pytest.mark.parametrize("scoring", ["filtered", "direct"])
-def test_topk_exact_filtered(widths, dk, k, kind, scoring, monkeypatch):
+def test_topk_exact_filtered(widths, dk, k, kind, scoring):
     """bf16 shapes the MFMA-filtered scoring can serve (widths multiples of 16, dk a multiple of 32 up to 128), with
     each scoring forced: ids and scores bit-exact, including the many exact ties of ternary inputs and duplicated
     sub-keys."""
-    monkeypatch.setenv("SDM_TOPK_SCORING", scoring)
     print(f"topk {scoring} widths={widths} dk={dk} k={k} kind={kind}", flush=True)
-    _topk_case(widths, dk, k, "bf16", kind, T=40)
+    _topk_case(widths, dk, k, "bf16", kind, T=40, scoring=scoring)
 
 
 @pytest.mark.parametrize("name", ["layer_65k", "large_1m"])
-def test_topk_filtered_equals_direct(name, monkeypatch):
+def test_topk_filtered_equals_direct(name):
     """The filtered (MFMA) scoring and the direct fp64 scoring return identical ids and scores at full size."""
     s = synth.WORKLOADS[name]
     x = synth.make_step_inputs(s.with_(tokens=256))
     q = to_dev(x["wkeys"], torch.bfloat16)
     sub = to_dev(synth.make_subkeys(s), torch.bfloat16)
     print(f"topk filtered vs direct, {name} T=256", flush=True)
-    monkeypatch.setenv("SDM_TOPK_SCORING", "filtered")
-    ids_f, sc_f = binding.topk_product_keys(q, sub, s.widths, s.num_writes)
+    ids_f, sc_f = binding.topk_product_keys(q, sub, s.widths, s.num_writes, scoring="filtered")
     torch.cuda.synchronize()
-    monkeypatch.setenv("SDM_TOPK_SCORING", "direct")
-    ids_d, sc_d = binding.topk_product_keys(q, sub, s.widths, s.num_writes)
+    ids_d, sc_d = binding.topk_product_keys(q, sub, s.widths, s.num_writes, scoring="direct")
     torch.cuda.synchronize()
     assert torch.equal(ids_f, ids_d)
     assert torch.equal(sc_f, sc_d)
