@@ -136,6 +136,8 @@ def load():
             lib.sdm_write_read_backward.argtypes = [cfgp] + [_vp] * 17 + [ctypes.c_size_t, _vp]
             lib.sdm_decode_step.restype = ctypes.c_int
             lib.sdm_decode_step.argtypes = [cfgp] + [_vp] * 12 + [ctypes.c_size_t, _vp]
+            lib.sdm_decode_step_noalloc.restype = ctypes.c_int
+            lib.sdm_decode_step_noalloc.argtypes = [cfgp] + [_vp] * 12
             lib.sdm_shared_bank_check.restype = ctypes.c_int
             lib.sdm_shared_bank_check.argtypes = [cfgp, _vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int32), _vp]
             lib.sdm_profile_enable.restype = ctypes.c_int
@@ -478,6 +480,44 @@ def sdm_decode_step(write_keys, read_queries, values, forget_gate, input_gate, s
                                   _ptr(out), _ptr(widx), _ptr(ridx), _ptr(ws), 0 if ws is None else ws.numel(),
                                   _stream(bank_in.device)))
     return out, widx, ridx, bank_out
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20  # SDM_NOALLOC_SCRATCH_BYTES in include/sdm.h
+
+
+def sdm_decode_step_noalloc(write_keys, read_queries, values, forget_gate, input_gate, subkeys, bank_in,
+                            bank_out=None, *, widths, num_writes, num_reads, out, write_idx=None, read_idx=None):
+    """sdm_decode_step without a workspace (the library's per-GPU scratch array instead): for callers that cannot
+    allocate device memory. Every output tensor is the caller's (out [B, 1, H, d]; write_idx / read_idx optional);
+    nothing is allocated here. Returns out."""
+    if bank_out is None:
+        bank_out = bank_in
+    B, T, H, Fdk = write_keys.shape
+    F = len(widths)
+    dk = Fdk // F
+    d = values.shape[-1]
+    act = write_keys.dtype
+    for name, t, shp in (("write_keys", write_keys, (B, T, H, Fdk)), ("read_queries", read_queries, (B, T, H, Fdk)),
+                         ("values", values, (B, T, H, d)), ("forget_gate", forget_gate, (B, T, H)),
+                         ("input_gate", input_gate, (B, T, H)), ("subkeys", subkeys, (H, sum(widths), dk)),
+                         ("out", out, (B, T, H, d))):
+        _need(t, name, shp, act)
+    for name, t, k in (("write_idx", write_idx, num_writes), ("read_idx", read_idx, num_reads)):
+        if t is not None:
+            _need(t, name, (B, T, H, k), torch.int32)
+    if bank_in.dim() != 4 or bank_in.shape[0] != B or bank_in.shape[1] != H or bank_in.shape[3] != d:
+        raise ValueError(f"bank_in has shape {tuple(bank_in.shape)}, expected ({B}, {H}, bank_rows, {d})")
+    ld = _bank_ld(bank_in, "bank_in")
+    if tuple(bank_out.shape) != tuple(bank_in.shape) or bank_out.dtype != bank_in.dtype or \
+            bank_out.stride() != bank_in.stride():
+        raise ValueError("bank_out must have bank_in's shape, dtype and strides")
+    cfg = make_config(B, T, H, widths, dk, d, num_writes, num_reads, 1, _dt(write_keys), _dt(bank_in),
+                      bank_in.shape[2], ld)
+    _check(load().sdm_decode_step_noalloc(ctypes.byref(cfg), _ptr(write_keys), _ptr(read_queries), _ptr(values),
+                                          _ptr(forget_gate), _ptr(input_gate), _ptr(subkeys), _ptr(bank_in),
+                                          _ptr(bank_out), _ptr(out), _ptr(write_idx), _ptr(read_idx),
+                                          _stream(bank_in.device)))
+    return out
 
 
 class DecodeStep:

@@ -671,10 +671,40 @@ sdm_status sdm_shared_bank_check(const sdm_config* cfg, const void* workspace, s
   return ok();
 }
 
-sdm_status sdm_decode_step(const sdm_config* cfg, const void* write_keys, const void* read_queries,
-                           const void* values, const void* forget_gate, const void* input_gate, const void* subkeys,
-                           const void* bank_in, void* bank_out, void* out, int32_t* write_idx, int32_t* read_idx,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+// Scratch of sdm_decode_step_noalloc: one array per device, kept until the process ends. Host code never uses the
+// array's name as an address (it is a host-side stand-in there); it uses the device address that
+// hipGetSymbolAddress returned for the current device.
+static __device__ __align__(256) unsigned char scratch[SDM_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];
+
+// The current device's address of `scratch`, looked up once per device (with that device current).
+sdm_status scratch_address(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SDM_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(SDM_ERR_DEVICE, "device ordinal %d out of range [0, 64)", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(SDM_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return SDM_OK;
+}
+
+// The decode step with the caller's workspace, or (noalloc) with the device's scratch array in its place.
+sdm_status decode_impl(const sdm_config* cfg, const void* write_keys, const void* read_queries, const void* values,
+                       const void* forget_gate, const void* input_gate, const void* subkeys, const void* bank_in,
+                       void* bank_out, void* out, int32_t* write_idx, int32_t* read_idx, void* workspace,
+                       size_t workspace_bytes, void* stream, bool noalloc) {
   Dims D;
   TopkPlan pw, pr;
   TRY(validate(cfg, SDM_OP_DECODE, 0, &D, &pw, &pr));
@@ -697,7 +727,13 @@ sdm_status sdm_decode_step(const sdm_config* cfg, const void* write_keys, const 
   TRY(aligned(bank_in, 16, "bank_in"));
   TRY(aligned(bank_out, 16, "bank_out"));
   const WsLayout L = layout(D, SDM_OP_DECODE);
-  TRY(check_ws(workspace, workspace_bytes, L.total));
+  if (noalloc) {
+    if (L.total > SDM_NOALLOC_SCRATCH_BYTES)
+      return fail(SDM_ERR_RANGE, "this decode step needs %zu bytes of scratch; sdm_decode_step_noalloc has %zu "
+                  "(use sdm_decode_step with a workspace)", L.total, (size_t)SDM_NOALLOC_SCRATCH_BYTES);
+  } else {
+    TRY(check_ws(workspace, workspace_bytes, L.total));
+  }
   const bool donated = bank_in == bank_out;
   const size_t qb = (size_t)rows * D.F * D.dk * ea;
   const Range ins[] = {{write_keys, qb, "write_keys"},
@@ -711,10 +747,11 @@ sdm_status sdm_decode_step(const sdm_config* cfg, const void* write_keys, const 
                         {out, (size_t)rows * D.d * ea, "out"},
                         {write_idx, (size_t)rows * D.W * 4, "write_idx"},
                         {read_idx, (size_t)rows * D.R * 4, "read_idx"},
-                        {workspace, L.total, "workspace"}};
+                        {noalloc ? nullptr : workspace, L.total, "workspace"}};
   TRY(check_alias(outs, 5, ins, 7));
   TRY(check_device());
   if (rows == 0) return ok();
+  if (noalloc) TRY(scratch_address(&workspace));
   hipStream_t st = (hipStream_t)stream;
   unsigned char* ws = (unsigned char*)workspace;
   if (!donated)
@@ -765,6 +802,25 @@ sdm_status sdm_decode_step(const sdm_config* cfg, const void* write_keys, const 
   a.rwt = (const float*)(ws + L.rwt);
   TRY(hip_status(timed(SDM_K_DECODE, st, [&] { return launch_decode(D, a, st); }), "decode launch"));
   return ok();
+}
+}  // namespace
+
+extern "C" {
+
+sdm_status sdm_decode_step(const sdm_config* cfg, const void* write_keys, const void* read_queries,
+                           const void* values, const void* forget_gate, const void* input_gate, const void* subkeys,
+                           const void* bank_in, void* bank_out, void* out, int32_t* write_idx, int32_t* read_idx,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(cfg, write_keys, read_queries, values, forget_gate, input_gate, subkeys, bank_in, bank_out, out,
+                     write_idx, read_idx, workspace, workspace_bytes, stream, false);
+}
+
+sdm_status sdm_decode_step_noalloc(const sdm_config* cfg, const void* write_keys, const void* read_queries,
+                                   const void* values, const void* forget_gate, const void* input_gate,
+                                   const void* subkeys, const void* bank_in, void* bank_out, void* out,
+                                   int32_t* write_idx, int32_t* read_idx, void* stream) {
+  return decode_impl(cfg, write_keys, read_queries, values, forget_gate, input_gate, subkeys, bank_in, bank_out, out,
+                     write_idx, read_idx, nullptr, 0, stream, true);
 }
 
 // ------------------------------------------------------------------------------------------- layer (forward)

@@ -194,6 +194,21 @@ sdm_status sdm_decode_step(const sdm_config* cfg, const void* write_keys, const 
                            const void* bank_in, void* bank_out, void* out, int32_t* write_idx, int32_t* read_idx,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* The decode step without a workspace, for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation). Same arguments, checks, kernels and results as
+ * sdm_decode_step (bit for bit), except that the temporary storage sdm_decode_step takes from `workspace` comes from
+ * a fixed array in device memory that the library holds on each GPU it runs on until the process ends
+ * (SDM_NOALLOC_SCRATCH_BYTES per GPU; its address is looked up once per device on the first call there). The call
+ * allocates nothing. A step whose workspace (sdm_workspace_size, SDM_OP_DECODE) exceeds SDM_NOALLOC_SCRATCH_BYTES is
+ * refused with SDM_ERR_RANGE before any work. Every call on one GPU shares that GPU's array: calls that overlap in
+ * time on one GPU (other streams or host threads) race and must be serialised by the caller; calls ordered on one
+ * stream are safe. */
+#define SDM_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+sdm_status sdm_decode_step_noalloc(const sdm_config* cfg, const void* write_keys, const void* read_queries,
+                                   const void* values, const void* forget_gate, const void* input_gate,
+                                   const void* subkeys, const void* bank_in, void* bank_out, void* out,
+                                   int32_t* write_idx, int32_t* read_idx, void* stream);
+
 /* The layer around the op (README usage example: SparseDeltaMemoryArgs(dim, num_heads, slots_per_head, num_writes,
  * num_reads, chunk_size); CHANGELOG 2.0.0, "Behavior changes": a layer call runs the projections, the top-k and the
  * bank copy, then the op; README "ideas": gates of Gated DeltaNet with FLA's A/dt parameterisation). Forward only.

@@ -317,3 +317,22 @@ def test_snapshot_dtype_settings_and_refusals(lib):
     # stops at the workspace check (which follows the route check) on every machine, never at the route refusal
     bf = _cfg(snapshot_dtype=B.SDM_BF16, chunk_size=7, act_dtype=B.SDM_BF16, bank_dtype=B.SDM_BF16)
     assert save(bf, short=1) == B.SDM_ERR_WORKSPACE
+
+
+@fake_pointers
+def test_decode_noalloc_refuses_before_device_work(lib):
+    """sdm_decode_step_noalloc: the decode step's host checks, and a step whose workspace exceeds the per-GPU
+    scratch (SDM_NOALLOC_SCRATCH_BYTES) refused with SDM_ERR_RANGE, all before any device work."""
+    base, step = 1 << 40, 1 << 36
+    p = [_fake(base + i * step) for i in range(11)]  # keys queries values gates(2) sub-keys bank_in bank_out out ids
+    cfg = _cfg(tokens=1)
+    q = list(p)
+    q[8] = None  # out
+    assert lib.sdm_decode_step_noalloc(ctypes.byref(cfg), *q, None) == B.SDM_ERR_NULL
+    q = list(p)
+    q[7] = _fake(base + 6 * step + 256)  # bank_out starts inside bank_in
+    assert lib.sdm_decode_step_noalloc(ctypes.byref(cfg), *q, None) == B.SDM_ERR_ALIAS
+    big = _cfg(tokens=1, batch=2048, num_writes=512, num_reads=512, widths=(32, 32))
+    assert B.workspace_size(big, B.SDM_OP_DECODE) > B.NOALLOC_SCRATCH_BYTES
+    assert lib.sdm_decode_step_noalloc(ctypes.byref(big), *p, None) == B.SDM_ERR_RANGE
+    assert "scratch" in B.last_error()
