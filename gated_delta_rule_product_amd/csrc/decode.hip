@@ -226,11 +226,6 @@ __host__ __device__ inline StepLds step_lds(unsigned char* base, const Dims& D, 
   return L;
 }
 
-// A float rounded to the bank dtype and back (the value a stored row holds).
-template <typename Bk> __device__ __forceinline__ float bank_round(float v);
-template <> __device__ __forceinline__ float bank_round<float>(float v) { return v; }
-template <> __device__ __forceinline__ float bank_round<bf16_t>(float v) { return bf16_to_f(f_to_bf16(v)); }
-
 // A 16-byte row piece (EPL elements of the bank dtype) as floats.
 template <typename Bk> __device__ __forceinline__ void piece_unpack(const w16_t& x, float* v);
 template <> __device__ __forceinline__ void piece_unpack<float>(const w16_t& x, float* v) {

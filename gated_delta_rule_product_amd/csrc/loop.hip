@@ -7,7 +7,8 @@
 //   B  solve   U_t = beta_t v_t - alpha_t beta_t H[t];  delta_t = sum_s T_ts U_s      (T from the plan)
 //   C  read    out_t = G[t] + sum_s Q_ts delta_s                             (act dtype)
 //   D  scatter per written slot j, its events in token order: M[j] <- alpha_s M[j] + w_sj delta_s, one read and
-//              one write of the row slice, rounded once to the bank dtype      (HBM: W row slices per token)
+//              one write of the row slice (HBM: W row slices per token); a bfloat16 row is rounded after every
+//              event, as the per-token recurrence stores it (bank_round)
 // A group of 4 lanes moves one 64-byte row slice (16 bytes per lane). In phase A each group accumulates one token's
 // terms in order (no cross-lane reduction), with its row loads back to back. Blocks are mapped so that
 // neighbouring column slices of a stream run on the same XCD and share its L2 (a 128-byte L2 line holds two
@@ -278,7 +279,7 @@ __global__ __launch_bounds__(LOOP_NT) void loop_kernel(Dims D, LoopArgs a, int n
               if (snap) Lane<Bk>::store(snap + ((long long)tk * D.W + (x.tok >> 16)) * D.d, m[u]);
               const float al = sA[tk];
 #pragma unroll
-              for (int k = 0; k < EPL; ++k) m[u][k] = al * m[u][k] + x.w * sD[tk * COLS + q * EPL + k];
+              for (int k = 0; k < EPL; ++k) m[u][k] = bank_round<Bk>(al * m[u][k] + x.w * sD[tk * COLS + q * EPL + k]);
             }
             Lane<Bk>::store(p[u], m[u]);
           }
@@ -1084,7 +1085,7 @@ __global__ __launch_bounds__(LOOP_NT) void loop_narrow_kernel(Dims D, LoopArgs a
             const Ev x = mev[e];
             const float al = sA[x.tok];
 #pragma unroll
-            for (int k = 0; k < EPL; ++k) m[k] = al * m[k] + x.w * sD[x.tok * EPL + k];
+            for (int k = 0; k < EPL; ++k) m[k] = bank_round<Bk>(al * m[k] + x.w * sD[x.tok * EPL + k]);
           }
         } else {  // own token, own weight (used when the slot's only event is this one)
           const float wgt = term_coef<U>(wt);
@@ -1142,7 +1143,7 @@ __global__ __launch_bounds__(LOOP_NT) void loop_narrow_kernel(Dims D, LoopArgs a
             const Ev x = mev[e];
             const float al = sA[x.tok];
 #pragma unroll
-            for (int k = 0; k < EPL; ++k) m[k] = al * m[k] + x.w * sD[x.tok * EPL + k];
+            for (int k = 0; k < EPL; ++k) m[k] = bank_round<Bk>(al * m[k] + x.w * sD[x.tok * EPL + k]);
           }
           const uint32_t off = in ? (uint32_t)sg.slot * ldb + colb : BUF_OOB;
           __builtin_amdgcn_raw_buffer_store_b128(pack_w<Bk>(m), rb, (int)off, 0, 0);

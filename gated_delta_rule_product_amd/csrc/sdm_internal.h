@@ -157,6 +157,15 @@ template <typename T> __device__ __forceinline__ T from_f(float v);
 template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
 template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float v) { return f_to_bf16(v); }
 
+// A bank row value after one write event, as the per-token recurrence stores it: float32 rows keep every bit,
+// bfloat16 rows are rounded to nearest even after every event (a slot written several times in one chunk goes
+// through the same roundings as when its events come one token at a time).
+template <typename Bk> __device__ __forceinline__ float bank_round(float v);
+template <> __device__ __forceinline__ float bank_round<float>(float v) { return v; }
+template <> __device__ __forceinline__ float bank_round<bf16_t>(float v) {
+  return __uint_as_float((uint32_t)f_to_bf16(v) << 16);
+}
+
 // Sort key half for "larger float first": ascending order of the returned value = descending order of x.
 // -0 and +0 map to the same key (they compare equal).
 __device__ __forceinline__ uint32_t desc_key(float x) {

@@ -701,32 +701,34 @@ def _sub(x, lo, hi):
     return {k: (v[:, lo:hi] if k in ("wkeys", "rq", "values", "alpha", "beta") else v) for k, v in x.items()}
 
 
+def _err_summary(got, ref):
+    """Row-wise relative errors: (max, 99.9th percentile, rows above 1e-2) for a diagnostic line."""
+    got = np.asarray(got, np.float64).reshape(-1, got.shape[-1])
+    ref = np.asarray(ref, np.float64).reshape(-1, ref.shape[-1])
+    e = np.abs(got - ref).max(axis=1) / np.maximum(np.abs(ref).max(axis=1), 1e-30)
+    return float(e.max()), float(np.quantile(e, 0.999)), int((e > 1e-2).sum())
+
+
 @pytest.mark.slow
+@pytest.mark.timeout(900)
 def test_three_factor_65k_full_size():
     """Three-factor workload at full size (B 1, T 32768, H 4, d 256, factors 64 x 32 x 32, W = R = 64, chunk 128,
-    bf16 bank). The oracle runs on the first 2048 tokens (outputs there depend on nothing later); at full size:
-    ids of sampled tokens against the oracle's top-k, and a run split at token 2048 equal bit for bit to one run."""
+    bf16 activations on a bf16 bank), the whole sequence against the oracle: every write and read id, every output
+    row and every final bank row; and a run split at token 2048 equal bit for bit to one run."""
     s = synth.WORKLOADS["three_factor_65k"]
     P = 2048
     print("full-size three_factor_65k: generating inputs", flush=True)
     x = synth.make_inputs(s)
     print("full-size three_factor_65k: GPU, whole sequence", flush=True)
     out, bank, widx, ridx = run_gpu(s, x)
-    print("full-size three_factor_65k: oracle on the prefix", flush=True)
-    sp = s.with_(tokens=P)
-    ref = run_oracle(sp, _sub(x, 0, P))
-    assert np.array_equal(widx[:, :P], ref["widx"]) and np.array_equal(ridx[:, :P], ref["ridx"])
-    e_out = rowwise_rel(out[:, :P], ref["out"])
-    assert e_out <= RTOL["bf16"], f"out rel err {e_out}"
-    rng = np.random.default_rng(5)
-    ts = np.sort(rng.choice(s.tokens, 64, replace=False))
-    for key, got in (("wkeys", widx), ("rq", ridx)):
-        rid, _ = oracle.topk(x[key][:, ts], x["subkeys"], s.widths, s.num_writes)
-        assert np.array_equal(got[:, ts], rid), f"{key}: sampled ids differ"
+    print("full-size three_factor_65k: oracle, whole sequence (4 streams)", flush=True)
+    ref = run_oracle(s, x)
+    print("full-size three_factor_65k: out (max, p99.9, rows > 1e-2)", _err_summary(out, ref["out"]),
+          "bank", _err_summary(bank, ref["bank"]), flush=True)
+    e_out, e_bank = check_parity(s, (out, bank, widx, ridx), ref)
     print("full-size three_factor_65k: GPU prefix and remainder", flush=True)
+    sp = s.with_(tokens=P)
     out_p, bank_p, _, _ = run_gpu(sp, _sub(x, 0, P))
-    e_bank = rowwise_rel(bank_p, ref["bank"])
-    assert e_bank <= RTOL["bf16"], f"prefix bank rel err {e_bank}"
     assert np.array_equal(out_p, out[:, :P])
     out_r, bank_r, _, _ = run_gpu(s.with_(tokens=s.tokens - P), _sub(x, P, s.tokens), bank=bank_p)
     assert np.array_equal(out_r, out[:, P:]) and np.array_equal(bank_r, bank)
