@@ -13,4 +13,6 @@ from .sdm_oracle import (  # noqa: F401
     topk_one,
     write_read,
     write_read_backward,
+    write_read_backward_bounds,
+    U_F32,
 )

@@ -366,7 +366,28 @@ int oracle_write_read(int B, int T, int H, int F, const int* widths, int dk, int
  * After the first token G is the gradient of the bank before the call. Every sum is fp64 in a fixed order.
  * exact = 1 keeps the bank states in fp64 (no rounding to the bank dtype): the smooth function that the finite-
  * difference pins differentiate. exact = 0 rounds them after every token exactly as oracle_write_read does.
+ *
+ * Error bounds (optional, for comparing another evaluation of this backward with it). For an evaluation that
+ *   (i)  reads pre-write rows P and read rows M[R_j] within eps_row * (that row's largest magnitude) of these, plus
+ *        q_rel * |element| for rows it reads from a rounded snapshot (a rounding that falls the other way: one
+ *        bfloat16 spacing is at most 2^-7 of the element),
+ *   (ii) has softmax weights within eps_w of these (relative), and
+ *   (iii) does every other sum, product and difference in an arithmetic with unit roundoff u, in any order,
+ * first-order running error analysis bounds the difference of every gradient element from this fp64 one:
+ *   a sum of n terms computed in any order is off by at most gamma(n) = n u / (1 - n u) times the sum of the terms'
+ *   magnitudes, plus the propagated errors of its terms; a product or difference adds u times its magnitude; and the
+ *   error of every quantity carries into the quantities computed from it with the magnitude of its coefficient
+ *   (the adjoint G carries its error from token to token like its value). The bound is that propagation, evaluated
+ *   alongside the backward with the magnitudes of this backward's own values (first order: products of two errors
+ *   are left out, and the caller allows a small relative slack for them).
  * ------------------------------------------------------------------------------------------------------------- */
+
+/* Parameters of the error bounds: u, eps_row, eps_w, q_rel (see above). */
+typedef struct {
+  double u, eps_row, eps_w, q_rel;
+} bound_par_t;
+
+static inline double gam(double n, double u) { return n * u / (1.0 - n * u); }
 
 typedef struct {
   int B, T, H, F, dk, d, W, R, bank_bf16, exact, snap_bf16;
@@ -374,6 +395,11 @@ typedef struct {
   const float *wkeys, *rq, *values, *alpha, *beta, *sub, *bank, *dout, *dbank;
   int64_t bank_rows, sumn;
   double *d_wkeys, *d_rq, *d_values, *d_alpha, *d_beta, *d_sub_stream, *d_bank, *out64, *bank64;
+  float* snap_out;                  /* optional [B, H, T, W, d]: the pre-write rows as the backward reads them */
+  const bound_par_t* bp;            /* NULL: no error bounds */
+  double *e_wkeys, *e_rq, *e_values, *e_alpha, *e_beta, *e_bank;
+  double *esub_stream, *msub_stream; /* per stream and sub-key element: propagated error, sum of term magnitudes */
+  int64_t* nsub_stream;             /* per stream and sub-key row: number of terms */
   int s_begin, s_end;
   int err;
 } bwd_job_t;
@@ -390,6 +416,29 @@ static void score_backward(int F, const int* widths, int dk, int64_t id, double 
       dx[(int64_t)f * dk + e] += ds * (double)c[e];
       dc[e] += ds * (double)x[(int64_t)f * dk + e];
     }
+    off += widths[f];
+  }
+}
+
+/* Error bound of score_backward's updates: the slot-score gradient ds (error eds) times sub-key and query values.
+ * Accumulates the propagated error into ex/esub and the term magnitudes into mx/msub, and counts a term per
+ * sub-key row in nsub. */
+static void score_bound(int F, const int* widths, int dk, int64_t id, double ds, double eds, const float* x,
+                        const float* sub, double* ex, double* mx, double* esub, double* msub, int64_t* nsub) {
+  int dig[ORACLE_MAX_F];
+  for (int f = F - 1; f >= 0; --f) { dig[f] = (int)(id % widths[f]); id /= widths[f]; }
+  int64_t off = 0;
+  for (int f = 0; f < F; ++f) {
+    const int64_t srow = off + dig[f];
+    const float* c = sub + srow * dk;
+    for (int e = 0; e < dk; ++e) {
+      const double xe = fabs((double)x[(int64_t)f * dk + e]), ce = fabs((double)c[e]);
+      ex[(int64_t)f * dk + e] += eds * ce;
+      mx[(int64_t)f * dk + e] += fabs(ds) * ce;
+      esub[srow * dk + e] += eds * xe;
+      msub[srow * dk + e] += fabs(ds) * xe;
+    }
+    nsub[srow] += 1;
     off += widths[f];
   }
 }
@@ -413,7 +462,24 @@ static void* bwd_worker(void* arg) {
   double* D = (double*)malloc(sizeof(double) * (size_t)d);
   double* dw = (double*)malloc(sizeof(double) * (size_t)(W > R ? W : R));
   unsigned char* later = (unsigned char*)malloc((size_t)rows);
-  if (!S || !Rd || !sc || !w || !rho || !P || !Vr || !rr || !del || !M || !G || !g || !D || !dw || !later) {
+  /* error-bound state (bound mode only): EG the bound on the adjoint bank, the rest per token */
+  const bound_par_t* bp = j->bp;
+  const int KM = W > R ? W : R;
+  double *EG = NULL, *Eg = NULL, *Er = NULL, *Mr = NULL, *Edl = NULL, *ED = NULL, *Edw = NULL, *Ex = NULL;
+  double* Mx = NULL;
+  if (bp) {
+    Mr = (double*)malloc(sizeof(double) * (size_t)d);
+    EG = (double*)malloc(sizeof(double) * (size_t)rows * d);
+    Eg = (double*)malloc(sizeof(double) * (size_t)W * d);
+    Er = (double*)malloc(sizeof(double) * (size_t)d);
+    Edl = (double*)malloc(sizeof(double) * (size_t)d);
+    ED = (double*)malloc(sizeof(double) * (size_t)d);
+    Edw = (double*)malloc(sizeof(double) * (size_t)KM);
+    Ex = (double*)malloc(sizeof(double) * (size_t)F * dk);
+    Mx = (double*)malloc(sizeof(double) * (size_t)F * dk);
+  }
+  if (!S || !Rd || !sc || !w || !rho || !P || !Vr || !rr || !del || !M || !G || !g || !D || !dw || !later ||
+      (bp && (!EG || !Eg || !Er || !Mr || !Edl || !ED || !Edw || !Ex || !Mx))) {
     j->err = 1;
     goto done;
   }
@@ -483,9 +549,15 @@ static void* bwd_worker(void* arg) {
         }
       }
     }
+    if (j->snap_out)
+      for (int64_t i = 0; i < (int64_t)T * W * d; ++i) j->snap_out[(int64_t)st * T * W * d + i] = (float)P[i];
     for (int64_t i = 0; i < rows; ++i) later[i] = 0;
     /* reverse sweep */
     for (int64_t i = 0; i < rows * d; ++i) G[i] = j->dbank ? (double)j->dbank[(int64_t)st * rows * d + i] : 0.0;
+    if (bp) for (int64_t i = 0; i < rows * d; ++i) EG[i] = 0.0;
+    double* esub = bp ? j->esub_stream + (int64_t)st * j->sumn * dk : NULL;
+    double* msub = bp ? j->msub_stream + (int64_t)st * j->sumn * dk : NULL;
+    int64_t* nsub = bp ? j->nsub_stream + (int64_t)st * j->sumn : NULL;
     for (int t = T - 1; t >= 0; --t) {
       const int64_t row = ((int64_t)b * T + t) * H + h;
       const int32_t* St = S + (int64_t)t * W;
@@ -506,12 +578,41 @@ static void* bwd_worker(void* arg) {
         for (int c = 0; c < d; ++c) acc += (double)dout[c] * (rounded ? (double)round_to(q[c], 1) : q[c]);
         dw[i] = acc;
         double* Gr = G + (int64_t)Rt[i] * d;
+        if (bp) { /* d rho_i from the read row (error eps_row of its largest magnitude, plus q_rel if rounded) */
+          const double u = bp->u;
+          double vmax = 0.0, e = 0.0, m = 0.0;
+          for (int c = 0; c < d; ++c) vmax = fmax(vmax, fabs(rounded ? (double)round_to(q[c], 1) : q[c]));
+          double* EGr = EG + (int64_t)Rt[i] * d;
+          for (int c = 0; c < d; ++c) {
+            const double qc = fabs(rounded ? (double)round_to(q[c], 1) : q[c]);
+            const double eq = bp->eps_row * vmax + (rounded ? bp->q_rel * (qc + bp->eps_row * vmax) : 0.0);
+            const double go = fabs((double)dout[c]);
+            e += go * eq;
+            m += go * qc;
+            EGr[c] += go * bp->eps_w * rt[i] + gam(2, u) * (fabs(Gr[c]) + rt[i] * go); /* G += rho dout */
+          }
+          Edw[i] = e + gam(d, u) * m;
+        }
         for (int c = 0; c < d; ++c) Gr[c] += rt[i] * (double)dout[c];
       }
       for (int i = 0; i < R; ++i) sum += rt[i] * dw[i];
       for (int i = 0; i < R; ++i)
         score_backward(F, j->widths, dk, Rt[i], rt[i] * (dw[i] - sum), j->rq + row * F * dk, sub,
                        j->d_rq + row * F * dk, dsub);
+      if (bp) { /* softmax derivative and the read query / sub-key updates */
+        const double u = bp->u;
+        double es = 0.0, ms = 0.0;
+        for (int i = 0; i < R; ++i) { es += rt[i] * Edw[i] + fabs(dw[i]) * bp->eps_w * rt[i]; ms += rt[i] * fabs(dw[i]); }
+        es += gam(R + 1, u) * ms;
+        for (int e = 0; e < F * dk; ++e) Ex[e] = Mx[e] = 0.0;
+        for (int i = 0; i < R; ++i) {
+          const double ds = rt[i] * (dw[i] - sum);
+          const double eds = rt[i] * (Edw[i] + es) + bp->eps_w * rt[i] * fabs(dw[i] - sum) +
+                             gam(2, u) * rt[i] * (fabs(dw[i]) + fabs(sum));
+          score_bound(F, j->widths, dk, Rt[i], ds, eds, j->rq + row * F * dk, sub, Ex, Mx, esub, msub, nsub);
+        }
+        for (int e = 0; e < F * dk; ++e) j->e_rq[row * F * dk + e] = Ex[e] + gam(R + 1, u) * Mx[e];
+      }
       /* the write */
       for (int i = 0; i < W; ++i)
         for (int c = 0; c < d; ++c) g[(int64_t)i * d + c] = G[(int64_t)St[i] * d + c];
@@ -537,10 +638,74 @@ static void* bwd_worker(void* arg) {
       dal -= be * rD;
       j->d_alpha[row] = dal;
       j->d_beta[row] = dbe;
+      if (bp) { /* bounds of r, delta, D, d values, d beta, d alpha, d w_i; then of the adjoint update below */
+        const double u = bp->u, qP = j->snap_bf16 ? bp->q_rel : 0.0;
+        /* r = sum_i w_i P_i (the rows within eps_row of their largest magnitude, plus qP if rounded) */
+        for (int c = 0; c < d; ++c) Er[c] = Mr[c] = 0.0;
+        for (int i = 0; i < W; ++i) {
+          const double* p = P + ((int64_t)t * W + i) * d;
+          double pmax = 0.0;
+          for (int c = 0; c < d; ++c) pmax = fmax(pmax, fabs(p[c]));
+          for (int c = 0; c < d; ++c) {
+            const double ep = bp->eps_row * pmax + qP * (fabs(p[c]) + bp->eps_row * pmax);
+            Er[c] += wt[i] * ep + fabs(p[c]) * bp->eps_w * wt[i];
+            Mr[c] += wt[i] * fabs(p[c]);
+          }
+        }
+        /* delta = beta (v - alpha r) */
+        for (int c = 0; c < d; ++c) {
+          Er[c] += gam(W + 1, u) * Mr[c];
+          Edl[c] = be * a * Er[c] + gam(3, u) * be * (fabs((double)v[c]) + a * fabs(r[c]));
+        }
+        for (int c = 0; c < d; ++c) {
+          double e = 0.0, m = 0.0;
+          for (int i = 0; i < W; ++i) {
+            Eg[(int64_t)i * d + c] = EG[(int64_t)St[i] * d + c];
+            e += wt[i] * Eg[(int64_t)i * d + c] + fabs(g[(int64_t)i * d + c]) * bp->eps_w * wt[i];
+            m += wt[i] * fabs(g[(int64_t)i * d + c]);
+          }
+          ED[c] = e + gam(W + 1, u) * m;
+          j->e_values[row * d + c] = be * ED[c] + u * be * fabs(D[c]);
+        }
+        double ebe = 0.0, mbe = 0.0, eal = 0.0, mal = 0.0;
+        for (int c = 0; c < d; ++c) {
+          const double y = (double)v[c] - a * r[c];
+          const double ey = a * Er[c] + gam(2, u) * (fabs((double)v[c]) + a * fabs(r[c]));
+          ebe += fabs(D[c]) * ey + fabs(y) * ED[c];
+          mbe += fabs(D[c] * y);
+          eal += be * (fabs(D[c]) * Er[c] + fabs(r[c]) * ED[c]);
+          mal += be * fabs(D[c] * r[c]);
+        }
+        for (int i = 0; i < W; ++i) {
+          const double* p = P + ((int64_t)t * W + i) * d;
+          const double* gi = g + (int64_t)i * d;
+          const double* egi = Eg + (int64_t)i * d;
+          double pmax = 0.0;
+          for (int c = 0; c < d; ++c) pmax = fmax(pmax, fabs(p[c]));
+          double ew = 0.0, mw = 0.0;
+          for (int c = 0; c < d; ++c) {
+            const double ep = bp->eps_row * pmax + qP * (fabs(p[c]) + bp->eps_row * pmax);
+            eal += fabs(gi[c]) * ep + fabs(p[c]) * egi[c];
+            mal += fabs(gi[c] * p[c]);
+            ew += fabs(gi[c]) * Edl[c] + fabs(dl[c]) * egi[c] + a * be * (fabs(D[c]) * ep + fabs(p[c]) * ED[c]);
+            mw += fabs(gi[c] * dl[c]) + a * be * fabs(D[c] * p[c]);
+          }
+          Edw[i] = ew + gam(d + 3, u) * mw;
+        }
+        j->e_beta[row] = ebe + gam(d + 1, u) * mbe;
+        j->e_alpha[row] = eal + gam((double)W * d + 2, u) * mal;
+      }
       for (int i = 0; i < W; ++i) {
         double* Gw = G + (int64_t)St[i] * d;
         const double* gi = g + (int64_t)i * d;
         for (int c = 0; c < d; ++c) Gw[c] = a * gi[c] - a * be * wt[i] * D[c];
+        if (bp) {
+          double* EGw = EG + (int64_t)St[i] * d;
+          const double* egi = Eg + (int64_t)i * d;
+          for (int c = 0; c < d; ++c)
+            EGw[c] = a * egi[c] + a * be * (wt[i] * ED[c] + fabs(D[c]) * bp->eps_w * wt[i]) +
+                     gam(4, bp->u) * (a * fabs(gi[c]) + a * be * wt[i] * fabs(D[c]));
+        }
         later[St[i]] = 1;
       }
       sum = 0.0;
@@ -548,12 +713,28 @@ static void* bwd_worker(void* arg) {
       for (int i = 0; i < W; ++i)
         score_backward(F, j->widths, dk, St[i], wt[i] * (dw[i] - sum), j->wkeys + row * F * dk, sub,
                        j->d_wkeys + row * F * dk, dsub);
+      if (bp) { /* softmax derivative and the write key / sub-key updates */
+        const double u = bp->u;
+        double es = 0.0, ms = 0.0;
+        for (int i = 0; i < W; ++i) { es += wt[i] * Edw[i] + fabs(dw[i]) * bp->eps_w * wt[i]; ms += wt[i] * fabs(dw[i]); }
+        es += gam(W + 1, u) * ms;
+        for (int e = 0; e < F * dk; ++e) Ex[e] = Mx[e] = 0.0;
+        for (int i = 0; i < W; ++i) {
+          const double ds = wt[i] * (dw[i] - sum);
+          const double eds = wt[i] * (Edw[i] + es) + bp->eps_w * wt[i] * fabs(dw[i] - sum) +
+                             gam(2, u) * wt[i] * (fabs(dw[i]) + fabs(sum));
+          score_bound(F, j->widths, dk, St[i], ds, eds, j->wkeys + row * F * dk, sub, Ex, Mx, esub, msub, nsub);
+        }
+        for (int e = 0; e < F * dk; ++e) j->e_wkeys[row * F * dk + e] = Ex[e] + gam(W + 1, u) * Mx[e];
+      }
     }
     for (int64_t i = 0; i < rows * d; ++i) j->d_bank[(int64_t)st * rows * d + i] = G[i];
+    if (bp) for (int64_t i = 0; i < rows * d; ++i) j->e_bank[(int64_t)st * rows * d + i] = EG[i];
   }
 done:
   free(S); free(Rd); free(sc); free(w); free(rho); free(P); free(Vr); free(rr); free(del); free(M); free(G);
   free(g); free(D); free(dw); free(later);
+  free(EG); free(Eg); free(Er); free(Mr); free(Edl); free(ED); free(Edw); free(Ex); free(Mx);
   return NULL;
 }
 
@@ -564,13 +745,14 @@ done:
  * [B, T, H], d_subkeys [H, sum n_f, dk] (summed over the batch in order b = 0, 1, ...), d_bank [B, H, bank_rows, d]
  * (the gradient with respect to the bank before the call); optional out64 [B, T, H, d] and bank64 (the forward's
  * outputs in fp64, unrounded, NULL to skip). Returns 0 or -1. */
-int oracle_write_read_backward(int B, int T, int H, int F, const int* widths, int dk, int d, int W, int R,
-                               int bank_bf16, int exact, int snap_bf16, const float* wkeys, const float* rq,
-                               const float* values,
-                               const float* alpha, const float* beta, const float* subkeys, const float* bank,
-                               int64_t bank_rows, const float* dout, const float* dbank, double* d_wkeys,
-                               double* d_rq, double* d_values, double* d_alpha, double* d_beta, double* d_subkeys,
-                               double* d_bank, double* out64, double* bank64, int nthreads) {
+static int backward_impl(int B, int T, int H, int F, const int* widths, int dk, int d, int W, int R, int bank_bf16,
+                         int exact, int snap_bf16, const float* wkeys, const float* rq, const float* values,
+                         const float* alpha, const float* beta, const float* subkeys, const float* bank,
+                         int64_t bank_rows, const float* dout, const float* dbank, double* d_wkeys, double* d_rq,
+                         double* d_values, double* d_alpha, double* d_beta, double* d_subkeys, double* d_bank,
+                         double* out64, double* bank64, float* snap_out, const bound_par_t* bp, double* e_wkeys,
+                         double* e_rq, double* e_values, double* e_alpha, double* e_beta, double* e_subkeys,
+                         double* e_bank, int nthreads) {
   int64_t sumn = 0, N = 1;
   for (int f = 0; f < F; ++f) { sumn += widths[f]; N *= widths[f]; }
   if (F < 1 || F > ORACLE_MAX_F || W < 1 || R < 1 || W > N || R > N || bank_rows < N) return -1;
@@ -580,6 +762,14 @@ int oracle_write_read_backward(int B, int T, int H, int F, const int* widths, in
   memset(d_subkeys, 0, sizeof(double) * (size_t)H * sumn * dk);
   double* dsub_stream = (double*)calloc((size_t)(streams > 0 ? streams : 1) * sumn * dk, sizeof(double));
   if (!dsub_stream) return -1;
+  double *esub = NULL, *msub = NULL;
+  int64_t* nsub = NULL;
+  if (bp) {
+    esub = (double*)calloc((size_t)(streams > 0 ? streams : 1) * sumn * dk, sizeof(double));
+    msub = (double*)calloc((size_t)(streams > 0 ? streams : 1) * sumn * dk, sizeof(double));
+    nsub = (int64_t*)calloc((size_t)(streams > 0 ? streams : 1) * sumn, sizeof(int64_t));
+    if (!esub || !msub || !nsub) { free(dsub_stream); free(esub); free(msub); free(nsub); return -1; }
+  }
   if (nthreads < 1) nthreads = 1;
   if (nthreads > streams) nthreads = streams > 0 ? streams : 1;
   if (nthreads > 256) nthreads = 256;
@@ -595,6 +785,9 @@ int oracle_write_read_backward(int B, int T, int H, int F, const int* widths, in
     j->dbank = dbank; j->bank_rows = bank_rows; j->sumn = sumn; j->d_wkeys = d_wkeys; j->d_rq = d_rq;
     j->d_values = d_values; j->d_alpha = d_alpha; j->d_beta = d_beta; j->d_sub_stream = dsub_stream;
     j->d_bank = d_bank; j->out64 = out64; j->bank64 = bank64; j->err = 0;
+    j->snap_out = snap_out; j->bp = bp; j->e_wkeys = e_wkeys; j->e_rq = e_rq; j->e_values = e_values;
+    j->e_alpha = e_alpha; j->e_beta = e_beta; j->e_bank = e_bank; j->esub_stream = esub; j->msub_stream = msub;
+    j->nsub_stream = nsub;
     j->s_begin = (int)((int64_t)streams * i / nthreads);
     j->s_end = (int)((int64_t)streams * (i + 1) / nthreads);
     started[i] = pthread_create(&th[i], NULL, bwd_worker, j) == 0;
@@ -607,6 +800,55 @@ int oracle_write_read_backward(int B, int T, int H, int F, const int* widths, in
       double* dst = d_subkeys + (int64_t)h * sumn * dk;
       for (int64_t i = 0; i < sumn * dk; ++i) dst[i] += src[i];
     }
-  free(dsub_stream);
+  if (bp) { /* sub-key gradients: the sum over every term of every stream of the head, in any order */
+    for (int h = 0; h < H; ++h)
+      for (int64_t rr = 0; rr < sumn; ++rr) {
+        int64_t n = 0;
+        for (int b = 0; b < B; ++b) n += nsub[((int64_t)b * H + h) * sumn + rr];
+        for (int e = 0; e < dk; ++e) {
+          double ee = 0.0, mm = 0.0;
+          for (int b = 0; b < B; ++b) {
+            ee += esub[(((int64_t)b * H + h) * sumn + rr) * dk + e];
+            mm += msub[(((int64_t)b * H + h) * sumn + rr) * dk + e];
+          }
+          e_subkeys[((int64_t)h * sumn + rr) * dk + e] = ee + gam((double)n + 1, bp->u) * mm;
+        }
+      }
+  }
+  free(dsub_stream); free(esub); free(msub); free(nsub);
   return err ? -1 : 0;
+}
+
+int oracle_write_read_backward(int B, int T, int H, int F, const int* widths, int dk, int d, int W, int R,
+                               int bank_bf16, int exact, int snap_bf16, const float* wkeys, const float* rq,
+                               const float* values,
+                               const float* alpha, const float* beta, const float* subkeys, const float* bank,
+                               int64_t bank_rows, const float* dout, const float* dbank, double* d_wkeys,
+                               double* d_rq, double* d_values, double* d_alpha, double* d_beta, double* d_subkeys,
+                               double* d_bank, double* out64, double* bank64, int nthreads) {
+  return backward_impl(B, T, H, F, widths, dk, d, W, R, bank_bf16, exact, snap_bf16, wkeys, rq, values, alpha, beta,
+                       subkeys, bank, bank_rows, dout, dbank, d_wkeys, d_rq, d_values, d_alpha, d_beta, d_subkeys,
+                       d_bank, out64, bank64, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, nthreads);
+}
+
+/* oracle_write_read_backward with error bounds (see the comment above bound_par_t): par = {u, eps_row, eps_w,
+ * q_rel}; e_* receive, per gradient element, the bound on the difference from this backward of an evaluation
+ * that meets the stated conditions (same shapes as the gradients; fp64). snap_out (optional, float32
+ * [B, H, T, W, d]) receives the pre-write rows of every write event as the backward reads them (rounded to
+ * bfloat16 with snap_bf16). The gradients and the other outputs are those of oracle_write_read_backward. */
+int oracle_write_read_backward_bounds(int B, int T, int H, int F, const int* widths, int dk, int d, int W, int R,
+                                      int bank_bf16, int snap_bf16, const float* wkeys, const float* rq,
+                                      const float* values, const float* alpha, const float* beta,
+                                      const float* subkeys, const float* bank, int64_t bank_rows, const float* dout,
+                                      const float* dbank, double* d_wkeys, double* d_rq, double* d_values,
+                                      double* d_alpha, double* d_beta, double* d_subkeys, double* d_bank,
+                                      double* out64, double* bank64, float* snap_out, const double* par,
+                                      double* e_wkeys, double* e_rq, double* e_values, double* e_alpha,
+                                      double* e_beta, double* e_subkeys, double* e_bank, int nthreads) {
+  if (!par || !e_wkeys || !e_rq || !e_values || !e_alpha || !e_beta || !e_subkeys || !e_bank) return -1;
+  bound_par_t bp = {par[0], par[1], par[2], par[3]};
+  return backward_impl(B, T, H, F, widths, dk, d, W, R, bank_bf16, 0, snap_bf16, wkeys, rq, values, alpha, beta,
+                       subkeys, bank, bank_rows, dout, dbank, d_wkeys, d_rq, d_values, d_alpha, d_beta, d_subkeys,
+                       d_bank, out64, bank64, snap_out, &bp, e_wkeys, e_rq, e_values, e_alpha, e_beta, e_subkeys,
+                       e_bank, nthreads);
 }

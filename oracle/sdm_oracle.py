@@ -70,6 +70,13 @@ def _load():
                 ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                 _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, ctypes.c_int64, _f32p, vp,
                 _f64p, _f64p, _f64p, _f64p, _f64p, _f64p, _f64p, vp, vp, ctypes.c_int]
+            lib.oracle_write_read_backward_bounds.restype = ctypes.c_int
+            lib.oracle_write_read_backward_bounds.argtypes = [
+                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, ctypes.c_int, ctypes.c_int,
+                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, ctypes.c_int64, _f32p, vp,
+                _f64p, _f64p, _f64p, _f64p, _f64p, _f64p, _f64p, vp, vp, vp, _f64p,
+                _f64p, _f64p, _f64p, _f64p, _f64p, _f64p, _f64p, ctypes.c_int]
             _lib = lib
     return _lib
 
@@ -210,4 +217,49 @@ def write_read_backward(wkeys, rq, values, alpha, beta, subkeys, bank, dout, dba
         res["d_values"], res["d_alpha"], res["d_beta"], res["d_subkeys"], res["d_bank"], fwd[0], fwd[1], nt)
     if rc != 0:
         raise ValueError("oracle_write_read_backward rejected its arguments")
+    return res
+
+
+U_F32 = 2.0 ** -24  # unit roundoff of float32 (round to nearest)
+
+
+def write_read_backward_bounds(wkeys, rq, values, alpha, beta, subkeys, bank, dout, dbank, widths, num_writes,
+                               num_reads, *, eps_row, eps_w=2 * U_F32, u=U_F32, q_rel=0.0, bank_bf16=False,
+                               snap_bf16=False, want_snapshot=False, nthreads: int | None = None):
+    """write_read_backward (rounded bank states, as the forward stores them) plus, for every gradient element, a
+    bound on how far another evaluation of the same backward may be from it (sdm_oracle.c, the comment above
+    bound_par_t): one that reads pre-write and read rows within eps_row of each row's largest magnitude (plus q_rel
+    of an element for rows read from a rounded snapshot), has softmax weights within eps_w relative, and does every
+    other operation with unit roundoff u in any order. Returns the gradients as write_read_backward does, the
+    bounds as e_wkeys, e_rq, e_values, e_alpha, e_beta, e_subkeys, e_bank, the forward's out and bank (fp64; the
+    bank rounded to its dtype after every token), and with want_snapshot the pre-write rows of every write event
+    as the backward reads them, float32 [B, H, T, W, d]."""
+    wk, rqa, v, al, be, sub = (_f32(x) for x in (wkeys, rq, values, alpha, beta, subkeys))
+    M = _f32(bank)
+    g_out = _f32(dout)
+    g_bank = None if dbank is None else _f32(dbank)
+    B, T, H, Fdk = wk.shape
+    d = v.shape[-1]
+    widths = np.ascontiguousarray(np.asarray(widths, dtype=np.int32))
+    dk = sub.shape[2]
+    W, R = int(num_writes), int(num_reads)
+    z = np.zeros
+    res = {"d_wkeys": z(wk.shape), "d_rq": z(rqa.shape), "d_values": z(v.shape), "d_alpha": z(al.shape),
+           "d_beta": z(be.shape), "d_subkeys": z(sub.shape), "d_bank": z(M.shape), "out": z((B, T, H, d)),
+           "bank": z(M.shape)}
+    for k in ("wkeys", "rq", "values", "alpha", "beta", "subkeys", "bank"):
+        res["e_" + k] = z(res["d_" + k].shape)
+    snap = np.empty((B, H, T, W, d), np.float32) if want_snapshot else None
+    par = np.array([u, eps_row, eps_w, q_rel], np.float64)
+    nt = nthreads or min(os.cpu_count() or 1, 16)
+    rc = _load().oracle_write_read_backward_bounds(
+        B, T, H, len(widths), widths, dk, d, W, R, int(bool(bank_bf16)), int(bool(snap_bf16)), wk, rqa, v, al, be,
+        sub, M, M.shape[2], g_out, None if g_bank is None else g_bank.ctypes.data, res["d_wkeys"], res["d_rq"],
+        res["d_values"], res["d_alpha"], res["d_beta"], res["d_subkeys"], res["d_bank"], res["out"].ctypes.data,
+        res["bank"].ctypes.data, None if snap is None else snap.ctypes.data, par, res["e_wkeys"], res["e_rq"],
+        res["e_values"], res["e_alpha"], res["e_beta"], res["e_subkeys"], res["e_bank"], nt)
+    if rc != 0:
+        raise ValueError("oracle_write_read_backward_bounds rejected its arguments")
+    if want_snapshot:
+        res["snapshot"] = snap
     return res
