@@ -127,12 +127,16 @@ def bench_write_read(args, torch, binding, synth):
     torch.cuda.synchronize()
     p2 = binding.profile_read()
     binding.profile_enable(False)
-    roof["unpadded_pitch_avg_launch_ms"] = round(p2["loop"][0] / p2["loop"][1], 4)
+    unpadded_ms = p2["loop"][0] / p2["loop"][1]
+    roof["unpadded_pitch_avg_launch_ms"] = round(unpadded_ms, 4)
+    # the same bytes against the loop on a dense [B, H, N, d] bank, and against the whole call's wall time (top-k,
+    # plan and loop, launches included)
+    roof["unpadded_pitch_frac"] = round(alg / (unpadded_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+    roof["whole_call_frac"] = round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
     del bank_np
     return {
         "tokens_per_s": tokens / (ms_step * 1e-3), "ms_per_step": ms_step, "kernels_avg_ms": kernels,
-        "roofline": roof, "whole_call_hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "shape": s, "pitch": pitch,
+        "roofline": roof, "shape": s, "pitch": pitch,
     }
 
 
@@ -451,21 +455,14 @@ def bench_decode(args, torch, binding, synth):
 
 
 def cpu_baseline(args, s, synth):
+    """The CPU oracle (sequential per-token fp64; streams spread over threads) on the host cores: the headline
+    workload in full with one thread per stream, a single-thread sample of it, and bounded samples of the decode and
+    three-factor workloads."""
     import numpy as np
 
     import oracle
 
     ncpu = os.cpu_count() or 1
-    threads = min(s.batch * s.heads, ncpu, 16)
-    T = args.cpu_tokens or s.tokens
-    ss = s.with_(tokens=T)
-    log(f"[bench] cpu baseline: oracle on {ss.name} B{ss.batch} T{T} H{ss.heads}, {threads} threads")
-    x = synth.make_inputs(ss)
-    t0 = time.perf_counter()
-    oracle.write_read(x["wkeys"], x["rq"], x["values"], x["alpha"], x["beta"], x["subkeys"], x["bank"], ss.widths,
-                      ss.num_writes, ss.num_reads, bank_bf16=ss.bank == "bf16", act_bf16=ss.act == "bf16",
-                      nthreads=threads, want_index=False)
-    dt = time.perf_counter() - t0
     model = platform.processor() or ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -475,11 +472,59 @@ def cpu_baseline(args, s, synth):
                     break
     except OSError:
         pass
+
+    def run(ss, threads, x=None):
+        x = synth.make_inputs(ss) if x is None else x
+        t0 = time.perf_counter()
+        oracle.write_read(x["wkeys"], x["rq"], x["values"], x["alpha"], x["beta"], x["subkeys"], x["bank"],
+                          ss.widths, ss.num_writes, ss.num_reads, bank_bf16=ss.bank == "bf16",
+                          act_bf16=ss.act == "bf16", nthreads=threads, want_index=False)
+        return time.perf_counter() - t0
+
+    threads = min(s.batch * s.heads, ncpu, 16)
+    T = args.cpu_tokens or s.tokens
+    ss = s.with_(tokens=T)
+    log(f"[bench] cpu baseline: oracle on {ss.name} B{ss.batch} T{T} H{ss.heads}, {threads} threads")
+    dt = run(ss, threads)
+    res = {"value": round(ss.batch * T / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"the full {ss.name} workload (B{ss.batch} x T{T} tokens, H{ss.heads}) in {dt:.1f} s; "
+                     f"sequential per-token fp64 oracle, one thread per stream; host CPU {model}, {ncpu} "
+                     f"logical CPUs visible"}
+    # one thread, a quarter of the sequence
+    s1 = s.with_(tokens=max(1, T // 4))
+    log(f"[bench] cpu baseline: {s1.name} T{s1.tokens}, 1 thread")
+    d1 = run(s1, 1)
+    res["single_thread"] = {"value": round(s1.batch * s1.tokens / d1, 2), "unit": "tokens/s", "cores": 1,
+                            "sample": f"{s1.name} B{s1.batch} x T{s1.tokens} tokens, H{s1.heads}, in {d1:.1f} s"}
+    other = {}
+    # decode: consecutive steps of the B = 128 workload, each a one-token write/read of every stream
+    sd = synth.WORKLOADS["decode_b128"]
+    nsteps = 16
+    th = min(sd.batch * sd.heads, ncpu, 16)
+    log(f"[bench] cpu baseline: {sd.name} {nsteps} steps, {th} threads")
+    bank = synth.make_bank(sd)
+    sub = synth.make_subkeys(sd)
+    xs = [synth.make_step_inputs(sd, step=i) for i in range(nsteps)]
+    t0 = time.perf_counter()
+    for x in xs:
+        r = oracle.write_read(x["wkeys"], x["rq"], x["values"], x["alpha"], x["beta"], sub, bank, sd.widths,
+                              sd.num_writes, sd.num_reads, nthreads=th, want_index=False)
+        bank = r["bank"]
+    dd = time.perf_counter() - t0
+    other["decode_b128"] = {"value": round(nsteps / dd, 2), "unit": "steps/s", "cores": th,
+                            "sample": f"{nsteps} consecutive steps of B{sd.batch} x H{sd.heads} streams in {dd:.1f} s"}
+    # three-factor workload: the first eighth of the sequence
+    s3 = synth.WORKLOADS["three_factor_65k"]
+    s3 = s3.with_(tokens=s3.tokens // 8)
+    th = min(s3.batch * s3.heads, ncpu, 16)
+    log(f"[bench] cpu baseline: {s3.name} T{s3.tokens}, {th} threads")
+    d3 = run(s3, th)
+    other["three_factor_65k"] = {"value": round(s3.batch * s3.tokens / d3, 2), "unit": "tokens/s", "cores": th,
+                                 "sample": f"B{s3.batch} x T{s3.tokens} tokens (an eighth of the sequence), "
+                                           f"H{s3.heads}, in {d3:.1f} s"}
+    res["other_workloads"] = other
     del np
-    return {"value": round(ss.batch * T / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"the full {ss.name} workload (B{ss.batch} x T{T} tokens, H{ss.heads}) in {dt:.1f} s; "
-                      f"sequential per-token fp64 oracle, one thread per stream; host CPU {model}, {ncpu} "
-                      f"logical CPUs visible"}
+    return res
 
 
 def main():
