@@ -438,6 +438,53 @@ def bench_decode(args, torch, binding, synth):
     res["graph"] = {"steps_per_s": round(args.decode_steps / (t1 - t0), 1),
                     "ms_per_step": round((t1 - t0) * 1e3 / args.decode_steps, 4), "equals_eager_bitwise": graph_equal}
     del graph
+    # the same timed steps as one sdm_decode_steps call (inputs [B, K, H, ...]; top-k of every step first, then
+    # each stream's steps in one launch), checked bit for bit against the eager donated steps
+    K = args.decode_steps
+    cat = {k: torch.stack([steps[i][k][:, 0] for i in range(args.decode_warmup, nsteps)], dim=1).contiguous()
+           for k in ("wkeys", "rq", "values", "alpha", "beta")}
+    m_out = torch.empty((s.batch, K, s.heads, s.head_dim), dtype=torch.float32, device=dev)
+    cfg_k = binding.make_config(s.batch, K, s.heads, s.widths, s.subkey_dim, s.head_dim, s.num_writes, s.num_reads, 1,
+                                binding.SDM_F32, binding.SDM_F32, s.rows)
+    ws_k = torch.empty(binding.workspace_size(cfg_k, binding.SDM_OP_DECODE_STEPS), dtype=torch.uint8, device=dev)
+    m_bank = torch.empty_like(bank0)
+
+    def multi():
+        binding.sdm_decode_steps(cat["wkeys"], cat["rq"], cat["values"], cat["alpha"], cat["beta"], sub, m_bank,
+                                 widths=s.widths, num_writes=s.num_writes, num_reads=s.num_reads, out=m_out,
+                                 workspace=ws_k)
+
+    # reference: the eager donated steps from the bank after the warm-up steps
+    r_bank = bank0.clone()
+    for i in range(nsteps):
+        a = steps[i]
+        step_fn(a["wkeys"], a["rq"], a["values"], a["alpha"], a["beta"], sub, r_bank, out=g_out)
+        if i == args.decode_warmup - 1:
+            warm_bank = r_bank.clone()
+    torch.cuda.synchronize()
+    m_bank.copy_(warm_bank)
+    multi()
+    torch.cuda.synchronize()
+    multi_equal = bool(torch.equal(m_bank, r_bank) and torch.equal(m_out[:, -1:], g_out))
+    reps = 5
+    t_m = 0.0
+    for _ in range(reps):
+        m_bank.copy_(warm_bank)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        multi()
+        torch.cuda.synchronize()
+        t_m += time.perf_counter() - t0
+    binding.profile_enable(True)
+    m_bank.copy_(warm_bank)
+    multi()
+    torch.cuda.synchronize()
+    mprof = binding.profile_read()
+    binding.profile_enable(False)
+    res["multi_step"] = {"steps_per_s": round(K * reps / t_m, 1), "ms_per_call": round(t_m * 1e3 / reps, 4),
+                         "steps_per_call": K, "equals_eager_bitwise": multi_equal,
+                         "kernels_ms_per_call": {k: round(v[0], 4) for k, v in mprof.items() if v[1]}}
+    del cat, m_out, ws_k, m_bank, r_bank, warm_bank
     equal = bool(torch.equal(outs["donated"][0], outs["copied"][0]) and torch.equal(outs["donated"][1],
                                                                                     outs["copied"][1]))
     sb = 4
@@ -447,7 +494,9 @@ def bench_decode(args, torch, binding, synth):
         "workload": "decode_b128: B128 streams x 1 token, H2 d256 N1024 (2x32) W=R=64, fp32 bank",
         "steps_per_s": res["donated"]["steps_per_s"], "steps_per_s_copied": res["copied"]["steps_per_s"],
         "steps_per_s_graph_replay": res["graph"]["steps_per_s"],
+        "steps_per_s_multi_step": res["multi_step"]["steps_per_s"],
         "donated": res["donated"], "copied": res["copied"], "graph_replay": res["graph"],
+        "multi_step": res["multi_step"],
         "donated_equals_copied_bitwise": equal,
         "warmup": args.decode_warmup, "steps": args.decode_steps,
         "decode_kernel_hbm_frac": round(per_step / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if dms else None,

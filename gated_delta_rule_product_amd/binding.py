@@ -22,7 +22,7 @@ SDM_ERR_LAYOUT, SDM_ERR_WORKSPACE, SDM_ERR_DEVICE, SDM_ERR_HIP, SDM_ERR_NULL = 5
 STATUS_NAMES = {0: "SDM_OK", 1: "SDM_ERR_DTYPE", 2: "SDM_ERR_RANGE", 3: "SDM_ERR_BANK_TOO_SMALL", 4: "SDM_ERR_ALIAS",
                 5: "SDM_ERR_LAYOUT", 6: "SDM_ERR_WORKSPACE", 7: "SDM_ERR_DEVICE", 8: "SDM_ERR_HIP", 9: "SDM_ERR_NULL"}
 SDM_F32, SDM_BF16, SDM_F16 = 0, 1, 2
-SDM_OP_TOPK, SDM_OP_WRITE_READ, SDM_OP_DECODE, SDM_OP_BACKWARD = 0, 1, 2, 3
+SDM_OP_TOPK, SDM_OP_WRITE_READ, SDM_OP_DECODE, SDM_OP_BACKWARD, SDM_OP_DECODE_STEPS = 0, 1, 2, 3, 4
 SCORING = {"auto": 0, "direct": 1, "filtered": 2}
 
 
@@ -136,6 +136,8 @@ def load():
             lib.sdm_write_read_backward.argtypes = [cfgp] + [_vp] * 17 + [ctypes.c_size_t, _vp]
             lib.sdm_decode_step.restype = ctypes.c_int
             lib.sdm_decode_step.argtypes = [cfgp] + [_vp] * 12 + [ctypes.c_size_t, _vp]
+            lib.sdm_decode_steps.restype = ctypes.c_int
+            lib.sdm_decode_steps.argtypes = [cfgp] + [_vp] * 12 + [ctypes.c_size_t, _vp]
             lib.sdm_decode_step_noalloc.restype = ctypes.c_int
             lib.sdm_decode_step_noalloc.argtypes = [cfgp] + [_vp] * 12
             lib.sdm_shared_bank_check.restype = ctypes.c_int
@@ -479,6 +481,44 @@ def sdm_decode_step(write_keys, read_queries, values, forget_gate, input_gate, s
                                   _ptr(forget_gate), _ptr(input_gate), _ptr(subkeys), _ptr(bank_in), _ptr(bank_out),
                                   _ptr(out), _ptr(widx), _ptr(ridx), _ptr(ws), 0 if ws is None else ws.numel(),
                                   _stream(bank_in.device)))
+    return out, widx, ridx, bank_out
+
+
+def sdm_decode_steps(write_keys, read_queries, values, forget_gate, input_gate, subkeys, bank_in, bank_out=None, *,
+                     widths, num_writes, num_reads, want_index=False, out=None, workspace=None):
+    """K consecutive decode steps in one call: inputs [B, K, H, ...], token k of each stream is step k's input;
+    bank_out None or bank_in: in place (donated), else a disjoint successor buffer that receives bank_in's copy.
+    Bitwise equal to K sdm_decode_step calls. Returns (out [B, K, H, d], write_idx, read_idx, bank_out)."""
+    if bank_out is None:
+        bank_out = bank_in
+    B, K, H, Fdk = write_keys.shape
+    F = len(widths)
+    dk = Fdk // F
+    d = values.shape[-1]
+    act = write_keys.dtype
+    for name, t, shp in (("write_keys", write_keys, (B, K, H, Fdk)), ("read_queries", read_queries, (B, K, H, Fdk)),
+                         ("values", values, (B, K, H, d)), ("forget_gate", forget_gate, (B, K, H)),
+                         ("input_gate", input_gate, (B, K, H)), ("subkeys", subkeys, (H, sum(widths), dk))):
+        _need(t, name, shp, act)
+    if bank_in.dim() != 4 or bank_in.shape[0] != B or bank_in.shape[1] != H or bank_in.shape[3] != d:
+        raise ValueError(f"bank_in has shape {tuple(bank_in.shape)}, expected ({B}, {H}, bank_rows, {d})")
+    ld = _bank_ld(bank_in, "bank_in")
+    if tuple(bank_out.shape) != tuple(bank_in.shape) or bank_out.dtype != bank_in.dtype or \
+            bank_out.stride() != bank_in.stride():
+        raise ValueError("bank_out must have bank_in's shape, dtype and strides")
+    cfg = make_config(B, K, H, widths, dk, d, num_writes, num_reads, 1, _dt(write_keys), _dt(bank_in),
+                      bank_in.shape[2], ld)
+    ws = _workspace(workspace_size(cfg, SDM_OP_DECODE_STEPS), bank_in.device, workspace)
+    if out is None:
+        out = torch.empty((B, K, H, d), dtype=act, device=bank_in.device)
+    else:
+        _need(out, "out", (B, K, H, d), act)
+    widx = torch.empty((B, K, H, num_writes), dtype=torch.int32, device=bank_in.device) if want_index else None
+    ridx = torch.empty((B, K, H, num_reads), dtype=torch.int32, device=bank_in.device) if want_index else None
+    _check(load().sdm_decode_steps(ctypes.byref(cfg), _ptr(write_keys), _ptr(read_queries), _ptr(values),
+                                   _ptr(forget_gate), _ptr(input_gate), _ptr(subkeys), _ptr(bank_in), _ptr(bank_out),
+                                   _ptr(out), _ptr(widx), _ptr(ridx), _ptr(ws), 0 if ws is None else ws.numel(),
+                                   _stream(bank_in.device)))
     return out, widx, ridx, bank_out
 
 

@@ -84,10 +84,11 @@ sdm_status make_plan(const Dims& D, int k, const char* what, TopkPlan* P) {
   return SDM_OK;
 }
 
-// op: SDM_OP_TOPK (k given), SDM_OP_WRITE_READ, SDM_OP_DECODE, SDM_OP_BACKWARD (the write/read's config)
+// op: SDM_OP_TOPK (k given), SDM_OP_WRITE_READ, SDM_OP_DECODE, SDM_OP_BACKWARD (the write/read's config),
+// SDM_OP_DECODE_STEPS (tokens = the number of steps)
 sdm_status validate(const sdm_config* cfg, int op, int k, Dims* D, TopkPlan* pw, TopkPlan* pr) {
   if (!cfg) return fail(SDM_ERR_NULL, "cfg is NULL");
-  if (op < SDM_OP_TOPK || op > SDM_OP_BACKWARD) return fail(SDM_ERR_RANGE, "unknown op %d", op);
+  if (op < SDM_OP_TOPK || op > SDM_OP_DECODE_STEPS) return fail(SDM_ERR_RANGE, "unknown op %d", op);
   const bool chunked = op == SDM_OP_WRITE_READ || op == SDM_OP_BACKWARD;
   const int act = cfg->act_dtype, bank = cfg->bank_dtype;
   if (act == SDM_F16 || (op != SDM_OP_TOPK && bank == SDM_F16))
@@ -198,8 +199,8 @@ WsLayout layout(const Dims& D, int op) {
   };
   L.cand = take(2 * MAX_CAND * 8);
   L.snorm = take((size_t)D.H * D.F * 4);
-  if (op == SDM_OP_DECODE) {
-    const size_t nw = (size_t)D.S * D.W, nr = (size_t)D.S * D.R;
+  if (op == SDM_OP_DECODE || op == SDM_OP_DECODE_STEPS) {  // ids and weights (steps: ids and scores) per token
+    const size_t nw = (size_t)D.S * D.T * D.W, nr = (size_t)D.S * D.T * D.R;
     L.widx = take(nw * 4);
     L.wwt = take(nw * 4);
     L.ridx = take(nr * 4);
@@ -704,11 +705,12 @@ sdm_status scratch_address(void** ptr) {
 sdm_status decode_impl(const sdm_config* cfg, const void* write_keys, const void* read_queries, const void* values,
                        const void* forget_gate, const void* input_gate, const void* subkeys, const void* bank_in,
                        void* bank_out, void* out, int32_t* write_idx, int32_t* read_idx, void* workspace,
-                       size_t workspace_bytes, void* stream, bool noalloc) {
+                       size_t workspace_bytes, void* stream, bool noalloc, bool steps = false) {
   Dims D;
   TopkPlan pw, pr;
-  TRY(validate(cfg, SDM_OP_DECODE, 0, &D, &pw, &pr));
-  const long long rows = (long long)D.B * D.H;
+  const int op = steps ? SDM_OP_DECODE_STEPS : SDM_OP_DECODE;
+  TRY(validate(cfg, op, 0, &D, &pw, &pr));
+  const long long rows = (long long)D.B * D.T * D.H;  // token rows (one token per stream for a single step)
   long long sumn = 0;
   for (int f = 0; f < D.F; ++f) sumn += D.widths[f];
   const size_t ea = esize(D.act), eb = esize(D.bank);
@@ -726,7 +728,7 @@ sdm_status decode_impl(const sdm_config* cfg, const void* write_keys, const void
   }
   TRY(aligned(bank_in, 16, "bank_in"));
   TRY(aligned(bank_out, 16, "bank_out"));
-  const WsLayout L = layout(D, SDM_OP_DECODE);
+  const WsLayout L = layout(D, op);
   if (noalloc) {
     if (L.total > SDM_NOALLOC_SCRATCH_BYTES)
       return fail(SDM_ERR_RANGE, "this decode step needs %zu bytes of scratch; sdm_decode_step_noalloc has %zu "
@@ -749,6 +751,19 @@ sdm_status decode_impl(const sdm_config* cfg, const void* write_keys, const void
                         {read_idx, (size_t)rows * D.R * 4, "read_idx"},
                         {noalloc ? nullptr : workspace, L.total, "workspace"}};
   TRY(check_alias(outs, 5, ins, 7));
+  if (steps && rows > 0) {  // the steps kernel runs the one-launch step's arithmetic: only its shapes
+    DecodeArgs probe;
+    memset(&probe, 0, sizeof probe);
+    probe.queries[0] = write_keys;
+    probe.queries[1] = read_queries;
+    probe.subkeys = subkeys;
+    probe.plan[0] = pw;
+    probe.plan[1] = pr;
+    if (!decode_step_fits(D, probe))
+      return fail(SDM_ERR_RANGE, "sdm_decode_steps runs the one-launch step's shapes only (num_writes, num_reads "
+                  "<= 64, <= 256 sub-keys per factor, <= 1024 candidates, 16-byte aligned queries and sub-key rows): "
+                  "use sdm_decode_step per token");
+  }
   TRY(check_device());
   if (rows == 0) return ok();
   if (noalloc) TRY(scratch_address(&workspace));
@@ -772,6 +787,35 @@ sdm_status decode_impl(const sdm_config* cfg, const void* write_keys, const void
   a.bank_in = bank_in;
   a.bank_out = bank_out;
   a.out = out;
+  if (steps) {  // the batched top-k of every step, then the steps' rows in one launch
+    const TopkPlan plans[2] = {pw, pr};
+    TRY(hip_status(timed(SDM_K_CAND, st, [&] { return launch_cand_tables(plans, 2, D.F, (uint64_t*)(ws + L.cand), st); }),
+                   "candidate table launch"));
+    TopkArgs ta;
+    memset(&ta, 0, sizeof ta);
+    ta.queries[0] = write_keys;
+    ta.queries[1] = read_queries;
+    ta.subkeys = subkeys;
+    ta.cand[0] = (const uint64_t*)(ws + L.cand);
+    ta.cand[1] = (const uint64_t*)(ws + L.cand) + MAX_CAND;
+    ta.plan[0] = pw;
+    ta.plan[1] = pr;
+    ta.nkinds = 2;
+    ta.stream_major = 0;  // row-major [B, K, H, k] ids and float32 slot scores
+    ta.ids[0] = (int32_t*)(ws + L.widx);
+    ta.ids[1] = (int32_t*)(ws + L.ridx);
+    ta.vals[0] = (float*)(ws + L.wwt);
+    ta.vals[1] = (float*)(ws + L.rwt);
+    ta.snorm = (float*)(ws + L.snorm);
+    TRY(hip_status(timed(SDM_K_TOPK, st, [&] { return launch_topk(D, ta, st); }), "top-k launch"));
+    a.wid = (const int32_t*)(ws + L.widx);
+    a.wwt = (const float*)(ws + L.wwt);
+    a.rid = (const int32_t*)(ws + L.ridx);
+    a.rwt = (const float*)(ws + L.rwt);
+    TRY(hip_status(timed(SDM_K_DECODE, st, [&] { return launch_decode_steps(D, a, D.T, st); }),
+                   "decode steps launch"));
+    return ok();
+  }
   if (decode_step_fits(D, a)) {  // top-k, update and read in one launch
     TRY(hip_status(timed(SDM_K_DECODE, st, [&] { return launch_decode_step(D, a, st); }), "decode step launch"));
     return ok();
@@ -813,6 +857,14 @@ sdm_status sdm_decode_step(const sdm_config* cfg, const void* write_keys, const 
                            void* workspace, size_t workspace_bytes, void* stream) {
   return decode_impl(cfg, write_keys, read_queries, values, forget_gate, input_gate, subkeys, bank_in, bank_out, out,
                      write_idx, read_idx, workspace, workspace_bytes, stream, false);
+}
+
+sdm_status sdm_decode_steps(const sdm_config* cfg, const void* write_keys, const void* read_queries,
+                            const void* values, const void* forget_gate, const void* input_gate, const void* subkeys,
+                            const void* bank_in, void* bank_out, void* out, int32_t* write_idx, int32_t* read_idx,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(cfg, write_keys, read_queries, values, forget_gate, input_gate, subkeys, bank_in, bank_out, out,
+                     write_idx, read_idx, workspace, workspace_bytes, stream, false, true);
 }
 
 sdm_status sdm_decode_step_noalloc(const sdm_config* cfg, const void* write_keys, const void* read_queries,

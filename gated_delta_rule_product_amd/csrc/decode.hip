@@ -242,82 +242,19 @@ template <> __device__ __forceinline__ void piece_unpack<bf16_t>(const w16_t& x,
 constexpr int STEP_NT = 256;
 constexpr int STEP_RPW = 16;  // rows of each kind per wave: W, R <= 64
 
-template <typename A, typename Bk, int NPL, int CPL>
-__global__ __launch_bounds__(STEP_NT) void decode_step_kernel(Dims D, DecodeArgs a) {
+// The rows of one step of one stream, after its top-k (L: ids, weights; rmatch and part are scratch): every wave
+// gathers write rows and read rows w, w + 4, ... (W, R <= 64) of a column pass of 64 lanes x 16 bytes from bin, all
+// of a pass's loads complete before any row of the pass is written; r = sum_i w_i M[S_i] per wave in row order,
+// then over the waves in order; delta = beta (v - alpha r); the updated write rows go to bout (rounded to the bank
+// dtype); a read row whose slot is also written this step is updated in registers with the same arithmetic and
+// rounding, so the read sees the successor; out = sum_j rho_j M'[R_j] per wave, then over the waves. values and
+// out point at the stream-row's d elements. Starts after a barrier that made L visible; every wave calls it.
+template <typename A, typename Bk>
+__device__ __forceinline__ void step_rows(const Dims& D, const StepLds& L, const Bk* bin, Bk* bout, const A* values,
+                                          A* out, float al, float be) {
   constexpr int EPL = DLane<Bk>::EPL;
   constexpr int COLW = 64 * EPL;
-  extern __shared__ __align__(16) unsigned char lds[];
-  const StepLds L = step_lds(lds, D, a.plan, EPL);
-  // the wave index as a scalar: plan fields picked by wave then load as scalar loads (a vector load of them would
-  // queue behind the sub-key loads issued early below and wait for them)
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int st = blockIdx.x;  // stream b * H + h; with one token the [B, 1, H] row index equals st
-  const int h = st % D.H;
-  // (members picked by kind or wave with conditionals, not indexed: a runtime index into a struct's array puts the
-  // struct in scratch memory)
-  auto pick2 = [](auto x0, auto x1, int i) { return i ? x1 : x0; };
-  auto pick4 = [](auto x0, auto x1, auto x2, auto x3, int i) { return i < 2 ? (i ? x1 : x0) : (i == 2 ? x2 : x3); };
-  // factor top-k of both queries: task kind * F + f on wave task % 4. Each wave issues the loads of its first
-  // task's first block now; they arrive while the candidate tables are built.
-  long long sumn = 0;
-  for (int f = 0; f < D.F; ++f) sumn += D.widths[f];
-  const A* subh = (const A*)a.subkeys + (long long)h * sumn * D.dk;
-  auto task_in = [&](int task, int* f, const A** qv, const A** tab) {
-    const int kind = task / D.F;
-    *f = task % D.F;
-    long long off = 0;
-    for (int g = 0; g < *f; ++g) off += D.widths[g];
-    *qv = (const A*)pick2(a.queries[0], a.queries[1], kind) + (long long)st * D.F * D.dk;
-    *tab = subh + off * D.dk;
-  };
-  FactorBlock<A, NPL> fb;
-  if (wv < 2 * D.F) {
-    int f;
-    const A *qv, *tab;
-    task_in(wv, &f, &qv, &tab);
-    factor_load<A, NPL>(D, f, qv, tab, 0, fb);
-  }
-  // candidate tables: threads 0-127 build the write table, 128-255 the read table (small tables: waves 0 and 2)
-  {
-    const int kind = wv >> 1, t = tid & 127;
-    const TopkPlan& P = kind ? a.plan[1] : a.plan[0];
-    if (cand_one_wave(a.plan[0], D.F) && cand_one_wave(a.plan[1], D.F)) {
-      if (t < 64) cand_table_wave(P, pick2(L.ctab[0], L.ctab[1], kind), lane);
-    } else {
-      cand_offsets(P, D.F, pick2(L.offs[0], L.offs[1], kind), t, 128);
-      __syncthreads();
-      cand_emit(P, D.F, pick2(L.offs[0], L.offs[1], kind), pick2(L.ctab[0], L.ctab[1], kind), t, 128);
-    }
-  }
-  uint64_t* wscr = pick4(L.scratch[0], L.scratch[1], L.scratch[2], L.scratch[3], wv);
-  uint64_t* wsrt = pick4(L.sorted[0], L.sorted[1], L.sorted[2], L.sorted[3], wv);
-  for (int task = wv; task < 2 * D.F; task += 4) {
-    const int kind = task / D.F;
-    int f;
-    const A *qv, *tab;
-    task_in(task, &f, &qv, &tab);
-    if (task != wv) factor_load<A, NPL>(D, f, qv, tab, 0, fb);
-    const TopkPlan& P = kind ? a.plan[1] : a.plan[0];
-    wave_factor_topk<A, NPL>(D, P, f, qv, tab, pick2(L.fsc[0], L.fsc[1], kind), pick2(L.fid[0], L.fid[1], kind),
-                             wscr, wsrt, fb);
-  }
-  __syncthreads();  // factor lists and candidate tables complete
-  if (wv < 2) {  // merges: wave 0 the write query, wave 1 the read query
-    const int kind = wv;
-    const TopkPlan& P = kind ? a.plan[1] : a.plan[0];
-    int32_t* ids = kind ? L.rid : L.wid;
-    wave_merge_topk<CPL>(D, P, pick2(L.ctab[0], L.ctab[1], kind), pick2(L.fsc[0], L.fsc[1], kind),
-                         pick2(L.fid[0], L.fid[1], kind), wscr, wsrt, ids, kind ? L.rwt : L.wwt);
-    int32_t* uid = pick2(a.user_ids[0], a.user_ids[1], kind);
-    if (uid)
-      for (int r = lane; r < P.k; r += 64) uid[(long long)st * P.k + r] = ids[r];
-  }
-  __syncthreads();
-  const float al = to_f<A>(((const A*)a.alpha)[st]);
-  const float be = to_f<A>(((const A*)a.beta)[st]);
-  const long long rowsd = D.rows * D.ld;
-  const Bk* bin = (const Bk*)a.bank_in + (long long)st * rowsd;
-  Bk* bout = (Bk*)a.bank_out + (long long)st * rowsd;
   float* part = L.part;
   for (int c0 = 0; c0 < D.d; c0 += COLW) {
     const int col = c0 + lane * EPL;
@@ -325,7 +262,7 @@ __global__ __launch_bounds__(STEP_NT) void decode_step_kernel(Dims D, DecodeArgs
     // the value piece first (used after the barrier below; loaded now so that its latency hides behind the rows)
     float va[EPL];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) va[e] = valid ? to_f<A>(((const A*)a.values)[(long long)st * D.d + col + e]) : 0.0f;
+    for (int e = 0; e < EPL; ++e) va[e] = valid ? to_f<A>(values[col + e]) : 0.0f;
     w16_t wr[STEP_RPW], rr[STEP_RPW];
     static_for<STEP_RPW>([&](auto u) {
       const int i = wv + 4 * u;
@@ -420,11 +357,88 @@ __global__ __launch_bounds__(STEP_NT) void decode_step_kernel(Dims D, DecodeArgs
       for (int e = 0; e < EPL; ++e) {
         const int c = lane * EPL + e;
         const float o = opart[c] + opart[COLW + c] + opart[2 * COLW + c] + opart[3 * COLW + c];
-        ((A*)a.out)[(long long)st * D.d + col + e] = from_f<A>(o);
+        out[col + e] = from_f<A>(o);
       }
     }
     if (c0 + COLW < D.d) __syncthreads();  // the partial sums are reused by the next pass
   }
+}
+
+template <typename A, typename Bk, int NPL, int CPL>
+__global__ __launch_bounds__(STEP_NT) void decode_step_kernel(Dims D, DecodeArgs a) {
+  constexpr int EPL = DLane<Bk>::EPL;
+  extern __shared__ __align__(16) unsigned char lds[];
+  const StepLds L = step_lds(lds, D, a.plan, EPL);
+  // the wave index as a scalar: plan fields picked by wave then load as scalar loads (a vector load of them would
+  // queue behind the sub-key loads issued early below and wait for them)
+  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int st = blockIdx.x;  // stream b * H + h; with one token the [B, 1, H] row index equals st
+  const int h = st % D.H;
+  // (members picked by kind or wave with conditionals, not indexed: a runtime index into a struct's array puts the
+  // struct in scratch memory)
+  auto pick2 = [](auto x0, auto x1, int i) { return i ? x1 : x0; };
+  auto pick4 = [](auto x0, auto x1, auto x2, auto x3, int i) { return i < 2 ? (i ? x1 : x0) : (i == 2 ? x2 : x3); };
+  // factor top-k of both queries: task kind * F + f on wave task % 4. Each wave issues the loads of its first
+  // task's first block now; they arrive while the candidate tables are built.
+  long long sumn = 0;
+  for (int f = 0; f < D.F; ++f) sumn += D.widths[f];
+  const A* subh = (const A*)a.subkeys + (long long)h * sumn * D.dk;
+  auto task_in = [&](int task, int* f, const A** qv, const A** tab) {
+    const int kind = task / D.F;
+    *f = task % D.F;
+    long long off = 0;
+    for (int g = 0; g < *f; ++g) off += D.widths[g];
+    *qv = (const A*)pick2(a.queries[0], a.queries[1], kind) + (long long)st * D.F * D.dk;
+    *tab = subh + off * D.dk;
+  };
+  FactorBlock<A, NPL> fb;
+  if (wv < 2 * D.F) {
+    int f;
+    const A *qv, *tab;
+    task_in(wv, &f, &qv, &tab);
+    factor_load<A, NPL>(D, f, qv, tab, 0, fb);
+  }
+  // candidate tables: threads 0-127 build the write table, 128-255 the read table (small tables: waves 0 and 2)
+  {
+    const int kind = wv >> 1, t = tid & 127;
+    const TopkPlan& P = kind ? a.plan[1] : a.plan[0];
+    if (cand_one_wave(a.plan[0], D.F) && cand_one_wave(a.plan[1], D.F)) {
+      if (t < 64) cand_table_wave(P, pick2(L.ctab[0], L.ctab[1], kind), lane);
+    } else {
+      cand_offsets(P, D.F, pick2(L.offs[0], L.offs[1], kind), t, 128);
+      __syncthreads();
+      cand_emit(P, D.F, pick2(L.offs[0], L.offs[1], kind), pick2(L.ctab[0], L.ctab[1], kind), t, 128);
+    }
+  }
+  uint64_t* wscr = pick4(L.scratch[0], L.scratch[1], L.scratch[2], L.scratch[3], wv);
+  uint64_t* wsrt = pick4(L.sorted[0], L.sorted[1], L.sorted[2], L.sorted[3], wv);
+  for (int task = wv; task < 2 * D.F; task += 4) {
+    const int kind = task / D.F;
+    int f;
+    const A *qv, *tab;
+    task_in(task, &f, &qv, &tab);
+    if (task != wv) factor_load<A, NPL>(D, f, qv, tab, 0, fb);
+    const TopkPlan& P = kind ? a.plan[1] : a.plan[0];
+    wave_factor_topk<A, NPL>(D, P, f, qv, tab, pick2(L.fsc[0], L.fsc[1], kind), pick2(L.fid[0], L.fid[1], kind),
+                             wscr, wsrt, fb);
+  }
+  __syncthreads();  // factor lists and candidate tables complete
+  if (wv < 2) {  // merges: wave 0 the write query, wave 1 the read query
+    const int kind = wv;
+    const TopkPlan& P = kind ? a.plan[1] : a.plan[0];
+    int32_t* ids = kind ? L.rid : L.wid;
+    wave_merge_topk<CPL>(D, P, pick2(L.ctab[0], L.ctab[1], kind), pick2(L.fsc[0], L.fsc[1], kind),
+                         pick2(L.fid[0], L.fid[1], kind), wscr, wsrt, ids, kind ? L.rwt : L.wwt);
+    int32_t* uid = pick2(a.user_ids[0], a.user_ids[1], kind);
+    if (uid)
+      for (int r = lane; r < P.k; r += 64) uid[(long long)st * P.k + r] = ids[r];
+  }
+  __syncthreads();
+  const float al = to_f<A>(((const A*)a.alpha)[st]);
+  const float be = to_f<A>(((const A*)a.beta)[st]);
+  const long long rowsd = D.rows * D.ld;
+  step_rows<A, Bk>(D, L, (const Bk*)a.bank_in + (long long)st * rowsd, (Bk*)a.bank_out + (long long)st * rowsd,
+                   (const A*)a.values + (long long)st * D.d, (A*)a.out + (long long)st * D.d, al, be);
 }
 
 static void step_shape(const Dims& D, const DecodeArgs& a, int* npl, int* cpl) {
@@ -478,6 +492,92 @@ hipError_t launch_decode_step(const Dims& D, const DecodeArgs& a, hipStream_t st
   if (D.act == SDM_BF16)
     return D.bank == SDM_BF16 ? launch_step_t<bf16_t, bf16_t>(D, a, st) : launch_step_t<bf16_t, float>(D, a, st);
   return D.bank == SDM_BF16 ? launch_step_t<float, bf16_t>(D, a, st) : launch_step_t<float, float>(D, a, st);
+}
+
+// ------------------------------------------------------------------------------------------- multi-step decode
+// K consecutive decode steps of every stream in one launch, after the batched top-k of all K tokens (ids and
+// float32 slot scores, row-major [B, K, H, k]; the top-k reads no bank, so all K run in parallel beforehand). One
+// workgroup per stream runs its K steps in order: per step, waves 0 and 1 form the write and read weights exactly
+// as the one-launch step does (wave_rank_softmax on the same scores), then step_rows. Step k + 1 reads the rows
+// step k wrote (every wave waits for its own stores, then a barrier), so the result is K one-launch steps, bit for
+// bit (the same arithmetic on the same values in the same order).
+__host__ __device__ inline StepLds steps_lds(unsigned char* base, const Dims& D, int epl) {
+  StepLds L = {};  // only the fields the steps kernel uses are set
+  size_t o = 0;
+  auto take = [&](size_t b) {
+    unsigned char* p = base + o;
+    o = (o + b + 15) & ~(size_t)15;
+    return p;
+  };
+  L.wid = (int32_t*)take((size_t)D.W * 4);
+  L.wwt = (float*)take((size_t)D.W * 4);
+  L.rid = (int32_t*)take((size_t)D.R * 4);
+  L.rwt = (float*)take((size_t)D.R * 4);
+  L.rmatch = (int32_t*)take((size_t)D.R * 4);
+  L.part = (float*)take((size_t)2 * 4 * 64 * epl * 4);
+  L.bytes = o;
+  return L;
+}
+
+template <typename A, typename Bk>
+__global__ __launch_bounds__(STEP_NT) void decode_steps_kernel(Dims D, DecodeArgs a, int K) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  const StepLds L = steps_lds(lds, D, DLane<Bk>::EPL);
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int st = blockIdx.x, b = st / D.H, h = st % D.H;
+  const long long rowsd = D.rows * D.ld;
+  const Bk* bin = (const Bk*)a.bank_in + (long long)st * rowsd;
+  Bk* bout = (Bk*)a.bank_out + (long long)st * rowsd;
+  // waves 0 and 1 hold the next step's write / read ids and scores in registers (lane r: rank r; k <= 64), loaded
+  // one step ahead so that their latency hides behind the current step's rows
+  const int kk = wv ? D.R : D.W;
+  const int32_t* gid = wv ? a.rid : a.wid;
+  const float* gsc = wv ? a.rwt : a.wwt;
+  int32_t nid = 0;
+  float nsc = 0.0f;
+  auto fetch = [&](int k) {
+    const long long row = ((long long)b * K + k) * D.H + h;
+    if (wv < 2 && lane < kk) {
+      nid = gid[row * kk + lane];
+      nsc = gsc[row * kk + lane];
+    }
+  };
+  fetch(0);
+  for (int k = 0; k < K; ++k) {
+    const long long row = ((long long)b * K + k) * D.H + h;
+    if (wv < 2) {  // wave 0: the write ids and weights, wave 1: the read ones
+      int32_t* ids = wv ? L.rid : L.wid;
+      int32_t* uid = wv ? a.user_ids[1] : a.user_ids[0];
+      if (lane < kk) {
+        ids[lane] = nid;
+        if (uid) uid[row * kk + lane] = nid;
+      }
+      const float s0 = __shfl(nsc, 0, 64);
+      const float mine = nsc;
+      wave_rank_softmax(kk, [&](int r) { return r == 0 ? s0 : mine; }, wv ? L.rwt : L.wwt);
+      if (k + 1 < K) fetch(k + 1);
+    }
+    __syncthreads();
+    const float al = to_f<A>(((const A*)a.alpha)[row]);
+    const float be = to_f<A>(((const A*)a.beta)[row]);
+    step_rows<A, Bk>(D, L, k == 0 ? bin : bout, bout, (const A*)a.values + row * D.d, (A*)a.out + row * D.d, al, be);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's row stores have completed before any wave reads them next step
+    __syncthreads();
+  }
+}
+
+template <typename A, typename Bk>
+static hipError_t launch_steps_t(const Dims& D, const DecodeArgs& a, int K, hipStream_t st) {
+  const size_t lds = steps_lds(nullptr, D, DLane<Bk>::EPL).bytes;
+  hipLaunchKernelGGL((decode_steps_kernel<A, Bk>), dim3((unsigned)D.S), dim3(STEP_NT), lds, st, D, a, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_steps(const Dims& D, const DecodeArgs& a, int K, hipStream_t st) {
+  if (D.S == 0 || K == 0) return hipSuccess;
+  if (D.act == SDM_BF16)
+    return D.bank == SDM_BF16 ? launch_steps_t<bf16_t, bf16_t>(D, a, K, st) : launch_steps_t<bf16_t, float>(D, a, K, st);
+  return D.bank == SDM_BF16 ? launch_steps_t<float, bf16_t>(D, a, K, st) : launch_steps_t<float, float>(D, a, K, st);
 }
 
 __global__ __launch_bounds__(256) void copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, size_t n) {

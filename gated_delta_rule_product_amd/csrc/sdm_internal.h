@@ -338,6 +338,10 @@ hipError_t launch_decode(const Dims& D, const DecodeArgs& a, hipStream_t st);
 // (then nothing is launched).
 bool decode_step_fits(const Dims& D, const DecodeArgs& a);
 hipError_t launch_decode_step(const Dims& D, const DecodeArgs& a, hipStream_t st);
+// K consecutive steps per stream (inputs [B, K, H, ...]) after the batched top-k of all K tokens: a.wid / a.rid hold
+// the ids and a.wwt / a.rwt the float32 slot scores (not weights), row-major [B, K, H, W|R]. Bitwise equal to K
+// one-launch steps; needs the shapes decode_step_fits accepts.
+hipError_t launch_decode_steps(const Dims& D, const DecodeArgs& a, int K, hipStream_t st);
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t st);
 // Shared bank: owner[h][slot] = -1 for every slot, flag = 0; then every addressed slot is claimed by its stream and
 // a slot claimed by two streams of a head sets the flag.

@@ -281,6 +281,33 @@ __device__ __forceinline__ double wave_sum_d(double x) {
   return ((readlane_d<0>(x) + readlane_d<16>(x)) + readlane_d<32>(x)) + readlane_d<48>(x);
 }
 
+// Softmax of the k selected slot scores, best first (score(r): the float32 score of rank r), as the decode step
+// computes it: fp64 exponentials relative to the best score, rank r = lane + 64 u kept on lane `lane`, per-lane
+// partial sums in u order, then wave_sum_d; wts[r] receives the float32 weight. One wave; every lane active.
+template <typename ScoreFn>
+__device__ __forceinline__ void wave_rank_softmax(int k, ScoreFn score, float* wts) {
+  const int lane = lane_id();
+  const double m = (double)score(0);
+  constexpr int RPL = MAX_K / 64;
+  double ex[RPL];
+  double zpart = 0.0;
+#pragma unroll
+  for (int u = 0; u < RPL; ++u) {
+    const int r = lane + 64 * u;
+    ex[u] = 0.0;
+    if (64 * u < k && r < k) {
+      ex[u] = exp((double)score(r) - m);
+      zpart += ex[u];
+    }
+  }
+  const double z = wave_sum_d(zpart);
+#pragma unroll
+  for (int u = 0; u < RPL; ++u) {
+    const int r = lane + 64 * u;
+    if (64 * u < k && r < k) wts[r] = (float)(ex[u] / z);
+  }
+}
+
 template <int CPL>
 __device__ void wave_merge_topk(const Dims& D, const TopkPlan& P, const uint64_t* cand, const float* fsc,
                                 const uint16_t* fid, uint64_t* scratch, uint64_t* sorted, int32_t* ids, float* wts) {
@@ -313,31 +340,13 @@ __device__ void wave_merge_topk(const Dims& D, const TopkPlan& P, const uint64_t
     ck[j] = c < P.ncand ? ((uint64_t)desc_key(S[j]) << 32) | ((uint64_t)ps[j] << 20) | (uint64_t)c : ~0ull;
   }
   wave_select_sorted<CPL, MERGE_RB>(ck, k, scratch, sorted);
-  const double m = (double)desc_key_value((uint32_t)(sorted[0] >> 32));
-  // rank r = lane + 64 u (u < MAX_K / 64): its exponential is kept for the weight
-  constexpr int RPL = MAX_K / 64;
-  double ex[RPL];
-  double zpart = 0.0;
-#pragma unroll
-  for (int u = 0; u < RPL; ++u) {
-    const int r = lane + 64 * u;
-    ex[u] = 0.0;
-    if (64 * u < k && r < k) {
-      const uint64_t kk = sorted[r];
-      const uint64_t t = cand[(int)(kk & 0xFFFFF)];
-      long long id = 0;
-      for (int f = 0; f < F; ++f) id = id * D.widths[f] + fid[f * kpmax + (int)((t >> (16 * f)) & 0xFFFF)];
-      ids[r] = (int32_t)id;
-      ex[u] = exp((double)desc_key_value((uint32_t)(kk >> 32)) - m);
-      zpart += ex[u];
-    }
+  for (int r = lane; r < k; r += 64) {
+    const uint64_t t = cand[(int)(sorted[r] & 0xFFFFF)];
+    long long id = 0;
+    for (int f = 0; f < F; ++f) id = id * D.widths[f] + fid[f * kpmax + (int)((t >> (16 * f)) & 0xFFFF)];
+    ids[r] = (int32_t)id;
   }
-  const double z = wave_sum_d(zpart);
-#pragma unroll
-  for (int u = 0; u < RPL; ++u) {
-    const int r = lane + 64 * u;
-    if (64 * u < k && r < k) wts[r] = (float)(ex[u] / z);
-  }
+  wave_rank_softmax(k, [&](int r) { return desc_key_value((uint32_t)(sorted[r] >> 32)); }, wts);
   wave_sync();
 }
 

@@ -108,7 +108,7 @@ typedef struct {
 
 enum { SDM_SCORING_AUTO = 0, SDM_SCORING_DIRECT = 1, SDM_SCORING_FILTERED = 2 };
 
-enum { SDM_OP_TOPK = 0, SDM_OP_WRITE_READ = 1, SDM_OP_DECODE = 2, SDM_OP_BACKWARD = 3 };
+enum { SDM_OP_TOPK = 0, SDM_OP_WRITE_READ = 1, SDM_OP_DECODE = 2, SDM_OP_BACKWARD = 3, SDM_OP_DECODE_STEPS = 4 };
 
 /* Message for the last non-OK status returned on the calling thread ("" if none). Valid until the next call. */
 const char* sdm_last_error(void);
@@ -193,6 +193,21 @@ sdm_status sdm_decode_step(const sdm_config* cfg, const void* write_keys, const 
                            const void* values, const void* forget_gate, const void* input_gate, const void* subkeys,
                            const void* bank_in, void* bank_out, void* out, int32_t* write_idx, int32_t* read_idx,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Consecutive decode steps in one call (CHANGELOG 2.0.0 "New": a single-token decode kernel; README "CUDA graphs":
+ * decode steps replayed without host work in between). cfg.tokens = K >= 0 steps; every input is [B, K, H, ...]
+ * (token k of stream (b, h) is step k's input), out [B, K, H, d], write_idx / read_idx (optional) [B, K, H, W|R].
+ * The result equals K calls of sdm_decode_step on the tokens in order, bit for bit: the same out rows, ids and
+ * final bank (bank_out == bank_in: every step in place; a disjoint bank_out: it receives bank_in's copy once, then
+ * every step runs on it, bank_in unchanged). The steps' top-k reads no bank, so all K run first, in parallel; then
+ * one launch runs each stream's K steps in order. Shapes: those of sdm_decode_step's one-launch step (num_writes,
+ * num_reads <= 64, <= 256 sub-keys per factor, <= 1024 candidate tuples, F * subkey_dim elements a 16-byte multiple,
+ * queries and sub-keys 16-byte aligned); others are refused with SDM_ERR_RANGE before any work. Workspace:
+ * SDM_OP_DECODE_STEPS with this cfg. */
+sdm_status sdm_decode_steps(const sdm_config* cfg, const void* write_keys, const void* read_queries,
+                            const void* values, const void* forget_gate, const void* input_gate, const void* subkeys,
+                            const void* bank_in, void* bank_out, void* out, int32_t* write_idx, int32_t* read_idx,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* The decode step without a workspace, for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation). Same arguments, checks, kernels and results as

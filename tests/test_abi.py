@@ -194,7 +194,7 @@ def test_backward_settings_and_refusals(lib):
     big = _cfg(batch=64, heads=64, tokens=4096, num_writes=128)
     assert _status(big, B.SDM_OP_BACKWARD)[0] == B.SDM_ERR_RANGE and "snapshot" in B.last_error()
     assert _status(_cfg(batch=64, heads=64, tokens=4096, num_writes=64), B.SDM_OP_BACKWARD)[0] == B.SDM_OK
-    assert _status(_cfg(), 4)[0] == B.SDM_ERR_RANGE  # no op 4
+    assert _status(_cfg(), 5)[0] == B.SDM_ERR_RANGE  # no op 5
 
 
 @fake_pointers
@@ -336,3 +336,29 @@ def test_decode_noalloc_refuses_before_device_work(lib):
     assert B.workspace_size(big, B.SDM_OP_DECODE) > B.NOALLOC_SCRATCH_BYTES
     assert lib.sdm_decode_step_noalloc(ctypes.byref(big), *p, None) == B.SDM_ERR_RANGE
     assert "scratch" in B.last_error()
+
+
+def test_decode_steps_settings(lib):
+    """sdm_decode_steps: its workspace grows with the steps (ids and scores of every token), a shared bank is
+    refused, and shapes outside the one-launch step (W > 64, wide factors) are refused before any device work."""
+    s1, n1 = _status(_cfg(tokens=1), B.SDM_OP_DECODE_STEPS)
+    s8, n8 = _status(_cfg(tokens=8), B.SDM_OP_DECODE_STEPS)
+    assert s1 == B.SDM_OK and s8 == B.SDM_OK and n8 > n1
+    assert _status(_cfg(tokens=8, shared_bank=True), B.SDM_OP_DECODE_STEPS)[0] == B.SDM_ERR_RANGE
+
+
+@fake_pointers
+def test_decode_steps_refuses_before_device_work(lib):
+    base, step = 1 << 40, 1 << 36
+    p = [_fake(base + i * step) for i in range(11)]
+    ws = _fake(base + 40 * step)
+    for cfg in (_cfg(tokens=4, num_writes=96, widths=(32, 32)), _cfg(tokens=4, widths=(512, 2))):
+        n = B.workspace_size(cfg, B.SDM_OP_DECODE_STEPS)
+        assert lib.sdm_decode_steps(ctypes.byref(cfg), *p, ws, n, None) == B.SDM_ERR_RANGE
+        assert "sdm_decode_step per token" in B.last_error()
+    cfg = _cfg(tokens=4)
+    n = B.workspace_size(cfg, B.SDM_OP_DECODE_STEPS)
+    q = list(p)
+    q[7] = _fake(base + 6 * step + 256)  # bank_out starts inside bank_in
+    assert lib.sdm_decode_steps(ctypes.byref(cfg), *q, ws, n, None) == B.SDM_ERR_ALIAS
+    assert lib.sdm_decode_steps(ctypes.byref(cfg), *p, ws, n - 1, None) == B.SDM_ERR_WORKSPACE

@@ -826,3 +826,98 @@ def test_decode_exact_ties(kind):
     assert np.array_equal(w.cpu().numpy(), ref["widx"]) and np.array_equal(r.cpu().numpy(), ref["ridx"])
     assert rowwise_rel(to_np(o), ref["out"]) <= RTOL["f32"]
     assert rowwise_rel(to_np(b), ref["bank"]) <= RTOL["f32"]
+
+
+# ------------------------------------------------------------------------------------------------ multi-step decode
+STEPS_SHAPES = [  # d, W, R, widths, dk, act, bank, batch
+    (256, 64, 64, (32, 32), 32, "f32", "f32", 8),     # the decode workload's shapes (8 streams of 128)
+    (512, 48, 40, (32, 16), 16, "bf16", "f32", 3),    # two column passes, W != R
+    (256, 64, 64, (16, 8, 8), 16, "bf16", "bf16", 4), # three factors, bf16 bank
+    (64, 7, 64, (64, 4), 8, "f32", "f32", 5),         # partial column pass, few writes
+]
+
+
+@pytest.mark.parametrize("d,W,R,widths,dk,act,bank,batch", STEPS_SHAPES)
+def test_decode_steps_equal_sequential_steps(d, W, R, widths, dk, act, bank, batch):
+    """sdm_decode_steps over K tokens equals K sdm_decode_step calls bit for bit (out, ids, bank; donated and
+    copied), and the oracle's recurrence over the K tokens within tolerance with ids exact."""
+    K = 12
+    s = synth.Shape(batch, K, 2, widths, dk, d, W, R, 1, act, bank, name="steps")
+    x = synth.make_inputs(s, seed=71)
+    at, bt = TORCH_DT[act], TORCH_DT[bank]
+    t = {k: to_dev(x[k], at) for k in ("wkeys", "rq", "values", "alpha", "beta")}
+    sub = to_dev(x["subkeys"], at)
+    kw = dict(widths=widths, num_writes=W, num_reads=R)
+    print(f"decode steps d={d} W={W} R={R} widths={widths} {act}/{bank} B={batch} K={K}", flush=True)
+    b_seq = to_dev(x["bank"], bt)
+    outs, wis, ris = [], [], []
+    for k in range(K):
+        one = {n: v[:, k:k + 1].contiguous() for n, v in t.items()}
+        o, wi, ri, _ = binding.sdm_decode_step(one["wkeys"], one["rq"], one["values"], one["alpha"], one["beta"],
+                                               sub, b_seq, want_index=True, **kw)
+        outs.append(o)
+        wis.append(wi)
+        ris.append(ri)
+    b_don = to_dev(x["bank"], bt)
+    o_don, w_don, r_don, _ = binding.sdm_decode_steps(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"], sub,
+                                                      b_don, want_index=True, **kw)
+    b_in = to_dev(x["bank"], bt)
+    b_out = torch.empty_like(b_in)
+    o_cp, _, _, _ = binding.sdm_decode_steps(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"], sub, b_in,
+                                             b_out, **kw)
+    torch.cuda.synchronize()
+    seq_out = torch.cat(outs, dim=1)
+    assert torch.equal(o_don, seq_out), "multi-step out differs from sequential steps"
+    assert torch.equal(w_don, torch.cat(wis, dim=1)) and torch.equal(r_don, torch.cat(ris, dim=1))
+    assert torch.equal(b_don, b_seq), "multi-step bank differs from sequential steps"
+    assert torch.equal(o_cp, seq_out) and torch.equal(b_out, b_seq), "copied multi-step differs"
+    assert torch.equal(b_in, to_dev(x["bank"], bt)), "copied multi-step changed bank_in"
+    ref = run_oracle(s, x)
+    assert np.array_equal(to_np(w_don), ref["widx"]) and np.array_equal(to_np(r_don), ref["ridx"])
+    assert rowwise_rel(to_np(o_don), ref["out"]) <= max(RTOL[act], RTOL[bank])
+    assert rowwise_rel(to_np(b_don), ref["bank"]) <= RTOL[bank]
+
+
+def test_decode_steps_zero_steps_and_graph_replay():
+    """K = 0 does nothing; a captured multi-step call replays to the eager bits."""
+    s = synth.WORKLOADS["decode_b128"].with_(batch=4, tokens=6)
+    x = synth.make_inputs(s, seed=72)
+    t = {k: to_dev(x[k], torch.float32) for k in ("wkeys", "rq", "values", "alpha", "beta", "subkeys")}
+    kw = dict(widths=s.widths, num_writes=s.num_writes, num_reads=s.num_reads)
+    bank0 = to_dev(x["bank"], torch.float32)
+    bank = bank0.clone()
+    z = {k: v[:, :0].contiguous() for k, v in t.items() if k != "subkeys"}
+    binding.sdm_decode_steps(z["wkeys"], z["rq"], z["values"], z["alpha"], z["beta"], t["subkeys"], bank, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(bank, bank0)
+    cfg = binding.make_config(s.batch, s.tokens, s.heads, s.widths, s.subkey_dim, s.head_dim, s.num_writes,
+                              s.num_reads, 1, binding.SDM_F32, binding.SDM_F32, s.rows)
+    ws = torch.empty(binding.workspace_size(cfg, binding.SDM_OP_DECODE_STEPS), dtype=torch.uint8, device=DEV)
+    out = torch.empty((s.batch, s.tokens, s.heads, s.head_dim), device=DEV)
+
+    def run():
+        binding.sdm_decode_steps(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"], t["subkeys"], bank,
+                                 out=out, workspace=ws, **kw)
+
+    run()
+    torch.cuda.synchronize()
+    ref_out, ref_bank = out.clone(), bank.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        bank.copy_(bank0)
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for rep in range(3):
+        bank.copy_(bank0)
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(bank, ref_bank), f"replay {rep} differs"
+        run()  # eager work between replays
+        torch.cuda.synchronize()
