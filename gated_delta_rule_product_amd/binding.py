@@ -146,7 +146,9 @@ def load():
             lcfgp = ctypes.POINTER(SdmLayerConfig)
             lib.sdm_layer_workspace_size.argtypes = [lcfgp, ctypes.POINTER(ctypes.c_size_t)]
             lib.sdm_layer_workspace_size.restype = ctypes.c_int
-            lib.sdm_layer_forward.argtypes = [lcfgp] + [_vp] * 11 + [ctypes.c_size_t, _vp]
+            lib.sdm_layer_forward.argtypes = [lcfgp] + [_vp] * 12 + [ctypes.c_size_t, _vp]
+            lib.sdm_bank_grad_sum.restype = ctypes.c_int
+            lib.sdm_bank_grad_sum.argtypes = [cfgp, _vp, _vp, _vp]
             lib.sdm_layer_forward.restype = ctypes.c_int
             lib.sdm_profile_enable.argtypes = [ctypes.c_int32]
             lib.sdm_profile_read.restype = ctypes.c_int
@@ -309,7 +311,8 @@ def layer_in_features(heads, widths, subkey_dim, head_dim) -> int:
 
 
 def sdm_layer_forward(x, w_in, a_log, dt_bias, w_out, subkeys, bank, *, heads, widths, num_writes, num_reads,
-                      chunk_size, want_index=False, y=None, workspace=None, return_workspace=False):
+                      chunk_size, want_index=False, y=None, workspace=None, return_workspace=False,
+                      initial_bank=None):
     """The layer's forward: projections of x [B, T, Dm] (bf16) by w_in, gates, the write/read op on bank
     [B, H, bank_rows, d] (advances in place), output projection by w_out [Dm, H d]. Returns (y, write_idx,
     read_idx), plus the workspace (uint8) with return_workspace (its first regions: layer_workspace_views)."""
@@ -326,6 +329,10 @@ def sdm_layer_forward(x, w_in, a_log, dt_bias, w_out, subkeys, bank, *, heads, w
     if bank.dim() != 4 or bank.shape[0] != B or bank.shape[1] != H:
         raise ValueError(f"bank has shape {tuple(bank.shape)}, expected ({B}, {H}, bank_rows, d)")
     ld = _bank_ld(bank, "bank")
+    if initial_bank is not None:
+        if tuple(initial_bank.shape) != (H,) + tuple(bank.shape[2:]) or initial_bank.dtype != bank.dtype or \
+                _bank_ld(initial_bank.unsqueeze(0), "initial_bank") != ld:
+            raise ValueError("initial_bank must be [heads, bank_rows, d] with the bank's dtype and row stride")
     lc = SdmLayerConfig()
     lc.op = make_config(B, T, H, widths, dk, d, num_writes, num_reads, chunk_size, SDM_BF16, _dt(bank),
                         bank.shape[2], ld)
@@ -340,7 +347,7 @@ def sdm_layer_forward(x, w_in, a_log, dt_bias, w_out, subkeys, bank, *, heads, w
     widx = torch.empty((B, T, H, num_writes), dtype=torch.int32, device=x.device) if want_index else None
     ridx = torch.empty((B, T, H, num_reads), dtype=torch.int32, device=x.device) if want_index else None
     _check(load().sdm_layer_forward(ctypes.byref(lc), _ptr(x), _ptr(w_in), _ptr(a_log), _ptr(dt_bias), _ptr(w_out),
-                                    _ptr(subkeys), _ptr(bank), _ptr(y), _ptr(widx), _ptr(ridx), _ptr(ws),
+                                    _ptr(subkeys), _ptr(initial_bank), _ptr(bank), _ptr(y), _ptr(widx), _ptr(ridx), _ptr(ws),
                                     0 if ws is None else ws.numel(), _stream(x.device)))
     return (y, widx, ridx, ws) if return_workspace else (y, widx, ridx)
 
@@ -520,6 +527,23 @@ def sdm_decode_steps(write_keys, read_queries, values, forget_gate, input_gate, 
                                    _ptr(out), _ptr(widx), _ptr(ridx), _ptr(ws), 0 if ws is None else ws.numel(),
                                    _stream(bank_in.device)))
     return out, widx, ridx, bank_out
+
+
+def sdm_bank_grad_sum(grad_bank, *, heads, widths, head_dim, out=None):
+    """Gradient of a learned initial bank copied into every batch row: grad_bank [B, H, bank_rows, d] float32 (rows
+    possibly padded) summed over the batch in order into [H, bank_rows, d] (the same row stride; rows >= N and the
+    padding are left as `out` had them, zeros when out is None)."""
+    B, H, rows, d = grad_bank.shape
+    ld = _bank_ld(grad_bank, "grad_bank")
+    if grad_bank.dtype != torch.float32:
+        raise ValueError("grad_bank must be float32")
+    if out is None:
+        out = torch.zeros((H, rows, ld), dtype=torch.float32, device=grad_bank.device)[..., :d]
+    if tuple(out.shape) != (H, rows, d) or _bank_ld(out.unsqueeze(0), "out") != ld:
+        raise ValueError("out must be [heads, bank_rows, d] float32 with grad_bank's row stride")
+    cfg = make_config(B, 1, H, widths, 1, d, 1, 1, 1, SDM_F32, SDM_F32, rows, ld)
+    _check(load().sdm_bank_grad_sum(ctypes.byref(cfg), _ptr(grad_bank), _ptr(out), _stream(grad_bank.device)))
+    return out
 
 
 NOALLOC_SCRATCH_BYTES = 8 << 20  # SDM_NOALLOC_SCRATCH_BYTES in include/sdm.h

@@ -84,6 +84,17 @@ sdm_status make_plan(const Dims& D, int k, const char* what, TopkPlan* P) {
   return SDM_OK;
 }
 
+// The chunk the kernels run for a requested chunk_size: the chunk_size itself when it fits their limits (at most
+// MAX_CHUNK tokens and MAX_CHUNK_EVENTS write events), else its largest divisor that does. The chunk size changes
+// results only through rounding (CHANGELOG 2.0.0, "Upgrading from v1"), so equal sub-chunks give a result of the
+// requested chunk size; chunk boundaries still fall on every multiple of chunk_size, so calls split there give the
+// bits of one call.
+int kernel_chunk(int C, int W) {
+  for (int c = C; c >= 1; --c)
+    if (C % c == 0 && c <= MAX_CHUNK && (long long)c * W <= MAX_CHUNK_EVENTS) return c;
+  return 1;
+}
+
 // op: SDM_OP_TOPK (k given), SDM_OP_WRITE_READ, SDM_OP_DECODE, SDM_OP_BACKWARD (the write/read's config),
 // SDM_OP_DECODE_STEPS (tokens = the number of steps)
 sdm_status validate(const sdm_config* cfg, int op, int k, Dims* D, TopkPlan* pw, TopkPlan* pr) {
@@ -154,11 +165,10 @@ sdm_status validate(const sdm_config* cfg, int op, int k, Dims* D, TopkPlan* pw,
                 "(2^31 or more)", (long long)D->S * D->T * D->W);
   if (chunked) {
     const int C = cfg->chunk_size;
-    if (C < 1 || C > MAX_CHUNK) return fail(SDM_ERR_RANGE, "chunk_size = %d out of range [1, %d]", C, MAX_CHUNK);
-    if ((long long)C * D->W > MAX_CHUNK_EVENTS)
-      return fail(SDM_ERR_RANGE, "chunk_size * num_writes = %lld exceeds %d", (long long)C * D->W, MAX_CHUNK_EVENTS);
-    D->C = C;
-    D->nch = (D->T + C - 1) / C;
+    if (C < 1 || C > MAX_CHUNK_SIZE)
+      return fail(SDM_ERR_RANGE, "chunk_size = %d out of range [1, %d]", C, MAX_CHUNK_SIZE);
+    D->C = kernel_chunk(C, D->W);
+    D->nch = (D->T + D->C - 1) / D->C;
   } else {
     D->C = 1;
     D->nch = 1;
@@ -922,9 +932,9 @@ sdm_status sdm_layer_workspace_size(const sdm_layer_config* cfg, size_t* bytes) 
 }
 
 sdm_status sdm_layer_forward(const sdm_layer_config* cfg, const void* x, const void* w_in, const float* a_log,
-                             const float* dt_bias, const void* w_out, const void* subkeys, void* bank, void* y,
-                             int32_t* write_idx, int32_t* read_idx, void* workspace, size_t workspace_bytes,
-                             void* stream) {
+                             const float* dt_bias, const void* w_out, const void* subkeys, const void* initial_bank,
+                             void* bank, void* y, int32_t* write_idx, int32_t* read_idx, void* workspace,
+                             size_t workspace_bytes, void* stream) {
   LayerWs L;
   TRY(layer_layout(cfg, &L));
   const sdm_config& oc = cfg->op;
@@ -943,9 +953,9 @@ sdm_status sdm_layer_forward(const sdm_layer_config* cfg, const void* x, const v
     TRY(need(subkeys, "subkeys"));
     TRY(need(bank, "bank"));
   }
-  const void* al[] = {x, w_in, a_log, dt_bias, w_out, y, subkeys, bank};
-  const char* an[] = {"x", "w_in", "a_log", "dt_bias", "w_out", "y", "subkeys", "bank"};
-  for (int i = 0; i < 8; ++i) TRY(aligned(al[i], 16, an[i]));
+  const void* al[] = {x, w_in, a_log, dt_bias, w_out, y, subkeys, bank, initial_bank};
+  const char* an[] = {"x", "w_in", "a_log", "dt_bias", "w_out", "y", "subkeys", "bank", "initial_bank"};
+  for (int i = 0; i < 9; ++i) TRY(aligned(al[i], 16, an[i]));
   TRY(check_ws(workspace, workspace_bytes, L.total));
   // the op's own checks (bank rows, pitch, ...) run here too, before any launch: a refused call does no work
   size_t opws = 0;
@@ -960,13 +970,14 @@ sdm_status sdm_layer_forward(const sdm_layer_config* cfg, const void* x, const v
                        {a_log, (size_t)H * 4, "a_log"},
                        {dt_bias, (size_t)H * 4, "dt_bias"},
                        {w_out, (size_t)(Dm * H * d * 2), "w_out"},
-                       {subkeys, (size_t)(H * sumn * oc.subkey_dim * 2), "subkeys"}};
+                       {subkeys, (size_t)(H * sumn * oc.subkey_dim * 2), "subkeys"},
+                       {initial_bank, (size_t)H * (size_t)oc.bank_rows * (size_t)ld * eb, "initial_bank"}};
   const Range outs[] = {{y, (size_t)(M * Dm * 2), "y"},
                         {workspace, L.total, "workspace"},
                         {bank, bank_bytes, "bank"},
                         {write_idx, (size_t)(M * H * oc.num_writes * 4), "write_idx"},
                         {read_idx, (size_t)(M * H * oc.num_reads * 4), "read_idx"}};
-  TRY(check_alias(outs, 5, ins, 6));
+  TRY(check_alias(outs, 5, ins, 7));
   TRY(check_device());
   if (M == 0 || H == 0) return ok();
   hipStream_t st = (hipStream_t)stream;
@@ -995,6 +1006,13 @@ sdm_status sdm_layer_forward(const sdm_layer_config* cfg, const void* x, const v
                    return launch_gates(gin, gin + H, (int)(2 * H), a_log, dt_bias, M * H, (int)H, alpha, beta, st);
                  }),
                  "gates launch"));
+  if (initial_bank) {  // the per-sequence copy of the learned bank into every batch row
+    long long N = 1;
+    for (int f = 0; f < oc.num_factors; ++f) N *= oc.factor_widths[f];
+    TRY(hip_status(launch_bank_broadcast(initial_bank, bank, oc.batch, (int)H, N, oc.bank_rows, (int)d, ld, (int)eb,
+                                         st),
+                   "bank copy launch"));
+  }
   TRY(write_read_impl(&oc, keys, queries, values, alpha, beta, subkeys, bank, o, nullptr, write_idx, read_idx,
                       ws + L.op, workspace_bytes - L.op, stream));
   GemmArgs go;
@@ -1007,6 +1025,32 @@ sdm_status sdm_layer_forward(const sdm_layer_config* cfg, const void* x, const v
   go.nseg = 1;
   go.seg[0] = {(int)Dm, (bf16_t*)y, (int)Dm};
   TRY(hip_status(timed(SDM_K_DENSE, st, [&] { return launch_gemm_bf16(go, st); }), "output projection launch"));
+  return ok();
+}
+
+sdm_status sdm_bank_grad_sum(const sdm_config* cfg, const float* grad_bank, float* grad_initial_bank,
+                             void* stream) {
+  Dims D;
+  TopkPlan pw, pr;
+  TRY(validate(cfg, SDM_OP_WRITE_READ, 0, &D, &pw, &pr));
+  if (D.shared) return fail(SDM_ERR_RANGE, "sdm_bank_grad_sum takes per-stream bank gradients (shared_bank = 0)");
+  if (D.S > 0) {
+    TRY(need(grad_bank, "grad_bank"));
+    TRY(need(grad_initial_bank, "grad_initial_bank"));
+  }
+  TRY(aligned(grad_bank, 16, "grad_bank"));
+  TRY(aligned(grad_initial_bank, 16, "grad_initial_bank"));
+  if ((D.ld * 4) % 16 != 0 || D.d % 4 != 0)
+    return fail(SDM_ERR_LAYOUT, "the bank gradient's rows must be 16-byte multiples (head_dim and row stride)");
+  const size_t row_bytes = (size_t)D.rows * (size_t)D.ld * 4;
+  const Range ins[] = {{grad_bank, (size_t)D.S * row_bytes, "grad_bank"}};
+  const Range outs[] = {{grad_initial_bank, (size_t)D.H * row_bytes, "grad_initial_bank"}};
+  TRY(check_alias(outs, 1, ins, 1));
+  TRY(check_device());
+  if (D.S == 0) return ok();
+  TRY(hip_status(launch_bank_grad_sum(grad_bank, grad_initial_bank, D.B, D.H, D.N, D.rows, D.d, D.ld,
+                                      (hipStream_t)stream),
+                 "bank gradient sum launch"));
   return ok();
 }
 

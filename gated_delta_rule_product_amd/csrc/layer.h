@@ -24,4 +24,12 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t st);
 hipError_t launch_gates(const bf16_t* ga, const bf16_t* gb, int ldg, const float* a_log, const float* dt_bias,
                         long long S, int H, bf16_t* alpha, bf16_t* beta, hipStream_t st);
 
+// The layer's per-sequence bank copy: bank[b, h, j, :d] = init[h, j, :d] for every batch row b and slot j < N (rows
+// ld elements apart in both; esize 2 or 4 bytes; d * esize a multiple of 16).
+hipError_t launch_bank_broadcast(const void* init, void* bank, int B, int H, long long N, long long rows, int d,
+                                 long long ld, int esize, hipStream_t st);
+// grad_init[h, j, c] = sum over b = 0, 1, ... B-1 (in that order, float32) of grad_bank[b, h, j, c], j < N, c < d.
+hipError_t launch_bank_grad_sum(const float* grad_bank, float* grad_init, int B, int H, long long N, long long rows,
+                                int d, long long ld, hipStream_t st);
+
 }  // namespace sdm

@@ -219,6 +219,53 @@ __global__ __launch_bounds__(256) void gates_kernel(const bf16_t* ga, const bf16
   beta[s] = f_to_bf16(1.0f / (1.0f + expf(-b)));
 }
 
+// One thread per 16-byte piece of a slot row of one head: the piece is read once and stored into every batch row.
+__global__ __launch_bounds__(256) void bank_broadcast_kernel(const unsigned char* init, unsigned char* bank, int B,
+                                                             int H, long long N, long long rows, long long pieces,
+                                                             long long ldb) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;  // (h, j, piece)
+  if (i >= (long long)H * N * pieces) return;
+  const long long hp = i / pieces, p = i - hp * pieces;
+  const long long h = hp / N, j = hp - h * N;
+  const uint4 v = *(const uint4*)(init + (h * rows + j) * ldb + 16 * p);
+  for (int b = 0; b < B; ++b) *(uint4*)(bank + (((long long)b * H + h) * rows + j) * ldb + 16 * p) = v;
+}
+
+hipError_t launch_bank_broadcast(const void* init, void* bank, int B, int H, long long N, long long rows, int d,
+                                 long long ld, int esize, hipStream_t st) {
+  const long long pieces = (long long)d * esize / 16;
+  const long long n = (long long)H * N * pieces;
+  if (n == 0 || B == 0) return hipSuccess;
+  hipLaunchKernelGGL(bank_broadcast_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                     (const unsigned char*)init, (unsigned char*)bank, B, H, N, rows, pieces, ld * esize);
+  return hipGetLastError();
+}
+
+// One thread per 4 columns of a slot row of one head, the batch rows added in order.
+__global__ __launch_bounds__(256) void bank_grad_sum_kernel(const float* gb, float* gi, int B, int H, long long N,
+                                                            long long rows, long long quads, long long ld) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;  // (h, j, quad)
+  if (i >= (long long)H * N * quads) return;
+  const long long hq = i / quads, q = i - hq * quads;
+  const long long h = hq / N, j = hq - h * N;
+  float4 acc = *(const float4*)(gb + (h * rows + j) * ld + 4 * q);
+  for (int b = 1; b < B; ++b) {
+    const float4 v = *(const float4*)(gb + (((long long)b * H + h) * rows + j) * ld + 4 * q);
+    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  }
+  *(float4*)(gi + (h * rows + j) * ld + 4 * q) = acc;
+}
+
+hipError_t launch_bank_grad_sum(const float* grad_bank, float* grad_init, int B, int H, long long N, long long rows,
+                                int d, long long ld, hipStream_t st) {
+  const long long quads = d / 4;
+  const long long n = (long long)H * N * quads;
+  if (n == 0 || B == 0) return hipSuccess;
+  hipLaunchKernelGGL(bank_grad_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, grad_bank, grad_init,
+                     B, H, N, rows, quads, ld);
+  return hipGetLastError();
+}
+
 hipError_t launch_gates(const bf16_t* ga, const bf16_t* gb, int ldg, const float* a_log, const float* dt_bias,
                         long long S, int H, bf16_t* alpha, bf16_t* beta, hipStream_t st) {
   if (S == 0) return hipSuccess;

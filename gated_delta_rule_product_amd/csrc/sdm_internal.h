@@ -19,6 +19,7 @@ constexpr int MAX_CAND = 4096;       // candidate tuples prod(p_f + 1) <= k
 constexpr int MAX_FDK = 1024;        // F * dk
 constexpr int MAX_CHUNK = 128;       // chunk_size
 constexpr int MAX_CHUNK_EVENTS = 8192;  // chunk_size * num_writes
+constexpr int MAX_CHUNK_SIZE = 65536;   // requested chunk_size (larger chunks run as equal sub-chunks)
 constexpr int TOPK_NT = 256;
 constexpr int PLAN_NT = 512;
 constexpr int LOOP_NT = 512;

@@ -82,7 +82,11 @@ typedef struct {
   int32_t head_dim;         /* d in [1, 2^20]; multiple of 4 (float32 bank) or 8 (bfloat16 bank) */
   int32_t num_writes;       /* W in [1, min(N, 512)] */
   int32_t num_reads;        /* R in [1, min(N, 512)] */
-  int32_t chunk_size;       /* C in [1, 128], C * W <= 8192 (write/read only) */
+  int32_t chunk_size;       /* C in [1, 65536] (write/read only). The kernels run chunks of at most 128 tokens and
+                               8192 write events (C * W); a larger C runs as equal sub-chunks, its largest divisor
+                               within those limits (e.g. 256 with W = 64 as two chunks of 128): the chunk size
+                               changes results only through rounding, and calls split at multiples of C still give
+                               the bits of one call */
   int32_t act_dtype;        /* sdm_dtype of queries, sub-keys, values, gates and out: F32 or BF16 */
   int32_t bank_dtype;       /* sdm_dtype of the bank: F32 or BF16 */
   int64_t bank_rows;        /* rows per stream in the bank buffer, >= N */
@@ -242,7 +246,12 @@ sdm_status sdm_decode_step_noalloc(const sdm_config* cfg, const void* write_keys
  * read_idx as in sdm_write_read. The workspace (sdm_layer_workspace_size) holds, in this order and each region
  * starting at a 256-byte multiple: keys [B, T, H, P], queries [B, T, H, P], values [B, T, H, d], gate inputs
  * [B, T, 2 H] (a then b), alpha [B, T, H], beta [B, T, H], o [B, T, H, d] (all bfloat16; left there by the call),
- * then the op's own workspace. */
+ * then the op's own workspace.
+ * Learned initial bank (README model wiring: the bank is learned when backprop_on_memory=true; "Behavior changes":
+ * the layer's bank copy runs before the op): initial_bank NULL leaves `bank` the caller's state, advanced in place;
+ * initial_bank [H, bank_rows, d] (the bank dtype and row stride) is first copied into the N slot rows of every
+ * batch row of `bank` (the per-sequence copy), which the op then advances. Its gradient is the sum over the batch
+ * of the op's bank gradient (sdm_bank_grad_sum). */
 typedef struct {
   sdm_config op;      /* write/read settings of the op inside the layer */
   int32_t model_dim;  /* Dm, the width of x and y */
@@ -251,9 +260,16 @@ typedef struct {
 
 sdm_status sdm_layer_workspace_size(const sdm_layer_config* cfg, size_t* bytes);
 sdm_status sdm_layer_forward(const sdm_layer_config* cfg, const void* x, const void* w_in, const float* a_log,
-                             const float* dt_bias, const void* w_out, const void* subkeys, void* bank, void* y,
-                             int32_t* write_idx, int32_t* read_idx, void* workspace, size_t workspace_bytes,
-                             void* stream);
+                             const float* dt_bias, const void* w_out, const void* subkeys, const void* initial_bank,
+                             void* bank, void* y, int32_t* write_idx, int32_t* read_idx, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Gradient of a learned initial bank copied into every batch row (sdm_layer_forward's initial_bank): grad_initial_bank
+ * [H, bank_rows, bank_row_stride] float32 receives, for every head h, slot j < N and column c < head_dim, the sum over
+ * b = 0, 1, ..., B - 1 (in that order, float32) of grad_bank[b, h, j, c] (grad_bank: sdm_write_read_backward's
+ * gradient with respect to the bank before the call, [B, H, bank_rows, bank_row_stride] float32). Rows >= N and
+ * padding columns are not written. cfg: the write/read's (per-stream banks). */
+sdm_status sdm_bank_grad_sum(const sdm_config* cfg, const float* grad_bank, float* grad_initial_bank, void* stream);
 
 /* Kernel timing (diagnostics, not part of the method). While enabled, every kernel launch of this library is
  * bracketed by a pair of HIP events recorded on the call's stream. sdm_profile_read waits for the recorded events

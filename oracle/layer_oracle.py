@@ -75,11 +75,21 @@ def split_projection(p, heads, widths, subkey_dim, head_dim):
     return keys, queries, values, a, b
 
 
+def initial_bank_copy(initial_bank, batch) -> np.ndarray:
+    """The per-sequence copy of a learned initial bank [H, rows, d] into every batch row: [B, H, rows, d]
+    (README model wiring: the bank is learned when backprop_on_memory=true; the layer copies it before the op)."""
+    init = np.asarray(initial_bank, dtype=np.float32)
+    return np.ascontiguousarray(np.broadcast_to(init[None], (int(batch),) + init.shape))
+
+
 def layer_forward(x, w_in, a_log, dt_bias, w_out, subkeys, bank, *, heads, widths, num_writes, num_reads,
-                  bank_bf16=False, nthreads=None):
+                  bank_bf16=False, nthreads=None, initial_bank=None):
     """The layer's forward on bfloat16 tensors (given as float arrays of bfloat16 values). Returns a dict with every
     intermediate (keys, queries, values, a, b, alpha, beta: bfloat16 values as float64; the op's result dict `op`;
-    y [B, T, Dm] bfloat16 values as float64). The bank is not modified (the op oracle advances a copy)."""
+    y [B, T, Dm] bfloat16 values as float64). The bank is not modified (the op oracle advances a copy). With
+    initial_bank [H, rows, d] the op starts from its copy in every batch row instead of `bank`."""
+    if initial_bank is not None:
+        bank = initial_bank_copy(initial_bank, np.asarray(x).shape[0])
     dk = np.asarray(subkeys).shape[-1]
     d = np.asarray(bank).shape[-1]
     p = round_bf16_array(dense(x, w_in))

@@ -71,9 +71,8 @@ def test_workspace_sizes(lib):
     (dict(head_dim=(1 << 20) + 4), B.SDM_ERR_RANGE),
     (dict(head_dim=66), B.SDM_ERR_LAYOUT),
     (dict(head_dim=68, bank_dtype=B.SDM_BF16), B.SDM_ERR_LAYOUT),
-    (dict(chunk_size=129), B.SDM_ERR_RANGE),
+    (dict(chunk_size=65537), B.SDM_ERR_RANGE),
     (dict(chunk_size=0), B.SDM_ERR_RANGE),
-    (dict(chunk_size=128, num_writes=128, widths=(256, 256)), B.SDM_ERR_RANGE),  # C * W > 8192
     (dict(bank_rows=1023), B.SDM_ERR_BANK_TOO_SMALL),
     (dict(bank_row_stride=60), B.SDM_ERR_LAYOUT),                          # pitch below head_dim
     (dict(bank_row_stride=66), B.SDM_ERR_LAYOUT),                          # pitch not a 16-byte multiple
@@ -270,8 +269,9 @@ def test_layer_refuses_before_device_work(lib):
     assert s == B.SDM_OK
     base = 1 << 40  # fake, never dereferenced: every check below fails before any HIP call
     step = 1 << 32
-    p = [_fake(base + i * step) for i in range(11)]  # x w_in a_log dt_bias w_out subkeys bank y widx ridx ws
-    call = lambda q, wsn=n: lib.sdm_layer_forward(ctypes.byref(lc), *q[:10], q[10], wsn, None)
+    # x w_in a_log dt_bias w_out subkeys initial_bank bank y widx ridx ws (initial_bank NULL)
+    p = [_fake(base + i * step) for i in range(11)]
+    call = lambda q, wsn=n: lib.sdm_layer_forward(ctypes.byref(lc), *q[:6], None, *q[6:10], q[10], wsn, None)
     q = list(p)
     q[6] = None  # bank
     assert call(q) == B.SDM_ERR_NULL
@@ -362,3 +362,16 @@ def test_decode_steps_refuses_before_device_work(lib):
     q[7] = _fake(base + 6 * step + 256)  # bank_out starts inside bank_in
     assert lib.sdm_decode_steps(ctypes.byref(cfg), *q, ws, n, None) == B.SDM_ERR_ALIAS
     assert lib.sdm_decode_steps(ctypes.byref(cfg), *p, ws, n - 1, None) == B.SDM_ERR_WORKSPACE
+
+
+def test_large_chunks_run_as_sub_chunks(lib):
+    """chunk_size above the kernels' 128 tokens / 8192 events runs as equal sub-chunks (its largest divisor within
+    them): the workspace (chunk plans) is that of the sub-chunk."""
+    base = dict(widths=(256, 256), num_writes=64, num_reads=64, tokens=1024)
+    n128 = _status(_cfg(chunk_size=128, **base))[1]
+    s256, n256 = _status(_cfg(chunk_size=256, **base))
+    assert s256 == B.SDM_OK and n256 == n128
+    s, n = _status(_cfg(chunk_size=128, widths=(256, 256), num_writes=128, num_reads=64, tokens=1024))
+    assert s == B.SDM_OK and n == _status(_cfg(chunk_size=64, widths=(256, 256), num_writes=128, num_reads=64,
+                                               tokens=1024))[1]
+    assert _status(_cfg(chunk_size=131))[0] == B.SDM_OK  # a prime above 128: chunks of one token

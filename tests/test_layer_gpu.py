@@ -163,3 +163,69 @@ def test_layer_padded_bank_pitch():
     torch.cuda.synchronize()
     assert torch.equal(y1, y2) and torch.equal(dense, padded)
     assert bool((buf[..., s.head_dim:] == 1234.5).all())
+
+
+def test_layer_learned_initial_bank():
+    """A learned initial bank (README model wiring; the layer's bank copy runs before the op): every batch row of the
+    bank starts from the copy, bit for bit the layer on a bank filled with the copy beforehand; the op then matches
+    the oracle started from the copy; rows past N and the row padding are never written."""
+    s = synth.Shape(3, 70, 2, (16, 16), 32, 64, 8, 8, 64, "bf16", "f32", bank_rows=300)
+    Dm = 256
+    x = synth.make_layer_inputs(s, Dm, 5)
+    rng = np.random.default_rng(6)
+    init_np = (0.02 * rng.standard_normal((s.heads, s.rows, s.head_dim))).astype(np.float32)
+    pitch, SENT = 80, 777.0
+    t = {k: to_dev(x[k], torch.bfloat16) for k in ("x", "w_in", "w_out", "subkeys")}
+    g = {k: to_dev(x[k], torch.float32) for k in ("a_log", "dt_bias")}
+    kw = dict(heads=s.heads, widths=s.widths, num_writes=s.num_writes, num_reads=s.num_reads,
+              chunk_size=s.chunk_size, want_index=True, return_workspace=True)
+    ibuf = torch.full((s.heads, s.rows, pitch), SENT, device=DEV)
+    init = ibuf[..., :s.head_dim]
+    init.copy_(to_dev(init_np, torch.float32))
+    bbuf = torch.full((s.batch, s.heads, s.rows, pitch), SENT, device=DEV)
+    bank = bbuf[..., :s.head_dim]
+    print("layer with a learned initial bank", flush=True)
+    y, widx, ridx, ws = binding.sdm_layer_forward(t["x"], t["w_in"], g["a_log"], g["dt_bias"], t["w_out"],
+                                                  t["subkeys"], bank, initial_bank=init, **kw)
+    # the same layer on a bank filled with the copy beforehand
+    bbuf2 = torch.full_like(bbuf, SENT)
+    bank2 = bbuf2[..., :s.head_dim]
+    bank2[:, :, :s.slots].copy_(init[:, :s.slots].unsqueeze(0).expand(s.batch, -1, -1, -1))
+    y2, widx2, _, _ = binding.sdm_layer_forward(t["x"], t["w_in"], g["a_log"], g["dt_bias"], t["w_out"],
+                                                t["subkeys"], bank2, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2) and torch.equal(widx, widx2) and torch.equal(bbuf, bbuf2)
+    assert bool((bbuf[..., s.head_dim:] == SENT).all()) and bool((bbuf[:, :, s.slots:] == SENT).all())
+    v = binding.layer_workspace_views(x["x"].shape, s.heads, s.widths, s.subkey_dim, s.head_dim, ws)
+    got = {k: to_np(u) for k, u in v.items()}
+    start = lo.initial_bank_copy(init_np[:, :s.slots], s.batch)
+    ref = oracle.write_read(got["keys"], got["queries"], got["values"], got["alpha"], got["beta"], x["subkeys"],
+                            start, s.widths, s.num_writes, s.num_reads, act_bf16=True)
+    assert np.array_equal(to_np(widx), ref["widx"]) and np.array_equal(to_np(ridx), ref["ridx"])
+    assert rowwise_rel(got["o"], ref["out"]) <= RTOL["bf16"]
+    assert rowwise_rel(to_np(bank[:, :, :s.slots]), ref["bank"]) <= RTOL["f32"]
+
+
+def test_bank_grad_sum():
+    """The learned bank's gradient: the op's per-stream bank gradients summed over the batch in order, each element
+    within the a-priori bound of a float32 sum of B terms ((B - 1) 2^-24 times the sum of their magnitudes) of the
+    fp64 sum, bitwise repeatable; rows past N and the padding are not written."""
+    B, H, rows, d, pitch, N = 5, 3, 70, 48, 52, 64
+    rng = np.random.default_rng(7)
+    gb_np = rng.standard_normal((B, H, rows, d)).astype(np.float32) * np.exp(rng.standard_normal((B, H, rows, 1)))
+    gbuf = torch.zeros((B, H, rows, pitch), device=DEV)
+    gb = gbuf[..., :d]
+    gb.copy_(to_dev(gb_np, torch.float32))
+    obuf = torch.full((H, rows, pitch), 5.0, device=DEV)
+    out = obuf[..., :d]
+    print("bank gradient sum", flush=True)
+    binding.sdm_bank_grad_sum(gb, heads=H, widths=(8, 8), head_dim=d, out=out)
+    out2 = torch.full_like(obuf, 5.0)[..., :d]
+    binding.sdm_bank_grad_sum(gb, heads=H, widths=(8, 8), head_dim=d, out=out2)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    got = to_np(out)[:, :N]
+    ref = gb_np[:, :, :N].astype(np.float64).sum(axis=0)
+    bound = (B - 1) * 2.0 ** -24 * np.abs(gb_np[:, :, :N].astype(np.float64)).sum(axis=0) * 1.01
+    assert np.all(np.abs(got - ref) <= bound)
+    assert bool((obuf[:, N:] == 5.0).all()) and bool((obuf[..., d:] == 5.0).all())

@@ -121,3 +121,26 @@ def test_layer_oracle_mistakes_are_caught(seed):
     r1 = sdm_oracle.write_read(k, q, v, g, g, sub, bank, widths, 3, 3, nthreads=1)
     r2 = sdm_oracle.write_read(q, k, v, g, g, sub, bank, widths, 3, 3, nthreads=1)
     assert not np.array_equal(r1["widx"], r2["widx"])
+
+
+def test_initial_bank_copy_is_the_op_on_every_batch_row():
+    """A learned initial bank: the layer starts every batch row from its copy, so each batch row's op equals the op
+    oracle run on that row alone from the initial bank (the rows are independent streams)."""
+    rng = np.random.default_rng(9)
+    B, T, H, widths, dk, d, Dm = 3, 5, 2, (4, 4), 4, 8, 32
+    P = len(widths) * dk
+    nin = 2 * H * P + H * d + 2 * H
+    r = lambda *shape: lo.round_bf16_array(rng.standard_normal(shape))
+    x, w_in, w_out = r(B, T, Dm), r(nin, Dm) * 0.2, r(Dm, H * d) * 0.2
+    sub = r(H, sum(widths), dk)
+    init = (0.1 * rng.standard_normal((H, 16, d))).astype(np.float32)
+    a_log, dt_bias = np.zeros(H), np.zeros(H)
+    kw = dict(heads=H, widths=widths, num_writes=3, num_reads=2)
+    full = lo.layer_forward(x, w_in, a_log, dt_bias, w_out, sub, np.zeros((B, H, 16, d), np.float32),
+                            initial_bank=init, **kw)
+    cp = lo.initial_bank_copy(init, B)
+    assert cp.shape == (B, H, 16, d) and all(np.array_equal(cp[b], init) for b in range(B))
+    for b in range(B):
+        one = lo.layer_forward(x[b:b + 1], w_in, a_log, dt_bias, w_out, sub, init[None], **kw)
+        assert np.array_equal(one["y"][0], full["y"][b])
+        assert np.array_equal(one["op"]["bank"][0], full["op"]["bank"][b])

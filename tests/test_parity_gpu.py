@@ -921,3 +921,25 @@ def test_decode_steps_zero_steps_and_graph_replay():
         assert torch.equal(out, ref_out) and torch.equal(bank, ref_bank), f"replay {rep} differs"
         run()  # eager work between replays
         torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------------------------------------ large chunks
+def test_chunk_256_and_above_the_kernels_chunk():
+    """chunk_size 256 (the 7B configuration's) runs as two chunks of 128 with W = 64: the result equals the oracle
+    within tolerance and chunk 128's bit for bit; chunk 200 (sub-chunks of 100) equals the oracle, and a call split
+    at token 200 gives the bits of one call."""
+    s = synth.Shape(2, 600, 2, (32, 32), 16, 64, 64, 64, 256, name="c256")
+    x = synth.make_inputs(s, seed=81)
+    print("chunk 256 / 128 / 200", flush=True)
+    g256 = run_gpu(s, x)
+    g128 = run_gpu(s, x, chunk_size=128)
+    for a, b in zip(g256, g128):
+        assert np.array_equal(a, b), "chunk 256 differs from chunk 128"
+    check_parity(s, g256, run_oracle(s, x))
+    s200 = s.with_(chunk_size=200)
+    g200 = run_gpu(s200, x)
+    check_parity(s200, g200, run_oracle(s200, x))
+    head = s200.with_(tokens=200)
+    o1, b1, w1, r1 = run_gpu(head, _sub(x, 0, 200))
+    o2, b2, w2, r2 = run_gpu(s200.with_(tokens=400), _sub(x, 200, 600), bank=b1)
+    assert np.array_equal(np.concatenate([o1, o2], axis=1), g200[0]) and np.array_equal(b2, g200[1])

@@ -26,7 +26,10 @@ digest = {}
 def put(name, *ts):
     h = hashlib.sha256()
     for t in ts:
-        h.update(t.detach().contiguous().cpu().numpy().tobytes())
+        t = t.detach().contiguous()
+        if t.dtype == torch.bfloat16:
+            t = t.view(torch.int16)  # the raw bits
+        h.update(t.cpu().numpy().tobytes())
     digest[name] = h.hexdigest()
 
 def dev_t(x, dt):
