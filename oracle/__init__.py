@@ -14,5 +14,8 @@ from .sdm_oracle import (  # noqa: F401
     write_read,
     write_read_backward,
     write_read_backward_bounds,
+    e4m3_round,
+    snap_rows,
+    snap_scale_exp,
     U_F32,
 )

@@ -68,6 +68,70 @@ double oracle_round_bf16(double x) {
 static inline float round_to(double x, int bf16) { return bf16 ? (float)oracle_round_bf16(x) : (float)x; }
 
 /* ---------------------------------------------------------------------------------------------------------------
+ * Quantized backward snapshots (fp8, int4). The pages name the modes but not their formats; the reading taken:
+ * a snapshot row (float32) is stored in groups of 16 consecutive columns, each group with a power-of-two scale
+ * s = 2^e, the smallest with (the group's largest magnitude) / s <= qmax, where qmax is the largest finite value of
+ * the element format: 448 for OCP FP8 E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, subnormals
+ * spaced 2^-9, no infinities) and 7 for int4 (integers in [-7, 7]). Each element x is stored as the format's
+ * nearest value to x / s (exact: s is a power of two), ties to even, and read back as that value times s.
+ * ------------------------------------------------------------------------------------------------------------- */
+#define SNAP_GROUP 16
+
+/* Nearest OCP E4M3 value to v, ties to even (|v| <= 448, so no saturation is needed). */
+double oracle_e4m3_round(double v) {
+  const double a = fabs(v);
+  if (a == 0.0) return 0.0;
+  int ex;
+  (void)frexp(a, &ex);                  /* a in [2^(ex-1), 2^ex) */
+  int E = ex - 1;                       /* binade exponent */
+  if (E < -6) E = -6;                   /* below 2^-6 the spacing stays 2^-9 (subnormals) */
+  const double step = ldexp(1.0, E - 3); /* 3 mantissa bits */
+  return copysign(nearbyint(a / step) * step, v);
+}
+
+/* Scale exponent e of a group whose largest magnitude is amax: the smallest e with amax / 2^e <= qmax. */
+int oracle_snap_scale_exp(double amax, double qmax) {
+  int ex;
+  (void)frexp(amax, &ex);
+  int e = ex - 40;
+  while (ldexp(amax, -e) > qmax) ++e;
+  return e;
+}
+
+/* A float32 row of d columns as a snapshot of the given mode stores it: 1 bfloat16, 2 fp8, 3 int4 (d % 16 == 0 for
+ * the last two); other modes leave it unchanged. */
+static void snap_row(const double* src, double* dst, int d, int mode) {
+  if (mode == 1) {
+    for (int c = 0; c < d; ++c) dst[c] = (double)round_to(src[c], 1);
+    return;
+  }
+  if (mode != 2 && mode != 3) {
+    for (int c = 0; c < d; ++c) dst[c] = src[c];
+    return;
+  }
+  const double qmax = mode == 2 ? 448.0 : 7.0;
+  for (int g = 0; g < d; g += SNAP_GROUP) {
+    double amax = 0.0;
+    for (int c = g; c < g + SNAP_GROUP; ++c) amax = fmax(amax, fabs(src[c]));
+    if (amax == 0.0) {
+      for (int c = g; c < g + SNAP_GROUP; ++c) dst[c] = 0.0;
+      continue;
+    }
+    const int e = oracle_snap_scale_exp(amax, qmax);
+    for (int c = g; c < g + SNAP_GROUP; ++c) {
+      const double x = ldexp(src[c], -e);
+      const double q = mode == 2 ? oracle_e4m3_round(x) : nearbyint(x);
+      dst[c] = ldexp(q, e);
+    }
+  }
+}
+
+/* Python-facing: rows [n, d] through snap_row (out may equal in). */
+void oracle_snap_rows(const double* in, double* out, int64_t n, int d, int mode) {
+  for (int64_t i = 0; i < n; ++i) snap_row(in + i * d, out + i * d, d, mode);
+}
+
+/* ---------------------------------------------------------------------------------------------------------------
  * Factor scores.
  * ------------------------------------------------------------------------------------------------------------- */
 
@@ -369,8 +433,9 @@ int oracle_write_read(int B, int T, int H, int F, const int* widths, int dk, int
  *
  * Error bounds (optional, for comparing another evaluation of this backward with it). For an evaluation that
  *   (i)  reads pre-write rows P and read rows M[R_j] within eps_row * (that row's largest magnitude) of these, plus
- *        q_rel * |element| for rows it reads from a rounded snapshot (a rounding that falls the other way: one
- *        bfloat16 spacing is at most 2^-7 of the element),
+ *        q_rel * |element| + q_grp * (the largest magnitude of the element's 16-column group) for rows it reads
+ *        from a rounded or quantized snapshot (a rounding that falls the other way: one bfloat16 spacing is at most
+ *        2^-7 of the element; one fp8 spacing at most 2^-3 of it; one int4 step at most 2/7 of the group),
  *   (ii) has softmax weights within eps_w of these (relative), and
  *   (iii) does every other sum, product and difference in an arithmetic with unit roundoff u, in any order,
  * first-order running error analysis bounds the difference of every gradient element from this fp64 one:
@@ -384,13 +449,21 @@ int oracle_write_read(int B, int T, int H, int F, const int* widths, int dk, int
 
 /* Parameters of the error bounds: u, eps_row, eps_w, q_rel (see above). */
 typedef struct {
-  double u, eps_row, eps_w, q_rel;
+  double u, eps_row, eps_w, q_rel, q_grp;
 } bound_par_t;
+
+/* Largest magnitude of the 16-column snapshot group of row element c (d % 16 == 0 where it is used). */
+static double group_max(const double* row, int c) {
+  const int g = c - c % SNAP_GROUP;
+  double m = 0.0;
+  for (int k = g; k < g + SNAP_GROUP; ++k) m = fmax(m, fabs(row[k]));
+  return m;
+}
 
 static inline double gam(double n, double u) { return n * u / (1.0 - n * u); }
 
 typedef struct {
-  int B, T, H, F, dk, d, W, R, bank_bf16, exact, snap_bf16;
+  int B, T, H, F, dk, d, W, R, bank_bf16, exact, snap_bf16; /* snap_bf16: the snapshot mode (0, 1 bf16, 2 fp8, 3 int4) */
   const int* widths;
   const float *wkeys, *rq, *values, *alpha, *beta, *sub, *bank, *dout, *dbank;
   int64_t bank_rows, sumn;
@@ -465,6 +538,7 @@ static void* bwd_worker(void* arg) {
   /* error-bound state (bound mode only): EG the bound on the adjoint bank, the rest per token */
   const bound_par_t* bp = j->bp;
   const int KM = W > R ? W : R;
+  double* qrow = (double*)malloc(sizeof(double) * (size_t)d); /* a read row as a snapshot restore left it */
   double *EG = NULL, *Eg = NULL, *Er = NULL, *Mr = NULL, *Edl = NULL, *ED = NULL, *Edw = NULL, *Ex = NULL;
   double* Mx = NULL;
   if (bp) {
@@ -478,7 +552,7 @@ static void* bwd_worker(void* arg) {
     Ex = (double*)malloc(sizeof(double) * (size_t)F * dk);
     Mx = (double*)malloc(sizeof(double) * (size_t)F * dk);
   }
-  if (!S || !Rd || !sc || !w || !rho || !P || !Vr || !rr || !del || !M || !G || !g || !D || !dw || !later ||
+  if (!S || !Rd || !sc || !w || !rho || !P || !Vr || !rr || !del || !M || !G || !g || !D || !dw || !later || !qrow ||
       (bp && (!EG || !Eg || !Er || !Mr || !Edl || !ED || !Edw || !Ex || !Mx))) {
     j->err = 1;
     goto done;
@@ -530,11 +604,11 @@ static void* bwd_worker(void* arg) {
     }
     if (j->bank64)
       for (int64_t i = 0; i < rows * d; ++i) j->bank64[(int64_t)st * rows * d + i] = M[i];
-    /* bfloat16 snapshot (CHANGELOG 2.0.0, "New"): the backward sees every pre-write row rounded to bfloat16, and r
-     * and delta rebuilt from those rows; a row read at token t whose slot a later token writes was restored in place
-     * from such a row, so it is rounded too (marked in `later` as the sweep goes back) */
+    /* bfloat16 / fp8 / int4 snapshot (CHANGELOG 2.0.0, "New"): the backward sees every pre-write row as the snapshot
+     * stores it, and r and delta rebuilt from those rows; a row read at token t whose slot a later token writes was
+     * restored in place from such a row, so it is stored that way too (marked in `later` as the sweep goes back) */
     if (j->snap_bf16) {
-      for (int64_t i = 0; i < (int64_t)T * W * d; ++i) P[i] = (double)round_to(P[i], 1);
+      for (int64_t i = 0; i < (int64_t)T * W; ++i) snap_row(P + i * d, P + i * d, d, j->snap_bf16);
       for (int t = 0; t < T; ++t) {
         const int64_t row = ((int64_t)b * T + t) * H + h;
         const double a = j->alpha[row], be = j->beta[row];
@@ -572,20 +646,25 @@ static void* bwd_worker(void* arg) {
       /* the read */
       double sum = 0.0;
       for (int i = 0; i < R; ++i) {
-        const double* q = Vr + ((int64_t)t * R + i) * d;
         const int rounded = j->snap_bf16 && later[Rt[i]];
+        const double* q = Vr + ((int64_t)t * R + i) * d;
+        if (rounded) { /* the row as the restore left it */
+          snap_row(q, qrow, d, j->snap_bf16);
+          q = qrow;
+        }
         double acc = 0.0;
-        for (int c = 0; c < d; ++c) acc += (double)dout[c] * (rounded ? (double)round_to(q[c], 1) : q[c]);
+        for (int c = 0; c < d; ++c) acc += (double)dout[c] * q[c];
         dw[i] = acc;
         double* Gr = G + (int64_t)Rt[i] * d;
         if (bp) { /* d rho_i from the read row (error eps_row of its largest magnitude, plus q_rel if rounded) */
           const double u = bp->u;
           double vmax = 0.0, e = 0.0, m = 0.0;
-          for (int c = 0; c < d; ++c) vmax = fmax(vmax, fabs(rounded ? (double)round_to(q[c], 1) : q[c]));
+          for (int c = 0; c < d; ++c) vmax = fmax(vmax, fabs(q[c]));
           double* EGr = EG + (int64_t)Rt[i] * d;
           for (int c = 0; c < d; ++c) {
-            const double qc = fabs(rounded ? (double)round_to(q[c], 1) : q[c]);
-            const double eq = bp->eps_row * vmax + (rounded ? bp->q_rel * (qc + bp->eps_row * vmax) : 0.0);
+            const double qc = fabs(q[c]);
+            const double ev = bp->eps_row * vmax;
+            const double eq = ev + (rounded ? bp->q_rel * (qc + ev) + bp->q_grp * (group_max(q, c) + ev) : 0.0);
             const double go = fabs((double)dout[c]);
             e += go * eq;
             m += go * qc;
@@ -639,7 +718,7 @@ static void* bwd_worker(void* arg) {
       j->d_alpha[row] = dal;
       j->d_beta[row] = dbe;
       if (bp) { /* bounds of r, delta, D, d values, d beta, d alpha, d w_i; then of the adjoint update below */
-        const double u = bp->u, qP = j->snap_bf16 ? bp->q_rel : 0.0;
+        const double u = bp->u, qP = j->snap_bf16 ? bp->q_rel : 0.0, qG = j->snap_bf16 ? bp->q_grp : 0.0;
         /* r = sum_i w_i P_i (the rows within eps_row of their largest magnitude, plus qP if rounded) */
         for (int c = 0; c < d; ++c) Er[c] = Mr[c] = 0.0;
         for (int i = 0; i < W; ++i) {
@@ -647,7 +726,8 @@ static void* bwd_worker(void* arg) {
           double pmax = 0.0;
           for (int c = 0; c < d; ++c) pmax = fmax(pmax, fabs(p[c]));
           for (int c = 0; c < d; ++c) {
-            const double ep = bp->eps_row * pmax + qP * (fabs(p[c]) + bp->eps_row * pmax);
+            const double ev = bp->eps_row * pmax;
+            const double ep = ev + qP * (fabs(p[c]) + ev) + qG * (group_max(p, c) + ev);
             Er[c] += wt[i] * ep + fabs(p[c]) * bp->eps_w * wt[i];
             Mr[c] += wt[i] * fabs(p[c]);
           }
@@ -684,7 +764,8 @@ static void* bwd_worker(void* arg) {
           for (int c = 0; c < d; ++c) pmax = fmax(pmax, fabs(p[c]));
           double ew = 0.0, mw = 0.0;
           for (int c = 0; c < d; ++c) {
-            const double ep = bp->eps_row * pmax + qP * (fabs(p[c]) + bp->eps_row * pmax);
+            const double ev = bp->eps_row * pmax;
+            const double ep = ev + qP * (fabs(p[c]) + ev) + qG * (group_max(p, c) + ev);
             eal += fabs(gi[c]) * ep + fabs(p[c]) * egi[c];
             mal += fabs(gi[c] * p[c]);
             ew += fabs(gi[c]) * Edl[c] + fabs(dl[c]) * egi[c] + a * be * (fabs(D[c]) * ep + fabs(p[c]) * ED[c]);
@@ -734,7 +815,7 @@ static void* bwd_worker(void* arg) {
 done:
   free(S); free(Rd); free(sc); free(w); free(rho); free(P); free(Vr); free(rr); free(del); free(M); free(G);
   free(g); free(D); free(dw); free(later);
-  free(EG); free(Eg); free(Er); free(Mr); free(Edl); free(ED); free(Edw); free(Ex); free(Mx);
+  free(EG); free(Eg); free(Er); free(Mr); free(Edl); free(ED); free(Edw); free(Ex); free(Mx); free(qrow);
   return NULL;
 }
 
@@ -756,6 +837,7 @@ static int backward_impl(int B, int T, int H, int F, const int* widths, int dk, 
   int64_t sumn = 0, N = 1;
   for (int f = 0; f < F; ++f) { sumn += widths[f]; N *= widths[f]; }
   if (F < 1 || F > ORACLE_MAX_F || W < 1 || R < 1 || W > N || R > N || bank_rows < N) return -1;
+  if (snap_bf16 < 0 || snap_bf16 > 3 || (snap_bf16 >= 2 && d % SNAP_GROUP != 0)) return -1;
   const int streams = B * H;
   memset(d_wkeys, 0, sizeof(double) * (size_t)B * T * H * F * dk);
   memset(d_rq, 0, sizeof(double) * (size_t)B * T * H * F * dk);
@@ -832,7 +914,7 @@ int oracle_write_read_backward(int B, int T, int H, int F, const int* widths, in
 }
 
 /* oracle_write_read_backward with error bounds (see the comment above bound_par_t): par = {u, eps_row, eps_w,
- * q_rel}; e_* receive, per gradient element, the bound on the difference from this backward of an evaluation
+ * q_rel, q_grp}; e_* receive, per gradient element, the bound on the difference from this backward of an evaluation
  * that meets the stated conditions (same shapes as the gradients; fp64). snap_out (optional, float32
  * [B, H, T, W, d]) receives the pre-write rows of every write event as the backward reads them (rounded to
  * bfloat16 with snap_bf16). The gradients and the other outputs are those of oracle_write_read_backward. */
@@ -846,7 +928,7 @@ int oracle_write_read_backward_bounds(int B, int T, int H, int F, const int* wid
                                       double* e_wkeys, double* e_rq, double* e_values, double* e_alpha,
                                       double* e_beta, double* e_subkeys, double* e_bank, int nthreads) {
   if (!par || !e_wkeys || !e_rq || !e_values || !e_alpha || !e_beta || !e_subkeys || !e_bank) return -1;
-  bound_par_t bp = {par[0], par[1], par[2], par[3]};
+  bound_par_t bp = {par[0], par[1], par[2], par[3], par[4]};
   return backward_impl(B, T, H, F, widths, dk, d, W, R, bank_bf16, 0, snap_bf16, wkeys, rq, values, alpha, beta,
                        subkeys, bank, bank_rows, dout, dbank, d_wkeys, d_rq, d_values, d_alpha, d_beta, d_subkeys,
                        d_bank, out64, bank64, snap_out, &bp, e_wkeys, e_rq, e_values, e_alpha, e_beta, e_subkeys,

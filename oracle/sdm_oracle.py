@@ -70,6 +70,12 @@ def _load():
                 ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                 _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, ctypes.c_int64, _f32p, vp,
                 _f64p, _f64p, _f64p, _f64p, _f64p, _f64p, _f64p, vp, vp, ctypes.c_int]
+            lib.oracle_e4m3_round.restype = ctypes.c_double
+            lib.oracle_e4m3_round.argtypes = [ctypes.c_double]
+            lib.oracle_snap_scale_exp.restype = ctypes.c_int
+            lib.oracle_snap_scale_exp.argtypes = [ctypes.c_double, ctypes.c_double]
+            lib.oracle_snap_rows.restype = None
+            lib.oracle_snap_rows.argtypes = [_f64p, _f64p, ctypes.c_int64, ctypes.c_int, ctypes.c_int]
             lib.oracle_write_read_backward_bounds.restype = ctypes.c_int
             lib.oracle_write_read_backward_bounds.argtypes = [
                 ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, ctypes.c_int, ctypes.c_int,
@@ -178,9 +184,38 @@ def write_read(wkeys, rq, values, alpha, beta, subkeys, bank, widths, num_writes
     return res
 
 
+SNAP_MODES = {"none": 0, "bf16": 1, "fp8": 2, "int4": 3}
+
+
+def _snap_mode(snap_bf16, snap_quant):
+    if snap_quant is not None:
+        return SNAP_MODES[snap_quant]
+    return 1 if snap_bf16 else 0
+
+
+def e4m3_round(v: float) -> float:
+    """Nearest OCP FP8 E4M3 value to v (|v| <= 448), ties to even (sdm_oracle.c)."""
+    return float(_load().oracle_e4m3_round(float(v)))
+
+
+def snap_scale_exp(amax: float, qmax: float) -> int:
+    """The smallest e with amax / 2^e <= qmax: a quantized snapshot group's scale exponent."""
+    return int(_load().oracle_snap_scale_exp(float(amax), float(qmax)))
+
+
+def snap_rows(rows, snap_quant: str) -> np.ndarray:
+    """Rows [..., d] (float32 values) as a snapshot of the mode stores them: "bf16" rounded, "fp8" / "int4" quantized
+    in groups of 16 columns with a power-of-two scale and read back (d % 16 == 0). fp64 result."""
+    x = np.ascontiguousarray(np.asarray(rows, dtype=np.float64))
+    out = np.empty_like(x)
+    d = x.shape[-1]
+    _load().oracle_snap_rows(x, out, x.size // d if d else 0, d, SNAP_MODES[snap_quant])
+    return out
+
+
 def write_read_backward(wkeys, rq, values, alpha, beta, subkeys, bank, dout, dbank, widths, num_writes, num_reads,
                         *, bank_bf16=False, exact=False, snap_bf16=False, want_forward=False,
-                        nthreads: int | None = None):
+                        nthreads: int | None = None, snap_quant=None):
     """Gradients of the write/read (the chain rule through the per-token recurrence, in reverse; sdm_oracle.c).
 
     bank is the bank before the call [B, H, bank_rows, d]; dout [B, T, H, d] and dbank (same shape as bank, or None
@@ -211,7 +246,8 @@ def write_read_backward(wkeys, rq, values, alpha, beta, subkeys, bank, dout, dba
         fwd = [res["out"].ctypes.data, res["bank"].ctypes.data]
     nt = nthreads or min(os.cpu_count() or 1, 16)
     rc = _load().oracle_write_read_backward(
-        B, T, H, len(widths), widths, dk, d, W, R, int(bool(bank_bf16)), int(bool(exact)), int(bool(snap_bf16)),
+        B, T, H, len(widths), widths, dk, d, W, R, int(bool(bank_bf16)), int(bool(exact)),
+        _snap_mode(snap_bf16, snap_quant),
         wk, rqa, v, al, be, sub,
         M, M.shape[2], g_out, None if g_bank is None else g_bank.ctypes.data, res["d_wkeys"], res["d_rq"],
         res["d_values"], res["d_alpha"], res["d_beta"], res["d_subkeys"], res["d_bank"], fwd[0], fwd[1], nt)
@@ -224,13 +260,15 @@ U_F32 = 2.0 ** -24  # unit roundoff of float32 (round to nearest)
 
 
 def write_read_backward_bounds(wkeys, rq, values, alpha, beta, subkeys, bank, dout, dbank, widths, num_writes,
-                               num_reads, *, eps_row, eps_w=2 * U_F32, u=U_F32, q_rel=0.0, bank_bf16=False,
-                               snap_bf16=False, want_snapshot=False, nthreads: int | None = None):
+                               num_reads, *, eps_row, eps_w=2 * U_F32, u=U_F32, q_rel=0.0, q_grp=0.0,
+                               bank_bf16=False, snap_bf16=False, want_snapshot=False, nthreads: int | None = None,
+                               snap_quant=None):
     """write_read_backward (rounded bank states, as the forward stores them) plus, for every gradient element, a
     bound on how far another evaluation of the same backward may be from it (sdm_oracle.c, the comment above
     bound_par_t): one that reads pre-write and read rows within eps_row of each row's largest magnitude (plus q_rel
-    of an element for rows read from a rounded snapshot), has softmax weights within eps_w relative, and does every
-    other operation with unit roundoff u in any order. Returns the gradients as write_read_backward does, the
+    of an element and q_grp of its 16-column group's largest magnitude for rows read from a rounded or quantized
+    snapshot, snap_quant "bf16", "fp8" or "int4"), has softmax weights within eps_w relative, and does every other
+    operation with unit roundoff u in any order. Returns the gradients as write_read_backward does, the
     bounds as e_wkeys, e_rq, e_values, e_alpha, e_beta, e_subkeys, e_bank, the forward's out and bank (fp64; the
     bank rounded to its dtype after every token), and with want_snapshot the pre-write rows of every write event
     as the backward reads them, float32 [B, H, T, W, d]."""
@@ -250,10 +288,11 @@ def write_read_backward_bounds(wkeys, rq, values, alpha, beta, subkeys, bank, do
     for k in ("wkeys", "rq", "values", "alpha", "beta", "subkeys", "bank"):
         res["e_" + k] = z(res["d_" + k].shape)
     snap = np.empty((B, H, T, W, d), np.float32) if want_snapshot else None
-    par = np.array([u, eps_row, eps_w, q_rel], np.float64)
+    par = np.array([u, eps_row, eps_w, q_rel, q_grp], np.float64)
     nt = nthreads or min(os.cpu_count() or 1, 16)
     rc = _load().oracle_write_read_backward_bounds(
-        B, T, H, len(widths), widths, dk, d, W, R, int(bool(bank_bf16)), int(bool(snap_bf16)), wk, rqa, v, al, be,
+        B, T, H, len(widths), widths, dk, d, W, R, int(bool(bank_bf16)), _snap_mode(snap_bf16, snap_quant), wk, rqa, v,
+        al, be,
         sub, M, M.shape[2], g_out, None if g_bank is None else g_bank.ctypes.data, res["d_wkeys"], res["d_rq"],
         res["d_values"], res["d_alpha"], res["d_beta"], res["d_subkeys"], res["d_bank"], res["out"].ctypes.data,
         res["bank"].ctypes.data, None if snap is None else snap.ctypes.data, par, res["e_wkeys"], res["e_rq"],
