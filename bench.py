@@ -171,7 +171,7 @@ def bench_train(args, torch, binding, synth):
                                         snap, gout, gbank, workspace=wsb, **kw)
     torch.cuda.synchronize()
     restored = bool(torch.equal(bank, bank0))
-    del bank0
+    bank_ref = bank0
     n = max(1, min(args.steps, 5))
     tf = tb = 0.0
     binding.profile_enable(True)
@@ -213,6 +213,36 @@ def bench_train(args, torch, binding, synth):
         tqb += c - b
     snap = snap_q
     ms_qf, ms_qb = tqf * 1e3 / n, tqb * 1e3 / n
+    # fp8 and int4 snapshots (groups of 16 columns with power-of-two scales)
+    quant = {}
+    del snap, snap_q
+    for mode in ("fp8", "int4"):
+        cfg_q = binding.make_config(s.batch, s.tokens, s.heads, s.widths, s.subkey_dim, s.head_dim, s.num_writes,
+                                    s.num_reads, s.chunk_size, binding.SDM_BF16, binding.SDM_F32, s.rows, pitch,
+                                    snapshot_dtype=binding._SNAP[mode])
+        nbytes = binding._snapshot_shape(cfg_q, binding._SNAP[mode], 0, 0, 0, 0, 0)[0]
+        snap_m = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        tf_m = tb_m = 0.0
+        for _ in range(n):
+            gbank.zero_()
+            torch.cuda.synchronize()
+            a = time.perf_counter()
+            binding.sdm_write_read_save(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"], t["subkeys"], bank,
+                                        out=out, snapshot=snap_m, workspace=wsf, snapshot_quant=mode, **kw)
+            torch.cuda.synchronize()
+            b = time.perf_counter()
+            binding.sdm_write_read_backward(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"], t["subkeys"],
+                                            bank, snap_m, gout, gbank, workspace=wsb, snapshot_quant=mode, **kw)
+            torch.cuda.synchronize()
+            c = time.perf_counter()
+            tf_m += b - a
+            tb_m += c - b
+            bank.copy_(bank_ref)  # the quantized restore leaves the written rows quantized: start every step alike
+        quant[mode] = {"tokens_per_s": round(s.batch * s.tokens / ((tf_m + tb_m) / n), 1),
+                       "ms_forward_save": round(tf_m * 1e3 / n, 4), "ms_backward": round(tb_m * 1e3 / n, 4),
+                       "snapshot_bytes": nbytes}
+        del snap_m
+    snap = None
     res = {"tokens_per_s": round(s.batch * s.tokens / ((ms_f + ms_b) * 1e-3), 1),
            "ms_forward_save": round(ms_f, 4), "ms_backward": round(ms_b, 4), "steps": n,
            "kernels_avg_ms": {k: round(v[0] / v[1], 4) for k, v in prof.items() if v[1]},
@@ -220,10 +250,11 @@ def bench_train(args, torch, binding, synth):
            "bank_restored_bitwise": restored,
            "bf16_snapshot": {"tokens_per_s": round(s.batch * s.tokens / ((ms_qf + ms_qb) * 1e-3), 1),
                              "ms_forward_save": round(ms_qf, 4), "ms_backward": round(ms_qb, 4),
-                             "snapshot_bytes": snap_q.numel() * snap_q.element_size()},
+                             "snapshot_bytes": s.batch * s.heads * s.tokens * s.num_writes * s.head_dim * 2},
+           "fp8_snapshot": quant["fp8"], "int4_snapshot": quant["int4"],
            "config": "layer_65k (as the headline), grad_out ~ N(0,1), float32 gradients"}
     log(f"[bench] train: forward+snapshot {ms_f:.3f} ms, backward {ms_b:.3f} ms")
-    del g, snap, gbank, bank, wsf, wsb, out, t, gout
+    del g, snap, gbank, bank, bank_ref, wsf, wsb, out, t, gout
     torch.cuda.empty_cache()
     return res
 

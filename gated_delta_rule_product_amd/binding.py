@@ -21,7 +21,7 @@ SDM_OK, SDM_ERR_DTYPE, SDM_ERR_RANGE, SDM_ERR_BANK_TOO_SMALL, SDM_ERR_ALIAS = 0,
 SDM_ERR_LAYOUT, SDM_ERR_WORKSPACE, SDM_ERR_DEVICE, SDM_ERR_HIP, SDM_ERR_NULL = 5, 6, 7, 8, 9
 STATUS_NAMES = {0: "SDM_OK", 1: "SDM_ERR_DTYPE", 2: "SDM_ERR_RANGE", 3: "SDM_ERR_BANK_TOO_SMALL", 4: "SDM_ERR_ALIAS",
                 5: "SDM_ERR_LAYOUT", 6: "SDM_ERR_WORKSPACE", 7: "SDM_ERR_DEVICE", 8: "SDM_ERR_HIP", 9: "SDM_ERR_NULL"}
-SDM_F32, SDM_BF16, SDM_F16 = 0, 1, 2
+SDM_F32, SDM_BF16, SDM_F16, SDM_FP8, SDM_INT4 = 0, 1, 2, 3, 4
 SDM_OP_TOPK, SDM_OP_WRITE_READ, SDM_OP_DECODE, SDM_OP_BACKWARD, SDM_OP_DECODE_STEPS = 0, 1, 2, 3, 4
 SCORING = {"auto": 0, "direct": 1, "filtered": 2}
 
@@ -71,14 +71,25 @@ def make_config(batch, tokens, heads, widths, subkey_dim, head_dim=1, num_writes
     return c
 
 
-_SNAP = {"none": 0, "bf16": SDM_BF16}
+_SNAP = {"none": 0, "bf16": SDM_BF16, "fp8": SDM_FP8, "int4": SDM_INT4}
 
 
 def _snapshot_dtype(snapshot_quant: str, bank: torch.Tensor):
     """(config code, torch dtype) of the backward snapshot: "none" = the bank dtype, "bf16" = bfloat16."""
     if snapshot_quant not in _SNAP:
         raise ValueError(f"snapshot_quant must be one of {sorted(_SNAP)}, not {snapshot_quant!r}")
+    if snapshot_quant in ("fp8", "int4"):
+        return _SNAP[snapshot_quant], torch.uint8  # bytes: elements, then scales (include/sdm.h)
     return _SNAP[snapshot_quant], (torch.bfloat16 if snapshot_quant == "bf16" else bank.dtype)
+
+
+def _snapshot_shape(cfg, scode, B, H, T, W, d):
+    """Shape of the snapshot tensor: [B, H, T, W, d] rows, or the byte count of a quantized snapshot."""
+    if scode in (SDM_FP8, SDM_INT4):
+        n = ctypes.c_size_t(0)
+        _check(load().sdm_snapshot_bytes(ctypes.byref(cfg), ctypes.byref(n)))
+        return (n.value,)
+    return (B, H, T, W, d)
 
 
 def bank_pitch(head_dim: int, dtype: torch.dtype) -> int:
@@ -147,6 +158,8 @@ def load():
             lib.sdm_layer_workspace_size.argtypes = [lcfgp, ctypes.POINTER(ctypes.c_size_t)]
             lib.sdm_layer_workspace_size.restype = ctypes.c_int
             lib.sdm_layer_forward.argtypes = [lcfgp] + [_vp] * 12 + [ctypes.c_size_t, _vp]
+            lib.sdm_snapshot_bytes.restype = ctypes.c_int
+            lib.sdm_snapshot_bytes.argtypes = [cfgp, ctypes.POINTER(ctypes.c_size_t)]
             lib.sdm_bank_grad_sum.restype = ctypes.c_int
             lib.sdm_bank_grad_sum.argtypes = [cfgp, _vp, _vp, _vp]
             lib.sdm_layer_forward.restype = ctypes.c_int
@@ -395,10 +408,11 @@ def sdm_write_read_save(write_keys, read_queries, values, forget_gate, input_gat
         out = torch.empty((B, T, H, d), dtype=act, device=bank.device)
     else:
         _need(out, "out", (B, T, H, d), act)
+    sshape = _snapshot_shape(cfg, scode, B, H, T, num_writes, d)
     if snapshot is None:
-        snapshot = torch.empty((B, H, T, num_writes, d), dtype=sdt, device=bank.device)
+        snapshot = torch.empty(sshape, dtype=sdt, device=bank.device)
     else:
-        _need(snapshot, "snapshot", (B, H, T, num_writes, d), sdt)
+        _need(snapshot, "snapshot", sshape, sdt)
     widx = torch.empty((B, T, H, num_writes), dtype=torch.int32, device=bank.device) if want_index else None
     ridx = torch.empty((B, T, H, num_reads), dtype=torch.int32, device=bank.device) if want_index else None
     _check(load().sdm_write_read_save(ctypes.byref(cfg), _ptr(write_keys), _ptr(read_queries), _ptr(values),
@@ -430,7 +444,6 @@ def sdm_write_read_backward(write_keys, read_queries, values, forget_gate, input
         raise ValueError(f"bank has shape {tuple(bank.shape)}, expected ({B}, {H}, bank_rows, {d})")
     ld = _bank_ld(bank, "bank")
     scode, sdt = _snapshot_dtype(snapshot_quant, bank)
-    _need(snapshot, "snapshot", (B, H, T, num_writes, d), sdt)
     dev = bank.device
     if grad_bank is None:
         grad_bank = torch.zeros((B, H, bank.shape[2], ld), dtype=torch.float32, device=dev)[..., :d]
@@ -439,6 +452,7 @@ def sdm_write_read_backward(write_keys, read_queries, values, forget_gate, input
         raise ValueError("grad_bank must be float32 with the bank's shape and strides")
     cfg = make_config(B, T, H, widths, dk, d, num_writes, num_reads, chunk_size, _dt(write_keys), _dt(bank),
                       bank.shape[2], ld, snapshot_dtype=scode)
+    _need(snapshot, "snapshot", _snapshot_shape(cfg, scode, B, H, T, num_writes, d), sdt)
     ws = _workspace(workspace_size(cfg, SDM_OP_BACKWARD), dev, workspace)
     f32 = torch.float32
     g = {"write_keys": torch.empty((B, T, H, Fdk), dtype=f32, device=dev),

@@ -349,17 +349,45 @@ sdm_status hip_status(hipError_t e, const char* what) {
 // bfloat16 bank) [CHANGELOG 2.0.0, "New": bf16 snapshots on a float32 bank]. A bfloat16 snapshot of a float32
 // bank has native kernels when the held-row loop writes the snapshot and the fast reverse sweep (W, R <= 128) reads
 // it; other training calls are refused before any work, as the pages refuse snapshot routes they lack.
-sdm_status snapshot_kind(const sdm_config* cfg, const Dims& D, bool* bf16_snap) {
-  *bf16_snap = false;
-  if (cfg->snapshot_dtype == 0 || (cfg->snapshot_dtype == SDM_BF16 && D.bank == SDM_BF16)) return SDM_OK;
-  if (cfg->snapshot_dtype != SDM_BF16)
-    return fail(SDM_ERR_DTYPE, "snapshot_dtype = %d (0: the bank dtype, or SDM_BF16)", cfg->snapshot_dtype);
+sdm_status snapshot_kind(const sdm_config* cfg, const Dims& D, int* mode) {
+  *mode = SNAP_BANK;
+  const int sd = cfg->snapshot_dtype;
+  if (sd == 0 || (sd == SDM_BF16 && D.bank == SDM_BF16)) return SDM_OK;
+  if (sd != SDM_BF16 && sd != SDM_FP8 && sd != SDM_INT4)
+    return fail(SDM_ERR_DTYPE, "snapshot_dtype = %d (0: the bank dtype, SDM_BF16, SDM_FP8 or SDM_INT4)", sd);
+  const char* name = sd == SDM_BF16 ? "bfloat16" : sd == SDM_FP8 ? "fp8" : "int4";
+  if (sd != SDM_BF16) {
+    if (D.bank != SDM_F32)
+      return fail(SDM_ERR_RANGE, "no native route for %s snapshots of a bfloat16 bank (only a float32 bank's snapshot "
+                  "is quantized): use snapshot_dtype 0", name);
+    // the pages' refusals for quantized snapshots (CHANGELOG 2.0.0, "Behavior changes")
+    const int n = (D.d + 127) / 128;
+    if (D.d > 16384 || D.d % 4 != 0 || D.d % n != 0 || (D.d / n) % 4 != 0)
+      return fail(SDM_ERR_RANGE, "no quantized route for head_dim %d (above 16384, not a multiple of 4, or not "
+                  "splitting into ceil(head_dim / 128) = %d equal column slices of 16-byte rows): use snapshot_dtype 0",
+                  D.d, n);
+    if (sd == SDM_INT4 && (D.d / n) % 8 == 4)
+      return fail(SDM_ERR_RANGE, "no native route for int4 snapshots of a float32 bank whose %d column slices are %d "
+                  "columns wide (4 mod 8): use SDM_FP8 or snapshot_dtype 0", n, D.d / n);
+    // this library's quantization groups
+    if (D.d % SNAP_GROUP != 0)
+      return fail(SDM_ERR_RANGE, "no native route for %s snapshots with head_dim %d (groups of %d columns): use "
+                  "snapshot_dtype 0", name, D.d, SNAP_GROUP);
+  }
   if (!loop_held_snap_ok(D) || !bwd_fast(D))
-    return fail(SDM_ERR_RANGE, "no native route for a bfloat16 snapshot of a float32 bank at these settings (it "
+    return fail(SDM_ERR_RANGE, "no native route for a %s snapshot of a float32 bank at these settings (it "
                 "needs the held-row loop: chunk a power of two in [8, 128], at most 32 terms per lane group, and "
-                "num_writes, num_reads <= 128): use snapshot_dtype 0");
-  *bf16_snap = true;
+                "num_writes, num_reads <= 128): use snapshot_dtype 0", name);
+  *mode = sd == SDM_BF16 ? SNAP_BF16 : sd == SDM_FP8 ? SNAP_FP8 : SNAP_INT4;
   return SDM_OK;
+}
+
+// Bytes of the backward snapshot of mode `mode` (snapshot_kind) for D.
+size_t snapshot_bytes(const Dims& D, int mode) {
+  const size_t rows = (size_t)D.S * D.T * D.W;
+  if (mode == SNAP_FP8 || mode == SNAP_INT4)
+    return rows * (size_t)(snap_row_elem_bytes(mode, D.d) + snap_row_scale_bytes(D.d));
+  return rows * (size_t)D.d * (mode == SNAP_BF16 ? 2 : esize(D.bank));
 }
 
 }  // namespace
@@ -428,9 +456,9 @@ static sdm_status write_read_impl(const sdm_config* cfg, const void* write_keys,
   Dims D;
   TopkPlan pw, pr;
   TRY(validate(cfg, SDM_OP_WRITE_READ, 0, &D, &pw, &pr));
-  bool bf16_snap = false;
-  if (snapshot) TRY(snapshot_kind(cfg, D, &bf16_snap));
-  const size_t snap_bytes = (size_t)D.S * D.T * D.W * D.d * (bf16_snap ? 2 : esize(D.bank));
+  int snap_mode = SNAP_BANK;
+  if (snapshot) TRY(snapshot_kind(cfg, D, &snap_mode));
+  const size_t snap_bytes = snapshot_bytes(D, snap_mode);
   if (snapshot || cfg->shared_bank) {
     if (cfg->shared_bank && snapshot)
       return fail(SDM_ERR_RANGE, "a shared bank has no backward (sdm_write_read_save refuses shared_bank)");
@@ -532,7 +560,7 @@ static sdm_status write_read_impl(const sdm_config* cfg, const void* write_keys,
   la.out = out;
   la.abort = abort;
   la.snap = snapshot;
-  la.snap_bf16 = bf16_snap ? 1 : 0;
+  la.snap_mode = snap_mode;
   TRY(hip_status(timed(SDM_K_LOOP, st, [&] { return launch_loop(D, la, st); }), "chunk loop launch"));
   return ok();
 }
@@ -566,8 +594,8 @@ sdm_status sdm_write_read_backward(const sdm_config* cfg, const void* write_keys
   Dims D;
   TopkPlan pw, pr;
   TRY(validate(cfg, SDM_OP_BACKWARD, 0, &D, &pw, &pr));
-  bool bf16_snap = false;
-  TRY(snapshot_kind(cfg, D, &bf16_snap));
+  int snap_mode = SNAP_BANK;
+  TRY(snapshot_kind(cfg, D, &snap_mode));
   const long long rows = (long long)D.B * D.T * D.H;
   long long sumn = 0;
   for (int f = 0; f < D.F; ++f) sumn += D.widths[f];
@@ -595,7 +623,7 @@ sdm_status sdm_write_read_backward(const sdm_config* cfg, const void* write_keys
                        {forget_gate, (size_t)rows * ea, "forget_gate"},
                        {input_gate, (size_t)rows * ea, "input_gate"},
                        {subkeys, (size_t)D.H * sumn * D.dk * ea, "subkeys"},
-                       {snapshot, (size_t)D.S * D.T * D.W * D.d * (bf16_snap ? 2 : eb), "snapshot"},
+                       {snapshot, snapshot_bytes(D, snap_mode), "snapshot"},
                        {grad_out, (size_t)rows * D.d * ea, "grad_out"}};
   const Range outs[] = {{bank, nbank * eb, "bank"},
                         {grad_bank, nbank * 4, "grad_bank"},
@@ -645,7 +673,7 @@ sdm_status sdm_write_read_backward(const sdm_config* cfg, const void* write_keys
   ba.gout = grad_out;
   ba.bank = bank;
   ba.snap = snapshot;
-  ba.snap_bf16 = bf16_snap ? 1 : 0;
+  ba.snap_mode = snap_mode;
   ba.gbank = grad_bank;
   ba.gwkeys = grad_write_keys;
   ba.grq = grad_read_queries;
@@ -1025,6 +1053,17 @@ sdm_status sdm_layer_forward(const sdm_layer_config* cfg, const void* x, const v
   go.nseg = 1;
   go.seg[0] = {(int)Dm, (bf16_t*)y, (int)Dm};
   TRY(hip_status(timed(SDM_K_DENSE, st, [&] { return launch_gemm_bf16(go, st); }), "output projection launch"));
+  return ok();
+}
+
+sdm_status sdm_snapshot_bytes(const sdm_config* cfg, size_t* bytes) {
+  if (!bytes) return fail(SDM_ERR_NULL, "bytes must not be NULL");
+  Dims D;
+  TopkPlan pw, pr;
+  TRY(validate(cfg, SDM_OP_BACKWARD, 0, &D, &pw, &pr));
+  int mode = SNAP_BANK;
+  TRY(snapshot_kind(cfg, D, &mode));
+  *bytes = snapshot_bytes(D, mode);
   return ok();
 }
 

@@ -281,15 +281,37 @@ __global__ __launch_bounds__(64) void bwd_match_kernel(Dims D, BwdArgs a) {
 // follow the end-of-token barrier, after every store of token t in the workgroup's program order (one CU: its
 // vector memory pipeline keeps that order).
 // LPG lanes per term group (4 columns each): slices of 4 LPG columns, 128 groups, 128 LPG threads (2 LPG waves).
-// Sk: the snapshot's element type (Bk, or bfloat16 rows of a float32 bank, which restore the bank widened).
-template <typename A, typename Bk, int LPG, typename Sk = Bk>
+// Sk: the snapshot's element type (Bk, or bfloat16 rows of a float32 bank, which restore the bank widened). SQ:
+// SNAP_FP8 / SNAP_INT4 for a quantized snapshot of a float32 bank (Sk unused): a lane reads its 4 elements (4 or 2
+// bytes) and its 16-column group's scale byte, and the bank is restored from the dequantized values.
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+template <int SQ> struct SnapQ {  // the raw snapshot piece of a lane: x = elements, y = scale byte
+  typedef u32x2_t T;
+  __device__ static T load(const unsigned char* el, const unsigned char* sc, long long row, int d, int col) {
+    const long long e = row * d + col;
+    const uint32_t x = SQ == SNAP_FP8 ? *(const uint32_t*)(el + e) : (uint32_t)*(const uint16_t*)(el + e / 2);
+    return u32x2_t{x, (uint32_t)sc[row * (d / SNAP_GROUP) + col / SNAP_GROUP]};
+  }
+  __device__ static void unpack(T r, float* v) {
+    const float s = ldexpf(1.0f, (int)r.y - 127);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float q = SQ == SNAP_FP8 ? e4m3_decode((r.x >> (8 * k)) & 0xFFu)
+                                     : (float)((int)(((r.x >> (4 * k)) & 0xFu) << 28) >> 28);
+      v[k] = q * s;
+    }
+  }
+};
+
+template <typename A, typename Bk, int LPG, typename Sk = Bk, int SQ = SNAP_BANK>
 __global__ __launch_bounds__(128 * LPG) void bwd_sweep_fast_kernel(Dims D, BwdArgs a, int nsl) {
   constexpr int COLS = 4 * LPG, NW = 2 * LPG;
+  constexpr bool QS = SQ == SNAP_FP8 || SQ == SNAP_INT4;
   __shared__ __align__(16) float sRedD[NW][COLS];
   __shared__ __align__(16) float sRedR[NW][COLS];
   __shared__ float sRedGP[NW];
   typedef typename Raw4<Bk>::T RawT;
-  typedef typename Raw4<Sk>::T RawS;
+  typedef typename std::conditional<QS, typename SnapQ<SQ>::T, typename Raw4<Sk>::T>::type RawS;
   typedef typename Raw4<A>::T ARaw;
   const int W = D.W, R = D.R, T = D.T, d = D.d;
   const int nblk = gridDim.x;
@@ -306,6 +328,13 @@ __global__ __launch_bounds__(128 * LPG) void bwd_sweep_fast_kernel(Dims D, BwdAr
   Bk* bank = (Bk*)a.bank + (long long)st * D.rows * D.ld;
   float* gbank = a.gbank + (long long)st * D.rows * D.ld;
   const Sk* snap = (const Sk*)a.snap + (long long)st * T * W * d;
+  // quantized snapshot: the elements of every stream, then the scale bytes of every stream
+  const unsigned long long qrows = (unsigned long long)T * W;
+  const unsigned char* qel = (const unsigned char*)a.snap + (QS ? st * qrows * snap_row_elem_bytes(SQ, d) : 0);
+  const unsigned char* qsc = (const unsigned char*)a.snap +
+                             (QS ? (unsigned long long)D.S * qrows * snap_row_elem_bytes(SQ, d) +
+                                       st * qrows * snap_row_scale_bytes(d)
+                                 : 0);
   const A* gout = (const A*)a.gout;
   const A* values = (const A*)a.values;
   const A* alpha = (const A*)a.alpha;
@@ -330,7 +359,10 @@ __global__ __launch_bounds__(128 * LPG) void bwd_sweep_fast_kernel(Dims D, BwdAr
     be_ = Word<A>::load(beta + row + zero);
     dout_ = Raw4<A>::load(gout + row * d + dcol);
     v_ = Raw4<A>::load(values + row * d + dcol);
-    sp_ = Raw4<Sk>::load(snap + ((long long)t * W + jw) * d + dcol);
+    if constexpr (QS)
+      sp_ = SnapQ<SQ>::load(qel, qsc, (long long)t * W + jw, d, dcol);
+    else
+      sp_ = Raw4<Sk>::load(snap + ((long long)t * W + jw) * d + dcol);
   };
 
   int rs, ws, rs1, ws1;
@@ -374,7 +406,10 @@ __global__ __launch_bounds__(128 * LPG) void bwd_sweep_fast_kernel(Dims D, BwdAr
     rg.x += rho * dout[0]; rg.y += rho * dout[1]; rg.z += rho * dout[2]; rg.w += rho * dout[3];
     // the write: g_i (plus this token's read update of the same slot), P_i
     float g[4] = {wg.x + mr * dout[0], wg.y + mr * dout[1], wg.z + mr * dout[2], wg.w + mr * dout[3]}, pp[4];
-    Raw4<Sk>::unpack(c_sp, pp);
+    if constexpr (QS)
+      SnapQ<SQ>::unpack(c_sp, pp);
+    else
+      Raw4<Sk>::unpack(c_sp, pp);
     if (!valid) pp[0] = pp[1] = pp[2] = pp[3] = 0.f;
     // the looked-ahead values are in (issued before this token's rows, which were just waited for): take them
     // here, before any store, so that moving them into place at the end of the token waits for nothing
@@ -443,9 +478,9 @@ __global__ __launch_bounds__(128 * LPG) void bwd_sweep_fast_kernel(Dims D, BwdAr
         const float cw = ab * w;
         *(float4*)(gbank + (long long)ws * D.ld + col) = make_float4(
             al * g[0] - cw * Dl[0], al * g[1] - cw * Dl[1], al * g[2] - cw * Dl[2], al * g[3] - cw * Dl[3]);
-        if constexpr (std::is_same<Sk, Bk>::value)
+        if constexpr (std::is_same<Sk, Bk>::value && !QS)
           Raw4<Bk>::store(bank + (long long)ws * D.ld + col, c_sp);
-        else  // a float32 bank from bfloat16 snapshot rows (pp: the widened values)
+        else  // a float32 bank from bfloat16 or quantized snapshot rows (pp: the widened values)
           *(float4*)(bank + (long long)ws * D.ld + col) = make_float4(pp[0], pp[1], pp[2], pp[3]);
       }
     }
@@ -592,17 +627,22 @@ static hipError_t launch_bwd_t(const Dims& D, const BwdArgs& a, hipStream_t st) 
   if (bwd_fast(D)) {
     hipLaunchKernelGGL(bwd_match_kernel, dim3((unsigned)((long long)D.S * D.T)), dim3(64), 0, st, D, a);
     const dim3 grid((unsigned)((long long)D.S * nsl));
-    auto fast = [&](auto sk) {  // sk: a value of the snapshot's element type
+    auto fast = [&](auto sk, auto sq) {  // sk: a value of the snapshot's element type; sq: its mode
       using Sk = decltype(sk);
+      constexpr int SQ = decltype(sq)::value;
       if (bwd_cols(D) == 8)
-        hipLaunchKernelGGL((bwd_sweep_fast_kernel<A, Bk, 2, Sk>), grid, dim3(256), 0, st, D, a, nsl);
+        hipLaunchKernelGGL((bwd_sweep_fast_kernel<A, Bk, 2, Sk, SQ>), grid, dim3(256), 0, st, D, a, nsl);
       else
-        hipLaunchKernelGGL((bwd_sweep_fast_kernel<A, Bk, 4, Sk>), grid, dim3(512), 0, st, D, a, nsl);
+        hipLaunchKernelGGL((bwd_sweep_fast_kernel<A, Bk, 4, Sk, SQ>), grid, dim3(512), 0, st, D, a, nsl);
     };
-    if (std::is_same<Bk, float>::value && a.snap_bf16)
-      fast(bf16_t{});  // bfloat16 snapshot rows of a float32 bank
+    if (std::is_same<Bk, float>::value && a.snap_mode == SNAP_BF16)
+      fast(bf16_t{}, std::integral_constant<int, SNAP_BANK>{});  // bfloat16 snapshot rows of a float32 bank
+    else if (std::is_same<Bk, float>::value && a.snap_mode == SNAP_FP8)
+      fast(Bk{}, std::integral_constant<int, SNAP_FP8>{});
+    else if (std::is_same<Bk, float>::value && a.snap_mode == SNAP_INT4)
+      fast(Bk{}, std::integral_constant<int, SNAP_INT4>{});
     else
-      fast(Bk{});
+      fast(Bk{}, std::integral_constant<int, SNAP_BANK>{});
   } else {
     const size_t lds = bwd_sweep_lds(D.W);
     (void)hipFuncSetAttribute((const void*)bwd_sweep_kernel<A, Bk>, hipFuncAttributeMaxDynamicSharedMemorySize,

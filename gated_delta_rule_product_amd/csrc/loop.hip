@@ -456,7 +456,7 @@ template <> struct Act4<bf16_t> {
 // snapshot (a.snap; the plan tagged every event with its term index): a slot's only event stores its held row (the
 // chunk-start row, the row before that event), and a slot written more than once stores its running row before
 // each of its events.
-template <typename A, typename Bk, bool FULL, bool SNAP, bool SB = false>
+template <typename A, typename Bk, bool FULL, bool SNAP, int SM = SNAP_BANK>
 __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, int nslices) {
   if (a.abort && *a.abort) return;  // shared-bank conflict: no work (uniform over the grid)
   constexpr int EPL = Lane<Bk>::EPL;
@@ -647,25 +647,61 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
     const bool mrows = cnt.nmseg <= HELD_MROWS;
     const MSeg* msegs_g = (const MSeg*)(greg + CL.multi);
     // snapshot rows of this stream: row (t, i) at (t * W + i) * d, through a buffer resource (base in scalar
-    // registers, 32-bit lane offsets: the held rows leave few vector registers); SB: bfloat16 rows (each float
-    // rounded to nearest even), 8 bytes per lane instead of 16
-    constexpr uint32_t SES = SB ? 2u : 4u;  // bytes per snapshot element
-    __amdgpu_buffer_rsrc_t rsnap;
-    if constexpr (SNAP)
+    // registers, 32-bit lane offsets: the held rows leave few vector registers); SM = SNAP_BF16: bfloat16 rows (each
+    // float rounded to nearest even), 8 bytes per lane instead of 16; SNAP_FP8 / SNAP_INT4: the 4 lanes of a lane
+    // group hold one 16-column group, whose scale comes from their largest magnitude (two DPP moves inside the
+    // quad); a lane stores its 4 elements (4 or 2 bytes) and the group's first lane the scale byte
+    constexpr bool QS = SM == SNAP_FP8 || SM == SNAP_INT4;
+    constexpr uint32_t SES = SM == SNAP_BF16 ? 2u : 4u;  // bytes per snapshot element (SNAP_BANK, SNAP_BF16)
+    __amdgpu_buffer_rsrc_t rsnap, rscale;
+    if constexpr (SNAP && !QS)
       rsnap = __builtin_amdgcn_make_buffer_rsrc((void*)((char*)a.snap + (long long)st * D.T * D.W * D.d * SES),
                                                 (short)0, (int)(uint32_t)((unsigned long long)D.T * D.W * D.d * SES),
                                                 BUF_RSRC_WORD3);
-    auto snap_off = [&](int t, int i) -> uint32_t {
-      return (uint32_t)((((uint32_t)(t0 + t) * (uint32_t)W + (uint32_t)i) * (uint32_t)D.d + (uint32_t)mycol) * SES);
-    };
-    auto snap_store = [&](uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3, uint32_t off) {
-      if constexpr (SB) {
+    if constexpr (SNAP && QS) {
+      const unsigned long long rows_s = (unsigned long long)D.T * D.W;  // snapshot rows per stream
+      const unsigned long long eb = snap_row_elem_bytes(SM, D.d), sb = snap_row_scale_bytes(D.d);
+      rsnap = __builtin_amdgcn_make_buffer_rsrc((void*)((char*)a.snap + st * rows_s * eb), (short)0,
+                                                (int)(uint32_t)(rows_s * eb), BUF_RSRC_WORD3);
+      rscale = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)((char*)a.snap + (unsigned long long)D.S * rows_s * eb + st * rows_s * sb), (short)0,
+          (int)(uint32_t)(rows_s * sb), BUF_RSRC_WORD3);
+    }
+    auto snap_row = [&](int t, int i) -> uint32_t { return (uint32_t)(t0 + t) * (uint32_t)W + (uint32_t)i; };
+    auto snap_store = [&](uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3, uint32_t srow) {
+      if constexpr (SM == SNAP_BANK) {
+        __builtin_amdgcn_raw_buffer_store_b128(w16_t{x0, x1, x2, x3}, rsnap,
+                                               (int)((srow * (uint32_t)D.d + (uint32_t)mycol) * SES), 0, 0);
+      } else if constexpr (SM == SNAP_BF16) {
         const uint32_t lo = (uint32_t)f_to_bf16(__uint_as_float(x0)) | ((uint32_t)f_to_bf16(__uint_as_float(x1)) << 16);
         const uint32_t hi = (uint32_t)f_to_bf16(__uint_as_float(x2)) | ((uint32_t)f_to_bf16(__uint_as_float(x3)) << 16);
         typedef unsigned int u32x2_t __attribute__((__vector_size__(2 * sizeof(unsigned int))));
-        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{lo, hi}, rsnap, (int)off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{lo, hi}, rsnap,
+                                              (int)((srow * (uint32_t)D.d + (uint32_t)mycol) * SES), 0, 0);
       } else {
-        __builtin_amdgcn_raw_buffer_store_b128(w16_t{x0, x1, x2, x3}, rsnap, (int)off, 0, 0);
+        const float v[4] = {__uint_as_float(x0), __uint_as_float(x1), __uint_as_float(x2), __uint_as_float(x3)};
+        float am = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+        am = fmaxf(am, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(am), 0xB1, 0xf, 0xf, false)));
+        am = fmaxf(am, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(am), 0x4E, 0xf, 0xf, false)));
+        uint32_t word = 0, sbyte = 0;
+        if (am > 0.0f) {
+          const int e = snap_scale_exp(am, SM == SNAP_FP8 ? 8 : 2);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float x = ldexpf(v[k], -e);
+            word |= (SM == SNAP_FP8 ? e4m3_encode(x) : ((uint32_t)(int)rintf(x) & 0xFu)) << ((SM == SNAP_FP8 ? 8 : 4) * k);
+          }
+          sbyte = (uint32_t)min(max(e + 127, 0), 255);
+        }
+        const uint32_t el = srow * (uint32_t)D.d + (uint32_t)mycol;  // element index
+        if constexpr (SM == SNAP_FP8)
+          __builtin_amdgcn_raw_buffer_store_b32(word, rsnap, (int)el, 0, 0);
+        else
+          __builtin_amdgcn_raw_buffer_store_b16((unsigned short)word, rsnap, (int)(el / 2), 0, 0);
+        if (q == 0)
+          __builtin_amdgcn_raw_buffer_store_b8((unsigned char)sbyte, rscale,
+                                               (int)(srow * (uint32_t)(D.d / SNAP_GROUP) + (uint32_t)mycol / SNAP_GROUP),
+                                               0, 0);
       }
     };
     if (act) {
@@ -676,7 +712,7 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
         if (FULL || u < tpw) {
           const int code = wl[u];
           if (code == -2) {  // the slot's only event: own token, own weight
-            if constexpr (SNAP) snap_store(row[u].x, row[u].y, row[u].z, row[u].w, snap_off(gt, part * tpw + u));
+            if constexpr (SNAP) snap_store(row[u].x, row[u].y, row[u].z, row[u].w, snap_row(gt, part * tpw + u));
             float m[EPL];
             Lane<Bk>::unpack(row[u], m);
             const Pair p = pw[u];
@@ -696,7 +732,7 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
                 const int tk = SNAP ? (x.tok & 0xFFFF) : x.tok;
                 if constexpr (SNAP)
                   snap_store(__float_as_uint(m[0]), __float_as_uint(m[1]), __float_as_uint(m[2]), __float_as_uint(m[3]),
-                             snap_off(tk, x.tok >> 16));
+                             snap_row(tk, x.tok >> 16));
                 const float al = sA[tk];
 #pragma unroll
                 for (int k = 0; k < EPL; ++k) m[k] = al * m[k] + x.w * sD[tk * COLS + q * EPL + k];
@@ -737,7 +773,7 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
             if constexpr (SNAP)
               if (valid)
                 snap_store(__float_as_uint(m[0]), __float_as_uint(m[1]), __float_as_uint(m[2]), __float_as_uint(m[3]),
-                           snap_off(tk, x.tok >> 16));
+                           snap_row(tk, x.tok >> 16));
             const float al = sA[tk];
             const float4 dd = *(const float4*)(sD + tk * COLS + q * EPL);
             m[0] = al * m[0] + x.w * dd.x; m[1] = al * m[1] + x.w * dd.y;
@@ -1206,8 +1242,12 @@ static hipError_t launch_loop_t(const Dims& D, const LoopArgs& a, hipStream_t st
         (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         hipLaunchKernelGGL(kern, dim3((unsigned)nblk), dim3(LOOP_NT), lds, st, D, a, nslices);
       };
-      if (a.snap && a.snap_bf16) {
-        if (full) go(loop_held_kernel<A, Bk, true, true, true>); else go(loop_held_kernel<A, Bk, false, true, true>);
+      if (a.snap && a.snap_mode == SNAP_BF16) {
+        if (full) go(loop_held_kernel<A, Bk, true, true, SNAP_BF16>); else go(loop_held_kernel<A, Bk, false, true, SNAP_BF16>);
+      } else if (a.snap && a.snap_mode == SNAP_FP8) {
+        if (full) go(loop_held_kernel<A, Bk, true, true, SNAP_FP8>); else go(loop_held_kernel<A, Bk, false, true, SNAP_FP8>);
+      } else if (a.snap && a.snap_mode == SNAP_INT4) {
+        if (full) go(loop_held_kernel<A, Bk, true, true, SNAP_INT4>); else go(loop_held_kernel<A, Bk, false, true, SNAP_INT4>);
       } else if (a.snap) {
         if (full) go(loop_held_kernel<A, Bk, true, true>); else go(loop_held_kernel<A, Bk, false, true>);
       } else {

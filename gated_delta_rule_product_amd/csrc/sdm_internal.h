@@ -158,6 +158,42 @@ template <typename T> __device__ __forceinline__ T from_f(float v);
 template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
 template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float v) { return f_to_bf16(v); }
 
+// Backward snapshot modes: the rows in the bank dtype, or a float32 bank's rows as bfloat16, fp8 or int4.
+enum { SNAP_BANK = 0, SNAP_BF16 = 1, SNAP_FP8 = 2, SNAP_INT4 = 3 };
+// Quantized snapshots (fp8, int4) of float32 rows: groups of SNAP_GROUP columns, each with a power-of-two scale 2^e
+// stored as the byte e + 127 (after all elements of all streams: [S][T][W][d / SNAP_GROUP]); elements [S][T][W][d]
+// as OCP FP8 E4M3 bytes (fp8) or int4 nibbles in [-7, 7] (two per byte, the even column in the low nibble), each the
+// format's nearest value to x / 2^e, ties to even. e is the smallest exponent with (the group's largest magnitude)
+// / 2^e <= 448 (E4M3's largest value) or <= 7 (int4).
+constexpr int SNAP_GROUP = 16;
+// Bytes of a stream's snapshot elements (T W rows) and scales, per row of d columns.
+__host__ __device__ inline unsigned long long snap_row_elem_bytes(int mode, int d) {
+  return mode == SNAP_FP8 ? (unsigned long long)d : (unsigned long long)d / 2;
+}
+__host__ __device__ inline unsigned long long snap_row_scale_bytes(int d) { return (unsigned long long)d / SNAP_GROUP; }
+
+// The scale exponent of a group with largest magnitude amax > 0 (a normal float): amax = m 2^e0 with m in [1, 2);
+// qmax = 1.75 * 2^k (k = 8 for E4M3, 2 for int4), so amax / 2^(e0 - k) = m 2^k <= qmax exactly when m <= 1.75.
+__device__ __forceinline__ int snap_scale_exp(float amax, int k) {
+  const uint32_t u = __float_as_uint(amax);
+  const int e0 = (int)((u >> 23) & 0xFF) - 127;
+  return e0 - k + ((u & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+}
+// Nearest OCP E4M3 byte to v (|v| <= 448), ties to even.
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+  const uint32_t sgn = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fabsf(v);
+  if (a < 0.015625f) return sgn | (uint32_t)rintf(a * 512.0f);  // subnormals (spacing 2^-9); 8 is 2^-6 (E = 1)
+  const uint32_t u = __float_as_uint(a);
+  const uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);            // round the 23-bit mantissa to 3 bits
+  return sgn | ((((r >> 23) - 120u) << 3) | ((r >> 20) & 7u));    // exponent field: e + 7 = (r >> 23) - 127 + 7
+}
+__device__ __forceinline__ float e4m3_decode(uint32_t b) {
+  const uint32_t E = (b >> 3) & 15u, M = b & 7u;
+  const float a = E == 0 ? (float)M * 0.001953125f : __uint_as_float(((E + 120u) << 23) | (M << 20));
+  return (b & 0x80u) ? -a : a;
+}
+
 // A bank row value after one write event, as the per-token recurrence stores it: float32 rows keep every bit,
 // bfloat16 rows are rounded to nearest even after every event (a slot written several times in one chunk goes
 // through the same roundings as when its events come one token at a time).
@@ -284,7 +320,7 @@ struct LoopArgs {
   const int32_t* abort;   // if not NULL and *abort != 0: do nothing (shared-bank conflict)
   void* snap;             // if not NULL: [S][T][W][d] bank dtype, the row of every write event before it (the
                           // held-row or the segmented loop writes it; needs PlanArgs::evcode)
-  int snap_bf16;          // the snapshot in bfloat16 (float32 bank, held-row loop only), rounded to nearest even
+  int snap_mode;          // SNAP_*: the snapshot's rows as stored (float32 bank, held-row loop only for 1-3)
 };
 hipError_t launch_loop(const Dims& D, const LoopArgs& a, hipStream_t st);
 // True if launch_loop runs the held-row variant (which reads last-event codes, not slot segments).
@@ -302,8 +338,8 @@ struct BwdArgs {
   const void* wkeys; const void* rq; const void* subkeys;                         // activation dtype
   const void* alpha; const void* beta; const void* values; const void* gout;      // activation dtype
   void* bank;             // [S][rows][ld] bank dtype: after the forward on entry, before it on return
-  const void* snap;       // [S][T][W][d] bank dtype
-  int snap_bf16;          // the snapshot holds bfloat16 rows (a float32 bank restored from them)
+  const void* snap;       // [S][T][W][d] bank dtype, or the snapshot of snap_mode
+  int snap_mode;          // SNAP_*: the snapshot's rows as stored (a float32 bank restored from them for 1-3)
   float* gbank;           // [S][rows][ld]: gradient w.r.t. the bank after the call in, before the call out
   float* gwkeys; float* grq; float* gvalues; float* galpha; float* gbeta; float* gsub;
   float* part; float* ds; float* sgpart;  // workspace

@@ -70,7 +70,13 @@ typedef enum {
   SDM_ERR_NULL = 9            /* a required pointer is NULL */
 } sdm_status;
 
-typedef enum { SDM_F32 = 0, SDM_BF16 = 1, SDM_F16 = 2 /* always refused */ } sdm_dtype;
+typedef enum {
+  SDM_F32 = 0,
+  SDM_BF16 = 1,
+  SDM_F16 = 2,  /* always refused */
+  SDM_FP8 = 3,  /* snapshot_dtype only: OCP FP8 E4M3 rows in groups of 16 columns with a power-of-two scale */
+  SDM_INT4 = 4  /* snapshot_dtype only: int4 rows in [-7, 7], groups of 16 columns with a power-of-two scale */
+} sdm_dtype;
 
 typedef struct {
   int32_t batch;            /* B >= 0 */
@@ -99,9 +105,10 @@ typedef struct {
                                figures are quoted with it. */
   int32_t shared_bank;      /* sdm_write_read only (0 elsewhere): 1 = the B streams of a head share one bank,
                                bank [H, bank_rows, d], and must address disjoint slots (see sdm_shared_bank_check) */
-  int32_t snapshot_dtype;   /* read by sdm_write_read_save and sdm_write_read_backward only: 0 = the backward
-                               snapshot in the bank dtype, SDM_BF16 = in bfloat16 (on a float32 bank: half the
-                               bytes; each row rounded to nearest even; on a bfloat16 bank the same as 0) */
+  int32_t snapshot_dtype;   /* read by sdm_write_read_save, sdm_write_read_backward and sdm_snapshot_bytes only:
+                               0 = the backward snapshot in the bank dtype, SDM_BF16 = in bfloat16 (on a float32
+                               bank: half the bytes; each row rounded to nearest even; on a bfloat16 bank the same
+                               as 0), SDM_FP8 / SDM_INT4 = quantized (float32 banks only; see sdm_snapshot_bytes) */
   int32_t topk_scoring;     /* factor-scoring kernel of the batched top-k (ids and scores are identical for every
                                value; only the speed differs): SDM_SCORING_AUTO (0) = the bf16 matrix-core filter
                                where a factor has >= 512 sub-keys, else the fp64 chain over every sub-key;
@@ -154,6 +161,22 @@ sdm_status sdm_write_read_save(const sdm_config* cfg, const void* write_keys, co
                                const void* values, const void* forget_gate, const void* input_gate,
                                const void* subkeys, void* bank, void* out, void* snapshot, int32_t* write_idx,
                                int32_t* read_idx, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of the backward snapshot of cfg (cfg.snapshot_dtype), the size of sdm_write_read_save's `snapshot`. With
+ * rows = B * H * T * W snapshot rows of d = head_dim columns:
+ *   0 (bank dtype) / SDM_BF16: rows * d elements of the bank dtype / bfloat16, [B, H, T, W, d];
+ *   SDM_FP8 / SDM_INT4 (CHANGELOG 2.0.0, "New" and "Behavior changes": fp8 and int4 snapshots; their formats are not
+ *   given there, so this library's): each row in groups of 16 columns, each group with a power-of-two scale 2^e, e
+ *   the smallest exponent with (the group's largest magnitude) / 2^e <= 448 (fp8) or <= 7 (int4); an element x is
+ *   stored as the nearest value to x / 2^e, ties to even, of OCP FP8 E4M3 (one byte) or int4 in [-7, 7] (two's
+ *   complement nibbles, two per byte, the even column in the low nibble); the buffer holds all elements
+ *   [B, H, T, W, d] (rows * d or rows * d / 2 bytes) followed by all scale bytes e + 127 [B, H, T, W, d / 16].
+ *   The backward reads the rows back as value times scale (and restores the bank's written rows as those values).
+ *   Refused (SDM_ERR_RANGE, before any work), as the pages refuse them: head_dim above 16384, not a multiple of 4, or
+ *   not splitting into ceil(head_dim / 128) equal column slices of 16-byte rows; int4 when those slices are 4 mod 8
+ *   columns wide; and where this library has no route: a bfloat16 bank, head_dim not a multiple of 16, or settings
+ *   outside the held-row loop and the fast reverse sweep (as for SDM_BF16). */
+sdm_status sdm_snapshot_bytes(const sdm_config* cfg, size_t* bytes);
 
 /* Deterministic backward of the write/read (CHANGELOG 2.0.0, "Deterministic": every gradient bitwise repeatable;
  * "New": exact product-key top-k with a deterministic sparse backward; "Known limitations": the first backward

@@ -375,3 +375,33 @@ def test_large_chunks_run_as_sub_chunks(lib):
     assert s == B.SDM_OK and n == _status(_cfg(chunk_size=64, widths=(256, 256), num_writes=128, num_reads=64,
                                                tokens=1024))[1]
     assert _status(_cfg(chunk_size=131))[0] == B.SDM_OK  # a prime above 128: chunks of one token
+
+
+def test_quantized_snapshot_routes_and_sizes(lib):
+    """fp8 / int4 snapshots: the pages' refusals (head_dim above 16384, not a multiple of 4, not splitting into
+    ceil(head_dim / 128) equal slices of 16-byte rows; int4 with slices 4 mod 8 wide), this library's (a bfloat16
+    bank, head_dim not a multiple of 16, no held-row route), all before any work; sizes per include/sdm.h."""
+    def snap(**kw):
+        base = dict(widths=(32, 32), num_writes=8, num_reads=8, chunk_size=16, tokens=64)
+        base.update(kw)
+        cfg = _cfg(**base)
+        n = ctypes.c_size_t(0)
+        st = lib.sdm_snapshot_bytes(ctypes.byref(cfg), ctypes.byref(n))
+        return st, n.value
+    rows = 2 * 2 * 64 * 8
+    for d in (64, 400, 1024):
+        assert snap(head_dim=d, snapshot_dtype=B.SDM_FP8) == (B.SDM_OK, rows * (d + d // 16))
+    assert snap(head_dim=64, snapshot_dtype=B.SDM_INT4) == (B.SDM_OK, rows * (64 // 2 + 64 // 16))
+    assert snap(head_dim=64) == (B.SDM_OK, rows * 64 * 4)
+    assert snap(head_dim=64, snapshot_dtype=B.SDM_BF16) == (B.SDM_OK, rows * 64 * 2)
+    refused = [dict(head_dim=400, snapshot_dtype=B.SDM_INT4),           # 4 slices of 100 columns: 4 mod 8
+               dict(head_dim=12, snapshot_dtype=B.SDM_INT4),            # 1 slice of 12: 4 mod 8
+               dict(head_dim=16400, snapshot_dtype=B.SDM_FP8),          # above 16384
+               dict(head_dim=136, snapshot_dtype=B.SDM_FP8),            # groups of 16 columns
+               dict(head_dim=64, snapshot_dtype=B.SDM_FP8, bank_dtype=B.SDM_BF16, act_dtype=B.SDM_BF16),
+               dict(head_dim=64, snapshot_dtype=B.SDM_FP8, chunk_size=7)]  # no held-row route
+    for kw in refused:
+        st, _ = snap(**kw)
+        assert st == B.SDM_ERR_RANGE, (kw, B.last_error())
+    assert "4 mod 8" in (snap(head_dim=400, snapshot_dtype=B.SDM_INT4), B.last_error())[1]
+    assert snap(head_dim=64, snapshot_dtype=9)[0] == B.SDM_ERR_DTYPE

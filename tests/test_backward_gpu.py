@@ -342,3 +342,119 @@ def test_bf16_snapshot_refused_without_a_native_route():
                                     chunk_size=s.chunk_size, snapshot_quant="bf16")
     torch.cuda.synchronize()
     assert torch.equal(bank, bank0)
+
+
+# ------------------------------------------------------------------ fp8 / int4 snapshots of a float32 bank
+QUANT = {  # mode: (q_rel, q_grp) of the bound: one rounding that falls the other way on each side
+    "fp8": (2.0 ** -2, 2.0 ** -14),   # an E4M3 spacing is at most 2^-3 of the element (subnormals: 2^-9 scale units)
+    "int4": (0.0, 1.0 / 3.0),         # an int4 step is at most 2/7 of the group's largest magnitude (6/7 of it stored)
+}
+
+
+def _quantize_ref(rows, mode):
+    """The snapshot bytes of float32 rows [n, d] by this library's format, computed here with torch (E4M3 by
+    torch's float8_e4m3fn conversion, int4 by torch.round): elements then scale bytes."""
+    x = rows.reshape(-1, rows.shape[-1] // 16, 16).to(torch.float64)
+    amax = x.abs().amax(dim=2)
+    m, ex = torch.frexp(amax)  # amax = m 2^ex, m in [0.5, 1): amax = (2m) 2^(ex - 1)
+    k = 8 if mode == "fp8" else 2
+    e = ex - 1 - k + (2 * m > 1.75).to(ex.dtype)
+    e = torch.where(amax > 0, e, torch.full_like(e, -127))
+    y = x * torch.pow(2.0, -e.to(torch.float64)).unsqueeze(2)
+    if mode == "fp8":
+        el = y.to(torch.float32).to(torch.float8_e4m3fn).view(torch.uint8).reshape(rows.shape[0], -1)
+    else:
+        q = (torch.round(y).to(torch.int32) & 0xF).reshape(rows.shape[0], -1)
+        el = (q[:, 0::2] | (q[:, 1::2] << 4)).to(torch.uint8)
+    sc = (e + 127).clamp(0, 255).to(torch.uint8)
+    return torch.cat([el.reshape(-1), sc.reshape(-1)])
+
+
+def _quant_case(s, mode, bank_grad, exact_rows=False):
+    x = synth.make_inputs(s, seed=53)
+    if exact_rows:  # rows never change (alpha 1, beta 0) and are already in the format: no rounding anywhere
+        x["alpha"][:] = 1.0
+        x["beta"][:] = 0.0
+        x["bank"] = oracle.snap_rows(x["bank"], mode).astype(np.float32)
+    dout, dbank = _upstream(s, 54, bank_grad)
+    at = TORCH_DT[s.act]
+    t = {k: to_dev(x[k], at) for k in ("wkeys", "rq", "values", "alpha", "beta", "subkeys")}
+    kw = dict(widths=s.widths, num_writes=s.num_writes, num_reads=s.num_reads, chunk_size=s.chunk_size)
+    b_none, b_q = to_dev(x["bank"], torch.float32), to_dev(x["bank"], torch.float32)
+    o1, w1, _, snap_none = binding.sdm_write_read_save(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"],
+                                                       t["subkeys"], b_none, want_index=True, **kw)
+    o2, w2, _, snap_q = binding.sdm_write_read_save(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"],
+                                                    t["subkeys"], b_q, want_index=True, snapshot_quant=mode, **kw)
+    torch.cuda.synchronize()
+    assert snap_q.dtype == torch.uint8
+    assert torch.equal(o1, o2) and torch.equal(b_none, b_q) and torch.equal(w1, w2)
+    # the quantized snapshot is this format's quantization of the float32 snapshot, byte for byte
+    assert torch.equal(snap_q, _quantize_ref(snap_none.reshape(-1, s.head_dim), mode))
+    del snap_none
+    fwd = {"bank": b_q.float().cpu().numpy()}
+    g = binding.sdm_write_read_backward(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"], t["subkeys"], b_q,
+                                        snap_q, to_dev(dout, at),
+                                        None if dbank is None else to_dev(dbank, torch.float32),
+                                        snapshot_quant=mode, **kw)
+    torch.cuda.synchronize()
+    # the bank comes back with exactly the written rows as the snapshot stores them
+    written = np.zeros((s.batch, s.heads, s.rows), bool)
+    wi = w1.cpu().numpy()
+    for b in range(s.batch):
+        for h in range(s.heads):
+            written[b, h, wi[b, :, h].reshape(-1)] = True
+    expect = np.where(written[..., None], oracle.snap_rows(x["bank"], mode), x["bank"])
+    assert np.array_equal(b_q.cpu().numpy(), expect.astype(np.float32)), "the bank is not the quantized restore"
+    q_rel, q_grp = (0.0, 0.0) if exact_rows else QUANT[mode]
+    eps = 0.0 if exact_rows else EPS_ROW[s.bank]
+    ref = oracle.write_read_backward_bounds(x["wkeys"], x["rq"], x["values"], x["alpha"], x["beta"], x["subkeys"],
+                                            x["bank"], dout, dbank, s.widths, s.num_writes, s.num_reads,
+                                            eps_row=eps, q_rel=q_rel, q_grp=q_grp, snap_quant=mode,
+                                            want_snapshot=True)
+    ok, e = rows_within(fwd["bank"], ref["bank"], EPS_ROW[s.bank])
+    assert ok, f"bank after the forward beyond the tolerance ({e:.3g})"
+    check(s, {k: v.cpu().numpy() for k, v in g.items()}, ref)
+
+
+@pytest.mark.parametrize("mode", ["fp8", "int4"])
+@pytest.mark.parametrize("name,s,bank_grad", SNAP_CASES, ids=[c[0] for c in SNAP_CASES])
+def test_quantized_snapshot(name, s, bank_grad, mode):
+    """CHANGELOG 2.0.0, "New" / "Behavior changes" (fp8 and int4 snapshots): the saving forward's out, bank and ids
+    equal the float32 snapshot's bit for bit, the snapshot is that snapshot quantized byte for byte (groups of 16
+    columns, power-of-two scales, E4M3 by torch's float8 conversion, int4 by torch.round), the bank comes back with
+    exactly the written rows quantized, and the gradients match the oracle's quantized-snapshot backward within its
+    a-priori bound (rows within the forward tolerance, plus one quantization step where a rounding may fall the
+    other way)."""
+    print(f"quantized snapshot {mode} {name}", flush=True)
+    _quant_case(s, mode, bank_grad)
+
+
+@pytest.mark.parametrize("mode", ["fp8", "int4"])
+def test_quantized_snapshot_exact_rows(mode):
+    """Rows that never change (forget gate 1, input gate 0) and are already in the format: the GPU's snapshot rows
+    equal the oracle's exactly, so the bound is the float32 arithmetic's alone (no row allowance)."""
+    s = synth.Shape(2, 64, 2, (16, 16), 8, 64, 8, 8, 16, name="qexact")
+    print(f"quantized snapshot {mode}, exact rows", flush=True)
+    _quant_case(s, mode, True, exact_rows=True)
+
+
+def test_quantized_snapshot_refused_before_any_work():
+    s = synth.WORKLOADS["tiny_1k"].with_(tokens=50, batch=1, heads=2, chunk_size=16, head_dim=40)
+    x = synth.make_inputs(s, seed=2)
+    t = {k: to_dev(x[k], torch.float32) for k in ("wkeys", "rq", "values", "alpha", "beta", "subkeys")}
+    bank = to_dev(x["bank"], torch.float32)
+    bank0 = bank.clone()
+    with pytest.raises(binding.UnsupportedConfigurationError, match="groups of 16"):
+        binding.sdm_write_read_save(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"], t["subkeys"], bank,
+                                    widths=s.widths, num_writes=s.num_writes, num_reads=s.num_reads,
+                                    chunk_size=s.chunk_size, snapshot_quant="fp8")
+    torch.cuda.synchronize()
+    assert torch.equal(bank, bank0)
+
+
+@pytest.mark.slow
+def test_fp8_snapshot_layer_65k_full_size():
+    """fp8 snapshot at the full layer_65k workload (8-column sweep slices sharing each group's scale)."""
+    s = synth.WORKLOADS["layer_65k"]
+    print("full-size fp8 snapshot", flush=True)
+    _quant_case(s, "fp8", True)
