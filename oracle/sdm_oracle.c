@@ -430,6 +430,9 @@ int oracle_write_read(int B, int T, int H, int F, const int* widths, int dk, int
  * After the first token G is the gradient of the bank before the call. Every sum is fp64 in a fixed order.
  * exact = 1 keeps the bank states in fp64 (no rounding to the bank dtype): the smooth function that the finite-
  * difference pins differentiate. exact = 0 rounds them after every token exactly as oracle_write_read does.
+ * grad_bank_bf16 = 1 accumulates the bank gradient in bfloat16, the bank dtype of a bfloat16 bank ([CL] 2.0.0,
+ * "Deterministic": float32 accumulation of the bank gradient, grad_bank_fp32, is the opt-in; the default keeps it in
+ * the bank dtype): every update of G (the read's and the write's) is rounded to bfloat16 (nearest, ties to even).
  *
  * Error bounds (optional, for comparing another evaluation of this backward with it). For an evaluation that
  *   (i)  reads pre-write rows P and read rows M[R_j] within eps_row * (that row's largest magnitude) of these, plus
@@ -450,6 +453,7 @@ int oracle_write_read(int B, int T, int H, int F, const int* widths, int dk, int
 /* Parameters of the error bounds: u, eps_row, eps_w, q_rel (see above). */
 typedef struct {
   double u, eps_row, eps_w, q_rel, q_grp;
+  double g_rel;  /* with a bfloat16-accumulated bank gradient: an update's rounding falling the other way */
 } bound_par_t;
 
 /* Largest magnitude of the 16-column snapshot group of row element c (d % 16 == 0 where it is used). */
@@ -464,6 +468,7 @@ static inline double gam(double n, double u) { return n * u / (1.0 - n * u); }
 
 typedef struct {
   int B, T, H, F, dk, d, W, R, bank_bf16, exact, snap_bf16; /* snap_bf16: the snapshot mode (0, 1 bf16, 2 fp8, 3 int4) */
+  int gacc_bf16;  /* the bank gradient accumulated in bfloat16: every update of G rounded to bfloat16 */
   const int* widths;
   const float *wkeys, *rq, *values, *alpha, *beta, *sub, *bank, *dout, *dbank;
   int64_t bank_rows, sumn;
@@ -671,8 +676,12 @@ static void* bwd_worker(void* arg) {
             EGr[c] += go * bp->eps_w * rt[i] + gam(2, u) * (fabs(Gr[c]) + rt[i] * go); /* G += rho dout */
           }
           Edw[i] = e + gam(d, u) * m;
+          if (j->gacc_bf16) /* a bfloat16 rounding of the updated entry, which may fall the other way */
+            for (int c = 0; c < d; ++c) EGr[c] += bp->g_rel * (fabs(Gr[c] + rt[i] * (double)dout[c]) + EGr[c]);
         }
         for (int c = 0; c < d; ++c) Gr[c] += rt[i] * (double)dout[c];
+        if (j->gacc_bf16)
+          for (int c = 0; c < d; ++c) Gr[c] = (double)round_to(Gr[c], 1);
       }
       for (int i = 0; i < R; ++i) sum += rt[i] * dw[i];
       for (int i = 0; i < R; ++i)
@@ -783,10 +792,14 @@ static void* bwd_worker(void* arg) {
         if (bp) {
           double* EGw = EG + (int64_t)St[i] * d;
           const double* egi = Eg + (int64_t)i * d;
-          for (int c = 0; c < d; ++c)
+          for (int c = 0; c < d; ++c) {
             EGw[c] = a * egi[c] + a * be * (wt[i] * ED[c] + fabs(D[c]) * bp->eps_w * wt[i]) +
                      gam(4, bp->u) * (a * fabs(gi[c]) + a * be * wt[i] * fabs(D[c]));
+            if (j->gacc_bf16) EGw[c] += bp->g_rel * (fabs(Gw[c]) + EGw[c]);
+          }
         }
+        if (j->gacc_bf16)
+          for (int c = 0; c < d; ++c) Gw[c] = (double)round_to(Gw[c], 1);
         later[St[i]] = 1;
       }
       sum = 0.0;
@@ -827,7 +840,7 @@ done:
  * (the gradient with respect to the bank before the call); optional out64 [B, T, H, d] and bank64 (the forward's
  * outputs in fp64, unrounded, NULL to skip). Returns 0 or -1. */
 static int backward_impl(int B, int T, int H, int F, const int* widths, int dk, int d, int W, int R, int bank_bf16,
-                         int exact, int snap_bf16, const float* wkeys, const float* rq, const float* values,
+                         int exact, int snap_bf16, int gacc_bf16, const float* wkeys, const float* rq, const float* values,
                          const float* alpha, const float* beta, const float* subkeys, const float* bank,
                          int64_t bank_rows, const float* dout, const float* dbank, double* d_wkeys, double* d_rq,
                          double* d_values, double* d_alpha, double* d_beta, double* d_subkeys, double* d_bank,
@@ -862,7 +875,7 @@ static int backward_impl(int B, int T, int H, int F, const int* widths, int dk, 
   for (int i = 0; i < nthreads; ++i) {
     bwd_job_t* j = &jobs[i];
     j->B = B; j->T = T; j->H = H; j->F = F; j->dk = dk; j->d = d; j->W = W; j->R = R;
-    j->bank_bf16 = bank_bf16; j->exact = exact; j->snap_bf16 = snap_bf16; j->widths = widths; j->wkeys = wkeys; j->rq = rq;
+    j->bank_bf16 = bank_bf16; j->exact = exact; j->snap_bf16 = snap_bf16; j->gacc_bf16 = gacc_bf16; j->widths = widths; j->wkeys = wkeys; j->rq = rq;
     j->values = values; j->alpha = alpha; j->beta = beta; j->sub = subkeys; j->bank = bank; j->dout = dout;
     j->dbank = dbank; j->bank_rows = bank_rows; j->sumn = sumn; j->d_wkeys = d_wkeys; j->d_rq = d_rq;
     j->d_values = d_values; j->d_alpha = d_alpha; j->d_beta = d_beta; j->d_sub_stream = dsub_stream;
@@ -902,15 +915,17 @@ static int backward_impl(int B, int T, int H, int F, const int* widths, int dk, 
 }
 
 int oracle_write_read_backward(int B, int T, int H, int F, const int* widths, int dk, int d, int W, int R,
-                               int bank_bf16, int exact, int snap_bf16, const float* wkeys, const float* rq,
+                               int bank_bf16, int exact, int snap_bf16, int grad_bank_bf16, const float* wkeys,
+                               const float* rq,
                                const float* values,
                                const float* alpha, const float* beta, const float* subkeys, const float* bank,
                                int64_t bank_rows, const float* dout, const float* dbank, double* d_wkeys,
                                double* d_rq, double* d_values, double* d_alpha, double* d_beta, double* d_subkeys,
                                double* d_bank, double* out64, double* bank64, int nthreads) {
-  return backward_impl(B, T, H, F, widths, dk, d, W, R, bank_bf16, exact, snap_bf16, wkeys, rq, values, alpha, beta,
-                       subkeys, bank, bank_rows, dout, dbank, d_wkeys, d_rq, d_values, d_alpha, d_beta, d_subkeys,
-                       d_bank, out64, bank64, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, nthreads);
+  return backward_impl(B, T, H, F, widths, dk, d, W, R, bank_bf16, exact, snap_bf16, grad_bank_bf16, wkeys, rq, values,
+                       alpha, beta, subkeys, bank, bank_rows, dout, dbank, d_wkeys, d_rq, d_values, d_alpha, d_beta,
+                       d_subkeys, d_bank, out64, bank64, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL,
+                       nthreads);
 }
 
 /* oracle_write_read_backward with error bounds (see the comment above bound_par_t): par = {u, eps_row, eps_w,
@@ -919,7 +934,8 @@ int oracle_write_read_backward(int B, int T, int H, int F, const int* widths, in
  * [B, H, T, W, d]) receives the pre-write rows of every write event as the backward reads them (rounded to
  * bfloat16 with snap_bf16). The gradients and the other outputs are those of oracle_write_read_backward. */
 int oracle_write_read_backward_bounds(int B, int T, int H, int F, const int* widths, int dk, int d, int W, int R,
-                                      int bank_bf16, int snap_bf16, const float* wkeys, const float* rq,
+                                      int bank_bf16, int snap_bf16, int grad_bank_bf16, const float* wkeys,
+                                      const float* rq,
                                       const float* values, const float* alpha, const float* beta,
                                       const float* subkeys, const float* bank, int64_t bank_rows, const float* dout,
                                       const float* dbank, double* d_wkeys, double* d_rq, double* d_values,
@@ -928,8 +944,9 @@ int oracle_write_read_backward_bounds(int B, int T, int H, int F, const int* wid
                                       double* e_wkeys, double* e_rq, double* e_values, double* e_alpha,
                                       double* e_beta, double* e_subkeys, double* e_bank, int nthreads) {
   if (!par || !e_wkeys || !e_rq || !e_values || !e_alpha || !e_beta || !e_subkeys || !e_bank) return -1;
-  bound_par_t bp = {par[0], par[1], par[2], par[3], par[4]};
-  return backward_impl(B, T, H, F, widths, dk, d, W, R, bank_bf16, 0, snap_bf16, wkeys, rq, values, alpha, beta,
+  bound_par_t bp = {par[0], par[1], par[2], par[3], par[4], par[5]};
+  return backward_impl(B, T, H, F, widths, dk, d, W, R, bank_bf16, 0, snap_bf16, grad_bank_bf16, wkeys, rq, values,
+                       alpha, beta,
                        subkeys, bank, bank_rows, dout, dbank, d_wkeys, d_rq, d_values, d_alpha, d_beta, d_subkeys,
                        d_bank, out64, bank64, snap_out, &bp, e_wkeys, e_rq, e_values, e_alpha, e_beta, e_subkeys,
                        e_bank, nthreads);

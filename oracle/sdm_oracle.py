@@ -67,7 +67,7 @@ def _load():
             lib.oracle_write_read_backward.restype = ctypes.c_int
             lib.oracle_write_read_backward.argtypes = [
                 ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, ctypes.c_int, ctypes.c_int,
-                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                 _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, ctypes.c_int64, _f32p, vp,
                 _f64p, _f64p, _f64p, _f64p, _f64p, _f64p, _f64p, vp, vp, ctypes.c_int]
             lib.oracle_e4m3_round.restype = ctypes.c_double
@@ -79,7 +79,7 @@ def _load():
             lib.oracle_write_read_backward_bounds.restype = ctypes.c_int
             lib.oracle_write_read_backward_bounds.argtypes = [
                 ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, ctypes.c_int, ctypes.c_int,
-                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                 _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, _f32p, ctypes.c_int64, _f32p, vp,
                 _f64p, _f64p, _f64p, _f64p, _f64p, _f64p, _f64p, vp, vp, vp, _f64p,
                 _f64p, _f64p, _f64p, _f64p, _f64p, _f64p, _f64p, ctypes.c_int]
@@ -215,7 +215,7 @@ def snap_rows(rows, snap_quant: str) -> np.ndarray:
 
 def write_read_backward(wkeys, rq, values, alpha, beta, subkeys, bank, dout, dbank, widths, num_writes, num_reads,
                         *, bank_bf16=False, exact=False, snap_bf16=False, want_forward=False,
-                        nthreads: int | None = None, snap_quant=None):
+                        nthreads: int | None = None, snap_quant=None, grad_bank_bf16=False):
     """Gradients of the write/read (the chain rule through the per-token recurrence, in reverse; sdm_oracle.c).
 
     bank is the bank before the call [B, H, bank_rows, d]; dout [B, T, H, d] and dbank (same shape as bank, or None
@@ -247,7 +247,7 @@ def write_read_backward(wkeys, rq, values, alpha, beta, subkeys, bank, dout, dba
     nt = nthreads or min(os.cpu_count() or 1, 16)
     rc = _load().oracle_write_read_backward(
         B, T, H, len(widths), widths, dk, d, W, R, int(bool(bank_bf16)), int(bool(exact)),
-        _snap_mode(snap_bf16, snap_quant),
+        _snap_mode(snap_bf16, snap_quant), int(bool(grad_bank_bf16)),
         wk, rqa, v, al, be, sub,
         M, M.shape[2], g_out, None if g_bank is None else g_bank.ctypes.data, res["d_wkeys"], res["d_rq"],
         res["d_values"], res["d_alpha"], res["d_beta"], res["d_subkeys"], res["d_bank"], fwd[0], fwd[1], nt)
@@ -262,7 +262,7 @@ U_F32 = 2.0 ** -24  # unit roundoff of float32 (round to nearest)
 def write_read_backward_bounds(wkeys, rq, values, alpha, beta, subkeys, bank, dout, dbank, widths, num_writes,
                                num_reads, *, eps_row, eps_w=2 * U_F32, u=U_F32, q_rel=0.0, q_grp=0.0,
                                bank_bf16=False, snap_bf16=False, want_snapshot=False, nthreads: int | None = None,
-                               snap_quant=None):
+                               snap_quant=None, grad_bank_bf16=False, g_rel=2.0 ** -7):
     """write_read_backward (rounded bank states, as the forward stores them) plus, for every gradient element, a
     bound on how far another evaluation of the same backward may be from it (sdm_oracle.c, the comment above
     bound_par_t): one that reads pre-write and read rows within eps_row of each row's largest magnitude (plus q_rel
@@ -288,10 +288,11 @@ def write_read_backward_bounds(wkeys, rq, values, alpha, beta, subkeys, bank, do
     for k in ("wkeys", "rq", "values", "alpha", "beta", "subkeys", "bank"):
         res["e_" + k] = z(res["d_" + k].shape)
     snap = np.empty((B, H, T, W, d), np.float32) if want_snapshot else None
-    par = np.array([u, eps_row, eps_w, q_rel, q_grp], np.float64)
+    par = np.array([u, eps_row, eps_w, q_rel, q_grp, g_rel], np.float64)
     nt = nthreads or min(os.cpu_count() or 1, 16)
     rc = _load().oracle_write_read_backward_bounds(
-        B, T, H, len(widths), widths, dk, d, W, R, int(bool(bank_bf16)), _snap_mode(snap_bf16, snap_quant), wk, rqa, v,
+        B, T, H, len(widths), widths, dk, d, W, R, int(bool(bank_bf16)), _snap_mode(snap_bf16, snap_quant),
+        int(bool(grad_bank_bf16)), wk, rqa, v,
         al, be,
         sub, M, M.shape[2], g_out, None if g_bank is None else g_bank.ctypes.data, res["d_wkeys"], res["d_rq"],
         res["d_values"], res["d_alpha"], res["d_beta"], res["d_subkeys"], res["d_bank"], res["out"].ctypes.data,

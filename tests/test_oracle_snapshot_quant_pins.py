@@ -142,3 +142,43 @@ def test_quantized_snapshot_one_token_gate_gradients_by_hand(mode):
     r = _bwd(x, dout, None, widths, 1, 1, snap_quant=mode)
     assert abs(r["d_alpha"][0, 0, 0] - (1 - be) * (g @ Pq)) <= 1e-12
     assert abs(r["d_beta"][0, 0, 0] - g @ (v - a * Pq)) <= 1e-12
+
+
+def _rbf16(x):
+    return np.array([oracle.round_bf16(float(v)) for v in np.ravel(x)]).reshape(np.shape(x))
+
+
+def test_bank_gradient_accumulated_in_bfloat16_by_hand():
+    """The pages' default bank-gradient accumulation on a bfloat16 bank (CHANGELOG 2.0.0, "Deterministic": float32
+    accumulation is the opt-in): every update of the adjoint bank is rounded to bfloat16. One token writing and reading
+    one slot (W = R = 1, weights 1): G[j] = rnd(dbank[j] + dout), then G[j] = rnd(alpha (1 - beta) G[j]); every other
+    row keeps dbank; every entry is a bfloat16 value."""
+    rng = np.random.default_rng(13)
+    widths, dk, d = (4,), 2, 8
+    q = rng.standard_normal((1, 1, 1, dk)).astype(np.float32)
+    x = {"wkeys": q, "rq": q.copy(), "values": rng.standard_normal((1, 1, 1, d)).astype(np.float32),
+         "alpha": np.array([[[0.7]]], np.float32), "beta": np.array([[[0.3]]], np.float32),
+         "subkeys": rng.standard_normal((1, 4, dk)).astype(np.float32),
+         "bank": _rbf16(rng.standard_normal((1, 1, 4, d)) / 3).astype(np.float32)}
+    dout = _rbf16(rng.standard_normal((1, 1, 1, d))).astype(np.float32)
+    dbank = _rbf16(rng.standard_normal((1, 1, 4, d))).astype(np.float32)
+    j = int(oracle.topk(q, x["subkeys"], widths, 1)[0][0, 0, 0, 0])
+    r = oracle.write_read_backward(x["wkeys"], x["rq"], x["values"], x["alpha"], x["beta"], x["subkeys"], x["bank"],
+                                   dout, dbank, widths, 1, 1, bank_bf16=True, grad_bank_bf16=True, nthreads=1)
+    a, b = float(x["alpha"][0, 0, 0]), float(x["beta"][0, 0, 0])
+    g = _rbf16(dbank[0, 0, j].astype(np.float64) + dout[0, 0, 0].astype(np.float64))
+    expect = _rbf16(a * g - a * b * 1.0 * g)
+    assert np.array_equal(r["d_bank"][0, 0, j], expect)
+    others = [i for i in range(4) if i != j]
+    assert np.array_equal(r["d_bank"][0, 0, others], dbank[0, 0, others].astype(np.float64))
+    f = oracle.write_read_backward(x["wkeys"], x["rq"], x["values"], x["alpha"], x["beta"], x["subkeys"], x["bank"],
+                                   dout, dbank, widths, 1, 1, bank_bf16=True, nthreads=1)
+    assert not np.array_equal(f["d_bank"], r["d_bank"])  # float32 (fp64 here) accumulation keeps the low bits
+
+
+def test_bank_gradient_in_bfloat16_holds_bfloat16_values():
+    x, dout, dbank = _case(5, 1, 16, 2, (4, 4), 3, 16)
+    x["bank"] = _rbf16(x["bank"]).astype(np.float32)
+    dbank = _rbf16(dbank).astype(np.float32)
+    r = _bwd(x, dout, dbank, (4, 4), 3, 2, bank_bf16=True, grad_bank_bf16=True)
+    assert np.array_equal(r["d_bank"], _rbf16(r["d_bank"]))
