@@ -42,6 +42,7 @@ class SdmConfig(ctypes.Structure):
         ("chunk_size", ctypes.c_int32), ("act_dtype", ctypes.c_int32), ("bank_dtype", ctypes.c_int32),
         ("bank_rows", ctypes.c_int64), ("bank_row_stride", ctypes.c_int64),
         ("shared_bank", ctypes.c_int32), ("snapshot_dtype", ctypes.c_int32), ("topk_scoring", ctypes.c_int32),
+        ("grad_bank_dtype", ctypes.c_int32),
     ]
 
 
@@ -51,7 +52,7 @@ class SdmLayerConfig(ctypes.Structure):
 
 def make_config(batch, tokens, heads, widths, subkey_dim, head_dim=1, num_writes=1, num_reads=1, chunk_size=1,
                 act_dtype=SDM_F32, bank_dtype=SDM_F32, bank_rows=None, bank_row_stride=0,
-                shared_bank=False, snapshot_dtype=0, topk_scoring=0) -> SdmConfig:
+                shared_bank=False, snapshot_dtype=0, topk_scoring=0, grad_bank_dtype=0) -> SdmConfig:
     c = SdmConfig()
     c.batch, c.tokens, c.heads = int(batch), int(tokens), int(heads)
     c.num_factors = len(widths)
@@ -68,6 +69,7 @@ def make_config(batch, tokens, heads, widths, subkey_dim, head_dim=1, num_writes
     c.shared_bank = 1 if shared_bank else 0
     c.snapshot_dtype = int(snapshot_dtype)
     c.topk_scoring = SCORING[topk_scoring] if isinstance(topk_scoring, str) else int(topk_scoring)
+    c.grad_bank_dtype = int(grad_bank_dtype)
     return c
 
 
@@ -424,12 +426,13 @@ def sdm_write_read_save(write_keys, read_queries, values, forget_gate, input_gat
 
 def sdm_write_read_backward(write_keys, read_queries, values, forget_gate, input_gate, subkeys, bank, snapshot,
                             grad_out, grad_bank=None, *, widths, num_writes, num_reads, chunk_size, workspace=None,
-                            snapshot_quant="none"):
+                            snapshot_quant="none", grad_bank_dtype=torch.float32):
     """Backward of sdm_write_read_save (the same snapshot_quant). bank (as the forward left it) steps back to its
     state before the forward (with a bfloat16 snapshot of a float32 bank, written rows come back rounded).
-    grad_bank: float32 with the bank's shape and row stride, the gradient w.r.t. the bank after the forward (None:
-    zeros), replaced in place by the gradient w.r.t. the bank before it. Returns a dict of float32 gradients:
-    write_keys, read_queries, values, forget_gate, input_gate, subkeys, bank."""
+    grad_bank: float32, or bfloat16 on a bfloat16 bank (every update rounded), with the bank's shape and row stride,
+    the gradient w.r.t. the bank after the forward (None: zeros of grad_bank_dtype), replaced in place by the
+    gradient w.r.t. the bank before it. Returns a dict of gradients: write_keys, read_queries, values, forget_gate,
+    input_gate, subkeys (float32) and bank (grad_bank)."""
     B, T, H, Fdk = write_keys.shape
     F = len(widths)
     dk = Fdk // F
@@ -446,12 +449,12 @@ def sdm_write_read_backward(write_keys, read_queries, values, forget_gate, input
     scode, sdt = _snapshot_dtype(snapshot_quant, bank)
     dev = bank.device
     if grad_bank is None:
-        grad_bank = torch.zeros((B, H, bank.shape[2], ld), dtype=torch.float32, device=dev)[..., :d]
-    if grad_bank.dtype != torch.float32 or tuple(grad_bank.shape) != tuple(bank.shape) or \
+        grad_bank = torch.zeros((B, H, bank.shape[2], ld), dtype=grad_bank_dtype, device=dev)[..., :d]
+    if grad_bank.dtype not in (torch.float32, torch.bfloat16) or tuple(grad_bank.shape) != tuple(bank.shape) or \
             grad_bank.stride() != bank.stride():
-        raise ValueError("grad_bank must be float32 with the bank's shape and strides")
+        raise ValueError("grad_bank must be float32 or bfloat16 with the bank's shape and strides")
     cfg = make_config(B, T, H, widths, dk, d, num_writes, num_reads, chunk_size, _dt(write_keys), _dt(bank),
-                      bank.shape[2], ld, snapshot_dtype=scode)
+                      bank.shape[2], ld, snapshot_dtype=scode, grad_bank_dtype=_dt(grad_bank))
     _need(snapshot, "snapshot", _snapshot_shape(cfg, scode, B, H, T, num_writes, d), sdt)
     ws = _workspace(workspace_size(cfg, SDM_OP_BACKWARD), dev, workspace)
     f32 = torch.float32
@@ -544,18 +547,19 @@ def sdm_decode_steps(write_keys, read_queries, values, forget_gate, input_gate, 
 
 
 def sdm_bank_grad_sum(grad_bank, *, heads, widths, head_dim, out=None):
-    """Gradient of a learned initial bank copied into every batch row: grad_bank [B, H, bank_rows, d] float32 (rows
-    possibly padded) summed over the batch in order into [H, bank_rows, d] (the same row stride; rows >= N and the
-    padding are left as `out` had them, zeros when out is None)."""
+    """Gradient of a learned initial bank copied into every batch row: grad_bank [B, H, bank_rows, d] float32 or
+    bfloat16 (rows possibly padded) summed over the batch in order, in float32, into [H, bank_rows, d] float32 (the
+    same row stride in elements; rows >= N and the padding are left as `out` had them, zeros when out is None)."""
     B, H, rows, d = grad_bank.shape
     ld = _bank_ld(grad_bank, "grad_bank")
-    if grad_bank.dtype != torch.float32:
-        raise ValueError("grad_bank must be float32")
+    if grad_bank.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("grad_bank must be float32 or bfloat16")
     if out is None:
         out = torch.zeros((H, rows, ld), dtype=torch.float32, device=grad_bank.device)[..., :d]
     if tuple(out.shape) != (H, rows, d) or _bank_ld(out.unsqueeze(0), "out") != ld:
         raise ValueError("out must be [heads, bank_rows, d] float32 with grad_bank's row stride")
-    cfg = make_config(B, 1, H, widths, 1, d, 1, 1, 1, SDM_F32, SDM_F32, rows, ld)
+    gdt = _dt(grad_bank)
+    cfg = make_config(B, 1, H, widths, 1, d, 1, 1, 1, SDM_F32, gdt, rows, ld, grad_bank_dtype=gdt)
     _check(load().sdm_bank_grad_sum(ctypes.byref(cfg), _ptr(grad_bank), _ptr(out), _stream(grad_bank.device)))
     return out
 

@@ -382,6 +382,23 @@ sdm_status snapshot_kind(const sdm_config* cfg, const Dims& D, int* mode) {
   return SDM_OK;
 }
 
+// The bank gradient's element (cfg.grad_bank_dtype): float32 (0), or bfloat16 (SDM_BF16: a bfloat16 bank; in the
+// backward, the fast reverse sweep's shapes only).
+sdm_status grad_bank_kind(const sdm_config* cfg, const Dims& D, bool backward, bool* bf16) {
+  const int g = cfg->grad_bank_dtype;
+  if (g != SDM_F32 && g != SDM_BF16)
+    return fail(SDM_ERR_DTYPE, "grad_bank_dtype = %d (0: float32, SDM_BF16: the bank dtype of a bfloat16 bank)", g);
+  *bf16 = g == SDM_BF16;
+  if (!*bf16) return SDM_OK;
+  if (D.bank != SDM_BF16)
+    return fail(SDM_ERR_RANGE, "a bfloat16 bank gradient is the bank dtype of a bfloat16 bank; a float32 bank's "
+                "gradient is float32 (grad_bank_dtype 0)");
+  if (backward && !bwd_fast(D))
+    return fail(SDM_ERR_RANGE, "no native route for a bfloat16 bank gradient with num_writes %d, num_reads %d (at "
+                "most 128 each): use grad_bank_dtype 0", D.W, D.R);
+  return SDM_OK;
+}
+
 // Bytes of the backward snapshot of mode `mode` (snapshot_kind) for D.
 size_t snapshot_bytes(const Dims& D, int mode) {
   const size_t rows = (size_t)D.S * D.T * D.W;
@@ -588,7 +605,7 @@ sdm_status sdm_write_read_save(const sdm_config* cfg, const void* write_keys, co
 sdm_status sdm_write_read_backward(const sdm_config* cfg, const void* write_keys, const void* read_queries,
                                    const void* values, const void* forget_gate, const void* input_gate,
                                    const void* subkeys, void* bank, const void* snapshot, const void* grad_out,
-                                   float* grad_bank, float* grad_write_keys, float* grad_read_queries,
+                                   void* grad_bank, float* grad_write_keys, float* grad_read_queries,
                                    float* grad_values, float* grad_forget_gate, float* grad_input_gate,
                                    float* grad_subkeys, void* workspace, size_t workspace_bytes, void* stream) {
   Dims D;
@@ -596,6 +613,8 @@ sdm_status sdm_write_read_backward(const sdm_config* cfg, const void* write_keys
   TRY(validate(cfg, SDM_OP_BACKWARD, 0, &D, &pw, &pr));
   int snap_mode = SNAP_BANK;
   TRY(snapshot_kind(cfg, D, &snap_mode));
+  bool gb16 = false;
+  TRY(grad_bank_kind(cfg, D, true, &gb16));
   const long long rows = (long long)D.B * D.T * D.H;
   long long sumn = 0;
   for (int f = 0; f < D.F; ++f) sumn += D.widths[f];
@@ -626,7 +645,7 @@ sdm_status sdm_write_read_backward(const sdm_config* cfg, const void* write_keys
                        {snapshot, snapshot_bytes(D, snap_mode), "snapshot"},
                        {grad_out, (size_t)rows * D.d * ea, "grad_out"}};
   const Range outs[] = {{bank, nbank * eb, "bank"},
-                        {grad_bank, nbank * 4, "grad_bank"},
+                        {grad_bank, nbank * (gb16 ? 2 : 4), "grad_bank"},
                         {grad_write_keys, qb * 4, "grad_write_keys"},
                         {grad_read_queries, qb * 4, "grad_read_queries"},
                         {grad_values, (size_t)rows * D.d * 4, "grad_values"},
@@ -675,6 +694,7 @@ sdm_status sdm_write_read_backward(const sdm_config* cfg, const void* write_keys
   ba.snap = snapshot;
   ba.snap_mode = snap_mode;
   ba.gbank = grad_bank;
+  ba.grad_bf16 = gb16 ? 1 : 0;
   ba.gwkeys = grad_write_keys;
   ba.grq = grad_read_queries;
   ba.gvalues = grad_values;
@@ -1067,11 +1087,13 @@ sdm_status sdm_snapshot_bytes(const sdm_config* cfg, size_t* bytes) {
   return ok();
 }
 
-sdm_status sdm_bank_grad_sum(const sdm_config* cfg, const float* grad_bank, float* grad_initial_bank,
+sdm_status sdm_bank_grad_sum(const sdm_config* cfg, const void* grad_bank, float* grad_initial_bank,
                              void* stream) {
   Dims D;
   TopkPlan pw, pr;
   TRY(validate(cfg, SDM_OP_WRITE_READ, 0, &D, &pw, &pr));
+  bool gb16 = false;
+  TRY(grad_bank_kind(cfg, D, false, &gb16));
   if (D.shared) return fail(SDM_ERR_RANGE, "sdm_bank_grad_sum takes per-stream bank gradients (shared_bank = 0)");
   if (D.S > 0) {
     TRY(need(grad_bank, "grad_bank"));
@@ -1082,12 +1104,12 @@ sdm_status sdm_bank_grad_sum(const sdm_config* cfg, const float* grad_bank, floa
   if ((D.ld * 4) % 16 != 0 || D.d % 4 != 0)
     return fail(SDM_ERR_LAYOUT, "the bank gradient's rows must be 16-byte multiples (head_dim and row stride)");
   const size_t row_bytes = (size_t)D.rows * (size_t)D.ld * 4;
-  const Range ins[] = {{grad_bank, (size_t)D.S * row_bytes, "grad_bank"}};
+  const Range ins[] = {{grad_bank, (size_t)D.S * row_bytes / (gb16 ? 2 : 1), "grad_bank"}};
   const Range outs[] = {{grad_initial_bank, (size_t)D.H * row_bytes, "grad_initial_bank"}};
   TRY(check_alias(outs, 1, ins, 1));
   TRY(check_device());
   if (D.S == 0) return ok();
-  TRY(hip_status(launch_bank_grad_sum(grad_bank, grad_initial_bank, D.B, D.H, D.N, D.rows, D.d, D.ld,
+  TRY(hip_status(launch_bank_grad_sum(grad_bank, gb16, grad_initial_bank, D.B, D.H, D.N, D.rows, D.d, D.ld,
                                       (hipStream_t)stream),
                  "bank gradient sum launch"));
   return ok();

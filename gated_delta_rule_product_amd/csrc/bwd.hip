@@ -116,7 +116,7 @@ __global__ __launch_bounds__(BWD_NT) void bwd_sweep_kernel(Dims D, BwdArgs a, in
   const bool valid = col < d;  // d % 4 == 0: a lane's four columns are all inside or all outside
   const int P = W + R + 2;
   Bk* bank = (Bk*)a.bank + (long long)st * D.rows * D.ld;
-  float* gbank = a.gbank + (long long)st * D.rows * D.ld;
+  float* gbank = (float*)a.gbank + (long long)st * D.rows * D.ld;
   const Bk* snap = (const Bk*)a.snap + (long long)st * T * W * d;
   const A* gout = (const A*)a.gout;
   const A* values = (const A*)a.values;
@@ -303,7 +303,28 @@ template <int SQ> struct SnapQ {  // the raw snapshot piece of a lane: x = eleme
   }
 };
 
-template <typename A, typename Bk, int LPG, typename Sk = Bk, int SQ = SNAP_BANK>
+// Four consecutive entries of the adjoint bank (the bank gradient): float32, or bfloat16 (the bank dtype of a
+// bfloat16 bank, CHANGELOG 2.0.0 "Deterministic": float32 accumulation is the opt-in), rounded at every store.
+template <typename Gk> struct GRow;
+template <> struct GRow<float> {
+  __device__ static float4 load(const float* p) { return *(const float4*)p; }
+  __device__ static void store(float* p, float4 v) { *(float4*)p = v; }
+  __device__ static float round(float v) { return v; }
+};
+template <> struct GRow<bf16_t> {
+  __device__ static float4 load(const bf16_t* p) {
+    const u32x2_t w = *(const u32x2_t*)p;
+    return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u), __uint_as_float(w.y << 16),
+                       __uint_as_float(w.y & 0xFFFF0000u));
+  }
+  __device__ static void store(bf16_t* p, float4 v) {
+    *(u32x2_t*)p = u32x2_t{(uint32_t)f_to_bf16(v.x) | ((uint32_t)f_to_bf16(v.y) << 16),
+                           (uint32_t)f_to_bf16(v.z) | ((uint32_t)f_to_bf16(v.w) << 16)};
+  }
+  __device__ static float round(float v) { return bank_round<bf16_t>(v); }
+};
+
+template <typename A, typename Bk, int LPG, typename Sk = Bk, int SQ = SNAP_BANK, typename Gk = float>
 __global__ __launch_bounds__(128 * LPG) void bwd_sweep_fast_kernel(Dims D, BwdArgs a, int nsl) {
   constexpr int COLS = 4 * LPG, NW = 2 * LPG;
   constexpr bool QS = SQ == SNAP_FP8 || SQ == SNAP_INT4;
@@ -326,7 +347,7 @@ __global__ __launch_bounds__(128 * LPG) void bwd_sweep_fast_kernel(Dims D, BwdAr
   const int jr = min(grp, R - 1), jw = min(grp, W - 1);  // clamped term indices: every lane loads in range
   const int P = W + R + 2;
   Bk* bank = (Bk*)a.bank + (long long)st * D.rows * D.ld;
-  float* gbank = a.gbank + (long long)st * D.rows * D.ld;
+  Gk* gbank = (Gk*)a.gbank + (long long)st * D.rows * D.ld;
   const Sk* snap = (const Sk*)a.snap + (long long)st * T * W * d;
   // quantized snapshot: the elements of every stream, then the scale bytes of every stream
   const unsigned long long qrows = (unsigned long long)T * W;
@@ -384,8 +405,8 @@ __global__ __launch_bounds__(128 * LPG) void bwd_sweep_fast_kernel(Dims D, BwdAr
     float* part = a.part + ((long long)slice * D.S * T + so) * P;
     // this token's rows (clamped ids: in range on every lane)
     const RawT rb = Raw4<Bk>::load(bank + (long long)rs * D.ld + dcol);
-    float4 rg = *(const float4*)(gbank + (long long)rs * D.ld + dcol);
-    const float4 wg = *(const float4*)(gbank + (long long)ws * D.ld + dcol);
+    float4 rg = GRow<Gk>::load(gbank + (long long)rs * D.ld + dcol);
+    const float4 wg = GRow<Gk>::load(gbank + (long long)ws * D.ld + dcol);
     // ahead: token t - 1's inputs and snapshot rows, token t - 2's ids (token indices clamped at 0)
     uint32_t n_al, n_be;
     ARaw n_v, n_dout;
@@ -405,7 +426,8 @@ __global__ __launch_bounds__(128 * LPG) void bwd_sweep_fast_kernel(Dims D, BwdAr
     const float rdot = sum_group_lanes<LPG>(((dout[0] * m[0] + dout[1] * m[1]) + dout[2] * m[2]) + dout[3] * m[3]);
     rg.x += rho * dout[0]; rg.y += rho * dout[1]; rg.z += rho * dout[2]; rg.w += rho * dout[3];
     // the write: g_i (plus this token's read update of the same slot), P_i
-    float g[4] = {wg.x + mr * dout[0], wg.y + mr * dout[1], wg.z + mr * dout[2], wg.w + mr * dout[3]}, pp[4];
+    float g[4] = {GRow<Gk>::round(wg.x + mr * dout[0]), GRow<Gk>::round(wg.y + mr * dout[1]),
+                  GRow<Gk>::round(wg.z + mr * dout[2]), GRow<Gk>::round(wg.w + mr * dout[3])}, pp[4];
     if constexpr (QS)
       SnapQ<SQ>::unpack(c_sp, pp);
     else
@@ -466,7 +488,7 @@ __global__ __launch_bounds__(128 * LPG) void bwd_sweep_fast_kernel(Dims D, BwdAr
     // the read's stores (its G row only if the token does not also write the slot)
     if (hasR) {
       if (q == 0) part[W + grp] = rdot;
-      if (valid && mw == 0.f) *(float4*)(gbank + (long long)rs * D.ld + col) = rg;
+      if (valid && mw == 0.f) GRow<Gk>::store(gbank + (long long)rs * D.ld + col, rg);
     }
     // d w partials, G[S_i] <- alpha g_i - alpha beta w_i D, M[S_i] <- P_i
     if (hasW) {
@@ -476,8 +498,8 @@ __global__ __launch_bounds__(128 * LPG) void bwd_sweep_fast_kernel(Dims D, BwdAr
       if (q == 0) part[grp] = gd - ab * Dp;
       if (valid) {
         const float cw = ab * w;
-        *(float4*)(gbank + (long long)ws * D.ld + col) = make_float4(
-            al * g[0] - cw * Dl[0], al * g[1] - cw * Dl[1], al * g[2] - cw * Dl[2], al * g[3] - cw * Dl[3]);
+        GRow<Gk>::store(gbank + (long long)ws * D.ld + col, make_float4(
+            al * g[0] - cw * Dl[0], al * g[1] - cw * Dl[1], al * g[2] - cw * Dl[2], al * g[3] - cw * Dl[3]));
         if constexpr (std::is_same<Sk, Bk>::value && !QS)
           Raw4<Bk>::store(bank + (long long)ws * D.ld + col, c_sp);
         else  // a float32 bank from bfloat16 or quantized snapshot rows (pp: the widened values)
@@ -630,10 +652,19 @@ static hipError_t launch_bwd_t(const Dims& D, const BwdArgs& a, hipStream_t st) 
     auto fast = [&](auto sk, auto sq) {  // sk: a value of the snapshot's element type; sq: its mode
       using Sk = decltype(sk);
       constexpr int SQ = decltype(sq)::value;
-      if (bwd_cols(D) == 8)
-        hipLaunchKernelGGL((bwd_sweep_fast_kernel<A, Bk, 2, Sk, SQ>), grid, dim3(256), 0, st, D, a, nsl);
-      else
-        hipLaunchKernelGGL((bwd_sweep_fast_kernel<A, Bk, 4, Sk, SQ>), grid, dim3(512), 0, st, D, a, nsl);
+      auto go = [&](auto gk) {  // gk: a value of the bank gradient's element type
+        using Gk = decltype(gk);
+        if (bwd_cols(D) == 8)
+          hipLaunchKernelGGL((bwd_sweep_fast_kernel<A, Bk, 2, Sk, SQ, Gk>), grid, dim3(256), 0, st, D, a, nsl);
+        else
+          hipLaunchKernelGGL((bwd_sweep_fast_kernel<A, Bk, 4, Sk, SQ, Gk>), grid, dim3(512), 0, st, D, a, nsl);
+      };
+      if constexpr (std::is_same<Bk, bf16_t>::value && SQ == SNAP_BANK)
+        if (a.grad_bf16) {
+          go(bf16_t{});
+          return;
+        }
+      go(float{});
     };
     if (std::is_same<Bk, float>::value && a.snap_mode == SNAP_BF16)
       fast(bf16_t{}, std::integral_constant<int, SNAP_BANK>{});  // bfloat16 snapshot rows of a float32 bank

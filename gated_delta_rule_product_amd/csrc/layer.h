@@ -28,8 +28,9 @@ hipError_t launch_gates(const bf16_t* ga, const bf16_t* gb, int ldg, const float
 // ld elements apart in both; esize 2 or 4 bytes; d * esize a multiple of 16).
 hipError_t launch_bank_broadcast(const void* init, void* bank, int B, int H, long long N, long long rows, int d,
                                  long long ld, int esize, hipStream_t st);
-// grad_init[h, j, c] = sum over b = 0, 1, ... B-1 (in that order, float32) of grad_bank[b, h, j, c], j < N, c < d.
-hipError_t launch_bank_grad_sum(const float* grad_bank, float* grad_init, int B, int H, long long N, long long rows,
-                                int d, long long ld, hipStream_t st);
+// grad_init[h, j, c] = sum over b = 0, 1, ... B-1 (in that order, float32) of grad_bank[b, h, j, c], j < N, c < d
+// (grad_bank float32, or bfloat16 with bf16; d a multiple of 4).
+hipError_t launch_bank_grad_sum(const void* grad_bank, bool bf16, float* grad_init, int B, int H, long long N,
+                                long long rows, int d, long long ld, hipStream_t st);
 
 }  // namespace sdm

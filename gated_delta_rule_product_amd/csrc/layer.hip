@@ -242,27 +242,41 @@ hipError_t launch_bank_broadcast(const void* init, void* bank, int B, int H, lon
 }
 
 // One thread per 4 columns of a slot row of one head, the batch rows added in order.
-__global__ __launch_bounds__(256) void bank_grad_sum_kernel(const float* gb, float* gi, int B, int H, long long N,
+// Four consecutive float32 or bfloat16 gradient entries, widened.
+__device__ inline float4 load4(const float* p) { return *(const float4*)p; }
+__device__ inline float4 load4(const bf16_t* p) {
+  const uint2 w = *(const uint2*)p;
+  return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u), __uint_as_float(w.y << 16),
+                     __uint_as_float(w.y & 0xFFFF0000u));
+}
+
+template <typename G>
+__global__ __launch_bounds__(256) void bank_grad_sum_kernel(const G* gb, float* gi, int B, int H, long long N,
                                                             long long rows, long long quads, long long ld) {
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;  // (h, j, quad)
   if (i >= (long long)H * N * quads) return;
   const long long hq = i / quads, q = i - hq * quads;
   const long long h = hq / N, j = hq - h * N;
-  float4 acc = *(const float4*)(gb + (h * rows + j) * ld + 4 * q);
+  float4 acc = load4(gb + (h * rows + j) * ld + 4 * q);
   for (int b = 1; b < B; ++b) {
-    const float4 v = *(const float4*)(gb + (((long long)b * H + h) * rows + j) * ld + 4 * q);
+    const float4 v = load4(gb + (((long long)b * H + h) * rows + j) * ld + 4 * q);
     acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
   }
   *(float4*)(gi + (h * rows + j) * ld + 4 * q) = acc;
 }
 
-hipError_t launch_bank_grad_sum(const float* grad_bank, float* grad_init, int B, int H, long long N, long long rows,
-                                int d, long long ld, hipStream_t st) {
+hipError_t launch_bank_grad_sum(const void* grad_bank, bool bf16, float* grad_init, int B, int H, long long N,
+                                long long rows, int d, long long ld, hipStream_t st) {
   const long long quads = d / 4;
   const long long n = (long long)H * N * quads;
   if (n == 0 || B == 0) return hipSuccess;
-  hipLaunchKernelGGL(bank_grad_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, grad_bank, grad_init,
-                     B, H, N, rows, quads, ld);
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (bf16)
+    hipLaunchKernelGGL(bank_grad_sum_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)grad_bank, grad_init, B,
+                       H, N, rows, quads, ld);
+  else
+    hipLaunchKernelGGL(bank_grad_sum_kernel<float>, grid, dim3(256), 0, st, (const float*)grad_bank, grad_init, B, H,
+                       N, rows, quads, ld);
   return hipGetLastError();
 }
 

@@ -340,7 +340,9 @@ struct BwdArgs {
   void* bank;             // [S][rows][ld] bank dtype: after the forward on entry, before it on return
   const void* snap;       // [S][T][W][d] bank dtype, or the snapshot of snap_mode
   int snap_mode;          // SNAP_*: the snapshot's rows as stored (a float32 bank restored from them for 1-3)
-  float* gbank;           // [S][rows][ld]: gradient w.r.t. the bank after the call in, before the call out
+  void* gbank;            // [S][rows][ld]: gradient w.r.t. the bank after the call in, before the call out (float32,
+                          // or bfloat16 with grad_bf16)
+  int grad_bf16;          // the bank gradient kept in bfloat16 (a bfloat16 bank; the fast reverse sweep only)
   float* gwkeys; float* grq; float* gvalues; float* galpha; float* gbeta; float* gsub;
   float* part; float* ds; float* sgpart;  // workspace
   float* mrho;            // workspace [S][T][W]: rho of the read term of the same token and slot as write term i, or 0

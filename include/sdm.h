@@ -115,6 +115,11 @@ typedef struct {
                                SDM_SCORING_DIRECT = the fp64 chain everywhere; SDM_SCORING_FILTERED = the filter
                                wherever it applies (bf16 activations, factor widths multiples of 16, subkey_dim a
                                multiple of 32 up to 128, 16-byte aligned queries; not the decode step's top-k) */
+  int32_t grad_bank_dtype;  /* read by sdm_write_read_backward and sdm_bank_grad_sum only: the element type of
+                               grad_bank. 0 (SDM_F32) = float32 accumulation (CHANGELOG 2.0.0 "Deterministic": the
+                               grad_bank_fp32 opt-in); SDM_BF16 = the bank dtype of a bfloat16 bank (that page's
+                               default), every update of the adjoint bank rounded to bfloat16 (bfloat16 banks with
+                               num_writes, num_reads <= 128 only, else SDM_ERR_RANGE before any work) */
 } sdm_config;
 
 enum { SDM_SCORING_AUTO = 0, SDM_SCORING_DIRECT = 1, SDM_SCORING_FILTERED = 2 };
@@ -185,9 +190,10 @@ sdm_status sdm_snapshot_bytes(const sdm_config* cfg, size_t* bytes);
  * On return `bank` is the bank before the forward, bit for bit; with a bfloat16 snapshot of a float32 bank, the rows
  * the forward wrote come back rounded to bfloat16 (restored from the snapshot), and every row the backward reads
  * from the snapshot or the restored bank is the rounded one (it enters the key, query, gate and sub-key gradients,
- * not grad_values or grad_bank). grad_bank (float32, [B, H, bank_rows, bank_row_stride], the bank's row
- * layout) holds the gradient w.r.t. the bank after the forward on entry (zeros if none) and the gradient w.r.t. the
- * bank before it on return. Written (float32, overwritten): grad_write_keys, grad_read_queries [B, T, H, F*dk],
+ * not grad_values or grad_bank). grad_bank ([B, H, bank_rows, bank_row_stride], the bank's row layout; float32, or
+ * bfloat16 with cfg.grad_bank_dtype = SDM_BF16) holds the gradient w.r.t. the bank after the forward on entry (zeros
+ * if none) and the gradient w.r.t. the bank before it on return; in bfloat16 every token's update of a row (its read,
+ * then its write) is rounded to nearest even as it is stored. Written (float32, overwritten): grad_write_keys, grad_read_queries [B, T, H, F*dk],
  * grad_values [B, T, H, d], grad_forget_gate, grad_input_gate [B, T, H], grad_subkeys [H, sum n_f, dk] (summed over
  * the batch). The selection itself has no gradient; the gradient reaches keys, queries and sub-keys through the
  * softmax weights of the selected slots, whose scores are sums of factor scores. Workspace: SDM_OP_BACKWARD. The
@@ -195,7 +201,7 @@ sdm_status sdm_snapshot_bytes(const sdm_config* cfg, size_t* bytes);
 sdm_status sdm_write_read_backward(const sdm_config* cfg, const void* write_keys, const void* read_queries,
                                    const void* values, const void* forget_gate, const void* input_gate,
                                    const void* subkeys, void* bank, const void* snapshot, const void* grad_out,
-                                   float* grad_bank, float* grad_write_keys, float* grad_read_queries,
+                                   void* grad_bank, float* grad_write_keys, float* grad_read_queries,
                                    float* grad_values, float* grad_forget_gate, float* grad_input_gate,
                                    float* grad_subkeys, void* workspace, size_t workspace_bytes, void* stream);
 
@@ -290,9 +296,10 @@ sdm_status sdm_layer_forward(const sdm_layer_config* cfg, const void* x, const v
 /* Gradient of a learned initial bank copied into every batch row (sdm_layer_forward's initial_bank): grad_initial_bank
  * [H, bank_rows, bank_row_stride] float32 receives, for every head h, slot j < N and column c < head_dim, the sum over
  * b = 0, 1, ..., B - 1 (in that order, float32) of grad_bank[b, h, j, c] (grad_bank: sdm_write_read_backward's
- * gradient with respect to the bank before the call, [B, H, bank_rows, bank_row_stride] float32). Rows >= N and
- * padding columns are not written. cfg: the write/read's (per-stream banks). */
-sdm_status sdm_bank_grad_sum(const sdm_config* cfg, const float* grad_bank, float* grad_initial_bank, void* stream);
+ * gradient with respect to the bank before the call, [B, H, bank_rows, bank_row_stride], float32 or, with
+ * cfg.grad_bank_dtype = SDM_BF16, bfloat16). Rows >= N and padding columns are not written. cfg: the write/read's
+ * (per-stream banks). */
+sdm_status sdm_bank_grad_sum(const sdm_config* cfg, const void* grad_bank, float* grad_initial_bank, void* stream);
 
 /* Kernel timing (diagnostics, not part of the method). While enabled, every kernel launch of this library is
  * bracketed by a pair of HIP events recorded on the call's stream. sdm_profile_read waits for the recorded events

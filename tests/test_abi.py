@@ -320,6 +320,45 @@ def test_snapshot_dtype_settings_and_refusals(lib):
 
 
 @fake_pointers
+def test_grad_bank_dtype_settings_and_refusals(lib):
+    """grad_bank_dtype: 0 (float32) or SDM_BF16, the latter only on a bfloat16 bank and, in the backward, within the
+    fast reverse sweep (num_writes, num_reads <= 128); refusals come before any device work. A bfloat16 gradient is
+    half the bytes: an output that overlaps it only past that size is not an alias."""
+    n = ctypes.c_size_t(0)
+    base, step = 1 << 40, 1 << 36
+    g = [_fake(base + i * step) for i in range(16)]
+    ws = _fake(base + 40 * step)
+
+    def bwd(cfg, ptrs=g):
+        assert lib.sdm_workspace_size(ctypes.byref(cfg), B.SDM_OP_BACKWARD, 0, ctypes.byref(n)) == B.SDM_OK
+        return lib.sdm_write_read_backward(ctypes.byref(cfg), *ptrs, ws, n.value, None)
+
+    bf = dict(act_dtype=B.SDM_BF16, bank_dtype=B.SDM_BF16)
+    assert bwd(_cfg(grad_bank_dtype=5, **bf)) == B.SDM_ERR_DTYPE
+    assert bwd(_cfg(grad_bank_dtype=B.SDM_BF16)) == B.SDM_ERR_RANGE  # float32 bank
+    assert "float32 bank" in B.last_error()
+    wide = _cfg(grad_bank_dtype=B.SDM_BF16, num_writes=160, num_reads=16, chunk_size=8, **bf)
+    assert bwd(wide) == B.SDM_ERR_RANGE and "no native route" in B.last_error()
+    # aliasing is sized by the gradient's element: grad_write_keys placed right after a bfloat16 grad_bank
+    cfg = _cfg(grad_bank_dtype=B.SDM_BF16, **bf)
+    nbank = cfg.batch * cfg.heads * cfg.bank_rows * cfg.head_dim
+    q = list(g)
+    q[10] = _fake(base + 9 * step + 2 * nbank)  # starts where the bfloat16 gradient ends
+    st = bwd(cfg, q)
+    assert st != B.SDM_ERR_ALIAS and st in (B.SDM_ERR_DEVICE, B.SDM_ERR_HIP), B.last_error()
+    q[10] = _fake(base + 9 * step + 2 * nbank - 16)  # one lane inside it
+    assert bwd(cfg, q) == B.SDM_ERR_ALIAS
+    f32 = _cfg(**bf)
+    q[10] = _fake(base + 9 * step + 2 * nbank)  # inside a float32 gradient of the same shape
+    assert bwd(f32, q) == B.SDM_ERR_ALIAS
+    # the batch sum reads the same field
+    gs = _cfg(grad_bank_dtype=B.SDM_BF16)
+    assert lib.sdm_bank_grad_sum(ctypes.byref(gs), g[0], g[1], None) == B.SDM_ERR_RANGE
+    gs = _cfg(grad_bank_dtype=7, **bf)
+    assert lib.sdm_bank_grad_sum(ctypes.byref(gs), g[0], g[1], None) == B.SDM_ERR_DTYPE
+
+
+@fake_pointers
 def test_decode_noalloc_refuses_before_device_work(lib):
     """sdm_decode_step_noalloc: the decode step's host checks, and a step whose workspace exceeds the per-GPU
     scratch (SDM_NOALLOC_SCRATCH_BYTES) refused with SDM_ERR_RANGE, all before any device work."""

@@ -66,7 +66,7 @@ def _upstream(s, seed, with_bank_grad):
     return dout, dbank
 
 
-def run_gpu(s, x, dout, dbank, pitch=None):
+def run_gpu(s, x, dout, dbank, pitch=None, gdt=torch.float32):
     at, bt = TORCH_DT[s.act], TORCH_DT[s.bank]
     t = {k: to_dev(x[k], at) for k in ("wkeys", "rq", "values", "alpha", "beta", "subkeys")}
     if pitch is None:
@@ -84,10 +84,11 @@ def run_gpu(s, x, dout, dbank, pitch=None):
     gbank = None
     if dbank is not None:
         ld = bank.stride(2)
-        gbank = torch.zeros((s.batch, s.heads, s.rows, ld), dtype=torch.float32, device=DEV)[..., :s.head_dim]
+        gbank = torch.zeros((s.batch, s.heads, s.rows, ld), dtype=gdt, device=DEV)[..., :s.head_dim]
         gbank.copy_(to_dev(dbank, torch.float32))
     g = binding.sdm_write_read_backward(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"], t["subkeys"], bank,
-                                        snap, to_dev(dout, at), gbank, **kw)
+                                        snap, to_dev(dout, at), gbank, grad_bank_dtype=gdt, **kw)
+    assert g["bank"].dtype == gdt
     torch.cuda.synchronize()
     assert torch.equal(bank, bank0), "the backward did not restore the bank bit for bit"
     # the first token's snapshot rows are initial bank rows
@@ -95,16 +96,17 @@ def run_gpu(s, x, dout, dbank, pitch=None):
     first = torch.stack([torch.stack([bank0[b, h, w0[b, h]] for h in range(s.heads)]) for b in range(s.batch)])
     assert torch.equal(snap[:, :, 0], first)
     fwd["out"] = out.float().cpu().numpy()
-    return {k: v.cpu().numpy() for k, v in g.items()}, fwd
+    return {k: v.float().cpu().numpy() for k, v in g.items()}, fwd
 
 
-def run_oracle(s, x, dout, dbank, snap_bf16=False):
+def run_oracle(s, x, dout, dbank, snap_bf16=False, grad_bank_bf16=False):
     """The oracle's backward with its error bounds for a float32 evaluation reading rows within the forward's
     tolerance (EPS_ROW of the bank dtype; plus one bfloat16 spacing per element with a bfloat16 snapshot)."""
     return oracle.write_read_backward_bounds(x["wkeys"], x["rq"], x["values"], x["alpha"], x["beta"], x["subkeys"],
                                              x["bank"], dout, dbank, s.widths, s.num_writes, s.num_reads,
                                              eps_row=EPS_ROW[s.bank], q_rel=Q_BF16 if snap_bf16 else 0.0,
-                                             bank_bf16=s.bank == "bf16", snap_bf16=snap_bf16, want_snapshot=True)
+                                             bank_bf16=s.bank == "bf16", snap_bf16=snap_bf16, want_snapshot=True,
+                                             grad_bank_bf16=grad_bank_bf16, g_rel=Q_BF16)
 
 
 
@@ -156,6 +158,57 @@ def test_backward_matches_oracle(name, s, bank_grad):
     print(f"backward {name}: {s}", flush=True)
     got, fwd = run_gpu(s, x, dout, dbank)
     check(s, got, run_oracle(s, x, dout, dbank), fwd)
+
+
+GB16_CASES = [
+    # name, shape (bfloat16 banks), with a bank gradient
+    ("bf16_bank", synth.Shape(1, 48, 2, (16, 16), 8, 64, 8, 8, 16, "bf16", "bf16", name="bf16b"), True),
+    # 64 slots, 16 reads and 16 writes a token: most tokens read rows they also write
+    ("collide", synth.Shape(1, 64, 2, (8, 8), 4, 32, 16, 16, 16, "bf16", "bf16", name="collide16"), True),
+    ("f32_act", synth.Shape(1, 40, 2, (8, 4, 4), 8, 32, 16, 12, 16, "f32", "bf16", name="f3b"), False),
+    ("slices16", synth.Shape(8, 24, 4, (16, 16), 8, 256, 16, 12, 8, "bf16", "bf16", name="s16b"), True),
+]
+
+
+@pytest.mark.parametrize("name,s,bank_grad", GB16_CASES, ids=[c[0] for c in GB16_CASES])
+def test_bf16_bank_gradient(name, s, bank_grad):
+    """The bank gradient in the bank dtype of a bfloat16 bank (CHANGELOG 2.0.0 "Deterministic": float32 accumulation
+    is the opt-in): every gradient within the oracle's bounds for an adjoint bank rounded to bfloat16 at every
+    update (one bfloat16 spacing per update that may round the other way); the gradient is bfloat16-valued, the
+    bank is restored bit for bit, and two calls give the same bits."""
+    x = synth.make_inputs(s, seed=51)
+    dout, dbank = _upstream(s, 52, bank_grad)
+    if dbank is not None:
+        dbank = synth.round_bf16_rne(dbank)
+    print(f"bf16 bank gradient {name}: {s}", flush=True)
+    got, fwd = run_gpu(s, x, dout, dbank, gdt=torch.bfloat16)
+    again, _ = run_gpu(s, x, dout, dbank, gdt=torch.bfloat16)
+    for k in got:
+        assert np.array_equal(got[k], again[k]), f"{k} differs between calls"
+    assert np.array_equal(synth.round_bf16_rne(got["bank"].astype(np.float32)), got["bank"])
+    ref = run_oracle(s, x, dout, dbank, grad_bank_bf16=True)
+    check(s, got, ref, fwd)
+
+
+def test_bf16_bank_gradient_batch_sum():
+    """sdm_bank_grad_sum over a bfloat16 bank gradient: the float32 sum over the batch in order, bit for bit (each
+    term widened exactly), rows past N and the padding not written."""
+    B, H, rows, d, pitch, N = 4, 2, 70, 48, 56, 64
+    rng = np.random.default_rng(9)
+    gb_np = synth.round_bf16_rne(rng.standard_normal((B, H, rows, d)).astype(np.float32))
+    gbuf = torch.zeros((B, H, rows, pitch), dtype=torch.bfloat16, device=DEV)
+    gb = gbuf[..., :d]
+    gb.copy_(to_dev(gb_np, torch.float32))
+    obuf = torch.full((H, rows, pitch), 5.0, device=DEV)
+    out = obuf[..., :d]
+    print("bf16 bank gradient sum", flush=True)
+    binding.sdm_bank_grad_sum(gb, heads=H, widths=(8, 8), head_dim=d, out=out)
+    torch.cuda.synchronize()
+    acc = gb_np[0, :, :N].copy()
+    for b in range(1, B):
+        acc = (acc + gb_np[b, :, :N]).astype(np.float32)
+    assert np.array_equal(out.cpu().numpy()[:, :N], acc)
+    assert bool((obuf[:, N:] == 5.0).all()) and bool((obuf[..., d:] == 5.0).all())
 
 
 def test_backward_padded_pitch_and_repeatable():
