@@ -133,7 +133,7 @@ __device__ __forceinline__ bf16x8_t load_bf16x8(const bf16_t* p) {
 //
 // Block mode (NW > 1): the NW waves of the workgroup hold NW * QW <= 16 consecutive queries, the rows of one MFMA
 // tile; wave w computes tiles w, w + NW, ... for all of them (each sub-key tile is read once per workgroup) into
-// the shared score buffer scs [16][64 NPL]; qb/nqb are the workgroup's first query and query count, row0 the
+// the shared score buffer scs [NW QW][64 NPL]; qb/nqb are the workgroup's first query and query count, row0 the
 // wave's first row, and qf/nq the wave's own queries. Every wave calls this (nq may be 0): it has two barriers.
 template <int NPL, int QW, int NW = 1>
 __device__ void factor_topk_filtered(const Dims& D, const TopkArgs& a, int f, int n, const bf16_t* tab,
@@ -221,35 +221,43 @@ __device__ void factor_topk_filtered(const Dims& D, const TopkArgs& a, int f, in
     const double nx = sqrt(__shfl(nx2, row0 + q, 64)) * (1.0 + 0x1p-40);
     const double E = (dk + 2) * 0x1p-23 * nx * cmax * (1.0 + 0x1p-20) + dk * 0x1p-125 * (nx + cmax + 1.0);
     bool bad = !(E <= 1e300);
-    float lmax = -INFINITY;
+    float lmax = -INFINITY, lmax2 = -INFINITY;  // the lane's largest and second largest s^
+    float sv[NPL];                               // the lane's s^, kept for the compaction below
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
       const int i = lane + 64 * j;
+      sv[j] = -INFINITY;
       if (i < n) {
         const float sh = scs[q * 64 * NPL + i];
+        sv[j] = sh;
         bad |= !(fabsf(sh) <= 3.4028234663852886e38f);
+        lmax2 = fmaxf(lmax2, fminf(lmax, sh));
         lmax = fmaxf(lmax, sh);
       }
     }
     const bool anybad = __ballot(bad) != 0ull;
-    // Wide factors first keep only the sub-keys that can reach the k_p-th largest lane maximum of s^ (k_p <= 64
-    // lanes hold a value at least that large): usually a small fraction of the factor.
+    // Wide factors first keep only the sub-keys that can reach a value L that at least k_p of them reach in s^:
+    // the k_p-th largest lane maximum (k_p <= 64 lanes hold a value at least that large), or the ceil(k_p / 2)-th
+    // largest lane second maximum (that many lanes hold two values at least that large; every lane holds at least
+    // four sub-keys here), whichever is larger: usually a small fraction of the factor.
     int mA = n;
     if constexpr (NPL >= 8) {
-      uint64_t lk[1] = {((uint64_t)desc_key(lmax) << 32) | (uint32_t)lane};
-      bool in1[1] = {true};
-      int need1 = kp, sh1 = 0, cs1 = 64;
-      const uint32_t r1 = radix_select32<1, true>(lk, in1, &need1, &sh1, &cs1);
-      uint32_t km1 = ((uint32_t)(lk[0] >> 32) >> sh1) <= (r1 >> sh1) ? (uint32_t)(lk[0] >> 32) : 0u;
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) km1 = max(km1, (uint32_t)__shfl_xor((int)km1, o, 64));
-      const float thrA =
-          (anybad || kp > 64) ? -INFINITY : __double2float_rd((double)desc_key_value(km1) - 2.0 * E);
+      auto kth_largest = [&](float v, int need) -> float {  // the need-th largest v over the wave's lanes
+        if (need >= 64) return desc_key_value(__ockl_wfred_max_u32(desc_key(v)));  // the smallest
+        uint64_t lk[1] = {((uint64_t)desc_key(v) << 32) | (uint32_t)lane};
+        bool in1[1] = {true};
+        int nd = need, sh1 = 0, cs1 = 64;
+        const uint32_t r1 = radix_select32<1, true>(lk, in1, &nd, &sh1, &cs1);
+        const uint32_t km = ((uint32_t)(lk[0] >> 32) >> sh1) <= (r1 >> sh1) ? (uint32_t)(lk[0] >> 32) : 0u;
+        return desc_key_value(__ockl_wfred_max_u32(km));
+      };
+      const float L = fmaxf(kth_largest(lmax, kp), kth_largest(lmax2, (kp + 1) / 2));
+      const float thrA = (anybad || kp > 64) ? -INFINITY : __double2float_rd((double)L - 2.0 * E);
       mA = 0;
 #pragma unroll
       for (int j = 0; j < NPL; ++j) {
         const int i = lane + 64 * j;
-        const bool kept = i < n && (anybad || scs[q * 64 * NPL + i] >= thrA);
+        const bool kept = i < n && (anybad || sv[j] >= thrA);
         const uint64_t bm = __ballot(kept);
         if (kept) klist[mA + __popcll(bm & below)] = (uint16_t)i;
         mA += __popcll(bm);
@@ -297,7 +305,14 @@ __device__ void factor_topk_filtered(const Dims& D, const TopkArgs& a, int f, in
     };
     int m;
     if constexpr (NPL >= 8) {
-      m = mA <= 256 ? stage_b(std::integral_constant<int, 4>{}) : stage_b(std::integral_constant<int, NPL>{});
+      if (mA <= 128)
+        m = stage_b(std::integral_constant<int, 2>{});
+      else if (mA <= 256)
+        m = stage_b(std::integral_constant<int, 4>{});
+      else if (NPL > 8 && mA <= 512)
+        m = stage_b(std::integral_constant<int, 8>{});
+      else
+        m = stage_b(std::integral_constant<int, NPL>{});
     } else {
       m = stage_b(std::integral_constant<int, NPL>{});
     }
@@ -306,13 +321,21 @@ __device__ void factor_topk_filtered(const Dims& D, const TopkArgs& a, int f, in
     const bf16_t* xq = qf + q * qstride;
     auto exact_key = [&](int r) -> uint64_t {
       const int i = klist[r];
-      const bf16_t* y = tab + (long long)i * dk;
+      const uint4* y = (const uint4*)(tab + (long long)i * dk);
+      const uint4* xv4 = (const uint4*)xq;
       double acc = 0.0;
-      for (int c0 = 0; c0 < dk; c0 += 8) {
-        const uint4 xv = *(const uint4*)(xq + c0);
-        const uint4 yv = *(const uint4*)(y + c0);
+      // 32 coordinates a round (dk % 32 == 0): the round's loads in flight together, then its FMAs in order
+      for (int p0 = 0; p0 < dk / 8; p0 += 4) {
+        uint4 xv[4], yv[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc = fma(Vec16<bf16_t>::at(xv, e), Vec16<bf16_t>::at(yv, e), acc);
+        for (int u = 0; u < 4; ++u) {
+          xv[u] = xv4[p0 + u];
+          yv[u] = y[p0 + u];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc = fma(Vec16<bf16_t>::at(xv[u], e), Vec16<bf16_t>::at(yv[u], e), acc);
       }
       return ((uint64_t)desc_key((float)acc) << 32) | (uint32_t)i;
     };
@@ -343,14 +366,23 @@ __device__ void factor_topk_filtered(const Dims& D, const TopkArgs& a, int f, in
 // Waves per workgroup: 4; the filtered scoring of wide factors uses 8 waves of 2 queries, so that one MFMA tile of 16
 // queries covers the workgroup and each sub-key tile is read once per workgroup (block mode of
 // factor_topk_filtered, scores in a shared LDS buffer).
-template <int NPL, bool MF> struct Topk2Waves { static constexpr int NW = (MF && WaveTile<NPL, true>::QW * 8 == 16) ? 8 : 4; };
+// Waves per workgroup in block mode (NW * QW rows of the MFMA tile, <= 16). Four waves of 2 queries leave half of
+// each MFMA tile's rows unused and read the sub-key table once per 8 queries, but their 50 KB of LDS lets three
+// workgroups share a CU where the 100 KB of eight waves allowed one: the selections, which set the time, then run at
+// 3 waves per SIMD instead of 2 (1,048,576 slots, 131,072 queries: 2.56 -> 1.87 ms; two waves: 2.01 ms).
+constexpr int TOPK_BLK_NW = 4;
+constexpr int TOPK_WIDE_WPE = 1;  // waves-per-SIMD hint of the kernels with NPL > 4 (their register budget)
+template <int NPL, bool MF> struct Topk2Waves {
+  static constexpr bool BLK = MF && WaveTile<NPL, true>::QW == 2;
+  static constexpr int NW = BLK ? TOPK_BLK_NW : 4;
+};
 
 // QW1: one query per wave (few rows, e.g. a decode step: parallelism over queries rather than reuse of sub-key rows).
 template <typename A, int NPL, int CPL, bool MF, bool QW1>
-__global__ __launch_bounds__((64 * Topk2Waves<NPL, MF>::NW)) __attribute__((amdgpu_waves_per_eu(NPL <= 4 ? 4 : 1))) void topk2_kernel(Dims D, TopkArgs a) {
+__global__ __launch_bounds__((64 * Topk2Waves<NPL, MF>::NW)) __attribute__((amdgpu_waves_per_eu(NPL <= 4 ? 4 : TOPK_WIDE_WPE))) void topk2_kernel(Dims D, TopkArgs a) {
   constexpr int QW = QW1 ? 1 : WaveTile<NPL, MF>::QW;
   constexpr int NW = QW1 ? 4 : Topk2Waves<NPL, MF>::NW;
-  constexpr bool BLK = NW == 8;  // block mode of the filtered scoring
+  constexpr bool BLK = !QW1 && Topk2Waves<NPL, MF>::BLK;  // block mode of the filtered scoring
   constexpr int VEC = Vec16<A>::N;
   extern __shared__ __align__(16) unsigned char lds[];
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -361,7 +393,7 @@ __global__ __launch_bounds__((64 * Topk2Waves<NPL, MF>::NW)) __attribute__((amdg
   const long long BT = (long long)D.B * D.T;
   const long long bt0 = ((long long)blockIdx.x * NW + wv) * QW;
   const uint64_t* cand = a.cand[kind];
-  const size_t shared_scs = BLK ? (size_t)16 * 64 * NPL * 4 : 0;  // block mode: [16][64 NPL] scores
+  const size_t shared_scs = BLK ? (size_t)NW * QW * 64 * NPL * 4 : 0;  // block mode: [NW QW][64 NPL] scores
   if constexpr (QW1) {  // few rows: the block builds its kind's candidate table itself (no separate launch)
     uint64_t* ctab = (uint64_t*)(lds + 4 * topk2_wave_lds(F, kpmax, k, QW, NPL));
     build_cand_table<256>(P, F, ctab, (int*)(ctab + P.ncand));
@@ -451,12 +483,37 @@ __global__ __launch_bounds__((64 * Topk2Waves<NPL, MF>::NW)) __attribute__((amdg
     off += n;
   }
 
+  // the merge's compaction buffer: this wave's factor-score rows, free once every factor is done
+  uint64_t* cbuf = (uint64_t*)(scs + (BLK ? wv * QW * 64 * NPL : 0));
+  const int ccap = QW * 64 * NPL / 2;  // uint64 entries
   for (int q = 0; q < nq; ++q) {
+    // A lower bound L on the k-th largest slot score: a block of position tuples p_f < a_f with prod a_f = k (a_f
+    // <= k_p) lies in the candidate table (prod(p_f + 1) <= k) and holds k candidates, each scoring at least the
+    // block's last corner (float32 addition is monotone). Candidates below L are not in the top k. Two factors
+    // only: with more, the corners of such blocks sit far down the factor lists and the bound keeps most of the
+    // table (three factors, 64 slots: no gain, 5 % slower).
+    float L = -INFINITY;
+    if (F == 2 && ccap >= 128) {
+      const float* fq = fsc + q * F * kpmax;
+      for (int g = 0; g < F; ++g) {  // one factor takes all k positions, the others their best
+        if (P.kp[g] < k) continue;
+        float S = fq[g == 0 ? k - 1 : 0];
+        for (int f = 1; f < F; ++f) S = S + fq[f * kpmax + (f == g ? k - 1 : 0)];
+        L = fmaxf(L, S);
+      }
+      if (F == 2)  // blocks a_0 x k / a_0 with a_0 a power of two that divides k
+        for (int i = 1; (2 << i) <= k + 1; ++i) {
+          const int a0 = 1 << i, a1 = k >> i;
+          if ((k & (a0 - 1)) == 0 && a0 <= P.kp[0] && a1 <= P.kp[1]) L = fmaxf(L, fq[a0 - 1] + fq[kpmax + a1 - 1]);
+        }
+    }
     uint64_t ck[CPL];
+    bool keep[CPL];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
       const int c = lane + 64 * j;
       uint64_t key = ~0ull;
+      keep[j] = false;
       if (c < P.ncand) {
         const uint64_t tup = cand[c];
         int p = (int)(tup & 0xFFFF);
@@ -468,10 +525,41 @@ __global__ __launch_bounds__((64 * Topk2Waves<NPL, MF>::NW)) __attribute__((amdg
           ps += p;
         }
         key = ((uint64_t)desc_key(S) << 32) | ((uint64_t)ps << 20) | (uint64_t)c;
+        keep[j] = S >= L;
       }
       ck[j] = key;
     }
-    wave_select_sorted<CPL>(ck, k, scratch, sorted);
+    int m2 = 0;
+    if (L > -INFINITY) {
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) m2 += __popcll(__ballot(keep[j]));
+    }
+    if (m2 >= k && m2 <= 256 && m2 <= ccap) {  // select among the kept ones only
+      const uint64_t below = lanes_below_mask();
+      int base = 0;
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        const uint64_t bm = __ballot(keep[j]);
+        if (keep[j]) cbuf[base + __popcll(bm & below)] = ck[j];
+        base += __popcll(bm);
+      }
+      wave_sync();
+      uint64_t ck4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ck4[j] = lane + 64 * j < m2 ? cbuf[lane + 64 * j] : ~0ull;
+      wave_sync();
+      if (m2 <= 64) {
+        uint64_t ck1[1] = {ck4[0]};
+        wave_select_sorted<1>(ck1, k, scratch, sorted);
+      } else if (m2 <= 128) {
+        uint64_t ck2[2] = {ck4[0], ck4[1]};
+        wave_select_sorted<2>(ck2, k, scratch, sorted);
+      } else {
+        wave_select_sorted<4>(ck4, k, scratch, sorted);
+      }
+    } else {
+      wave_select_sorted<CPL>(ck, k, scratch, sorted);
+    }
     const long long bt = bt0 + q;
     const long long b = bt / D.T, t = bt % D.T;
     const long long row = (b * D.T + t) * D.H + h;
@@ -582,11 +670,13 @@ static bool launch_topk2(const Dims& D, const TopkArgs& a, hipStream_t st) {
   const int cpl = ncand <= 256 ? 4 : ncand <= 512 ? 8 : 16;
   const bool mf = !a.one_query_per_wave && topk_filtered(D, a);
   const int QW = a.one_query_per_wave ? 1 : wave_qw(npl, mf);
-  // block mode of the filtered scoring (8 waves of 2 queries, shared [16][64 npl] scores) for wide factors
-  const bool blk = mf && QW * 8 == 16;
+  // block mode of the filtered scoring (TOPK_BLK_NW waves of 2 queries, shared [2 TOPK_BLK_NW][64 npl] scores) for
+  // wide factors
+  const bool blk = mf && QW == 2;
   size_t lds = 0;
   for (int q = 0; q < a.nkinds; ++q) {
-    size_t l = blk ? (size_t)16 * 64 * npl * 4 + 8 * topk2_wave_lds(D.F, a.plan[q].kpmax, a.plan[q].k, QW, npl, true)
+    size_t l = blk ? (size_t)TOPK_BLK_NW * QW * 64 * npl * 4 +
+                         TOPK_BLK_NW * topk2_wave_lds(D.F, a.plan[q].kpmax, a.plan[q].k, QW, npl, true)
                    : 4 * topk2_wave_lds(D.F, a.plan[q].kpmax, a.plan[q].k, QW, npl);
     if (a.one_query_per_wave) l += (size_t)a.plan[q].ncand * 8 + (size_t)(a.plan[q].kp[0] + 1) * 4;
     lds = l > lds ? l : lds;
