@@ -243,6 +243,14 @@ WsLayout layout(const Dims& D, int op) {
     L.sgpart = take((size_t)bwd_row_blocks(D) * D.H * sumn * D.dk * 4);
     L.mrho = take(nw * 4);
     L.mread = take(nr * 4);
+    const int G = bwd_group_tokens(D);
+    if (G > 1) {
+      const size_t st = (size_t)D.S * D.T, nb = (size_t)D.S * ((D.T + G - 1) / G);
+      L.gent = take(st * 4);
+      L.gcnt = take(nb * 4);
+      L.giter = take(st * 4);
+      L.gn = take((size_t)D.S * 4);
+    }
   }
   L.total = o;
   return L;
@@ -706,6 +714,11 @@ sdm_status sdm_write_read_backward(const sdm_config* cfg, const void* write_keys
   ba.sgpart = (float*)(ws + L.sgpart);
   ba.mrho = (float*)(ws + L.mrho);
   ba.mread = (float*)(ws + L.mread);
+  const bool grouped = bwd_group_tokens(D) > 1;
+  ba.gent = grouped ? (int32_t*)(ws + L.gent) : nullptr;
+  ba.gcnt = grouped ? (int32_t*)(ws + L.gcnt) : nullptr;
+  ba.giter = grouped ? (int32_t*)(ws + L.giter) : nullptr;
+  ba.gn = grouped ? (int32_t*)(ws + L.gn) : nullptr;
   TRY(hip_status(timed(SDM_K_BWD, st, [&] { return launch_bwd(D, ba, st); }), "backward launch"));
   return ok();
 }

@@ -268,19 +268,21 @@ __global__ __launch_bounds__(64) void bwd_match_kernel(Dims D, BwdArgs a) {
   }
 }
 
-// The same sweep for W, R <= 128 (one write and one read term per 4-lane group), two barriers and one HBM load
-// round trip per token: the read rows, their G rows and the write terms' G rows of token t are loaded together; the snapshot rows, gates, output gradient and values of token t - 1 and the ids of token
-// t - 2 are loaded a token ahead (read-only data) and kept raw until used (a conversion next to its load would make
-// the compiler wait for every earlier load). A write slot that the token also reads gets the read's G update
-// (rho_j dout, rho_j from bwd_match_kernel) added in registers, since its loaded G row predates that update. Sums
-// over the write terms: a fixed shuffle tree inside each wave, then every lane adds the 8 wave partials of its own
-// columns in order (the same sums on every lane, so no barrier for a broadcast). Every store of a token comes after
-// its last use of loaded data: loads and stores share one memory counter, and a wait for a load issued before a
-// store would also wait for the store. So the read's G update is stored with the write's, and not at all when the
-// token also writes that slot (the write's G row includes it). The loads of token t - 1's rows
-// follow the end-of-token barrier, after every store of token t in the workgroup's program order (one CU: its
-// vector memory pipeline keeps that order).
-// LPG lanes per term group (4 columns each): slices of 4 LPG columns, 128 groups, 128 LPG threads (2 LPG waves).
+// The same sweep for W, R <= 128 (one write and one read term per lane group), two barriers and one HBM load round
+// trip per step. A step takes one token, or a run of consecutive tokens with pairwise disjoint slots (at most one
+// per block of wb waves; bwd_group_kernel), each token on its own block with its own step's arithmetic: the read
+// rows, their G rows and the write terms' G rows of the step's tokens are loaded together; the snapshot rows, gates,
+// output gradient and values of the next step and the ids of the one after are loaded a step ahead (read-only data)
+// and kept raw until used (a conversion next to its load would make the compiler wait for every earlier load). A
+// write slot that the token also reads gets the read's G update (rho_j dout, rho_j from bwd_match_kernel) added in
+// registers, since its loaded G row predates that update. Sums over a token's write terms: a fixed shuffle tree
+// inside each wave, then every lane adds the wave partials of its token's block, for its own columns, in order (the
+// same sums on every lane, so no barrier for a broadcast). Every store of a step comes after its last use of loaded
+// data: loads and stores share one memory counter, and a wait for a load issued before a store would also wait for
+// the store. So the read's G update is stored with the write's, and not at all when the token also writes that slot
+// (the write's G row includes it). The next step's row loads follow the end-of-step barrier, after every store of
+// this step in the workgroup's program order (one CU: its vector memory pipeline keeps that order).
+// LPG lanes per term group (4 columns each): slices of 4 LPG columns, BWD_FAST_GROUPS groups.
 // Sk: the snapshot's element type (Bk, or bfloat16 rows of a float32 bank, which restore the bank widened). SQ:
 // SNAP_FP8 / SNAP_INT4 for a quantized snapshot of a float32 bank (Sk unused): a lane reads its 4 elements (4 or 2
 // bytes) and its 16-column group's scale byte, and the bank is restored from the dequantized values.
@@ -325,8 +327,8 @@ template <> struct GRow<bf16_t> {
 };
 
 template <typename A, typename Bk, int LPG, typename Sk = Bk, int SQ = SNAP_BANK, typename Gk = float>
-__global__ __launch_bounds__(128 * LPG) void bwd_sweep_fast_kernel(Dims D, BwdArgs a, int nsl) {
-  constexpr int COLS = 4 * LPG, NW = 2 * LPG;
+__global__ __launch_bounds__(BWD_FAST_GROUPS * LPG) void bwd_sweep_fast_kernel(Dims D, BwdArgs a, int nsl, int wb) {
+  constexpr int COLS = 4 * LPG, NW = BWD_FAST_GROUPS * LPG / 64;
   constexpr bool QS = SQ == SNAP_FP8 || SQ == SNAP_INT4;
   __shared__ __align__(16) float sRedD[NW][COLS];
   __shared__ __align__(16) float sRedR[NW][COLS];
@@ -343,8 +345,10 @@ __global__ __launch_bounds__(128 * LPG) void bwd_sweep_fast_kernel(Dims D, BwdAr
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, grp = tid / LPG, q = tid % LPG;
   const int col = slice * COLS + q * 4;
   const bool valid = col < d;
-  const bool hasR = grp < R, hasW = grp < W;
-  const int jr = min(grp, R - 1), jw = min(grp, W - 1);  // clamped term indices: every lane loads in range
+  // token blocks of wb waves: block `sub` takes the iteration's sub-th token, its group lgrp that token's terms
+  const int sub = wv / wb, lgrp = grp - sub * wb * (64 / LPG);
+  const bool blk_ok = (sub + 1) * wb <= NW;               // a whole block (waves past the last one idle)
+  const int jr = min(lgrp, R - 1), jw = min(lgrp, W - 1);  // clamped term indices: every lane loads in range
   const int P = W + R + 2;
   Bk* bank = (Bk*)a.bank + (long long)st * D.rows * D.ld;
   Gk* gbank = (Gk*)a.gbank + (long long)st * D.rows * D.ld;
@@ -386,20 +390,37 @@ __global__ __launch_bounds__(128 * LPG) void bwd_sweep_fast_kernel(Dims D, BwdAr
       sp_ = Raw4<Sk>::load(snap + ((long long)t * W + jw) * d + dcol);
   };
 
+  // iterations: entry (first token << 4) | number of tokens; the tokens of one entry are consecutive, in
+  // decreasing order, and address pairwise disjoint slots (bwd_group_kernel); without grouping, one token each
+  // (the entry is then the token itself)
+  const bool grouped = a.giter != nullptr;
+  const int niter = grouped ? a.gn[st] : T;
+  auto entry = [&](int it) -> int32_t {
+    it = min(it, niter - 1);  // past the last: the last again (its loads stay in range; it stores nothing)
+    return grouped ? a.giter[(long long)st * T + it] : T - 1 - it;
+  };
+  auto first_tok = [&](int32_t e) { return grouped ? e >> 4 : e; };
+  auto tok_of = [&](int32_t e) { return blk_ok ? max(first_tok(e) - sub, 0) : first_tok(e); };
+  int32_t e0 = entry(0), e1 = entry(1), e2 = entry(2);
+
   int rs, ws, rs1, ws1;
   float rho, w, mr, mw, rho1, w1, mr1, mw1;
   uint32_t c_al, c_be;
   ARaw c_v, c_dout;
   RawS c_sp;
-  load_ids(T - 1, rs, rho, ws, w, mr, mw);
-  load_ids(max(T - 2, 0), rs1, rho1, ws1, w1, mr1, mw1);
-  load_tok(T - 1, c_al, c_be, c_v, c_dout, c_sp);
+  load_ids(tok_of(e0), rs, rho, ws, w, mr, mw);
+  load_ids(tok_of(e1), rs1, rho1, ws1, w1, mr1, mw1);
+  load_tok(tok_of(e0), c_al, c_be, c_v, c_dout, c_sp);
   // the loop's first values in before it starts: a load still in flight on the way in would make the loop head wait
   // for everything outstanding, the previous token's stores included, on every token
   asm volatile("" ::"v"(rs), "v"(ws), "v"(rho), "v"(w), "v"(mr), "v"(mw), "v"(rs1), "v"(ws1), "v"(rho1), "v"(w1),
                "v"(mr1), "v"(mw1), "v"(c_al), "v"(c_be), "v"(c_v), "v"(c_dout), "v"(c_sp));
 
-  for (int t = T - 1; t >= 0; --t) {
+  for (int it = 0; it < niter; ++it) {
+    const int t = tok_of(e0);
+    const bool act = blk_ok && sub < (grouped ? (e0 & 15) : 1);  // this block has a token in this iteration
+    const bool hasR = act && lgrp < R, hasW = act && lgrp < W;
+    const int32_t e3 = entry(it + 3);
     const long long so = (long long)st * T + t;
     const long long row = ((long long)b * T + t) * D.H + h;
     float* part = a.part + ((long long)slice * D.S * T + so) * P;
@@ -407,14 +428,14 @@ __global__ __launch_bounds__(128 * LPG) void bwd_sweep_fast_kernel(Dims D, BwdAr
     const RawT rb = Raw4<Bk>::load(bank + (long long)rs * D.ld + dcol);
     float4 rg = GRow<Gk>::load(gbank + (long long)rs * D.ld + dcol);
     const float4 wg = GRow<Gk>::load(gbank + (long long)ws * D.ld + dcol);
-    // ahead: token t - 1's inputs and snapshot rows, token t - 2's ids (token indices clamped at 0)
+    // ahead: the next iteration's inputs and snapshot rows, the ids of the one after
     uint32_t n_al, n_be;
     ARaw n_v, n_dout;
     RawS n_sp;
     int rs2, ws2;
     float rho2, w2, mr2, mw2;
-    load_tok(max(t - 1, 0), n_al, n_be, n_v, n_dout, n_sp);
-    load_ids(max(t - 2, 0), rs2, rho2, ws2, w2, mr2, mw2);
+    load_tok(tok_of(e1), n_al, n_be, n_v, n_dout, n_sp);
+    load_ids(tok_of(e2), rs2, rho2, ws2, w2, mr2, mw2);
     const float al = Word<A>::get(c_al, alpha + row), be = Word<A>::get(c_be, beta + row);
     float dout[4], v[4];
     Raw4<A>::unpack(c_dout, dout);
@@ -457,10 +478,10 @@ __global__ __launch_bounds__(128 * LPG) void bwd_sweep_fast_kernel(Dims D, BwdAr
       if (lane == 0) sRedGP[wv] = gp;
     }
     __syncthreads();
-    // D, r and delta of this lane's four columns (the NW wave partials in order, on every lane alike)
+    // D, r and delta of this lane's four columns (the block's wave partials in order, on every lane alike)
     float Dl[4] = {0.f, 0.f, 0.f, 0.f}, r[4] = {0.f, 0.f, 0.f, 0.f}, dl[4];
-#pragma unroll
-    for (int k = 0; k < NW; ++k) {
+    const int k0 = blk_ok ? sub * wb : 0;
+    for (int k = k0; k < k0 + wb; ++k) {
       const float4 x = *(const float4*)&sRedD[k][q * 4];
       const float4 y = *(const float4*)&sRedR[k][q * 4];
       Dl[0] += x.x; Dl[1] += x.y; Dl[2] += x.z; Dl[3] += x.w;
@@ -472,22 +493,21 @@ __global__ __launch_bounds__(128 * LPG) void bwd_sweep_fast_kernel(Dims D, BwdAr
       e[k] = v[k] - al * r[k];  // v - alpha r
       dl[k] = be * e[k];
     }
-    if (grp == 0) {  // dv, and the slice partials of d alpha and d beta (LPG lanes x 4 columns)
+    if (act && lgrp == 0) {  // dv, and the slice partials of d alpha and d beta (LPG lanes x 4 columns)
       if (valid)
         *(float4*)(a.gvalues + row * d + col) = make_float4(be * Dl[0], be * Dl[1], be * Dl[2], be * Dl[3]);
       const float db = sum_group_lanes<LPG>(((Dl[0] * e[0] + Dl[1] * e[1]) + Dl[2] * e[2]) + Dl[3] * e[3]);
       const float rd = sum_group_lanes<LPG>(((Dl[0] * r[0] + Dl[1] * r[1]) + Dl[2] * r[2]) + Dl[3] * r[3]);
       if (q == 0) {
         float gps = 0.f;
-#pragma unroll
-        for (int k = 0; k < NW; ++k) gps += sRedGP[k];
+        for (int k = k0; k < k0 + wb; ++k) gps += sRedGP[k];
         part[W + R] = gps - be * rd;
         part[W + R + 1] = db;
       }
     }
     // the read's stores (its G row only if the token does not also write the slot)
     if (hasR) {
-      if (q == 0) part[W + grp] = rdot;
+      if (q == 0) part[W + lgrp] = rdot;
       if (valid && mw == 0.f) GRow<Gk>::store(gbank + (long long)rs * D.ld + col, rg);
     }
     // d w partials, G[S_i] <- alpha g_i - alpha beta w_i D, M[S_i] <- P_i
@@ -495,7 +515,7 @@ __global__ __launch_bounds__(128 * LPG) void bwd_sweep_fast_kernel(Dims D, BwdAr
       const float ab = al * be;
       const float gd = sum_group_lanes<LPG>(((g[0] * dl[0] + g[1] * dl[1]) + g[2] * dl[2]) + g[3] * dl[3]);
       const float Dp = sum_group_lanes<LPG>(((Dl[0] * pp[0] + Dl[1] * pp[1]) + Dl[2] * pp[2]) + Dl[3] * pp[3]);
-      if (q == 0) part[grp] = gd - ab * Dp;
+      if (q == 0) part[lgrp] = gd - ab * Dp;
       if (valid) {
         const float cw = ab * w;
         GRow<Gk>::store(gbank + (long long)ws * D.ld + col, make_float4(
@@ -506,10 +526,11 @@ __global__ __launch_bounds__(128 * LPG) void bwd_sweep_fast_kernel(Dims D, BwdAr
           *(float4*)(bank + (long long)ws * D.ld + col) = make_float4(pp[0], pp[1], pp[2], pp[3]);
       }
     }
-    // next token
+    // next iteration
     rs = rs1; rho = rho1; ws = ws1; w = w1; mr = mr1; mw = mw1;
     rs1 = rs2; rho1 = rho2; ws1 = ws2; w1 = w2; mr1 = mr2; mw1 = mw2;
     c_al = n_al; c_be = n_be; c_v = n_v; c_dout = n_dout; c_sp = n_sp;
+    e0 = e1; e1 = e2; e2 = e3;
     __syncthreads();
   }
 }
@@ -643,11 +664,93 @@ __global__ __launch_bounds__(256) void bwd_subkey_sum_kernel(const float* __rest
   gsub[i] = s;
 }
 
+// Token grouping of the fast sweep. Tokens are cut, in decreasing order, into blocks of G; within a block, runs of
+// consecutive tokens whose slot sets (read and write ids) are pairwise disjoint are greedy-grown from its first
+// token. The tokens of a run touch disjoint bank and gradient rows, so the sweep takes them in one step, each with
+// the arithmetic of its own step (the same results, bit for bit). One workgroup per (stream, block).
+constexpr int BWD_MAX_G = 16;
+__global__ __launch_bounds__(64) void bwd_group_kernel(Dims D, BwdArgs a, int G, int nb) {
+  __shared__ int32_t sl[BWD_MAX_G][2 * 128];
+  __shared__ int32_t conf[BWD_MAX_G][BWD_MAX_G];
+  const int st = blockIdx.x / nb, g = blockIdx.x % nb;
+  const int W = D.W, R = D.R, T = D.T, n = W + R;
+  const int t0 = T - 1 - g * G;     // the block's first (largest) token
+  const int nv = min(G, t0 + 1);    // its tokens: t0, t0 - 1, ..., t0 - nv + 1
+  for (int i = threadIdx.x; i < BWD_MAX_G * BWD_MAX_G; i += 64) conf[i / BWD_MAX_G][i % BWD_MAX_G] = 0;
+  for (int i = threadIdx.x; i < nv * n; i += 64) {
+    const int k = i / n, e = i % n;
+    const long long so = (long long)st * T + (t0 - k);
+    sl[k][e] = e < R ? a.ridx[so * R + e] : a.widx[so * W + (e - R)];
+  }
+  __syncthreads();
+  // conf[k0][k1], k0 < k1: the block's tokens k0 and k1 address a common slot
+  for (int i = threadIdx.x; i < nv * nv * n; i += 64) {
+    const int k0 = i / (nv * n), k1 = (i / n) % nv, e = i % n;
+    if (k0 >= k1) continue;
+    const int32_t x = sl[k1][e];
+    bool hit = false;
+    for (int f = 0; f < n; ++f) hit |= sl[k0][f] == x;
+    if (hit) conf[k0][k1] = 1;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int runs = 0;
+    for (int k = 0; k < nv;) {
+      int size = 1;
+      for (; k + size < nv; ++size) {
+        bool ok = true;
+        for (int m = k; m < k + size; ++m) ok = ok && conf[m][k + size] == 0;
+        if (!ok) break;
+      }
+      a.gent[(long long)st * T + g * G + runs] = ((t0 - k) << 4) | size;
+      ++runs;
+      k += size;
+    }
+    a.gcnt[(long long)st * nb + g] = runs;
+  }
+}
+
+// Every stream's entries in order (the blocks' runs, compacted): an exclusive scan of the run counts. One
+// workgroup per stream.
+__global__ __launch_bounds__(256) void bwd_group_scan_kernel(Dims D, BwdArgs a, int G, int nb) {
+  __shared__ int32_t ssum[256];
+  __shared__ int32_t base;
+  const int st = blockIdx.x, tid = threadIdx.x, T = D.T;
+  if (tid == 0) base = 0;
+  __syncthreads();
+  for (int c0 = 0; c0 < nb; c0 += 256) {
+    const int g = c0 + tid;
+    const int c = g < nb ? a.gcnt[(long long)st * nb + g] : 0;
+    ssum[tid] = c;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {  // inclusive scan
+      const int v = tid >= o ? ssum[tid - o] : 0;
+      __syncthreads();
+      ssum[tid] += v;
+      __syncthreads();
+    }
+    const int pos = base + ssum[tid] - c;
+    for (int e = 0; e < c; ++e) a.giter[(long long)st * T + pos + e] = a.gent[(long long)st * T + g * G + e];
+    __syncthreads();  // every thread has read base
+    if (tid == 255) base += ssum[255];
+    __syncthreads();
+  }
+  if (tid == 0) a.gn[st] = base;
+}
+
 template <typename A, typename Bk>
 static hipError_t launch_bwd_t(const Dims& D, const BwdArgs& a, hipStream_t st) {
   const int nsl = bwd_nsl(D);
   if (bwd_fast(D)) {
     hipLaunchKernelGGL(bwd_match_kernel, dim3((unsigned)((long long)D.S * D.T)), dim3(64), 0, st, D, a);
+    const int G = bwd_group_tokens(D), wb = bwd_wave_block(D);
+    if (G > BWD_MAX_G || wb < 1 || wb * 64 > BWD_FAST_GROUPS * (bwd_cols(D) / 4))
+      return hipErrorInvalidValue;  // never: W, R <= 128
+    if (G > 1) {
+      const int nb = (D.T + G - 1) / G;
+      hipLaunchKernelGGL(bwd_group_kernel, dim3((unsigned)((long long)D.S * nb)), dim3(64), 0, st, D, a, G, nb);
+      hipLaunchKernelGGL(bwd_group_scan_kernel, dim3((unsigned)D.S), dim3(256), 0, st, D, a, G, nb);
+    }
     const dim3 grid((unsigned)((long long)D.S * nsl));
     auto fast = [&](auto sk, auto sq) {  // sk: a value of the snapshot's element type; sq: its mode
       using Sk = decltype(sk);
@@ -655,9 +758,11 @@ static hipError_t launch_bwd_t(const Dims& D, const BwdArgs& a, hipStream_t st) 
       auto go = [&](auto gk) {  // gk: a value of the bank gradient's element type
         using Gk = decltype(gk);
         if (bwd_cols(D) == 8)
-          hipLaunchKernelGGL((bwd_sweep_fast_kernel<A, Bk, 2, Sk, SQ, Gk>), grid, dim3(256), 0, st, D, a, nsl);
+          hipLaunchKernelGGL((bwd_sweep_fast_kernel<A, Bk, 2, Sk, SQ, Gk>), grid, dim3(BWD_FAST_GROUPS * 2), 0, st, D,
+                             a, nsl, wb);
         else
-          hipLaunchKernelGGL((bwd_sweep_fast_kernel<A, Bk, 4, Sk, SQ, Gk>), grid, dim3(512), 0, st, D, a, nsl);
+          hipLaunchKernelGGL((bwd_sweep_fast_kernel<A, Bk, 4, Sk, SQ, Gk>), grid, dim3(BWD_FAST_GROUPS * 4), 0, st, D,
+                             a, nsl, wb);
       };
       if constexpr (std::is_same<Bk, bf16_t>::value && SQ == SNAP_BANK)
         if (a.grad_bf16) {

@@ -254,6 +254,7 @@ struct WsLayout {
   size_t owner, conflict;                      // shared bank: int32 [H][N] first stream of each slot; int32 flag
   size_t part;                                 // backward: float [slices][S][T][W + R + 2] per-slice dot products
   size_t mrho;                                 // backward: float [S][T][W] read weight of the same slot, or 0
+  size_t gent, gcnt, giter, gn;                // backward: token grouping of the fast sweep (bwd_group_kernel)
   size_t mread;                                // backward: float [S][T][R] 1 if the read slot is also written
   size_t ds;                                   // backward: float [S][T][W + R] slot-score gradients
   size_t sgpart;                               // backward: float [row blocks][H][sum n_f][dk] sub-key partial sums
@@ -347,6 +348,10 @@ struct BwdArgs {
   float* part; float* ds; float* sgpart;  // workspace
   float* mrho;            // workspace [S][T][W]: rho of the read term of the same token and slot as write term i, or 0
   float* mread;           // workspace [S][T][R]: 1 if read term j's slot is also written by the token, else 0
+  // workspace, the fast sweep's token grouping (NULL: one token per iteration): gent [S][T] the entries of each
+  // block of G tokens, gcnt [S][ceil(T / G)] their number, giter [S][T] every stream's entries in order, gn [S]
+  // their number. An entry is (first token << 4) | token count.
+  int32_t* gent; int32_t* gcnt; int32_t* giter; int32_t* gn;
 };
 // Slices of 16 columns the backward sweep splits a row into, and the row blocks of the sub-key sums.
 inline int bwd_slices(const Dims& D) { return (D.d + 15) / 16; }

@@ -148,6 +148,9 @@ CASES = [
     # enough streams x 16-column slices (32 x 16 = 512) that the sweep keeps 16-column slices; the shapes above take
     # 8-column slices (two token chains per CU)
     ("slices16", synth.Shape(8, 24, 4, (16, 16), 8, 256, 16, 12, 8, name="s16"), True),
+    # steps of up to four consecutive tokens with disjoint slots (W, R <= 32 on 16-column slices), 4,096 slots so
+    # that runs of every length occur, and a token count that is not a multiple of four
+    ("token_runs", synth.Shape(2, 61, 2, (64, 64), 8, 64, 12, 20, 16, name="runs"), True),
 ]
 
 
