@@ -16,6 +16,11 @@ here (the plainest one) is:
 Every tensor between the steps is a bfloat16 tensor (the layer runs in bfloat16, README usage example), so the
 oracle rounds each to bfloat16 (nearest, ties to even) after computing it in fp64.
 
+The backward (``layer_backward``) is the chain rule through those steps, last first; the gradients passed between
+steps are bfloat16 like the tensors they belong to. Pins of the backward (``tests/test_layer_oracle_backward_pins.py``):
+central finite differences of the unrounded layer along random directions in every input and parameter, the gates'
+derivatives against finite differences and closed forms, and the dense maps' transposes by hand-summed loops.
+
 Pins (``tests/test_layer_oracle_pins.py``): the dense map against a brute-force sum with the weight's row/column
 roles fixed by a non-square example; softplus against ``numpy.logaddexp``; the gates' closed forms (alpha = 1 when
 A = 0 or when a + dt_bias runs to minus infinity, alpha = e^-1 when A = 1 and softplus = 1, beta = 1/2 at b = 0);
@@ -83,23 +88,104 @@ def initial_bank_copy(initial_bank, batch) -> np.ndarray:
 
 
 def layer_forward(x, w_in, a_log, dt_bias, w_out, subkeys, bank, *, heads, widths, num_writes, num_reads,
-                  bank_bf16=False, nthreads=None, initial_bank=None):
+                  bank_bf16=False, nthreads=None, initial_bank=None, rounded=True):
     """The layer's forward on bfloat16 tensors (given as float arrays of bfloat16 values). Returns a dict with every
     intermediate (keys, queries, values, a, b, alpha, beta: bfloat16 values as float64; the op's result dict `op`;
-    y [B, T, Dm] bfloat16 values as float64). The bank is not modified (the op oracle advances a copy). With
-    initial_bank [H, rows, d] the op starts from its copy in every batch row instead of `bank`."""
+    o [B, T, H d] the op's output; y [B, T, Dm] bfloat16 values as float64). The bank is not modified (the op oracle
+    advances a copy). With initial_bank [H, rows, d] the op starts from its copy in every batch row instead of
+    `bank`. rounded=False: the same steps with no bfloat16 rounding anywhere and the op's bank states in fp64 (its
+    inputs still pass as float32), the smooth function that the backward differentiates (finite-difference pins)."""
     if initial_bank is not None:
         bank = initial_bank_copy(initial_bank, np.asarray(x).shape[0])
+    rnd = round_bf16_array if rounded else (lambda v: np.asarray(v, dtype=np.float64))
     dk = np.asarray(subkeys).shape[-1]
     d = np.asarray(bank).shape[-1]
-    p = round_bf16_array(dense(x, w_in))
+    p = rnd(dense(x, w_in))
     keys, queries, values, a, b = split_projection(p, heads, widths, dk, d)
     alpha, beta = gates(a, b, a_log, dt_bias)
-    alpha, beta = round_bf16_array(alpha), round_bf16_array(beta)
-    op = sdm_oracle.write_read(keys, queries, values, alpha, beta, subkeys, bank, widths, num_writes, num_reads,
-                               bank_bf16=bank_bf16, act_bf16=True, nthreads=nthreads)
+    alpha, beta = rnd(alpha), rnd(beta)
+    if rounded:
+        op = sdm_oracle.write_read(keys, queries, values, alpha, beta, subkeys, bank, widths, num_writes, num_reads,
+                                   bank_bf16=bank_bf16, act_bf16=True, nthreads=nthreads)
+    else:  # the fp64-state forward of the op (its backward run with zero upstream gradients)
+        B0, T0 = p.shape[:2]
+        op = sdm_oracle.write_read_backward(keys, queries, values, alpha, beta, subkeys, bank,
+                                            np.zeros((B0, T0, heads, d)), None, widths, num_writes, num_reads,
+                                            exact=True, want_forward=True, nthreads=nthreads)
     B, T = p.shape[:2]
     o = np.asarray(op["out"], dtype=np.float64).reshape(B, T, -1)
-    y = round_bf16_array(dense(o, w_out))
+    y = rnd(dense(o, w_out))
     return {"keys": keys, "queries": queries, "values": values, "a": a, "b": b, "alpha": alpha, "beta": beta,
-            "op": op, "y": y}
+            "op": op, "o": o, "y": y, "bank_in": np.asarray(bank)}
+
+
+def sigmoid(x) -> np.ndarray:
+    """1 / (1 + e^-x) in fp64, without overflow for large |x|."""
+    x = np.asarray(x, dtype=np.float64)
+    e = np.exp(-np.abs(x))
+    return np.where(x >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+
+
+def gates_backward(a, b, a_log, dt_bias, d_alpha, d_beta):
+    """The chain rule through gates() (fp64; alpha and beta recomputed from a and b, unrounded). With z = a + dt_bias[h]
+    and A = exp(a_log[h]): alpha = exp(-A softplus(z)), so d alpha / d a = d alpha / d dt_bias = -alpha A sigmoid(z)
+    (the derivative of softplus is the sigmoid) and d alpha / d a_log = -alpha A softplus(z); beta = sigmoid(b), so
+    d beta / d b = beta (1 - beta). Returns d_a, d_b (the shape of a) and d_a_log, d_dt_bias [H], summed over every
+    leading index."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    A = np.exp(np.asarray(a_log, dtype=np.float64))
+    z = a + np.asarray(dt_bias, dtype=np.float64)
+    sp = softplus(z)
+    alpha = np.exp(-A * sp)
+    beta = sigmoid(b)
+    da_ = np.asarray(d_alpha, dtype=np.float64)
+    d_a = da_ * alpha * (-A) * sigmoid(z)
+    d_b = np.asarray(d_beta, dtype=np.float64) * beta * (1.0 - beta)
+    lead = tuple(range(d_a.ndim - 1))
+    d_a_log = np.sum(da_ * alpha * (-A * sp), axis=lead)
+    d_dt_bias = np.sum(d_a, axis=lead)
+    return d_a, d_b, d_a_log, d_dt_bias
+
+
+def layer_backward(x, w_in, a_log, dt_bias, w_out, subkeys, bank, grad_y, grad_bank=None, *, heads, widths,
+                   num_writes, num_reads, bank_bf16=False, nthreads=None, initial_bank=None, rounded=True, fwd=None):
+    """Gradients of the layer (the chain rule through layer_forward's steps, last step first). grad_y [B, T, Dm] is
+    the gradient of the loss with respect to y and grad_bank (the bank's shape, or None for zero) the one with
+    respect to the bank after the call. Every tensor between the steps is bfloat16 (rounded=True, as in the
+    forward), so the gradients passed between them are rounded to bfloat16 too: d o (into the op's backward) and
+    d p (the input map's output, assembled from the op's key, query and value gradients and the gate inputs'
+    gradients). Parameter and input gradients are fp64:
+      d o = grad_y w_out,  d w_out = sum over (b, t) of grad_y^T o
+      the op's backward (sdm_oracle.write_read_backward) on d o and grad_bank
+      d a, d b, d a_log, d dt_bias: gates_backward on the op's d alpha, d beta
+      d x = d p w_in,  d w_in = sum over (b, t) of d p^T x
+    Returns d_o, d_p (as bfloat16 values when rounded), d_x, d_w_in, d_a_log, d_dt_bias, d_w_out, d_subkeys, d_bank
+    (with respect to the bank the op started from), the op's result `op`, d_a, d_b, the forward `fwd`, and with
+    initial_bank d_initial_bank (d_bank summed over the batch)."""
+    kw = dict(heads=heads, widths=widths, num_writes=num_writes, num_reads=num_reads, bank_bf16=bank_bf16,
+              nthreads=nthreads, initial_bank=initial_bank, rounded=rounded)
+    f = fwd if fwd is not None else layer_forward(x, w_in, a_log, dt_bias, w_out, subkeys, bank, **kw)
+    rnd = round_bf16_array if rounded else (lambda v: np.asarray(v, dtype=np.float64))
+    x = np.asarray(x, dtype=np.float64)
+    w_in = np.asarray(w_in, dtype=np.float64)
+    w_out = np.asarray(w_out, dtype=np.float64)
+    gy = np.asarray(grad_y, dtype=np.float64)
+    B, T, _ = x.shape
+    H = int(heads)
+    d = np.asarray(f["bank_in"]).shape[-1]
+    o = f["o"]
+    d_o = rnd(gy @ w_out)                                  # [B, T, H d]
+    d_w_out = np.einsum("btn,btk->nk", gy, o)             # [Dm, H d]
+    ob = sdm_oracle.write_read_backward(f["keys"], f["queries"], f["values"], f["alpha"], f["beta"], subkeys,
+                                        f["bank_in"], d_o.reshape(B, T, H, d), grad_bank, widths, num_writes,
+                                        num_reads, bank_bf16=bank_bf16, exact=not rounded, nthreads=nthreads)
+    d_a, d_b, d_a_log, d_dt_bias = gates_backward(f["a"], f["b"], a_log, dt_bias, ob["d_alpha"], ob["d_beta"])
+    d_p = rnd(np.concatenate([ob["d_wkeys"].reshape(B, T, -1), ob["d_rq"].reshape(B, T, -1),
+                              ob["d_values"].reshape(B, T, -1), d_a, d_b], axis=-1))
+    res = {"d_o": d_o, "d_p": d_p, "d_x": d_p @ w_in, "d_w_in": np.einsum("btn,btk->nk", d_p, x),
+           "d_a_log": d_a_log, "d_dt_bias": d_dt_bias, "d_w_out": d_w_out, "d_subkeys": ob["d_subkeys"],
+           "d_bank": ob["d_bank"], "op": ob, "d_a": d_a, "d_b": d_b, "fwd": f}
+    if initial_bank is not None:
+        res["d_initial_bank"] = ob["d_bank"].sum(axis=0)
+    return res
