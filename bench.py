@@ -368,7 +368,45 @@ def bench_layer(args, torch, binding, synth):
            "config": f"x [{s.batch}, {s.tokens}, {Dm}] bf16, w_in [{n_in}, {Dm}], w_out [{Dm}, "
                      f"{s.heads * s.head_dim}], op as layer_65k (f32 bank)"}
     log(f"[bench] layer: {res['tokens_per_s']} tokens/s, dense {dense_ms:.3f} ms per call")
-    del bank, ws, y, t, g
+    del ws
+    # the layer's training step: the snapshot-saving forward and the backward (which steps the bank back)
+    gy = torch.randn((s.batch, s.tokens, Dm), generator=torch.Generator(device=dev).manual_seed(5),
+                     device=dev).to(torch.bfloat16)
+    gbank = torch.zeros((s.batch, s.heads, s.rows, pitch), dtype=torch.float32, device=dev)[..., :s.head_dim]
+    bank0 = bank.clone()
+    y, snap, wsb, _, _ = binding.sdm_layer_forward_save(t["x"], t["w_in"], g["a_log"], g["dt_bias"], t["w_out"],
+                                                        t["subkeys"], bank, **kw)
+    binding.sdm_layer_backward(t["x"], t["w_in"], g["a_log"], g["dt_bias"], t["w_out"], t["subkeys"], bank, snap, gy,
+                               wsb, gbank, **kw)
+    torch.cuda.synchronize()
+    restored = bool(torch.equal(bank, bank0))
+    tf = tb = 0.0
+    binding.profile_enable(True)
+    for _ in range(n):
+        gbank.zero_()
+        torch.cuda.synchronize()
+        a = time.perf_counter()
+        binding.sdm_layer_forward_save(t["x"], t["w_in"], g["a_log"], g["dt_bias"], t["w_out"], t["subkeys"], bank,
+                                       y=y, snapshot=snap, workspace=wsb, **kw)
+        torch.cuda.synchronize()
+        b = time.perf_counter()
+        binding.sdm_layer_backward(t["x"], t["w_in"], g["a_log"], g["dt_bias"], t["w_out"], t["subkeys"], bank, snap,
+                                   gy, wsb, gbank, **kw)
+        torch.cuda.synchronize()
+        tf += b - a
+        tb += time.perf_counter() - b
+    prof = binding.profile_read()
+    binding.profile_enable(False)
+    ms_f, ms_b = tf * 1e3 / n, tb * 1e3 / n
+    # dense maps of the step: the forward's two, the backward's four (d o, d w_out, d x, d w_in), same shapes
+    res["train"] = {"tokens_per_s": round(M / ((ms_f + ms_b) * 1e-3), 1), "ms_forward_save": round(ms_f, 4),
+                    "ms_backward": round(ms_b, 4), "bank_restored_bitwise": restored,
+                    "dense_ms_per_step": round(prof["dense"][0] / n, 4), "dense_flops_per_step": 3 * flops,
+                    "kernels_ms_per_step": {k: round(v[0] / n, 4) for k, v in prof.items() if v[1]},
+                    "config": "the layer above; grad_y ~ N(0, 1) bf16, float32 gradients"}
+    log(f"[bench] layer train: {res['train']['tokens_per_s']} tokens/s (forward {ms_f:.3f} ms, backward "
+        f"{ms_b:.3f} ms)")
+    del bank, bank0, wsb, snap, gbank, gy, y, t, g
     torch.cuda.empty_cache()
     return res
 

@@ -165,6 +165,12 @@ def load():
             lib.sdm_bank_grad_sum.restype = ctypes.c_int
             lib.sdm_bank_grad_sum.argtypes = [cfgp, _vp, _vp, _vp]
             lib.sdm_layer_forward.restype = ctypes.c_int
+            lib.sdm_layer_forward_save.argtypes = [lcfgp] + [_vp] * 13 + [ctypes.c_size_t, _vp]
+            lib.sdm_layer_forward_save.restype = ctypes.c_int
+            lib.sdm_layer_backward_workspace_size.argtypes = [lcfgp, ctypes.POINTER(ctypes.c_size_t)]
+            lib.sdm_layer_backward_workspace_size.restype = ctypes.c_int
+            lib.sdm_layer_backward.argtypes = [lcfgp] + [_vp] * 17 + [ctypes.c_size_t, _vp]
+            lib.sdm_layer_backward.restype = ctypes.c_int
             lib.sdm_profile_enable.argtypes = [ctypes.c_int32]
             lib.sdm_profile_read.restype = ctypes.c_int
             lib.sdm_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
@@ -365,6 +371,131 @@ def sdm_layer_forward(x, w_in, a_log, dt_bias, w_out, subkeys, bank, *, heads, w
                                     _ptr(subkeys), _ptr(initial_bank), _ptr(bank), _ptr(y), _ptr(widx), _ptr(ridx), _ptr(ws),
                                     0 if ws is None else ws.numel(), _stream(x.device)))
     return (y, widx, ridx, ws) if return_workspace else (y, widx, ridx)
+
+
+def _layer_config(x, bank, heads, widths, dk, num_writes, num_reads, chunk_size, snapshot_dtype=0,
+                  grad_bank_dtype=0):
+    B, T, Dm = x.shape
+    ld = _bank_ld(bank, "bank")
+    lc = SdmLayerConfig()
+    lc.op = make_config(B, T, int(heads), widths, dk, bank.shape[-1], num_writes, num_reads, chunk_size, SDM_BF16,
+                        _dt(bank), bank.shape[2], ld, snapshot_dtype=snapshot_dtype, grad_bank_dtype=grad_bank_dtype)
+    lc.model_dim = int(Dm)
+    return lc
+
+
+def _check_layer_args(x, w_in, a_log, dt_bias, w_out, subkeys, bank, heads, widths):
+    B, T, Dm = x.shape
+    H = int(heads)
+    dk = subkeys.shape[-1]
+    d = bank.shape[-1]
+    _need(x, "x", None, torch.bfloat16)
+    _need(w_in, "w_in", (layer_in_features(H, widths, dk, d), Dm), torch.bfloat16)
+    _need(a_log, "a_log", (H,), torch.float32)
+    _need(dt_bias, "dt_bias", (H,), torch.float32)
+    _need(w_out, "w_out", (Dm, H * d), torch.bfloat16)
+    _need(subkeys, "subkeys", (H, sum(widths), dk), torch.bfloat16)
+    if bank.dim() != 4 or bank.shape[0] != B or bank.shape[1] != H:
+        raise ValueError(f"bank has shape {tuple(bank.shape)}, expected ({B}, {H}, bank_rows, d)")
+    return B, T, Dm, H, dk, d
+
+
+def layer_backward_workspace_size(lc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().sdm_layer_backward_workspace_size(ctypes.byref(lc), ctypes.byref(n)))
+    return n.value
+
+
+def sdm_layer_forward_save(x, w_in, a_log, dt_bias, w_out, subkeys, bank, *, heads, widths, num_writes, num_reads,
+                           chunk_size, initial_bank=None, snapshot_quant="none", want_index=False, y=None,
+                           snapshot=None, workspace=None):
+    """The layer's training forward: sdm_layer_forward with the op saving its backward snapshot. Returns (y, snapshot,
+    workspace, write_idx, read_idx); pass the snapshot and the workspace (uint8, layer_backward_workspace_size
+    bytes; do not reuse it in between) to sdm_layer_backward."""
+    B, T, Dm, H, dk, d = _check_layer_args(x, w_in, a_log, dt_bias, w_out, subkeys, bank, heads, widths)
+    scode, sdt = _snapshot_dtype(snapshot_quant, bank)
+    lc = _layer_config(x, bank, H, widths, dk, num_writes, num_reads, chunk_size, snapshot_dtype=scode)
+    if initial_bank is not None:
+        if tuple(initial_bank.shape) != (H,) + tuple(bank.shape[2:]) or initial_bank.dtype != bank.dtype or \
+                _bank_ld(initial_bank.unsqueeze(0), "initial_bank") != lc.op.bank_row_stride:
+            raise ValueError("initial_bank must be [heads, bank_rows, d] with the bank's dtype and row stride")
+    ws = _workspace(layer_backward_workspace_size(lc), x.device, workspace)
+    shp = _snapshot_shape(lc.op, scode, B, H, T, num_writes, d)
+    if snapshot is None:
+        snapshot = torch.empty(shp, dtype=sdt, device=x.device)
+    _need(snapshot, "snapshot", shp, sdt)
+    if y is None:
+        y = torch.empty((B, T, Dm), dtype=torch.bfloat16, device=x.device)
+    _need(y, "y", (B, T, Dm), torch.bfloat16)
+    widx = torch.empty((B, T, H, num_writes), dtype=torch.int32, device=x.device) if want_index else None
+    ridx = torch.empty((B, T, H, num_reads), dtype=torch.int32, device=x.device) if want_index else None
+    _check(load().sdm_layer_forward_save(ctypes.byref(lc), _ptr(x), _ptr(w_in), _ptr(a_log), _ptr(dt_bias),
+                                         _ptr(w_out), _ptr(subkeys), _ptr(initial_bank), _ptr(bank), _ptr(y),
+                                         _ptr(snapshot), _ptr(widx), _ptr(ridx), _ptr(ws), ws.numel(),
+                                         _stream(x.device)))
+    return y, snapshot, ws, widx, ridx
+
+
+def sdm_layer_backward(x, w_in, a_log, dt_bias, w_out, subkeys, bank, snapshot, grad_y, workspace, grad_bank=None, *,
+                       heads, widths, num_writes, num_reads, chunk_size, snapshot_quant="none",
+                       grad_bank_dtype=torch.float32):
+    """Backward of the layer (after sdm_layer_forward_save with the same arguments; bank as it left it, stepped back
+    here). grad_y [B, T, Dm] bfloat16; grad_bank (the bank's shape and strides, float32 or bfloat16 on a bfloat16
+    bank) the gradient w.r.t. the bank after the forward (None: zeros), replaced by the one w.r.t. the bank the op
+    started from. Returns float32 gradients x, w_in, a_log, dt_bias, w_out, subkeys, and bank (grad_bank)."""
+    B, T, Dm, H, dk, d = _check_layer_args(x, w_in, a_log, dt_bias, w_out, subkeys, bank, heads, widths)
+    _need(grad_y, "grad_y", (B, T, Dm), torch.bfloat16)
+    scode, sdt = _snapshot_dtype(snapshot_quant, bank)
+    dev = x.device
+    ld = _bank_ld(bank, "bank")
+    if grad_bank is None:
+        grad_bank = torch.zeros((B, H, bank.shape[2], ld), dtype=grad_bank_dtype, device=dev)[..., :d]
+    if grad_bank.dtype not in (torch.float32, torch.bfloat16) or tuple(grad_bank.shape) != tuple(bank.shape) or \
+            grad_bank.stride() != bank.stride():
+        raise ValueError("grad_bank must be float32 or bfloat16 with the bank's shape and strides")
+    lc = _layer_config(x, bank, H, widths, dk, num_writes, num_reads, chunk_size, snapshot_dtype=scode,
+                       grad_bank_dtype=_dt(grad_bank))
+    _need(snapshot, "snapshot", _snapshot_shape(lc.op, scode, B, H, T, num_writes, d), sdt)
+    f32 = torch.float32
+    g = {"x": torch.empty((B, T, Dm), dtype=f32, device=dev), "w_in": torch.empty(tuple(w_in.shape), dtype=f32,
+                                                                                 device=dev),
+         "a_log": torch.empty((H,), dtype=f32, device=dev), "dt_bias": torch.empty((H,), dtype=f32, device=dev),
+         "w_out": torch.empty((Dm, H * d), dtype=f32, device=dev),
+         "subkeys": torch.empty(tuple(subkeys.shape), dtype=f32, device=dev), "bank": grad_bank}
+    _check(load().sdm_layer_backward(ctypes.byref(lc), _ptr(x), _ptr(w_in), _ptr(a_log), _ptr(dt_bias), _ptr(w_out),
+                                     _ptr(subkeys), _ptr(bank), _ptr(snapshot), _ptr(grad_y), _ptr(grad_bank),
+                                     _ptr(g["x"]), _ptr(g["w_in"]), _ptr(g["a_log"]), _ptr(g["dt_bias"]),
+                                     _ptr(g["w_out"]), _ptr(g["subkeys"]), _ptr(workspace), workspace.numel(),
+                                     _stream(dev)))
+    return g
+
+
+def layer_backward_workspace_views(x_shape, heads, widths, subkey_dim, head_dim, lc, ws):
+    """Views of what sdm_layer_backward leaves in its workspace after the forward's regions (include/sdm.h): d o
+    [B, T, H, d] bf16, the op's float32 gradients d keys, d queries [B, T, H, F dk], d values [B, T, H, d], d alpha,
+    d beta [B, T, H], and d p [B, T, Np] bf16 (Np: the input map's width rounded up to 64)."""
+    B, T, _ = x_shape
+    H, P, d = int(heads), len(widths) * int(subkey_dim), int(head_dim)
+    al = lambda n: (n + 255) // 256 * 256
+    off = 0
+    for n in (B * T * H * P * 2, B * T * H * P * 2, B * T * H * d * 2, B * T * 2 * H * 2, B * T * H * 2,
+              B * T * H * 2, B * T * H * d * 2):
+        off = al(off + n)
+    opsize = max(workspace_size(lc.op, SDM_OP_WRITE_READ), workspace_size(lc.op, SDM_OP_BACKWARD))
+    off = al(off + opsize)
+    nin = 2 * H * P + H * d + 2 * H
+    Np = (nin + 63) // 64 * 64
+    out = {}
+    for name, shp, dt, es in (("d_o", (B, T, H, d), torch.bfloat16, 2), ("d_keys", (B, T, H, P), torch.float32, 4),
+                              ("d_queries", (B, T, H, P), torch.float32, 4), ("d_values", (B, T, H, d), torch.float32, 4),
+                              ("d_alpha", (B, T, H), torch.float32, 4), ("d_beta", (B, T, H), torch.float32, 4),
+                              ("d_p", (B, T, Np), torch.bfloat16, 2)):
+        n = 1
+        for v in shp:
+            n *= v
+        out[name] = ws[off:off + es * n].view(dt).view(shp)
+        off = al(off + es * n)
+    return out
 
 
 def layer_workspace_views(x_shape, heads, widths, subkey_dim, head_dim, ws):

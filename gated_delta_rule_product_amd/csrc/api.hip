@@ -949,7 +949,10 @@ sdm_status sdm_decode_step_noalloc(const sdm_config* cfg, const void* write_keys
 // ------------------------------------------------------------------------------------------- layer (forward)
 namespace {
 struct LayerWs {
-  size_t keys, queries, values, gin, alpha, beta, o, op, total;
+  size_t keys, queries, values, gin, alpha, beta, o, op, total;  // the forward (total: its workspace bytes)
+  size_t opsize;                                                // the op region with the backward
+  size_t dO, gk, gq, gv, gal, gbe, dp, tparam, w_outT, gyT, oT, xT, w_inT, dpT, btotal;  // the backward
+  long long Mp, Np;                                             // B T and the input map's width, padded to 64
 };
 sdm_status layer_layout(const sdm_layer_config* cfg, LayerWs* L) {
   if (!cfg) return fail(SDM_ERR_NULL, "cfg must not be NULL");
@@ -980,6 +983,35 @@ sdm_status layer_layout(const sdm_layer_config* cfg, LayerWs* L) {
   L->o = take((size_t)(M * H * d * 2));
   L->op = take(opws);
   L->total = o;
+  // the backward: the same prefix, the op region large enough for the op's backward, then its own regions (none
+  // when the op has no backward for these settings: btotal 0, and the training calls refuse)
+  size_t opb = 0;
+  if (sdm_workspace_size(&cfg->op, SDM_OP_BACKWARD, 0, &opb) != SDM_OK) {
+    L->opsize = opws;
+    L->btotal = 0;
+    return SDM_OK;
+  }
+  L->opsize = opb > opws ? opb : opws;
+  o = L->op;
+  take(L->opsize);
+  const long long nin = 2 * H * P + H * d + 2 * H;
+  L->Mp = (M + 63) / 64 * 64;
+  L->Np = (nin + 63) / 64 * 64;
+  L->dO = take((size_t)(M * H * d * 2));
+  L->gk = take((size_t)(M * H * P * 4));
+  L->gq = take((size_t)(M * H * P * 4));
+  L->gv = take((size_t)(M * H * d * 4));
+  L->gal = take((size_t)(M * H * 4));
+  L->gbe = take((size_t)(M * H * 4));
+  L->dp = take((size_t)(M * L->Np * 2));
+  L->tparam = take((size_t)(2 * M * H * 4));
+  L->w_outT = take((size_t)(H * d * Dm * 2));
+  L->gyT = take((size_t)(Dm * L->Mp * 2));
+  L->oT = take((size_t)(H * d * L->Mp * 2));
+  L->xT = take((size_t)(Dm * L->Mp * 2));
+  L->w_inT = take((size_t)(Dm * L->Np * 2));
+  L->dpT = take((size_t)(L->Np * L->Mp * 2));
+  L->btotal = o;
   return SDM_OK;
 }
 }  // namespace
@@ -992,10 +1024,11 @@ sdm_status sdm_layer_workspace_size(const sdm_layer_config* cfg, size_t* bytes) 
   return ok();
 }
 
-sdm_status sdm_layer_forward(const sdm_layer_config* cfg, const void* x, const void* w_in, const float* a_log,
-                             const float* dt_bias, const void* w_out, const void* subkeys, const void* initial_bank,
-                             void* bank, void* y, int32_t* write_idx, int32_t* read_idx, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+namespace {
+sdm_status layer_forward_impl(const sdm_layer_config* cfg, const void* x, const void* w_in, const float* a_log,
+                              const float* dt_bias, const void* w_out, const void* subkeys, const void* initial_bank,
+                              void* bank, void* y, void* snapshot, int32_t* write_idx, int32_t* read_idx,
+                              void* workspace, size_t workspace_bytes, void* stream) {
   LayerWs L;
   TRY(layer_layout(cfg, &L));
   const sdm_config& oc = cfg->op;
@@ -1033,12 +1066,15 @@ sdm_status sdm_layer_forward(const sdm_layer_config* cfg, const void* x, const v
                        {w_out, (size_t)(Dm * H * d * 2), "w_out"},
                        {subkeys, (size_t)(H * sumn * oc.subkey_dim * 2), "subkeys"},
                        {initial_bank, (size_t)H * (size_t)oc.bank_rows * (size_t)ld * eb, "initial_bank"}};
+  size_t snap_bytes = 0;
+  if (snapshot) TRY(sdm_snapshot_bytes(&oc, &snap_bytes));
   const Range outs[] = {{y, (size_t)(M * Dm * 2), "y"},
                         {workspace, L.total, "workspace"},
                         {bank, bank_bytes, "bank"},
                         {write_idx, (size_t)(M * H * oc.num_writes * 4), "write_idx"},
-                        {read_idx, (size_t)(M * H * oc.num_reads * 4), "read_idx"}};
-  TRY(check_alias(outs, 5, ins, 7));
+                        {read_idx, (size_t)(M * H * oc.num_reads * 4), "read_idx"},
+                        {snapshot, snap_bytes, "snapshot"}};
+  TRY(check_alias(outs, 6, ins, 7));
   TRY(check_device());
   if (M == 0 || H == 0) return ok();
   hipStream_t st = (hipStream_t)stream;
@@ -1074,7 +1110,7 @@ sdm_status sdm_layer_forward(const sdm_layer_config* cfg, const void* x, const v
                                          st),
                    "bank copy launch"));
   }
-  TRY(write_read_impl(&oc, keys, queries, values, alpha, beta, subkeys, bank, o, nullptr, write_idx, read_idx,
+  TRY(write_read_impl(&oc, keys, queries, values, alpha, beta, subkeys, bank, o, snapshot, write_idx, read_idx,
                       ws + L.op, workspace_bytes - L.op, stream));
   GemmArgs go;
   memset(&go, 0, sizeof go);
@@ -1086,6 +1122,165 @@ sdm_status sdm_layer_forward(const sdm_layer_config* cfg, const void* x, const v
   go.nseg = 1;
   go.seg[0] = {(int)Dm, (bf16_t*)y, (int)Dm};
   TRY(hip_status(timed(SDM_K_DENSE, st, [&] { return launch_gemm_bf16(go, st); }), "output projection launch"));
+  return ok();
+}
+}  // namespace
+
+sdm_status sdm_layer_forward(const sdm_layer_config* cfg, const void* x, const void* w_in, const float* a_log,
+                             const float* dt_bias, const void* w_out, const void* subkeys, const void* initial_bank,
+                             void* bank, void* y, int32_t* write_idx, int32_t* read_idx, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return layer_forward_impl(cfg, x, w_in, a_log, dt_bias, w_out, subkeys, initial_bank, bank, y, nullptr, write_idx,
+                            read_idx, workspace, workspace_bytes, stream);
+}
+
+sdm_status sdm_layer_forward_save(const sdm_layer_config* cfg, const void* x, const void* w_in, const float* a_log,
+                                  const float* dt_bias, const void* w_out, const void* subkeys,
+                                  const void* initial_bank, void* bank, void* y, void* snapshot, int32_t* write_idx,
+                                  int32_t* read_idx, void* workspace, size_t workspace_bytes, void* stream) {
+  if (cfg && (long long)cfg->op.batch * cfg->op.tokens * cfg->op.heads > 0 && !snapshot)
+    return fail(SDM_ERR_NULL, "snapshot is NULL");
+  size_t need_ws = 0;
+  TRY(sdm_layer_backward_workspace_size(cfg, &need_ws));
+  TRY(check_ws(workspace, workspace_bytes, need_ws));  // the backward's workspace: the backward reads this one
+  return layer_forward_impl(cfg, x, w_in, a_log, dt_bias, w_out, subkeys, initial_bank, bank, y, snapshot,
+                            write_idx, read_idx, workspace, workspace_bytes, stream);
+}
+
+sdm_status sdm_layer_backward_workspace_size(const sdm_layer_config* cfg, size_t* bytes) {
+  if (!bytes) return fail(SDM_ERR_NULL, "bytes must not be NULL");
+  LayerWs L;
+  TRY(layer_layout(cfg, &L));
+  if (L.btotal == 0) {  // the op's own refusal, with its message
+    size_t opb = 0;
+    return sdm_workspace_size(&cfg->op, SDM_OP_BACKWARD, 0, &opb);
+  }
+  *bytes = L.btotal;
+  return ok();
+}
+
+sdm_status sdm_layer_backward(const sdm_layer_config* cfg, const void* x, const void* w_in, const float* a_log,
+                              const float* dt_bias, const void* w_out, const void* subkeys, void* bank,
+                              const void* snapshot, const void* grad_y, void* grad_bank, float* grad_x,
+                              float* grad_w_in, float* grad_a_log, float* grad_dt_bias, float* grad_w_out,
+                              float* grad_subkeys, void* workspace, size_t workspace_bytes, void* stream) {
+  LayerWs L;
+  TRY(layer_layout(cfg, &L));
+  size_t need_ws = 0;
+  TRY(sdm_layer_backward_workspace_size(cfg, &need_ws));
+  const sdm_config& oc = cfg->op;
+  const long long M = (long long)oc.batch * oc.tokens, H = oc.heads, d = oc.head_dim, Dm = cfg->model_dim;
+  const long long P = (long long)oc.num_factors * oc.subkey_dim, Hd = H * d;
+  const long long nin = 2 * H * P + Hd + 2 * H;
+  if (M > 0) {
+    const void* ptrs[] = {x, w_in, a_log, dt_bias, w_out, subkeys, bank, snapshot, grad_y, grad_bank, grad_x,
+                          grad_w_in, grad_a_log, grad_dt_bias, grad_w_out, grad_subkeys};
+    const char* names[] = {"x", "w_in", "a_log", "dt_bias", "w_out", "subkeys", "bank", "snapshot", "grad_y",
+                           "grad_bank", "grad_x", "grad_w_in", "grad_a_log", "grad_dt_bias", "grad_w_out",
+                           "grad_subkeys"};
+    for (int i = 0; i < 16; ++i) TRY(need(ptrs[i], names[i]));
+  }
+  const void* al[] = {x, w_in, w_out, grad_y, grad_x, grad_w_in, grad_w_out};
+  const char* an[] = {"x", "w_in", "w_out", "grad_y", "grad_x", "grad_w_in", "grad_w_out"};
+  for (int i = 0; i < 7; ++i) TRY(aligned(al[i], 16, an[i]));
+  TRY(check_ws(workspace, workspace_bytes, L.btotal));
+  // the op's own checks (dtypes, snapshot route, gradient dtype, ...) before any launch
+  Dims D;
+  TopkPlan pw, pr;
+  TRY(validate(&oc, SDM_OP_BACKWARD, 0, &D, &pw, &pr));
+  int snap_mode = SNAP_BANK;
+  TRY(snapshot_kind(&oc, D, &snap_mode));
+  bool gb16 = false;
+  TRY(grad_bank_kind(&oc, D, true, &gb16));
+  long long sumn = 0;
+  for (int f = 0; f < oc.num_factors; ++f) sumn += oc.factor_widths[f];
+  const size_t nbank = (size_t)D.S * (size_t)D.rows * (size_t)D.ld;
+  const Range ins[] = {{x, (size_t)(M * Dm * 2), "x"},
+                       {w_in, (size_t)(nin * Dm * 2), "w_in"},
+                       {a_log, (size_t)H * 4, "a_log"},
+                       {dt_bias, (size_t)H * 4, "dt_bias"},
+                       {w_out, (size_t)(Dm * Hd * 2), "w_out"},
+                       {subkeys, (size_t)(H * sumn * oc.subkey_dim * 2), "subkeys"},
+                       {snapshot, snapshot_bytes(D, snap_mode), "snapshot"},
+                       {grad_y, (size_t)(M * Dm * 2), "grad_y"}};
+  const Range outs[] = {{bank, nbank * esize(D.bank), "bank"},
+                        {grad_bank, nbank * (gb16 ? 2 : 4), "grad_bank"},
+                        {grad_x, (size_t)(M * Dm * 4), "grad_x"},
+                        {grad_w_in, (size_t)(nin * Dm * 4), "grad_w_in"},
+                        {grad_a_log, (size_t)H * 4, "grad_a_log"},
+                        {grad_dt_bias, (size_t)H * 4, "grad_dt_bias"},
+                        {grad_w_out, (size_t)(Dm * Hd * 4), "grad_w_out"},
+                        {grad_subkeys, (size_t)(H * sumn * oc.subkey_dim * 4), "grad_subkeys"},
+                        {workspace, L.btotal, "workspace"}};
+  TRY(check_alias(outs, 9, ins, 8));
+  TRY(check_device());
+  if (M == 0 || H == 0) return ok();
+  hipStream_t st = (hipStream_t)stream;
+  unsigned char* ws = (unsigned char*)workspace;
+  const bf16_t* gy = (const bf16_t*)grad_y;
+  auto transpose = [&](const void* in, long long R, long long C, long long ldi, size_t off, long long Rp) {
+    return hip_status(timed(SDM_K_DENSE, st, [&] {
+                        return launch_transpose_bf16((const bf16_t*)in, (int)R, (int)C, ldi, (bf16_t*)(ws + off),
+                                                     (int)Rp, Rp, st);
+                      }),
+                      "transpose launch");
+  };
+  auto gemm = [&](const void* xa, size_t wt, long long m, long long n, long long k, void* dst, bool f32) {
+    GemmArgs g;
+    memset(&g, 0, sizeof g);
+    g.x = (const bf16_t*)xa;
+    g.w = (const bf16_t*)(ws + wt);
+    g.M = (int)m;
+    g.N = (int)n;
+    g.K = (int)k;
+    g.nseg = 1;
+    if (f32) {
+      g.f32 = (float*)dst;
+      g.f32ld = n;
+    } else {
+      g.seg[0] = {(int)n, (bf16_t*)dst, (int)n};
+    }
+    return hip_status(timed(SDM_K_DENSE, st, [&] { return launch_gemm_bf16(g, st); }), "dense map launch");
+  };
+  // the output map: d o = grad_y w_out (bfloat16), d w_out = grad_y^T o
+  TRY(transpose(w_out, Dm, Hd, Hd, L.w_outT, Dm));
+  TRY(transpose(grad_y, M, Dm, Dm, L.gyT, L.Mp));
+  TRY(transpose(ws + L.o, M, Hd, Hd, L.oT, L.Mp));
+  TRY(gemm(gy, L.w_outT, M, Hd, Dm, ws + L.dO, false));
+  TRY(gemm(ws + L.gyT, L.oT, Dm, Hd, L.Mp, grad_w_out, true));
+  // the op's backward on d o, from the activations the forward left in the workspace
+  TRY(sdm_write_read_backward(&oc, ws + L.keys, ws + L.queries, ws + L.values, ws + L.alpha, ws + L.beta, subkeys,
+                              bank, snapshot, ws + L.dO, grad_bank, (float*)(ws + L.gk), (float*)(ws + L.gq),
+                              (float*)(ws + L.gv), (float*)(ws + L.gal), (float*)(ws + L.gbe), grad_subkeys,
+                              ws + L.op, L.opsize, stream));
+  // the gates' derivatives and d p (bfloat16), then the input map: d x = d p w_in, d w_in = d p^T x
+  GateBwdArgs ga;
+  ga.gk = (const float*)(ws + L.gk);
+  ga.gq = (const float*)(ws + L.gq);
+  ga.gv = (const float*)(ws + L.gv);
+  ga.galpha = (const float*)(ws + L.gal);
+  ga.gbeta = (const float*)(ws + L.gbe);
+  ga.gin = (const bf16_t*)(ws + L.gin);
+  ga.a_log = a_log;
+  ga.dt_bias = dt_bias;
+  ga.dp = (bf16_t*)(ws + L.dp);
+  ga.tparam = (float*)(ws + L.tparam);
+  ga.M = M;
+  ga.H = (int)H;
+  ga.HP = (int)(H * P);
+  ga.Hd = (int)Hd;
+  ga.ldp = (int)L.Np;
+  TRY(hip_status(timed(SDM_K_DENSE, st, [&] { return launch_layer_grad_assemble(ga, st); }), "gate gradient launch"));
+  TRY(hip_status(timed(SDM_K_DENSE, st, [&] {
+                   return launch_layer_param_sums((const float*)(ws + L.tparam), M, (int)H, grad_a_log, grad_dt_bias,
+                                                  st);
+                 }),
+                 "gate parameter sum launch"));
+  TRY(transpose(w_in, nin, Dm, Dm, L.w_inT, L.Np));
+  TRY(transpose(ws + L.dp, M, L.Np, L.Np, L.dpT, L.Mp));
+  TRY(transpose(x, M, Dm, Dm, L.xT, L.Mp));
+  TRY(gemm(ws + L.dp, L.w_inT, M, Dm, L.Np, grad_x, true));
+  TRY(gemm(ws + L.dpT, L.xT, nin, Dm, L.Mp, grad_w_in, true));
   return ok();
 }
 

@@ -28,6 +28,21 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float gemm_f32x4_t;
 __device__ __forceinline__ void gemm_store(const GemmArgs& g, const gemm_f32x4_t (&acc)[4][4], int m0, int n0,
                                            int lane) {
   const int ql = lane & 15;
+  if (g.f32) {  // float32 results (parameter and input gradients)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + 16 * j + ql;
+      if (n >= g.N) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = m0 + 16 * i + 4 * (lane >> 4) + r;
+          if (m < g.M) g.f32[(long long)m * g.f32ld + n] = acc[i][j][r];
+        }
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int n = n0 + 16 * j + ql;
@@ -217,6 +232,98 @@ __global__ __launch_bounds__(256) void gates_kernel(const bf16_t* ga, const bf16
   const float decay = expf(a_log[h]) * softplus_f(a + dt_bias[h]);
   alpha[s] = f_to_bf16(expf(-decay));
   beta[s] = f_to_bf16(1.0f / (1.0f + expf(-b)));
+}
+
+// A 64 x 64 tile per workgroup through LDS (rows padded to 65 elements): reads coalesced along in's rows, writes
+// along out's rows.
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16_t* in, int R, int C, long long ldi,
+                                                             bf16_t* out, int Rp, long long ldo) {
+  __shared__ bf16_t t[64][65];
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;  // 64 x 4 threads
+  for (int i = ty; i < 64; i += 4) {
+    const int r = r0 + i, c = c0 + tx;
+    t[i][tx] = (r < R && c < C) ? in[(long long)r * ldi + c] : (bf16_t)0;
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int c = c0 + i, r = r0 + tx;
+    if (c < C && r < Rp) out[(long long)c * ldo + r] = t[tx][i];
+  }
+}
+
+hipError_t launch_transpose_bf16(const bf16_t* in, int R, int C, long long ldi, bf16_t* out, int Rp, long long ldo,
+                                 hipStream_t st) {
+  if (C == 0 || Rp == 0) return hipSuccess;
+  hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)((C + 63) / 64), (unsigned)((Rp + 63) / 64)), dim3(256),
+                     0, st, in, R, C, ldi, out, Rp, ldo);
+  return hipGetLastError();
+}
+
+// One thread per element of d p. The gate derivatives in float32 from the bfloat16 gate inputs (alpha recomputed,
+// not the rounded one): z = a + dt_bias, A = exp(a_log), d a = d alpha * alpha * (-A) * sigmoid(z),
+// d b = d beta * beta * (1 - beta); the d a_log term d alpha * alpha * (-A * softplus(z)).
+__global__ __launch_bounds__(256) void layer_grad_assemble_kernel(GateBwdArgs g) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= g.M * g.ldp) return;
+  const long long m = i / g.ldp;
+  const int c = (int)(i - m * g.ldp);
+  const int HP = g.HP, Hd = g.Hd, H = g.H;
+  float v = 0.f;
+  if (c < HP) {
+    v = g.gk[m * HP + c];
+  } else if (c < 2 * HP) {
+    v = g.gq[m * HP + c - HP];
+  } else if (c < 2 * HP + Hd) {
+    v = g.gv[m * Hd + c - 2 * HP];
+  } else if (c < 2 * HP + Hd + H) {
+    const int h = c - 2 * HP - Hd;
+    const float a = bf16_to_f(g.gin[m * 2 * H + h]);
+    const float z = a + g.dt_bias[h], A = expf(g.a_log[h]);
+    const float sp = softplus_f(z), alpha = expf(-A * sp), sig = 1.0f / (1.0f + expf(-z));
+    const float da = g.galpha[m * H + h];
+    v = da * alpha * (-A) * sig;
+    g.tparam[m * H + h] = da * alpha * (-A * sp);
+    g.tparam[g.M * H + m * H + h] = v;
+  } else if (c < 2 * HP + Hd + 2 * H) {
+    const int h = c - 2 * HP - Hd - H;
+    const float b = bf16_to_f(g.gin[m * 2 * H + H + h]);
+    const float beta = 1.0f / (1.0f + expf(-b));
+    v = g.gbeta[m * H + h] * beta * (1.0f - beta);
+  }
+  g.dp[i] = f_to_bf16(v);
+}
+
+hipError_t launch_layer_grad_assemble(const GateBwdArgs& g, hipStream_t st) {
+  const long long n = g.M * g.ldp;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(layer_grad_assemble_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, g);
+  return hipGetLastError();
+}
+
+// One workgroup per (head, parameter): thread t adds rows t, t + 256, ... in order, then a fixed tree over threads.
+__global__ __launch_bounds__(256) void layer_param_sums_kernel(const float* tparam, long long M, int H,
+                                                               float* grad_a_log, float* grad_dt_bias) {
+  __shared__ float s[256];
+  const int h = blockIdx.x, which = blockIdx.y, t = threadIdx.x;
+  const float* src = tparam + (long long)which * M * H + h;
+  float acc = 0.f;
+  for (long long m = t; m < M; m += 256) acc += src[m * H];
+  s[t] = acc;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (t < o) s[t] += s[t + o];
+    __syncthreads();
+  }
+  if (t == 0) (which == 0 ? grad_a_log : grad_dt_bias)[h] = s[0];
+}
+
+hipError_t launch_layer_param_sums(const float* tparam, long long M, int H, float* grad_a_log, float* grad_dt_bias,
+                                   hipStream_t st) {
+  if (H == 0) return hipSuccess;
+  hipLaunchKernelGGL(layer_param_sums_kernel, dim3((unsigned)H, 2), dim3(256), 0, st, tparam, M, H, grad_a_log,
+                     grad_dt_bias);
+  return hipGetLastError();
 }
 
 // One thread per 16-byte piece of a slot row of one head: the piece is read once and stored into every batch row.

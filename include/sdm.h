@@ -293,6 +293,42 @@ sdm_status sdm_layer_forward(const sdm_layer_config* cfg, const void* x, const v
                              void* bank, void* y, int32_t* write_idx, int32_t* read_idx, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* Training forward of the layer (CHANGELOG 2.0.0: training saves a backward snapshot): sdm_layer_forward with the
+ * op run as sdm_write_read_save (cfg.op.snapshot_dtype; `snapshot` of sdm_snapshot_bytes(&cfg.op)). The workspace
+ * must be sdm_layer_backward_workspace_size bytes: its first part is the forward's (same layout), and
+ * sdm_layer_backward reads the activations the call leaves there, so it must be passed to the backward untouched. */
+sdm_status sdm_layer_forward_save(const sdm_layer_config* cfg, const void* x, const void* w_in, const float* a_log,
+                                  const float* dt_bias, const void* w_out, const void* subkeys,
+                                  const void* initial_bank, void* bank, void* y, void* snapshot, int32_t* write_idx,
+                                  int32_t* read_idx, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of sdm_layer_forward_save and sdm_layer_backward. */
+sdm_status sdm_layer_backward_workspace_size(const sdm_layer_config* cfg, size_t* bytes);
+
+/* Backward of the layer (the chain rule through sdm_layer_forward's steps, last first; README model wiring: the layer
+ * is trained end to end). Inputs: the forward's x, w_in, a_log, dt_bias, w_out, subkeys, `bank` as the forward left
+ * it (the op's backward steps it back to the bank the op started from, as sdm_write_read_backward), its snapshot,
+ * grad_y [B, T, Dm] bfloat16 (the gradient w.r.t. y), and the workspace of the sdm_layer_forward_save call.
+ * Every tensor between the steps being bfloat16, the gradients passed between them are rounded to bfloat16 too:
+ *   d o = grad_y w_out (bfloat16, [B, T, H d])              d w_out = grad_y^T o       (grad_w_out [Dm, H d])
+ *   the op's backward on d o (sdm_write_read_backward; grad_bank as there, in and out, cfg.op.grad_bank_dtype)
+ *   d a = d alpha alpha (-exp(a_log)) sigmoid(a + dt_bias),  d b = d beta beta (1 - beta)   (float32; alpha and
+ *     beta recomputed from the bfloat16 gate inputs), grad_a_log[h] = sum of d alpha alpha (-exp(a_log) softplus),
+ *     grad_dt_bias[h] = sum of d a (over every token row, a fixed order)
+ *   d p = [d keys | d queries | d values | d a | d b] rounded to bfloat16 ([B, T, N_in], the input map's layout)
+ *   d x = d p w_in (grad_x [B, T, Dm])                      d w_in = d p^T x           (grad_w_in [N_in, Dm])
+ * grad_subkeys [H, sum n_f, dk] is the op's. Every gradient output is float32 and overwritten (grad_bank excepted).
+ * Dense maps accumulate in float32 on the matrix cores. A learned initial bank's gradient is sdm_bank_grad_sum of
+ * grad_bank. Workspace regions after the forward's (each at a 256-byte multiple, in this order): the op's region
+ * (large enough for its backward), d o [B, T, H d] bfloat16, the op's gradients d keys, d queries [B, T, H P],
+ * d values [B, T, H d], d alpha, d beta [B, T, H] (float32), d p [B, T, Np] bfloat16 (Np: N_in rounded up to 64,
+ * zero columns past N_in), then scratch. */
+sdm_status sdm_layer_backward(const sdm_layer_config* cfg, const void* x, const void* w_in, const float* a_log,
+                              const float* dt_bias, const void* w_out, const void* subkeys, void* bank,
+                              const void* snapshot, const void* grad_y, void* grad_bank, float* grad_x,
+                              float* grad_w_in, float* grad_a_log, float* grad_dt_bias, float* grad_w_out,
+                              float* grad_subkeys, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Gradient of a learned initial bank copied into every batch row (sdm_layer_forward's initial_bank): grad_initial_bank
  * [H, bank_rows, bank_row_stride] float32 receives, for every head h, slot j < N and column c < head_dim, the sum over
  * b = 0, 1, ..., B - 1 (in that order, float32) of grad_bank[b, h, j, c] (grad_bank: sdm_write_read_backward's

@@ -229,3 +229,141 @@ def test_bank_grad_sum():
     bound = (B - 1) * 2.0 ** -24 * np.abs(gb_np[:, :, :N].astype(np.float64)).sum(axis=0) * 1.01
     assert np.all(np.abs(got - ref) <= bound)
     assert bool((obuf[:, N:] == 5.0).all()) and bool((obuf[..., d:] == 5.0).all())
+
+
+# ---------------------------------------------------------------------------------------------------------- backward
+# The layer's backward (sdm_layer_forward_save + sdm_layer_backward), step by step on the GPU's own intermediates,
+# each against the oracle's definition of that step (oracle/layer_oracle.py: layer_backward):
+#   d o       bfloat16(grad_y w_out): the dense-map bound above (K = Dm)
+#   d w_out   grad_y^T o (float32 result): |err| <= K 2^-24 S, K = B T, S = sum |terms| (float32 sums in any order)
+#   the op    sdm_oracle's backward with its a-priori bounds (write_read_backward_bounds) on the GPU's keys, queries,
+#             values, gates and d o, after the bound's hypothesis (the GPU's forward rows within the op's tolerance)
+#   d p       its key, query and value columns the GPU's own float32 gradients rounded to nearest even (bit for
+#             bit); its gate columns against gates_backward on the GPU's d alpha, d beta and gate inputs: one
+#             bfloat16 rounding plus a float32 evaluation of exp, log1p and a few products (EVAL u (1 + |A softplus|)
+#             relative, EVAL = 16)
+#   d a_log, d dt_bias   the same terms summed in float32 over B T rows: (B T 2^-24 + EVAL u (1 + max |A softplus|))
+#             times the sum of the terms' magnitudes
+#   d x, d w_in   d p w_in and d p^T x in float32: K 2^-24 S (K = the padded input width, or B T)
+# and the bank stepped back to its state before the forward bit for bit.
+EVAL = 16
+U32 = 2.0 ** -24
+EPS_ROW = {"f32": 1e-5, "bf16": 2e-2}
+
+
+def f32_ok(got, ref, S, K):
+    bound = 1.01 * K * U32 * S + 1e-30
+    return float((np.abs(np.asarray(got, np.float64) - ref) / bound).max())
+
+
+BWD_CASES = {
+    # float32 bank, model width 64 (every dense map on the LDS-tiled kernel)
+    "small": (synth.Shape(2, 40, 2, (16, 16), 8, 32, 8, 8, 16, "bf16", "f32"), 64),
+    # bfloat16 bank, model width 96 (d o's map, K = 96, on the register-only kernel), ragged chunk
+    "bf16_bank_w96": (synth.Shape(1, 36, 2, (8, 8), 8, 32, 6, 5, 8, "bf16", "bf16"), 96),
+}
+
+
+@pytest.mark.parametrize("name", list(BWD_CASES))
+def test_layer_backward_steps_against_oracle(name):
+    s, Dm = BWD_CASES[name]
+    bank_dt = torch.float32 if s.bank == "f32" else torch.bfloat16
+    x = synth.make_layer_inputs(s, Dm, 3)
+    rng = np.random.default_rng(31)
+    gy_np = synth.round_bf16_rne(rng.standard_normal((s.batch, s.tokens, Dm)).astype(np.float32))
+    gb_np = rng.standard_normal((s.batch, s.heads, s.rows, s.head_dim)).astype(np.float32)
+    t = {k: to_dev(x[k], torch.bfloat16) for k in ("x", "w_in", "w_out", "subkeys")}
+    t.update({k: to_dev(x[k], torch.float32) for k in ("a_log", "dt_bias")})
+    bank = to_dev(x["bank"], bank_dt)
+    bank0 = bank.clone()
+    kw = dict(heads=s.heads, widths=s.widths, num_writes=s.num_writes, num_reads=s.num_reads, chunk_size=s.chunk_size)
+    print(f"layer backward {name}: {s} Dm {Dm}", flush=True)
+    y, snap, ws, widx, ridx = binding.sdm_layer_forward_save(t["x"], t["w_in"], t["a_log"], t["dt_bias"], t["w_out"],
+                                                             t["subkeys"], bank, want_index=True, **kw)
+    torch.cuda.synchronize()
+    fv = {k: to_np(v) for k, v in binding.layer_workspace_views(x["x"].shape, s.heads, s.widths, s.subkey_dim,
+                                                                s.head_dim, ws).items()}
+    fwd_bank = to_np(bank)
+    fwd_snap = to_np(snap)
+    gbank = to_dev(gb_np, torch.float32)
+    g = binding.sdm_layer_backward(t["x"], t["w_in"], t["a_log"], t["dt_bias"], t["w_out"], t["subkeys"], bank, snap,
+                                   to_dev(gy_np, torch.bfloat16), ws, gbank, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(bank, bank0), "the backward did not restore the bank bit for bit"
+    lc = binding._layer_config(t["x"], bank, s.heads, s.widths, s.subkey_dim, s.num_writes, s.num_reads,
+                               s.chunk_size)
+    bv = {k: to_np(v) for k, v in binding.layer_backward_workspace_views(x["x"].shape, s.heads, s.widths,
+                                                                         s.subkey_dim, s.head_dim, lc, ws).items()}
+    got = {k: to_np(v) for k, v in g.items()}
+    B, T, H, d, P = s.batch, s.tokens, s.heads, s.head_dim, len(s.widths) * s.subkey_dim
+    M = B * T
+    gy = gy_np.astype(np.float64)
+    w_out = x["w_out"].astype(np.float64)
+    o = fv["o"].reshape(B, T, H * d).astype(np.float64)
+    # the output map
+    r = dense_ok(bv["d_o"].reshape(B, T, H * d), gy, w_out.T)
+    assert r <= 1.0, f"d o beyond its bound ({r:.3g})"
+    ref = np.einsum("btn,btk->nk", gy, o)
+    S = np.einsum("btn,btk->nk", np.abs(gy), np.abs(o))
+    r = f32_ok(got["w_out"], ref, S, M)
+    assert r <= 1.0, f"d w_out beyond its bound ({r:.3g})"
+    # the op's backward on the GPU's own inputs
+    ob = oracle.write_read_backward_bounds(fv["keys"], fv["queries"], fv["values"], fv["alpha"], fv["beta"],
+                                           x["subkeys"], x["bank"], bv["d_o"], gb_np, s.widths, s.num_writes,
+                                           s.num_reads, eps_row=EPS_ROW[s.bank], bank_bf16=s.bank == "bf16",
+                                           want_snapshot=True)
+    assert np.array_equal(to_np(widx), ob_ids(fv, x, s)[0]) and np.array_equal(to_np(ridx), ob_ids(fv, x, s)[1])
+    for gpu_rows, ref_rows, what in ((fwd_snap, ob["snapshot"], "snapshot"), (fwd_bank, ob["bank"], "bank")):
+        gr = np.asarray(gpu_rows, np.float64).reshape(-1, d)
+        rr = np.asarray(ref_rows, np.float64).reshape(-1, d)
+        allow = EPS_ROW[s.bank] * np.abs(rr).max(axis=1, keepdims=True)
+        assert np.all(np.abs(gr - rr) <= allow), f"the forward's {what} rows beyond the op's tolerance"
+    pairs = (("d_keys", "wkeys"), ("d_queries", "rq"), ("d_values", "values"), ("d_alpha", "alpha"),
+             ("d_beta", "beta"))
+    for gk, ok in pairs:
+        err = np.abs(bv[gk].astype(np.float64) - ob["d_" + ok])
+        assert np.all(err <= 1.01 * ob["e_" + ok] + 1e-30), f"op gradient {gk} beyond its bound"
+    for gk, ok in (("subkeys", "subkeys"), ("bank", "bank")):
+        err = np.abs(got[gk].astype(np.float64) - ob["d_" + ok])
+        assert np.all(err <= 1.01 * ob["e_" + ok] + 1e-30), f"gradient {gk} beyond its bound"
+    # d p: the op's gradients rounded, then the gate inputs' gradients
+    dp = bv["d_p"].reshape(M, -1).astype(np.float64)
+    HP, Hd = H * P, H * d
+    np.testing.assert_array_equal(dp[:, :HP], synth.round_bf16_rne(bv["d_keys"].reshape(M, HP)))
+    np.testing.assert_array_equal(dp[:, HP:2 * HP], synth.round_bf16_rne(bv["d_queries"].reshape(M, HP)))
+    np.testing.assert_array_equal(dp[:, 2 * HP:2 * HP + Hd], synth.round_bf16_rne(bv["d_values"].reshape(M, Hd)))
+    nin = 2 * HP + Hd + 2 * H
+    assert np.all(dp[:, nin:] == 0.0)
+    gin = fv["gin"].reshape(M, 2 * H).astype(np.float64)
+    a_, b_ = gin[:, :H], gin[:, H:]
+    da_alpha = bv["d_alpha"].reshape(M, H).astype(np.float64)
+    da_beta = bv["d_beta"].reshape(M, H).astype(np.float64)
+    d_a, d_b, d_alog, d_dtb = lo.gates_backward(a_, b_, x["a_log"], x["dt_bias"], da_alpha, da_beta)
+    A = np.exp(x["a_log"].astype(np.float64))
+    Asp = A * lo.softplus(a_ + x["dt_bias"].astype(np.float64))
+    ev = EVAL * U32 * (1.0 + Asp)
+    for cols, ref in ((slice(2 * HP + Hd, 2 * HP + Hd + H), d_a), (slice(2 * HP + Hd + H, nin), d_b)):
+        err = np.abs(dp[:, cols] - ref)
+        assert np.all(err <= 2.0 ** -8 * np.abs(ref) + ev * np.abs(ref) * 1.01 + 1e-30), "gate gradients"
+    t_alog = np.abs(da_alpha * np.exp(-Asp) * Asp)
+    t_dtb = np.abs(d_a)
+    for gv_, ref, tm in ((got["a_log"], d_alog, t_alog), (got["dt_bias"], d_dtb, t_dtb)):
+        bound = (M * U32 + EVAL * U32 * (1.0 + Asp.max(axis=0))) * tm.sum(axis=0) * 1.01 + 1e-30
+        assert np.all(np.abs(gv_.astype(np.float64) - ref) <= bound), "gate parameter gradients"
+    # the input map
+    xx = x["x"].reshape(M, Dm).astype(np.float64)
+    w_in = x["w_in"].astype(np.float64)
+    Np = dp.shape[1]
+    ref = dp[:, :nin] @ w_in
+    r = f32_ok(got["x"].reshape(M, Dm), ref, np.abs(dp[:, :nin]) @ np.abs(w_in), Np)
+    assert r <= 1.0, f"d x beyond its bound ({r:.3g})"
+    ref = dp[:, :nin].T @ xx
+    r = f32_ok(got["w_in"], ref, np.abs(dp[:, :nin]).T @ np.abs(xx), M)
+    assert r <= 1.0, f"d w_in beyond its bound ({r:.3g})"
+
+
+def ob_ids(fv, x, s):
+    """The op oracle's selected slots on the GPU's keys and queries (its top-k: the backward recomputes them)."""
+    ids_w, _ = oracle.topk(fv["keys"], x["subkeys"], s.widths, s.num_writes)
+    ids_r, _ = oracle.topk(fv["queries"], x["subkeys"], s.widths, s.num_reads)
+    return ids_w, ids_r
