@@ -1155,6 +1155,8 @@ sdm_status sdm_layer_backward_workspace_size(const sdm_layer_config* cfg, size_t
     size_t opb = 0;
     return sdm_workspace_size(&cfg->op, SDM_OP_BACKWARD, 0, &opb);
   }
+  size_t sb = 0;
+  TRY(sdm_snapshot_bytes(&cfg->op, &sb));  // the snapshot's route (cfg.op.snapshot_dtype) refused here already
   *bytes = L.btotal;
   return ok();
 }

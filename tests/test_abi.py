@@ -287,6 +287,55 @@ def test_layer_refuses_before_device_work(lib):
     assert call(list(p), n - 1) == B.SDM_ERR_WORKSPACE
 
 
+def test_layer_backward_workspace(lib):
+    """The training calls' workspace: the forward's as a prefix plus the op's backward and the layer backward's
+    regions (larger than the forward's); the op's own backward refusals surface through it."""
+    lc = _layer_cfg()
+    _, nf = _layer_ws(lc)
+    n = ctypes.c_size_t(0)
+    assert lib.sdm_layer_backward_workspace_size(ctypes.byref(lc), ctypes.byref(n)) == B.SDM_OK
+    assert n.value > nf
+    # settings the op's backward refuses (a bfloat16 snapshot of a float32 bank outside the held-row loop)
+    bad = _layer_cfg(snapshot_dtype=B.SDM_BF16, chunk_size=7)
+    assert _layer_ws(bad)[0] == B.SDM_OK  # the plain forward does not need the backward
+    assert lib.sdm_layer_backward_workspace_size(ctypes.byref(bad), ctypes.byref(n)) == B.SDM_ERR_RANGE
+
+
+@fake_pointers
+def test_layer_training_calls_refuse_before_device_work(lib):
+    lc = _layer_cfg()
+    n = ctypes.c_size_t(0)
+    assert lib.sdm_layer_backward_workspace_size(ctypes.byref(lc), ctypes.byref(n)) == B.SDM_OK
+    nb = n.value
+    _, nf = _layer_ws(lc)
+    base, step = 1 << 40, 1 << 34
+    # x w_in a_log dt_bias w_out subkeys initial_bank bank y snapshot widx ridx ws
+    p = [_fake(base + i * step) for i in range(13)]
+    p[6] = None
+    fwd = lambda q, wsn: lib.sdm_layer_forward_save(ctypes.byref(lc), *q, wsn, None)
+    assert fwd(p, nf) == B.SDM_ERR_WORKSPACE  # the forward's size is not enough: the backward reads this one
+    q = list(p)
+    q[9] = None
+    assert fwd(q, nb) == B.SDM_ERR_NULL  # no snapshot
+    q = list(p)
+    q[9] = _fake(base + 7 * step + 256)  # the snapshot inside the bank
+    assert fwd(q, nb) == B.SDM_ERR_ALIAS
+    # x w_in a_log dt_bias w_out subkeys bank snapshot grad_y grad_bank grad_x grad_w_in grad_a_log grad_dt_bias
+    # grad_w_out grad_subkeys ws
+    g = [_fake(base + i * step) for i in range(17)]
+    bwd = lambda q, wsn=nb: lib.sdm_layer_backward(ctypes.byref(lc), *q, wsn, None)
+    assert bwd(g, nb - 1) == B.SDM_ERR_WORKSPACE
+    q = list(g)
+    q[8] = None
+    assert bwd(q) == B.SDM_ERR_NULL  # no grad_y
+    q = list(g)
+    q[10] = g[0]  # grad_x over x
+    assert bwd(q) == B.SDM_ERR_ALIAS
+    q = list(g)
+    q[11] = _fake(base + 11 * step + 4)  # misaligned grad_w_in
+    assert bwd(q) == B.SDM_ERR_LAYOUT
+
+
 @fake_pointers
 def test_snapshot_dtype_settings_and_refusals(lib):
     """snapshot_dtype: 0 (the bank dtype) or SDM_BF16; a bfloat16 snapshot of a float32 bank needs the held-row

@@ -258,15 +258,19 @@ def f32_ok(got, ref, S, K):
 
 BWD_CASES = {
     # float32 bank, model width 64 (every dense map on the LDS-tiled kernel)
-    "small": (synth.Shape(2, 40, 2, (16, 16), 8, 32, 8, 8, 16, "bf16", "f32"), 64),
+    "small": (synth.Shape(2, 40, 2, (16, 16), 8, 32, 8, 8, 16, "bf16", "f32"), 64, False),
     # bfloat16 bank, model width 96 (d o's map, K = 96, on the register-only kernel), ragged chunk
-    "bf16_bank_w96": (synth.Shape(1, 36, 2, (8, 8), 8, 32, 6, 5, 8, "bf16", "bf16"), 96),
+    "bf16_bank_w96": (synth.Shape(1, 36, 2, (8, 8), 8, 32, 6, 5, 8, "bf16", "bf16"), 96, False),
+    # a learned initial bank copied into every batch row; its gradient the batch sum of the bank gradient
+    "learned_bank": (synth.Shape(3, 24, 2, (16, 16), 8, 32, 8, 8, 8, "bf16", "f32"), 64, True),
+    # the 65,536-slot op shapes at model width 2048 (256 tokens a stream)
+    "w2048_65k": (synth.WORKLOADS["layer_65k"].with_(tokens=256), 2048, False),
 }
 
 
 @pytest.mark.parametrize("name", list(BWD_CASES))
 def test_layer_backward_steps_against_oracle(name):
-    s, Dm = BWD_CASES[name]
+    s, Dm, learned = BWD_CASES[name]
     bank_dt = torch.float32 if s.bank == "f32" else torch.bfloat16
     x = synth.make_layer_inputs(s, Dm, 3)
     rng = np.random.default_rng(31)
@@ -275,16 +279,22 @@ def test_layer_backward_steps_against_oracle(name):
     t = {k: to_dev(x[k], torch.bfloat16) for k in ("x", "w_in", "w_out", "subkeys")}
     t.update({k: to_dev(x[k], torch.float32) for k in ("a_log", "dt_bias")})
     bank = to_dev(x["bank"], bank_dt)
-    bank0 = bank.clone()
+    init = None
+    if learned:  # the op starts from this bank's copy in every batch row; the caller's bank is overwritten
+        init_np = (0.02 * rng.standard_normal((s.heads, s.rows, s.head_dim))).astype(np.float32)
+        init = to_dev(init_np, bank_dt)
+        x["bank"] = np.ascontiguousarray(np.broadcast_to(init_np[None], x["bank"].shape))
     kw = dict(heads=s.heads, widths=s.widths, num_writes=s.num_writes, num_reads=s.num_reads, chunk_size=s.chunk_size)
     print(f"layer backward {name}: {s} Dm {Dm}", flush=True)
     y, snap, ws, widx, ridx = binding.sdm_layer_forward_save(t["x"], t["w_in"], t["a_log"], t["dt_bias"], t["w_out"],
-                                                             t["subkeys"], bank, want_index=True, **kw)
+                                                             t["subkeys"], bank, want_index=True, initial_bank=init,
+                                                             **kw)
     torch.cuda.synchronize()
     fv = {k: to_np(v) for k, v in binding.layer_workspace_views(x["x"].shape, s.heads, s.widths, s.subkey_dim,
                                                                 s.head_dim, ws).items()}
     fwd_bank = to_np(bank)
     fwd_snap = to_np(snap)
+    bank0 = to_dev(x["bank"], bank_dt)  # the bank the op started from
     gbank = to_dev(gb_np, torch.float32)
     g = binding.sdm_layer_backward(t["x"], t["w_in"], t["a_log"], t["dt_bias"], t["w_out"], t["subkeys"], bank, snap,
                                    to_dev(gy_np, torch.bfloat16), ws, gbank, **kw)
@@ -360,6 +370,13 @@ def test_layer_backward_steps_against_oracle(name):
     ref = dp[:, :nin].T @ xx
     r = f32_ok(got["w_in"], ref, np.abs(dp[:, :nin]).T @ np.abs(xx), M)
     assert r <= 1.0, f"d w_in beyond its bound ({r:.3g})"
+    if learned:  # the learned bank's gradient: the batch sum, in order, of the bank gradient (within its bounds)
+        gi = binding.sdm_bank_grad_sum(g["bank"], heads=H, widths=s.widths, head_dim=d)
+        torch.cuda.synchronize()
+        ref = ob["d_bank"].sum(axis=0)
+        bound = 1.01 * (ob["e_bank"].sum(axis=0) + (B - 1) * U32 * np.abs(ob["d_bank"]).sum(axis=0)) + 1e-30
+        N = int(np.prod(s.widths))
+        assert np.all(np.abs(to_np(gi)[:, :N] - ref[:, :N]) <= bound[:, :N]), "the learned bank's gradient"
 
 
 def ob_ids(fv, x, s):
