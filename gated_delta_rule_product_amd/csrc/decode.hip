@@ -427,6 +427,8 @@ __global__ __launch_bounds__(STEP_NT) void decode_step_kernel(Dims D, DecodeArgs
     const int kind = wv;
     const TopkPlan& P = kind ? a.plan[1] : a.plan[0];
     int32_t* ids = kind ? L.rid : L.wid;
+    // (no lower-bound prefilter here: at one step's latency its compaction costs more than the smaller select saves;
+    // 128 streams, 32 x 32 sub-keys: 9.2 k cycles with it, 7.9 k without)
     wave_merge_topk<CPL>(D, P, pick2(L.ctab[0], L.ctab[1], kind), pick2(L.fsc[0], L.fsc[1], kind),
                          pick2(L.fid[0], L.fid[1], kind), wscr, wsrt, ids, kind ? L.rwt : L.wwt);
     int32_t* uid = pick2(a.user_ids[0], a.user_ids[1], kind);

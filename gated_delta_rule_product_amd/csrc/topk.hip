@@ -487,26 +487,8 @@ __global__ __launch_bounds__((64 * Topk2Waves<NPL, MF>::NW)) __attribute__((amdg
   uint64_t* cbuf = (uint64_t*)(scs + (BLK ? wv * QW * 64 * NPL : 0));
   const int ccap = QW * 64 * NPL / 2;  // uint64 entries
   for (int q = 0; q < nq; ++q) {
-    // A lower bound L on the k-th largest slot score: a block of position tuples p_f < a_f with prod a_f = k (a_f
-    // <= k_p) lies in the candidate table (prod(p_f + 1) <= k) and holds k candidates, each scoring at least the
-    // block's last corner (float32 addition is monotone). Candidates below L are not in the top k. Two factors
-    // only: with more, the corners of such blocks sit far down the factor lists and the bound keeps most of the
-    // table (three factors, 64 slots: no gain, 5 % slower).
-    float L = -INFINITY;
-    if (F == 2 && ccap >= 128) {
-      const float* fq = fsc + q * F * kpmax;
-      for (int g = 0; g < F; ++g) {  // one factor takes all k positions, the others their best
-        if (P.kp[g] < k) continue;
-        float S = fq[g == 0 ? k - 1 : 0];
-        for (int f = 1; f < F; ++f) S = S + fq[f * kpmax + (f == g ? k - 1 : 0)];
-        L = fmaxf(L, S);
-      }
-      if (F == 2)  // blocks a_0 x k / a_0 with a_0 a power of two that divides k
-        for (int i = 1; (2 << i) <= k + 1; ++i) {
-          const int a0 = 1 << i, a1 = k >> i;
-          if ((k & (a0 - 1)) == 0 && a0 <= P.kp[0] && a1 <= P.kp[1]) L = fmaxf(L, fq[a0 - 1] + fq[kpmax + a1 - 1]);
-        }
-    }
+    // candidates below a lower bound on the k-th slot score (two factors) are not selected from
+    const float L = ccap >= 128 ? merge_lower_bound(P, F, k, fsc + q * F * kpmax, kpmax) : -INFINITY;
     uint64_t ck[CPL];
     bool keep[CPL];
 #pragma unroll
@@ -529,37 +511,7 @@ __global__ __launch_bounds__((64 * Topk2Waves<NPL, MF>::NW)) __attribute__((amdg
       }
       ck[j] = key;
     }
-    int m2 = 0;
-    if (L > -INFINITY) {
-#pragma unroll
-      for (int j = 0; j < CPL; ++j) m2 += __popcll(__ballot(keep[j]));
-    }
-    if (m2 >= k && m2 <= 256 && m2 <= ccap) {  // select among the kept ones only
-      const uint64_t below = lanes_below_mask();
-      int base = 0;
-#pragma unroll
-      for (int j = 0; j < CPL; ++j) {
-        const uint64_t bm = __ballot(keep[j]);
-        if (keep[j]) cbuf[base + __popcll(bm & below)] = ck[j];
-        base += __popcll(bm);
-      }
-      wave_sync();
-      uint64_t ck4[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) ck4[j] = lane + 64 * j < m2 ? cbuf[lane + 64 * j] : ~0ull;
-      wave_sync();
-      if (m2 <= 64) {
-        uint64_t ck1[1] = {ck4[0]};
-        wave_select_sorted<1>(ck1, k, scratch, sorted);
-      } else if (m2 <= 128) {
-        uint64_t ck2[2] = {ck4[0], ck4[1]};
-        wave_select_sorted<2>(ck2, k, scratch, sorted);
-      } else {
-        wave_select_sorted<4>(ck4, k, scratch, sorted);
-      }
-    } else {
-      wave_select_sorted<CPL>(ck, k, scratch, sorted);
-    }
+    select_kept_candidates<CPL, 8>(ck, keep, L > -INFINITY, k, cbuf, ccap, scratch, sorted);
     const long long bt = bt0 + q;
     const long long b = bt / D.T, t = bt % D.T;
     const long long row = (b * D.T + t) * D.H + h;

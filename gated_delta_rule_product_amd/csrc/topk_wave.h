@@ -257,6 +257,77 @@ __device__ void wave_factor_topk(const Dims& D, const TopkPlan& P, int f, const 
 
 constexpr int MERGE_RB = 32;  // rank-placement batch of the merge's selection (its scratch: >= k + MERGE_RB)
 
+// A lower bound L on the k-th largest slot score of a two-factor candidate table (fq: the factor scores [2][kpmax],
+// best first): a block of position tuples p_f < a_f with a_0 a_1 = k (a_f <= k_p) lies in the table (prod(p_f + 1)
+// <= k) and holds k candidates, each scoring at least the block's last corner (float32 addition is monotone);
+// candidates below L are not in the top k. The blocks tried: 1 x k, k x 1, and a_0 a power of two dividing k.
+// -inf for other factor counts: with more, the corners of such blocks sit far down the factor lists and the bound
+// keeps most of the table (three factors, 64 slots: no gain, 5 % slower).
+__device__ __forceinline__ float merge_lower_bound(const TopkPlan& P, int F, int k, const float* fq, int kpmax) {
+  if (F != 2) return -INFINITY;
+  // one block per lane, their corners read at once: lane 0 k x 1, lane 1 1 x k, lane i >= 2 2^(i-1) x k / 2^(i-1)
+  const int lane = lane_id();
+  int a0 = 0, a1 = 0;
+  if (lane == 0) {
+    a0 = k;
+    a1 = 1;
+  } else if (lane == 1) {
+    a0 = 1;
+    a1 = k;
+  } else if (lane < 31) {
+    a0 = 1 << (lane - 1);
+    a1 = (k & (a0 - 1)) == 0 ? k >> (lane - 1) : 0;
+  }
+  float S = -INFINITY;
+  if (a1 >= 1 && a0 <= P.kp[0] && a1 <= P.kp[1] && a0 <= k) {
+    S = fq[a0 - 1] + fq[kpmax + a1 - 1];
+    if (!(S == S)) S = -INFINITY;
+  }
+  return desc_key_value(__ockl_wfred_min_u32(desc_key(S)));  // the largest
+}
+
+// The k smallest candidate keys, ascending, into sorted (wave_select_sorted): ck[j] the keys (~0ull unused) and
+// keep[j] whether the candidate scores at or above a lower bound on the k-th largest score (all of them when there
+// is no bound, bounded = false). When at least k and at most min(256, ccap) are kept, they are compacted into cbuf
+// (this wave's, ccap uint64 entries, not overlapping scratch or sorted) and selected from at most four a lane;
+// otherwise from all CPL a lane.
+template <int CPL, int RB>
+__device__ void select_kept_candidates(const uint64_t (&ck)[CPL], const bool (&keep)[CPL], bool bounded, int k,
+                                       uint64_t* cbuf, int ccap, uint64_t* scratch, uint64_t* sorted) {
+  const int lane = lane_id();
+  int m2 = 0;
+  if (bounded) {
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) m2 += __popcll(__ballot(keep[j]));
+  }
+  if (m2 >= k && m2 <= 256 && m2 <= ccap) {
+    const uint64_t below = lanes_below_mask();
+    int base = 0;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const uint64_t bm = __ballot(keep[j]);
+      if (keep[j]) cbuf[base + __popcll(bm & below)] = ck[j];
+      base += __popcll(bm);
+    }
+    wave_sync();
+    uint64_t ck4[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ck4[j] = lane + 64 * j < m2 ? cbuf[lane + 64 * j] : ~0ull;
+    wave_sync();
+    if (m2 <= 64) {
+      uint64_t ck1[1] = {ck4[0]};
+      wave_select_sorted<1, RB>(ck1, k, scratch, sorted);
+    } else if (m2 <= 128) {
+      uint64_t ck2[2] = {ck4[0], ck4[1]};
+      wave_select_sorted<2, RB>(ck2, k, scratch, sorted);
+    } else {
+      wave_select_sorted<4, RB>(ck4, k, scratch, sorted);
+    }
+  } else {
+    wave_select_sorted<CPL, RB>(ck, k, scratch, sorted);
+  }
+}
+
 // A double moved between lanes by a DPP control (two 32-bit moves; all lanes active).
 template <int CTRL> __device__ __forceinline__ double dpp_d(double x) {
   const uint64_t u = __double_as_longlong(x);
@@ -308,9 +379,11 @@ __device__ __forceinline__ void wave_rank_softmax(int k, ScoreFn score, float* w
   }
 }
 
+// cbuf: this wave's compaction buffer for the two-factor bound (select_kept_candidates; NULL: select among all).
 template <int CPL>
 __device__ void wave_merge_topk(const Dims& D, const TopkPlan& P, const uint64_t* cand, const float* fsc,
-                                const uint16_t* fid, uint64_t* scratch, uint64_t* sorted, int32_t* ids, float* wts) {
+                                const uint16_t* fid, uint64_t* scratch, uint64_t* sorted, int32_t* ids, float* wts,
+                                uint64_t* cbuf = nullptr, int ccap = 0) {
   const int lane = lane_id();
   const int F = D.F, k = P.k, kpmax = P.kpmax;
   // every candidate's tuple, then the factor scores one factor at a time over all of them (the LDS reads of a
@@ -333,13 +406,16 @@ __device__ void wave_merge_topk(const Dims& D, const TopkPlan& P, const uint64_t
       ps[j] += p;
     }
   }
+  const float L = cbuf ? merge_lower_bound(P, F, k, fsc, kpmax) : -INFINITY;
   uint64_t ck[CPL];
+  bool keep[CPL];
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
     const int c = lane + 64 * j;
     ck[j] = c < P.ncand ? ((uint64_t)desc_key(S[j]) << 32) | ((uint64_t)ps[j] << 20) | (uint64_t)c : ~0ull;
+    keep[j] = c < P.ncand && S[j] >= L;
   }
-  wave_select_sorted<CPL, MERGE_RB>(ck, k, scratch, sorted);
+  select_kept_candidates<CPL, MERGE_RB>(ck, keep, L > -INFINITY, k, cbuf, ccap, scratch, sorted);
   for (int r = lane; r < k; r += 64) {
     const uint64_t t = cand[(int)(sorted[r] & 0xFFFFF)];
     long long id = 0;
