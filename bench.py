@@ -63,6 +63,18 @@ def loop_algorithmic_bytes(s, token_heads):
     return token_heads * ((2 * s.num_writes + s.num_reads) * s.head_dim * sb + 2 * s.head_dim * sa + 2 * sa)
 
 
+def bwd_algorithmic_bytes(s, token_heads):
+    """Bytes the backward must move per call with a float32 snapshot and float32 gradients: per token-head, the read
+    rows of the bank and of the adjoint bank, the adjoint rows and snapshot rows of the write terms, loaded; the read
+    rows' and write rows' adjoint rows and the restored bank rows, stored ((3R + 4W) d elements with the bank's rows at
+    the bank dtype); the output gradient and the values read and their gradient written."""
+    sb = 2 if s.bank == "bf16" else 4
+    sa = 2 if s.act == "bf16" else 4
+    W, R, d = s.num_writes, s.num_reads, s.head_dim
+    rows = R * d * (sb + 4) + W * d * (4 + 4) + R * d * 4 + W * d * (4 + sb)
+    return token_heads * (rows + 2 * d * sa + d * 4)
+
+
 def bench_write_read(args, torch, binding, synth):
     s = synth.WORKLOADS["layer_65k"]
     dt = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -243,9 +255,21 @@ def bench_train(args, torch, binding, synth):
                        "snapshot_bytes": nbytes}
         del snap_m
     snap = None
+    # the backward's kernels (reverse sweep, token grouping, token and sub-key sums) against HBM: a per-token latency
+    # chain, so the fraction says how far the round trips keep it from the bandwidth bound
+    bwd_bytes = bwd_algorithmic_bytes(s, s.batch * s.heads * s.tokens)
+    bwd_ms = prof["bwd"][0] / prof["bwd"][1] if prof.get("bwd", (0, 0))[1] else None
+    bwd_roof = None
+    if bwd_ms:
+        gbps = bwd_bytes / (bwd_ms * 1e-3) / 1e9
+        bwd_roof = {"kernel": "bwd (reverse sweep + token grouping, token and sub-key sums)", "bound": "hbm",
+                    "achieved": round(gbps, 1), "peak": 8000.0, "unit": "GB/s", "frac": round(gbps / 8000.0, 4),
+                    "algorithmic_bytes_per_call": bwd_bytes, "avg_launch_ms": round(bwd_ms, 4),
+                    "limit": "one HBM round trip per step of disjoint tokens"}
     res = {"tokens_per_s": round(s.batch * s.tokens / ((ms_f + ms_b) * 1e-3), 1),
            "ms_forward_save": round(ms_f, 4), "ms_backward": round(ms_b, 4), "steps": n,
            "kernels_avg_ms": {k: round(v[0] / v[1], 4) for k, v in prof.items() if v[1]},
+           "backward_roofline": bwd_roof,
            "snapshot_bytes": s.batch * s.heads * s.tokens * s.num_writes * s.head_dim * 4,
            "bank_restored_bitwise": restored,
            "bf16_snapshot": {"tokens_per_s": round(s.batch * s.tokens / ((ms_qf + ms_qb) * 1e-3), 1),
