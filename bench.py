@@ -115,14 +115,16 @@ def bench_write_read(args, torch, binding, synth):
     tokens = s.batch * s.tokens
     kernels = {k: round(v[0] / v[1], 4) for k, v in prof.items() if v[1]}
     loop_ms = prof["loop"][0] / prof["loop"][1]
-    alg = loop_algorithmic_bytes(s, s.batch * s.tokens * s.heads)
+    # one loop launch per call here (the loop's workgroups fill the chip, so the call is not pipelined); were it
+    # pipelined, a launch would cover 1/launches of the call's tokens
+    alg = loop_algorithmic_bytes(s, s.batch * s.tokens * s.heads) * args.steps // prof["loop"][1]
     achieved = alg / (loop_ms * 1e-3) / 1e9
     traffic = traffic_from_counters()
     roof = {"kernel": "loop_kernel (chunk loop: gather, solve, read, scatter)", "bound": "hbm",
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "algorithmic_bytes_per_launch": alg, "avg_launch_ms": round(loop_ms, 4)}
-    step_bytes = alg  # the loop's bank traffic dominates the call's bytes
+    step_bytes = loop_algorithmic_bytes(s, s.batch * s.tokens * s.heads)  # the loop's bank traffic dominates
     # the same workload on an unpadded bank (row pitch = head_dim), for comparison
     bank_np = torch.empty((s.batch, s.heads, s.rows, s.head_dim), dtype=dt[s.bank], device=dev)
     bank_np.copy_(bank)
@@ -323,20 +325,23 @@ def bench_other(args, torch, binding, synth):
         prof = binding.profile_read()
         binding.profile_enable(False)
         ms = (t1 - t0) * 1e3 / n
-        loop_ms = prof["loop"][0] / prof["loop"][1]
+        # per call: a pipelined call (the three-factor workload) launches its top-k, plan and loop once per piece,
+        # the top-k and plan beside the loop on a second stream, so kernel times are summed over a call's launches
+        loop_ms = prof["loop"][0] / n
         alg = loop_algorithmic_bytes(s, s.batch * s.tokens * s.heads)
-        topk_ms = prof["topk"][0] / prof["topk"][1]
+        topk_ms = prof["topk"][0] / n
         # factor scoring as a dense contraction: both kinds, every query against every sub-key of every factor
         flops = 2 * s.batch * s.tokens * s.heads * sum(s.widths) * s.subkey_dim * 2
         filtered = s.act == "bf16" and min(s.widths) >= 512
         res_mfma = {"kernel": "topk2_kernel (%s factor scoring + exact selection)" % (
                         "bf16 MFMA-filtered" if filtered else "fp64 direct"),
-                    "bound": "latency (selection chains)", "scoring_flops_per_launch": flops,
+                    "bound": "latency (selection chains)", "scoring_flops_per_call": flops,
                     "achieved": round(flops / (topk_ms * 1e-3) / 1e12, 2), "peak": 2500.0, "unit": "TFLOP/s",
-                    "frac": round(flops / (topk_ms * 1e-3) / 1e12 / 2500.0, 5), "avg_launch_ms": round(topk_ms, 4)}
+                    "frac": round(flops / (topk_ms * 1e-3) / 1e12 / 2500.0, 5), "ms_per_call": round(topk_ms, 4)}
         res[name] = {"tokens_per_s": round(s.batch * s.tokens / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
                      "topk_scoring_mfma": res_mfma,
-                     "steps": n, "kernels_avg_ms": {k: round(v[0] / v[1], 4) for k, v in prof.items() if v[1]},
+                     "steps": n, "kernels_ms_per_call": {k: round(v[0] / n, 4) for k, v in prof.items() if v[1]},
+                     "launches_per_call": {k: round(v[1] / n, 2) for k, v in prof.items() if v[1]},
                      "loop_algorithmic_bytes": alg, "loop_achieved_GBps": round(alg / (loop_ms * 1e-3) / 1e9, 1),
                      "loop_frac_of_8TBps": round(alg / (loop_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "bank_bytes": s.batch * s.heads * s.rows * s.head_dim * (2 if s.bank == "bf16" else 4),

@@ -474,6 +474,55 @@ sdm_status topk_product_keys(const sdm_config* cfg, const void* queries, const v
 }
 
 // The write/read; with a snapshot (not NULL) also the backward's snapshot, through the segmented chunk loop.
+// The pipelined write/read: when the chunk loop's workgroups (one per stream and column slice) leave at least half of
+// the compute units free, the sequence runs as up to PIPE_MAX pieces of whole chunks, and the top-k and chunk plan
+// of piece p + 1 (bank-independent) run on a side stream beside the chunk loop of piece p on the caller's stream.
+// The loop of piece p waits for its own plan only, and its launches are those of calls split at the pieces'
+// chunk boundaries, which give the bits of one call. With the chip full of loop workgroups the side stream's work
+// would only queue behind them, so it is not used then. The side stream (default priority) and its events are made
+// once per device, outside any stream capture, and kept until the process ends; a call forks the side stream from
+// the caller's stream and joins it back before it returns (under capture, ordinary graph dependencies).
+namespace {
+constexpr int PIPE_MAX = 16;
+struct PipeDev {
+  hipStream_t side = nullptr;
+  hipEvent_t ev[PIPE_MAX + 2] = {};  // ev[p]: piece p planned; ev[PIPE_MAX]: fork; ev[PIPE_MAX + 1]: join
+  int cus = 0;
+  bool tried = false;
+};
+constexpr int PIPE_DEVICES = 64;
+std::mutex g_pipe_mu;  // held while a call enqueues its pieces (one set of events per device)
+PipeDev g_pipe[PIPE_DEVICES];
+
+// The current device's side stream and events, or nullptr (made on the first call outside a stream capture).
+PipeDev* pipe_device(hipStream_t st) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= PIPE_DEVICES) return nullptr;
+  PipeDev& p = g_pipe[dev];
+  if (!p.tried) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+    p.tried = true;
+    bool made = hipDeviceGetAttribute(&p.cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+                hipStreamCreateWithFlags(&p.side, hipStreamNonBlocking) == hipSuccess;
+    for (int i = 0; made && i < PIPE_MAX + 2; ++i)
+      made = hipEventCreateWithFlags(&p.ev[i], hipEventDisableTiming) == hipSuccess;
+    if (!made) p.side = nullptr;  // whatever was made is kept, never used
+  }
+  return p.side ? &p : nullptr;
+}
+
+// Chunks per piece of a pipelined call, or 0 to run the call in order on the caller's stream.
+int pipe_chunks(const Dims& D, bool snapshot, const PipeDev* pd) {
+  if (pd == nullptr || D.shared || D.nch < 2) return 0;
+  if (loop_workgroups(D, snapshot) * 2 > pd->cus) return 0;
+  const int per = (D.nch + PIPE_MAX - 1) / PIPE_MAX;
+  // a window of several batch rows is a multiple of 16 tokens (the top-k's rows of a wave stay in one batch row)
+  if (D.B > 1 && ((per * D.C) % 16 != 0 || D.T % 16 != 0)) return 0;
+  return per;
+}
+}  // namespace
+
 static sdm_status write_read_impl(const sdm_config* cfg, const void* write_keys, const void* read_queries,
                            const void* values, const void* forget_gate, const void* input_gate, const void* subkeys,
                            void* bank, void* out, void* snapshot, int32_t* write_idx, int32_t* read_idx,
@@ -529,8 +578,6 @@ static sdm_status write_read_impl(const sdm_config* cfg, const void* write_keys,
   hipStream_t st = (hipStream_t)stream;
   unsigned char* ws = (unsigned char*)workspace;
   const TopkPlan plans[2] = {pw, pr};
-  TRY(hip_status(timed(SDM_K_CAND, st, [&] { return launch_cand_tables(plans, 2, D.F, (uint64_t*)(ws + L.cand), st); }),
-                 "candidate table launch"));
   TopkArgs ta;
   memset(&ta, 0, sizeof ta);
   ta.queries[0] = write_keys;
@@ -549,14 +596,7 @@ static sdm_status write_read_impl(const sdm_config* cfg, const void* write_keys,
   ta.user_ids[0] = write_idx;
   ta.user_ids[1] = read_idx;
   ta.snorm = (float*)(ws + L.snorm);
-  TRY(hip_status(timed(SDM_K_TOPK, st, [&] { return launch_topk(D, ta, st); }), "top-k launch"));
-  const int32_t* abort = nullptr;
-  if (D.shared) {  // the streams of a head must address disjoint slots; if not, the plan and the loop do nothing
-    TRY(hip_status(launch_shared_check(D, (const int32_t*)(ws + L.widx), (const int32_t*)(ws + L.ridx),
-                                       (int32_t*)(ws + L.owner), (int32_t*)(ws + L.conflict), st),
-                   "shared-bank check launch"));
-    abort = (const int32_t*)(ws + L.conflict);
-  }
+  const int32_t* abort = D.shared ? (const int32_t*)(ws + L.conflict) : nullptr;
   PlanArgs pa;
   pa.abort = abort;
   pa.widx = (const int32_t*)(ws + L.widx);
@@ -574,7 +614,6 @@ static sdm_status write_read_impl(const sdm_config* cfg, const void* write_keys,
   pa.scat = held || narrow ? 0 : 1;
   pa.lanemajor = narrow && loop_narrow_lanemajor(D) ? 1 : 0;
   pa.evcode = snapshot ? 1 : 0;
-  TRY(hip_status(timed(SDM_K_PLAN, st, [&] { return launch_plan(D, pa, st); }), "chunk plan launch"));
   LoopArgs la;
   la.alpha = forget_gate;
   la.beta = input_gate;
@@ -586,9 +625,54 @@ static sdm_status write_read_impl(const sdm_config* cfg, const void* write_keys,
   la.abort = abort;
   la.snap = snapshot;
   la.snap_mode = snap_mode;
-  TRY(hip_status(timed(SDM_K_LOOP, st, [&] { return launch_loop(D, la, st); }), "chunk loop launch"));
+  std::unique_lock<std::mutex> lock(g_pipe_mu);
+  PipeDev* pd = pipe_device(st);
+  const int per = pipe_chunks(D, snapshot != nullptr, pd);
+  if (per == 0) {  // in order on the caller's stream
+    lock.unlock();
+    TRY(hip_status(timed(SDM_K_CAND, st, [&] { return launch_cand_tables(plans, 2, D.F, (uint64_t*)(ws + L.cand), st); }),
+                   "candidate table launch"));
+    TRY(hip_status(timed(SDM_K_TOPK, st, [&] { return launch_topk(D, ta, st); }), "top-k launch"));
+    if (D.shared)  // the streams of a head must address disjoint slots; if not, the plan and the loop do nothing
+      TRY(hip_status(launch_shared_check(D, (const int32_t*)(ws + L.widx), (const int32_t*)(ws + L.ridx),
+                                         (int32_t*)(ws + L.owner), (int32_t*)(ws + L.conflict), st),
+                     "shared-bank check launch"));
+    TRY(hip_status(timed(SDM_K_PLAN, st, [&] { return launch_plan(D, pa, st); }), "chunk plan launch"));
+    TRY(hip_status(timed(SDM_K_LOOP, st, [&] { return launch_loop(D, la, st); }), "chunk loop launch"));
+    return ok();
+  }
+  // pipelined: fork the side stream from the caller's stream, then per piece the top-k and plan on the side stream
+  // and the loop on the caller's stream after that piece's plan; the side stream is joined back on every exit
+  hipStream_t side = pd->side;
+  TRY(hip_status(hipEventRecord(pd->ev[PIPE_MAX], st), "fork event record"));
+  TRY(hip_status(hipStreamWaitEvent(side, pd->ev[PIPE_MAX], 0), "fork event wait"));
+  auto pieces = [&]() -> sdm_status {
+    TRY(hip_status(timed(SDM_K_CAND, side, [&] {
+      return launch_cand_tables(plans, 2, D.F, (uint64_t*)(ws + L.cand), side); }), "candidate table launch"));
+    for (int c0 = 0, p = 0; c0 < D.nch; c0 += per, ++p) {
+      const int nc = D.nch - c0 < per ? D.nch - c0 : per;
+      ta.t0 = c0 * D.C;
+      ta.tn = ((c0 + nc) * D.C < D.T ? (c0 + nc) * D.C : D.T) - ta.t0;
+      TRY(hip_status(timed(SDM_K_TOPK, side, [&] { return launch_topk(D, ta, side); }), "top-k launch"));
+      pa.ch0 = c0;
+      pa.chn = nc;
+      TRY(hip_status(timed(SDM_K_PLAN, side, [&] { return launch_plan(D, pa, side); }), "chunk plan launch"));
+      TRY(hip_status(hipEventRecord(pd->ev[p], side), "piece event record"));
+      TRY(hip_status(hipStreamWaitEvent(st, pd->ev[p], 0), "piece event wait"));
+      la.ch0 = c0;
+      la.ch1 = c0 + nc;
+      TRY(hip_status(timed(SDM_K_LOOP, st, [&] { return launch_loop(D, la, st); }), "chunk loop launch"));
+    }
+    return ok();
+  };
+  const sdm_status rc = pieces();
+  hipError_t ej = hipEventRecord(pd->ev[PIPE_MAX + 1], side);
+  if (ej == hipSuccess) ej = hipStreamWaitEvent(st, pd->ev[PIPE_MAX + 1], 0);
+  if (rc != SDM_OK) return rc;
+  TRY(hip_status(ej, "join event"));
   return ok();
 }
+
 
 sdm_status sdm_write_read(const sdm_config* cfg, const void* write_keys, const void* read_queries,
                           const void* values, const void* forget_gate, const void* input_gate, const void* subkeys,

@@ -110,13 +110,14 @@ __global__ __launch_bounds__(LOOP_NT) void loop_kernel(Dims D, LoopArgs a, int n
   const ChunkLayout CL = chunk_layout(C, W, R);
   const long long CW = (long long)C * W;
 
-  ChunkCounts cnt = a.counts[(long long)st * D.nch];
-  for (int ch = 0; ch < D.nch; ++ch) {
+  const int ch1 = a.ch1 ? a.ch1 : D.nch;  // chunks [a.ch0, ch1)
+  ChunkCounts cnt = a.counts[(long long)st * D.nch + a.ch0];
+  for (int ch = a.ch0; ch < ch1; ++ch) {
     const int t0 = ch * C;
     const int Cc = min(C, D.T - t0);
     const long long cidx = (long long)st * D.nch + ch;
     const unsigned char* greg = a.chunks + cidx * CL.bytes;
-    const ChunkCounts next = a.counts[ch + 1 < D.nch ? cidx + 1 : cidx];
+    const ChunkCounts next = a.counts[ch + 1 < ch1 ? cidx + 1 : cidx];
     // region pointers (LDS copy or global)
     const unsigned char* reg = greg;
     if (STAGED) {
@@ -507,25 +508,26 @@ __global__ __launch_bounds__(LOOP_NT) void loop_held_kernel(Dims D, LoopArgs a, 
   constexpr int NST = 4;                    // 16-byte words of row pointers, lists and multi-event table per thread
 
   // write and read terms of the first chunk
+  const int ch1 = a.ch1 ? a.ch1 : D.nch;  // chunks [a.ch0, ch1)
   {
-    const unsigned char* g0 = a.chunks + (long long)st * D.nch * CL.bytes;
+    const unsigned char* g0 = a.chunks + ((long long)st * D.nch + a.ch0) * CL.bytes;
     stage16<NWP>((const uint4*)g0, (uint4*)sW0, nw16);
     stage16<NRP>((const uint4*)(g0 + CL.rpairs), (uint4*)sR, nr16);
   }
   __syncthreads();
 
-  ChunkCounts cnt = a.counts[(long long)st * D.nch];
-  for (int ch = 0; ch < D.nch; ++ch) {
+  ChunkCounts cnt = a.counts[(long long)st * D.nch + a.ch0];
+  for (int ch = a.ch0; ch < ch1; ++ch) {
     const int t0 = ch * C;
     const int Cc = min(C, D.T - t0);
     const long long cidx = (long long)st * D.nch + ch;
     const unsigned char* greg = a.chunks + cidx * CL.bytes;
-    const bool more = ch + 1 < D.nch;
+    const bool more = ch + 1 < ch1;
     const ChunkCounts next = a.counts[more ? cidx + 1 : cidx];
     const bool act = valid && gt < Cc;
     const bool lead = part == 0 && act;     // computes U, delta and the output of token gt's row slice
-    unsigned char* sWc = sW0 + (ch & 1) * WT;
-    unsigned char* sWn = sW0 + ((ch + 1) & 1) * WT;
+    unsigned char* sWc = sW0 + ((ch - a.ch0) & 1) * WT;
+    unsigned char* sWn = sW0 + ((ch - a.ch0 + 1) & 1) * WT;
     const Pair* pw = (const Pair*)sWc + gt * W + part * tpw;
     const int16_t* wl = (const int16_t*)(sWc + align16((long long)C * W * 8)) + gt * W + part * tpw;
 
@@ -942,20 +944,21 @@ __global__ __launch_bounds__(LOOP_NT) void loop_narrow_kernel(Dims D, LoopArgs a
   const long long roff = FULL ? 0 : (long long)gt * R + part * tpr;
 
   NarrowTerms rt;
+  const int ch1 = a.ch1 ? a.ch1 : D.nch;  // chunks [a.ch0, ch1)
   {
-    const unsigned char* g0 = a.chunks + (long long)st * D.nch * CL.bytes;
+    const unsigned char* g0 = a.chunks + ((long long)st * D.nch + a.ch0) * CL.bytes;
     narrow_load_terms<FULL, false>(rt, (const Pair*)(g0 + CL.rpairs) + roff, nullptr, tpr);
 #pragma unroll
     for (int i = 0; i < NARROW_HOLD / 2; ++i) asm volatile("" : "+v"(rt.p[i]));  // arrived before the loop
   }
 
-  ChunkCounts cnt = a.counts[(long long)st * D.nch];
-  for (int ch = 0; ch < D.nch; ++ch) {
+  ChunkCounts cnt = a.counts[(long long)st * D.nch + a.ch0];
+  for (int ch = a.ch0; ch < ch1; ++ch) {
     const int t0 = ch * C;
     const int Cc = min(C, D.T - t0);
     const long long cidx = (long long)st * D.nch + ch;
     const unsigned char* greg = a.chunks + cidx * CL.bytes;
-    const bool more = ch + 1 < D.nch;
+    const bool more = ch + 1 < ch1;
     const ChunkCounts next = a.counts[more ? cidx + 1 : cidx];
     const bool act = valid && gt < Cc;
     const bool lead = part == 0 && act;
@@ -1225,6 +1228,14 @@ bool loop_held_path(const Dims& D) {
 // The held-row variant can also write the snapshot when a stream's snapshot fits 32-bit byte offsets.
 bool loop_held_snap_ok(const Dims& D) {
   return loop_held_path(D) && (unsigned long long)D.T * D.W * D.d * 4 < BUF_OOB;
+}
+
+long long loop_workgroups(const Dims& D, bool snapshot) {
+  const int epl = D.bank == SDM_BF16 ? 8 : 4;  // bank elements in 16 bytes
+  if (D.bank == SDM_F32 && (snapshot ? loop_held_snap_ok(D) : loop_held_path(D)))
+    return (long long)D.S * ((D.d + 15) / 16);
+  if (loop_narrow_path(D) && !snapshot) return (long long)D.S * (D.d / epl);
+  return (long long)D.S * ((D.d + 4 * epl - 1) / (4 * epl));
 }
 
 template <typename A, typename Bk>

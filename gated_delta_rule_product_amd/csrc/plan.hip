@@ -271,7 +271,7 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int st = blockIdx.y;
-  const int ch = blockIdx.x;
+  const int ch = a.ch0 + blockIdx.x;
   const int b = st / D.H, h = st % D.H;
   const int W = D.W, R = D.R, C = D.C;
   const int t0 = ch * C;
@@ -643,7 +643,7 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
 hipError_t launch_plan(const Dims& D, const PlanArgs& a, hipStream_t st) {
   if (D.S == 0 || D.T == 0) return hipSuccess;
   const size_t lds = plan_lds_bytes(D.C, D.W, D.R);
-  dim3 grid((unsigned)D.nch, (unsigned)D.S);
+  dim3 grid((unsigned)(a.chn ? a.chn : D.nch), (unsigned)D.S);
   if (D.act == SDM_BF16) {
     (void)hipFuncSetAttribute((const void*)plan_kernel<bf16_t>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     hipLaunchKernelGGL(plan_kernel<bf16_t>, grid, dim3(PLAN_NT), lds, st, D, a);

@@ -281,6 +281,9 @@ struct TopkArgs {
   int32_t* user_ids[2];  // optional user ids [B,T,H,k] in stream-major mode
   float* snorm;          // workspace [H][F]: largest sub-key norms for the filtered (MFMA) scoring, or NULL
   int one_query_per_wave;  // few rows (a decode step): one query per wave
+  // token window: tokens [t0, t0 + tn) of every batch row (tn = 0: the whole sequence). With B > 1 a window's tn is
+  // a multiple of 16, so the query rows a wave or a workgroup takes never straddle two batch rows.
+  int t0, tn;
 };
 hipError_t launch_topk(const Dims& D, const TopkArgs& a, hipStream_t st);
 
@@ -293,6 +296,7 @@ struct PlanArgs {
   int lanemajor;          // write the gather terms lane-major for the narrow loop (term_pos)
   const int32_t* abort;   // if not NULL and *abort != 0: do nothing (shared-bank conflict)
   int evcode;             // events also carry their term index (Ev::tok bits 16..31), for the snapshot
+  int ch0 = 0, chn = 0;   // chunks [ch0, ch0 + chn) of every stream (chn = 0: all of them)
 };
 
 // Position of gather term i (of n per token) of chunk-local token t in a chunk's term section. Token-major: t n + i.
@@ -322,6 +326,8 @@ struct LoopArgs {
   void* snap;             // if not NULL: [S][T][W][d] bank dtype, the row of every write event before it (the
                           // held-row or the segmented loop writes it; needs PlanArgs::evcode)
   int snap_mode;          // SNAP_*: the snapshot's rows as stored (float32 bank, held-row loop only for 1-3)
+  int ch0 = 0, ch1 = 0;   // chunks [ch0, ch1) of every stream (ch1 = 0: to the last); the bank holds the state
+                          // after chunk ch0 - 1
 };
 hipError_t launch_loop(const Dims& D, const LoopArgs& a, hipStream_t st);
 // True if launch_loop runs the held-row variant (which reads last-event codes, not slot segments).
@@ -330,6 +336,8 @@ bool loop_held_path(const Dims& D);
 bool loop_held_snap_ok(const Dims& D);
 // True if launch_loop runs the narrow variant (16-byte column slices; also reads last-event codes).
 bool loop_narrow_path(const Dims& D);
+// Workgroups launch_loop starts (one per stream and column slice), for a call with or without a snapshot.
+long long loop_workgroups(const Dims& D, bool snapshot);
 // True if it runs the narrow variant with 16 terms of each kind per lane, which reads lane-major terms.
 bool loop_narrow_lanemajor(const Dims& D);
 

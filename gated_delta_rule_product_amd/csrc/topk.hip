@@ -26,11 +26,12 @@ __global__ __launch_bounds__(TOPK_NT) void topk_kernel(Dims D, TopkArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
   const int kind = blockIdx.y;
   const TopkPlan& P = a.plan[kind];
-  const long long row = blockIdx.x;  // (b * T + t) * H + h
-  const int h = (int)(row % D.H);
-  const long long bt = row / D.H;
-  const int t = (int)(bt % D.T);
-  const int b = (int)(bt / D.T);
+  const int tn = a.tn ? a.tn : D.T;  // token window [a.t0, a.t0 + tn) of every batch row
+  const int h = (int)(blockIdx.x % D.H);
+  const long long btw = blockIdx.x / D.H;
+  const int t = a.t0 + (int)(btw % tn);
+  const int b = (int)(btw / tn);
+  const long long row = ((long long)b * D.T + t) * D.H + h;
   const int Fdk = D.F * D.dk;
   long long sumn = 0;
   for (int f = 0; f < D.F; ++f) sumn += D.widths[f];
@@ -390,7 +391,10 @@ __global__ __launch_bounds__((64 * Topk2Waves<NPL, MF>::NW)) __attribute__((amdg
   const int kind = blockIdx.y, h = blockIdx.z;
   const TopkPlan& P = a.plan[kind];
   const int F = D.F, dk = D.dk, k = P.k, kpmax = P.kpmax;
-  const long long BT = (long long)D.B * D.T;
+  // rows bt of the token window [a.t0, a.t0 + tn) of every batch row: (b, t) = (bt / tn, a.t0 + bt % tn)
+  const int tn = a.tn ? a.tn : D.T;
+  const long long BT = (long long)D.B * tn;
+  auto grow = [&](long long bt) { return (bt / tn) * D.T + a.t0 + bt % tn; };  // b T + t
   const long long bt0 = ((long long)blockIdx.x * NW + wv) * QW;
   const uint64_t* cand = a.cand[kind];
   const size_t shared_scs = BLK ? (size_t)NW * QW * 64 * NPL * 4 : 0;  // block mode: [NW QW][64 NPL] scores
@@ -414,8 +418,8 @@ __global__ __launch_bounds__((64 * Topk2Waves<NPL, MF>::NW)) __attribute__((amdg
   const A* sub = (const A*)a.subkeys + (long long)h * sumn * dk;
   const int Fdk = F * dk;
   const int nq = (int)max(0LL, min((long long)QW, BT - bt0));
-  // rows (b, t) = bt0 + q are consecutive: row index (bt0 + q) * H + h
-  const A* qbase = (const A*)a.queries[kind] + ((long long)bt0 * D.H + h) * Fdk;
+  // the rows of bt0 + q are consecutive (a window of several batch rows is a multiple of 16 tokens)
+  const A* qbase = (const A*)a.queries[kind] + (grow(bt0) * D.H + h) * Fdk;
   const long long qstride = (long long)D.H * Fdk;
 
   long long off = 0;
@@ -424,7 +428,7 @@ __global__ __launch_bounds__((64 * Topk2Waves<NPL, MF>::NW)) __attribute__((amdg
     const A* tab = sub + off * dk;
     if constexpr (MF && BLK) {
       const long long bb = (long long)blockIdx.x * NW * QW;  // the workgroup's first row
-      const bf16_t* qb = (const bf16_t*)a.queries[kind] + ((long long)bb * D.H + h) * Fdk + f * dk;
+      const bf16_t* qb = (const bf16_t*)a.queries[kind] + (grow(bb) * D.H + h) * Fdk + f * dk;
       factor_topk_filtered<NPL, QW, NW>(D, a, f, n, (const bf16_t*)tab, (const bf16_t*)qbase + f * dk, qstride, nq,
                                         scs, fsc, fid, scratch, sorted, klist, kpmax, qb,
                                         (int)max(0LL, min((long long)NW * QW, BT - bb)), wv * QW);
@@ -513,10 +517,10 @@ __global__ __launch_bounds__((64 * Topk2Waves<NPL, MF>::NW)) __attribute__((amdg
     }
     select_kept_candidates<CPL, 8>(ck, keep, L > -INFINITY, k, cbuf, ccap, scratch, sorted);
     const long long bt = bt0 + q;
-    const long long b = bt / D.T, t = bt % D.T;
+    const long long b = bt / tn, t = a.t0 + bt % tn;
     const long long row = (b * D.T + t) * D.H + h;
     const double m = (double)desc_key_value((uint32_t)(sorted[0] >> 32));
-    double zpart = 0.0;
+    double zpart = 0.0, e0 = 0.0;  // e0: the exponential of this lane's first rank, kept for the weights
     for (int r = lane; r < k; r += 64) {
       const uint64_t kk = sorted[r];
       const uint64_t tup = cand[(int)(kk & 0xFFFFF)];
@@ -528,7 +532,9 @@ __global__ __launch_bounds__((64 * Topk2Waves<NPL, MF>::NW)) __attribute__((amdg
         const long long so = ((b * D.H + h) * D.T + t) * k;
         a.ids[kind][so + r] = (int32_t)id;
         if (a.user_ids[kind]) a.user_ids[kind][row * k + r] = (int32_t)id;
-        zpart += exp((double)sc - m);
+        const double ex = exp((double)sc - m);
+        if (r == lane) e0 = ex;
+        zpart += ex;
       } else {
         a.ids[kind][row * k + r] = (int32_t)id;
         if (a.vals[kind]) a.vals[kind][row * k + r] = sc;
@@ -541,8 +547,8 @@ __global__ __launch_bounds__((64 * Topk2Waves<NPL, MF>::NW)) __attribute__((amdg
       for (int o = 32; o >= 1; o >>= 1) z += __shfl_xor(z, o);
       const long long so = ((b * D.H + h) * D.T + t) * k;
       for (int r = lane; r < k; r += 64) {
-        const float sc = desc_key_value((uint32_t)(sorted[r] >> 32));
-        a.vals[kind][so + r] = (float)(exp((double)sc - m) / z);
+        const double ex = r == lane ? e0 : exp((double)desc_key_value((uint32_t)(sorted[r] >> 32)) - m);
+        a.vals[kind][so + r] = (float)(ex / z);
       }
     }
     wave_sync();
@@ -560,7 +566,7 @@ static void launch_topk2_k(dim3 grid, size_t lds, hipStream_t st, const Dims& D,
 template <typename A, int NPL>
 static bool launch_topk2_npl(const Dims& D, const TopkArgs& a, hipStream_t st, int cpl, size_t lds, bool mf) {
   const int QW = a.one_query_per_wave ? 1 : (mf ? WaveTile<NPL, true>::QW : WaveTile<NPL>::QW);
-  const long long BT = (long long)D.B * D.T;
+  const long long BT = (long long)D.B * (a.tn ? a.tn : D.T);
   const long long tiles = (BT + QW - 1) / QW;
   const int NW = (!a.one_query_per_wave && mf) ? Topk2Waves<NPL, true>::NW : 4;
   dim3 grid((unsigned)((tiles + NW - 1) / NW), (unsigned)a.nkinds, (unsigned)D.H);
@@ -648,7 +654,7 @@ static bool launch_topk2(const Dims& D, const TopkArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_topk(const Dims& D, const TopkArgs& a, hipStream_t st) {
-  const long long rows = (long long)D.B * D.T * D.H;
+  const long long rows = (long long)D.B * (a.tn ? a.tn : D.T) * D.H;
   if (rows == 0) return hipSuccess;
   const bool done = D.act == SDM_BF16 ? launch_topk2<bf16_t>(D, a, st) : launch_topk2<float>(D, a, st);
   if (done) return hipGetLastError();

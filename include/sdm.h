@@ -39,8 +39,11 @@
  * Ownership and streams: the caller owns every buffer. The library never allocates or frees memory (temporary
  * storage comes from the caller's workspace, sized by sdm_workspace_size), never synchronises the stream, keeps no
  * pointer after a call returns, and writes only the outputs named for each call and the workspace. All work is
- * enqueued on `stream` (a hipStream_t; NULL = the null stream) of the current HIP device. Results are bitwise
- * repeatable for fixed inputs and settings (no floating-point atomics).
+ * ordered on `stream` (a hipStream_t; NULL = the null stream) of the current HIP device: it starts after the work
+ * enqueued on `stream` before the call and ends before the work enqueued after it (sdm_write_read, and the calls
+ * that run it: sdm_write_read_save, the layer's forward, may run part of it on a second stream of the library's
+ * own, forked from and joined back to `stream`; see sdm_write_read). Results are
+ * bitwise repeatable for fixed inputs and settings (no floating-point atomics).
  *
  * Errors: every check runs on the host before any device work, and a refused call does no work (CHANGELOG 2.0.0,
  * "Behavior changes": refusals are raised at the entry of the op, no fallback paths). On a non-OK status,
@@ -146,7 +149,15 @@ sdm_status topk_product_keys(const sdm_config* cfg, const void* queries, const v
  * gated delta-rule update of the W write rows with values, forget_gate and input_gate, and the read of the R read
  * rows into out. `bank` [B, H, bank_rows, d] advances in place. write_idx / read_idx, if not NULL, receive the
  * selected slot ids. The result equals the one-token-at-a-time recurrence up to floating-point rounding, for any
- * chunk_size; two calls split at a multiple of chunk_size give the same bits as one call. */
+ * chunk_size; two calls split at a multiple of chunk_size give the same bits as one call.
+ * Streams: when the chunk loop's workgroups (one per stream and column slice: B * H * ceil(head_dim * bank bytes /
+ * 64), or / 16 for the narrow loop of short rows) fill at most half of the device's compute units, the call runs
+ * as up to 16 pieces of whole chunks, the top-k and plan of each piece on a side stream that the library makes once
+ * per device (default priority, kept until the process ends) and the chunk loop of each piece on `stream` after
+ * that piece's plan: the bits of calls split at those chunks, with the top-k and plan hidden behind the loop. The
+ * side stream waits for `stream` at the call's start and `stream` waits for it before the call returns, also under
+ * stream capture (a graph records the fork and join as dependencies). Calls from several host threads take turns
+ * on the side stream. Not with shared_bank (its slot check needs every token's top-k before any plan). */
 sdm_status sdm_write_read(const sdm_config* cfg, const void* write_keys, const void* read_queries,
                           const void* values, const void* forget_gate, const void* input_gate, const void* subkeys,
                           void* bank, void* out, int32_t* write_idx, int32_t* read_idx, void* workspace,
@@ -338,7 +349,7 @@ sdm_status sdm_layer_backward(const sdm_layer_config* cfg, const void* x, const 
 sdm_status sdm_bank_grad_sum(const sdm_config* cfg, const void* grad_bank, float* grad_initial_bank, void* stream);
 
 /* Kernel timing (diagnostics, not part of the method). While enabled, every kernel launch of this library is
- * bracketed by a pair of HIP events recorded on the call's stream. sdm_profile_read waits for the recorded events
+ * bracketed by a pair of HIP events recorded on the stream it runs on. sdm_profile_read waits for the recorded events
  * and returns, per kernel family, the summed milliseconds (ms) and the number of launches (launches) since timing
  * was enabled; both arrays have SDM_K_COUNT entries and are owned by the caller. Enabling resets the totals;
  * disabling drops pending events. Not thread-safe with concurrent calls on other threads. */

@@ -456,6 +456,41 @@ def test_write_read_split_at_chunk_multiple_is_bitwise():
     assert np.array_equal(np.concatenate([w1, w2], 1), full[2])
 
 
+PIPE_CASES = [
+    # four streams of 512-byte bf16 rows (the narrow loop's 128 workgroups), three factors, chunk 128
+    ("narrow_3f", synth.Shape(1, 1024, 4, (64, 32, 32), 32, 256, 64, 64, 128, "bf16", "bf16", name="pipe_narrow")),
+    # two batch rows (windows of whole 16-token multiples), float32 bank on the held-row loop, chunk 32
+    ("held_b2", synth.Shape(2, 320, 2, (16, 16), 16, 64, 16, 16, 32, "bf16", "f32", name="pipe_held")),
+    # one batch row, chunk 7 (segmented loop) with a ragged last chunk
+    ("segmented_c7", synth.Shape(1, 100, 2, (16, 16), 8, 48, 8, 8, 7, "f32", "f32", name="pipe_seg")),
+]
+
+
+@pytest.mark.parametrize("name,s", PIPE_CASES, ids=[c[0] for c in PIPE_CASES])
+def test_write_read_pipelined_equals_chunk_calls(name, s):
+    """Calls whose chunk loop leaves most compute units free run as pieces, the top-k and plan of the next piece
+    beside the loop of this one on a second stream: bitwise equal to one call per chunk (each run in order), and
+    within the oracle's tolerance."""
+    x = synth.make_inputs(s, seed=61)
+    print(f"write/read pipelined {name}", flush=True)
+    full = run_gpu(s, x)
+    check_parity(s, full, run_oracle(s, x))
+    outs, widx, ridx = [], [], []
+    bank = None
+    for t0 in range(0, s.tokens, s.chunk_size):
+        t1 = min(s.tokens, t0 + s.chunk_size)
+        part = {k: (np.ascontiguousarray(v[:, t0:t1]) if k in ("wkeys", "rq", "values", "alpha", "beta") else v)
+                for k, v in x.items()}
+        o, bank, w, r = run_gpu(s.with_(tokens=t1 - t0), part, bank=bank)
+        outs.append(o)
+        widx.append(w)
+        ridx.append(r)
+    assert np.array_equal(np.concatenate(outs, 1), full[0])
+    assert np.array_equal(bank, full[1])
+    assert np.array_equal(np.concatenate(widx, 1), full[2])
+    assert np.array_equal(np.concatenate(ridx, 1), full[3])
+
+
 def test_write_read_empty_tokens():
     s = synth.WORKLOADS["tiny_1k"].with_(tokens=0)
     x = synth.make_inputs(s)
