@@ -29,9 +29,11 @@ namespace sdm {
 // Number of keys the event sort works on: the chunk's events padded to 4096 or 8192 (C W <= 8192).
 __host__ __device__ inline int plan_sort_n(int CW) { return CW <= 4096 ? 4096 : 8192; }
 
+constexpr int PLAN_HIST_BYTES = (PLAN_NT / 64) * 256 * 4;
+
 // LDS layout of the plan kernel (16-byte aligned parts).
 struct PlanLds {
-  size_t keys, sslot, sev, pos, scode, sA, sB, kmask, qmask, rmask, roff, lev, loff, tot, bytes;
+  size_t keys, sslot, sev, pos, scode, sA, sB, kmask, qmask, rmask, roff, lev, loff, tot, hist, bytes;
   int kwm, qwm;  // 64-bit words per token of the K / Q term masks
 };
 
@@ -57,6 +59,10 @@ __host__ __device__ inline PlanLds plan_lds(int C, int W, int R) {
   L.lev = o;   o += align16((long long)C * 4);
   L.loff = o;  o += align16((long long)(C + 2) * 4);
   L.tot = o;   o += align16(3 * 8 * 4 + 16);
+  // radix sort: per-wave digit counts, then offsets (8 KiB); in the slot array, free during the sort, when it is
+  // that large
+  L.hist = CW * 4 >= (size_t)PLAN_HIST_BYTES ? L.sslot : o;
+  if (CW * 4 < (size_t)PLAN_HIST_BYTES) o += PLAN_HIST_BYTES;
   L.bytes = o;
   return L;
 }
@@ -206,6 +212,94 @@ __device__ void sort_keys(uint64_t* keys) {
   __syncthreads();
 }
 
+// Stable LSD radix sort of the first E of NS = 512 * EPT 32-bit keys (slot << EB | event index) on their slot bits
+// [EB, EB + sbits), 8-bit digits: the events come out ordered by (slot, event index), as the 64-bit bitonic sort
+// orders them, in a fraction of its steps. Wave w takes keys [w BW, (w + 1) BW) in rows j of 64 (index
+// w BW + j 64 + lane), the order a stable pass keeps: in each row a key's rank among equal digits comes from the
+// digit bits' ballots, plus the wave's running count of that digit (the digit's lowest lane adds the row's count);
+// an exclusive scan in (digit, wave) order then gives every (wave, digit) its first output index. loc: E entries of
+// scratch for the keys' ranks within their wave and digit. Keys ping-pong between src and dst; returns the buffer
+// holding the result.
+template <int EPT>
+__device__ uint32_t* radix_sort_keys(uint32_t* src, uint32_t* dst, uint16_t* loc, int* hist, int* tot, int E, int EB,
+                                     int sbits) {
+  constexpr int BW = 64 * EPT;
+  constexpr int NWV = PLAN_NT / 64;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const uint64_t below = lanes_below();
+  int* wh = hist + wv * 256;
+  for (int shift = EB; shift < EB + sbits; shift += 8) {
+    const int bits = EB + sbits - shift < 8 ? EB + sbits - shift : 8;
+    const uint32_t dmask = (1u << bits) - 1u;
+    for (int i = lane; i < 256; i += 64) wh[i] = 0;
+    wave_sync_lds();
+#pragma unroll 1
+    for (int j = 0; j < EPT; ++j) {
+      const int i = wv * BW + j * 64 + lane;
+      const bool real = i < E;
+      const uint32_t d = (src[i] >> shift) & dmask;
+      uint64_t m = __ballot(real);
+      for (int b = 0; b < bits; ++b) {
+        const uint64_t bb = __ballot((d >> b) & 1u);
+        m &= ((d >> b) & 1u) ? bb : ~bb;
+      }
+      if (real) {
+        const int cur = wh[d];
+        loc[i] = (uint16_t)(cur + __popcll(m & below));
+        if ((m & below) == 0ull) wh[d] = cur + __popcll(m);  // the digit's lowest lane in this row
+      }
+      wave_sync_lds();
+    }
+    __syncthreads();
+    // first output index of every (wave, digit): digits in order, waves in order within a digit (threads 0..255
+    // own the digits; the others read along and write nothing)
+    {
+      const int d = threadIdx.x & 255;
+      int c[NWV], sum = 0;
+#pragma unroll
+      for (int w = 0; w < NWV; ++w) { c[w] = hist[w * 256 + d]; sum += c[w]; }
+      const int incl = wave_incl_scan(sum);
+      if (lane == 63 && threadIdx.x < 256) tot[wv] = incl;
+      __syncthreads();
+      if (threadIdx.x < 256) {
+        int base = incl - sum;
+        for (int w = 0; w < wv; ++w) base += tot[w];
+#pragma unroll
+        for (int w = 0; w < NWV; ++w) { hist[w * 256 + d] = base; base += c[w]; }
+      }
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int j = 0; j < EPT; ++j) {
+      const int i = wv * BW + j * 64 + lane;
+      if (i < E) {
+        const uint32_t k = src[i];
+        dst[wh[(k >> shift) & dmask] + loc[i]] = k;
+      }
+    }
+    __syncthreads();
+    uint32_t* t = src; src = dst; dst = t;
+  }
+  return src;
+}
+
+// Lower bounds of Q slots j[q] in the sorted slots s[0..E) (E >= 1), the searches interleaved: every step halves the
+// same range length for all of them (branch-free), so their LDS reads go out together.
+template <int Q>
+__device__ __forceinline__ void lower_bound_slots(const int32_t* s, int E, const int (&j)[Q], int (&out)[Q]) {
+  int base[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) base[q] = 0;
+  for (int n = E; n > 1;) {
+    const int half = n >> 1;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) base[q] = s[base[q] + half] < j[q] ? base[q] + half : base[q];
+    n -= half;
+  }
+#pragma unroll
+  for (int q = 0; q < Q; ++q) out[q] = base[q] + (s[base[q]] < j[q] ? 1 : 0);
+}
+
 // Lower bound of slot j in the sorted slots s[0..E).
 __device__ __forceinline__ int lower_bound_slot(const int32_t* s, int E, int j) {
   int l = 0, r = E;
@@ -294,7 +388,11 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
 
   const PlanLds PL = plan_lds(C, W, R);
   uint64_t* keys = (uint64_t*)(lds + PL.keys);
-  float* sw = (float*)(lds + PL.keys);     // after the sort: write weights in sorted event order
+  // after the sort: write weights in sorted event order, behind the dense rows when both fit in the sort keys'
+  // area (then K and Q read them there instead of from global memory)
+  const int swoff = (int)align16((long long)C * C * 4);
+  const bool swkeep = swoff + (long long)C * W * 4 <= (long long)NS * 8;
+  float* sw = (float*)(lds + PL.keys + (swkeep ? swoff : 0));
   float* dense = (float*)(lds + PL.keys);  // after the segments: K, T, Q rows
   int32_t* sslot = (int32_t*)(lds + PL.sslot);
   uint16_t* sev = (uint16_t*)(lds + PL.sev);
@@ -310,11 +408,20 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
   int* loff = (int*)(lds + PL.loff);
   int* tot = (int*)(lds + PL.tot);
 
-  // 1. write events -> sort keys (slot, event index); gates of the chunk; empty term masks.
+  // 1. write events -> sort keys (slot, event index); gates of the chunk; empty term masks. Slot and event index
+  //    packed in 32 bits when they fit (radix sort), else 64-bit keys (bitonic sort).
+  const int EB = NS == 4096 ? 12 : 13;
+  const int SB = D.N > 1 ? 64 - __clzll((unsigned long long)(D.N - 1)) : 1;  // bits of the largest slot
+  const bool radix = SB + EB <= 32;
+  uint32_t* keys32 = (uint32_t*)keys;
   for (int e = tid; e < NS; e += PLAN_NT) {
-    uint64_t key = ~0ull;
-    if (e < E) key = ((uint64_t)(uint32_t)a.widx[wbase + e] << 32) | (uint32_t)e;
-    keys[e] = key;
+    if (radix) {
+      keys32[e] = e < E ? ((uint32_t)a.widx[wbase + e] << EB) | (uint32_t)e : ~0u;
+    } else {
+      uint64_t key = ~0ull;
+      if (e < E) key = ((uint64_t)(uint32_t)a.widx[wbase + e] << 32) | (uint32_t)e;
+      keys[e] = key;
+    }
   }
   for (int t = tid; t < C; t += PLAN_NT) {
     float al = 1.0f, be = 0.0f;
@@ -329,12 +436,25 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
   for (int i = tid; i < C * PL.kwm; i += PLAN_NT) kmask[i] = 0ull;
   for (int i = tid; i < C * PL.qwm; i += PLAN_NT) qmask[i] = 0ull;
   __syncthreads();
-  if (NS == 4096) sort_keys<8>(keys); else sort_keys<16>(keys);
-  for (int e = tid; e < E; e += PLAN_NT) {
-    const uint64_t k = keys[e];
-    sslot[e] = (int32_t)(k >> 32);
-    sev[e] = (uint16_t)(k & 0xFFFF);
-    pos[k & 0xFFFF] = (uint16_t)e;
+  if (radix) {
+    const uint32_t* sorted = NS == 4096
+        ? radix_sort_keys<8>(keys32, keys32 + NS, pos, (int*)(lds + PL.hist), tot, E, EB, SB)
+        : radix_sort_keys<16>(keys32, keys32 + NS, pos, (int*)(lds + PL.hist), tot, E, EB, SB);
+    for (int e = tid; e < E; e += PLAN_NT) {
+      const uint32_t k = sorted[e];
+      const uint32_t ev = k & ((1u << EB) - 1u);
+      sslot[e] = (int32_t)(k >> EB);
+      sev[e] = (uint16_t)ev;
+      pos[ev] = (uint16_t)e;
+    }
+  } else {
+    if (NS == 4096) sort_keys<8>(keys); else sort_keys<16>(keys);
+    for (int e = tid; e < E; e += PLAN_NT) {
+      const uint64_t k = keys[e];
+      sslot[e] = (int32_t)(k >> 32);
+      sev[e] = (uint16_t)(k & 0xFFFF);
+      pos[k & 0xFFFF] = (uint16_t)e;
+    }
   }
   __syncthreads();
   {  // write weights in sorted event order (loads issued together: the flat loads may not pass the LDS stores)
@@ -459,11 +579,11 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
         const int evi = t * W + i;
         const int e = pos[evi];
         const int slot = sslot[e];
-        const float wt = a.wwt[wbase + evi];
+        const float wt = swkeep ? sw[e] : a.wwt[wbase + evi];
         float prod = 1.0f;
         for (int e2 = e - 1; e2 >= 0 && sslot[e2] == slot; --e2) {
           const int s = sev[e2] / W;
-          dense[t * C + s] += wt * a.wwt[wbase + sev[e2]] * prod;
+          dense[t * C + s] += wt * (swkeep ? sw[e2] : a.wwt[wbase + sev[e2]]) * prod;
           prod *= sA[s];
         }
       }
@@ -582,13 +702,15 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
         jj[k] = a.ridx[rbase + x];
         rr[k] = a.rwt[rbase + x];
       });
+      int lbs[QB];
+      lower_bound_slots<QB>(sslot, E, jj, lbs);
       static_for<QB>([&](auto kc) {
         constexpr int k = decltype(kc)::value;
         const int x = x0 + k * nth;
         if (x < nx) {
           const int t = x / R;
           const int j = jj[k];
-          const int l = lower_bound_slot(sslot, E, j);
+          const int l = lbs[k];
           float prod = 1.0f;
           if (l < E && sslot[l] == j && sev[l] / W <= t) {
             int e1 = l;
@@ -626,7 +748,7 @@ __global__ __launch_bounds__(PLAN_NT) void plan_kernel(Dims D, PlanArgs a) {
         float prod = 1.0f;
         for (int e2 = e1; e2 >= l; --e2) {
           const int s = sev[e2] / W;
-          dense[t * C + s] += rho * a.wwt[wbase + sev[e2]] * prod;
+          dense[t * C + s] += rho * (swkeep ? sw[e2] : a.wwt[wbase + sev[e2]]) * prod;
           prod *= sA[s];
         }
       }
