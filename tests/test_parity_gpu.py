@@ -491,6 +491,67 @@ def test_write_read_pipelined_equals_chunk_calls(name, s):
     assert np.array_equal(np.concatenate(ridx, 1), full[3])
 
 
+def test_write_read_pipelined_from_two_threads():
+    """Two host threads, each with its own stream, workspace and bank, run pipelined calls at the same time (the
+    library's side stream is shared; a call enqueues its pieces under a lock): every result equals the same calls
+    run one after another."""
+    import threading
+    s = PIPE_CASES[0][1].with_(tokens=512)
+    jobs = []
+    for seed in (63, 64):
+        x = synth.make_inputs(s, seed=seed)
+        t = {k: to_dev(x[k], torch.bfloat16) for k in ("wkeys", "rq", "values", "alpha", "beta", "subkeys")}
+        jobs.append((t, to_dev(x["bank"], torch.bfloat16)))
+    kw = dict(widths=s.widths, num_writes=s.num_writes, num_reads=s.num_reads, chunk_size=s.chunk_size)
+    print("write/read pipelined from two threads", flush=True)
+
+    def calls(t, bank, n):
+        outs = []
+        for _ in range(n):
+            o, _, _ = binding.sdm_write_read(t["wkeys"], t["rq"], t["values"], t["alpha"], t["beta"], t["subkeys"],
+                                             bank, **kw)
+            outs.append(o)
+        return outs
+
+    ref = []
+    for t, bank0 in jobs:  # one after another, on the current stream
+        bank = bank0.clone()
+        outs = calls(t, bank, 3)
+        torch.cuda.synchronize()
+        ref.append(([to_np(o) for o in outs], to_np(bank)))
+    got = [None, None]
+
+    def worker(i):
+        t, bank0 = jobs[i]
+        st = torch.cuda.Stream()
+        with torch.cuda.stream(st):
+            bank = bank0.clone()
+            outs = calls(t, bank, 3)
+        st.synchronize()
+        got[i] = ([to_np(o) for o in outs], to_np(bank))
+
+    torch.cuda.synchronize()
+    th = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for x in th:
+        x.start()
+    for x in th:
+        x.join()
+    for i in range(2):
+        assert got[i] is not None, f"thread {i} failed"
+        for a, b in zip(got[i][0], ref[i][0]):
+            assert np.array_equal(a, b)
+        assert np.array_equal(got[i][1], ref[i][1])
+
+
+def test_write_read_two_million_slots():
+    """2,097,152 slots (factors 1024 x 2048): a slot id and an event index need more than 32 bits together, so the
+    chunk plan sorts its events with 64-bit keys (bitonic) instead of the 32-bit radix sort; parity with the oracle."""
+    s = synth.Shape(1, 96, 1, (1024, 2048), 16, 16, 8, 8, 32, "f32", "f32", name="slots_2m")
+    x = synth.make_inputs(s, seed=62)
+    print("write/read 2,097,152 slots", flush=True)
+    check_parity(s, run_gpu(s, x), run_oracle(s, x))
+
+
 def test_write_read_empty_tokens():
     s = synth.WORKLOADS["tiny_1k"].with_(tokens=0)
     x = synth.make_inputs(s)
