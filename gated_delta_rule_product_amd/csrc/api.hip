@@ -480,8 +480,9 @@ sdm_status topk_product_keys(const sdm_config* cfg, const void* queries, const v
 // The loop of piece p waits for its own plan only, and its launches are those of calls split at the pieces'
 // chunk boundaries, which give the bits of one call. With the chip full of loop workgroups the side stream's work
 // would only queue behind them, so it is not used then. The side stream (default priority) and its events are made
-// once per device, outside any stream capture, and kept until the process ends; a call forks the side stream from
-// the caller's stream and joins it back before it returns (under capture, ordinary graph dependencies).
+// once per device and kept until the process ends; a call forks the side stream from the caller's stream and joins
+// it back before it returns. A call on a capturing stream runs in order on that stream: a side stream that joined a
+// capture would stay in it until the capture ends, and another thread's calls would then be recorded into it.
 namespace {
 constexpr int PIPE_MAX = 16;
 struct PipeDev {
@@ -494,22 +495,33 @@ constexpr int PIPE_DEVICES = 64;
 std::mutex g_pipe_mu;  // held while a call enqueues its pieces (one set of events per device)
 PipeDev g_pipe[PIPE_DEVICES];
 
-// The current device's side stream and events, or nullptr (made on the first call outside a stream capture).
+// The current device's side stream and events for a call on `st`, or nullptr: `st` is capturing, or they could not
+// be made (another thread's capture may forbid it for now; then a later call tries again).
 PipeDev* pipe_device(hipStream_t st) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= PIPE_DEVICES) return nullptr;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
   PipeDev& p = g_pipe[dev];
   if (!p.tried) {
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
-    p.tried = true;
-    bool made = hipDeviceGetAttribute(&p.cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-                hipStreamCreateWithFlags(&p.side, hipStreamNonBlocking) == hipSuccess;
-    for (int i = 0; made && i < PIPE_MAX + 2; ++i)
-      made = hipEventCreateWithFlags(&p.ev[i], hipEventDisableTiming) == hipSuccess;
-    if (!made) p.side = nullptr;  // whatever was made is kept, never used
+    PipeDev n;
+    bool made = hipDeviceGetAttribute(&n.cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+                hipStreamCreateWithFlags(&n.side, hipStreamNonBlocking) == hipSuccess;
+    int ne = 0;
+    while (made && ne < PIPE_MAX + 2) {
+      made = hipEventCreateWithFlags(&n.ev[ne], hipEventDisableTiming) == hipSuccess;
+      if (made) ++ne;
+    }
+    if (!made) {  // give back what was made
+      for (int i = 0; i < ne; ++i) (void)hipEventDestroy(n.ev[i]);
+      if (n.side) (void)hipStreamDestroy(n.side);
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    n.tried = true;
+    p = n;
   }
-  return p.side ? &p : nullptr;
+  return &p;
 }
 
 // Chunks per piece of a pipelined call, or 0 to run the call in order on the caller's stream.

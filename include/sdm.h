@@ -155,9 +155,9 @@ sdm_status topk_product_keys(const sdm_config* cfg, const void* queries, const v
  * as up to 16 pieces of whole chunks, the top-k and plan of each piece on a side stream that the library makes once
  * per device (default priority, kept until the process ends) and the chunk loop of each piece on `stream` after
  * that piece's plan: the bits of calls split at those chunks, with the top-k and plan hidden behind the loop. The
- * side stream waits for `stream` at the call's start and `stream` waits for it before the call returns, also under
- * stream capture (a graph records the fork and join as dependencies). Calls from several host threads take turns
- * on the side stream. Not with shared_bank (its slot check needs every token's top-k before any plan). */
+ * side stream waits for `stream` at the call's start and `stream` waits for it before the call returns. Calls from
+ * several host threads take turns on the side stream. A call on a capturing stream, and a call with shared_bank
+ * (its slot check needs every token's top-k before any plan), run in order on `stream`. */
 sdm_status sdm_write_read(const sdm_config* cfg, const void* write_keys, const void* read_queries,
                           const void* values, const void* forget_gate, const void* input_gate, const void* subkeys,
                           void* bank, void* out, int32_t* write_idx, int32_t* read_idx, void* workspace,
