@@ -497,7 +497,7 @@ PipeDev g_pipe[PIPE_DEVICES];
 
 // The current device's side stream and events for a call on `st`, or nullptr: `st` is capturing, or they could not
 // be made (another thread's capture may forbid it for now; then a later call tries again).
-PipeDev* pipe_device(hipStream_t st) {
+static PipeDev* pipe_device(hipStream_t st) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= PIPE_DEVICES) return nullptr;
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
@@ -525,7 +525,7 @@ PipeDev* pipe_device(hipStream_t st) {
 }
 
 // Chunks per piece of a pipelined call, or 0 to run the call in order on the caller's stream.
-int pipe_chunks(const Dims& D, bool snapshot, const PipeDev* pd) {
+static int pipe_chunks(const Dims& D, bool snapshot, const PipeDev* pd) {
   if (pd == nullptr || D.shared || D.nch < 2) return 0;
   if (loop_workgroups(D, snapshot) * 2 > pd->cus) return 0;
   const int per = (D.nch + PIPE_MAX - 1) / PIPE_MAX;
@@ -1050,7 +1050,7 @@ struct LayerWs {
   size_t dO, gk, gq, gv, gal, gbe, dp, tparam, w_outT, gyT, oT, xT, w_inT, dpT, btotal;  // the backward
   long long Mp, Np;                                             // B T and the input map's width, padded to 64
 };
-sdm_status layer_layout(const sdm_layer_config* cfg, LayerWs* L) {
+static sdm_status layer_layout(const sdm_layer_config* cfg, LayerWs* L) {
   if (!cfg) return fail(SDM_ERR_NULL, "cfg must not be NULL");
   if (cfg->reserved != 0) return fail(SDM_ERR_RANGE, "sdm_layer_config.reserved must be 0");
   if (cfg->op.shared_bank) return fail(SDM_ERR_RANGE, "the layer does not take a shared bank");
@@ -1121,7 +1121,7 @@ sdm_status sdm_layer_workspace_size(const sdm_layer_config* cfg, size_t* bytes) 
 }
 
 namespace {
-sdm_status layer_forward_impl(const sdm_layer_config* cfg, const void* x, const void* w_in, const float* a_log,
+static sdm_status layer_forward_impl(const sdm_layer_config* cfg, const void* x, const void* w_in, const float* a_log,
                               const float* dt_bias, const void* w_out, const void* subkeys, const void* initial_bank,
                               void* bank, void* y, void* snapshot, int32_t* write_idx, int32_t* read_idx,
                               void* workspace, size_t workspace_bytes, void* stream) {
