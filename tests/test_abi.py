@@ -25,6 +25,18 @@ def test_exports_every_declared_function(lib):
         assert hasattr(lib, n), n
 
 
+def test_exports_no_other_c_function():
+    """Every unmangled function the library exports is one the header declares (helpers keep internal linkage)."""
+    import shutil
+    import subprocess
+    if not os.path.exists(B.LIB_PATH) or shutil.which("nm") is None:
+        pytest.skip("needs the built library and nm")
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = {f[2] for f in (ln.split() for ln in out.stdout.splitlines())
+                if len(f) == 3 and f[1] == "T" and not f[2].startswith("_Z")}
+    assert exported <= set(B.declared_functions()), sorted(exported - set(B.declared_functions()))
+
+
 def test_binding_refuses_to_run_without_the_library(monkeypatch):
     monkeypatch.setattr(B, "_lib", None)
     monkeypatch.setattr(B, "LIB_PATH", "/nonexistent/libsdm.so")
