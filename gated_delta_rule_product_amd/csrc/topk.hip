@@ -93,8 +93,8 @@ __host__ __device__ inline size_t topk2_wave_lds(int F, int kpmax, int k, int QW
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-// Largest Euclidean norm of the sub-key rows of each factor (fp64 sum of squares, rounded up to float32):
-// snmax[h][f]. One block per (factor, head); the maximum is order independent.
+// Largest Euclidean norm of the sub-key rows of each factor (fp64 sum of squares, rounded up to float32; +inf when a
+// row holds an infinity or a NaN): snmax[h][f]. One block per (factor, head); the maximum is order independent.
 __global__ __launch_bounds__(256) void subkey_maxnorm_kernel(const bf16_t* __restrict__ sub, Dims D,
                                                              float* __restrict__ snmax) {
   __shared__ float wmax[4];
@@ -113,7 +113,8 @@ __global__ __launch_bounds__(256) void subkey_maxnorm_kernel(const bf16_t* __res
       const double y = (double)bf16_to_f(r[c]);
       s2 = fma(y, y, s2);
     }
-    m = fmaxf(m, __double2float_ru(sqrt(s2) * (1.0 + 0x1p-40)));
+    const float nr = __double2float_ru(sqrt(s2) * (1.0 + 0x1p-40));
+    m = nr == nr ? fmaxf(m, nr) : INFINITY;  // a row with a NaN counts as unbounded
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
@@ -187,25 +188,42 @@ __device__ void factor_topk_filtered(const Dims& D, const TopkArgs& a, int f, in
       bv[u][0] = load_bf16x8(row);
       if (KB > 1) bv[u][1] = load_bf16x8(row + 32);
     });
+    // the batch's MFMAs first (tiles past the end score the last tile again and are not stored), then the stores
+    f32x4_t acc[TB];
     static_for<TB>([&](auto tc) {
       constexpr int u = decltype(tc)::value;
-      const int T = T0 + u * NW + wv;
-      if (T < ntile) {
-        const bf16_t* row = tab + (long long)(T * 16 + ql) * dk + pt * 8;
-        f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0], bv[u][0], acc, 0, 0, 0);
-        if (KB > 1) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[1], bv[u][1], acc, 0, 0, 0);
-        static_for<KBMAX - 2>([&](auto kc) {  // dk = 96, 128: the remaining blocks, loaded here
-          constexpr int kb = decltype(kc)::value + 2;
-          if (kb < KB) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kb], load_bf16x8(row + kb * 32), acc, 0, 0, 0);
-        });
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {  // D row 4 (lane / 16) + r = query, column lane % 16 = sub-key in the tile
-          const int qi = 4 * pt + r;
-          if (qi < nqa) scs[qi * 64 * NPL + T * 16 + ql] = acc[r];
-        }
-      }
+      const bf16_t* row = tab + (long long)(min(T0 + u * NW + wv, ntile - 1) * 16 + ql) * dk + pt * 8;
+      acc[u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0], bv[u][0], acc[u], 0, 0, 0);
+      if (KB > 1) acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[1], bv[u][1], acc[u], 0, 0, 0);
+      static_for<KBMAX - 2>([&](auto kc) {  // dk = 96, 128: the remaining blocks, loaded here
+        constexpr int kb = decltype(kc)::value + 2;
+        if (kb < KB)
+          acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kb], load_bf16x8(row + kb * 32), acc[u], 0, 0, 0);
+      });
     });
+    // D row 4 (lane / 16) + r = query, column lane % 16 = sub-key in the tile; a lane's four rows are all stored or
+    // none unless the tile's last query falls inside them
+    if (4 * pt + 4 <= nqa) {
+      static_for<TB>([&](auto tc) {
+        constexpr int u = decltype(tc)::value;
+        const int T = T0 + u * NW + wv;
+        if (T < ntile) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) scs[(4 * pt + r) * 64 * NPL + T * 16 + ql] = acc[u][r];
+        }
+      });
+    } else if (4 * pt < nqa) {
+      static_for<TB>([&](auto tc) {
+        constexpr int u = decltype(tc)::value;
+        const int T = T0 + u * NW + wv;
+        if (T < ntile) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (4 * pt + r < nqa) scs[(4 * pt + r) * 64 * NPL + T * 16 + ql] = acc[u][r];
+        }
+      });
+    }
   }
   if constexpr (BLK) {
     __syncthreads();  // every tile's scores in LDS
@@ -221,22 +239,22 @@ __device__ void factor_topk_filtered(const Dims& D, const TopkArgs& a, int f, in
   for (int q = 0; q < nq; ++q) {
     const double nx = sqrt(__shfl(nx2, row0 + q, 64)) * (1.0 + 0x1p-40);
     const double E = (dk + 2) * 0x1p-23 * nx * cmax * (1.0 + 0x1p-20) + dk * 0x1p-125 * (nx + cmax + 1.0);
-    bool bad = !(E <= 1e300);
+    // Every s^ is finite when |x| |c| <= 2^127: each partial sum of the MFMA, in any order, is at most
+    // sum_i |x_i c_i| (1 + 2^-24)^dk <= |x| |c| (1 + 2^-17) for dk <= 128 (Cauchy-Schwarz), far below the float32
+    // maximum. Otherwise (large or non-finite inputs: the norm of a non-finite row is +inf, a NaN query gives a NaN
+    // bound) every sub-key is kept and scored exactly.
+    const bool anybad = __ballot(!(E <= 1e300 && nx * cmax <= 0x1p127)) != 0ull;
+    const float* srow = scs + q * 64 * NPL;
+    float sv[NPL];  // the lane's s^ (-inf past the factor), kept for the compaction below
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) sv[j] = srow[lane + 64 * j];  // inside the row buffer: read without a bound
     float lmax = -INFINITY, lmax2 = -INFINITY;  // the lane's largest and second largest s^
-    float sv[NPL];                               // the lane's s^, kept for the compaction below
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
-      const int i = lane + 64 * j;
-      sv[j] = -INFINITY;
-      if (i < n) {
-        const float sh = scs[q * 64 * NPL + i];
-        sv[j] = sh;
-        bad |= !(fabsf(sh) <= 3.4028234663852886e38f);
-        lmax2 = fmaxf(lmax2, fminf(lmax, sh));
-        lmax = fmaxf(lmax, sh);
-      }
+      sv[j] = lane + 64 * j < n ? sv[j] : -INFINITY;
+      lmax2 = fmaxf(lmax2, fminf(lmax, sv[j]));
+      lmax = fmaxf(lmax, sv[j]);
     }
-    const bool anybad = __ballot(bad) != 0ull;
     // Wide factors first keep only the sub-keys that can reach a value L that at least k_p of them reach in s^:
     // the k_p-th largest lane maximum (k_p <= 64 lanes hold a value at least that large), or the ceil(k_p / 2)-th
     // largest lane second maximum (that many lanes hold two values at least that large; every lane holds at least
@@ -245,12 +263,8 @@ __device__ void factor_topk_filtered(const Dims& D, const TopkArgs& a, int f, in
     if constexpr (NPL >= 8) {
       auto kth_largest = [&](float v, int need) -> float {  // the need-th largest v over the wave's lanes
         if (need >= 64) return desc_key_value(__ockl_wfred_max_u32(desc_key(v)));  // the smallest
-        uint64_t lk[1] = {((uint64_t)desc_key(v) << 32) | (uint32_t)lane};
-        bool in1[1] = {true};
-        int nd = need, sh1 = 0, cs1 = 64;
-        const uint32_t r1 = radix_select32<1, true>(lk, in1, &nd, &sh1, &cs1);
-        const uint32_t km = ((uint32_t)(lk[0] >> 32) >> sh1) <= (r1 >> sh1) ? (uint32_t)(lk[0] >> 32) : 0u;
-        return desc_key_value(__ockl_wfred_max_u32(km));
+        const uint64_t lk[1] = {((uint64_t)desc_key(v) << 32) | (uint32_t)lane};
+        return desc_key_value(wave_kth_high<1>(lk, need));
       };
       const float L = fmaxf(kth_largest(lmax, kp), kth_largest(lmax2, (kp + 1) / 2));
       const float thrA = (anybad || kp > 64) ? -INFINITY : __double2float_rd((double)L - 2.0 * E);
@@ -269,29 +283,17 @@ __device__ void factor_topk_filtered(const Dims& D, const TopkArgs& a, int f, in
     // v = the smallest of them; keep every candidate with s^ >= v - 2E
     auto stage_b = [&](auto nsc) -> int {
       constexpr int NS = decltype(nsc)::value;
+      // the candidates' sub-key indices, then their s^ (each step's reads in flight together)
+      int ci[NS];
+#pragma unroll
+      for (int j = 0; j < NS; ++j) ci[j] = NPL >= 8 ? (int)klist[min(lane + 64 * j, mA - 1)] : min(lane + 64 * j, n - 1);
       uint64_t key[NS];
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
-        const int r = lane + 64 * j;
-        key[j] = ~0ull;
-        if (r < mA) {
-          const int i = NPL >= 8 ? (int)klist[r] : r;
-          key[j] = ((uint64_t)desc_key(scs[q * 64 * NPL + i]) << 32) | (uint32_t)i;
-        }
+        const uint64_t kj = ((uint64_t)desc_key(srow[ci[j]]) << 32) | (uint32_t)ci[j];
+        key[j] = lane + 64 * j < mA ? kj : ~0ull;
       }
-      bool all[NS];
-#pragma unroll
-      for (int j = 0; j < NS; ++j) all[j] = true;
-      int need = kp, shift = 0, csize = 64 * NS;
-      const uint32_t res = radix_select32<NS, true>(key, all, &need, &shift, &csize);
-      uint32_t kmax = 0;
-#pragma unroll
-      for (int j = 0; j < NS; ++j) {
-        const uint32_t hk = (uint32_t)(key[j] >> 32);
-        if ((hk >> shift) <= (res >> shift) && key[j] != ~0ull) kmax = max(kmax, hk);
-      }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+      const uint32_t kmax = wave_kth_high<NS>(key, kp);
       const float thr = anybad ? -INFINITY : __double2float_rd((double)desc_key_value(kmax) - 2.0 * E);
       wave_sync();  // every lane has read its candidates before the kept list overwrites them
       int m = 0;
@@ -493,28 +495,38 @@ __global__ __launch_bounds__((64 * Topk2Waves<NPL, MF>::NW)) __attribute__((amdg
   for (int q = 0; q < nq; ++q) {
     // candidates below a lower bound on the k-th slot score (two factors) are not selected from
     const float L = ccap >= 128 ? merge_lower_bound(P, F, k, fsc + q * F * kpmax, kpmax) : -INFINITY;
+    // the candidates in groups of up to 8 a lane: the group's tuples (loads in flight together), then the factor
+    // scores one factor at a time; each slot score is the float32 sum over factors left to right
+    constexpr int MB = CPL < 8 ? CPL : 8;
     uint64_t ck[CPL];
     bool keep[CPL];
+    static_for<CPL / MB>([&](auto gc) {
+      constexpr int j0 = decltype(gc)::value * MB;
+      uint64_t tup[MB];
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      const int c = lane + 64 * j;
-      uint64_t key = ~0ull;
-      keep[j] = false;
-      if (c < P.ncand) {
-        const uint64_t tup = cand[c];
-        int p = (int)(tup & 0xFFFF);
-        float S = fsc[(q * F) * kpmax + p];
-        int ps = p;
-        for (int f = 1; f < F; ++f) {
-          p = (int)((tup >> (16 * f)) & 0xFFFF);
-          S = S + fsc[(q * F + f) * kpmax + p];  // float32 sum, left to right
-          ps += p;
-        }
-        key = ((uint64_t)desc_key(S) << 32) | ((uint64_t)ps << 20) | (uint64_t)c;
-        keep[j] = S >= L;
+      for (int u = 0; u < MB; ++u) tup[u] = cand[min(lane + 64 * (j0 + u), P.ncand - 1)];
+      float S[MB];
+      int ps[MB];
+#pragma unroll
+      for (int u = 0; u < MB; ++u) {
+        ps[u] = (int)(tup[u] & 0xFFFF);
+        S[u] = fsc[(q * F) * kpmax + ps[u]];
       }
-      ck[j] = key;
-    }
+      for (int f = 1; f < F; ++f) {
+#pragma unroll
+        for (int u = 0; u < MB; ++u) {
+          const int p = (int)((tup[u] >> (16 * f)) & 0xFFFF);
+          S[u] = S[u] + fsc[(q * F + f) * kpmax + p];
+          ps[u] += p;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < MB; ++u) {
+        const int c = lane + 64 * (j0 + u);
+        ck[j0 + u] = c < P.ncand ? ((uint64_t)desc_key(S[u]) << 32) | ((uint64_t)ps[u] << 20) | (uint64_t)c : ~0ull;
+        keep[j0 + u] = c < P.ncand && S[u] >= L;
+      }
+    });
     select_kept_candidates<CPL, 8>(ck, keep, L > -INFINITY, k, cbuf, ccap, scratch, sorted);
     const long long bt = bt0 + q;
     const long long b = bt / tn, t = a.t0 + bt % tn;

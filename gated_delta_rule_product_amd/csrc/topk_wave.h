@@ -79,6 +79,71 @@ __device__ __forceinline__ uint32_t radix_select32(const uint64_t (&key)[N], con
 extern "C" __device__ __attribute__((const)) unsigned int __ockl_wfred_and_u32(unsigned int);
 extern "C" __device__ __attribute__((const)) unsigned int __ockl_wfred_or_u32(unsigned int);
 
+// Where a radix search over the high halves of the wave's keys (key[j] of every lane, unused slots ~0ull) for the
+// k smallest may start. When at least k lanes hold a used key, the largest lane minimum bounds the k-th smallest
+// high half (each of those lanes holds a key at or below it): keys above it are never selected, so the high bits
+// shared by every used key at or below it (wave AND == wave OR) decide nothing and the search starts below them.
+// Sets *top (the highest bit left to search; -1: every such key shares the whole high half), *res0 (the shared
+// prefix, zero at and below top) and *csize (keys with that prefix); leaves them at 31, 0 and 64 N when bit 31
+// already differs. Wave-uniform k.
+template <int N>
+__device__ __forceinline__ void radix_start(const uint64_t (&key)[N], int k, int* top, uint32_t* res0, int* csize) {
+  uint32_t lmin = ~0u;
+  bool has = false;
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    if (key[j] != ~0ull) {
+      lmin = min(lmin, (uint32_t)(key[j] >> 32));
+      has = true;
+    }
+  }
+  const uint32_t bound = __popcll(__ballot(has)) >= k ? __ockl_wfred_max_u32(has ? lmin : 0u) : ~0u;
+  uint32_t andv = ~0u, orv = 0u;
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    const uint32_t h = (uint32_t)(key[j] >> 32);
+    if (key[j] != ~0ull && h <= bound) { andv &= h; orv |= h; }
+  }
+  andv = __ockl_wfred_and_u32(andv);
+  orv = __ockl_wfred_or_u32(orv);
+  const uint32_t diff = andv ^ orv;
+  *top = 31;
+  *res0 = 0;
+  *csize = 64 * N;
+  if (diff == 0 || (diff >> 31) == 0) {
+    const int t = diff ? 31 - __clz(diff) : -1;  // highest differing bit
+    const int s = t + 1;                         // 1..31, or 0
+    const uint32_t r0 = andv & ~((1u << s) - 1u);
+    int cs = 0;  // keys with that prefix (every key at or below the bound, maybe more)
+#pragma unroll
+    for (int j = 0; j < N; ++j) cs += __popcll(__ballot(((uint32_t)(key[j] >> 32) >> s) == (r0 >> s)));
+    *top = t;
+    *res0 = r0;
+    *csize = cs;
+  }
+}
+
+// The k-th smallest high half of the wave's used keys (unused slots ~0ull; 1 <= k <= used count): the radix search
+// from radix_start; when it stops early, the largest high half of the decided class is the k-th.
+template <int N>
+__device__ __forceinline__ uint32_t wave_kth_high(const uint64_t (&key)[N], int k) {
+  int top, csize;
+  uint32_t res0;
+  radix_start<N>(key, k, &top, &res0, &csize);
+  bool all[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) all[j] = true;
+  int need = k, shift = 0;
+  const uint32_t hi = radix_select32<N, true>(key, all, &need, &shift, &csize, top, res0);
+  uint32_t km = 0;
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    const uint32_t h = (uint32_t)(key[j] >> 32);
+    if (key[j] != ~0ull && (h >> shift) <= (hi >> shift)) km = max(km, h);
+  }
+  return __ockl_wfred_max_u32(km);
+}
+
 // Selects the k smallest of the wave's keys (key[j] of every lane; unused slots hold ~0ull, which no used key
 // equals; k <= number of used slots), writes them ascending to out[0..k). RB: selected keys read per batch in the
 // rank placement (more reads in flight, a larger pad). scratch: >= k + RB entries of this wave's LDS, not
@@ -98,39 +163,9 @@ __device__ void wave_select_sorted(const uint64_t (&key)[N], int k, uint64_t* sc
 #pragma unroll
     for (int j = 0; j < N; ++j) sel[j] = key[j] != ~0ull;
   } else {
-    // A bound on the k-th smallest high half: when at least k lanes hold a used key, the largest lane minimum is
-    // one (each of those lanes holds a key at or below it). Keys above it are never selected, so the high bits
-    // shared by every used key at or below it (wave AND == wave OR) decide nothing: the search starts below them.
-    uint32_t lmin = ~0u;
-    bool has = false;
-#pragma unroll
-    for (int j = 0; j < N; ++j) {
-      if (key[j] != ~0ull) {
-        lmin = min(lmin, (uint32_t)(key[j] >> 32));
-        has = true;
-      }
-    }
-    const uint32_t bound = __popcll(__ballot(has)) >= k ? __ockl_wfred_max_u32(has ? lmin : 0u) : ~0u;
-    uint32_t andv = ~0u, orv = 0u;
-#pragma unroll
-    for (int j = 0; j < N; ++j) {
-      const uint32_t h = (uint32_t)(key[j] >> 32);
-      if (key[j] != ~0ull && h <= bound) { andv &= h; orv |= h; }
-    }
-    andv = __ockl_wfred_and_u32(andv);
-    orv = __ockl_wfred_or_u32(orv);
-    const uint32_t diff = andv ^ orv;
-    int top = 31;
-    uint32_t res0 = 0;
-    if (diff == 0 || (diff >> 31) == 0) {
-      top = diff ? 31 - __clz(diff) : -1;  // highest differing bit (-1: all used keys share the high half)
-      const int s = top + 1;               // 1..31, or 0
-      res0 = andv & ~((1u << s) - 1u);     // the shared prefix, zero at and below top
-      int cs = 0;                          // keys with that prefix (every key at or below the bound, maybe more)
-#pragma unroll
-      for (int j = 0; j < N; ++j) cs += __popcll(__ballot(((uint32_t)(key[j] >> 32) >> s) == (res0 >> s)));
-      csize = cs;
-    }
+    int top;
+    uint32_t res0;
+    radix_start<N>(key, k, &top, &res0, &csize);
     const uint32_t hi = radix_select32<N, true>(key, all, &need, &shift, &csize, top, res0);
     if (csize == need) {  // decided on the high halves
 #pragma unroll

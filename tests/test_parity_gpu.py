@@ -141,6 +141,30 @@ def test_topk_filtered_equals_direct(name):
     assert torch.equal(sc_f, sc_d)
 
 
+def test_topk_filtered_nonfinite_equals_direct():
+    """Inputs the MFMA filter cannot bound: a NaN and an infinite sub-key row, NaN and infinite query values, and a
+    query whose norm times the largest sub-key norm passes 2^127 (finite scores). The filtered scoring keeps every
+    sub-key of such a factor and returns the direct scoring's ids and score bits."""
+    widths, dk, k = (1024, 32), 64, 40
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((1, 48, 3, 2 * dk)).astype(np.float32)
+    sub = rng.standard_normal((3, sum(widths), dk)).astype(np.float32)
+    sub[0, 17, 3] = np.nan            # head 0, factor 0
+    sub[1, 1024 + 5, 0] = np.inf      # head 1, factor 1
+    q[0, 3, 0, 7] = np.nan            # head 0, factor 0
+    q[0, 4, 1, dk + 2] = -np.inf      # head 1, factor 1
+    q[0, 5, 2, :dk] = 5e36            # head 2 (finite sub-keys), factor 0: |x| |c| > 2^127
+    qd, sd = to_dev(q, torch.bfloat16), to_dev(sub, torch.bfloat16)
+    print("topk filtered vs direct, non-finite inputs", flush=True)
+    ids_f, sc_f = binding.topk_product_keys(qd, sd, widths, k, scoring="filtered")
+    torch.cuda.synchronize()
+    ids_d, sc_d = binding.topk_product_keys(qd, sd, widths, k, scoring="direct")
+    torch.cuda.synchronize()
+    assert torch.equal(ids_f, ids_d)
+    assert torch.equal(sc_f.view(torch.int32), sc_d.view(torch.int32))
+    assert bool(torch.isfinite(sc_d[0, 5, 2]).all())  # the large query's scores stay finite
+
+
 def test_topk_zero_query_tie_order():
     q = np.zeros((1, 1, 1, 2 * 8), np.float32)
     sub = np.random.default_rng(0).standard_normal((1, 64, 8)).astype(np.float32)
