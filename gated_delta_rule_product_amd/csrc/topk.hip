@@ -68,14 +68,25 @@ __host__ __device__ constexpr int wave_qw(int npl, bool mf = false) {
 }
 template <int NPL, bool MF = false> struct WaveTile { static constexpr int QW = wave_qw(NPL, MF); };
 
-// Per-wave LDS: factor scores [QW][64 NPL] (float), kept factor lists [QW][F][kpmax] (float score + uint16 id),
-// selection scratch [KS + 8] and sorted output [KS] (uint64).
+// Whether the selection buffers of a wave in block mode (shared score rows; see factor_topk_filtered) live in its own
+// score rows of 256 NPL bytes, which are free once a query's candidates are scored exactly: a factor's selection
+// scratch [KS + 8] and sorted output [KS] (uint64) in the query's row, the merge's compaction buffer [256], scratch
+// and sorted output in the wave's QW rows. KS = max(k_p max, k).
+__host__ __device__ inline bool topk2_rows_scratch(int kpmax, int k, int QW, int NPL, bool shared_scores) {
+  const int KS = kpmax > k ? kpmax : k;
+  const int R = 256 * NPL;
+  return shared_scores && (2 * KS + 8) * 8 <= R && (256 + 2 * KS + 8) * 8 <= QW * R;
+}
+
+// Per-wave LDS: factor scores [QW][64 NPL] (float; block mode: in the workgroup's shared rows), kept factor lists
+// [QW][F][kpmax] (float score + uint16 id), selection scratch [KS + 8] and sorted output [KS] (uint64) unless they
+// live in the score rows. The filtered scoring lists its candidates in each query's score row.
 __host__ __device__ inline size_t topk2_wave_lds(int F, int kpmax, int k, int QW, int NPL, bool shared_scores = false) {
   const int KS = kpmax > k ? kpmax : k;
   size_t n = shared_scores ? 0 : (size_t)QW * 64 * NPL * 4;
   n += (size_t)QW * F * kpmax * 6;
   n = (n + 7) & ~(size_t)7;
-  return n + (size_t)(2 * KS + 8) * 8 + (size_t)64 * NPL * 2;  // + kept-candidate list (filtered scoring)
+  return n + (topk2_rows_scratch(kpmax, k, QW, NPL, shared_scores) ? 0 : (size_t)(2 * KS + 8) * 8);
 }
 
 // ------------------------------------------------------------------------------------------- filtered scoring
@@ -140,7 +151,7 @@ __device__ __forceinline__ bf16x8_t load_bf16x8(const bf16_t* p) {
 template <int NPL, int QW, int NW = 1>
 __device__ void factor_topk_filtered(const Dims& D, const TopkArgs& a, int f, int n, const bf16_t* tab,
                                      const bf16_t* qf, long long qstride, int nq, float* scs, float* fsc,
-                                     uint16_t* fid, uint64_t* scratch, uint64_t* sorted, uint16_t* klist, int kpmax,
+                                     uint16_t* fid, uint64_t* scratch, uint64_t* sorted, int kpmax,
                                      const bf16_t* qb = nullptr, int nqb = 0, int row0 = 0) {
   constexpr int KBMAX = 4;
   constexpr bool BLK = NW > 1;
@@ -236,6 +247,8 @@ __device__ void factor_topk_filtered(const Dims& D, const TopkArgs& a, int f, in
   // any sub-key below that threshold has s < L - E and is not a member (ties included)
   const double cmax = (double)a.snorm[(long long)blockIdx.z * F + f];
   const uint64_t below = lanes_below_mask();
+  const int KS = a.plan[kind].kpmax > a.plan[kind].k ? a.plan[kind].kpmax : a.plan[kind].k;
+  const bool rows_scratch = topk2_rows_scratch(a.plan[kind].kpmax, a.plan[kind].k, QW, NPL, BLK);
   for (int q = 0; q < nq; ++q) {
     const double nx = sqrt(__shfl(nx2, row0 + q, 64)) * (1.0 + 0x1p-40);
     const double E = (dk + 2) * 0x1p-23 * nx * cmax * (1.0 + 0x1p-20) + dk * 0x1p-125 * (nx + cmax + 1.0);
@@ -244,7 +257,12 @@ __device__ void factor_topk_filtered(const Dims& D, const TopkArgs& a, int f, in
     // maximum. Otherwise (large or non-finite inputs: the norm of a non-finite row is +inf, a NaN query gives a NaN
     // bound) every sub-key is kept and scored exactly.
     const bool anybad = __ballot(!(E <= 1e300 && nx * cmax <= 0x1p127)) != 0ull;
-    const float* srow = scs + q * 64 * NPL;
+    // The query's score row (256 NPL bytes) is read into registers first and then holds, in turn, the candidate keys
+    // of the first stage (uint64, up to 32 NPL), the candidates kept for exact scoring (uint16) and, in block mode
+    // when they fit, the selection buffers.
+    float* srow = scs + q * 64 * NPL;
+    uint64_t* row64 = (uint64_t*)srow;
+    uint16_t* klist = (uint16_t*)srow;
     float sv[NPL];  // the lane's s^ (-inf past the factor), kept for the compaction below
 #pragma unroll
     for (int j = 0; j < NPL; ++j) sv[j] = srow[lane + 64 * j];  // inside the row buffer: read without a bound
@@ -260,6 +278,7 @@ __device__ void factor_topk_filtered(const Dims& D, const TopkArgs& a, int f, in
     // largest lane second maximum (that many lanes hold two values at least that large; every lane holds at least
     // four sub-keys here), whichever is larger: usually a small fraction of the factor.
     int mA = n;
+    float thrA = -INFINITY;
     if constexpr (NPL >= 8) {
       auto kth_largest = [&](float v, int need) -> float {  // the need-th largest v over the wave's lanes
         if (need >= 64) return desc_key_value(__ockl_wfred_max_u32(desc_key(v)));  // the smallest
@@ -267,31 +286,42 @@ __device__ void factor_topk_filtered(const Dims& D, const TopkArgs& a, int f, in
         return desc_key_value(wave_kth_high<1>(lk, need));
       };
       const float L = fmaxf(kth_largest(lmax, kp), kth_largest(lmax2, (kp + 1) / 2));
-      const float thrA = (anybad || kp > 64) ? -INFINITY : __double2float_rd((double)L - 2.0 * E);
+      thrA = (anybad || kp > 64) ? -INFINITY : __double2float_rd((double)L - 2.0 * E);
+      wave_sync();  // every lane has read its scores before the candidate keys overwrite the row
       mA = 0;
 #pragma unroll
       for (int j = 0; j < NPL; ++j) {
         const int i = lane + 64 * j;
         const bool kept = i < n && (anybad || sv[j] >= thrA);
         const uint64_t bm = __ballot(kept);
-        if (kept) klist[mA + __popcll(bm & below)] = (uint16_t)i;
+        const int pos = mA + __popcll(bm & below);
+        if (kept && pos < 32 * NPL) row64[pos] = ((uint64_t)desc_key(sv[j]) << 32) | (uint32_t)i;
         mA += __popcll(bm);
       }
       wave_sync();
     }
     // approximate keys of the candidates, the k_p best approximate scores (radix select, stopped once decided),
     // v = the smallest of them; keep every candidate with s^ >= v - 2E
-    auto stage_b = [&](auto nsc) -> int {
+    // LISTED: the first stage's keys from the row (mA <= 32 NPL); otherwise from the registers: every sub-key of the
+    // factor that the first stage kept (narrow factors: all of them), NS = NPL
+    auto stage_b = [&](auto nsc, auto listed) -> int {
       constexpr int NS = decltype(nsc)::value;
-      // the candidates' sub-key indices, then their s^ (each step's reads in flight together)
-      int ci[NS];
-#pragma unroll
-      for (int j = 0; j < NS; ++j) ci[j] = NPL >= 8 ? (int)klist[min(lane + 64 * j, mA - 1)] : min(lane + 64 * j, n - 1);
+      constexpr bool LISTED = decltype(listed)::value;
       uint64_t key[NS];
+      if constexpr (LISTED) {
 #pragma unroll
-      for (int j = 0; j < NS; ++j) {
-        const uint64_t kj = ((uint64_t)desc_key(srow[ci[j]]) << 32) | (uint32_t)ci[j];
-        key[j] = lane + 64 * j < mA ? kj : ~0ull;
+        for (int j = 0; j < NS; ++j) {
+          const uint64_t kj = row64[min(lane + 64 * j, 32 * NPL - 1)];
+          key[j] = lane + 64 * j < mA ? kj : ~0ull;
+        }
+      } else {
+        static_assert(NS == NPL, "keys from the registers: one a sub-key");
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+          const int i = lane + 64 * j;
+          key[j] = i < n && (NPL < 8 || anybad || sv[j] >= thrA) ? ((uint64_t)desc_key(sv[j]) << 32) | (uint32_t)i
+                                                                : ~0ull;
+        }
       }
       const uint32_t kmax = wave_kth_high<NS>(key, kp);
       const float thr = anybad ? -INFINITY : __double2float_rd((double)desc_key_value(kmax) - 2.0 * E);
@@ -309,15 +339,15 @@ __device__ void factor_topk_filtered(const Dims& D, const TopkArgs& a, int f, in
     int m;
     if constexpr (NPL >= 8) {
       if (mA <= 128)
-        m = stage_b(std::integral_constant<int, 2>{});
+        m = stage_b(std::integral_constant<int, 2>{}, std::true_type{});
       else if (mA <= 256)
-        m = stage_b(std::integral_constant<int, 4>{});
+        m = stage_b(std::integral_constant<int, 4>{}, std::true_type{});
       else if (NPL > 8 && mA <= 512)
-        m = stage_b(std::integral_constant<int, 8>{});
+        m = stage_b(std::integral_constant<int, 8>{}, std::true_type{});
       else
-        m = stage_b(std::integral_constant<int, NPL>{});
+        m = stage_b(std::integral_constant<int, NPL>{}, std::false_type{});
     } else {
-      m = stage_b(std::integral_constant<int, NPL>{});
+      m = stage_b(std::integral_constant<int, NPL>{}, std::false_type{});
     }
     wave_sync();
     // exact scores of the kept sub-keys (the fp64 chain), then the exact top k_p among them
@@ -342,22 +372,28 @@ __device__ void factor_topk_filtered(const Dims& D, const TopkArgs& a, int f, in
       }
       return ((uint64_t)desc_key((float)acc) << 32) | (uint32_t)i;
     };
+    // the selection buffers: the row's, once every exact key is in registers, or the wave's own
+    uint64_t* scr = rows_scratch ? row64 : scratch;
+    uint64_t* srt = rows_scratch ? row64 + KS + 8 : sorted;
     if (m <= 64) {
       uint64_t ek[1] = {lane < m ? exact_key(lane) : ~0ull};
-      wave_select_sorted<1>(ek, kp, scratch, sorted);
+      wave_sync();
+      wave_select_sorted<1>(ek, kp, scr, srt);
     } else if (m <= 128) {
       uint64_t ek[2];
       ek[0] = exact_key(lane);
       ek[1] = lane + 64 < m ? exact_key(lane + 64) : ~0ull;
-      wave_select_sorted<2>(ek, kp, scratch, sorted);
+      wave_sync();
+      wave_select_sorted<2>(ek, kp, scr, srt);
     } else {
       uint64_t ek[NPL];
 #pragma unroll
       for (int j = 0; j < NPL; ++j) ek[j] = lane + 64 * j < m ? exact_key(lane + 64 * j) : ~0ull;
-      wave_select_sorted<NPL>(ek, kp, scratch, sorted);
+      wave_sync();
+      wave_select_sorted<NPL>(ek, kp, scr, srt);
     }
     for (int p = lane; p < kp; p += 64) {
-      const uint64_t kk = sorted[p];
+      const uint64_t kk = srt[p];
       fsc[(q * F + f) * kpmax + p] = desc_key_value((uint32_t)(kk >> 32));
       fid[(q * F + f) * kpmax + p] = (uint16_t)(uint32_t)kk;
     }
@@ -382,7 +418,7 @@ template <int NPL, bool MF> struct Topk2Waves {
 
 // QW1: one query per wave (few rows, e.g. a decode step: parallelism over queries rather than reuse of sub-key rows).
 template <typename A, int NPL, int CPL, bool MF, bool QW1>
-__global__ __launch_bounds__((64 * Topk2Waves<NPL, MF>::NW)) __attribute__((amdgpu_waves_per_eu(NPL <= 4 ? 4 : TOPK_WIDE_WPE))) void topk2_kernel(Dims D, TopkArgs a) {
+__global__ __launch_bounds__((64 * Topk2Waves<NPL, MF>::NW)) __attribute__((amdgpu_waves_per_eu((NPL <= 4 || (MF && !QW1)) ? 4 : TOPK_WIDE_WPE))) void topk2_kernel(Dims D, TopkArgs a) {
   constexpr int QW = QW1 ? 1 : WaveTile<NPL, MF>::QW;
   constexpr int NW = QW1 ? 4 : Topk2Waves<NPL, MF>::NW;
   constexpr bool BLK = !QW1 && Topk2Waves<NPL, MF>::BLK;  // block mode of the filtered scoring
@@ -413,8 +449,7 @@ __global__ __launch_bounds__((64 * Topk2Waves<NPL, MF>::NW)) __attribute__((amdg
   uint16_t* fid = (uint16_t*)(fsc + QW * F * kpmax);        // [QW][F][kpmax]
   uint64_t* scratch = (uint64_t*)(wl + (((BLK ? 0 : (size_t)QW * 64 * NPL * 4) + (size_t)QW * F * kpmax * 6 + 7) &
                                         ~(size_t)7));
-  uint64_t* sorted = scratch + KS + 8;
-  uint16_t* klist = (uint16_t*)(sorted + KS);               // [64 NPL] kept candidates (filtered scoring)
+  uint64_t* sorted = scratch + KS + 8;                      // (unused when the score rows hold them)
   long long sumn = 0;
   for (int f = 0; f < F; ++f) sumn += D.widths[f];
   const A* sub = (const A*)a.subkeys + (long long)h * sumn * dk;
@@ -432,14 +467,14 @@ __global__ __launch_bounds__((64 * Topk2Waves<NPL, MF>::NW)) __attribute__((amdg
       const long long bb = (long long)blockIdx.x * NW * QW;  // the workgroup's first row
       const bf16_t* qb = (const bf16_t*)a.queries[kind] + (grow(bb) * D.H + h) * Fdk + f * dk;
       factor_topk_filtered<NPL, QW, NW>(D, a, f, n, (const bf16_t*)tab, (const bf16_t*)qbase + f * dk, qstride, nq,
-                                        scs, fsc, fid, scratch, sorted, klist, kpmax, qb,
+                                        scs, fsc, fid, scratch, sorted, kpmax, qb,
                                         (int)max(0LL, min((long long)NW * QW, BT - bb)), wv * QW);
       off += n;
       continue;
     } else if constexpr (MF) {
       factor_topk_filtered<NPL, QW>(D, a, f, n, (const bf16_t*)tab,
                                     (const bf16_t*)qbase + f * dk, qstride, nq, scs, fsc, fid, scratch, sorted,
-                                    klist, kpmax);
+                                    kpmax);
       off += n;
       continue;
     }
@@ -489,9 +524,15 @@ __global__ __launch_bounds__((64 * Topk2Waves<NPL, MF>::NW)) __attribute__((amdg
     off += n;
   }
 
-  // the merge's compaction buffer: this wave's factor-score rows, free once every factor is done
+  // the merge's compaction buffer: this wave's factor-score rows, free once every factor is done (in block mode with
+  // the selection buffers in the rows: their first 256 entries, the merge's scratch and sorted output after them)
   uint64_t* cbuf = (uint64_t*)(scs + (BLK ? wv * QW * 64 * NPL : 0));
-  const int ccap = QW * 64 * NPL / 2;  // uint64 entries
+  const bool rows_scratch = topk2_rows_scratch(kpmax, k, QW, NPL, BLK);
+  const int ccap = rows_scratch ? 256 : QW * 64 * NPL / 2;  // uint64 entries
+  if (rows_scratch) {
+    scratch = cbuf + 256;
+    sorted = scratch + KS + 8;
+  }
   for (int q = 0; q < nq; ++q) {
     // candidates below a lower bound on the k-th slot score (two factors) are not selected from
     const float L = ccap >= 128 ? merge_lower_bound(P, F, k, fsc + q * F * kpmax, kpmax) : -INFINITY;
