@@ -250,6 +250,10 @@ __device__ void factor_topk_filtered(const Dims& D, const TopkArgs& a, int f, in
   const int KS = a.plan[kind].kpmax > a.plan[kind].k ? a.plan[kind].kpmax : a.plan[kind].k;
   const bool rows_scratch = topk2_rows_scratch(a.plan[kind].kpmax, a.plan[kind].k, QW, NPL, BLK);
   for (int q = 0; q < nq; ++q) {
+    // the lane index taken afresh each query (an empty asm hides its value): the compiler otherwise hoists the
+    // per-slot sub-key indices and bounds derived from it out of this loop and spills them to scratch memory
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
     const double nx = sqrt(__shfl(nx2, row0 + q, 64)) * (1.0 + 0x1p-40);
     const double E = (dk + 2) * 0x1p-23 * nx * cmax * (1.0 + 0x1p-20) + dk * 0x1p-125 * (nx + cmax + 1.0);
     // Every s^ is finite when |x| |c| <= 2^127: each partial sum of the MFMA, in any order, is at most
@@ -267,12 +271,22 @@ __device__ void factor_topk_filtered(const Dims& D, const TopkArgs& a, int f, in
 #pragma unroll
     for (int j = 0; j < NPL; ++j) sv[j] = srow[lane + 64 * j];  // inside the row buffer: read without a bound
     float lmax = -INFINITY, lmax2 = -INFINITY;  // the lane's largest and second largest s^
+    // a factor filling the row (the usual case) takes no per-element bound checks: the compiler would otherwise keep
+    // the sixteen loop-invariant lane masks of i < n in scalar registers, which spill
+    const bool full = n == 64 * NPL;
+    auto lane_max = [&](auto fc) {
+      constexpr bool FULL = decltype(fc)::value;
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) {
-      sv[j] = lane + 64 * j < n ? sv[j] : -INFINITY;
-      lmax2 = fmaxf(lmax2, fminf(lmax, sv[j]));
-      lmax = fmaxf(lmax, sv[j]);
-    }
+      for (int j = 0; j < NPL; ++j) {
+        if (!FULL) sv[j] = lane + 64 * j < n ? sv[j] : -INFINITY;
+        lmax2 = fmaxf(lmax2, fminf(lmax, sv[j]));
+        lmax = fmaxf(lmax, sv[j]);
+      }
+    };
+    if (full)
+      lane_max(std::true_type{});
+    else
+      lane_max(std::false_type{});
     // Wide factors first keep only the sub-keys that can reach a value L that at least k_p of them reach in s^:
     // the k_p-th largest lane maximum (k_p <= 64 lanes hold a value at least that large), or the ceil(k_p / 2)-th
     // largest lane second maximum (that many lanes hold two values at least that large; every lane holds at least
@@ -287,19 +301,30 @@ __device__ void factor_topk_filtered(const Dims& D, const TopkArgs& a, int f, in
       };
       const float L = fmaxf(kth_largest(lmax, kp), kth_largest(lmax2, (kp + 1) / 2));
       thrA = (anybad || kp > 64) ? -INFINITY : __double2float_rd((double)L - 2.0 * E);
-      wave_sync();  // every lane has read its scores before the candidate keys overwrite the row
-      mA = 0;
+      if (!anybad) {  // (otherwise every sub-key is a candidate, taken from the registers)
+        // the candidates listed as (s^ bits, index), up to 32 NPL of them
+        wave_sync();  // every lane has read its scores before the list overwrites the row
+        mA = 0;
+        auto list = [&](auto fc) {
+          constexpr bool FULL = decltype(fc)::value;
 #pragma unroll
-      for (int j = 0; j < NPL; ++j) {
-        const int i = lane + 64 * j;
-        const bool kept = i < n && (anybad || sv[j] >= thrA);
-        const uint64_t bm = __ballot(kept);
-        const int pos = mA + __popcll(bm & below);
-        if (kept && pos < 32 * NPL) row64[pos] = ((uint64_t)desc_key(sv[j]) << 32) | (uint32_t)i;
-        mA += __popcll(bm);
+          for (int j = 0; j < NPL; ++j) {
+            const int i = lane + 64 * j;
+            const bool kept = (FULL || i < n) && sv[j] >= thrA;
+            const uint64_t bm = __ballot(kept);
+            const int pos = mA + __popcll(bm & below);
+            if (kept && pos < 32 * NPL) row64[pos] = ((uint64_t)__float_as_uint(sv[j]) << 32) | (uint32_t)i;
+            mA += __popcll(bm);
+          }
+        };
+        if (full)
+          list(std::true_type{});
+        else
+          list(std::false_type{});
+        wave_sync();
       }
-      wave_sync();
     }
+    const bool listed = NPL >= 8 && !anybad && mA <= 32 * NPL;
     // approximate keys of the candidates, the k_p best approximate scores (radix select, stopped once decided),
     // v = the smallest of them; keep every candidate with s^ >= v - 2E
     // LISTED: the first stage's keys from the row (mA <= 32 NPL); otherwise from the registers: every sub-key of the
@@ -312,7 +337,8 @@ __device__ void factor_topk_filtered(const Dims& D, const TopkArgs& a, int f, in
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
           const uint64_t kj = row64[min(lane + 64 * j, 32 * NPL - 1)];
-          key[j] = lane + 64 * j < mA ? kj : ~0ull;
+          const uint64_t kd = ((uint64_t)desc_key(__uint_as_float((uint32_t)(kj >> 32))) << 32) | (uint32_t)kj;
+          key[j] = lane + 64 * j < mA ? kd : ~0ull;
         }
       } else {
         static_assert(NS == NPL, "keys from the registers: one a sub-key");
@@ -338,11 +364,11 @@ __device__ void factor_topk_filtered(const Dims& D, const TopkArgs& a, int f, in
     };
     int m;
     if constexpr (NPL >= 8) {
-      if (mA <= 128)
+      if (listed && mA <= 128)
         m = stage_b(std::integral_constant<int, 2>{}, std::true_type{});
-      else if (mA <= 256)
+      else if (listed && mA <= 256)
         m = stage_b(std::integral_constant<int, 4>{}, std::true_type{});
-      else if (NPL > 8 && mA <= 512)
+      else if (NPL > 8 && listed)
         m = stage_b(std::integral_constant<int, 8>{}, std::true_type{});
       else
         m = stage_b(std::integral_constant<int, NPL>{}, std::false_type{});
@@ -507,6 +533,8 @@ __global__ __launch_bounds__((64 * Topk2Waves<NPL, MF>::NW)) __attribute__((amdg
       for (int j = 0; j < NPL; ++j) scs[q * 64 * NPL + lane + 64 * j] = (float)acc[q][j];
     wave_sync();
     for (int q = 0; q < nq; ++q) {
+      int lane = threadIdx.x & 63;  // taken afresh (see factor_topk_filtered): nothing derived from it is hoisted
+      asm volatile("" : "+v"(lane));
       uint64_t key[NPL];
 #pragma unroll
       for (int j = 0; j < NPL; ++j) {
@@ -534,6 +562,8 @@ __global__ __launch_bounds__((64 * Topk2Waves<NPL, MF>::NW)) __attribute__((amdg
     sorted = scratch + KS + 8;
   }
   for (int q = 0; q < nq; ++q) {
+    int lane = threadIdx.x & 63;  // taken afresh (see factor_topk_filtered): nothing derived from it is hoisted
+    asm volatile("" : "+v"(lane));
     // candidates below a lower bound on the k-th slot score (two factors) are not selected from
     const float L = ccap >= 128 ? merge_lower_bound(P, F, k, fsc + q * F * kpmax, kpmax) : -INFINITY;
     // the candidates in groups of up to 8 a lane: the group's tuples (loads in flight together), then the factor
