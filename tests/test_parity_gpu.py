@@ -104,7 +104,8 @@ def _topk_case(widths, dk, k, act, kind, B=1, T=24, H=2, seed=0, scoring="auto")
 
 
 @pytest.mark.parametrize("widths,dk,k", [((32, 32), 16, 4), ((32, 32), 16, 64), ((8, 8), 4, 5), ((4, 3, 5), 3, 7),
-                                         ((16,), 4, 6), ((3, 2, 2, 3), 2, 9), ((7, 9), 5, 63), ((64, 32, 32), 8, 64)])
+                                         ((16,), 4, 6), ((3, 2, 2, 3), 2, 9), ((7, 9), 5, 63), ((64, 32, 32), 8, 64),
+                                         ((32, 32), 16, 512)])  # the largest k
 @pytest.mark.parametrize("kind", ["random", "ternary", "dup"])
 @pytest.mark.parametrize("act", ["f32", "bf16"])
 def test_topk_exact(widths, dk, k, kind, act):
@@ -114,7 +115,9 @@ def test_topk_exact(widths, dk, k, kind, act):
 
 @pytest.mark.parametrize("widths,dk,k", [((32, 32), 32, 64), ((64, 32, 16), 64, 64), ((16,), 32, 9),
                                          ((256, 256), 64, 64), ((48, 16), 96, 33), ((32, 32), 128, 17),
-                                         ((512, 16), 32, 64), ((1024, 32), 64, 40)])
+                                         ((512, 16), 32, 64), ((1024, 32), 64, 40),
+                                         # selection buffers too large for the score rows (the per-wave layout)
+                                         ((512, 64), 64, 200), ((1024, 32), 32, 254)])
 @pytest.mark.parametrize("kind", ["random", "ternary", "dup"])
 @pytest.mark.parametrize("scoring", ["filtered", "direct"])
 def test_topk_exact_filtered(widths, dk, k, kind, scoring):
@@ -227,6 +230,16 @@ def test_write_read_dense_limit():
     s = synth.Shape(1, 40, 1, (4, 4), 3, 16, 16, 16, 8, name="dense")
     x = synth.make_inputs(s, seed=6)
     print("write/read dense limit", flush=True)
+    check_parity(s, run_gpu(s, x), run_oracle(s, x))
+
+
+@pytest.mark.parametrize("act,bank", [("f32", "f32"), ("bf16", "bf16")])
+def test_write_read_largest_k(act, bank):
+    """W = R = 512, the largest top-k, on 1024 slots: chunk 16 (16 x 512 = 8192 write events, the loop's largest
+    chunk), 40 tokens (a ragged last chunk); half the slots written and read by every token."""
+    s = synth.Shape(1, 40, 2, (32, 32), 16, 64, 512, 512, 16, act, bank, name="k512")
+    x = synth.make_inputs(s, seed=30)
+    print(f"write/read W = R = 512 act={act} bank={bank}", flush=True)
     check_parity(s, run_gpu(s, x), run_oracle(s, x))
 
 
