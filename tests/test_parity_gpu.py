@@ -128,6 +128,33 @@ def test_topk_exact_filtered(widths, dk, k, kind, scoring):
     _topk_case(widths, dk, k, "bf16", kind, T=40, scoring=scoring)
 
 
+@pytest.mark.parametrize("kind", ["ternary_onehot", "binary_onehot"])
+@pytest.mark.parametrize("scoring", ["filtered", "direct"])
+def test_topk_massive_ties(kind, scoring):
+    """Queries with one nonzero coordinate (+-1) per factor over ternary or 0/1 sub-keys (1024 of them, k 64): 300 to
+    650 sub-keys of a factor tie at its k_p-th score, so the filtered scoring's first stage keeps that many (its
+    widest listed selection, and past 512 the keys taken from registers) and the tie rule (smaller index first)
+    decides the ids; both scorings against the oracle, bit for bit."""
+    widths, dk, k, T, H = (1024, 32), 64, 64, 40, 2
+    rng = np.random.default_rng(11)
+    q = np.zeros((1, T, H, 2 * dk), np.float32)
+    for f in range(2):
+        j = rng.integers(0, dk, (1, T, H))
+        sign = rng.choice([-1.0, 1.0], (1, T, H, 1)).astype(np.float32)
+        np.put_along_axis(q[..., f * dk:(f + 1) * dk], j[..., None], sign, -1)
+    if kind == "ternary_onehot":
+        sub = rng.integers(-1, 2, (H, sum(widths), dk)).astype(np.float32)
+    else:
+        sub = (rng.random((H, sum(widths), dk)) < 0.6).astype(np.float32)
+    print(f"topk massive ties {kind} {scoring}", flush=True)
+    ids, sc = binding.topk_product_keys(to_dev(q, torch.bfloat16), to_dev(sub, torch.bfloat16), widths, k,
+                                        scoring=scoring)
+    torch.cuda.synchronize()
+    rid, rsc = oracle.topk(q, sub, widths, k)
+    assert np.array_equal(ids.cpu().numpy(), rid)
+    assert np.array_equal(sc.cpu().numpy(), rsc)
+
+
 @pytest.mark.parametrize("name", ["layer_65k", "large_1m"])
 def test_topk_filtered_equals_direct(name):
     """The filtered (MFMA) scoring and the direct fp64 scoring return identical ids and scores at full size."""
