@@ -620,13 +620,30 @@ __global__ __launch_bounds__(64) void bwd_subkey_kernel(Dims D, BwdArgs a, int c
   for (int q0 = r0; q0 < r1; q0 += BWD_SK_ROWS) {
     const int nr = min(BWD_SK_ROWS, r1 - q0);
     __syncthreads();  // the previous rows' staging is consumed
-    for (int e = lane; e < nr * K; e += 64) {
-      const int rr = e / K, i = e % K;
-      const int r = q0 + rr, b = r / T, t = r % T;
-      const long long so = ((long long)b * D.H + h) * T + t;
-      const int slot = i < W ? a.widx[so * W + i] : a.ridx[so * R + (i - W)];
-      sid[e] = (int)((slot / stride) % n);  // the factor-f sub-key (divisions here, in parallel, not in the serial sums)
-      sds[e] = a.ds[so * K + i];
+    // the terms' slot ids and gradients, SKL loads a lane in flight together, then the factor-f sub-keys (32-bit
+    // divisions here, in parallel, not in the serial sums; slot ids and stride are below 2^31)
+    constexpr int SKL = 8;
+    const int ne = nr * K, istride = (int)stride;
+    for (int e0 = lane; e0 < ne; e0 += 64 * SKL) {
+      int slot[SKL];
+      float dsv[SKL];
+#pragma unroll
+      for (int u = 0; u < SKL; ++u) {
+        const int e = min(e0 + 64 * u, ne - 1);
+        const int rr = e / K, i = e % K;
+        const int r = q0 + rr, b = r / T, t = r % T;
+        const long long so = ((long long)b * D.H + h) * T + t;
+        slot[u] = i < W ? a.widx[so * W + i] : a.ridx[so * R + (i - W)];
+        dsv[u] = a.ds[so * K + i];
+      }
+#pragma unroll
+      for (int u = 0; u < SKL; ++u) {
+        const int e = e0 + 64 * u;
+        if (e < ne) {
+          sid[e] = (slot[u] / istride) % n;
+          sds[e] = dsv[u];
+        }
+      }
     }
     float xw[BWD_SK_ROWS], xr[BWD_SK_ROWS];
 #pragma unroll
