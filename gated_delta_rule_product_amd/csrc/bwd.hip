@@ -540,6 +540,7 @@ __global__ __launch_bounds__(BWD_FAST_GROUPS * LPG) void bwd_sweep_fast_kernel(D
 template <typename A>
 __global__ __launch_bounds__(256) void bwd_token_kernel(Dims D, BwdArgs a, int nsl) {
   __shared__ float sd[MAX_K * 2 + 2];
+  __shared__ float swt[MAX_K * 2];              // the terms' softmax weights (write, then read)
   __shared__ float sm[2];
   __shared__ uint16_t ssub[MAX_K * 2][MAX_F];  // factor sub-key of every term (n_f <= 4096)
   const long long so = blockIdx.x;
@@ -547,33 +548,48 @@ __global__ __launch_bounds__(256) void bwd_token_kernel(Dims D, BwdArgs a, int n
   const int st = (int)(so / T), t = (int)(so % T);
   const int b = st / D.H, h = st % D.H;
   const long long row = ((long long)b * T + t) * D.H + h;
+  // slice partials added in slice order (eight loads a thread in flight), the weights and slot ids alongside
+  constexpr int NB = 8;
   for (int p = threadIdx.x; p < P; p += 256) {
     float s = 0.f;
-    for (int sl = 0; sl < nsl; ++sl) s += a.part[((long long)sl * D.S * T + so) * P + p];
+    int sl = 0;
+    for (; sl + NB <= nsl; sl += NB) {
+      float v[NB];
+#pragma unroll
+      for (int u = 0; u < NB; ++u) v[u] = a.part[((long long)(sl + u) * D.S * T + so) * P + p];
+#pragma unroll
+      for (int u = 0; u < NB; ++u) s += v[u];
+    }
+    for (; sl < nsl; ++sl) s += a.part[((long long)sl * D.S * T + so) * P + p];
     sd[p] = s;
+  }
+  int sid = 0;  // the slot id of term threadIdx.x (W + R <= 256 here; the loop below covers more)
+  for (int i = threadIdx.x; i < W + R; i += 256) {
+    swt[i] = i < W ? a.wwt[so * W + i] : a.rwt[so * R + (i - W)];
+    sid = i < W ? a.widx[so * W + i] : a.ridx[so * R + (i - W)];
   }
   __syncthreads();
   if (threadIdx.x == 0) {
     a.galpha[row] = sd[W + R];
     a.gbeta[row] = sd[W + R + 1];
     float m = 0.f;
-    for (int i = 0; i < W; ++i) m += a.wwt[so * W + i] * sd[i];
+    for (int i = 0; i < W; ++i) m += swt[i] * sd[i];
     sm[0] = m;
   } else if (threadIdx.x == 64) {
     float m = 0.f;
-    for (int j = 0; j < R; ++j) m += a.rwt[so * R + j] * sd[W + j];
+    for (int j = 0; j < R; ++j) m += swt[W + j] * sd[W + j];
     sm[1] = m;
   }
   __syncthreads();
   float* ds = a.ds + so * (W + R);
   for (int i = threadIdx.x; i < W + R; i += 256) {
     const bool wr = i < W;
-    const float wt = wr ? a.wwt[so * W + i] : a.rwt[so * R + (i - W)];
-    const float v = wt * (sd[i] - sm[wr ? 0 : 1]);
+    const float v = swt[i] * (sd[i] - sm[wr ? 0 : 1]);
     sd[i] = v;
     ds[i] = v;
-    long long id = wr ? a.widx[so * W + i] : a.ridx[so * R + (i - W)];
-    for (int f = D.F - 1; f >= 0; --f) {  // mixed radix, factor 0 most significant
+    // mixed radix, factor 0 most significant (slot ids are below 2^31)
+    int id = W + R <= 256 ? sid : (wr ? a.widx[so * W + i] : a.ridx[so * R + (i - W)]);
+    for (int f = D.F - 1; f >= 0; --f) {
       ssub[i][f] = (uint16_t)(id % D.widths[f]);
       id /= D.widths[f];
     }
@@ -590,8 +606,17 @@ __global__ __launch_bounds__(256) void bwd_token_kernel(Dims D, BwdArgs a, int n
     long long off = 0;
     for (int g = 0; g < f; ++g) off += D.widths[g];
     const int n = kind ? R : W, i0 = kind ? W : 0;
+    const A* subc = sub + off * D.dk + c;
     float acc = 0.f;
-    for (int i = 0; i < n; ++i) acc += sd[i0 + i] * to_f<A>(sub[(off + ssub[i0 + i][f]) * D.dk + c]);
+    int i = 0;
+    for (; i + NB <= n; i += NB) {  // the terms in order, eight sub-key loads in flight
+      float y[NB];
+#pragma unroll
+      for (int u = 0; u < NB; ++u) y[u] = to_f<A>(subc[(long long)ssub[i0 + i + u][f] * D.dk]);
+#pragma unroll
+      for (int u = 0; u < NB; ++u) acc += sd[i0 + i + u] * y[u];
+    }
+    for (; i < n; ++i) acc += sd[i0 + i] * to_f<A>(subc[(long long)ssub[i0 + i][f] * D.dk]);
     (kind ? a.grq : a.gwkeys)[row * Fdk + fc] = acc;
   }
 }
