@@ -616,6 +616,17 @@ def test_write_read_two_million_slots():
     check_parity(s, run_gpu(s, x), run_oracle(s, x))
 
 
+@pytest.mark.parametrize("W,R", [(64, 40), (24, 200)])
+def test_write_read_filtered_kinds_differ(W, R):
+    """bf16 write/read on 1024-sub-key factors (the filtered top-k in block mode) with different write and read k:
+    the two kinds' workgroups lay out their score rows and selection buffers differently in one launch (k 200 leaves
+    the buffers outside the rows); parity with the oracle."""
+    s = synth.Shape(2, 48, 2, (1024, 32), 64, 64, W, R, 16, "bf16", "f32", name="filtered_kinds")
+    x = synth.make_inputs(s, seed=63)
+    print(f"write/read filtered W={W} R={R}", flush=True)
+    check_parity(s, run_gpu(s, x), run_oracle(s, x))
+
+
 def test_write_read_split_off_the_chunk_grid():
     """Resume at a token that is not a multiple of chunk_size: the chunk grid restarts at the second call, so the
     result may differ from one call only by rounding (chunk size changes results only through rounding); both match
