@@ -18,6 +18,7 @@
 // writes its partial sums and a second kernel adds them over the slices in order. Every sum has a fixed order.
 #include "bwd_shape.h"
 #include "sdm_internal.h"
+#include "topk_wave.h"  // wave_sync, lanes_below_mask
 
 namespace sdm {
 
@@ -697,6 +698,149 @@ __global__ __launch_bounds__(64) void bwd_subkey_kernel(Dims D, BwdArgs a, int c
     for (int i = 0; i < n; ++i) a.sgpart[(((long long)rb * D.H + h) * sumn + off + i) * D.dk + c] = acc[i * cb + lane];
 }
 
+// Sub-key partial sums of one block of token rows, by sub-key: the block's terms are counting-sorted by their
+// factor-f sub-key (stable: a sub-key's terms keep their order), then each sub-key's run of terms is summed in a
+// register in that order, with the same additions as bwd_subkey_kernel's (so the same bits), and stored once;
+// sub-keys without a term store zero. Four waves: the count on every thread, the scan and the placement on wave 0
+// (chunks of 64 terms, lanes with the same sub-key matched by ballots on its bits), the sub-keys split between the
+// waves by where their buckets start. Lane c owns column 64 cblk + c. For blocks of at most BWD_SKS_ROWS rows and
+// BWD_SKS_TERMS terms and at most 4096 sub-keys a factor (the old one-wave kernel serves the rest).
+constexpr int BWD_SKS_TERMS = 8192, BWD_SKS_ROWS = 64;
+inline size_t bwd_subkey_sorted_lds(int nmax, int rows, int K) {
+  const size_t nt = (size_t)rows * K;
+  return (size_t)align16(3LL * nmax * 4) + (size_t)align16((long long)nt * 2) + nt * 8 + (size_t)rows * 2 * 64 * 4;
+}
+
+template <typename A>
+__global__ __launch_bounds__(256) void bwd_subkey_sorted_kernel(Dims D, BwdArgs a, int ncb, int rows_per_block) {
+  extern __shared__ __align__(16) unsigned char skl[];
+  const int rb = blockIdx.x, h = blockIdx.y, f = blockIdx.z / ncb, cblk = blockIdx.z % ncb;
+  const int n = D.widths[f], tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int W = D.W, R = D.R, T = D.T, Fdk = D.F * D.dk, K = W + R;
+  const int r0 = rb * rows_per_block, nr = max(0, min(rows_per_block, D.B * T - r0));
+  const int nt = nr * K;
+  int* hist = (int*)skl;                                               // [n] terms per sub-key
+  int* start = hist + n;                                               // [n] bucket starts (advanced)
+  int* bstart = start + n;                                             // [n] bucket starts
+  uint16_t* tsf = (uint16_t*)(skl + align16(3LL * n * 4));            // [nt] sub-key of term e
+  // [nt] terms by sub-key, packed (sub-key << 20) | (row 2 + query << 13) | term (12 + 7 + 13 bits)
+  uint32_t* sorted = (uint32_t*)((unsigned char*)tsf + align16((long long)nt * 2));
+  float* tds = (float*)(sorted + nt);                                  // [nt] slot-score gradients
+  float* xs = tds + nt;                                                // [nr][2][64] key / query column values
+  long long stride = 1, off = 0, sumn = 0;
+  for (int g = D.F - 1; g > f; --g) stride *= D.widths[g];
+  for (int g = 0; g < f; ++g) off += D.widths[g];
+  for (int g = 0; g < D.F; ++g) sumn += D.widths[g];
+  for (int i = tid; i < n; i += 256) hist[i] = 0;
+  // the terms' sub-keys and gradients (eight loads a thread in flight; slot ids and stride below 2^31)
+  constexpr int SKL = 8;
+  const int istride = (int)stride;
+  for (int e0 = tid; e0 < nt; e0 += 256 * SKL) {
+    int slot[SKL];
+    float dsv[SKL];
+#pragma unroll
+    for (int u = 0; u < SKL; ++u) {
+      const int e = min(e0 + 256 * u, nt - 1);
+      const int rr = e / K, i = e % K;
+      const int r = r0 + rr, b = r / T, t = r % T;
+      const long long so = ((long long)b * D.H + h) * T + t;
+      slot[u] = i < W ? a.widx[so * W + i] : a.ridx[so * R + (i - W)];
+      dsv[u] = a.ds[so * K + i];
+    }
+#pragma unroll
+    for (int u = 0; u < SKL; ++u) {
+      const int e = e0 + 256 * u;
+      if (e < nt) {
+        tsf[e] = (uint16_t)((slot[u] / istride) % n);
+        tds[e] = dsv[u];
+      }
+    }
+  }
+  const int c = cblk * 64 + lane;
+  const bool on = c < D.dk;
+  for (int rr = wv; rr < nr; rr += 4) {
+    const int r = r0 + rr, b = r / T, t = r % T;
+    const long long row = ((long long)b * T + t) * D.H + h;
+    xs[(rr * 2) * 64 + lane] = on ? to_f<A>(((const A*)a.wkeys)[row * Fdk + f * D.dk + c]) : 0.f;
+    xs[(rr * 2 + 1) * 64 + lane] = on ? to_f<A>(((const A*)a.rq)[row * Fdk + f * D.dk + c]) : 0.f;
+  }
+  __syncthreads();
+  for (int e = tid; e < nt; e += 256) atomicAdd(&hist[tsf[e]], 1);  // integer counts: order independent
+  __syncthreads();
+  if (wv == 0) {
+    // exclusive scan of the counts, 64 sub-keys a step
+    int carry = 0;
+    for (int i0 = 0; i0 < n; i0 += 64) {
+      const int i = i0 + lane;
+      const int v = i < n ? hist[i] : 0;
+      int incl = v;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+      }
+      if (i < n) start[i] = bstart[i] = carry + incl - v;
+      carry += __shfl(incl, 63, 64);
+    }
+    wave_sync();
+    // stable placement, 64 terms a step in term order
+    int nb = 0;
+    while ((1 << nb) < n) ++nb;
+    const uint64_t below = lanes_below_mask();
+    for (int e0 = 0; e0 < nt; e0 += 64) {
+      const int e = e0 + lane;
+      const bool ok = e < nt;
+      const int s = ok ? tsf[e] : 0;
+      uint64_t m = __ballot(ok);
+      for (int bt = 0; bt < nb; ++bt) {
+        const bool one = ((s >> bt) & 1) != 0;
+        const uint64_t bb = __ballot(one);
+        m &= one ? bb : ~bb;
+      }
+      const int s0 = start[s];  // every lane reads before any lane advances a bucket
+      wave_sync();
+      if (ok) {
+        const int rr = e / K;
+        const uint32_t xo = (uint32_t)(rr * 2 + (e - rr * K < W ? 0 : 1));
+        sorted[s0 + __popcll(m & below)] = ((uint32_t)s << 20) | (xo << 13) | (uint32_t)e;
+      }
+      if (ok && (m & ~below & ~(1ull << lane)) == 0) start[s] = s0 + __popcll(m);  // the group's last lane
+      wave_sync();
+    }
+  }
+  __syncthreads();
+  // the sums: wave w takes the sub-keys whose bucket starts in [w nt / 4, (w + 1) nt / 4) (the last wave also those
+  // starting at nt: empty ones), each bucket's terms in order, branch-free within a bucket; empty buckets store zero
+  float* outc = a.sgpart + (((long long)rb * D.H + h) * sumn + off) * D.dk + c;
+  const int lo = (int)((long long)wv * nt / 4), hi = wv == 3 ? nt + 1 : (int)((long long)(wv + 1) * nt / 4);
+  constexpr int RB = 4;
+  for (int sk = 0; sk < n; ++sk) {
+    const int b = bstart[sk];
+    if (b < lo || b >= hi) continue;
+    const int cnt = hist[sk];
+    float acc = 0.f;
+    int i = b;
+    for (; i + RB <= b + cnt; i += RB) {
+      uint32_t pk[RB];
+      float dv[RB], xv[RB];
+#pragma unroll
+      for (int u = 0; u < RB; ++u) pk[u] = sorted[i + u];
+#pragma unroll
+      for (int u = 0; u < RB; ++u) {
+        dv[u] = tds[pk[u] & 0x1FFF];
+        xv[u] = xs[((pk[u] >> 13) & 0x7F) * 64 + lane];
+      }
+#pragma unroll
+      for (int u = 0; u < RB; ++u) acc += dv[u] * xv[u];
+    }
+    for (; i < b + cnt; ++i) {
+      const uint32_t pk = sorted[i];
+      acc += tds[pk & 0x1FFF] * xs[((pk >> 13) & 0x7F) * 64 + lane];
+    }
+    if (on) outc[(long long)sk * D.dk] = acc;  // 0 for an empty bucket
+  }
+}
+
 __global__ __launch_bounds__(256) void bwd_subkey_sum_kernel(const float* __restrict__ sgpart, float* __restrict__ gsub,
                                                              long long n, int nrb) {
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
@@ -835,6 +979,19 @@ static hipError_t launch_bwd_t(const Dims& D, const BwdArgs& a, hipStream_t st) 
   for (int f = 0; f < D.F; ++f) {
     sumn += D.widths[f];
     nmax = max(nmax, D.widths[f]);
+  }
+  const int K = D.W + D.R;
+  if (nmax <= 4096 && rpb <= BWD_SKS_ROWS && (long long)rpb * K <= BWD_SKS_TERMS) {
+    const int ncb2 = (D.dk + 63) / 64;
+    const size_t l2 = bwd_subkey_sorted_lds(nmax, rpb, K);
+    (void)hipFuncSetAttribute((const void*)bwd_subkey_sorted_kernel<A>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)l2);
+    hipLaunchKernelGGL((bwd_subkey_sorted_kernel<A>), dim3((unsigned)nrb, (unsigned)D.H, (unsigned)(D.F * ncb2)),
+                       dim3(256), l2, st, D, a, ncb2, rpb);
+    const long long n = (long long)D.H * sumn * D.dk;
+    hipLaunchKernelGGL(bwd_subkey_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.sgpart, a.gsub,
+                       n, nrb);
+    return hipGetLastError();
   }
   const size_t stage = (size_t)BWD_SK_ROWS * (D.W + D.R) * 8;  // <= 128 KiB (W, R <= 512)
   const size_t budget = 150 * 1024 - stage;                     // >= 22 KiB: n_f * 4 <= 16 KiB always fits

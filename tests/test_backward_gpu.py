@@ -151,6 +151,9 @@ CASES = [
     # steps of up to four consecutive tokens with disjoint slots (W, R <= 32 on 16-column slices), 4,096 slots so
     # that runs of every length occur, and a token count that is not a multiple of four
     ("token_runs", synth.Shape(2, 61, 2, (64, 64), 8, 64, 12, 20, 16, name="runs"), True),
+    # more than 8192 terms in a row block of the sub-key sums (16 rows x 560 terms): the one-wave kernel instead of
+    # the sorting one
+    ("subkey_one_wave", synth.Shape(1, 20, 1, (32, 32), 8, 16, 300, 260, 4, name="sk1w"), True),
 ]
 
 
