@@ -846,7 +846,15 @@ __global__ __launch_bounds__(256) void bwd_subkey_sum_kernel(const float* __rest
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
   float s = 0.f;
-  for (int rb = 0; rb < nrb; ++rb) s += sgpart[(long long)rb * n + i];
+  int rb = 0;
+  for (; rb + 8 <= nrb; rb += 8) {  // the blocks in order, eight loads in flight
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = sgpart[(long long)(rb + u) * n + i];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; rb < nrb; ++rb) s += sgpart[(long long)rb * n + i];
   gsub[i] = s;
 }
 
