@@ -154,6 +154,8 @@ CASES = [
     # more than 8192 terms in a row block of the sub-key sums (16 rows x 560 terms): the one-wave kernel instead of
     # the sorting one
     ("subkey_one_wave", synth.Shape(1, 20, 1, (32, 32), 8, 16, 300, 260, 4, name="sk1w"), True),
+    # sub-keys of 96 coordinates: the sub-key sums in two column blocks, the second one partly past dk
+    ("dk96", synth.Shape(1, 24, 2, (16, 16), 96, 32, 8, 8, 8, name="dk96"), True),
 ]
 
 
